@@ -1,0 +1,285 @@
+/*
+ * libkvfuse - one transformer layer of RAG KV-cache fusion with selective
+ * recomputation, for AMD Instinct MI355X (gfx950).
+ *
+ * Sources, cited by page title and section / equation:
+ *   [QCF] "QCFuse: Query-Aware Cache Fusion via Compressed View for Efficient
+ *         RAG Serving": 2.1.1 (Eq. 1, context C and query U), 2.1.2 (Eq. 3-5,
+ *         per-chunk caches and their re-positioning), 2.1.3 (Eq. 6-7,
+ *         selective recomputation and the fused cache), 3.2.1 (Eq. 9-11,
+ *         query-to-context attention mass and TopK).
+ *   [KVB] "KVBoost: Chunk-Level Key-Value Cache Reuse with Deviation-Guided
+ *         Recomputation for Efficient Large Language Model Inference":
+ *         3.1 (Eq. 1-2, projections, attention, cache layout), 3.2 (Eq. 3,
+ *         RoPE and the rotation correction), 4.5 (Eq. 7, KIVI int8/int4),
+ *         4.6.2 (Algorithm 2, key-deviation scoring).
+ *
+ * One layer, per request:  N context tokens (stitched chunks) then U query
+ * tokens, T = N + U.  The path is
+ *   kvf_rerotate -> kvf_score -> kvf_select_topk -> kvf_recompute_qkv
+ *   -> kvf_scatter_kv -> kvf_sparse_q_attention
+ * every call enqueues HIP kernels on the caller's stream and returns; there
+ * is no host synchronisation inside the library.
+ *
+ * Conventions for every call:
+ *  - Pointers are DEVICE pointers unless the comment says "host".
+ *  - All tensors are contiguous row-major.  K/V caches are token-major
+ *    [rows, Hkv, d] ([KVB] 3.1).  Q is [rows, Hq, d].  Query head h reads
+ *    kv head h / (Hq / Hkv).  Weights are [out, in], the projection is x W^T.
+ *  - Element type: kvf_layer_desc.dtype selects fp32 or bf16 for every
+ *    float tensor of a call (activations, weights, caches, outputs).
+ *    Scores, statistics, LSE and rope tables are always fp32.
+ *  - Ownership: the caller allocates every buffer, including workspaces
+ *    (sized by the *_workspace_size queries).  The library never allocates or
+ *    frees device memory and keeps no pointer after a call returns.
+ *  - Streams: `stream` is a hipStream_t passed as void*; NULL is the null
+ *    stream.
+ *  - Errors: arguments are validated on the host before anything is
+ *    enqueued: KVF_ERR_INVALID_ARG for malformed arguments,
+ *    KVF_ERR_UNSUPPORTED for shapes the kernels do not implement,
+ *    KVF_ERR_WORKSPACE for a too-small workspace.  A failed launch returns
+ *    KVF_ERR_HIP.  kvf_last_error() gives a thread-local text of the last
+ *    failure.  On error, output contents are undefined.  No C++ exception
+ *    crosses this interface and the library never aborts.
+ *  - Device-side indices (row maps, positions, chunk tables) are checked
+ *    inside the kernels against the sizes passed here; an out-of-range
+ *    entry makes the kernel skip that row (its outputs are left unwritten)
+ *    instead of reading or writing outside the buffers.
+ *  - Thread safety: calls may be made from several host threads; calls that
+ *    write the same buffers must be ordered by the caller.
+ */
+#ifndef KVFUSE_H
+#define KVFUSE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVF_ABI_VERSION 1
+#define KVF_MAX_REQ 64      /* requests per call (batch metadata is passed by value) */
+
+typedef enum {
+  KVF_OK = 0,
+  KVF_ERR_INVALID_ARG = 1,
+  KVF_ERR_UNSUPPORTED = 2,
+  KVF_ERR_WORKSPACE = 3,
+  KVF_ERR_HIP = 4
+} kvf_status;
+
+typedef enum { KVF_F32 = 0, KVF_BF16 = 1 } kvf_dtype;
+
+typedef enum {
+  KVF_SCORE_DEVIATION = 0,   /* [KVB] 4.6.2 Algorithm 2: 1 - mean_h cos(K, K~) */
+  KVF_SCORE_ATTN_MASS = 1    /* [QCF] 3.2.1 Eq. 9-10: query-to-context mass  */
+} kvf_score_mode;
+
+enum { KVF_OUT_Q = 1, KVF_OUT_K = 2, KVF_OUT_V = 4 };
+
+/* Layer shape (host struct).  head_dim must be 64 or 128; n_q_heads must be a
+ * multiple of n_kv_heads.  RoPE is the rotate-half form (channel j paired
+ * with j + d/2), the reading this library takes of [KVB] 3.2 Eq. 3. */
+typedef struct {
+  int32_t hidden;
+  int32_t n_q_heads;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t dtype;             /* kvf_dtype */
+} kvf_layer_desc;
+
+/* Request batch (host struct, HOST arrays).  Request r owns rows
+ * [cu_T[r], cu_T[r+1]) of x and of the fused cache; its first n_ctx[r] rows
+ * are the context C, the rest the query U ([QCF] 2.1.1). */
+typedef struct {
+  int32_t n_req;             /* 1 .. KVF_MAX_REQ */
+  const int32_t* cu_T;       /* host [n_req + 1], cu_T[0] = 0, non-decreasing */
+  const int32_t* n_ctx;      /* host [n_req], 0 <= n_ctx[r] <= T_r */
+} kvf_batch;
+
+/* One stitched chunk (device array element, 32 bytes): `len` cached rows
+ * starting at pool row `src_row`, encoded at chunk-local positions 0..len-1,
+ * land at fused rows dst_row.. with request positions pos0.. ([QCF] 2.1.2
+ * Eq. 4).  pool_chunk indexes per-chunk KIVI key statistics. */
+typedef struct {
+  int32_t src_row;
+  int32_t dst_row;
+  int32_t pos0;
+  int32_t len;
+  int32_t pool_chunk;
+  int32_t reserved[3];
+} kvf_chunk;
+
+/* KIVI int8 cache ([KVB] 4.5 Eq. 7, b = 8): value = min + code * scale.
+ * Keys: per (pool chunk, kv head, channel) statistics; values: per
+ * (pool row, kv head). */
+typedef struct {
+  const uint8_t* k_codes;    /* [pool_rows, Hkv, d] */
+  const uint8_t* v_codes;    /* [pool_rows, Hkv, d] */
+  const float* k_min;        /* [n_pool_chunks, Hkv, d] */
+  const float* k_scale;      /* [n_pool_chunks, Hkv, d] */
+  const float* v_min;        /* [pool_rows, Hkv] */
+  const float* v_scale;      /* [pool_rows, Hkv] */
+  int32_t n_pool_chunks;
+} kvf_kivi8;
+
+/* ---------------------------------------------------------------------------
+ * kvf_rope_table - cos/sin of the rotation angles p * theta_j for positions
+ * p in [0, n_pos) and j in [0, d/2), theta_j = base^(-2j/d) ([KVB] 3.2,
+ * Eq. 3).  Angles and cos/sin are evaluated in fp64 on the device and
+ * rounded to fp32.  cos_tab, sin_tab: [n_pos, d/2] fp32.  Built once per
+ * (base, d); every call that rotates takes these tables.
+ */
+kvf_status kvf_rope_table(double base, int32_t head_dim, int32_t n_pos,
+                          float* cos_tab, float* sin_tab, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * kvf_rerotate - S1: re-position and stitch per-chunk caches into the fused
+ * cache ([QCF] 2.1.2 Eq. 4; [KVB] 3.2).  For every chunk c and t < len:
+ *   fused_k[dst_row + t] = R(pos0) * K_pool[src_row + t]   (delta rotation:
+ *                          the cached key already carries R(t), and
+ *                          R(pos0) R(t) = R(pos0 + t))
+ *   fused_v[dst_row + t] = V_pool[src_row + t]
+ * Dense caches: pool_k, pool_v [pool_rows, Hkv, d] in dtype, kivi = NULL.
+ * int8 caches: pool_k = pool_v = NULL and kivi != NULL; codes are decoded
+ * (min + code * scale, fp32) before the rotation (dequant-on-load).
+ * Output dtype must be bf16 for int8 caches.
+ * chunks: device [n_chunks]; max_chunk_len (host) bounds every len.
+ * rope tables cover positions [0, rope_n_pos); pos0 >= rope_n_pos skips the
+ * chunk.  Fused rows no chunk covers are not written.
+ */
+kvf_status kvf_rerotate(const kvf_layer_desc* layer, const kvf_chunk* chunks,
+                        int32_t n_chunks, int32_t max_chunk_len,
+                        const void* pool_k, const void* pool_v,
+                        const kvf_kivi8* kivi, int64_t pool_rows,
+                        const float* rope_cos, const float* rope_sin,
+                        int32_t rope_n_pos, void* fused_k, void* fused_v,
+                        int64_t fused_rows, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * kvf_score - S2: one fp32 score per context token; scores [sum_r n_ctx[r]]
+ * request-major.
+ * KVF_SCORE_DEVIATION ([KVB] 4.6.2 Algorithm 2, one layer):
+ *   score_t = 1 - (1/Hkv) sum_h cos(fused_k[t, h], k_fresh[t, h]),
+ *   cos := 0 when either norm is 0.  fused_k and k_fresh are [sum T, Hkv, d]
+ *   indexed by the same rows; only context rows are read.  q_u unused.
+ * KVF_SCORE_ATTN_MASS ([QCF] 3.2.1 Eq. 9-10, one layer):
+ *   q_u [sum_r U_r, Hq, d] holds the rotated queries of each request's query
+ *   tokens (positions N..T-1), request-major.  fused_k must already hold the
+ *   query tokens' keys at rows N..T-1.  Query token i attends causally to
+ *   keys 0..N+i; each (i, head) softmax is over that whole row, and
+ *   score_t = sum over the last n_last_q query tokens (all when <= 0) and all
+ *   query heads of the probability at context position t.  Softmax scale is
+ *   1/sqrt(d).  Needs a workspace of kvf_score_workspace_size() bytes.
+ */
+kvf_status kvf_score(kvf_score_mode mode, const kvf_layer_desc* layer,
+                     const kvf_batch* batch, const void* fused_k,
+                     const void* k_fresh, const void* q_u, int32_t n_last_q,
+                     float* scores, void* workspace, size_t ws_bytes,
+                     void* stream);
+size_t kvf_score_workspace_size(kvf_score_mode mode, const kvf_layer_desc* layer,
+                                const kvf_batch* batch, int32_t n_last_q);
+
+/* ---------------------------------------------------------------------------
+ * kvf_select_topk - S3: P_r = TopK(score, k_r) per request ([QCF] 3.2.1
+ * Eq. 11).  Order: larger score first; ties to the lower position; -0 == +0;
+ * NaN ranks below every number.  k_per_req: HOST [n_req], 0 <= k_r <= N_r.
+ *   out_idx  [sum k_r]: P_r ascending, positions within the request.
+ *   out_rows [sum (k_r + U_r)] (may be NULL): flat rows (cu_T[r] + p) of
+ *            P_r followed by the request's query rows, i.e. the rows to
+ *            recompute, ascending per request.
+ *   out_pos  [sum (k_r + U_r)] (may be NULL): the matching positions.
+ * Needs kvf_select_workspace_size() bytes of workspace (0 today; the
+ * argument is reserved).
+ */
+kvf_status kvf_select_topk(const float* scores, const kvf_batch* batch,
+                           const int32_t* k_per_req, int32_t* out_idx,
+                           int32_t* out_rows, int32_t* out_pos,
+                           void* workspace, size_t ws_bytes, void* stream);
+size_t kvf_select_workspace_size(const kvf_batch* batch);
+
+/* ---------------------------------------------------------------------------
+ * kvf_recompute_qkv - S4: fresh Q/K/V of M rows ([QCF] 2.1.3 KV^New;
+ * [KVB] 3.1 Eq. 1 and 3.2 Eq. 3).  For m < M with r = row_src[m] and
+ * p = row_pos[m]:
+ *   q_out[m] = R(p) x[r] Wq^T   (if out_mask & KVF_OUT_Q)   [M, Hq, d]
+ *   k_out[m] = R(p) x[r] Wk^T   (if out_mask & KVF_OUT_K)   [M, Hkv, d]
+ *   v_out[m] =      x[r] Wv^T   (if out_mask & KVF_OUT_V)   [M, Hkv, d]
+ * x: [x_rows, hidden]; w_qkv: [(Hq + 2 Hkv) d, hidden] = [Wq; Wk; Wv].
+ * row_src may be NULL (identity, requires M <= x_rows).  fp32 accumulation.
+ * The same call builds per-chunk caches ahead of serving ([QCF] 2.1.2 Eq. 3):
+ * pass the cached hidden states with chunk-local positions and mask K|V.
+ */
+kvf_status kvf_recompute_qkv(const kvf_layer_desc* layer, const void* x,
+                             int64_t x_rows, const int32_t* row_src,
+                             const int32_t* row_pos, int32_t M,
+                             const void* w_qkv, uint32_t out_mask,
+                             const float* rope_cos, const float* rope_sin,
+                             int32_t rope_n_pos, void* q_out, void* k_out,
+                             void* v_out, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * kvf_scatter_kv - S5: KV^Fuse_p = KV^New_p for the recomputed rows
+ * ([QCF] 2.1.3 Eq. 7), written in place:
+ *   fused_k[dst_row[m]] = k_src[k_src_row ? k_src_row[m] : m]
+ *   fused_v[dst_row[m]] = v_src[v_src_row ? v_src_row[m] : m]
+ * k_src: [k_src_rows, Hkv, d], v_src: [v_src_rows, Hkv, d]; either side may
+ * be NULL to leave that cache untouched.  Destination rows must be unique
+ * (duplicates race).
+ */
+kvf_status kvf_scatter_kv(const kvf_layer_desc* layer, const void* k_src,
+                          const int32_t* k_src_row, int64_t k_src_rows,
+                          const void* v_src, const int32_t* v_src_row,
+                          int64_t v_src_rows, const int32_t* dst_row, int32_t M,
+                          void* fused_k, void* fused_v, int64_t fused_rows,
+                          void* stream);
+
+/* ---------------------------------------------------------------------------
+ * kvf_sparse_q_attention - S6: causal attention of the recomputed rows over
+ * the fused cache ([QCF] 2.1.3: a recomputed token reads prefix positions
+ * j <= p; [KVB] 3.1 Eq. 2).  Request r owns q rows [cu_q[r], cu_q[r+1]) whose
+ * positions q_pos (within the request) are ascending; for q head h:
+ *   out[m, h] = sum_{j <= q_pos[m]} softmax_j(q[m,h] . K[cu_T[r]+j, h/G] *
+ *               sm_scale) V[cu_T[r]+j, h/G]
+ *   lse[m, h] = natural log-sum-exp of the scaled scores (lse may be NULL).
+ * cu_q: HOST [n_req + 1].  q_pos[m] must be < T_r (else the row is skipped).
+ */
+kvf_status kvf_sparse_q_attention(const kvf_layer_desc* layer,
+                                  const kvf_batch* batch, const void* q,
+                                  const int32_t* q_pos, const int32_t* cu_q,
+                                  const void* fused_k, const void* fused_v,
+                                  float sm_scale, void* out, float* lse,
+                                  void* stream);
+
+/* ---------------------------------------------------------------------------
+ * kvf_kivi8_encode - offline encoder of a dense bf16 per-chunk cache into the
+ * int8 KIVI form read by kvf_rerotate ([KVB] 4.5 Eq. 7, b = 8).  Runs ahead
+ * of serving, not on the fused-layer path.  fp32 arithmetic, in this order:
+ * range = max - min; scale = range / 255; inv = 255 / range;
+ * code = round-half-even((x - min) * inv) clamped to [0, 255]; range 0 gives
+ * scale 0 and code 0.  Keys: statistics per (pool chunk, head, channel) over
+ * the chunk's rows pool_cu[c]..pool_cu[c+1]-1 (pool_cu: device
+ * [n_pool_chunks + 1]); values: per (row, head) over the channels.
+ * out must point at writable arrays (the const members are written).
+ */
+kvf_status kvf_kivi8_encode(const kvf_layer_desc* layer, const void* pool_k,
+                            const void* pool_v, const int32_t* pool_cu,
+                            int32_t n_pool_chunks, int64_t pool_rows,
+                            int32_t max_chunk_len, const kvf_kivi8* out,
+                            void* stream);
+
+/* floor(ratio_pct * n_ctx / 100) in integer arithmetic: the recompute budget
+ * |P| = floor(rho N) of [QCF] 3.2.1 Eq. 11.  Returns -1 for negative input
+ * or ratio_pct > 100. */
+int32_t kvf_recompute_budget(int32_t n_ctx, int32_t ratio_pct);
+
+const char* kvf_status_string(kvf_status status);
+const char* kvf_last_error(void);
+int32_t kvf_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVFUSE_H */

@@ -1,0 +1,77 @@
+"""Build libkvfuse.so (gfx950) from the HIP sources in this directory.
+
+    python -m rag_kv_cache_kvf_amd.csrc.build [--jobs N]
+
+Every .hip file is compiled to an object under <repo>/_build/ with hipcc and
+the objects are linked into rag_kv_cache_kvf_amd/libkvfuse.so.  The build
+always recompiles (it is the "does it build" check); it never needs a GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import glob
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+PKG = os.path.dirname(HERE)
+ROOT = os.path.dirname(PKG)
+INCLUDE = os.path.join(ROOT, "include")
+OUT_LIB = os.path.join(PKG, "libkvfuse.so")
+BUILD_DIR = os.path.join(ROOT, "_build")
+ARCH = "gfx950"
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+CFLAGS = [
+    "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-Wall",
+    # packed fp32 instructions stay off (plain scalar fp32 code only)
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I", INCLUDE, "-I", HERE,
+]
+
+
+def sources():
+    return sorted(glob.glob(os.path.join(HERE, "*.hip")) + glob.glob(os.path.join(HERE, "kernels", "*.hip")))
+
+
+def _compile(src: str) -> str:
+    rel = os.path.relpath(src, HERE).replace(os.sep, "_")
+    obj = os.path.join(BUILD_DIR, rel[:-4] + ".o")
+    cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
+    # keep real diagnostics, drop the host pass's note about the GPU-only feature
+    noise = "'-packed-fp32-ops' is not a recognized feature"
+    warn = "\n".join(l for l in r.stderr.splitlines() if noise not in l).strip()
+    if warn:
+        print(warn, file=sys.stderr)
+    return obj
+
+
+def build(jobs: int | None = None, verbose: bool = True) -> str:
+    if not os.path.exists(HIPCC):
+        raise RuntimeError(f"hipcc not found at {HIPCC}")
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = sources()
+    jobs = jobs or min(len(srcs), max(1, (os.cpu_count() or 4)))
+    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(_compile, srcs))
+    tmp = OUT_LIB + ".tmp"
+    cmd = [HIPCC, "-shared", f"--offload-arch={ARCH}", "-fPIC", "-o", tmp, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    shutil.move(tmp, OUT_LIB)
+    if verbose:
+        print(f"built {OUT_LIB} from {len(srcs)} sources")
+    return OUT_LIB
+
+
+if __name__ == "__main__":
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--jobs", type=int, default=None)
+    build(ap.parse_args().jobs)

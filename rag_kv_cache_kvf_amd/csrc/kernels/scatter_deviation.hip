@@ -1,0 +1,141 @@
+// S5 in-place K/V scatter into the fused cache and S2 key-deviation score.
+//
+// Scatter: QCFuse page, section 2.1.3, Eq. 7 - the fused cache takes the
+// recomputed entry at every selected position and keeps the reused one
+// elsewhere; entries are written back at the same positions.
+// Deviation: KVBoost page, section 4.6.2, Algorithm 2 - delta_t = 1 minus the
+// mean over heads of cos(K_t, K~_t), here for one layer and the key heads.
+//
+// Both are HBM streams.  Scatter moves 16-byte vectors with a grid-stride
+// loop over (row, vector); deviation gives each context token one wave that
+// reads the two key rows with 16-byte loads and reduces per head with
+// cross-lane shuffles.
+#include "../kvf_common.h"
+
+namespace kvf {
+
+// ---------------------------------------------------------------------------
+// S5: scatter
+// ---------------------------------------------------------------------------
+struct ScatterArgs {
+  const uint8_t* k_src;
+  const int32_t* k_src_row;
+  int64_t k_src_rows;
+  const uint8_t* v_src;
+  const int32_t* v_src_row;
+  int64_t v_src_rows;
+  const int32_t* dst_row;
+  int M;
+  uint8_t* fused_k;
+  uint8_t* fused_v;
+  int64_t fused_rows;
+  int row_vecs;          // 16-byte vectors per row
+};
+
+__global__ void __launch_bounds__(256) scatter_kernel(ScatterArgs a) {
+  const int64_t total = static_cast<int64_t>(a.M) * a.row_vecs;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  const int64_t row_bytes = static_cast<int64_t>(a.row_vecs) * 16;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total;
+       i += stride) {
+    const int m = static_cast<int>(i / a.row_vecs);
+    const int v = static_cast<int>(i - static_cast<int64_t>(m) * a.row_vecs);
+    const int32_t dst = a.dst_row[m];
+    if (dst < 0 || dst >= a.fused_rows) continue;
+    if (a.k_src) {
+      const int64_t s = a.k_src_row ? a.k_src_row[m] : m;
+      if (s >= 0 && s < a.k_src_rows) {
+        const u32x4_t x = *reinterpret_cast<const u32x4_t*>(a.k_src + s * row_bytes + v * 16);
+        *reinterpret_cast<u32x4_t*>(a.fused_k + dst * row_bytes + v * 16) = x;
+      }
+    }
+    if (a.v_src) {
+      const int64_t s = a.v_src_row ? a.v_src_row[m] : m;
+      if (s >= 0 && s < a.v_src_rows) {
+        const u32x4_t x = *reinterpret_cast<const u32x4_t*>(a.v_src + s * row_bytes + v * 16);
+        *reinterpret_cast<u32x4_t*>(a.fused_v + dst * row_bytes + v * 16) = x;
+      }
+    }
+  }
+}
+
+hipError_t launch_scatter(const kvf_layer_desc& L, const void* ks, const int32_t* ksr,
+                          int64_t ks_rows, const void* vs, const int32_t* vsr, int64_t vs_rows,
+                          const int32_t* dst, int M, void* fk, void* fv, int64_t fused_rows,
+                          hipStream_t st) {
+  ScatterArgs a{};
+  a.k_src = static_cast<const uint8_t*>(ks);
+  a.k_src_row = ksr;
+  a.k_src_rows = ks_rows;
+  a.v_src = static_cast<const uint8_t*>(vs);
+  a.v_src_row = vsr;
+  a.v_src_rows = vs_rows;
+  a.dst_row = dst;
+  a.M = M;
+  a.fused_k = static_cast<uint8_t*>(fk);
+  a.fused_v = static_cast<uint8_t*>(fv);
+  a.fused_rows = fused_rows;
+  const int esz = L.dtype == KVF_BF16 ? 2 : 4;
+  a.row_vecs = L.n_kv_heads * L.head_dim * esz / 16;
+  const int64_t total = static_cast<int64_t>(M) * a.row_vecs;
+  const int64_t blocks = std::min<int64_t>((total + 255) / 256, 256 * 16);
+  hipLaunchKernelGGL(scatter_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// S2: key deviation
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ void __launch_bounds__(256) deviation_kernel(BatchArgs B, const T* __restrict__ fk,
+                                                        const T* __restrict__ kf, int hkv, int d,
+                                                        float* __restrict__ scores) {
+  const int wave = (blockIdx.x * blockDim.x + threadIdx.x) / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int total = B.cu_N[B.n_req];
+  if (wave >= total) return;
+  const int r = find_segment(B.cu_N, B.n_req, wave);
+  const int64_t row = B.cu_T[r] + (wave - B.cu_N[r]);
+  const int row_elems = hkv * d;
+  const int lanes_per_head = d >> 3;           // 8 elements per lane
+  const T* a = fk + row * row_elems;
+  const T* b = kf + row * row_elems;
+  float cos_acc = 0.f;
+  for (int e0 = lane * 8; e0 < row_elems; e0 += kWave * 8) {
+    float x[8], y[8];
+    Elem<T>::load8(a + e0, x);
+    Elem<T>::load8(b + e0, y);
+    float dot = 0.f, nx = 0.f, ny = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      dot = fmaf(x[i], y[i], dot);
+      nx = fmaf(x[i], x[i], nx);
+      ny = fmaf(y[i], y[i], ny);
+    }
+    dot = group_sum(dot, lanes_per_head);
+    nx = group_sum(nx, lanes_per_head);
+    ny = group_sum(ny, lanes_per_head);
+    const float den = sqrtf(nx) * sqrtf(ny);
+    if ((lane & (lanes_per_head - 1)) == 0 && den > 0.f) cos_acc += dot / den;
+  }
+  // lanes past the row end still take part in the shuffles above with zeros
+  cos_acc = wave_sum(cos_acc);
+  if (lane == 0) scores[wave] = 1.f - cos_acc / static_cast<float>(hkv);
+}
+
+hipError_t launch_deviation(const kvf_layer_desc& L, const BatchArgs& B, const void* fk,
+                            const void* kf, float* scores, hipStream_t st) {
+  const int total = B.cu_N[B.n_req];
+  const int blocks = ceil_div(total, 256 / kWave);
+  if (L.dtype == KVF_BF16)
+    hipLaunchKernelGGL(deviation_kernel<bf16_t>, dim3(blocks), dim3(256), 0, st, B,
+                       static_cast<const bf16_t*>(fk), static_cast<const bf16_t*>(kf),
+                       L.n_kv_heads, L.head_dim, scores);
+  else
+    hipLaunchKernelGGL(deviation_kernel<float>, dim3(blocks), dim3(256), 0, st, B,
+                       static_cast<const float*>(fk), static_cast<const float*>(kf),
+                       L.n_kv_heads, L.head_dim, scores);
+  return hipGetLastError();
+}
+
+}  // namespace kvf

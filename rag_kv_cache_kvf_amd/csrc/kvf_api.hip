@@ -1,0 +1,326 @@
+// libkvfuse C ABI: argument validation and dispatch to the HIP launchers.
+//
+// Every entry point validates on the host before anything is enqueued, maps
+// failures to kvf_status, records a thread-local message, and never lets a
+// C++ exception cross the interface.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <exception>
+
+#include "kvf_common.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+kvf_status fail(kvf_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+kvf_status from_hip(hipError_t e, const char* what) {
+  if (e == hipSuccess) {
+    g_err[0] = '\0';
+    return KVF_OK;
+  }
+  return fail(KVF_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define KVF_CHECK(cond, st, ...)            \
+  do {                                      \
+    if (!(cond)) return fail(st, __VA_ARGS__); \
+  } while (0)
+
+kvf_status check_layer(const kvf_layer_desc* L) {
+  KVF_CHECK(L != nullptr, KVF_ERR_INVALID_ARG, "layer descriptor is NULL");
+  KVF_CHECK(L->hidden > 0 && L->n_q_heads > 0 && L->n_kv_heads > 0 && L->head_dim > 0,
+            KVF_ERR_INVALID_ARG, "layer sizes must be positive");
+  KVF_CHECK(L->dtype == KVF_F32 || L->dtype == KVF_BF16, KVF_ERR_INVALID_ARG,
+            "dtype %d is not a kvf_dtype", L->dtype);
+  KVF_CHECK(L->n_q_heads % L->n_kv_heads == 0, KVF_ERR_UNSUPPORTED,
+            "n_q_heads (%d) must be a multiple of n_kv_heads (%d)", L->n_q_heads, L->n_kv_heads);
+  KVF_CHECK(L->head_dim == 64 || L->head_dim == 128, KVF_ERR_UNSUPPORTED,
+            "head_dim %d unsupported (64 or 128)", L->head_dim);
+  KVF_CHECK(L->n_q_heads / L->n_kv_heads <= 64, KVF_ERR_UNSUPPORTED,
+            "more than 64 query heads per kv head");
+  KVF_CHECK(L->hidden % 64 == 0, KVF_ERR_UNSUPPORTED, "hidden %d must be a multiple of 64",
+            L->hidden);
+  KVF_CHECK((static_cast<int64_t>(L->n_q_heads) + 2 * L->n_kv_heads) * L->head_dim < (1 << 30),
+            KVF_ERR_UNSUPPORTED, "layer too wide");
+  return KVF_OK;
+}
+
+kvf_status check_batch(const kvf_batch* b, kvf::BatchArgs* out) {
+  KVF_CHECK(b != nullptr, KVF_ERR_INVALID_ARG, "batch is NULL");
+  KVF_CHECK(b->n_req >= 1 && b->n_req <= KVF_MAX_REQ, KVF_ERR_INVALID_ARG,
+            "n_req %d outside [1, %d]", b->n_req, KVF_MAX_REQ);
+  KVF_CHECK(b->cu_T != nullptr && b->n_ctx != nullptr, KVF_ERR_INVALID_ARG,
+            "batch arrays are NULL");
+  KVF_CHECK(b->cu_T[0] == 0, KVF_ERR_INVALID_ARG, "cu_T[0] must be 0");
+  std::memset(out, 0, sizeof(*out));
+  out->n_req = b->n_req;
+  for (int r = 0; r < b->n_req; ++r) {
+    const int T = b->cu_T[r + 1] - b->cu_T[r];
+    KVF_CHECK(b->cu_T[r + 1] >= b->cu_T[r], KVF_ERR_INVALID_ARG, "cu_T decreases at %d", r);
+    KVF_CHECK(b->n_ctx[r] >= 0 && b->n_ctx[r] <= T, KVF_ERR_INVALID_ARG,
+              "n_ctx[%d] = %d outside [0, %d]", r, b->n_ctx[r], T);
+    out->cu_T[r + 1] = b->cu_T[r + 1];
+    out->n_ctx[r] = b->n_ctx[r];
+    out->cu_N[r + 1] = out->cu_N[r] + b->n_ctx[r];
+    out->cu_U[r + 1] = out->cu_U[r] + (T - b->n_ctx[r]);
+  }
+  return KVF_OK;
+}
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+}  // namespace
+
+#define KVF_GUARD_BEGIN try {
+#define KVF_GUARD_END                                                   \
+  }                                                                     \
+  catch (const std::exception& e) {                                     \
+    return fail(KVF_ERR_INVALID_ARG, "internal error: %s", e.what());   \
+  }                                                                     \
+  catch (...) {                                                         \
+    return fail(KVF_ERR_INVALID_ARG, "internal error");                 \
+  }
+
+extern "C" {
+
+int32_t kvf_abi_version(void) { return KVF_ABI_VERSION; }
+
+const char* kvf_status_string(kvf_status s) {
+  switch (s) {
+    case KVF_OK: return "KVF_OK";
+    case KVF_ERR_INVALID_ARG: return "KVF_ERR_INVALID_ARG";
+    case KVF_ERR_UNSUPPORTED: return "KVF_ERR_UNSUPPORTED";
+    case KVF_ERR_WORKSPACE: return "KVF_ERR_WORKSPACE";
+    case KVF_ERR_HIP: return "KVF_ERR_HIP";
+  }
+  return "KVF_UNKNOWN_STATUS";
+}
+
+const char* kvf_last_error(void) { return g_err; }
+
+int32_t kvf_recompute_budget(int32_t n_ctx, int32_t ratio_pct) {
+  if (n_ctx < 0 || ratio_pct < 0 || ratio_pct > 100) return -1;
+  return static_cast<int32_t>((static_cast<int64_t>(n_ctx) * ratio_pct) / 100);
+}
+
+kvf_status kvf_rope_table(double base, int32_t head_dim, int32_t n_pos, float* cos_tab,
+                          float* sin_tab, void* stream) {
+  KVF_GUARD_BEGIN
+  KVF_CHECK(base > 1.0, KVF_ERR_INVALID_ARG, "rope base must exceed 1");
+  KVF_CHECK(head_dim > 0 && head_dim % 2 == 0 && head_dim <= 1024, KVF_ERR_INVALID_ARG,
+            "head_dim %d must be even and at most 1024", head_dim);
+  KVF_CHECK(n_pos >= 0, KVF_ERR_INVALID_ARG, "n_pos negative");
+  if (n_pos == 0) return KVF_OK;
+  KVF_CHECK(cos_tab && sin_tab, KVF_ERR_INVALID_ARG, "table pointers are NULL");
+  return from_hip(kvf::launch_rope_table(base, head_dim, n_pos, cos_tab, sin_tab,
+                                         as_stream(stream)), "kvf_rope_table");
+  KVF_GUARD_END
+}
+
+kvf_status kvf_rerotate(const kvf_layer_desc* layer, const kvf_chunk* chunks, int32_t n_chunks,
+                        int32_t max_chunk_len, const void* pool_k, const void* pool_v,
+                        const kvf_kivi8* kivi, int64_t pool_rows, const float* rope_cos,
+                        const float* rope_sin, int32_t rope_n_pos, void* fused_k, void* fused_v,
+                        int64_t fused_rows, void* stream) {
+  KVF_GUARD_BEGIN
+  kvf_status st = check_layer(layer);
+  if (st != KVF_OK) return st;
+  KVF_CHECK(n_chunks >= 0 && max_chunk_len >= 0 && pool_rows >= 0 && fused_rows >= 0 &&
+                rope_n_pos >= 0, KVF_ERR_INVALID_ARG, "negative size");
+  if (n_chunks == 0 || max_chunk_len == 0) return KVF_OK;
+  KVF_CHECK(chunks && rope_cos && rope_sin && fused_k && fused_v, KVF_ERR_INVALID_ARG,
+            "required pointer is NULL");
+  if (kivi) {
+    KVF_CHECK(layer->dtype == KVF_BF16, KVF_ERR_UNSUPPORTED, "int8 caches decode to bf16 only");
+    KVF_CHECK(pool_k == nullptr && pool_v == nullptr, KVF_ERR_INVALID_ARG,
+              "pass either dense pool pointers or kivi, not both");
+    KVF_CHECK(kivi->k_codes && kivi->v_codes && kivi->k_min && kivi->k_scale && kivi->v_min &&
+                  kivi->v_scale && kivi->n_pool_chunks > 0, KVF_ERR_INVALID_ARG,
+              "incomplete kvf_kivi8");
+  } else {
+    KVF_CHECK(pool_k && pool_v, KVF_ERR_INVALID_ARG, "pool pointers are NULL");
+  }
+  KVF_CHECK(max_chunk_len <= (1 << 24), KVF_ERR_UNSUPPORTED, "max_chunk_len too large");
+  return from_hip(kvf::launch_rerotate(*layer, chunks, n_chunks, max_chunk_len, pool_k, pool_v,
+                                       kivi, pool_rows, rope_cos, rope_sin, rope_n_pos, fused_k,
+                                       fused_v, fused_rows, as_stream(stream)),
+                  "kvf_rerotate");
+  KVF_GUARD_END
+}
+
+kvf_status kvf_kivi8_encode(const kvf_layer_desc* layer, const void* pool_k, const void* pool_v,
+                            const int32_t* pool_cu, int32_t n_pool_chunks, int64_t pool_rows,
+                            int32_t max_chunk_len, const kvf_kivi8* out, void* stream) {
+  KVF_GUARD_BEGIN
+  kvf_status st = check_layer(layer);
+  if (st != KVF_OK) return st;
+  KVF_CHECK(layer->dtype == KVF_BF16, KVF_ERR_UNSUPPORTED, "the int8 encoder reads bf16 caches");
+  KVF_CHECK(n_pool_chunks >= 0 && pool_rows >= 0 && max_chunk_len >= 0, KVF_ERR_INVALID_ARG,
+            "negative size");
+  if (n_pool_chunks == 0 || pool_rows == 0) return KVF_OK;
+  KVF_CHECK(pool_k && pool_v && pool_cu && out, KVF_ERR_INVALID_ARG, "required pointer is NULL");
+  KVF_CHECK(out->k_codes && out->v_codes && out->k_min && out->k_scale && out->v_min &&
+                out->v_scale, KVF_ERR_INVALID_ARG, "incomplete output kvf_kivi8");
+  KVF_CHECK(out->n_pool_chunks >= n_pool_chunks, KVF_ERR_INVALID_ARG,
+            "output statistics hold %d chunks, need %d", out->n_pool_chunks, n_pool_chunks);
+  return from_hip(kvf::launch_kivi8_encode(*layer, pool_k, pool_v, pool_cu, n_pool_chunks,
+                                           pool_rows, max_chunk_len, *out, as_stream(stream)),
+                  "kvf_kivi8_encode");
+  KVF_GUARD_END
+}
+
+size_t kvf_score_workspace_size(kvf_score_mode mode, const kvf_layer_desc* layer,
+                                const kvf_batch* batch, int32_t n_last_q) {
+  try {
+    if (mode != KVF_SCORE_ATTN_MASS) return 0;
+    kvf::BatchArgs B;
+    if (check_layer(layer) != KVF_OK || check_batch(batch, &B) != KVF_OK) return 0;
+    return kvf::attn_mass_workspace(*layer, B, n_last_q);
+  } catch (...) {
+    return 0;
+  }
+}
+
+kvf_status kvf_score(kvf_score_mode mode, const kvf_layer_desc* layer, const kvf_batch* batch,
+                     const void* fused_k, const void* k_fresh, const void* q_u, int32_t n_last_q,
+                     float* scores, void* workspace, size_t ws_bytes, void* stream) {
+  KVF_GUARD_BEGIN
+  kvf_status st = check_layer(layer);
+  if (st != KVF_OK) return st;
+  kvf::BatchArgs B;
+  st = check_batch(batch, &B);
+  if (st != KVF_OK) return st;
+  if (B.cu_N[B.n_req] == 0) return KVF_OK;
+  KVF_CHECK(fused_k && scores, KVF_ERR_INVALID_ARG, "required pointer is NULL");
+  if (mode == KVF_SCORE_DEVIATION) {
+    KVF_CHECK(k_fresh != nullptr, KVF_ERR_INVALID_ARG, "k_fresh is NULL");
+    return from_hip(kvf::launch_deviation(*layer, B, fused_k, k_fresh, scores,
+                                          as_stream(stream)), "kvf_score(deviation)");
+  }
+  KVF_CHECK(mode == KVF_SCORE_ATTN_MASS, KVF_ERR_INVALID_ARG, "unknown score mode %d", mode);
+  KVF_CHECK(q_u != nullptr, KVF_ERR_INVALID_ARG, "q_u is NULL");
+  const size_t need = kvf::attn_mass_workspace(*layer, B, n_last_q);
+  KVF_CHECK(ws_bytes >= need, KVF_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);
+  KVF_CHECK(need == 0 || workspace != nullptr, KVF_ERR_WORKSPACE, "workspace is NULL");
+  return from_hip(kvf::launch_attn_mass(*layer, B, fused_k, q_u, n_last_q, scores, workspace,
+                                        ws_bytes, as_stream(stream)), "kvf_score(attn_mass)");
+  KVF_GUARD_END
+}
+
+size_t kvf_select_workspace_size(const kvf_batch* batch) {
+  (void)batch;
+  return 0;
+}
+
+kvf_status kvf_select_topk(const float* scores, const kvf_batch* batch, const int32_t* k_per_req,
+                           int32_t* out_idx, int32_t* out_rows, int32_t* out_pos,
+                           void* workspace, size_t ws_bytes, void* stream) {
+  KVF_GUARD_BEGIN
+  (void)workspace;
+  (void)ws_bytes;
+  kvf::BatchArgs B;
+  kvf_status st = check_batch(batch, &B);
+  if (st != KVF_OK) return st;
+  KVF_CHECK(k_per_req != nullptr, KVF_ERR_INVALID_ARG, "k_per_req is NULL");
+  int64_t total_k = 0, total_m = 0;
+  for (int r = 0; r < B.n_req; ++r) {
+    KVF_CHECK(k_per_req[r] >= 0 && k_per_req[r] <= B.n_ctx[r], KVF_ERR_INVALID_ARG,
+              "k_per_req[%d] = %d outside [0, %d]", r, k_per_req[r], B.n_ctx[r]);
+    total_k += k_per_req[r];
+    total_m += k_per_req[r] + (B.cu_T[r + 1] - B.cu_T[r] - B.n_ctx[r]);
+  }
+  if (total_m == 0) return KVF_OK;
+  KVF_CHECK(total_k == 0 || (scores && out_idx), KVF_ERR_INVALID_ARG, "required pointer is NULL");
+  KVF_CHECK((out_rows == nullptr) == (out_pos == nullptr), KVF_ERR_INVALID_ARG,
+            "out_rows and out_pos must both be given or both be NULL");
+  return from_hip(kvf::launch_topk(scores, B, k_per_req, out_idx, out_rows, out_pos,
+                                   as_stream(stream)), "kvf_select_topk");
+  KVF_GUARD_END
+}
+
+kvf_status kvf_recompute_qkv(const kvf_layer_desc* layer, const void* x, int64_t x_rows,
+                             const int32_t* row_src, const int32_t* row_pos, int32_t M,
+                             const void* w_qkv, uint32_t out_mask, const float* rope_cos,
+                             const float* rope_sin, int32_t rope_n_pos, void* q_out,
+                             void* k_out, void* v_out, void* stream) {
+  KVF_GUARD_BEGIN
+  kvf_status st = check_layer(layer);
+  if (st != KVF_OK) return st;
+  KVF_CHECK(M >= 0 && x_rows >= 0 && rope_n_pos >= 0, KVF_ERR_INVALID_ARG, "negative size");
+  KVF_CHECK((out_mask & ~7u) == 0, KVF_ERR_INVALID_ARG, "unknown bits in out_mask");
+  if (M == 0 || out_mask == 0) return KVF_OK;
+  KVF_CHECK(x && w_qkv && row_pos, KVF_ERR_INVALID_ARG, "required pointer is NULL");
+  KVF_CHECK(row_src != nullptr || M <= x_rows, KVF_ERR_INVALID_ARG,
+            "identity row map needs M <= x_rows");
+  KVF_CHECK(!(out_mask & KVF_OUT_Q) || q_out, KVF_ERR_INVALID_ARG, "q_out is NULL");
+  KVF_CHECK(!(out_mask & KVF_OUT_K) || k_out, KVF_ERR_INVALID_ARG, "k_out is NULL");
+  KVF_CHECK(!(out_mask & KVF_OUT_V) || v_out, KVF_ERR_INVALID_ARG, "v_out is NULL");
+  KVF_CHECK(!(out_mask & (KVF_OUT_Q | KVF_OUT_K)) || (rope_cos && rope_sin && rope_n_pos > 0),
+            KVF_ERR_INVALID_ARG, "rope tables needed for Q/K");
+  KVF_CHECK(layer->dtype != KVF_BF16 ||
+                ((layer->n_q_heads * layer->head_dim) % 128 == 0 &&
+                 (layer->n_kv_heads * layer->head_dim) % 128 == 0),
+            KVF_ERR_UNSUPPORTED, "bf16 projection needs Hq*d and Hkv*d multiples of 128");
+  return from_hip(kvf::launch_recompute(*layer, x, x_rows, row_src, row_pos, M, w_qkv, out_mask,
+                                        rope_cos, rope_sin, rope_n_pos, q_out, k_out, v_out,
+                                        as_stream(stream)), "kvf_recompute_qkv");
+  KVF_GUARD_END
+}
+
+kvf_status kvf_scatter_kv(const kvf_layer_desc* layer, const void* k_src,
+                          const int32_t* k_src_row, int64_t k_src_rows, const void* v_src,
+                          const int32_t* v_src_row, int64_t v_src_rows, const int32_t* dst_row,
+                          int32_t M, void* fused_k, void* fused_v, int64_t fused_rows,
+                          void* stream) {
+  KVF_GUARD_BEGIN
+  kvf_status st = check_layer(layer);
+  if (st != KVF_OK) return st;
+  KVF_CHECK(M >= 0 && k_src_rows >= 0 && v_src_rows >= 0 && fused_rows >= 0,
+            KVF_ERR_INVALID_ARG, "negative size");
+  if (M == 0 || (k_src == nullptr && v_src == nullptr)) return KVF_OK;
+  KVF_CHECK(dst_row != nullptr, KVF_ERR_INVALID_ARG, "dst_row is NULL");
+  KVF_CHECK(!k_src || fused_k, KVF_ERR_INVALID_ARG, "fused_k is NULL");
+  KVF_CHECK(!v_src || fused_v, KVF_ERR_INVALID_ARG, "fused_v is NULL");
+  KVF_CHECK(!k_src || k_src_row || M <= k_src_rows, KVF_ERR_INVALID_ARG,
+            "identity k source map needs M <= k_src_rows");
+  KVF_CHECK(!v_src || v_src_row || M <= v_src_rows, KVF_ERR_INVALID_ARG,
+            "identity v source map needs M <= v_src_rows");
+  return from_hip(kvf::launch_scatter(*layer, k_src, k_src_row, k_src_rows, v_src, v_src_row,
+                                      v_src_rows, dst_row, M, fused_k, fused_v, fused_rows,
+                                      as_stream(stream)), "kvf_scatter_kv");
+  KVF_GUARD_END
+}
+
+kvf_status kvf_sparse_q_attention(const kvf_layer_desc* layer, const kvf_batch* batch,
+                                  const void* q, const int32_t* q_pos, const int32_t* cu_q,
+                                  const void* fused_k, const void* fused_v, float sm_scale,
+                                  void* out, float* lse, void* stream) {
+  KVF_GUARD_BEGIN
+  kvf_status st = check_layer(layer);
+  if (st != KVF_OK) return st;
+  kvf::BatchArgs B;
+  st = check_batch(batch, &B);
+  if (st != KVF_OK) return st;
+  KVF_CHECK(cu_q != nullptr, KVF_ERR_INVALID_ARG, "cu_q is NULL");
+  KVF_CHECK(cu_q[0] == 0, KVF_ERR_INVALID_ARG, "cu_q[0] must be 0");
+  for (int r = 0; r < B.n_req; ++r)
+    KVF_CHECK(cu_q[r + 1] >= cu_q[r], KVF_ERR_INVALID_ARG, "cu_q decreases at %d", r);
+  KVF_CHECK(sm_scale > 0.f && sm_scale < 1e30f, KVF_ERR_INVALID_ARG, "bad sm_scale");
+  if (cu_q[B.n_req] == 0) return KVF_OK;
+  KVF_CHECK(q && q_pos && fused_k && fused_v && out, KVF_ERR_INVALID_ARG,
+            "required pointer is NULL");
+  return from_hip(kvf::launch_attention(*layer, B, q, q_pos, cu_q, fused_k, fused_v, sm_scale,
+                                        out, lse, as_stream(stream)), "kvf_sparse_q_attention");
+  KVF_GUARD_END
+}
+
+}  // extern "C"

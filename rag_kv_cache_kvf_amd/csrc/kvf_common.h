@@ -1,0 +1,160 @@
+// Shared device/host definitions of libkvfuse (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "kvfuse.h"
+
+namespace kvf {
+
+constexpr int kWave = 64;
+constexpr int kXcds = 8;          // MI355X: 8 accelerator complex dies, one L2 each
+
+using bf16_t = uint16_t;          // storage form of bf16 values
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
+typedef uint16_t u16x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------------------
+// scalar conversions
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_to_f32(bf16_t v) {
+  return __uint_as_float(static_cast<uint32_t>(v) << 16);
+}
+// Round to nearest even (the hardware conversion on gfx950).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  return __builtin_bit_cast(bf16_t, static_cast<__bf16>(f));
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2_t v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// ---------------------------------------------------------------------------
+// element traits: 8-wide loads/stores in fp32 registers
+// ---------------------------------------------------------------------------
+template <typename T> struct Elem;
+
+template <> struct Elem<float> {
+  static constexpr kvf_dtype kDtype = KVF_F32;
+  __device__ __forceinline__ static void load8(const float* p, float (&v)[8]) {
+    const float4 a = *reinterpret_cast<const float4*>(p);
+    const float4 b = *reinterpret_cast<const float4*>(p + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+  __device__ __forceinline__ static void store8(float* p, const float (&v)[8]) {
+    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+    *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+  }
+  __device__ __forceinline__ static float load1(const float* p) { return *p; }
+  __device__ __forceinline__ static void store1(float* p, float v) { *p = v; }
+};
+
+template <> struct Elem<bf16_t> {
+  static constexpr kvf_dtype kDtype = KVF_BF16;
+  __device__ __forceinline__ static void load8(const bf16_t* p, float (&v)[8]) {
+    const u32x4_t a = *reinterpret_cast<const u32x4_t*>(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(a[i] << 16);
+      v[2 * i + 1] = __uint_as_float(a[i] & 0xffff0000u);
+    }
+  }
+  __device__ __forceinline__ static void store8(bf16_t* p, const float (&v)[8]) {
+    u32x4_t a;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
+    *reinterpret_cast<u32x4_t*>(p) = a;
+  }
+  __device__ __forceinline__ static float load1(const bf16_t* p) { return bf16_to_f32(*p); }
+  __device__ __forceinline__ static void store1(bf16_t* p, float v) { *p = f32_to_bf16(v); }
+};
+
+// ---------------------------------------------------------------------------
+// wave reductions (wave64)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+// sum over aligned groups of `width` lanes (width a power of two <= 64)
+__device__ __forceinline__ float group_sum(float v, int width) {
+  for (int o = width >> 1; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// batch metadata passed by value in kernel arguments
+// ---------------------------------------------------------------------------
+struct BatchArgs {
+  int n_req;
+  int cu_T[KVF_MAX_REQ + 1];   // row offsets of each request (x, fused cache)
+  int n_ctx[KVF_MAX_REQ];      // context tokens N_r
+  int cu_N[KVF_MAX_REQ + 1];   // offsets of each request's scores
+  int cu_U[KVF_MAX_REQ + 1];   // offsets of each request's query rows (q_u)
+};
+
+// index of the request whose [cu[r], cu[r+1]) holds i (cu non-decreasing)
+__device__ __forceinline__ int find_segment(const int* cu, int n, int i) {
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cu[mid] <= i) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+__host__ __device__ constexpr int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+}  // namespace kvf
+
+// ---------------------------------------------------------------------------
+// host-side launchers implemented in the kernel files
+// ---------------------------------------------------------------------------
+namespace kvf {
+hipError_t launch_rope_table(double base, int d, int n_pos, float* c, float* s, hipStream_t st);
+hipError_t launch_rerotate(const kvf_layer_desc& L, const kvf_chunk* chunks, int n_chunks,
+                           int max_len, const void* pk, const void* pv, const kvf_kivi8* q,
+                           int64_t pool_rows, const float* rc, const float* rs, int rope_n,
+                           void* fk, void* fv, int64_t fused_rows, hipStream_t st);
+hipError_t launch_kivi8_encode(const kvf_layer_desc& L, const void* pk, const void* pv,
+                               const int32_t* pool_cu, int n_pool, int64_t pool_rows,
+                               int max_len, const kvf_kivi8& out, hipStream_t st);
+hipError_t launch_deviation(const kvf_layer_desc& L, const BatchArgs& B, const void* fk,
+                            const void* kf, float* scores, hipStream_t st);
+hipError_t launch_attn_mass(const kvf_layer_desc& L, const BatchArgs& B, const void* fk,
+                            const void* q_u, int n_last_q, float* scores, void* ws,
+                            size_t ws_bytes, hipStream_t st);
+size_t attn_mass_workspace(const kvf_layer_desc& L, const BatchArgs& B, int n_last_q);
+hipError_t launch_topk(const float* scores, const BatchArgs& B, const int32_t* k_host,
+                       int32_t* out_idx, int32_t* out_rows, int32_t* out_pos, hipStream_t st);
+hipError_t launch_recompute(const kvf_layer_desc& L, const void* x, int64_t x_rows,
+                            const int32_t* row_src, const int32_t* row_pos, int M,
+                            const void* w, uint32_t mask, const float* rc, const float* rs,
+                            int rope_n, void* q, void* k, void* v, hipStream_t st);
+hipError_t launch_scatter(const kvf_layer_desc& L, const void* ks, const int32_t* ksr,
+                          int64_t ks_rows, const void* vs, const int32_t* vsr, int64_t vs_rows,
+                          const int32_t* dst, int M, void* fk, void* fv, int64_t fused_rows,
+                          hipStream_t st);
+hipError_t launch_attention(const kvf_layer_desc& L, const BatchArgs& B, const void* q,
+                            const int32_t* q_pos, const int32_t* cu_q_host, const void* fk,
+                            const void* fv, float sm_scale, void* out, float* lse,
+                            hipStream_t st);
+}  // namespace kvf

@@ -1,0 +1,277 @@
+"""ctypes binding of libkvfuse (include/kvfuse.h).
+
+Argument marshalling only: every function takes torch tensors that already
+live on the GPU, passes their device pointers and the current HIP stream to
+the C entry point of the same name, and raises KvfError on a non-OK status.
+Nothing here computes; the library must be built (`__graft_entry__.build()`)
+or importing this module fails.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Optional, Sequence
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvfuse.so")
+
+KVF_OK, KVF_ERR_INVALID_ARG, KVF_ERR_UNSUPPORTED, KVF_ERR_WORKSPACE, KVF_ERR_HIP = range(5)
+KVF_F32, KVF_BF16 = 0, 1
+KVF_SCORE_DEVIATION, KVF_SCORE_ATTN_MASS = 0, 1
+KVF_OUT_Q, KVF_OUT_K, KVF_OUT_V = 1, 2, 4
+KVF_MAX_REQ = 64
+
+
+class KvfError(RuntimeError):
+    def __init__(self, status: int, func: str, msg: str):
+        super().__init__(f"{func}: {status_name(status)}: {msg}")
+        self.status = status
+
+
+def load_library(path: str = _LIB_PATH) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise ImportError(f"libkvfuse is not built ({path} missing); run __graft_entry__.build()")
+    return ctypes.CDLL(path)
+
+
+_lib = load_library()
+
+
+# ----------------------------------------------------------------------------
+# C structs
+# ----------------------------------------------------------------------------
+class LayerDesc(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("dtype", ctypes.c_int32)]
+
+
+class BatchDesc(ctypes.Structure):
+    _fields_ = [("n_req", ctypes.c_int32), ("cu_T", ctypes.POINTER(ctypes.c_int32)),
+                ("n_ctx", ctypes.POINTER(ctypes.c_int32))]
+
+
+class Kivi8Desc(ctypes.Structure):
+    _fields_ = [("k_codes", ctypes.c_void_p), ("v_codes", ctypes.c_void_p),
+                ("k_min", ctypes.c_void_p), ("k_scale", ctypes.c_void_p),
+                ("v_min", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
+                ("n_pool_chunks", ctypes.c_int32)]
+
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_SZ = ctypes.c_size_t
+_LP = ctypes.POINTER(LayerDesc)
+_BP = ctypes.POINTER(BatchDesc)
+_IP = ctypes.POINTER(ctypes.c_int32)
+
+_SIGS = {
+    "kvf_rope_table": (_I32, [ctypes.c_double, _I32, _I32, _P, _P, _P]),
+    "kvf_rerotate": (_I32, [_LP, _P, _I32, _I32, _P, _P, ctypes.POINTER(Kivi8Desc), _I64, _P, _P,
+                            _I32, _P, _P, _I64, _P]),
+    "kvf_score": (_I32, [_I32, _LP, _BP, _P, _P, _P, _I32, _P, _P, _SZ, _P]),
+    "kvf_score_workspace_size": (_SZ, [_I32, _LP, _BP, _I32]),
+    "kvf_select_topk": (_I32, [_P, _BP, _IP, _P, _P, _P, _P, _SZ, _P]),
+    "kvf_select_workspace_size": (_SZ, [_BP]),
+    "kvf_recompute_qkv": (_I32, [_LP, _P, _I64, _P, _P, _I32, _P, ctypes.c_uint32, _P, _P, _I32,
+                                 _P, _P, _P, _P]),
+    "kvf_scatter_kv": (_I32, [_LP, _P, _P, _I64, _P, _P, _I64, _P, _I32, _P, _P, _I64, _P]),
+    "kvf_sparse_q_attention": (_I32, [_LP, _BP, _P, _P, _IP, _P, _P, ctypes.c_float, _P, _P, _P]),
+    "kvf_kivi8_encode": (_I32, [_LP, _P, _P, _P, _I32, _I64, _I32, ctypes.POINTER(Kivi8Desc), _P]),
+    "kvf_recompute_budget": (_I32, [_I32, _I32]),
+    "kvf_status_string": (ctypes.c_char_p, [_I32]),
+    "kvf_last_error": (ctypes.c_char_p, []),
+    "kvf_abi_version": (_I32, []),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _f = getattr(_lib, _name)
+    _f.restype = _res
+    _f.argtypes = _args
+
+
+def status_name(status: int) -> str:
+    return _lib.kvf_status_string(status).decode()
+
+
+def last_error() -> str:
+    return _lib.kvf_last_error().decode()
+
+
+def abi_version() -> int:
+    return _lib.kvf_abi_version()
+
+
+def recompute_budget(n_ctx: int, ratio_pct: int) -> int:
+    return _lib.kvf_recompute_budget(n_ctx, ratio_pct)
+
+
+def _check(status: int, func: str):
+    if status != KVF_OK:
+        raise KvfError(status, func, last_error())
+
+
+# ----------------------------------------------------------------------------
+# marshalling helpers
+# ----------------------------------------------------------------------------
+@dataclasses.dataclass(frozen=True)
+class Layer:
+    hidden: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    dtype: str          # "f32" | "bf16"
+
+    def desc(self) -> LayerDesc:
+        return LayerDesc(self.hidden, self.n_q_heads, self.n_kv_heads, self.head_dim,
+                         KVF_BF16 if self.dtype == "bf16" else KVF_F32)
+
+    @property
+    def torch_dtype(self):
+        return torch.bfloat16 if self.dtype == "bf16" else torch.float32
+
+
+class Batch:
+    """Host-side request layout (cu_T, n_ctx) held as ctypes arrays."""
+
+    def __init__(self, cu_T: Sequence[int], n_ctx: Sequence[int]):
+        self.cu_T_list = [int(v) for v in cu_T]
+        self.n_ctx_list = [int(v) for v in n_ctx]
+        n = len(self.n_ctx_list)
+        self._cu = (ctypes.c_int32 * (n + 1))(*self.cu_T_list)
+        self._nc = (ctypes.c_int32 * max(n, 1))(*self.n_ctx_list)
+        self.desc = BatchDesc(n, ctypes.cast(self._cu, _IP), ctypes.cast(self._nc, _IP))
+
+    @property
+    def n_req(self) -> int:
+        return len(self.n_ctx_list)
+
+    def n_query(self, r: int) -> int:
+        return self.cu_T_list[r + 1] - self.cu_T_list[r] - self.n_ctx_list[r]
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream=None) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _int_array(vals: Sequence[int]):
+    return (ctypes.c_int32 * max(len(vals), 1))(*[int(v) for v in vals])
+
+
+def _rows(t: Optional[torch.Tensor]) -> int:
+    return 0 if t is None else int(t.shape[0])
+
+
+# ----------------------------------------------------------------------------
+# entry points
+# ----------------------------------------------------------------------------
+def rope_table(base: float, head_dim: int, n_pos: int, cos_out: torch.Tensor,
+               sin_out: torch.Tensor, stream=None):
+    _check(_lib.kvf_rope_table(float(base), head_dim, n_pos, _ptr(cos_out), _ptr(sin_out),
+                               _stream(stream)), "kvf_rope_table")
+
+
+def rerotate(layer: Layer, chunks: torch.Tensor, max_chunk_len: int,
+             pool_k: Optional[torch.Tensor], pool_v: Optional[torch.Tensor],
+             rope_cos: torch.Tensor, rope_sin: torch.Tensor, fused_k: torch.Tensor,
+             fused_v: torch.Tensor, kivi: Optional[dict] = None, stream=None):
+    """chunks: int32 [n_chunks, 8] device tensor (kvf_chunk rows)."""
+    kd = None
+    pool_rows = _rows(pool_k)
+    if kivi is not None:
+        kd = ctypes.byref(Kivi8Desc(_ptr(kivi["k_codes"]), _ptr(kivi["v_codes"]),
+                                    _ptr(kivi["k_min"]), _ptr(kivi["k_scale"]),
+                                    _ptr(kivi["v_min"]), _ptr(kivi["v_scale"]),
+                                    int(kivi["k_min"].shape[0])))
+        pool_rows = int(kivi["k_codes"].shape[0])
+    d = layer.desc()
+    _check(_lib.kvf_rerotate(ctypes.byref(d), _ptr(chunks), int(chunks.shape[0]), max_chunk_len,
+                             _ptr(pool_k), _ptr(pool_v), kd, pool_rows, _ptr(rope_cos),
+                             _ptr(rope_sin), int(rope_cos.shape[0]), _ptr(fused_k), _ptr(fused_v),
+                             _rows(fused_k), _stream(stream)), "kvf_rerotate")
+
+
+def score_workspace_size(mode: int, layer: Layer, batch: Batch, n_last_q: int = 0) -> int:
+    d = layer.desc()
+    return int(_lib.kvf_score_workspace_size(mode, ctypes.byref(d), ctypes.byref(batch.desc), n_last_q))
+
+
+def score(mode: int, layer: Layer, batch: Batch, fused_k: torch.Tensor,
+          k_fresh: Optional[torch.Tensor], q_u: Optional[torch.Tensor], scores: torch.Tensor,
+          workspace: Optional[torch.Tensor] = None, n_last_q: int = 0, stream=None):
+    d = layer.desc()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.kvf_score(mode, ctypes.byref(d), ctypes.byref(batch.desc), _ptr(fused_k),
+                          _ptr(k_fresh), _ptr(q_u), n_last_q, _ptr(scores), _ptr(workspace),
+                          ws_bytes, _stream(stream)), "kvf_score")
+
+
+def select_topk(scores: torch.Tensor, batch: Batch, k_per_req: Sequence[int],
+                out_idx: torch.Tensor, out_rows: Optional[torch.Tensor] = None,
+                out_pos: Optional[torch.Tensor] = None, stream=None):
+    ka = _int_array(k_per_req)
+    _check(_lib.kvf_select_topk(_ptr(scores), ctypes.byref(batch.desc), ka, _ptr(out_idx),
+                                _ptr(out_rows), _ptr(out_pos), None, 0, _stream(stream)),
+           "kvf_select_topk")
+
+
+def recompute_qkv(layer: Layer, x: torch.Tensor, row_src: Optional[torch.Tensor],
+                  row_pos: torch.Tensor, w_qkv: torch.Tensor, out_mask: int,
+                  rope_cos: torch.Tensor, rope_sin: torch.Tensor,
+                  q_out: Optional[torch.Tensor] = None, k_out: Optional[torch.Tensor] = None,
+                  v_out: Optional[torch.Tensor] = None, M: Optional[int] = None, stream=None):
+    d = layer.desc()
+    M = int(row_pos.shape[0]) if M is None else M
+    _check(_lib.kvf_recompute_qkv(ctypes.byref(d), _ptr(x), _rows(x), _ptr(row_src), _ptr(row_pos),
+                                  M, _ptr(w_qkv), out_mask, _ptr(rope_cos), _ptr(rope_sin),
+                                  _rows(rope_cos), _ptr(q_out), _ptr(k_out), _ptr(v_out),
+                                  _stream(stream)), "kvf_recompute_qkv")
+
+
+def scatter_kv(layer: Layer, k_src: Optional[torch.Tensor], k_src_row: Optional[torch.Tensor],
+               v_src: Optional[torch.Tensor], v_src_row: Optional[torch.Tensor],
+               dst_row: torch.Tensor, fused_k: torch.Tensor, fused_v: torch.Tensor,
+               M: Optional[int] = None, stream=None):
+    d = layer.desc()
+    M = int(dst_row.shape[0]) if M is None else M
+    _check(_lib.kvf_scatter_kv(ctypes.byref(d), _ptr(k_src), _ptr(k_src_row), _rows(k_src),
+                               _ptr(v_src), _ptr(v_src_row), _rows(v_src), _ptr(dst_row), M,
+                               _ptr(fused_k), _ptr(fused_v), _rows(fused_k), _stream(stream)),
+           "kvf_scatter_kv")
+
+
+def sparse_q_attention(layer: Layer, batch: Batch, q: torch.Tensor, q_pos: torch.Tensor,
+                       cu_q: Sequence[int], fused_k: torch.Tensor, fused_v: torch.Tensor,
+                       sm_scale: float, out: torch.Tensor, lse: Optional[torch.Tensor] = None,
+                       stream=None):
+    d = layer.desc()
+    cq = _int_array(cu_q)
+    _check(_lib.kvf_sparse_q_attention(ctypes.byref(d), ctypes.byref(batch.desc), _ptr(q),
+                                       _ptr(q_pos), cq, _ptr(fused_k), _ptr(fused_v),
+                                       float(sm_scale), _ptr(out), _ptr(lse), _stream(stream)),
+           "kvf_sparse_q_attention")
+
+
+def kivi8_encode(layer: Layer, pool_k: torch.Tensor, pool_v: torch.Tensor, pool_cu: torch.Tensor,
+                 max_chunk_len: int, out: dict, stream=None):
+    d = layer.desc()
+    n_pool = int(pool_cu.shape[0]) - 1
+    od = Kivi8Desc(_ptr(out["k_codes"]), _ptr(out["v_codes"]), _ptr(out["k_min"]),
+                   _ptr(out["k_scale"]), _ptr(out["v_min"]), _ptr(out["v_scale"]),
+                   int(out["k_min"].shape[0]))
+    _check(_lib.kvf_kivi8_encode(ctypes.byref(d), _ptr(pool_k), _ptr(pool_v), _ptr(pool_cu),
+                                 n_pool, _rows(pool_k), max_chunk_len, ctypes.byref(od),
+                                 _stream(stream)), "kvf_kivi8_encode")

@@ -1,0 +1,219 @@
+"""One fused layer on the GPU: buffers plus the ordered libkvfuse calls.
+
+This module sequences the six library calls of the hot path for one batch of
+requests and owns the device buffers between them; it computes nothing
+itself.  Order (all on one stream, no host synchronisation):
+
+  deviation mode (KVBoost page, section 4.6.2, Algorithm 2 at one layer)
+    kvf_rerotate -> kvf_recompute_qkv(all rows, K: probe K~) ->
+    kvf_score(DEVIATION) -> kvf_select_topk -> kvf_recompute_qkv(P+U, Q|V) ->
+    kvf_scatter_kv(K from the probe, V new) -> kvf_sparse_q_attention
+  attention-mass mode (QCFuse page, section 3.2.1 at one layer)
+    kvf_rerotate -> kvf_recompute_qkv(U, Q|K|V) -> kvf_scatter_kv(U) ->
+    kvf_score(ATTN_MASS) -> kvf_select_topk -> kvf_recompute_qkv(P+U, Q|K|V)
+    -> kvf_scatter_kv(P+U) -> kvf_sparse_q_attention
+
+The per-chunk caches are built ahead of serving (QCFuse page, section 2.1.2,
+Eq. 3) either by the caller (`pic=`) or on the GPU by this library's own
+projection at chunk-local positions (and its int8 encoder for int8 caches).
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+from . import kvfuse as kvf
+from .synth import Batch as SynthBatch
+
+
+def _dev(a: np.ndarray, dtype: str, device) -> torch.Tensor:
+    """Upload a storage-encoded numpy array (float32 or bf16 bits)."""
+    if dtype == "bf16" and a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16).copy()).to(device).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+def _i32(a, device) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(np.asarray(a, dtype=np.int32))).to(device)
+
+
+class FusedLayerGPU:
+    def __init__(self, batch: SynthBatch, ratio_pct: int, device="cuda",
+                 pic: Optional[dict] = None, n_last_q: int = 0, mode: Optional[str] = None):
+        wl = batch.wl
+        self.wl = wl
+        self.batch = batch
+        self.mode = mode or wl.score
+        self.n_last_q = n_last_q
+        self.device = torch.device(device)
+        dev = self.device
+        L = kvf.Layer(wl.hidden, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.dtype)
+        self.layer = L
+        self.kb = kvf.Batch(batch.cu_T, batch.n_ctx)
+        td = L.torch_dtype
+        hq, hkv, d = wl.n_q_heads, wl.n_kv_heads, wl.head_dim
+        R = batch.n_req
+        T_total = batch.total_rows
+
+        self.x = _dev(batch.x, wl.dtype, dev)
+        self.w = _dev(batch.w_qkv, wl.dtype, dev)
+        self.chunks = _i32(batch.chunk_table, dev)
+        self.max_chunk_len = int(batch.chunk_table[:, 3].max())
+        max_T = int(np.diff(batch.cu_T).max())
+        self.rope_n = max(max_T, self.max_chunk_len)
+        self.rope_cos = torch.empty((self.rope_n, d // 2), dtype=torch.float32, device=dev)
+        self.rope_sin = torch.empty_like(self.rope_cos)
+        kvf.rope_table(wl.rope_base, d, self.rope_n, self.rope_cos, self.rope_sin)
+
+        # per-chunk caches (ahead of serving)
+        self.pool_k = self.pool_v = None
+        self.kivi = None
+        pool_rows = batch.pool_rows
+        if pic is not None:
+            if "k_codes" in pic:
+                self.kivi = {k: torch.from_numpy(np.ascontiguousarray(v)).to(dev)
+                             for k, v in pic.items()}
+            else:
+                self.pool_k = _dev(pic["k"], wl.dtype, dev)
+                self.pool_v = _dev(pic["v"], wl.dtype, dev)
+        else:
+            pool_hidden = _dev(batch.pool_hidden, wl.dtype, dev)
+            pool_pos = _i32(batch.pool_pos, dev)
+            pk = torch.empty((pool_rows, hkv, d), dtype=td, device=dev)
+            pv = torch.empty_like(pk)
+            kvf.recompute_qkv(L, pool_hidden, None, pool_pos, self.w, kvf.KVF_OUT_K | kvf.KVF_OUT_V,
+                              self.rope_cos, self.rope_sin, k_out=pk, v_out=pv)
+            if wl.kivi8:
+                n_pool = len(batch.pool_cu) - 1
+                self.kivi = {
+                    "k_codes": torch.empty((pool_rows, hkv, d), dtype=torch.uint8, device=dev),
+                    "v_codes": torch.empty((pool_rows, hkv, d), dtype=torch.uint8, device=dev),
+                    "k_min": torch.empty((n_pool, hkv, d), dtype=torch.float32, device=dev),
+                    "k_scale": torch.empty((n_pool, hkv, d), dtype=torch.float32, device=dev),
+                    "v_min": torch.empty((pool_rows, hkv), dtype=torch.float32, device=dev),
+                    "v_scale": torch.empty((pool_rows, hkv), dtype=torch.float32, device=dev),
+                }
+                kvf.kivi8_encode(L, pk, pv, _i32(batch.pool_cu, dev), self.max_chunk_len, self.kivi)
+                del pk, pv
+            else:
+                self.pool_k, self.pool_v = pk, pv
+            del pool_hidden
+
+        # budgets and buffers
+        self.k_per_req = [kvf.recompute_budget(int(n), ratio_pct) for n in batch.n_ctx]
+        self.U = [self.kb.n_query(r) for r in range(R)]
+        self.M_per_req = [k + u for k, u in zip(self.k_per_req, self.U)]
+        self.cu_q = [0] + list(np.cumsum(self.M_per_req).astype(int))
+        M = self.cu_q[-1]
+        self.M = M
+        n_scores = int(np.sum(batch.n_ctx))
+        self.fused_k = torch.zeros((T_total, hkv, d), dtype=td, device=dev)
+        self.fused_v = torch.zeros_like(self.fused_k)
+        self.scores = torch.zeros(max(n_scores, 1), dtype=torch.float32, device=dev)
+        self.sel = torch.zeros(max(sum(self.k_per_req), 1), dtype=torch.int32, device=dev)
+        self.rows = torch.zeros(max(M, 1), dtype=torch.int32, device=dev)
+        self.pos = torch.zeros(max(M, 1), dtype=torch.int32, device=dev)
+        self.q = torch.zeros((max(M, 1), hq, d), dtype=td, device=dev)
+        self.k_new = torch.zeros((max(M, 1), hkv, d), dtype=td, device=dev)
+        self.v_new = torch.zeros_like(self.k_new)
+        self.out = torch.zeros((max(M, 1), hq, d), dtype=td, device=dev)
+        self.lse = torch.zeros((max(M, 1), hq), dtype=torch.float32, device=dev)
+        self.sm_scale = 1.0 / math.sqrt(d)
+        self.u_rows = _i32(batch.query_rows(), dev)
+        self.u_pos = _i32(batch.query_pos(), dev)
+        nU = int(self.u_rows.shape[0])
+        self.ws = None
+        if self.mode == "deviation":
+            self.all_pos = _i32(batch.all_pos(), dev)
+            self.k_probe = torch.zeros((T_total, hkv, d), dtype=td, device=dev)
+        else:
+            self.q_u = torch.zeros((max(nU, 1), hq, d), dtype=td, device=dev)
+            self.k_u = torch.zeros((max(nU, 1), hkv, d), dtype=td, device=dev)
+            self.v_u = torch.zeros_like(self.k_u)
+            nbytes = kvf.score_workspace_size(kvf.KVF_SCORE_ATTN_MASS, L, self.kb, n_last_q)
+            self.ws = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=dev)
+
+    # ------------------------------------------------------------------ stages
+    def stage_rerotate(self):
+        kvf.rerotate(self.layer, self.chunks, self.max_chunk_len, self.pool_k, self.pool_v,
+                     self.rope_cos, self.rope_sin, self.fused_k, self.fused_v, kivi=self.kivi)
+
+    def stage_score(self):
+        L = self.layer
+        if self.mode == "deviation":
+            kvf.recompute_qkv(L, self.x, None, self.all_pos, self.w, kvf.KVF_OUT_K, self.rope_cos,
+                              self.rope_sin, k_out=self.k_probe)
+            kvf.score(kvf.KVF_SCORE_DEVIATION, L, self.kb, self.fused_k, self.k_probe, None,
+                      self.scores)
+        else:
+            kvf.recompute_qkv(L, self.x, self.u_rows, self.u_pos, self.w,
+                              kvf.KVF_OUT_Q | kvf.KVF_OUT_K | kvf.KVF_OUT_V, self.rope_cos,
+                              self.rope_sin, q_out=self.q_u, k_out=self.k_u, v_out=self.v_u)
+            kvf.scatter_kv(L, self.k_u, None, self.v_u, None, self.u_rows, self.fused_k, self.fused_v)
+            kvf.score(kvf.KVF_SCORE_ATTN_MASS, L, self.kb, self.fused_k, None, self.q_u, self.scores,
+                      self.ws, n_last_q=self.n_last_q)
+
+    def stage_select(self):
+        kvf.select_topk(self.scores, self.kb, self.k_per_req, self.sel, self.rows, self.pos)
+
+    def force_selection(self, sel: Sequence[np.ndarray]):
+        """Replace the selection with given per-request positions (tests)."""
+        rows, pos, flat = [], [], []
+        b = self.batch
+        for r in range(b.n_req):
+            s = np.asarray(sel[r], dtype=np.int32)
+            assert len(s) == self.k_per_req[r]
+            p = np.concatenate([s, np.arange(b.n_ctx[r], b.cu_T[r + 1] - b.cu_T[r], dtype=np.int32)])
+            pos.append(p)
+            rows.append(p + b.cu_T[r])
+            flat.append(s)
+        self.rows.copy_(_i32(np.concatenate(rows), self.device))
+        self.pos.copy_(_i32(np.concatenate(pos), self.device))
+        if sum(self.k_per_req):
+            self.sel.copy_(_i32(np.concatenate(flat), self.device))
+
+    def stage_recompute_fuse(self):
+        L = self.layer
+        if self.M == 0:
+            return
+        if self.mode == "deviation":
+            kvf.recompute_qkv(L, self.x, self.rows, self.pos, self.w, kvf.KVF_OUT_Q | kvf.KVF_OUT_V,
+                              self.rope_cos, self.rope_sin, q_out=self.q, v_out=self.v_new, M=self.M)
+            kvf.scatter_kv(L, self.k_probe, self.rows, self.v_new, None, self.rows, self.fused_k,
+                           self.fused_v, M=self.M)
+        else:
+            kvf.recompute_qkv(L, self.x, self.rows, self.pos, self.w,
+                              kvf.KVF_OUT_Q | kvf.KVF_OUT_K | kvf.KVF_OUT_V, self.rope_cos,
+                              self.rope_sin, q_out=self.q, k_out=self.k_new, v_out=self.v_new,
+                              M=self.M)
+            kvf.scatter_kv(L, self.k_new, None, self.v_new, None, self.rows, self.fused_k,
+                           self.fused_v, M=self.M)
+
+    def stage_attention(self):
+        if self.M == 0:
+            return
+        kvf.sparse_q_attention(self.layer, self.kb, self.q, self.pos, self.cu_q, self.fused_k,
+                               self.fused_v, self.sm_scale, self.out, self.lse)
+
+    def run(self, forced_sel: Optional[Sequence[np.ndarray]] = None):
+        """Enqueue one pass of the whole path on the current stream."""
+        self.stage_rerotate()
+        self.stage_score()
+        if forced_sel is None:
+            self.stage_select()
+        else:
+            self.force_selection(forced_sel)
+        self.stage_recompute_fuse()
+        self.stage_attention()
+
+    # ------------------------------------------------------------------ readback
+    def selection(self):
+        s = self.sel.cpu().numpy()
+        out, off = [], 0
+        for k in self.k_per_req:
+            out.append(s[off:off + k].copy())
+            off += k
+        return out

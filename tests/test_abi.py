@@ -1,0 +1,133 @@
+"""The C-ABI library: it loads, exports every declared entry point, and its
+host-side validation rejects malformed arguments before anything reaches the
+GPU (CPU only: no call here launches a kernel)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import fusion
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvfuse.h")
+LIB = os.path.join(ROOT, "rag_kv_cache_kvf_amd", "libkvfuse.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libkvfuse.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvf_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return ctypes.CDLL(LIB)
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) >= 14
+    for n in ["kvf_rerotate", "kvf_score", "kvf_select_topk", "kvf_recompute_qkv",
+              "kvf_scatter_kv", "kvf_sparse_q_attention"]:
+        assert n in names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings_and_version(lib):
+    lib.kvf_status_string.restype = ctypes.c_char_p
+    assert lib.kvf_status_string(0) == b"KVF_OK"
+    assert lib.kvf_status_string(2) == b"KVF_ERR_UNSUPPORTED"
+    assert lib.kvf_abi_version() == 1
+
+
+def test_budget_matches_oracle(lib):
+    for n in (0, 1, 7, 9, 256, 3072, 5120, 10240, 32768):
+        for pct in (0, 15, 20, 30, 33, 100):
+            assert lib.kvf_recompute_budget(n, pct) == fusion.budget(n, pct)
+    assert lib.kvf_recompute_budget(-1, 30) == -1
+    assert lib.kvf_recompute_budget(10, 101) == -1
+
+
+class Layer(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("dtype", ctypes.c_int32)]
+
+
+class Batch(ctypes.Structure):
+    _fields_ = [("n_req", ctypes.c_int32), ("cu_T", ctypes.POINTER(ctypes.c_int32)),
+                ("n_ctx", ctypes.POINTER(ctypes.c_int32))]
+
+
+def _batch(cu, nc):
+    a = (ctypes.c_int32 * len(cu))(*cu)
+    b = (ctypes.c_int32 * len(nc))(*nc)
+    return Batch(len(nc), ctypes.cast(a, ctypes.POINTER(ctypes.c_int32)),
+                 ctypes.cast(b, ctypes.POINTER(ctypes.c_int32))), (a, b)
+
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+
+
+def test_validation_errors(lib):
+    lib.kvf_last_error.restype = ctypes.c_char_p
+    ok = Layer(256, 4, 4, 64, 0)
+    # head_dim and GQA shape
+    assert lib.kvf_recompute_qkv(ctypes.byref(Layer(256, 4, 4, 96, 0)), FAKE, 10, None, FAKE, 1,
+                                 FAKE, 7, FAKE, FAKE, 4, FAKE, FAKE, FAKE, None) == 2
+    assert lib.kvf_recompute_qkv(ctypes.byref(Layer(256, 6, 4, 64, 0)), FAKE, 10, None, FAKE, 1,
+                                 FAKE, 7, FAKE, FAKE, 4, FAKE, FAKE, FAKE, None) == 2
+    assert b"multiple" in lib.kvf_last_error()
+    # bad dtype, NULL layer, bad mask
+    assert lib.kvf_recompute_qkv(ctypes.byref(Layer(256, 4, 4, 64, 7)), FAKE, 10, None, FAKE, 1,
+                                 FAKE, 7, FAKE, FAKE, 4, FAKE, FAKE, FAKE, None) == 1
+    assert lib.kvf_recompute_qkv(None, FAKE, 10, None, FAKE, 1, FAKE, 7, FAKE, FAKE, 4, FAKE, FAKE,
+                                 FAKE, None) == 1
+    assert lib.kvf_recompute_qkv(ctypes.byref(ok), FAKE, 10, None, FAKE, 1, FAKE, 8, FAKE, FAKE, 4,
+                                 FAKE, FAKE, FAKE, None) == 1
+    # identity row map larger than x
+    assert lib.kvf_recompute_qkv(ctypes.byref(ok), FAKE, 10, None, FAKE, 11, FAKE, 1, FAKE, FAKE, 4,
+                                 FAKE, FAKE, FAKE, None) == 1
+    # bf16 projection with Hkv * d not a multiple of 128
+    assert lib.kvf_recompute_qkv(ctypes.byref(Layer(256, 3, 1, 64, 1)), FAKE, 10, None, FAKE, 1,
+                                 FAKE, 7, FAKE, FAKE, 4, FAKE, FAKE, FAKE, None) == 2
+    # batch checks
+    b, keep = _batch([0, 10, 5], [4, 2])
+    assert lib.kvf_score(0, ctypes.byref(ok), ctypes.byref(b), FAKE, FAKE, None, 0, FAKE, None, 0,
+                         None) == 1
+    b, keep = _batch([0, 10], [11])
+    assert lib.kvf_score(0, ctypes.byref(ok), ctypes.byref(b), FAKE, FAKE, None, 0, FAKE, None, 0,
+                         None) == 1
+    # attention mass needs a workspace
+    b, keep = _batch([0, 10], [6])
+    assert lib.kvf_score(1, ctypes.byref(ok), ctypes.byref(b), FAKE, None, FAKE, 0, FAKE, None, 0,
+                         None) == 3
+    # top-k: k > N
+    k = (ctypes.c_int32 * 1)(7)
+    assert lib.kvf_select_topk(FAKE, ctypes.byref(b), k, FAKE, None, None, None, 0, None) == 1
+    # too many requests
+    cu = list(range(0, 66))
+    b, keep = _batch(cu, [0] * 65)
+    assert lib.kvf_score(0, ctypes.byref(ok), ctypes.byref(b), FAKE, FAKE, None, 0, FAKE, None, 0,
+                         None) == 1
+    # rerotate: int8 caches need bf16 output
+    class Kivi(ctypes.Structure):
+        _fields_ = [(n, ctypes.c_void_p) for n in ("kc", "vc", "km", "ks", "vm", "vs")] + [
+            ("n", ctypes.c_int32)]
+    kv = Kivi(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1)
+    assert lib.kvf_rerotate(ctypes.byref(ok), FAKE, 1, 4, None, None, ctypes.byref(kv), 4, FAKE,
+                            FAKE, 4, FAKE, FAKE, 4, None) == 2
+
+
+def test_empty_calls_are_noops(lib):
+    ok = Layer(256, 4, 4, 64, 0)
+    assert lib.kvf_rope_table(ctypes.c_double(1e4), 64, 0, None, None, None) == 0
+    assert lib.kvf_recompute_qkv(ctypes.byref(ok), None, 0, None, None, 0, None, 7, None, None, 0,
+                                 None, None, None, None) == 0
+    assert lib.kvf_scatter_kv(ctypes.byref(ok), None, None, 0, None, None, 0, None, 0, None, None, 0,
+                              None) == 0

@@ -1,0 +1,152 @@
+"""End-to-end parity of the fused layer (all six calls in order) against the
+oracle, plus determinism and HIP-graph replay (GPU).
+
+Inputs: the seeded synthetic batch; the per-chunk caches are built by the
+oracle in float64 and stored in the workload's format (bf16 / fp32 / int8
+KIVI), then fed to both sides.  Checks:
+  * scores: max|d| / rms within the dtype tolerance;
+  * the GPU's selection is a valid top-k of the oracle's scores (every
+    selected score >= every unselected one, up to the score tolerance);
+  * with the oracle's selection forced into the GPU path, the fused cache,
+    the attention output and its LSE match the oracle.
+"""
+import numpy as np
+import pytest
+
+from oracle import fusion, kivi
+from rag_kv_cache_kvf_amd import synth
+from tests.gpu_util import TOL, assert_close, decode, encode, from_gpu, raw
+
+pytestmark = pytest.mark.gpu
+
+E2E = ["tiny_fp32_dev", "mini_bf16_mass", "mini_bf16_dev_pool", "mini_bf16_kivi8",
+       "mini_bf16_d64_mass", "mini_f32_mass"]
+
+
+@pytest.fixture(scope="module")
+def layer_mod():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from rag_kv_cache_kvf_amd import layer
+    return layer
+
+
+def _oracle_inputs(name, pct=None):
+    b = synth.make_batch(name)
+    wl = b.wl
+    lo = fusion.Layer(wl.hidden, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.rope_base)
+    x = decode(b.x, wl.dtype)
+    w = decode(b.w_qkv, wl.dtype)
+    pk, pv = fusion.pic_encode(decode(b.pool_hidden, wl.dtype), b.pool_pos, w, lo)
+    if wl.kivi8:
+        pk32 = decode(encode(pk, "bf16"), "bf16").astype(np.float32)
+        pv32 = decode(encode(pv, "bf16"), "bf16").astype(np.float32)
+        kc, kmin, ksc = kivi.encode_keys(pk32, b.pool_cu)
+        vc, vmin, vsc = kivi.encode_values(pv32)
+        pic = {"k_codes": kc, "v_codes": vc, "k_min": kmin, "k_scale": ksc, "v_min": vmin,
+               "v_scale": vsc}
+        opk = kivi.decode_keys(kc, kmin, ksc, b.pool_cu)
+        opv = kivi.decode_values(vc, vmin, vsc)
+    else:
+        pic = {"k": encode(pk, wl.dtype), "v": encode(pv, wl.dtype)}
+        opk, opv = decode(pic["k"], wl.dtype), decode(pic["v"], wl.dtype)
+    pct = pct if pct is not None else wl.ratio_pct[0]
+    ks = [fusion.budget(int(n), pct) for n in b.n_ctx]
+    return b, wl, lo, x, w, pic, opk, opv, pct, ks
+
+
+def _check_selection_valid(sel_gpu, scores_ref, tol_abs, what):
+    n = len(scores_ref)
+    mask = np.zeros(n, dtype=bool)
+    mask[sel_gpu] = True
+    if mask.all() or not mask.any():
+        return
+    lo_sel = scores_ref[mask].min()
+    hi_uns = scores_ref[~mask].max()
+    print(f"[parity] {what}: min selected {lo_sel:.6g}, max unselected {hi_uns:.6g}", flush=True)
+    assert lo_sel >= hi_uns - tol_abs, f"{what}: selection is not a top-k of the oracle scores"
+
+
+@pytest.mark.parametrize("name", E2E)
+def test_fused_layer_end_to_end(layer_mod, name):
+    import torch
+    b, wl, lo, x, w, pic, opk, opv, pct, ks = _oracle_inputs(name)
+    print(f"[case] {name}", flush=True)
+    g = layer_mod.FusedLayerGPU(b, pct, pic=pic)
+    g.run()
+    torch.cuda.synchronize()
+    ref = fusion.fused_layer(x, w, opk, opv, b.chunk_table, b.cu_T, b.n_ctx, lo, wl.score, ks)
+    tol = TOL[wl.dtype]
+    gs = from_gpu(g.scores)[: int(np.sum(b.n_ctx))]
+    rs = np.concatenate(ref["scores"])
+    assert_close(gs, rs, wl.dtype, f"{name} scores")
+    rms = float(np.sqrt(np.mean(rs * rs)))
+    sel = g.selection()
+    agree = []
+    for r in range(b.n_req):
+        off = int(np.sum(b.n_ctx[:r]))
+        _check_selection_valid(sel[r], rs[off:off + int(b.n_ctx[r])], 2 * tol * rms, f"{name} req {r}")
+        inter = len(np.intersect1d(sel[r], ref["sel"][r]))
+        agree.append(inter / max(1, len(sel[r])))
+        assert len(sel[r]) == ks[r] and np.all(np.diff(sel[r]) > 0)
+    print(f"[info] {name}: selection overlap with the oracle {np.mean(agree):.4f}", flush=True)
+
+    # downstream with the oracle's selection
+    g.run(forced_sel=ref["sel"])
+    torch.cuda.synchronize()
+    assert np.array_equal(raw(g.rows)[: g.M], ref["rows"])
+    assert_close(from_gpu(g.fused_k), ref["fused_k"], wl.dtype, f"{name} fused K")
+    assert_close(from_gpu(g.fused_v), ref["fused_v"], wl.dtype, f"{name} fused V")
+    assert_close(from_gpu(g.q)[: g.M], ref["q"], wl.dtype, f"{name} recomputed Q")
+    assert_close(from_gpu(g.out)[: g.M], ref["out"], wl.dtype, f"{name} attention output")
+    assert_close(from_gpu(g.lse)[: g.M], ref["lse"], wl.dtype, f"{name} lse",
+                 tol=1e-3 if wl.dtype == "bf16" else 1e-4)
+
+
+@pytest.mark.parametrize("name,pct", [("mini_bf16_mass", 0), ("mini_bf16_mass", 100),
+                                      ("mini_bf16_dev_pool", 0), ("mini_bf16_dev_pool", 100)])
+def test_ratio_endpoints(layer_mod, name, pct):
+    """rho = 0 (direct reuse) and rho = 100% (every context token recomputed)."""
+    import torch
+    b, wl, lo, x, w, pic, opk, opv, pct, ks = _oracle_inputs(name, pct)
+    g = layer_mod.FusedLayerGPU(b, pct, pic=pic)
+    g.run()
+    torch.cuda.synchronize()
+    ref = fusion.fused_layer(x, w, opk, opv, b.chunk_table, b.cu_T, b.n_ctx, lo, wl.score, ks)
+    assert np.array_equal(raw(g.rows)[: g.M], ref["rows"])
+    assert_close(from_gpu(g.fused_k), ref["fused_k"], wl.dtype, f"{name}@{pct} fused K")
+    assert_close(from_gpu(g.out)[: g.M], ref["out"], wl.dtype, f"{name}@{pct} output")
+    if pct == 100:
+        full = fusion.full_prefill(x, w, b.cu_T, lo)
+        assert_close(from_gpu(g.fused_k), full["k"], wl.dtype, f"{name} rho=1 vs full prefill K")
+        assert_close(from_gpu(g.out)[: g.M], full["out"], wl.dtype, f"{name} rho=1 vs full prefill O")
+
+
+def test_deterministic_and_graph_replay(layer_mod):
+    import torch
+    b, wl, lo, x, w, pic, opk, opv, pct, ks = _oracle_inputs("mini_bf16_mass")
+    g = layer_mod.FusedLayerGPU(b, pct, pic=pic)
+    g.run()
+    torch.cuda.synchronize()
+    first = {k: raw(getattr(g, k)).copy() for k in ("scores", "sel", "fused_k", "fused_v", "out", "lse")}
+    g.run()
+    torch.cuda.synchronize()
+    for k, v in first.items():
+        assert np.array_equal(raw(getattr(g, k)), v), f"{k} differs between runs"
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        g.run()                       # warm-up on the capture stream
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=s):
+            g.run()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        g.out.zero_()
+        g.fused_k.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for k, v in first.items():
+            assert np.array_equal(raw(getattr(g, k)), v), f"replay {rep}: {k} differs"
