@@ -44,7 +44,7 @@ from typing import Optional, Sequence
 
 import numpy as np
 
-from . import rope
+from . import rope, storage
 
 
 @dataclasses.dataclass(frozen=True)
@@ -254,7 +254,8 @@ def fused_layer(x: np.ndarray, w_qkv: np.ndarray, pool_k: np.ndarray, pool_v: np
                 chunk_table: np.ndarray, cu_T: Sequence[int], n_ctx: Sequence[int],
                 layer: Layer, mode: str, k_per_req: Sequence[int],
                 n_last_q: Optional[int] = None,
-                forced_sel: Optional[Sequence[np.ndarray]] = None) -> dict:
+                forced_sel: Optional[Sequence[np.ndarray]] = None,
+                store: Optional[str] = None) -> dict:
     """Run the fused layer for a batch of independent requests.
 
     mode "deviation" ([KVB] Algorithm 2 at one layer): probe K~ for every row,
@@ -267,20 +268,33 @@ def fused_layer(x: np.ndarray, w_qkv: np.ndarray, pool_k: np.ndarray, pool_v: np
 
     `forced_sel` replaces the selection with given per-request positions
     (used to evaluate the rest of the layer on another selection).
+
+    `store` ("bf16" or "f32", default None) evaluates the layer at a serving
+    precision: every tensor a serving stack materialises - cache entries
+    written by re-positioning or fusion, the key probe, the projected Q/K/V -
+    is rounded to that format (round to nearest even) when it is produced;
+    arithmetic between those points stays float64 and the attention output
+    and LSE are not rounded.  The QCFuse page runs every strategy in a BF16
+    serving stack (section 4.1.1); store="bf16" is that reading.  With
+    store=None nothing is rounded.
     Returns every intermediate, float64, in flat request-major layouts.
     """
+    def S(a):
+        return a if store is None else storage.decode(storage.encode(a, store), store)
+
     x = np.asarray(x, dtype=np.float64)
     cu_T = [int(v) for v in cu_T]
     n_req = len(cu_T) - 1
     total = cu_T[-1]
     fk, fv = rerotate_stitch(pool_k, pool_v, chunk_table, total, layer)
+    fk, fv = S(fk), S(fv)
     res = {"fused_k_pic": fk.copy(), "fused_v_pic": fv.copy()}
 
     scores, sels, rows_all, pos_all = [], [], [], []
     k_probe = None
     if mode == "deviation":
         allpos = np.concatenate([np.arange(cu_T[r + 1] - cu_T[r]) for r in range(n_req)])
-        k_probe = recompute(x, allpos, w_qkv, layer, want=("k",))["k"]
+        k_probe = S(recompute(x, allpos, w_qkv, layer, want=("k",))["k"])
         res["k_probe"] = k_probe
     elif mode != "attn_mass":
         raise ValueError(mode)
@@ -293,7 +307,7 @@ def fused_layer(x: np.ndarray, w_qkv: np.ndarray, pool_k: np.ndarray, pool_v: np
         else:
             qr = np.arange(a + N, b)
             qpos = np.arange(N, b - a)
-            new = recompute(x[qr], qpos, w_qkv, layer)
+            new = {k: S(v) for k, v in recompute(x[qr], qpos, w_qkv, layer).items()}
             fk[qr] = new["k"]
             fv[qr] = new["v"]
             q_u_all.append(new["q"])
@@ -314,10 +328,10 @@ def fused_layer(x: np.ndarray, w_qkv: np.ndarray, pool_k: np.ndarray, pool_v: np
     rows = np.concatenate(rows_all)
     pos = np.concatenate(pos_all)
     if mode == "deviation":
-        new = recompute(x[rows], pos, w_qkv, layer, want=("q", "v"))
+        new = {k: S(v) for k, v in recompute(x[rows], pos, w_qkv, layer, want=("q", "v")).items()}
         new["k"] = k_probe[rows]
     else:
-        new = recompute(x[rows], pos, w_qkv, layer)
+        new = {k: S(v) for k, v in recompute(x[rows], pos, w_qkv, layer).items()}
     fk, fv = fuse(fk, fv, rows, new["k"], new["v"])
 
     outs, lses = [], []

@@ -188,7 +188,10 @@ __global__ void __launch_bounds__(256) attn_bf16_kernel(AttnArgs a) {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float p = exp2f(s[kb][i] - m_use);
+        float p = exp2f(s[kb][i] - m_use);
+        // the V product consumes bf16 probabilities: normalise by the sum of
+        // exactly those values so the weights used sum to one
+        if constexpr (!STATS_ONLY) p = static_cast<float>(static_cast<__bf16>(p));
         s[kb][i] = p;
         rs += p;
       }

@@ -45,8 +45,40 @@ def rel_err(gpu: np.ndarray, ref: np.ndarray) -> float:
 def assert_close(gpu, ref, dtype: str, what: str, tol: float = None):
     e = rel_err(gpu, ref)
     t = TOL[dtype] if tol is None else tol
-    print(f"[parity] {what}: max|d|/rms = {e:.3e} (tol {t:.1e})", flush=True)
+    where = ""
+    if np.size(ref):
+        d = np.abs(np.asarray(gpu, np.float64) - np.asarray(ref, np.float64))
+        idx = np.unravel_index(int(np.argmax(d)), d.shape)
+        where = f" at {tuple(int(i) for i in idx)} gpu={float(np.asarray(gpu)[idx]):.6g} ref={float(np.asarray(ref)[idx]):.6g}"
+    print(f"[parity] {what}: max|d|/rms = {e:.3e} (tol {t:.1e}){where}", flush=True)
     assert e <= t, f"{what}: relative error {e:.3e} > {t:.1e}"
+
+
+def rel_err_vectors(gpu: np.ndarray, ref: np.ndarray) -> float:
+    """max over output vectors (last axis) of max|d| / rms(reference vector)."""
+    ref = np.asarray(ref, dtype=np.float64)
+    gpu = np.asarray(gpu, dtype=np.float64)
+    assert gpu.shape == ref.shape, (gpu.shape, ref.shape)
+    if ref.size == 0:
+        return 0.0
+    r = ref.reshape(-1, ref.shape[-1])
+    g = gpu.reshape(-1, ref.shape[-1])
+    floor = 1e-3 * float(np.sqrt(np.mean(r * r))) + 1e-30
+    rms = np.maximum(np.sqrt(np.mean(r * r, axis=1)), floor)
+    return float(np.max(np.max(np.abs(g - r), axis=1) / rms))
+
+
+def assert_close_vectors(gpu, ref, dtype: str, what: str, tol: float = None):
+    """Attention outputs: the RMS is taken per output vector (one token, one
+    head).  Outputs of rows that see few keys are an order of magnitude
+    larger than those of long rows, so a single RMS over the tensor would be
+    exceeded by the bf16 storage rounding of those few vectors alone."""
+    e = rel_err_vectors(gpu, ref)
+    whole = rel_err(gpu, ref)
+    t = TOL[dtype] if tol is None else tol
+    print(f"[parity] {what}: max over vectors of max|d|/rms(vector) = {e:.3e} (tol {t:.1e}); "
+          f"whole-tensor max|d|/rms = {whole:.3e}", flush=True)
+    assert e <= t, f"{what}: per-vector relative error {e:.3e} > {t:.1e}"
 
 
 def encode(x: np.ndarray, dtype: str) -> np.ndarray:

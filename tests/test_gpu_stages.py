@@ -14,7 +14,7 @@ import pytest
 
 from oracle import fusion, kivi, rope, storage
 from rag_kv_cache_kvf_amd import synth
-from tests.gpu_util import TOL, assert_close, decode, encode, from_gpu, raw, to_gpu
+from tests.gpu_util import TOL, assert_close, assert_close_vectors, decode, encode, from_gpu, raw, to_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -443,7 +443,7 @@ def test_attention(kvf, case):
                                        dk[cu_T[r]:cu_T[r + 1]], dv[cu_T[r]:cu_T[r + 1]], lo)
         refs.append(o)
         lses.append(l)
-    assert_close(from_gpu(out), np.concatenate(refs), dtype, f"attention {case[:4]}")
+    assert_close_vectors(from_gpu(out), np.concatenate(refs), dtype, f"attention {case[:4]}")
     assert_close(from_gpu(lse), np.concatenate(lses), "f32" if dtype == "f32" else "bf16",
                  f"attention lse {case[:4]}", tol=1e-4 if dtype == "f32" else 1e-3)
 
@@ -484,5 +484,5 @@ def test_attention_full_size_sampled(kvf, wl_name):
         o, l = fusion.causal_attention(decode(q_s[m:m + 1], "bf16"), pos[m:m + 1], kr, vr, lo)
         ref_o.append(o[0])
         ref_l.append(l[0])
-    assert_close(go[samp], np.array(ref_o), "bf16", f"{wl_name} attention (sampled rows)")
+    assert_close_vectors(go[samp], np.array(ref_o), "bf16", f"{wl_name} attention (sampled rows)")
     assert_close(gl[samp], np.array(ref_l), "bf16", f"{wl_name} lse (sampled rows)", tol=1e-3)

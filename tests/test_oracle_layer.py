@@ -113,3 +113,28 @@ def test_perturbation_creates_deviation():
     first = int(b.chunk_table[0, 3])
     assert np.all(s[:first] < 1e-12)        # first chunk: cached == fresh
     assert np.all(s[first:] > 1e-5)          # later chunks deviate
+
+
+@pytest.mark.parametrize("name", ["mini_bf16_mass", "mini_bf16_dev_pool"])
+def test_serving_precision_mode(name):
+    """store= rounds the tensors a serving stack materialises; store=None is
+    the exact layer, store="f32" moves it by float32 rounding only, and with
+    store="bf16" every cache entry and projection is a bf16 value while the
+    outputs stay within bf16 rounding of the exact layer."""
+    wl, b, layer, x, w, pk, pv = _setup(name)
+    exact = _run(wl, b, layer, x, w, pk, pv, 30)
+    k = [fusion.budget(int(n), 30) for n in b.n_ctx]
+    args = (x, w, pk, pv, b.chunk_table, b.cu_T, b.n_ctx, layer, wl.score, k)
+    none = fusion.fused_layer(*args, forced_sel=exact["sel"], store=None)
+    np.testing.assert_array_equal(none["out"], exact["out"])
+    f32 = fusion.fused_layer(*args, forced_sel=exact["sel"], store="f32")
+    rms = np.sqrt(np.mean(exact["out"] ** 2))
+    assert np.max(np.abs(f32["out"] - exact["out"])) < 1e-5 * rms
+    bf = fusion.fused_layer(*args, forced_sel=exact["sel"], store="bf16")
+    for key in ("fused_k", "fused_v", "q", "k_new", "v_new"):
+        v = bf[key]
+        assert np.array_equal(storage.decode(storage.encode(v, "bf16"), "bf16"), v), key
+        e = np.max(np.abs(v - exact[key])) / np.sqrt(np.mean(exact[key] ** 2))
+        assert 0 < e < 2e-2, (key, e)
+    e = np.max(np.abs(bf["out"] - exact["out"])) / rms
+    assert 0 < e < 0.1
