@@ -31,11 +31,12 @@
 //
 // fp32 path: one wave per (row, head) with lane-parallel keys; used by the
 // small fp32 workloads only.
+#include <type_traits>
+
 #include "../kvf_common.h"
 
 namespace kvf {
 
-constexpr int kAK = 64;          // keys per LDS tile
 constexpr int kAQ = 128;         // query vectors per workgroup
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -59,7 +60,7 @@ struct AttnArgs {
   float* part_l;
   int64_t plane;                 // rows * Hq: stride between split planes
   int n_splits;
-  int split_keys;                // keys per split (multiple of kAK)
+  int split_keys;                // keys per split (a multiple of the key tile)
   int hq, hkv, G;
   float scale_log2;
 };
@@ -67,14 +68,41 @@ struct AttnArgs {
 // ---------------------------------------------------------------------------
 // bf16 MFMA kernel
 // ---------------------------------------------------------------------------
+// 8 waves: wave w owns query vectors [32*(w%4), +32) and key half w/4 of every
+// 128-key tile.  K and V tiles are copied global -> LDS by the DMA path
+// (global_load_lds, 16 bytes per lane, no registers involved) into two
+// static buffers: tile t+1 streams in while tile t is computed.  Both tiles
+// are row-major with the 16-byte chunks of row r XOR-swizzled by r mod
+// (D/8), so the key-row reads of the score MFMA and the transposing reads of
+// V (ds_read_b64_tr_b16, one 4-key x 4-channel transpose per 16 lanes) hit
+// distinct banks.
+constexpr int kAT = 128;         // keys per tile (two halves of 64)
+constexpr int kAThreads = 512;
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) const void global_cvoid_t;
+
+template <int D>
+__device__ __forceinline__ int swz(int row, int d) {       // element index in a tile
+  constexpr int CPR = D / 8;
+  return row * D + ((((d >> 3) ^ (row & (CPR - 1)))) << 3) + (d & 7);
+}
+
 template <int D, bool STATS_ONLY>
-__global__ void __launch_bounds__(256) attn_bf16_kernel(AttnArgs a) {
+__global__ void __launch_bounds__(kAThreads) attn_bf16_kernel(AttnArgs a) {
   constexpr int KS = D / 16;       // MFMA k-steps over the head dimension
   constexpr int DB = D / 32;       // 32-channel output blocks
-  constexpr int LDK = D + 8;       // padded K row (bf16)
-  __shared__ __attribute__((aligned(16))) bf16_t Ks[kAK][LDK];
-  __shared__ __attribute__((aligned(16))) bf16_t Vs[kAK / 4][D][4];
-  __shared__ int s_maxpos;
+  constexpr int CPR = D / 8;       // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;    // rows per DMA instruction (64 lanes x 16 B)
+  constexpr int NDMA = kAT / RPI / 8;   // DMA instructions per wave per tile and tensor
+  constexpr int TILE = kAT * D;
+  __shared__ __attribute__((aligned(16))) bf16_t k0s[TILE];
+  __shared__ __attribute__((aligned(16))) bf16_t k1s[TILE];
+  __shared__ __attribute__((aligned(16))) bf16_t v0s[STATS_ONLY ? 8 : TILE];
+  __shared__ __attribute__((aligned(16))) bf16_t v1s[STATS_ONLY ? 8 : TILE];
+  __shared__ int s_pos[2];
 
   const int hkv = a.hkv;
   const int g = blockIdx.x % hkv;
@@ -82,14 +110,15 @@ __global__ void __launch_bounds__(256) attn_bf16_kernel(AttnArgs a) {
   const int r = find_segment(a.cu_tiles, a.b.n_req, tile);
   const int tr = tile - a.cu_tiles[r];
   const int R = a.rows_per_tile;
-  const int lrow0 = tr * R;                               // first row inside the request
+  const int lrow0 = tr * R;
   const int nrows = min(R, a.nrows[r] - lrow0);
   const int T = a.b.cu_T[r + 1] - a.b.cu_T[r];
   const int64_t krow0 = a.b.cu_T[r];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int qg = w & 3, kg = w >> 2;
   const int c = lane & 31, hf = lane >> 5;
-  const int qv = 32 * w + c;
+  const int qv = 32 * qg + c;
   const int row_l = qv % R, head_l = qv / R;
   const bool valid = head_l < a.G && row_l < nrows;
   const int64_t qrow = static_cast<int64_t>(a.qrow0[r]) + lrow0 + row_l;
@@ -99,11 +128,18 @@ __global__ void __launch_bounds__(256) attn_bf16_kernel(AttnArgs a) {
     pos = a.q_pos ? a.q_pos[qrow] : a.pos0[r] + lrow0 + row_l;
     if (pos < 0 || pos >= T) pos = -1;
   }
-  if (tid == 0) s_maxpos = -1;
+  if (tid == 0) {
+    s_pos[0] = -1;                 // max position
+    s_pos[1] = 0x7fffffff;         // min position
+  }
   __syncthreads();
-  if (pos >= 0) atomicMax(&s_maxpos, pos);
+  if (pos >= 0) {
+    atomicMax(&s_pos[0], pos);
+    atomicMin(&s_pos[1], pos);
+  }
   __syncthreads();
-  const int kend = s_maxpos + 1;                           // keys [0, kend) are visible to someone
+  const int kend = s_pos[0] + 1;                  // keys [0, kend) are visible to someone
+  const int pmin = s_pos[1];                      // keys <= pmin are visible to everyone
 
   int kbeg = 0, klim = kend;
   if constexpr (STATS_ONLY) {
@@ -111,7 +147,6 @@ __global__ void __launch_bounds__(256) attn_bf16_kernel(AttnArgs a) {
     klim = min(kend, kbeg + a.split_keys);
   }
 
-  // Q fragments (B operand of S^T = K Q^T): channel chunk ks*16 + hf*8
   const bf16_t* Q = static_cast<const bf16_t*>(a.q);
   bf16x8_t qf[KS];
 #pragma unroll
@@ -125,103 +160,220 @@ __global__ void __launch_bounds__(256) attn_bf16_kernel(AttnArgs a) {
   }
 
   f32x16_t o[DB];
-  if constexpr (!STATS_ONLY) {
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+  for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
-  }
+    for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
 
-  const bf16_t* Kg = static_cast<const bf16_t*>(a.k);
-  const bf16_t* Vg = static_cast<const bf16_t*>(a.v);
-  constexpr int VPR = D / 8;                              // 16-byte vectors per key row
-  for (int kb0 = kbeg; kb0 < klim; kb0 += kAK) {
-    __syncthreads();
-    for (int idx = tid; idx < kAK * VPR; idx += 256) {
-      const int kr = idx / VPR, vc = idx - kr * VPR;
-      const int key = kb0 + kr;
-      u32x4_t kv4 = {0u, 0u, 0u, 0u}, vv4 = {0u, 0u, 0u, 0u};
-      if (key < klim) {
-        const int64_t off = ((krow0 + key) * hkv + g) * D + vc * 8;
-        kv4 = *reinterpret_cast<const u32x4_t*>(Kg + off);
-        if constexpr (!STATS_ONLY) vv4 = *reinterpret_cast<const u32x4_t*>(Vg + off);
-      }
-      *reinterpret_cast<u32x4_t*>(&Ks[kr][vc * 8]) = kv4;
-      if constexpr (!STATS_ONLY) {
-        const u16x8_t vh = __builtin_bit_cast(u16x8_t, vv4);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) Vs[kr >> 2][vc * 8 + e][kr & 3] = vh[e];
-      }
-    }
-    __syncthreads();
+  // per-request base of this kv head; rows are row_stride elements apart
+  const int64_t row_stride = static_cast<int64_t>(hkv) * D;
+  const bf16_t* Kreq = static_cast<const bf16_t*>(a.k) + krow0 * row_stride + static_cast<int64_t>(g) * D;
+  const bf16_t* Vreq = static_cast<const bf16_t*>(a.v) + krow0 * row_stride + static_cast<int64_t>(g) * D;
+  // this lane's DMA slot: row lane / CPR of each group, physical chunk lane % CPR
+  const int dma_rr = lane / CPR, dma_p = lane % CPR;
 
-    // S^T for two 32-key blocks
+  auto dma_tile = [&](const bf16_t* src_req, bf16_t* dst, int kb0) {
+#pragma unroll
+    for (int j = 0; j < NDMA; ++j) {
+      const int grp = w * NDMA + j;
+      const int row = grp * RPI + dma_rr;
+      const int q = dma_p ^ (row & (CPR - 1));            // logical chunk held by this slot
+      const int key = min(kb0 + row, klim - 1);           // tail rows repeat a valid key
+      const bf16_t* src = src_req + static_cast<int64_t>(key) * row_stride + q * 8;
+      __builtin_amdgcn_global_load_lds((global_cvoid_t*)(src), (lds_void_t*)(dst + grp * RPI * D), 16, 0, 0);
+    }
+  };
+
+  // Softmax state in the log2 domain: scores enter as s * c with
+  // c = sm_scale * log2(e).  The running max m_run is raised only when a
+  // tile's max exceeds it by more than kSlack (then O and l are rescaled);
+  // otherwise probabilities are taken against the old max and may exceed 1
+  // by at most 2^kSlack, which fp32 sums and bf16 operands carry exactly as
+  // well.  The result is the same softmax, with far fewer rescales.
+  constexpr float kSlack = 8.f;
+  const float c_scale = a.scale_log2;
+  const f32x16_t zero16 = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  const bf16x2_t ones2 = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
+  // LDS element offsets of this lane's operand reads, with the XOR swizzle
+  // resolved once: the swizzle term depends only on row mod D/8, which the
+  // 32-key and 16-key block steps (multiples of 16 rows) do not change.
+  // K rows 64 kg + 32 kb + c, channel chunk 2 kk + hf:
+  int koff[KS];
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk)
+    koff[kk] = (64 * kg + c) * D + (((2 * kk + hf) ^ (c & (CPR - 1))) << 3);
+  // transposed V reads: lane i of 16-lane group G reads keys 4 hf + i/4 (+8)
+  // and channels 32 db + 16 (G%2) + 4 (i%4) .. +3
+  const int tr_key = 4 * hf + ((lane & 15) >> 2);
+  const int tr_d = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  int voff[2][DB];
+#pragma unroll
+  for (int hl = 0; hl < 2; ++hl) {
+    const int row = tr_key + 8 * hl;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+      voff[hl][db] = (64 * kg + row) * D + ((((4 * db + (tr_d >> 3)) ^ (row & (CPR - 1)))) << 3) + (tr_d & 7);
+  }
+
+  // One 128-key tile computed from (ks, vs).  MASK selects the variant that
+  // applies the causal and range mask (only the last tiles need it).
+  auto step = [&](const bf16_t* ks_, const bf16_t* vs_, int kb0, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    const int k_half = kb0 + 64 * kg;             // first key of this wave's half
+    if (k_half >= klim) return;                   // wave-uniform
     f32x16_t s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
+      const bf16_t* krow = ks_ + kb * 32 * D;      // + koff: row 64 kg + 32 kb + c
+      const bf16x8_t k0 = *reinterpret_cast<const bf16x8_t*>(krow + koff[0]);
+      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[0], zero16, 0, 0, 0);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8_t kfrag = *reinterpret_cast<const bf16x8_t*>(&Ks[kb * 32 + c][ks * 16 + hf * 8]);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag, qf[ks], s[kb], 0, 0, 0);
+      for (int kk = 1; kk < KS; ++kk) {
+        const bf16x8_t kfrag = *reinterpret_cast<const bf16x8_t*>(krow + koff[kk]);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag, qf[kk], s[kb], 0, 0, 0);
       }
     }
-    // scale, mask, tile max
-    float mx = -INFINITY;
+    if constexpr (MASK) {
+      // key = k_half + 32 kb + 8 (i/4) + 4 hf + (i%4) is visible iff key <= lim
+      const int lim = min(pos, klim - 1) - k_half - 4 * hf;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (kb * 32 + 8 * (i >> 2) + (i & 3) > lim) s[kb][i] = -INFINITY;
+    }
+    float mx = fmaxf(s[0][0], s[0][1]);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = kb0 + kb * 32 + 8 * (i >> 2) + 4 * hf + (i & 3);
-        const float v = (key <= pos && key < klim) ? s[kb][i] * a.scale_log2 : -INFINITY;
-        s[kb][i] = v;
-        mx = fmaxf(mx, v);
+      for (int i = (kb == 0 ? 2 : 0); i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave)) * c_scale;     // tile max, log2 domain
+    if (__builtin_expect(__any(mx > m_run + kSlack), 0)) {
+      asm volatile("; rescale");                  // keeps this rare path a branch
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+      if constexpr (!STATS_ONLY) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
       }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = exp2f(m_run - m_use);
+      m_run = m_new;
+    }
+    const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
     float rs = 0.f;
+    if constexpr (STATS_ONLY) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float p = exp2f(s[kb][i] - m_use);
-        // the V product consumes bf16 probabilities: normalise by the sum of
-        // exactly those values so the weights used sum to one
-        if constexpr (!STATS_ONLY) p = static_cast<float>(static_cast<__bf16>(p));
-        s[kb][i] = p;
-        rs += p;
-      }
-    rs += __shfl_xor(rs, 32, kWave);
-    l_run = l_run * alpha + rs;
-    m_run = m_new;
-
-    if constexpr (!STATS_ONLY) {
+        for (int i = 0; i < 16; ++i) rs += __builtin_amdgcn_exp2f(fmaf(s[kb][i], c_scale, neg_m));
+    } else {
+      uint32_t pk[2][8];                          // bf16 probability pairs
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+        for (int i = 0; i < 8; ++i) {
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][2 * i], c_scale, neg_m));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][2 * i + 1], c_scale, neg_m));
+          pk[kb][i] = pack_bf16x2(p0, p1);
+          // normalise by the sum of the bf16 values the V product consumes
+          rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[kb][i]), ones2, rs, false);
+        }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
-          bf16x8_t pb;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) pb[e] = static_cast<__bf16>(s[kb][8 * st + e]);
-          const int key_a = kb * 32 + 16 * st + 4 * hf;  // keys key_a..+3 and key_a+8..+11
+          const u32x4_t pw = {pk[kb][4 * st], pk[kb][4 * st + 1], pk[kb][4 * st + 2], pk[kb][4 * st + 3]};
+          const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pw);
+          const bf16_t* vblk = vs_ + (kb * 32 + 16 * st) * D;   // + voff: this lane's rows
+          // keep each 16-key group's V reads next to its MFMAs (register pressure)
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int db = 0; db < DB; ++db) {
-            const u16x4_t lo = *reinterpret_cast<const u16x4_t*>(&Vs[key_a >> 2][db * 32 + c][0]);
-            const u16x4_t hi = *reinterpret_cast<const u16x4_t*>(&Vs[(key_a + 8) >> 2][db * 32 + c][0]);
-            const u16x8_t vv = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vblk + voff[0][db]));
+            const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vblk + voff[1][db]));
+            const s16x4_t vv[2] = {lo, hi};
             o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vv), pb,
                                                             o[db], 0, 0, 0);
           }
         }
       }
+    }
+    rs += __shfl_xor(rs, 32, kWave);
+    l_run += rs;
+  };
+
+  const int ntiles = klim > kbeg ? ceil_div(klim - kbeg, kAT) : 0;
+  // leading tiles every row sees completely need no mask
+  int n_plain = 0;
+  if (pmin >= kbeg) n_plain = min(min(ntiles, (pmin + 1 - kbeg) / kAT), (klim - kbeg) / kAT);
+  auto run_tile = [&](int t, const bf16_t* ks_, const bf16_t* vs_) {
+    if (t < n_plain)
+      step(ks_, vs_, kbeg + t * kAT, std::false_type{});
+    else
+      step(ks_, vs_, kbeg + t * kAT, std::true_type{});
+  };
+  if (ntiles > 0) {
+    dma_tile(Kreq, k0s, kbeg);
+    if constexpr (!STATS_ONLY) dma_tile(Vreq, v0s, kbeg);
+  }
+  __syncthreads();                                // waits for the DMA (vmcnt) too
+  // two tiles per trip so every buffer is a distinct static array
+  for (int t = 0; t < ntiles; t += 2) {
+    if (t + 1 < ntiles) {
+      dma_tile(Kreq, k1s, kbeg + (t + 1) * kAT);
+      if constexpr (!STATS_ONLY) dma_tile(Vreq, v1s, kbeg + (t + 1) * kAT);
+    }
+    run_tile(t, k0s, v0s);
+    __syncthreads();
+    if (t + 1 >= ntiles) break;
+    if (t + 2 < ntiles) {
+      dma_tile(Kreq, k0s, kbeg + (t + 2) * kAT);
+      if constexpr (!STATS_ONLY) dma_tile(Vreq, v0s, kbeg + (t + 2) * kAT);
+    }
+    run_tile(t + 1, k1s, v1s);
+    __syncthreads();
+  }
+
+  // merge the two key halves: waves 4..7 hand (m, l, O) to waves 0..3
+  const int slot = qg * 64 + lane;
+  float* xo0 = reinterpret_cast<float*>(k0s);     // O blocks [0, DB/2)
+  float* xo1 = reinterpret_cast<float*>(k1s);     // O blocks [DB/2, DB)
+  float* xml = STATS_ONLY ? reinterpret_cast<float*>(k1s) : reinterpret_cast<float*>(v0s);
+  constexpr int HO = 8 * DB;                      // floats per lane in each O half
+  if (kg == 1) {
+    xml[2 * slot] = m_run;
+    xml[2 * slot + 1] = l_run;
+    if constexpr (!STATS_ONLY) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float* dstp = db < DB / 2 ? xo0 : xo1;
+          dstp[slot * HO + (db % (DB / 2)) * 16 + i] = o[db][i];
+        }
+    }
+  }
+  __syncthreads();
+  if (kg == 1) return;
+  {
+    const float m2 = xml[2 * slot];
+    const float l2 = xml[2 * slot + 1];
+    const float mm = fmaxf(m_run, m2);
+    const float mu = mm == -INFINITY ? 0.f : mm;
+    const float a1 = __builtin_amdgcn_exp2f(m_run - mu), a2 = __builtin_amdgcn_exp2f(m2 - mu);
+    l_run = l_run * a1 + l2 * a2;
+    m_run = mm;
+    if constexpr (!STATS_ONLY) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float* srcp = db < DB / 2 ? xo0 : xo1;
+          o[db][i] = o[db][i] * a1 + srcp[slot * HO + (db % (DB / 2)) * 16 + i] * a2;
+        }
     }
   }
 
@@ -241,13 +393,19 @@ __global__ void __launch_bounds__(256) attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int d0 = db * 32 + 8 * i + 4 * hf;
-        u32x2_t pk;
-        pk[0] = pack_bf16x2(o[db][4 * i] * inv, o[db][4 * i + 1] * inv);
-        pk[1] = pack_bf16x2(o[db][4 * i + 2] * inv, o[db][4 * i + 3] * inv);
-        *reinterpret_cast<u32x2_t*>(O + d0) = pk;
+        u32x2_t pk2;
+        pk2[0] = pack_bf16x2(o[db][4 * i] * inv, o[db][4 * i + 1] * inv);
+        pk2[1] = pack_bf16x2(o[db][4 * i + 2] * inv, o[db][4 * i + 3] * inv);
+        *reinterpret_cast<u32x2_t*>(O + d0) = pk2;
       }
     if (a.lse && hf == 0) a.lse[orow * a.hq + h] = (m_run + log2f(l_run)) * kLn2;
   }
+}
+
+template <int D, bool STATS_ONLY>
+static hipError_t launch_attn_bf16(const AttnArgs& a, dim3 grid, hipStream_t st) {
+  hipLaunchKernelGGL((attn_bf16_kernel<D, STATS_ONLY>), grid, dim3(kAThreads), 0, st, a);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
@@ -361,10 +519,9 @@ hipError_t launch_attention(const kvf_layer_desc& L, const BatchArgs& B, const v
     const int64_t blocks = static_cast<int64_t>(a.total_tiles) * a.hkv;
     if (blocks == 0) return hipSuccess;
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-    if (L.head_dim == 128)
-      hipLaunchKernelGGL((attn_bf16_kernel<128, false>), dim3(blocks), dim3(256), 0, st, a);
-    else
-      hipLaunchKernelGGL((attn_bf16_kernel<64, false>), dim3(blocks), dim3(256), 0, st, a);
+    const hipError_t e = L.head_dim == 128 ? launch_attn_bf16<128, false>(a, dim3(blocks), st)
+                                           : launch_attn_bf16<64, false>(a, dim3(blocks), st);
+    if (e != hipSuccess) return e;
   } else {
     const int total_rows = cu_q[B.n_req];
     const int64_t waves = static_cast<int64_t>(total_rows) * a.hq;
@@ -377,22 +534,20 @@ hipError_t launch_attention(const kvf_layer_desc& L, const BatchArgs& B, const v
 // ---------------------------------------------------------------------------
 // attention mass
 // ---------------------------------------------------------------------------
-// combine split statistics into log2-domain LSE per (row, head)
+// combine split statistics into log2-domain LSE per (row, head): one wave per
+// entry, one lane per split (n_splits <= 64)
 __global__ void __launch_bounds__(256) lse_combine_kernel(const float* __restrict__ pm,
                                                           const float* __restrict__ pl, int n_splits,
                                                           int64_t plane, int64_t n,
                                                           float* __restrict__ lse2) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t i = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
   if (i >= n) return;
-  float m = -INFINITY;
-  for (int s = 0; s < n_splits; ++s) m = fmaxf(m, pm[s * plane + i]);
-  float l = 0.f;
-  if (m > -INFINITY)
-    for (int s = 0; s < n_splits; ++s) {
-      const float ms = pm[s * plane + i];
-      if (ms > -INFINITY) l += pl[s * plane + i] * exp2f(ms - m);
-    }
-  lse2[i] = l > 0.f ? m + log2f(l) : INFINITY;     // INFINITY: row contributes nothing
+  const float ms = lane < n_splits ? pm[lane * plane + i] : -INFINITY;
+  const float ls = lane < n_splits ? pl[lane * plane + i] : 0.f;
+  const float m = wave_max(ms);
+  const float l = wave_sum(ms > -INFINITY ? ls * exp2f(ms - m) : 0.f);
+  if (lane == 0) lse2[i] = l > 0.f ? m + log2f(l) : INFINITY;     // INFINITY: contributes nothing
 }
 
 struct MassArgs {
@@ -544,10 +699,10 @@ MassLayout mass_layout(const kvf_layer_desc& L, const BatchArgs& B, int n_last_q
   // enough workgroups in the statistics pass to cover the chip twice
   const int64_t base = std::max<int64_t>(1, L.dtype == KVF_BF16 ? tiles * L.n_kv_heads
                                                                 : m.rows * L.n_q_heads / 4);
-  const int key_tiles = std::max(1, ceil_div(max_T, kAK));
+  const int key_tiles = std::max(1, ceil_div(max_T, kAT));
   int splits = static_cast<int>(std::min<int64_t>(key_tiles, ceil_div(512, static_cast<int>(std::min<int64_t>(base, 512)))));
   splits = std::max(1, std::min(splits, 64));
-  m.split_keys = ceil_div(key_tiles, splits) * kAK;
+  m.split_keys = ceil_div(key_tiles, splits) * kAT;
   m.n_splits = ceil_div(std::max(max_T, 1), m.split_keys);
   const int64_t plane = m.rows * L.n_q_heads;
   auto align = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
@@ -608,10 +763,9 @@ hipError_t launch_attn_mass(const kvf_layer_desc& L, const BatchArgs& B, const v
     if (L.dtype == KVF_BF16) {
       fill_tiles(a, rows_per_tile(G));
       const dim3 grid(a.total_tiles * a.hkv, lay.n_splits);
-      if (L.head_dim == 128)
-        hipLaunchKernelGGL((attn_bf16_kernel<128, true>), grid, dim3(256), 0, st, a);
-      else
-        hipLaunchKernelGGL((attn_bf16_kernel<64, true>), grid, dim3(256), 0, st, a);
+      const hipError_t e1 = L.head_dim == 128 ? launch_attn_bf16<128, true>(a, grid, st)
+                                              : launch_attn_bf16<64, true>(a, grid, st);
+      if (e1 != hipSuccess) return e1;
     } else {
       const dim3 grid(ceil_div(static_cast<int>(plane), 4), lay.n_splits);
       hipLaunchKernelGGL((attn_f32_kernel<true>), grid, dim3(256), 0, st, a, L.head_dim,
@@ -619,8 +773,8 @@ hipError_t launch_attn_mass(const kvf_layer_desc& L, const BatchArgs& B, const v
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(lse_combine_kernel, dim3(ceil_div(static_cast<int>(plane), 256)), dim3(256),
-                       0, st, pm, pl, lay.n_splits, plane, plane, lse2);
+    hipLaunchKernelGGL(lse_combine_kernel, dim3(ceil_div(static_cast<int>(plane), 256 / kWave)),
+                       dim3(256), 0, st, pm, pl, lay.n_splits, plane, plane, lse2);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
