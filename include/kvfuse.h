@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define KVF_ABI_VERSION 1
+#define KVF_ABI_VERSION 2
 #define KVF_MAX_REQ 64      /* requests per call (batch metadata is passed by value) */
 
 typedef enum {
@@ -208,16 +208,24 @@ size_t kvf_select_workspace_size(const kvf_batch* batch);
  *   v_out[m] =      x[r] Wv^T   (if out_mask & KVF_OUT_V)   [M, Hkv, d]
  * x: [x_rows, hidden]; w_qkv: [(Hq + 2 Hkv) d, hidden] = [Wq; Wk; Wv].
  * row_src may be NULL (identity, requires M <= x_rows).  fp32 accumulation.
+ * A row whose row_src entry is outside [0, x_rows) or (for Q/K) whose
+ * position is outside the rope table is left unwritten.
  * The same call builds per-chunk caches ahead of serving ([QCF] 2.1.2 Eq. 3):
  * pass the cached hidden states with chunk-local positions and mask K|V.
+ * workspace: kvf_recompute_workspace_size(layer, M, out_mask) bytes of
+ * device memory (may be NULL when that is 0); calls with few rows use it for
+ * per-slice partial sums, so two calls sharing one workspace must be ordered.
  */
+size_t kvf_recompute_workspace_size(const kvf_layer_desc* layer, int32_t M,
+                                    uint32_t out_mask);
 kvf_status kvf_recompute_qkv(const kvf_layer_desc* layer, const void* x,
                              int64_t x_rows, const int32_t* row_src,
                              const int32_t* row_pos, int32_t M,
                              const void* w_qkv, uint32_t out_mask,
                              const float* rope_cos, const float* rope_sin,
                              int32_t rope_n_pos, void* q_out, void* k_out,
-                             void* v_out, void* stream);
+                             void* v_out, void* workspace,
+                             size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * kvf_scatter_kv - S5: KV^Fuse_p = KV^New_p for the recomputed rows

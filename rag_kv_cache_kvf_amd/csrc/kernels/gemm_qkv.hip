@@ -6,19 +6,21 @@
 // queries and keys carry the rotation of their position.
 //
 // bf16 path: Y[m, n] = sum_k X[row_src[m], k] W[n, k] on MFMA
-// (v_mfma_f32_32x32x16_bf16, fp32 accumulate).  Workgroup tile 128 x 128 x 64,
-// 4 waves in a 2 x 2 layout, double-buffered LDS, one barrier per K step.
-// Rows of X are gathered through row_src while they are staged (each row
-// slice is a contiguous 128-byte read).  Each wave owns two 32-column groups
-// that are RoPE partners (channel j and j + d/2 of the same head), so the
-// rotation is applied in registers on the accumulators.  Only the column
-// tiles of the requested outputs (Q, K, V mask) are launched.
+// (v_mfma_f32_32x32x16_bf16, fp32 accumulate); tiling and staging are
+// described at the kernel.  Only the column tiles of the requested outputs
+// (Q, K, V mask) are launched.
 //
 // fp32 path: a plain LDS-tiled FMA kernel (the fp32 workloads are small
 // correctness shapes; MFMA is reserved for the bf16 contractions).
+#include <climits>
+#include <type_traits>
+
 #include "../kvf_common.h"
 
 namespace kvf {
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) const void global_cvoid_t;
 
 struct GemmArgs {
   const void* x;
@@ -36,7 +38,22 @@ struct GemmArgs {
   int seg_heads[3];         // heads of each segment
   int seg_w_row0[3];        // first weight row of each segment
   void* out[3];
+  // split-K: blockIdx.z covers K range [z k_len, (z+1) k_len) and writes raw
+  // fp32 sums to partial[z][m][c] (c = weight row, c_total columns); a
+  // second kernel adds the slices, rotates and stores.  partial == nullptr:
+  // one slice, the kernel finishes the rows itself.
+  float* partial;
+  int k_len;
+  int c_total;
 };
+
+// Row m is computed and stored only if its source row and (for Q/K) its
+// position are inside the tables.
+__device__ __forceinline__ bool row_ok(const GemmArgs& a, int m) {
+  if (!a.row_src) return true;
+  const int s = a.row_src[m];
+  return s >= 0 && s < a.x_rows;
+}
 
 __device__ __forceinline__ int segment_of(const int (&n_tiles)[3], int& t) {
   int seg = 0;
@@ -50,129 +67,334 @@ __device__ __forceinline__ int segment_of(const int (&n_tiles)[3], int& t) {
 // ---------------------------------------------------------------------------
 // bf16 MFMA kernel
 // ---------------------------------------------------------------------------
-constexpr int kBM = 128, kBN = 128, kBK = 64, kPadK = 8, kLdK = kBK + kPadK;
+// Workgroup tile BM x BN x 64 (BM a multiple of 32, BN 128 or 256, chosen per
+// call so the tile count fills the chip in whole rounds); 4 waves, wave w owns
+// output columns [w BN/4, (w+1) BN/4) for all BM rows (BM/32 x BN/128
+// accumulators of 32 x 32).
+// Operand tiles stream global -> LDS through the DMA path (16 bytes per lane,
+// rows of X gathered through row_src by each lane's own source address) into
+// a ring of 3-4 static stage buffers, so the next stages load while one
+// computes.  Rows are 64 bf16 (8 chunks of 16 B) with chunks XOR-swizzled by
+// row mod 8.  Few-row calls split K over blockIdx.z (see GemmArgs).
+// Epilogue: 32 rows at a time go through LDS as fp32, where each thread
+// takes 8 channels j.. of a head together with their RoPE partners j+d/2..,
+// rotates them at the row's position and writes both as 16-byte bf16 stores.
+constexpr int kBK = 64, kGThreads = 256;
 
-__global__ void __launch_bounds__(256) gemm_qkv_bf16_kernel(GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) bf16_t As[2][kBM][kLdK];
-  __shared__ __attribute__((aligned(16))) bf16_t Bs[2][kBN][kLdK];
+template <int BM, int BN>
+struct GemmTile {
+  static constexpr int kA = BM * kBK;       // elements of an A stage
+  static constexpr int kB = BN * kBK;       // elements of a B stage
+  // stages in flight: as many as 160 KB of LDS holds, at most 4
+  static constexpr int kStages =
+      (kA + kB) * 2 * 4 <= 160 * 1024 ? 4 : ((kA + kB) * 2 * 3 <= 160 * 1024 ? 3 : 2);
+};
+
+__device__ __forceinline__ int gswz(int row, int chunk) {   // element offset of a 16-B chunk
+  return row * kBK + ((chunk ^ (row & 7)) << 3);
+}
+
+// One 16-byte-per-lane global -> LDS copy (the DMA path).  Issued from inline
+// assembly so the copies are invisible to the compiler's wait-count tracking:
+// their completion is awaited explicitly by dma_wait_barrier, which lets
+// stages k+1.. stay in flight while stage k is read.  lds_base must be
+// wave-uniform; lane l writes lds_base + 16 l.
+__device__ __forceinline__ void dma16(const void* src, const void* lds_base) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds_base)));
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(src)
+               : "memory");
+}
+
+// Wait until at most N of this wave's DMA copies are in flight, then meet
+// the other waves: every wave's part of the stage has landed in LDS.  The
+// workgroup fence of __syncthreads() would wait for all copies instead.
+template <int N>
+__device__ __forceinline__ void dma_wait_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"i"(N) : "memory");
+}
+
+template <int BM, int BN>
+__global__ void __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+gemm_qkv_bf16_kernel(GemmArgs a) {
+  constexpr int MB = BM / 32;               // 32-row MFMA blocks
+  constexpr int NI = BN / 128;              // 32-column MFMA blocks per wave
+  constexpr int AG = BM / 8;                // DMA groups (8 rows) of an A stage
+  constexpr int BG = BN / 8;                // DMA groups of a B stage
+  constexpr int AGW = AG / 4;               // A groups per wave (BM is a multiple of 32)
+  constexpr int BGW = BG / 4;
+  constexpr int PER = AGW + BGW;            // DMA instructions per wave per stage
+  constexpr int NST = GemmTile<BM, BN>::kStages;
+  static_assert(NST >= 3, "the ring below needs three stages");
+  constexpr int SA = GemmTile<BM, BN>::kA, SB = GemmTile<BM, BN>::kB;
+  __shared__ __attribute__((aligned(16))) bf16_t a0s[SA];
+  __shared__ __attribute__((aligned(16))) bf16_t a1s[SA];
+  __shared__ __attribute__((aligned(16))) bf16_t a2s[SA];
+  __shared__ __attribute__((aligned(16))) bf16_t a3s[NST > 3 ? SA : 8];
+  __shared__ __attribute__((aligned(16))) bf16_t b0s[SB];
+  __shared__ __attribute__((aligned(16))) bf16_t b1s[SB];
+  __shared__ __attribute__((aligned(16))) bf16_t b2s[SB];
+  __shared__ __attribute__((aligned(16))) bf16_t b3s[NST > 3 ? SB : 8];
+  auto abuf = [&](auto i) -> bf16_t* {
+    constexpr int I = decltype(i)::value;
+    if constexpr (I == 0) return a0s; else if constexpr (I == 1) return a1s;
+    else if constexpr (I == 2) return a2s; else return a3s;
+  };
+  auto bbuf = [&](auto i) -> bf16_t* {
+    constexpr int I = decltype(i)::value;
+    if constexpr (I == 0) return b0s; else if constexpr (I == 1) return b1s;
+    else if constexpr (I == 2) return b2s; else return b3s;
+  };
 
   int t = blockIdx.y;
   const int seg = segment_of(a.n_tiles, t);
-  const int n0 = t * kBN;                       // first column inside the segment
-  const int m0 = blockIdx.x * kBM;
+  const int n0 = t * BN;                    // first column inside the segment
+  const int m0 = blockIdx.x * BM;
   const int K = a.K;
-  const bf16_t* X = static_cast<const bf16_t*>(a.x);
-  const bf16_t* W = static_cast<const bf16_t*>(a.w) + static_cast<int64_t>(a.seg_w_row0[seg] + n0) * K;
+  const int kz0 = blockIdx.z * a.k_len;     // first k of this slice
+  const bf16_t* X = static_cast<const bf16_t*>(a.x) + kz0;
+  const bf16_t* W = static_cast<const bf16_t*>(a.w) + static_cast<int64_t>(a.seg_w_row0[seg] + n0) * K + kz0;
 
-  const int tid = threadIdx.x;
-  const int lr = tid >> 3;                      // 0..31
-  const int lk = (tid & 7) * 8;                 // 0..56
-  const bf16_t* aptr[4];
-  bool aval[4];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // DMA slots: lane -> (row lane/8 of a group, physical chunk lane%8)
+  const int drow = lane >> 3, dchunk = lane & 7;
+  const bf16_t* asrc[AGW];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int m = m0 + lr + 32 * i;
-    int64_t src = -1;
-    if (m < a.M) src = a.row_src ? static_cast<int64_t>(a.row_src[m]) : m;
-    aval[i] = src >= 0 && src < a.x_rows;
-    aptr[i] = X + (aval[i] ? src : 0) * K + lk;
+  for (int i = 0; i < AGW; ++i) {
+    const int row = (w + 4 * i) * 8 + drow;
+    const int m = m0 + row;
+    int64_t src = 0;
+    if (m < a.M) {
+      src = a.row_src ? static_cast<int64_t>(a.row_src[m]) : m;
+      if (src < 0 || src >= a.x_rows) src = 0;     // row skipped at the store
+    }
+    asrc[i] = X + src * K + ((dchunk ^ (row & 7)) << 3);
   }
-  const bf16_t* bptr = W + static_cast<int64_t>(lr) * K + lk;
-
-  u32x4_t ra[4], rb[4];
-  const u32x4_t zero4 = {0u, 0u, 0u, 0u};
+  const bf16_t* bsrc[BGW];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    ra[i] = aval[i] ? *reinterpret_cast<const u32x4_t*>(aptr[i]) : zero4;
-    rb[i] = *reinterpret_cast<const u32x4_t*>(bptr + static_cast<int64_t>(32 * i) * K);
+  for (int i = 0; i < BGW; ++i) {
+    const int row = (w + 4 * i) * 8 + drow;
+    bsrc[i] = W + static_cast<int64_t>(row) * K + ((dchunk ^ (row & 7)) << 3);
   }
+  auto dma_stage = [&](bf16_t* as, bf16_t* bs, int k0) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    *reinterpret_cast<u32x4_t*>(&As[0][lr + 32 * i][lk]) = ra[i];
-    *reinterpret_cast<u32x4_t*>(&Bs[0][lr + 32 * i][lk]) = rb[i];
+    for (int i = 0; i < AGW; ++i) dma16(asrc[i] + k0, as + (w + 4 * i) * 8 * kBK);
+#pragma unroll
+    for (int i = 0; i < BGW; ++i) dma16(bsrc[i] + k0, bs + (w + 4 * i) * 8 * kBK);
+  };
+
+  // operand read offsets (the swizzle depends on row mod 8 = lane mod 8)
+  const int lr = lane & 31, hf = lane >> 5;
+  int aoff[kBK / 16], boff[kBK / 16];
+#pragma unroll
+  for (int kk = 0; kk < kBK / 16; ++kk) {
+    aoff[kk] = gswz(lr, 2 * kk + hf);
+    boff[kk] = gswz(32 * NI * w + lr, 2 * kk + hf);   // + 32 ni rows
   }
-  __syncthreads();
 
-  const int w = tid >> 6, lane = tid & 63;
-  const int wm = w >> 1, wn = w & 1;
-  const int hg = a.d / 64;                      // 32-column groups per half head
-  const int ga = (wn % hg) + (wn / hg) * 2 * hg;
-  const int gb = ga + hg;
-  const int lrow = lane & 31, lk8 = (lane >> 5) * 8;
-
-  f32x16_t acc[2][2];
+  f32x16_t acc[MB][NI];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < MB; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < NI; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  const int nk = K / kBK;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      const int64_t ko = static_cast<int64_t>(kt + 1) * kBK;
+  // operand fragments of k-step kk+1 are read while the MFMAs of kk run
+  auto compute = [&](const bf16_t* as, const bf16_t* bs) {
+    constexpr int KK = kBK / 16;
+    bf16x8_t af[2][MB], bfr[2][NI];
+    auto load_frags = [&](int slot, int kk) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        ra[i] = aval[i] ? *reinterpret_cast<const u32x4_t*>(aptr[i] + ko) : zero4;
-        rb[i] = *reinterpret_cast<const u32x4_t*>(bptr + static_cast<int64_t>(32 * i) * K + ko);
-      }
+      for (int ni = 0; ni < NI; ++ni)
+        bfr[slot][ni] = *reinterpret_cast<const bf16x8_t*>(bs + ni * 32 * kBK + boff[kk]);
+#pragma unroll
+      for (int mi = 0; mi < MB; ++mi)
+        af[slot][mi] = *reinterpret_cast<const bf16x8_t*>(as + mi * 32 * kBK + aoff[kk]);
+    };
+    load_frags(0, 0);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const int cur = kk & 1;
+      if (kk + 1 < KK) load_frags(cur ^ 1, kk + 1);
+#pragma unroll
+      for (int mi = 0; mi < MB; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][mi], bfr[cur][ni], acc[mi][ni], 0, 0, 0);
     }
+    // instruction order for the scheduler: fragments of k-step 0, then for
+    // each k-step the reads of the next one ahead of its own MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, MB + NI, 0);
 #pragma unroll
-    for (int kk = 0; kk < kBK / 16; ++kk) {
-      bf16x8_t af[2], bfr[2];
-#pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
-        af[mi] = *reinterpret_cast<const bf16x8_t*>(&As[cur][wm * 64 + mi * 32 + lrow][kk * 16 + lk8]);
-      bfr[0] = *reinterpret_cast<const bf16x8_t*>(&Bs[cur][ga * 32 + lrow][kk * 16 + lk8]);
-      bfr[1] = *reinterpret_cast<const bf16x8_t*>(&Bs[cur][gb * 32 + lrow][kk * 16 + lk8]);
-#pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < 2; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
+    for (int kk = 0; kk < KK; ++kk) {
+      if (kk + 1 < KK) __builtin_amdgcn_sched_group_barrier(0x100, MB + NI, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, MB * NI, 0);
     }
-    if (more) {
+  };
+
+  // Ring of NST stage buffers.  Stage k lives in buffer k % NST.  At stage k:
+  // wait for its copies and meet (which also means every wave is done with
+  // stage k-1), refill buffer (k-1) % NST with stage k+NST-1, compute k.
+  const int nk = a.k_len / kBK;
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  dma_stage(abuf(I0{}), bbuf(I0{}), 0);
+  if (1 < nk) dma_stage(abuf(I1{}), bbuf(I1{}), kBK);
+  if (NST > 3 && 2 < nk) dma_stage(abuf(I2{}), bbuf(I2{}), 2 * kBK);
+  auto stage = [&](int k, auto cur, auto prev) {
+    // copies issued after stage k: stages k+1 .. min(k+NST-2, nk-1)
+    if (k + NST - 2 < nk) dma_wait_barrier<(NST - 2) * PER>();
+    else if (NST > 3 && k + 1 < nk) dma_wait_barrier<PER>();
+    else dma_wait_barrier<0>();
+    if (k + NST - 1 < nk) dma_stage(abuf(prev), bbuf(prev), (k + NST - 1) * kBK);
+    compute(abuf(cur), bbuf(cur));
+  };
+  for (int kt = 0; kt < nk; kt += NST) {
+    if constexpr (NST == 4) {
+      stage(kt, I0{}, I3{});
+      if (kt + 1 < nk) stage(kt + 1, I1{}, I0{});
+      if (kt + 2 < nk) stage(kt + 2, I2{}, I1{});
+      if (kt + 3 < nk) stage(kt + 3, I3{}, I2{});
+    } else {
+      stage(kt, I0{}, I2{});
+      if (kt + 1 < nk) stage(kt + 1, I1{}, I0{});
+      if (kt + 2 < nk) stage(kt + 2, I2{}, I1{});
+    }
+  }
+  if (a.partial) {
+    // raw slice sums; each 32-lane run stores 128 contiguous bytes of a row
+    float* part = a.partial + static_cast<int64_t>(blockIdx.z) * a.M * a.c_total;
+    const int c0 = a.seg_w_row0[seg] + n0 + 32 * NI * w + lr;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        *reinterpret_cast<u32x4_t*>(&As[cur ^ 1][lr + 32 * i][lk]) = ra[i];
-        *reinterpret_cast<u32x4_t*>(&Bs[cur ^ 1][lr + 32 * i][lk]) = rb[i];
+    for (int mi = 0; mi < MB; ++mi)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + mi * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+        if (m >= a.M) continue;
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni)
+          part[static_cast<int64_t>(m) * a.c_total + c0 + 32 * ni] = acc[mi][ni][r];
       }
+    return;
+  }
+  __syncthreads();
+
+  // epilogue through LDS, 32 rows at a time (b0s holds 32 x BN fp32)
+  float* ep = reinterpret_cast<float*>(b0s);
+  auto eidx = [](int row, int col) {        // fp32 element index, 16-B chunks swizzled
+    return row * BN + ((((col >> 2) ^ (row & 31))) << 2) + (col & 3);
+  };
+  const bool rope = seg < 2;
+  const int d = a.d, half = d >> 1;
+  const int ld = a.seg_heads[seg] * d;
+  bf16_t* out = static_cast<bf16_t*>(a.out[seg]);
+#pragma unroll
+  for (int mi = 0; mi < MB; ++mi) {
+    if (m0 + mi * 32 >= a.M) break;         // block-uniform
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = 8 * (r >> 2) + 4 * hf + (r & 3);
+        ep[eidx(row, 32 * NI * w + 32 * ni + lr)] = acc[mi][ni][r];
+      }
+    __syncthreads();
+    // 32 rows x (BN / 16) units: unit = 8 low channels + their partners
+    for (int u = tid; u < 32 * (BN / 16); u += kGThreads) {
+      const int row = u / (BN / 16);
+      const int p = u % (BN / 16);          // which 8-wide low-half chunk of the tile
+      const int head = p / (half / 8);      // head inside the tile
+      const int j0 = (p % (half / 8)) * 8;  // channel inside the head's low half
+      const int cl = head * d + j0, ch = cl + half;
+      const int m = m0 + mi * 32 + row;
+      if (m >= a.M || !row_ok(a, m)) continue;
+      float lo[8], hi[8];
+#pragma unroll
+      for (int hpart = 0; hpart < 2; ++hpart) {
+        const float4 l4 = *reinterpret_cast<const float4*>(&ep[eidx(row, cl + 4 * hpart)]);
+        const float4 h4 = *reinterpret_cast<const float4*>(&ep[eidx(row, ch + 4 * hpart)]);
+        lo[4 * hpart] = l4.x; lo[4 * hpart + 1] = l4.y; lo[4 * hpart + 2] = l4.z; lo[4 * hpart + 3] = l4.w;
+        hi[4 * hpart] = h4.x; hi[4 * hpart + 1] = h4.y; hi[4 * hpart + 2] = h4.z; hi[4 * hpart + 3] = h4.w;
+      }
+      if (rope) {
+        const int pos = a.row_pos[m];
+        if (pos < 0 || pos >= a.rope_n) continue;
+        float cs[8], sn[8];
+        Elem<float>::load8(a.rope_cos + static_cast<int64_t>(pos) * half + j0, cs);
+        Elem<float>::load8(a.rope_sin + static_cast<int64_t>(pos) * half + j0, sn);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x = lo[e], y = hi[e];
+          lo[e] = x * cs[e] - y * sn[e];
+          hi[e] = y * cs[e] + x * sn[e];
+        }
+      }
+      bf16_t* orow = out + static_cast<int64_t>(m) * ld + n0;
+      Elem<bf16_t>::store8(orow + cl, lo);
+      Elem<bf16_t>::store8(orow + ch, hi);
     }
     __syncthreads();
   }
+}
 
-  // epilogue: rotate (Q, K) and store bf16
-  const bool rope = seg < 2;
-  const int half = a.d >> 1;
-  const int ld = a.seg_heads[seg] * a.d;
-  bf16_t* out = static_cast<bf16_t*>(a.out[seg]);
-  const int ca = n0 + ga * 32 + lrow;
-  const int cb = n0 + gb * 32 + lrow;
-  const int j = ca % a.d;                       // < d/2 by construction
-#pragma unroll
-  for (int mi = 0; mi < 2; ++mi) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = m0 + wm * 64 + mi * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-      if (row >= a.M) continue;
-      float va = acc[mi][0][r], vb = acc[mi][1][r];
-      if (rope) {
-        const int p = a.row_pos[row];
-        if (p < 0 || p >= a.rope_n) continue;
-        const float c = a.rope_cos[static_cast<int64_t>(p) * half + j];
-        const float s = a.rope_sin[static_cast<int64_t>(p) * half + j];
-        const float oa = va * c - vb * s;
-        const float ob = vb * c + va * s;
-        va = oa;
-        vb = ob;
-      }
-      out[static_cast<int64_t>(row) * ld + ca] = f32_to_bf16(va);
-      out[static_cast<int64_t>(row) * ld + cb] = f32_to_bf16(vb);
+// ---------------------------------------------------------------------------
+// split-K finish: one thread per (row, 8 low channels of a head): add the
+// K slices of those channels and of their RoPE partners, rotate, store bf16.
+// units_q / units_k / units_v: such units per row in each requested segment.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) gemm_split_finish_kernel(GemmArgs a, int splits,
+                                                                int units_q, int units_k,
+                                                                int units_v) {
+  const int upr = units_q + units_k + units_v;
+  const int64_t u = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (u >= static_cast<int64_t>(a.M) * upr) return;
+  const int m = static_cast<int>(u / upr);
+  int r = static_cast<int>(u % upr);
+  int seg = 0;
+  if (r >= units_q) {
+    r -= units_q;
+    seg = 1;
+    if (r >= units_k) {
+      r -= units_k;
+      seg = 2;
     }
   }
+  if (!row_ok(a, m)) return;
+  const int d = a.d, half = d >> 1;
+  const int head = r / (half / 8), j0 = (r % (half / 8)) * 8;
+  const int cl = head * d + j0, ch = cl + half;
+  float lo[8] = {0, 0, 0, 0, 0, 0, 0, 0}, hi[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  const int64_t slice = static_cast<int64_t>(a.M) * a.c_total;
+  const float* p = a.partial + static_cast<int64_t>(m) * a.c_total + a.seg_w_row0[seg];
+  for (int z = 0; z < splits; ++z, p += slice) {
+    float t[8];
+    Elem<float>::load8(p + cl, t);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) lo[e] += t[e];
+    Elem<float>::load8(p + ch, t);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) hi[e] += t[e];
+  }
+  if (seg < 2) {
+    const int pos = a.row_pos[m];
+    if (pos < 0 || pos >= a.rope_n) return;
+    float cs[8], sn[8];
+    Elem<float>::load8(a.rope_cos + static_cast<int64_t>(pos) * half + j0, cs);
+    Elem<float>::load8(a.rope_sin + static_cast<int64_t>(pos) * half + j0, sn);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float x = lo[e], y = hi[e];
+      lo[e] = x * cs[e] - y * sn[e];
+      hi[e] = y * cs[e] + x * sn[e];
+    }
+  }
+  bf16_t* orow = static_cast<bf16_t*>(a.out[seg]) + static_cast<int64_t>(m) * a.seg_heads[seg] * d;
+  Elem<bf16_t>::store8(orow + cl, lo);
+  Elem<bf16_t>::store8(orow + ch, hi);
 }
 
 // ---------------------------------------------------------------------------
@@ -252,7 +474,7 @@ __global__ void __launch_bounds__(256) gemm_qkv_f32_kernel(GemmArgs a, int pair_
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int row = m0 + rg + 4 * i;
-    if (row >= a.M) continue;
+    if (row >= a.M || !row_ok(a, row)) continue;
     float lo = alo[i], hi = ahi[i];
     if (seg < 2) {
       const int pos = a.row_pos[row];
@@ -268,10 +490,69 @@ __global__ void __launch_bounds__(256) gemm_qkv_f32_kernel(GemmArgs a, int pair_
   }
 }
 
+namespace {
+
+struct Bf16Plan {
+  int bm, bn, splits;
+  int n_tiles[3];           // column tiles per segment at bn
+};
+
+// Tile shape of a bf16 call.  Column tile 256 when every requested segment
+// is a multiple of it; row-tile height the candidate whose tiles fill 256 CUs
+// with the least per-CU work (rounds x tile area, ties to the larger tile).
+// A call with too few tiles for half the chip (few rows) splits K instead:
+// 64 or 128-row tiles, K cut into 2^j slices of >= 256 until about two tiles
+// per CU, the slices added by gemm_split_finish_kernel.
+Bf16Plan plan_bf16(const kvf_layer_desc& L, int M, uint32_t mask) {
+  const int heads[3] = {L.n_q_heads, L.n_kv_heads, L.n_kv_heads};
+  const uint32_t bits[3] = {KVF_OUT_Q, KVF_OUT_K, KVF_OUT_V};
+  auto tiles = [&](int bn, int* per) {
+    int total = 0;
+    for (int s = 0; s < 3; ++s) {
+      const int cols = heads[s] * L.head_dim;
+      const int t = (mask & bits[s]) ? cols / bn : 0;
+      if (per) per[s] = t;
+      total += t;
+    }
+    return total;
+  };
+  Bf16Plan p{128, 256, 1, {0, 0, 0}};
+  for (int s = 0; s < 3; ++s)
+    if ((mask & bits[s]) && (heads[s] * L.head_dim) % 256 != 0) p.bn = 128;
+  const int total = tiles(p.bn, p.n_tiles);
+  int64_t best_cost = INT64_MAX;
+  for (int bm : {256, 192, 160, 128}) {
+    if (p.bn == 256 && bm > 160) continue;      // fewer than 3 stages fit in LDS
+    const int64_t blocks = static_cast<int64_t>(ceil_div(M, bm)) * total;
+    const int64_t cost = (blocks + 255) / 256 * bm;
+    if (cost < best_cost) {
+      best_cost = cost;
+      p.bm = bm;
+    }
+  }
+  if (static_cast<int64_t>(ceil_div(M, p.bm)) * total >= 128) return p;
+  Bf16Plan q{M <= 64 ? 64 : 128, 128, 1, {0, 0, 0}};
+  const int64_t base = static_cast<int64_t>(ceil_div(M, q.bm)) * tiles(128, q.n_tiles);
+  while (base * q.splits * 2 <= 512 && L.hidden % (q.splits * 2 * kBK) == 0 &&
+         L.hidden / (q.splits * 2) >= 256)
+    q.splits *= 2;
+  return q.splits > 1 ? q : p;
+}
+
+}  // namespace
+
+size_t recompute_workspace(const kvf_layer_desc& L, int M, uint32_t mask) {
+  if (L.dtype != KVF_BF16 || M <= 0 || mask == 0) return 0;
+  const Bf16Plan p = plan_bf16(L, M, mask);
+  if (p.splits == 1) return 0;
+  const int64_t c_total = static_cast<int64_t>(L.n_q_heads + 2 * L.n_kv_heads) * L.head_dim;
+  return static_cast<size_t>(p.splits) * M * c_total * sizeof(float);
+}
+
 hipError_t launch_recompute(const kvf_layer_desc& L, const void* x, int64_t x_rows,
                             const int32_t* row_src, const int32_t* row_pos, int M, const void* w,
                             uint32_t mask, const float* rc, const float* rs, int rope_n, void* q,
-                            void* k, void* v, hipStream_t st) {
+                            void* k, void* v, void* ws, size_t ws_bytes, hipStream_t st) {
   GemmArgs a{};
   a.x = x;
   a.x_rows = x_rows;
@@ -280,6 +561,7 @@ hipError_t launch_recompute(const kvf_layer_desc& L, const void* x, int64_t x_ro
   a.M = M;
   a.w = w;
   a.K = L.hidden;
+  a.k_len = L.hidden;
   a.rope_cos = rc;
   a.rope_sin = rs;
   a.rope_n = rope_n;
@@ -294,16 +576,48 @@ hipError_t launch_recompute(const kvf_layer_desc& L, const void* x, int64_t x_ro
     a.out[s] = outs[s];
     row0 += heads[s] * L.head_dim;
   }
+  a.c_total = row0;
   if (L.dtype == KVF_BF16) {
+    for (int s = 0; s < 3; ++s)
+      if ((heads[s] * L.head_dim) % 128 != 0) return hipErrorInvalidValue;  // rejected earlier
+    if (L.hidden % kBK != 0) return hipErrorInvalidValue;
+    const Bf16Plan p = plan_bf16(L, M, mask);
     int total = 0;
     for (int s = 0; s < 3; ++s) {
-      const int cols = heads[s] * L.head_dim;
-      if (cols % kBN != 0) return hipErrorInvalidValue;   // rejected on the host earlier
-      a.n_tiles[s] = (mask & bits[s]) ? cols / kBN : 0;
-      total += a.n_tiles[s];
+      a.n_tiles[s] = p.n_tiles[s];
+      total += p.n_tiles[s];
     }
-    if (L.hidden % kBK != 0 || total == 0 || total > 65535) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(gemm_qkv_bf16_kernel, dim3(ceil_div(M, kBM), total), dim3(256), 0, st, a);
+    if (total == 0 || total > 65535) return hipErrorInvalidValue;
+    if (p.splits > 1) {
+      if (ws == nullptr || ws_bytes < recompute_workspace(L, M, mask)) return hipErrorInvalidValue;
+      a.partial = static_cast<float*>(ws);
+      a.k_len = L.hidden / p.splits;
+    }
+    const dim3 grid(ceil_div(M, p.bm), total, p.splits);
+    bool launched = false;
+#define KVF_GEMM_CASE(BM_, BN_)                                                           \
+  if (!launched && p.bm == BM_ && p.bn == BN_) {                                          \
+    hipLaunchKernelGGL((gemm_qkv_bf16_kernel<BM_, BN_>), grid, dim3(kGThreads), 0, st, a); \
+    launched = true;                                                                      \
+  }
+    KVF_GEMM_CASE(256, 128)
+    KVF_GEMM_CASE(192, 128)
+    KVF_GEMM_CASE(160, 128)
+    KVF_GEMM_CASE(128, 128)
+    KVF_GEMM_CASE(64, 128)
+    KVF_GEMM_CASE(160, 256)
+    KVF_GEMM_CASE(128, 256)
+#undef KVF_GEMM_CASE
+    if (!launched) return hipErrorInvalidValue;
+    if (p.splits > 1) {
+      const int per_head = L.head_dim / 16;
+      const int uq = (mask & KVF_OUT_Q) ? L.n_q_heads * per_head : 0;
+      const int uk = (mask & KVF_OUT_K) ? L.n_kv_heads * per_head : 0;
+      const int uv = (mask & KVF_OUT_V) ? L.n_kv_heads * per_head : 0;
+      const int64_t units = static_cast<int64_t>(M) * (uq + uk + uv);
+      hipLaunchKernelGGL(gemm_split_finish_kernel, dim3(static_cast<unsigned>((units + 255) / 256)),
+                         dim3(256), 0, st, a, p.splits, uq, uk, uv);
+    }
   } else {
     int pt[3], total = 0;
     for (int s = 0; s < 3; ++s) {

@@ -247,11 +247,21 @@ kvf_status kvf_select_topk(const float* scores, const kvf_batch* batch, const in
   KVF_GUARD_END
 }
 
+size_t kvf_recompute_workspace_size(const kvf_layer_desc* layer, int32_t M, uint32_t out_mask) {
+  try {
+    if (check_layer(layer) != KVF_OK || M <= 0 || (out_mask & ~7u) != 0) return 0;
+    return kvf::recompute_workspace(*layer, M, out_mask);
+  } catch (...) {
+    return 0;
+  }
+}
+
 kvf_status kvf_recompute_qkv(const kvf_layer_desc* layer, const void* x, int64_t x_rows,
                              const int32_t* row_src, const int32_t* row_pos, int32_t M,
                              const void* w_qkv, uint32_t out_mask, const float* rope_cos,
                              const float* rope_sin, int32_t rope_n_pos, void* q_out,
-                             void* k_out, void* v_out, void* stream) {
+                             void* k_out, void* v_out, void* workspace, size_t ws_bytes,
+                             void* stream) {
   KVF_GUARD_BEGIN
   kvf_status st = check_layer(layer);
   if (st != KVF_OK) return st;
@@ -259,6 +269,7 @@ kvf_status kvf_recompute_qkv(const kvf_layer_desc* layer, const void* x, int64_t
   KVF_CHECK((out_mask & ~7u) == 0, KVF_ERR_INVALID_ARG, "unknown bits in out_mask");
   if (M == 0 || out_mask == 0) return KVF_OK;
   KVF_CHECK(x && w_qkv && row_pos, KVF_ERR_INVALID_ARG, "required pointer is NULL");
+  KVF_CHECK(x_rows > 0, KVF_ERR_INVALID_ARG, "x has no rows");
   KVF_CHECK(row_src != nullptr || M <= x_rows, KVF_ERR_INVALID_ARG,
             "identity row map needs M <= x_rows");
   KVF_CHECK(!(out_mask & KVF_OUT_Q) || q_out, KVF_ERR_INVALID_ARG, "q_out is NULL");
@@ -270,9 +281,13 @@ kvf_status kvf_recompute_qkv(const kvf_layer_desc* layer, const void* x, int64_t
                 ((layer->n_q_heads * layer->head_dim) % 128 == 0 &&
                  (layer->n_kv_heads * layer->head_dim) % 128 == 0),
             KVF_ERR_UNSUPPORTED, "bf16 projection needs Hq*d and Hkv*d multiples of 128");
+  const size_t need = kvf::recompute_workspace(*layer, M, out_mask);
+  KVF_CHECK(ws_bytes >= need && (need == 0 || workspace != nullptr), KVF_ERR_WORKSPACE,
+            "workspace of %zu bytes given, %zu needed", ws_bytes, need);
   return from_hip(kvf::launch_recompute(*layer, x, x_rows, row_src, row_pos, M, w_qkv, out_mask,
                                         rope_cos, rope_sin, rope_n_pos, q_out, k_out, v_out,
-                                        as_stream(stream)), "kvf_recompute_qkv");
+                                        workspace, ws_bytes, as_stream(stream)),
+                  "kvf_recompute_qkv");
   KVF_GUARD_END
 }
 

@@ -77,7 +77,8 @@ _SIGS = {
     "kvf_select_topk": (_I32, [_P, _BP, _IP, _P, _P, _P, _P, _SZ, _P]),
     "kvf_select_workspace_size": (_SZ, [_BP]),
     "kvf_recompute_qkv": (_I32, [_LP, _P, _I64, _P, _P, _I32, _P, ctypes.c_uint32, _P, _P, _I32,
-                                 _P, _P, _P, _P]),
+                                 _P, _P, _P, _P, _SZ, _P]),
+    "kvf_recompute_workspace_size": (_SZ, [_LP, _I32, ctypes.c_uint32]),
     "kvf_scatter_kv": (_I32, [_LP, _P, _P, _I64, _P, _P, _I64, _P, _I32, _P, _P, _I64, _P]),
     "kvf_sparse_q_attention": (_I32, [_LP, _BP, _P, _P, _IP, _P, _P, ctypes.c_float, _P, _P, _P]),
     "kvf_kivi8_encode": (_I32, [_LP, _P, _P, _P, _I32, _I64, _I32, ctypes.POINTER(Kivi8Desc), _P]),
@@ -232,13 +233,26 @@ def recompute_qkv(layer: Layer, x: torch.Tensor, row_src: Optional[torch.Tensor]
                   row_pos: torch.Tensor, w_qkv: torch.Tensor, out_mask: int,
                   rope_cos: torch.Tensor, rope_sin: torch.Tensor,
                   q_out: Optional[torch.Tensor] = None, k_out: Optional[torch.Tensor] = None,
-                  v_out: Optional[torch.Tensor] = None, M: Optional[int] = None, stream=None):
+                  v_out: Optional[torch.Tensor] = None, M: Optional[int] = None,
+                  workspace: Optional[torch.Tensor] = None, stream=None):
+    """workspace: kvf_recompute_workspace_size bytes; allocated here when
+    omitted and needed (pass one to keep the call allocation-free)."""
     d = layer.desc()
     M = int(row_pos.shape[0]) if M is None else M
+    if workspace is None:
+        need = recompute_workspace_size(layer, M, out_mask)
+        if need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_lib.kvf_recompute_qkv(ctypes.byref(d), _ptr(x), _rows(x), _ptr(row_src), _ptr(row_pos),
                                   M, _ptr(w_qkv), out_mask, _ptr(rope_cos), _ptr(rope_sin),
                                   _rows(rope_cos), _ptr(q_out), _ptr(k_out), _ptr(v_out),
-                                  _stream(stream)), "kvf_recompute_qkv")
+                                  _ptr(workspace), ws_bytes, _stream(stream)), "kvf_recompute_qkv")
+
+
+def recompute_workspace_size(layer: Layer, M: int, out_mask: int) -> int:
+    d = layer.desc()
+    return int(_lib.kvf_recompute_workspace_size(ctypes.byref(d), M, out_mask))
 
 
 def scatter_kv(layer: Layer, k_src: Optional[torch.Tensor], k_src_row: Optional[torch.Tensor],

@@ -135,6 +135,15 @@ class FusedLayerGPU:
             self.v_u = torch.zeros_like(self.k_u)
             nbytes = kvf.score_workspace_size(kvf.KVF_SCORE_ATTN_MASS, L, self.kb, n_last_q)
             self.ws = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=dev)
+        # one projection workspace for every recompute call (they are ordered
+        # on the stream), so the stages allocate nothing
+        QKV = kvf.KVF_OUT_Q | kvf.KVF_OUT_K | kvf.KVF_OUT_V
+        need = [kvf.recompute_workspace_size(L, M, QKV)]
+        if self.mode == "deviation":
+            need.append(kvf.recompute_workspace_size(L, T_total, kvf.KVF_OUT_K))
+        else:
+            need.append(kvf.recompute_workspace_size(L, nU, QKV))
+        self.gemm_ws = torch.empty(max(max(need), 1), dtype=torch.uint8, device=dev)
 
     # ------------------------------------------------------------------ stages
     def stage_rerotate(self):
@@ -145,13 +154,14 @@ class FusedLayerGPU:
         L = self.layer
         if self.mode == "deviation":
             kvf.recompute_qkv(L, self.x, None, self.all_pos, self.w, kvf.KVF_OUT_K, self.rope_cos,
-                              self.rope_sin, k_out=self.k_probe)
+                              self.rope_sin, k_out=self.k_probe, workspace=self.gemm_ws)
             kvf.score(kvf.KVF_SCORE_DEVIATION, L, self.kb, self.fused_k, self.k_probe, None,
                       self.scores)
         else:
             kvf.recompute_qkv(L, self.x, self.u_rows, self.u_pos, self.w,
                               kvf.KVF_OUT_Q | kvf.KVF_OUT_K | kvf.KVF_OUT_V, self.rope_cos,
-                              self.rope_sin, q_out=self.q_u, k_out=self.k_u, v_out=self.v_u)
+                              self.rope_sin, q_out=self.q_u, k_out=self.k_u, v_out=self.v_u,
+                              workspace=self.gemm_ws)
             kvf.scatter_kv(L, self.k_u, None, self.v_u, None, self.u_rows, self.fused_k, self.fused_v)
             kvf.score(kvf.KVF_SCORE_ATTN_MASS, L, self.kb, self.fused_k, None, self.q_u, self.scores,
                       self.ws, n_last_q=self.n_last_q)
@@ -181,14 +191,15 @@ class FusedLayerGPU:
             return
         if self.mode == "deviation":
             kvf.recompute_qkv(L, self.x, self.rows, self.pos, self.w, kvf.KVF_OUT_Q | kvf.KVF_OUT_V,
-                              self.rope_cos, self.rope_sin, q_out=self.q, v_out=self.v_new, M=self.M)
+                              self.rope_cos, self.rope_sin, q_out=self.q, v_out=self.v_new, M=self.M,
+                              workspace=self.gemm_ws)
             kvf.scatter_kv(L, self.k_probe, self.rows, self.v_new, None, self.rows, self.fused_k,
                            self.fused_v, M=self.M)
         else:
             kvf.recompute_qkv(L, self.x, self.rows, self.pos, self.w,
                               kvf.KVF_OUT_Q | kvf.KVF_OUT_K | kvf.KVF_OUT_V, self.rope_cos,
                               self.rope_sin, q_out=self.q, k_out=self.k_new, v_out=self.v_new,
-                              M=self.M)
+                              M=self.M, workspace=self.gemm_ws)
             kvf.scatter_kv(L, self.k_new, None, self.v_new, None, self.rows, self.fused_k,
                            self.fused_v, M=self.M)
 

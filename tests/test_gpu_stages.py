@@ -301,6 +301,9 @@ RECOMP_CASES = [
     ("bf16", 512, 8, 2, 128, 700, 129, 5),
     ("bf16", 384, 4, 4, 128, 300, 300, 2),
     ("bf16", 256, 4, 2, 64, 200, 77, 7),
+    ("bf16", 1024, 8, 2, 128, 100, 40, 7),      # K split in 4 slices, 64-row tile
+    ("bf16", 2048, 8, 4, 64, 50, 1, 3),         # one row, K split
+    ("bf16", 512, 16, 8, 128, 2100, 2050, 7),   # many rows, 256-wide column tile
     ("f32", 256, 4, 4, 64, 300, 108, 7),
     ("f32", 128, 4, 2, 64, 90, 45, 6),
 ]
@@ -331,6 +334,38 @@ def test_recompute(kvf, case):
             assert_close(from_gpu(t), ref[name], dtype, f"recompute {name} {case}")
         else:
             assert not from_gpu(t).any()
+
+
+@pytest.mark.parametrize("dtype,hidden,M", [("bf16", 1024, 40), ("bf16", 256, 300), ("f32", 128, 50)])
+def test_recompute_skips_rows_outside_tables(kvf, dtype, hidden, M):
+    """A row map entry outside x or a position outside the rope table leaves
+    that row unwritten (Q/K for a bad position, Q/K/V for a bad source row)."""
+    import torch
+    hq, hkv, d, xr, n_pos = 4, 2, 64, 120, 500
+    x_s = encode(_randn((xr, hidden), 8, "x"), dtype)
+    w_s = encode(_randn(((hq + 2 * hkv) * d, hidden), 8, "w", std=1 / math.sqrt(hidden)), dtype)
+    rows = synth.random_rows(xr, M, 9) if M <= xr else np.arange(M, dtype=np.int32) % xr
+    pos = synth.random_rows(n_pos, M, 10) if M <= n_pos else np.arange(M, dtype=np.int32) % n_pos
+    bad_src = np.array([1, M - 1]), np.array([3])
+    rows[bad_src[0]] = [-1, xr]
+    pos[bad_src[1]] = n_pos
+    L = _layer(kvf, hidden, hq, hkv, d, dtype)
+    c, s = _rope_tables(kvf, 1e4, d, n_pos)
+    td = L.torch_dtype
+    outs = [torch.full((M, h, d), 7.0, dtype=td, device="cuda") for h in (hq, hkv, hkv)]
+    kvf.recompute_qkv(L, to_gpu(x_s, dtype), to_gpu(rows), to_gpu(pos), to_gpu(w_s, dtype), 7, c, s,
+                      q_out=outs[0], k_out=outs[1], v_out=outs[2])
+    good = np.setdiff1d(np.arange(M), np.concatenate(bad_src))
+    lo = fusion.Layer(hidden, hq, hkv, d, 1e4)
+    ref = fusion.recompute(decode(x_s, dtype)[rows[good]], pos[good], decode(w_s, dtype), lo)
+    for name, t in zip("qkv", outs):
+        got = from_gpu(t)
+        assert_close(got[good], ref[name], dtype, f"recompute {name} good rows")
+        assert np.all(got[bad_src[0]] == 7.0), name
+        if name in "qk":
+            assert np.all(got[bad_src[1]] == 7.0), name
+        else:
+            assert not np.all(got[bad_src[1]] == 7.0)
 
 
 @pytest.mark.parametrize("wl_name,kind", [("qwen3_8b_mass", "p_and_u"), ("qwen3_8b_mass", "u_probe"),
