@@ -1,7 +1,8 @@
 """Benchmark of one fused RAG KV-cache layer on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--no-cpu-baseline] [--graph]
+                    [--ratio PCT] [--no-cpu-baseline] [--graph]
+    python bench.py --copy-calibration      # plain 1 GiB device copy (counter scale)
 
 A step is one pass of the whole hot path over one batch of synthetic input:
 re-position/stitch -> score -> top-k -> Q/K/V recompute -> scatter ->
@@ -11,17 +12,25 @@ starts (the caches are built by the library's own projection at chunk-local
 positions, ahead of the timed region).  The metric is fused context tokens per
 second per layer: (sum over requests of N) / step time.
 
-Prints one JSON line.  Each library call of a step is bracketed with HIP
-events on the stream it is launched on; the dominant kernel's average
-duration over the timed steps gives the roofline fraction.  The CPU baseline
-runs the float64 oracle on the same workload (one full pass) on the host.
+Two timed loops of K steps each, after W warm-up steps:
+  1. plain: the steps back to back; its wall clock (synchronised on both
+     sides) gives `value` and `ms_per_step`;
+  2. per call: every library call of every step bracketed by HIP events on
+     the stream it is launched on; the averages give each call's duration and
+     its roofline fraction (algorithmic bytes or flops / duration).
+The roofline object describes the call that takes longest; its `traffic` is
+the HBM bytes per launch from the committed counter summary of that kernel
+and workload under profiles/, or null when the kernel source has changed
+since the counters were taken.  The CPU baseline runs the float64 oracle on
+the same batch on the host cores.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
-import math
 import os
+import re
 import sys
 import time
 
@@ -30,7 +39,23 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 DEFAULT_WORKLOAD = "qwen3_8b_mass"
-PEAK = {"hbm_gbs": 8000.0, "bf16_tflops": 2500.0, "fp32_tflops": 157.3}
+METRIC = "fused context tokens/s per layer @r=30% on 1 MI355X; % MFMA/HBM roofline"
+UNIT = "fused context tokens/s per layer"
+# MI355X published peaks: HBM3E bandwidth, dense MFMA bf16, fp32 vector
+PEAK = {"hbm": 8000.0, "bf16": 2500.0, "f32": 157.3}
+KDIR = os.path.join(ROOT, "rag_kv_cache_kvf_amd", "csrc")
+# library call -> (kernel that dominates it, its source file)
+CALL_KERNEL = {
+    "rerotate": ("rerotate_kernel", "kernels/rope_rerotate.hip"),
+    "k_probe": ("gemm_qkv_bf16_kernel", "kernels/gemm_qkv.hip"),
+    "u_probe": ("gemm_qkv_bf16_kernel", "kernels/gemm_qkv.hip"),
+    "u_scatter": ("scatter_kernel", "kernels/scatter_deviation.hip"),
+    "score": ("mass_colsum_bf16_kernel", "kernels/attention.hip"),
+    "select": ("topk_kernel", "kernels/topk.hip"),
+    "recompute": ("gemm_qkv_bf16_kernel", "kernels/gemm_qkv.hip"),
+    "scatter": ("scatter_kernel", "kernels/scatter_deviation.hip"),
+    "attention": ("attn_bf16_kernel", "kernels/attention.hip"),
+}
 
 
 def _parse():
@@ -42,16 +67,19 @@ def _parse():
     ap.add_argument("--ratio", type=int, default=None, help="recompute ratio in percent")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true", help="replay the step as one HIP graph")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device-to-device copy of 1 GiB, 3 times")
     return ap.parse_args()
 
 
-def stage_work(g):
-    """Algorithmic work of every stage of one step (flops or bytes)."""
+def call_work(g):
+    """Algorithmic work of every library call of one step:
+    name -> ("hbm", bytes) or ("mfma", flops)."""
     wl = g.wl
     b = g.batch
     hq, hkv, d, hid = wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.hidden
     esz = 2 if wl.dtype == "bf16" else 4
-    krow = hkv * d * esz
+    krow = hkv * d * esz                           # bytes of one token's K (or V)
     n_ctx = int(sum(b.n_ctx))
     total = b.total_rows
     nU = total - n_ctx
@@ -59,119 +87,104 @@ def stage_work(g):
     pos = g.pos.cpu().numpy()[:M].astype("int64")
     work = {}
     if wl.kivi8:
-        # codes K + V, V stats (8 B per head per token), K stats amortised per chunk
+        # read K/V codes (1 B each) + V per-token stats (min, scale) + K
+        # per-channel stats once per chunk; write bf16 K and V
         n_chunks = b.chunk_table.shape[0]
-        s1 = n_ctx * (2 * hkv * d + 8 * hkv + 2 * krow) + n_chunks * 8 * hkv * d
+        work["rerotate"] = ("hbm", n_ctx * (2 * hkv * d + 8 * hkv + 2 * krow)
+                            + n_chunks * 8 * hkv * d)
     else:
-        s1 = n_ctx * 4 * krow                       # read K,V from the pool, write K,V
-    work["rerotate"] = ("hbm", s1)
+        work["rerotate"] = ("hbm", n_ctx * 4 * krow)      # read pool K,V; write fused K,V
     if g.mode == "deviation":
         work["k_probe"] = ("mfma", 2.0 * hid * hkv * d * total)
-        work["score"] = ("hbm", n_ctx * (2 * krow + 4))
+        work["score"] = ("hbm", n_ctx * (2 * krow + 4))   # fused K, probe K -> one fp32
         work["recompute"] = ("mfma", 2.0 * hid * d * (hq + hkv) * M)
     else:
-        G = hq // hkv
         work["u_probe"] = ("mfma", 2.0 * hid * d * (hq + 2 * hkv) * nU)
         work["u_scatter"] = ("hbm", nU * 4 * krow)
         flops = 0.0
         for r in range(b.n_req):
             U = b.n_query(r)
             N = int(b.n_ctx[r])
-            keys = sum(N + i + 1 for i in range(U))        # pass 1 (statistics)
-            flops += 2.0 * d * hq * keys + 2.0 * d * hq * U * N   # pass 2 (context keys)
+            keys = sum(N + i + 1 for i in range(U))        # row statistics over the causal row
+            flops += 2.0 * d * hq * keys + 2.0 * d * hq * U * N   # then Q K^T over the context
         work["score"] = ("mfma", flops)
         work["recompute"] = ("mfma", 2.0 * hid * d * (hq + 2 * hkv) * M)
-    work["select"] = ("hbm", n_ctx * 4 + M * 8)
-    work["scatter"] = ("hbm", M * 4 * krow)
-    work["attention"] = ("mfma", 4.0 * d * hq * float((pos + 1).sum()))
+    work["select"] = ("hbm", n_ctx * 4 + M * 8)       # scores in; row ids + positions out
+    work["scatter"] = ("hbm", M * 4 * krow)           # new K,V in; fused rows out
+    work["attention"] = ("mfma", 4.0 * d * hq * float((pos + 1).sum()))   # QK^T + PV, causal
     return work
 
 
-def run_steps(g, steps, use_graph):
-    """Run `steps` steps; with events around every library call."""
+def _timed_plain(g, steps, use_graph):
     import torch
-    names = ["rerotate", "score_all", "select", "recompute_fuse", "attention"]
-    ev = {n: [] for n in names}
-
-    def one_step(record):
-        def bracket(name, fn):
-            if record:
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                e0.record()
-                fn()
-                e1.record()
-                ev[name].append((e0, e1))
-            else:
-                fn()
-        bracket("rerotate", g.stage_rerotate)
-        bracket("score_all", g.stage_score)
-        bracket("select", g.stage_select)
-        bracket("recompute_fuse", g.stage_recompute_fuse)
-        bracket("attention", g.stage_attention)
-
     if use_graph:
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.stream(s):
-            one_step(False)
+            g.run()
             torch.cuda.synchronize()
             with torch.cuda.graph(graph, stream=s):
-                one_step(False)
+                g.run()
         torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(steps):
-            graph.replay()
-        torch.cuda.synchronize()
-        t1 = time.perf_counter()
-        return (t1 - t0) / steps, None
+        run = graph.replay
+    else:
+        run = g.run
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
-        one_step(True)
+        run()
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    per = {n: sum(a.elapsed_time(b) for a, b in v) / max(1, len(v)) for n, v in ev.items()}
-    return (t1 - t0) / steps, per
+    return (time.perf_counter() - t0) / steps
 
 
-def kernel_times(g, steps):
-    """Per-kernel average durations (ms) of the dominant-kernel candidates,
-    with HIP events on the launch stream, over `steps` steps."""
+def _timed_per_call(g, steps):
+    """Average duration (ms) of every library call, HIP events on the
+    current stream (the one the library launches on)."""
     import torch
-    from rag_kv_cache_kvf_amd import kvfuse as kvf
-    L = g.layer
-    res = {"recompute": [], "attention": []}
-    for _ in range(steps):
-        g.stage_rerotate()
-        g.stage_score()
-        g.stage_select()
-        e0, e1, e2, e3 = (torch.cuda.Event(enable_timing=True) for _ in range(4))
-        if g.mode == "deviation":
-            e0.record()
-            kvf.recompute_qkv(L, g.x, g.rows, g.pos, g.w, kvf.KVF_OUT_Q | kvf.KVF_OUT_V, g.rope_cos,
-                              g.rope_sin, q_out=g.q, v_out=g.v_new, M=g.M)
-            e1.record()
-            kvf.scatter_kv(L, g.k_probe, g.rows, g.v_new, None, g.rows, g.fused_k, g.fused_v, M=g.M)
-        else:
-            e0.record()
-            kvf.recompute_qkv(L, g.x, g.rows, g.pos, g.w, kvf.KVF_OUT_Q | kvf.KVF_OUT_K | kvf.KVF_OUT_V,
-                              g.rope_cos, g.rope_sin, q_out=g.q, k_out=g.k_new, v_out=g.v_new, M=g.M)
-            e1.record()
-            kvf.scatter_kv(L, g.k_new, None, g.v_new, None, g.rows, g.fused_k, g.fused_v, M=g.M)
-        e2.record()
-        g.stage_attention()
-        e3.record()
-        res["recompute"].append((e0, e1))
-        res["attention"].append((e2, e3))
+    calls = g.calls()
+    ev = {name: [] for name, _, _ in calls}
     torch.cuda.synchronize()
-    return {k: sum(a.elapsed_time(b) for a, b in v) / len(v) for k, v in res.items()}
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        for name, _, fn in calls:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            ev[name].append((e0, e1))
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    per = {n: sum(a.elapsed_time(b) for a, b in v) / len(v) for n, v in ev.items()}
+    return per, wall
 
 
-def cpu_baseline(batch, ratio):
-    """The float64 oracle on the same workload: one full pass (every stage of
-    the layer), timed on the host cores."""
+def _source_hash(rel):
+    h = hashlib.sha256()
+    for f in (rel, "kvf_common.h"):
+        with open(os.path.join(KDIR, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def _traffic(kernel, src, workload):
+    """HBM bytes per launch from profiles/<kernel>.<workload>.md, if its
+    recorded source hash matches the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}.{workload}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_b = re.search(r"^traffic_bytes_per_launch:\s*([0-9.eE+]+)\s*$", text, re.M)
+    m_h = re.search(r"^source_sha256:\s*([0-9a-f]{64})\s*$", text, re.M)
+    if not (m_b and m_h) or m_h.group(1) != _source_hash(src):
+        return None
+    return float(m_b.group(1))
+
+
+def cpu_baseline(batch, ratio, min_seconds=10.0):
+    """The float64 oracle on the same batch (one full pass of every stage of
+    the layer), repeated until at least `min_seconds` of host time."""
     import numpy as np
     from oracle import fusion, storage
     wl = batch.wl
@@ -186,14 +199,36 @@ def cpu_baseline(batch, ratio):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:  # pragma: no cover
         threads = len(os.sched_getaffinity(0))
-    t0 = time.perf_counter()
-    fusion.fused_layer(x, w, pk, pv, batch.chunk_table, batch.cu_T, batch.n_ctx, lo, wl.score, ks)
-    dt = time.perf_counter() - t0
+    runs, t0 = 0, time.perf_counter()
+    while True:
+        fusion.fused_layer(x, w, pk, pv, batch.chunk_table, batch.cu_T, batch.n_ctx, lo, wl.score,
+                           ks)
+        runs += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
     n_ctx = int(np.sum(batch.n_ctx))
-    return {"value": n_ctx / dt, "unit": "fused context tokens/s per layer", "cores": int(threads),
-            "kind": "oracle", "seconds": dt,
-            "sample": f"one full pass of the layer over the whole {wl.name} batch "
+    return {"value": round(n_ctx * runs / dt, 1), "unit": UNIT, "cores": int(threads),
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": f"{runs} full pass(es) of the layer over the whole {wl.name} batch "
                       f"({batch.n_req} request(s), {n_ctx} context tokens), float64 numpy"}
+
+
+def copy_calibration():
+    """A plain 1 GiB device-to-device copy, three times: the HBM byte
+    counters read for it scale the counters of the kernels."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / 3
+    print(json.dumps({"copy_bytes": n, "copies": 3, "read_bytes": n, "write_bytes": n,
+                      "GBps_read_plus_write": round(2 * n / dt / 1e9, 1)}), flush=True)
 
 
 def main():
@@ -204,10 +239,13 @@ def main():
         sys.exit(2)
     import numpy as np
     import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_calibration:
+        copy_calibration()
+        return
     from rag_kv_cache_kvf_amd import synth
     from rag_kv_cache_kvf_amd.layer import FusedLayerGPU
 
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
     wl = synth.get_workload(args.workload)
     ratio = args.ratio if args.ratio is not None else wl.ratio_pct[-1]
     batch = synth.make_batch(wl)
@@ -216,35 +254,37 @@ def main():
         g.run()
     torch.cuda.synchronize()
 
-    sec, per_stage = run_steps(g, args.steps, args.graph)
-    kt = kernel_times(g, max(5, min(args.steps, 20)))
-    work = stage_work(g)
+    sec = _timed_plain(g, args.steps, args.graph)
+    per_call, wall_events = _timed_per_call(g, args.steps)
+    work = call_work(g)
     n_ctx = int(np.sum(batch.n_ctx))
-    value = n_ctx / sec
 
-    # dominant kernel: the larger of the projection and attention kernels
-    dom = max(kt, key=kt.get)
+    peak_mfma = PEAK["bf16"] if wl.dtype == "bf16" else PEAK["f32"]
+    calls = {}
+    for name, ms in per_call.items():
+        kind, amount = work[name]
+        if kind == "hbm":
+            ach, peak, unit = amount / (ms * 1e-3) / 1e9, PEAK["hbm"], "GB/s"
+        else:
+            ach, peak, unit = amount / (ms * 1e-3) / 1e12, peak_mfma, "TFLOP/s"
+        calls[name] = {"ms": round(ms, 5), "bound": kind, "achieved": round(ach, 2),
+                       "unit": unit, "frac": round(ach / peak, 4),
+                       "tokens_per_s": round(n_ctx / (ms * 1e-3), 1)}
+    dom = max(per_call, key=per_call.get)
+    kname, ksrc = CALL_KERNEL[dom]
+    if dom == "score" and g.mode == "deviation":
+        kname, ksrc = "deviation_kernel", "kernels/scatter_deviation.hip"
     kind, amount = work[dom]
-    achieved = amount / (kt[dom] * 1e-3) / 1e12
-    roofline = {"kernel": "gemm_qkv_bf16_kernel" if dom == "recompute" else "attn_bf16_kernel",
-                "bound": "mfma", "achieved": round(achieved, 2),
-                "peak": PEAK["bf16_tflops"] if wl.dtype == "bf16" else PEAK["fp32_tflops"],
-                "unit": "TFLOP/s", "avg_ms": round(kt[dom], 5), "traffic": None}
-    roofline["frac"] = round(roofline["achieved"] / roofline["peak"], 4)
-
-    stages = {}
-    if per_stage:
-        for k, v in per_stage.items():
-            stages[k] = {"ms": round(v, 5)}
-    for k, v in kt.items():
-        stages.setdefault(f"{k}_kernel", {})["ms"] = round(v, 5)
-        kk, amt = work[k]
-        stages[f"{k}_kernel"]["tflops"] = round(amt / (v * 1e-3) / 1e12, 2)
+    c = calls[dom]
+    roofline = {"kernel": kname, "call": dom, "bound": kind, "achieved": c["achieved"],
+                "peak": PEAK["hbm"] if kind == "hbm" else peak_mfma, "unit": c["unit"],
+                "frac": c["frac"], "avg_ms": c["ms"], "algorithmic_per_launch": amount,
+                "traffic": _traffic(kname, ksrc, wl.name)}
 
     out = {
-        "metric": "fused context tokens/s per layer @r=30% on 1 MI355X; % MFMA/HBM roofline",
-        "value": round(value, 1),
-        "unit": "fused context tokens/s per layer",
+        "metric": METRIC,
+        "value": round(n_ctx / sec, 1),
+        "unit": UNIT,
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -258,7 +298,8 @@ def main():
                    "context_tokens": n_ctx, "query_tokens": batch.total_rows - n_ctx,
                    "recompute_ratio_pct": ratio, "score": g.mode, "graph": bool(args.graph)},
         "roofline": roofline,
-        "stages": stages,
+        "calls": calls,
+        "ms_per_step_with_call_events": round(wall_events * 1e3, 5),
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(batch, ratio)

@@ -145,29 +145,93 @@ class FusedLayerGPU:
             need.append(kvf.recompute_workspace_size(L, nU, QKV))
         self.gemm_ws = torch.empty(max(max(need), 1), dtype=torch.uint8, device=dev)
 
-    # ------------------------------------------------------------------ stages
-    def stage_rerotate(self):
+    # ------------------------------------------------------------------ calls
+    def _rerotate(self):
         kvf.rerotate(self.layer, self.chunks, self.max_chunk_len, self.pool_k, self.pool_v,
                      self.rope_cos, self.rope_sin, self.fused_k, self.fused_v, kivi=self.kivi)
 
-    def stage_score(self):
-        L = self.layer
+    def _k_probe(self):
+        kvf.recompute_qkv(self.layer, self.x, None, self.all_pos, self.w, kvf.KVF_OUT_K,
+                          self.rope_cos, self.rope_sin, k_out=self.k_probe, workspace=self.gemm_ws)
+
+    def _u_probe(self):
+        kvf.recompute_qkv(self.layer, self.x, self.u_rows, self.u_pos, self.w,
+                          kvf.KVF_OUT_Q | kvf.KVF_OUT_K | kvf.KVF_OUT_V, self.rope_cos,
+                          self.rope_sin, q_out=self.q_u, k_out=self.k_u, v_out=self.v_u,
+                          workspace=self.gemm_ws)
+
+    def _u_scatter(self):
+        kvf.scatter_kv(self.layer, self.k_u, None, self.v_u, None, self.u_rows, self.fused_k,
+                       self.fused_v)
+
+    def _score(self):
         if self.mode == "deviation":
-            kvf.recompute_qkv(L, self.x, None, self.all_pos, self.w, kvf.KVF_OUT_K, self.rope_cos,
-                              self.rope_sin, k_out=self.k_probe, workspace=self.gemm_ws)
-            kvf.score(kvf.KVF_SCORE_DEVIATION, L, self.kb, self.fused_k, self.k_probe, None,
-                      self.scores)
+            kvf.score(kvf.KVF_SCORE_DEVIATION, self.layer, self.kb, self.fused_k, self.k_probe,
+                      None, self.scores)
         else:
-            kvf.recompute_qkv(L, self.x, self.u_rows, self.u_pos, self.w,
+            kvf.score(kvf.KVF_SCORE_ATTN_MASS, self.layer, self.kb, self.fused_k, None, self.q_u,
+                      self.scores, self.ws, n_last_q=self.n_last_q)
+
+    def _select(self):
+        kvf.select_topk(self.scores, self.kb, self.k_per_req, self.sel, self.rows, self.pos)
+
+    def _recompute(self):
+        if self.M == 0:
+            return
+        if self.mode == "deviation":
+            # K of these rows is already in the probe
+            kvf.recompute_qkv(self.layer, self.x, self.rows, self.pos, self.w,
+                              kvf.KVF_OUT_Q | kvf.KVF_OUT_V, self.rope_cos, self.rope_sin,
+                              q_out=self.q, v_out=self.v_new, M=self.M, workspace=self.gemm_ws)
+        else:
+            kvf.recompute_qkv(self.layer, self.x, self.rows, self.pos, self.w,
                               kvf.KVF_OUT_Q | kvf.KVF_OUT_K | kvf.KVF_OUT_V, self.rope_cos,
-                              self.rope_sin, q_out=self.q_u, k_out=self.k_u, v_out=self.v_u,
-                              workspace=self.gemm_ws)
-            kvf.scatter_kv(L, self.k_u, None, self.v_u, None, self.u_rows, self.fused_k, self.fused_v)
-            kvf.score(kvf.KVF_SCORE_ATTN_MASS, L, self.kb, self.fused_k, None, self.q_u, self.scores,
-                      self.ws, n_last_q=self.n_last_q)
+                              self.rope_sin, q_out=self.q, k_out=self.k_new, v_out=self.v_new,
+                              M=self.M, workspace=self.gemm_ws)
+
+    def _scatter(self):
+        if self.M == 0:
+            return
+        if self.mode == "deviation":
+            kvf.scatter_kv(self.layer, self.k_probe, self.rows, self.v_new, None, self.rows,
+                           self.fused_k, self.fused_v, M=self.M)
+        else:
+            kvf.scatter_kv(self.layer, self.k_new, None, self.v_new, None, self.rows, self.fused_k,
+                           self.fused_v, M=self.M)
+
+    def _attention(self):
+        if self.M == 0:
+            return
+        kvf.sparse_q_attention(self.layer, self.kb, self.q, self.pos, self.cu_q, self.fused_k,
+                               self.fused_v, self.sm_scale, self.out, self.lse)
+
+    def calls(self):
+        """The library calls of one pass, in order, as (name, stage, fn):
+        stage is one of rerotate / score / select / recompute_fuse / attention."""
+        if self.mode == "deviation":
+            score = [("k_probe", "score", self._k_probe), ("score", "score", self._score)]
+        else:
+            score = [("u_probe", "score", self._u_probe), ("u_scatter", "score", self._u_scatter),
+                     ("score", "score", self._score)]
+        return ([("rerotate", "rerotate", self._rerotate)] + score +
+                [("select", "select", self._select),
+                 ("recompute", "recompute_fuse", self._recompute),
+                 ("scatter", "recompute_fuse", self._scatter),
+                 ("attention", "attention", self._attention)])
+
+    def _stage(self, stage):
+        for _, st, fn in self.calls():
+            if st == stage:
+                fn()
+
+    def stage_rerotate(self):
+        self._stage("rerotate")
+
+    def stage_score(self):
+        self._stage("score")
 
     def stage_select(self):
-        kvf.select_topk(self.scores, self.kb, self.k_per_req, self.sel, self.rows, self.pos)
+        self._stage("select")
 
     def force_selection(self, sel: Sequence[np.ndarray]):
         """Replace the selection with given per-request positions (tests)."""
@@ -186,39 +250,22 @@ class FusedLayerGPU:
             self.sel.copy_(_i32(np.concatenate(flat), self.device))
 
     def stage_recompute_fuse(self):
-        L = self.layer
-        if self.M == 0:
-            return
-        if self.mode == "deviation":
-            kvf.recompute_qkv(L, self.x, self.rows, self.pos, self.w, kvf.KVF_OUT_Q | kvf.KVF_OUT_V,
-                              self.rope_cos, self.rope_sin, q_out=self.q, v_out=self.v_new, M=self.M,
-                              workspace=self.gemm_ws)
-            kvf.scatter_kv(L, self.k_probe, self.rows, self.v_new, None, self.rows, self.fused_k,
-                           self.fused_v, M=self.M)
-        else:
-            kvf.recompute_qkv(L, self.x, self.rows, self.pos, self.w,
-                              kvf.KVF_OUT_Q | kvf.KVF_OUT_K | kvf.KVF_OUT_V, self.rope_cos,
-                              self.rope_sin, q_out=self.q, k_out=self.k_new, v_out=self.v_new,
-                              M=self.M, workspace=self.gemm_ws)
-            kvf.scatter_kv(L, self.k_new, None, self.v_new, None, self.rows, self.fused_k,
-                           self.fused_v, M=self.M)
+        self._stage("recompute_fuse")
 
     def stage_attention(self):
-        if self.M == 0:
-            return
-        kvf.sparse_q_attention(self.layer, self.kb, self.q, self.pos, self.cu_q, self.fused_k,
-                               self.fused_v, self.sm_scale, self.out, self.lse)
+        self._stage("attention")
 
     def run(self, forced_sel: Optional[Sequence[np.ndarray]] = None):
         """Enqueue one pass of the whole path on the current stream."""
-        self.stage_rerotate()
-        self.stage_score()
         if forced_sel is None:
-            self.stage_select()
-        else:
-            self.force_selection(forced_sel)
-        self.stage_recompute_fuse()
-        self.stage_attention()
+            for _, _, fn in self.calls():
+                fn()
+            return
+        for _, st, fn in self.calls():
+            if st == "select":
+                self.force_selection(forced_sel)
+            else:
+                fn()
 
     # ------------------------------------------------------------------ readback
     def selection(self):
