@@ -55,6 +55,22 @@ __device__ __forceinline__ bool row_ok(const GemmArgs& a, int m) {
   return s >= 0 && s < a.x_rows;
 }
 
+// Hardware hands workgroups to the 8 XCDs round-robin by linear id, and
+// each XCD has its own L2.  Renumber so that XCD x runs one contiguous range
+// of logical tiles: with the row tile varying fastest, the row tiles of a
+// column tile (which share its weight slab) then share one L2, and W is
+// fetched from HBM about once instead of once per XCD.
+__device__ __forceinline__ void xcd_tile(int& tx, int& ty, int& tz) {
+  const int gx = gridDim.x, gy = gridDim.y;
+  const int n = gx * gy * gridDim.z;
+  const int b = blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z);
+  const int q = n >> 3, r = n & 7, x = b & 7;
+  const int l = x * q + min(x, r) + (b >> 3);
+  tx = l % gx;
+  ty = (l / gx) % gy;
+  tz = l / (gx * gy);
+}
+
 __device__ __forceinline__ int segment_of(const int (&n_tiles)[3], int& t) {
   int seg = 0;
   while (seg < 2 && t >= n_tiles[seg]) {
@@ -68,9 +84,9 @@ __device__ __forceinline__ int segment_of(const int (&n_tiles)[3], int& t) {
 // bf16 MFMA kernel
 // ---------------------------------------------------------------------------
 // Workgroup tile BM x BN x 64 (BM a multiple of 32, BN 128 or 256, chosen per
-// call so the tile count fills the chip in whole rounds); 4 waves, wave w owns
-// output columns [w BN/4, (w+1) BN/4) for all BM rows (BM/32 x BN/128
-// accumulators of 32 x 32).
+// call so the tile count fills the chip in whole rounds); 4 waves in a
+// WM x (4/WM) grid, each owning a (BM/WM) x (BN/(4/WM)) block of the tile
+// as 32 x 32 MFMA accumulators.
 // Operand tiles stream global -> LDS through the DMA path (16 bytes per lane,
 // rows of X gathered through row_src by each lane's own source address) into
 // a ring of 3-4 static stage buffers, so the next stages load while one
@@ -88,10 +104,24 @@ struct GemmTile {
   // stages in flight: as many as 160 KB of LDS holds, at most 4
   static constexpr int kStages =
       (kA + kB) * 2 * 4 <= 160 * 1024 ? 4 : ((kA + kB) * 2 * 3 <= 160 * 1024 ? 3 : 2);
+  static_assert((kA + kB) * 2 * 2 <= 160 * 1024, "two stages must fit in LDS");
+  // the epilogue stages fp32 results in the same memory, as many 32-row
+  // blocks per round as fit
+  static constexpr int kStageBytes = (kA + kB) * 2 * kStages;
+  static constexpr int kEpRows = (160 * 1024 / (BN * 4)) / 32 * 32 < BM
+                                     ? (160 * 1024 / (BN * 4)) / 32 * 32 : BM;
+  static constexpr int kLdsBytes =
+      kStageBytes > kEpRows * BN * 4 ? kStageBytes : kEpRows * BN * 4;
 };
 
+// Physical 16-B chunk of logical chunk `chunk` in LDS row `row` (rows of
+// 128 B).  A 16-byte-per-lane read is served 16 lanes at a time across 64
+// banks (256 B): the 16 rows a fragment read touches at once must cover both
+// 128-B halves of the bank window with distinct chunks, hence row/2 in the
+// XOR (rows r and r+8 differ in it, r and r+1 differ in the half).
+__device__ __forceinline__ int gchunk(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
 __device__ __forceinline__ int gswz(int row, int chunk) {   // element offset of a 16-B chunk
-  return row * kBK + ((chunk ^ (row & 7)) << 3);
+  return row * kBK + (gchunk(row, chunk) << 3);
 }
 
 // One 16-byte-per-lane global -> LDS copy (the DMA path).  Issued from inline
@@ -114,27 +144,40 @@ __device__ __forceinline__ void dma_wait_barrier() {
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"i"(N) : "memory");
 }
 
-template <int BM, int BN>
+// As dma_wait_barrier, after this wave's own LDS reads have completed: once
+// every wave has passed it, the stage buffer those reads used may be
+// overwritten.
+template <int N>
+__device__ __forceinline__ void lds_dma_wait_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"i"(N) : "memory");
+}
+
+template <int BM, int BN, int WM>
 __global__ void __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 gemm_qkv_bf16_kernel(GemmArgs a) {
-  constexpr int MB = BM / 32;               // 32-row MFMA blocks
-  constexpr int NI = BN / 128;              // 32-column MFMA blocks per wave
+  constexpr int WN = 4 / WM;                // wave grid WM x WN
+  constexpr int WR = BM / WM, WC = BN / WN; // rows and columns of one wave
+  static_assert(WR % 32 == 0 && WC % 32 == 0, "wave block must be whole MFMA tiles");
+  constexpr int MB = WR / 32;               // 32-row MFMA blocks per wave
+  constexpr int NI = WC / 32;               // 32-column MFMA blocks per wave
   constexpr int AG = BM / 8;                // DMA groups (8 rows) of an A stage
   constexpr int BG = BN / 8;                // DMA groups of a B stage
   constexpr int AGW = AG / 4;               // A groups per wave (BM is a multiple of 32)
   constexpr int BGW = BG / 4;
   constexpr int PER = AGW + BGW;            // DMA instructions per wave per stage
   constexpr int NST = GemmTile<BM, BN>::kStages;
-  static_assert(NST >= 3, "the ring below needs three stages");
   constexpr int SA = GemmTile<BM, BN>::kA, SB = GemmTile<BM, BN>::kB;
-  __shared__ __attribute__((aligned(16))) bf16_t a0s[SA];
-  __shared__ __attribute__((aligned(16))) bf16_t a1s[SA];
-  __shared__ __attribute__((aligned(16))) bf16_t a2s[SA];
-  __shared__ __attribute__((aligned(16))) bf16_t a3s[NST > 3 ? SA : 8];
-  __shared__ __attribute__((aligned(16))) bf16_t b0s[SB];
-  __shared__ __attribute__((aligned(16))) bf16_t b1s[SB];
-  __shared__ __attribute__((aligned(16))) bf16_t b2s[SB];
-  __shared__ __attribute__((aligned(16))) bf16_t b3s[NST > 3 ? SB : 8];
+  constexpr int ER = GemmTile<BM, BN>::kEpRows;
+  // stage buffers A0..A(NST-1), B0..B(NST-1), reused by the epilogue
+  __shared__ __attribute__((aligned(16))) unsigned char smem[GemmTile<BM, BN>::kLdsBytes];
+  bf16_t* const a0s = reinterpret_cast<bf16_t*>(smem);
+  bf16_t* const a1s = a0s + SA;
+  bf16_t* const a2s = a0s + 2 * SA;
+  bf16_t* const a3s = a0s + 3 * SA;
+  bf16_t* const b0s = a0s + NST * SA;
+  bf16_t* const b1s = b0s + SB;
+  bf16_t* const b2s = b0s + 2 * SB;
+  bf16_t* const b3s = b0s + 3 * SB;
   auto abuf = [&](auto i) -> bf16_t* {
     constexpr int I = decltype(i)::value;
     if constexpr (I == 0) return a0s; else if constexpr (I == 1) return a1s;
@@ -146,17 +189,19 @@ gemm_qkv_bf16_kernel(GemmArgs a) {
     else if constexpr (I == 2) return b2s; else return b3s;
   };
 
-  int t = blockIdx.y;
+  int tx, t, kz;
+  xcd_tile(tx, t, kz);
   const int seg = segment_of(a.n_tiles, t);
   const int n0 = t * BN;                    // first column inside the segment
-  const int m0 = blockIdx.x * BM;
+  const int m0 = tx * BM;
   const int K = a.K;
-  const int kz0 = blockIdx.z * a.k_len;     // first k of this slice
+  const int kz0 = kz * a.k_len;             // first k of this slice
   const bf16_t* X = static_cast<const bf16_t*>(a.x) + kz0;
   const bf16_t* W = static_cast<const bf16_t*>(a.w) + static_cast<int64_t>(a.seg_w_row0[seg] + n0) * K + kz0;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wr = w / WN, wc = w % WN;       // this wave's block of the tile
   // DMA slots: lane -> (row lane/8 of a group, physical chunk lane%8)
   const int drow = lane >> 3, dchunk = lane & 7;
   const bf16_t* asrc[AGW];
@@ -169,13 +214,13 @@ gemm_qkv_bf16_kernel(GemmArgs a) {
       src = a.row_src ? static_cast<int64_t>(a.row_src[m]) : m;
       if (src < 0 || src >= a.x_rows) src = 0;     // row skipped at the store
     }
-    asrc[i] = X + src * K + ((dchunk ^ (row & 7)) << 3);
+    asrc[i] = X + src * K + (gchunk(row, dchunk) << 3);
   }
   const bf16_t* bsrc[BGW];
 #pragma unroll
   for (int i = 0; i < BGW; ++i) {
     const int row = (w + 4 * i) * 8 + drow;
-    bsrc[i] = W + static_cast<int64_t>(row) * K + ((dchunk ^ (row & 7)) << 3);
+    bsrc[i] = W + static_cast<int64_t>(row) * K + (gchunk(row, dchunk) << 3);
   }
   auto dma_stage = [&](bf16_t* as, bf16_t* bs, int k0) {
 #pragma unroll
@@ -184,13 +229,37 @@ gemm_qkv_bf16_kernel(GemmArgs a) {
     for (int i = 0; i < BGW; ++i) dma16(bsrc[i] + k0, bs + (w + 4 * i) * 8 * kBK);
   };
 
+  // The epilogue's rows (thread tid handles units tid + 256 i of each round;
+  // a unit is 8 low channels of a head plus their partners in one row): read
+  // their positions and validity now, off the epilogue's critical path.
+  constexpr int UPR = BN / 16;                          // units per row
+  constexpr int UPT = ER * UPR / kGThreads;             // units per thread per round
+  static_assert(ER * UPR % kGThreads == 0, "whole units per thread");
+  constexpr int ROUNDS = (BM + ER - 1) / ER;
+  int epos[ROUNDS][UPT];
+  if (!a.partial) {
+#pragma unroll
+    for (int rd = 0; rd < ROUNDS; ++rd)
+#pragma unroll
+      for (int i = 0; i < UPT; ++i) {
+        const int m = m0 + rd * ER + (tid + kGThreads * i) / UPR;
+        int pos = -1;                                   // -1: row not stored
+        if (rd * ER + (tid + kGThreads * i) / UPR < BM && m < a.M && row_ok(a, m)) {
+          pos = a.row_pos[m];
+          if (seg < 2 && (pos < 0 || pos >= a.rope_n)) pos = -1;
+          if (seg == 2) pos = 0;
+        }
+        epos[rd][i] = pos;
+      }
+  }
+
   // operand read offsets (the swizzle depends on row mod 8 = lane mod 8)
   const int lr = lane & 31, hf = lane >> 5;
   int aoff[kBK / 16], boff[kBK / 16];
 #pragma unroll
   for (int kk = 0; kk < kBK / 16; ++kk) {
-    aoff[kk] = gswz(lr, 2 * kk + hf);
-    boff[kk] = gswz(32 * NI * w + lr, 2 * kk + hf);   // + 32 ni rows
+    aoff[kk] = gswz(WR * wr + lr, 2 * kk + hf);   // + 32 mi rows
+    boff[kk] = gswz(WC * wc + lr, 2 * kk + hf);   // + 32 ni rows
   }
 
   f32x16_t acc[MB][NI];
@@ -201,42 +270,32 @@ gemm_qkv_bf16_kernel(GemmArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // operand fragments of k-step kk+1 are read while the MFMAs of kk run
-  auto compute = [&](const bf16_t* as, const bf16_t* bs) {
-    constexpr int KK = kBK / 16;
-    bf16x8_t af[2][MB], bfr[2][NI];
-    auto load_frags = [&](int slot, int kk) {
+  // Operand fragments of k-step kk+1 are read while the MFMAs of kk run, and
+  // across stages: the first fragments of stage k+1 are read before the last
+  // MFMAs of stage k.
+  constexpr int KK = kBK / 16;
+  bf16x8_t af[2][MB], bfr[2][NI];
+  auto load_frags = [&](const bf16_t* as, const bf16_t* bs, int slot, int kk) {
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni)
+      bfr[slot][ni] = *reinterpret_cast<const bf16x8_t*>(bs + ni * 32 * kBK + boff[kk]);
+#pragma unroll
+    for (int mi = 0; mi < MB; ++mi)
+      af[slot][mi] = *reinterpret_cast<const bf16x8_t*>(as + mi * 32 * kBK + aoff[kk]);
+  };
+  auto mfmas = [&](int slot) {
+#pragma unroll
+    for (int mi = 0; mi < MB; ++mi)
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni)
-        bfr[slot][ni] = *reinterpret_cast<const bf16x8_t*>(bs + ni * 32 * kBK + boff[kk]);
-#pragma unroll
-      for (int mi = 0; mi < MB; ++mi)
-        af[slot][mi] = *reinterpret_cast<const bf16x8_t*>(as + mi * 32 * kBK + aoff[kk]);
-    };
-    load_frags(0, 0);
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      const int cur = kk & 1;
-      if (kk + 1 < KK) load_frags(cur ^ 1, kk + 1);
-#pragma unroll
-      for (int mi = 0; mi < MB; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][mi], bfr[cur][ni], acc[mi][ni], 0, 0, 0);
-    }
-    // instruction order for the scheduler: fragments of k-step 0, then for
-    // each k-step the reads of the next one ahead of its own MFMAs
-    __builtin_amdgcn_sched_group_barrier(0x100, MB + NI, 0);
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      if (kk + 1 < KK) __builtin_amdgcn_sched_group_barrier(0x100, MB + NI, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, MB * NI, 0);
-    }
+        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[slot][mi], bfr[slot][ni], acc[mi][ni], 0, 0, 0);
   };
 
-  // Ring of NST stage buffers.  Stage k lives in buffer k % NST.  At stage k:
-  // wait for its copies and meet (which also means every wave is done with
-  // stage k-1), refill buffer (k-1) % NST with stage k+NST-1, compute k.
+  // Ring of NST stage buffers; stage k lives in buffer k % NST and all NST
+  // are in flight.  During stage k, once every wave holds the fragments of
+  // its last k-step, the waves meet (which also means stage k+1 has landed),
+  // buffer k % NST is refilled with stage k+NST and the first fragments of
+  // stage k+1 are read; then the last MFMAs of stage k run.
   const int nk = a.k_len / kBK;
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
@@ -244,36 +303,70 @@ gemm_qkv_bf16_kernel(GemmArgs a) {
   using I3 = std::integral_constant<int, 3>;
   dma_stage(abuf(I0{}), bbuf(I0{}), 0);
   if (1 < nk) dma_stage(abuf(I1{}), bbuf(I1{}), kBK);
-  if (NST > 3 && 2 < nk) dma_stage(abuf(I2{}), bbuf(I2{}), 2 * kBK);
-  auto stage = [&](int k, auto cur, auto prev) {
-    // copies issued after stage k: stages k+1 .. min(k+NST-2, nk-1)
-    if (k + NST - 2 < nk) dma_wait_barrier<(NST - 2) * PER>();
-    else if (NST > 3 && k + 1 < nk) dma_wait_barrier<PER>();
+  if (NST > 2 && 2 < nk) dma_stage(abuf(I2{}), bbuf(I2{}), 2 * kBK);
+  if (NST > 3 && 3 < nk) dma_stage(abuf(I3{}), bbuf(I3{}), 3 * kBK);
+  // stage 0 landed: the copies of stages 1 .. min(NST, nk) - 1 may be pending
+  {
+    const int pend = min(NST, nk) - 1;
+    if (pend >= 3) dma_wait_barrier<3 * PER>();
+    else if (pend == 2) dma_wait_barrier<2 * PER>();
+    else if (pend == 1) dma_wait_barrier<PER>();
     else dma_wait_barrier<0>();
-    if (k + NST - 1 < nk) dma_stage(abuf(prev), bbuf(prev), (k + NST - 1) * kBK);
-    compute(abuf(cur), bbuf(cur));
+  }
+  load_frags(abuf(I0{}), bbuf(I0{}), 0, 0);
+  auto stage = [&](int k, auto cur, auto next) {
+#pragma unroll
+    for (int kk = 0; kk + 1 < KK; ++kk) {
+      load_frags(abuf(cur), bbuf(cur), (kk + 1) & 1, kk + 1);
+      mfmas(kk & 1);
+    }
+    // issue order: reads of k-step kk+1, then the MFMAs of kk
+#pragma unroll
+    for (int kk = 0; kk + 1 < KK; ++kk) {
+      __builtin_amdgcn_sched_group_barrier(0x100, MB + NI, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, MB * NI, 0);
+    }
+    if (k + 1 < nk) {
+      // copies still allowed in flight: stages k+2 .. min(k+NST-1, nk-1)
+      const int pend = min(NST - 2, nk - 2 - k);
+      if (pend >= 2) lds_dma_wait_barrier<2 * PER>();
+      else if (pend == 1) lds_dma_wait_barrier<PER>();
+      else lds_dma_wait_barrier<0>();
+      if (k + NST < nk) dma_stage(abuf(cur), bbuf(cur), (k + NST) * kBK);
+    }
+    // after the last stage these reads are unused (their buffer is settled:
+    // no copy is in flight); one unconditional path keeps the compiler's
+    // LDS wait counts exact for the MFMAs below
+    load_frags(abuf(next), bbuf(next), 0, 0);
+    mfmas((KK - 1) & 1);
+    __builtin_amdgcn_sched_group_barrier(0x100, MB + NI, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, MB * NI, 0);
   };
   for (int kt = 0; kt < nk; kt += NST) {
     if constexpr (NST == 4) {
-      stage(kt, I0{}, I3{});
+      stage(kt, I0{}, I1{});
+      if (kt + 1 < nk) stage(kt + 1, I1{}, I2{});
+      if (kt + 2 < nk) stage(kt + 2, I2{}, I3{});
+      if (kt + 3 < nk) stage(kt + 3, I3{}, I0{});
+    } else if constexpr (NST == 2) {
+      stage(kt, I0{}, I1{});
       if (kt + 1 < nk) stage(kt + 1, I1{}, I0{});
-      if (kt + 2 < nk) stage(kt + 2, I2{}, I1{});
-      if (kt + 3 < nk) stage(kt + 3, I3{}, I2{});
     } else {
-      stage(kt, I0{}, I2{});
-      if (kt + 1 < nk) stage(kt + 1, I1{}, I0{});
-      if (kt + 2 < nk) stage(kt + 2, I2{}, I1{});
+      stage(kt, I0{}, I1{});
+      if (kt + 1 < nk) stage(kt + 1, I1{}, I2{});
+      if (kt + 2 < nk) stage(kt + 2, I2{}, I0{});
     }
   }
+
   if (a.partial) {
     // raw slice sums; each 32-lane run stores 128 contiguous bytes of a row
-    float* part = a.partial + static_cast<int64_t>(blockIdx.z) * a.M * a.c_total;
-    const int c0 = a.seg_w_row0[seg] + n0 + 32 * NI * w + lr;
+    float* part = a.partial + static_cast<int64_t>(kz) * a.M * a.c_total;
+    const int c0 = a.seg_w_row0[seg] + n0 + WC * wc + lr;
 #pragma unroll
     for (int mi = 0; mi < MB; ++mi)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int m = m0 + mi * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+        const int m = m0 + WR * wr + mi * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
         if (m >= a.M) continue;
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni)
@@ -283,9 +376,9 @@ gemm_qkv_bf16_kernel(GemmArgs a) {
   }
   __syncthreads();
 
-  // epilogue through LDS, 32 rows at a time (b0s holds 32 x BN fp32)
-  float* ep = reinterpret_cast<float*>(b0s);
-  auto eidx = [](int row, int col) {        // fp32 element index, 16-B chunks swizzled
+  // epilogue through LDS, ER rows per round as fp32 (16-B chunks swizzled)
+  float* ep = reinterpret_cast<float*>(smem);
+  auto eidx = [](int row, int col) {
     return row * BN + ((((col >> 2) ^ (row & 31))) << 2) + (col & 3);
   };
   const bool rope = seg < 2;
@@ -293,51 +386,64 @@ gemm_qkv_bf16_kernel(GemmArgs a) {
   const int ld = a.seg_heads[seg] * d;
   bf16_t* out = static_cast<bf16_t*>(a.out[seg]);
 #pragma unroll
-  for (int mi = 0; mi < MB; ++mi) {
-    if (m0 + mi * 32 >= a.M) break;         // block-uniform
+  for (int rd = 0; rd < ROUNDS; ++rd) {
+    if (m0 + rd * ER >= a.M) break;          // block-uniform
+    // rows [rd ER, rd ER + ER) of the tile: this wave's 32-row blocks in them
 #pragma unroll
-    for (int ni = 0; ni < NI; ++ni)
+    for (int mi = 0; mi < MB; ++mi) {
+      const int trow = WR * wr + 32 * mi;    // first tile row of the block
+      if (trow < rd * ER || trow >= rd * ER + ER) continue;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = 8 * (r >> 2) + 4 * hf + (r & 3);
-        ep[eidx(row, 32 * NI * w + 32 * ni + lr)] = acc[mi][ni][r];
-      }
-    __syncthreads();
-    // 32 rows x (BN / 16) units: unit = 8 low channels + their partners
-    for (int u = tid; u < 32 * (BN / 16); u += kGThreads) {
-      const int row = u / (BN / 16);
-      const int p = u % (BN / 16);          // which 8-wide low-half chunk of the tile
-      const int head = p / (half / 8);      // head inside the tile
-      const int j0 = (p % (half / 8)) * 8;  // channel inside the head's low half
-      const int cl = head * d + j0, ch = cl + half;
-      const int m = m0 + mi * 32 + row;
-      if (m >= a.M || !row_ok(a, m)) continue;
-      float lo[8], hi[8];
+      for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
-      for (int hpart = 0; hpart < 2; ++hpart) {
-        const float4 l4 = *reinterpret_cast<const float4*>(&ep[eidx(row, cl + 4 * hpart)]);
-        const float4 h4 = *reinterpret_cast<const float4*>(&ep[eidx(row, ch + 4 * hpart)]);
-        lo[4 * hpart] = l4.x; lo[4 * hpart + 1] = l4.y; lo[4 * hpart + 2] = l4.z; lo[4 * hpart + 3] = l4.w;
-        hi[4 * hpart] = h4.x; hi[4 * hpart + 1] = h4.y; hi[4 * hpart + 2] = h4.z; hi[4 * hpart + 3] = h4.w;
-      }
-      if (rope) {
-        const int pos = a.row_pos[m];
-        if (pos < 0 || pos >= a.rope_n) continue;
-        float cs[8], sn[8];
-        Elem<float>::load8(a.rope_cos + static_cast<int64_t>(pos) * half + j0, cs);
-        Elem<float>::load8(a.rope_sin + static_cast<int64_t>(pos) * half + j0, sn);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float x = lo[e], y = hi[e];
-          lo[e] = x * cs[e] - y * sn[e];
-          hi[e] = y * cs[e] + x * sn[e];
+        for (int r = 0; r < 16; ++r) {
+          const int row = trow - rd * ER + 8 * (r >> 2) + 4 * hf + (r & 3);
+          ep[eidx(row, WC * wc + 32 * ni + lr)] = acc[mi][ni][r];
         }
-      }
-      bf16_t* orow = out + static_cast<int64_t>(m) * ld + n0;
-      Elem<bf16_t>::store8(orow + cl, lo);
-      Elem<bf16_t>::store8(orow + ch, hi);
     }
     __syncthreads();
+    // read every unit's rope factors first, then rotate and store
+    float lo[UPT][8], hi[UPT][8], cs[UPT][8], sn[UPT][8];
+#pragma unroll
+    for (int i = 0; i < UPT; ++i) {
+      const int u = tid + kGThreads * i;
+      const int row = u / UPR, p = u % UPR;
+      const int head = p / (half / 8), j0 = (p % (half / 8)) * 8;
+      const int cl = head * d + j0, ch = cl + half;
+      const int pos = epos[rd][i];
+      if (rope && pos >= 0) {
+        Elem<float>::load8(a.rope_cos + static_cast<int64_t>(pos) * half + j0, cs[i]);
+        Elem<float>::load8(a.rope_sin + static_cast<int64_t>(pos) * half + j0, sn[i]);
+      }
+#pragma unroll
+      for (int hp = 0; hp < 2; ++hp) {
+        const float4 l4 = *reinterpret_cast<const float4*>(&ep[eidx(row, cl + 4 * hp)]);
+        const float4 h4 = *reinterpret_cast<const float4*>(&ep[eidx(row, ch + 4 * hp)]);
+        lo[i][4 * hp] = l4.x; lo[i][4 * hp + 1] = l4.y; lo[i][4 * hp + 2] = l4.z; lo[i][4 * hp + 3] = l4.w;
+        hi[i][4 * hp] = h4.x; hi[i][4 * hp + 1] = h4.y; hi[i][4 * hp + 2] = h4.z; hi[i][4 * hp + 3] = h4.w;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < UPT; ++i) {
+      const int u = tid + kGThreads * i;
+      const int row = u / UPR, p = u % UPR;
+      const int head = p / (half / 8), j0 = (p % (half / 8)) * 8;
+      const int cl = head * d + j0, ch = cl + half;
+      const int pos = epos[rd][i];
+      if (pos < 0) continue;
+      if (rope) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x = lo[i][e], y = hi[i][e];
+          lo[i][e] = x * cs[i][e] - y * sn[i][e];
+          hi[i][e] = y * cs[i][e] + x * sn[i][e];
+        }
+      }
+      bf16_t* orow = out + static_cast<int64_t>(m0 + rd * ER + row) * ld + n0;
+      Elem<bf16_t>::store8(orow + cl, lo[i]);
+      Elem<bf16_t>::store8(orow + ch, hi[i]);
+    }
+    if (rd + 1 < ROUNDS) __syncthreads();
   }
 }
 
@@ -493,7 +599,7 @@ __global__ void __launch_bounds__(256) gemm_qkv_f32_kernel(GemmArgs a, int pair_
 namespace {
 
 struct Bf16Plan {
-  int bm, bn, splits;
+  int bm, bn, wm, splits;
   int n_tiles[3];           // column tiles per segment at bn
 };
 
@@ -516,7 +622,7 @@ Bf16Plan plan_bf16(const kvf_layer_desc& L, int M, uint32_t mask) {
     }
     return total;
   };
-  Bf16Plan p{128, 256, 1, {0, 0, 0}};
+  Bf16Plan p{128, 256, 1, 1, {0, 0, 0}};
   for (int s = 0; s < 3; ++s)
     if ((mask & bits[s]) && (heads[s] * L.head_dim) % 256 != 0) p.bn = 128;
   const int total = tiles(p.bn, p.n_tiles);
@@ -531,7 +637,7 @@ Bf16Plan plan_bf16(const kvf_layer_desc& L, int M, uint32_t mask) {
     }
   }
   if (static_cast<int64_t>(ceil_div(M, p.bm)) * total >= 128) return p;
-  Bf16Plan q{M <= 64 ? 64 : 128, 128, 1, {0, 0, 0}};
+  Bf16Plan q{M <= 64 ? 64 : 128, 128, 1, 1, {0, 0, 0}};
   const int64_t base = static_cast<int64_t>(ceil_div(M, q.bm)) * tiles(128, q.n_tiles);
   while (base * q.splits * 2 <= 512 && L.hidden % (q.splits * 2 * kBK) == 0 &&
          L.hidden / (q.splits * 2) >= 256)
@@ -595,18 +701,19 @@ hipError_t launch_recompute(const kvf_layer_desc& L, const void* x, int64_t x_ro
     }
     const dim3 grid(ceil_div(M, p.bm), total, p.splits);
     bool launched = false;
-#define KVF_GEMM_CASE(BM_, BN_)                                                           \
-  if (!launched && p.bm == BM_ && p.bn == BN_) {                                          \
-    hipLaunchKernelGGL((gemm_qkv_bf16_kernel<BM_, BN_>), grid, dim3(kGThreads), 0, st, a); \
-    launched = true;                                                                      \
+#define KVF_GEMM_CASE(BM_, BN_, WM_)                                                       \
+  if (!launched && p.bm == BM_ && p.bn == BN_ && p.wm == WM_) {                            \
+    hipLaunchKernelGGL((gemm_qkv_bf16_kernel<BM_, BN_, WM_>), grid, dim3(kGThreads), 0, st, \
+                       a);                                                                 \
+    launched = true;                                                                       \
   }
-    KVF_GEMM_CASE(256, 128)
-    KVF_GEMM_CASE(192, 128)
-    KVF_GEMM_CASE(160, 128)
-    KVF_GEMM_CASE(128, 128)
-    KVF_GEMM_CASE(64, 128)
-    KVF_GEMM_CASE(160, 256)
-    KVF_GEMM_CASE(128, 256)
+    KVF_GEMM_CASE(256, 128, 1)
+    KVF_GEMM_CASE(192, 128, 1)
+    KVF_GEMM_CASE(160, 128, 1)
+    KVF_GEMM_CASE(128, 128, 1)
+    KVF_GEMM_CASE(64, 128, 1)
+    KVF_GEMM_CASE(160, 256, 1)
+    KVF_GEMM_CASE(128, 256, 1)
 #undef KVF_GEMM_CASE
     if (!launched) return hipErrorInvalidValue;
     if (p.splits > 1) {
