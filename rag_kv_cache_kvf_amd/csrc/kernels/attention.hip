@@ -17,10 +17,8 @@
 //  * Scores are computed transposed, S^T = K Q^T (keys on the MFMA rows), so
 //    each lane holds one query vector's scores and the online-softmax max/sum
 //    are lane-local plus one cross-half shuffle.  The probabilities then feed
-//    O^T += V^T P^T directly from registers: the K dimension of that MFMA is
-//    permuted to match the accumulator layout, and V is staged in LDS in a
-//    4-key interleaved layout so each lane reads 4 consecutive keys of one
-//    channel with one 8-byte LDS read.
+//    O^T += V^T P^T directly from registers; the V operand comes from the
+//    row-major V tile through transposing LDS reads (ds_read_b64_tr_b16).
 //  * The causal mask uses each row's own position; keys beyond the tile's
 //    last position are never loaded.
 // The mass score runs the same loop in "statistics only" mode over key
@@ -72,9 +70,9 @@ struct AttnArgs {
 // 128-key tile.  K and V tiles are copied global -> LDS by the DMA path
 // (global_load_lds, 16 bytes per lane, no registers involved) into two
 // static buffers: tile t+1 streams in while tile t is computed.  Both tiles
-// are row-major with the 16-byte chunks of row r XOR-swizzled by r mod
-// (D/8), so the key-row reads of the score MFMA and the transposing reads of
-// V (ds_read_b64_tr_b16, one 4-key x 4-channel transpose per 16 lanes) hit
+// are row-major with the 16-byte chunks of row r XOR-swizzled (chunk_xor), so
+// the key-row reads of the score MFMA and the transposing reads of V
+// (ds_read_b64_tr_b16, one 4-key x 4-channel transpose per 16 lanes) hit
 // distinct banks.
 constexpr int kAT = 128;         // keys per tile (two halves of 64)
 constexpr int kAThreads = 512;
@@ -84,10 +82,23 @@ typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) const void global_cvoid_t;
 
+// XOR applied to the 16-byte chunk index of tile row `row`.  LDS serves a
+// wide read over 64 banks (256 B) per cycle: 16 lanes of a 16-byte read or
+// 32 lanes of an 8-byte one.
+//  D = 128 (256-B rows, each row spans all banks): the 16 rows of a key read
+//    need 16 distinct chunks, and the V transpose reads 4 consecutive rows x 4
+//    adjacent chunks at once, so rows 0..3 must move the chunk into different
+//    groups of 4: a rotation of the row's low 4 bits, (r & 3) << 2 | (r >> 2) & 3.
+//  D = 64 (128-B rows, two rows per bank window): the same conditions apply
+//    to row pairs, on bits 1..3 of the row.
 template <int D>
-__device__ __forceinline__ int swz(int row, int d) {       // element index in a tile
-  constexpr int CPR = D / 8;
-  return row * D + ((((d >> 3) ^ (row & (CPR - 1)))) << 3) + (d & 7);
+__device__ __forceinline__ int chunk_xor(int row) {
+  if constexpr (D == 128) {
+    return ((row & 3) << 2) | ((row >> 2) & 3);
+  } else {
+    const int x = (row >> 1) & 7;
+    return ((x & 1) << 2) | (x >> 1);
+  }
 }
 
 template <int D, bool STATS_ONLY>
@@ -178,7 +189,7 @@ __global__ void __launch_bounds__(kAThreads) attn_bf16_kernel(AttnArgs a) {
     for (int j = 0; j < NDMA; ++j) {
       const int grp = w * NDMA + j;
       const int row = grp * RPI + dma_rr;
-      const int q = dma_p ^ (row & (CPR - 1));            // logical chunk held by this slot
+      const int q = dma_p ^ chunk_xor<D>(row);            // logical chunk held by this slot
       const int key = min(kb0 + row, klim - 1);           // tail rows repeat a valid key
       const bf16_t* src = src_req + static_cast<int64_t>(key) * row_stride + q * 8;
       __builtin_amdgcn_global_load_lds((global_cvoid_t*)(src), (lds_void_t*)(dst + grp * RPI * D), 16, 0, 0);
@@ -196,13 +207,13 @@ __global__ void __launch_bounds__(kAThreads) attn_bf16_kernel(AttnArgs a) {
   const f32x16_t zero16 = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   const bf16x2_t ones2 = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
   // LDS element offsets of this lane's operand reads, with the XOR swizzle
-  // resolved once: the swizzle term depends only on row mod D/8, which the
+  // resolved once: the swizzle term depends only on row mod 16, which the
   // 32-key and 16-key block steps (multiples of 16 rows) do not change.
   // K rows 64 kg + 32 kb + c, channel chunk 2 kk + hf:
   int koff[KS];
 #pragma unroll
   for (int kk = 0; kk < KS; ++kk)
-    koff[kk] = (64 * kg + c) * D + (((2 * kk + hf) ^ (c & (CPR - 1))) << 3);
+    koff[kk] = (64 * kg + c) * D + (((2 * kk + hf) ^ chunk_xor<D>(c)) << 3);
   // transposed V reads: lane i of 16-lane group G reads keys 4 hf + i/4 (+8)
   // and channels 32 db + 16 (G%2) + 4 (i%4) .. +3
   const int tr_key = 4 * hf + ((lane & 15) >> 2);
@@ -213,7 +224,7 @@ __global__ void __launch_bounds__(kAThreads) attn_bf16_kernel(AttnArgs a) {
     const int row = tr_key + 8 * hl;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
-      voff[hl][db] = (64 * kg + row) * D + ((((4 * db + (tr_d >> 3)) ^ (row & (CPR - 1)))) << 3) + (tr_d & 7);
+      voff[hl][db] = (64 * kg + row) * D + ((((4 * db + (tr_d >> 3)) ^ chunk_xor<D>(row))) << 3) + (tr_d & 7);
   }
 
   // One 128-key tile computed from (ks, vs).  MASK selects the variant that
