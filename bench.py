@@ -49,7 +49,6 @@ CALL_KERNEL = {
     "rerotate": ("rerotate_kernel", "kernels/rope_rerotate.hip"),
     "k_probe": ("gemm_qkv_bf16_kernel", "kernels/gemm_qkv.hip"),
     "u_probe": ("gemm_qkv_bf16_kernel", "kernels/gemm_qkv.hip"),
-    "u_scatter": ("scatter_kernel", "kernels/scatter_deviation.hip"),
     "score": ("mass_colsum_bf16_kernel", "kernels/attention.hip"),
     "select": ("topk_kernel", "kernels/topk.hip"),
     "recompute": ("gemm_qkv_bf16_kernel", "kernels/gemm_qkv.hip"),
@@ -100,7 +99,6 @@ def call_work(g):
         work["recompute"] = ("mfma", 2.0 * hid * d * (hq + hkv) * M)
     else:
         work["u_probe"] = ("mfma", 2.0 * hid * d * (hq + 2 * hkv) * nU)
-        work["u_scatter"] = ("hbm", nU * 4 * krow)
         flops = 0.0
         for r in range(b.n_req):
             U = b.n_query(r)
@@ -110,7 +108,8 @@ def call_work(g):
         work["score"] = ("mfma", flops)
         work["recompute"] = ("mfma", 2.0 * hid * d * (hq + 2 * hkv) * M)
     work["select"] = ("hbm", n_ctx * 4 + M * 8)       # scores in; row ids + positions out
-    work["scatter"] = ("hbm", M * 4 * krow)           # new K,V in; fused rows out
+    if g.mode == "deviation":
+        work["scatter"] = ("hbm", M * 2 * krow)       # probe K in; fused K rows out
     work["attention"] = ("mfma", 4.0 * d * hq * float((pos + 1).sum()))   # QK^T + PV, causal
     return work
 

@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define KVF_ABI_VERSION 2
+#define KVF_ABI_VERSION 3
 #define KVF_MAX_REQ 64      /* requests per call (batch metadata is passed by value) */
 
 typedef enum {
@@ -212,6 +212,11 @@ size_t kvf_select_workspace_size(const kvf_batch* batch);
  * position is outside the rope table is left unwritten.
  * The same call builds per-chunk caches ahead of serving ([QCF] 2.1.2 Eq. 3):
  * pass the cached hidden states with chunk-local positions and mask K|V.
+ * kv_out_row (optional, [M]): when given, K/V row m is written to row
+ * kv_out_row[m] of k_out / v_out, which then hold kv_out_rows rows - the
+ * fresh K/V go straight into the fused cache, which fuses S5's scatter
+ * ([QCF] 2.1.3 Eq. 7) into this call.  Entries outside [0, kv_out_rows) are
+ * skipped; destination rows must be unique.  Q is always written densely.
  * workspace: kvf_recompute_workspace_size(layer, M, out_mask) bytes of
  * device memory (may be NULL when that is 0); calls with few rows use it for
  * per-slice partial sums, so two calls sharing one workspace must be ordered.
@@ -224,7 +229,8 @@ kvf_status kvf_recompute_qkv(const kvf_layer_desc* layer, const void* x,
                              const void* w_qkv, uint32_t out_mask,
                              const float* rope_cos, const float* rope_sin,
                              int32_t rope_n_pos, void* q_out, void* k_out,
-                             void* v_out, void* workspace,
+                             void* v_out, const int32_t* kv_out_row,
+                             int64_t kv_out_rows, void* workspace,
                              size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------

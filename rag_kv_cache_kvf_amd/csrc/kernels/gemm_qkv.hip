@@ -45,7 +45,18 @@ struct GemmArgs {
   float* partial;
   int k_len;
   int c_total;
+  // K/V destination rows: row m of K and V goes to row kv_row[m] of its
+  // output (kv_rows rows; entries outside are skipped); nullptr: row m
+  const int32_t* kv_row;
+  int64_t kv_rows;
 };
+
+// Output row of row m in segment seg (0 Q, 1 K, 2 V), or -1 to skip it.
+__device__ __forceinline__ int64_t out_row(const GemmArgs& a, int seg, int m) {
+  if (seg == 0 || !a.kv_row) return m;
+  const int64_t r = a.kv_row[m];
+  return (r >= 0 && r < a.kv_rows) ? r : -1;
+}
 
 // Row m is computed and stored only if its source row and (for Q/K) its
 // position are inside the tables.
@@ -237,6 +248,7 @@ gemm_qkv_bf16_kernel(GemmArgs a) {
   static_assert(ER * UPR % kGThreads == 0, "whole units per thread");
   constexpr int ROUNDS = (BM + ER - 1) / ER;
   int epos[ROUNDS][UPT];
+  int64_t erow[ROUNDS][UPT];
   if (!a.partial) {
 #pragma unroll
     for (int rd = 0; rd < ROUNDS; ++rd)
@@ -244,12 +256,16 @@ gemm_qkv_bf16_kernel(GemmArgs a) {
       for (int i = 0; i < UPT; ++i) {
         const int m = m0 + rd * ER + (tid + kGThreads * i) / UPR;
         int pos = -1;                                   // -1: row not stored
+        int64_t orow = -1;
         if (rd * ER + (tid + kGThreads * i) / UPR < BM && m < a.M && row_ok(a, m)) {
           pos = a.row_pos[m];
           if (seg < 2 && (pos < 0 || pos >= a.rope_n)) pos = -1;
           if (seg == 2) pos = 0;
+          orow = out_row(a, seg, m);
+          if (orow < 0) pos = -1;
         }
         epos[rd][i] = pos;
+        erow[rd][i] = orow;
       }
   }
 
@@ -425,8 +441,7 @@ gemm_qkv_bf16_kernel(GemmArgs a) {
     }
 #pragma unroll
     for (int i = 0; i < UPT; ++i) {
-      const int u = tid + kGThreads * i;
-      const int row = u / UPR, p = u % UPR;
+      const int p = (tid + kGThreads * i) % UPR;
       const int head = p / (half / 8), j0 = (p % (half / 8)) * 8;
       const int cl = head * d + j0, ch = cl + half;
       const int pos = epos[rd][i];
@@ -439,7 +454,7 @@ gemm_qkv_bf16_kernel(GemmArgs a) {
           hi[i][e] = y * cs[i][e] + x * sn[i][e];
         }
       }
-      bf16_t* orow = out + static_cast<int64_t>(m0 + rd * ER + row) * ld + n0;
+      bf16_t* orow = out + erow[rd][i] * ld + n0;
       Elem<bf16_t>::store8(orow + cl, lo[i]);
       Elem<bf16_t>::store8(orow + ch, hi[i]);
     }
@@ -498,7 +513,9 @@ __global__ void __launch_bounds__(256) gemm_split_finish_kernel(GemmArgs a, int 
       hi[e] = y * cs[e] + x * sn[e];
     }
   }
-  bf16_t* orow = static_cast<bf16_t*>(a.out[seg]) + static_cast<int64_t>(m) * a.seg_heads[seg] * d;
+  const int64_t dst = out_row(a, seg, m);
+  if (dst < 0) return;
+  bf16_t* orow = static_cast<bf16_t*>(a.out[seg]) + dst * a.seg_heads[seg] * d;
   Elem<bf16_t>::store8(orow + cl, lo);
   Elem<bf16_t>::store8(orow + ch, hi);
 }
@@ -591,8 +608,10 @@ __global__ void __launch_bounds__(256) gemm_qkv_f32_kernel(GemmArgs a, int pair_
       hi = hi * c + lo * s;
       lo = l2;
     }
-    out[static_cast<int64_t>(row) * ld + head * d + j] = lo;
-    out[static_cast<int64_t>(row) * ld + head * d + half + j] = hi;
+    const int64_t dst = out_row(a, seg, row);
+    if (dst < 0) continue;
+    out[dst * ld + head * d + j] = lo;
+    out[dst * ld + head * d + half + j] = hi;
   }
 }
 
@@ -658,8 +677,11 @@ size_t recompute_workspace(const kvf_layer_desc& L, int M, uint32_t mask) {
 hipError_t launch_recompute(const kvf_layer_desc& L, const void* x, int64_t x_rows,
                             const int32_t* row_src, const int32_t* row_pos, int M, const void* w,
                             uint32_t mask, const float* rc, const float* rs, int rope_n, void* q,
-                            void* k, void* v, void* ws, size_t ws_bytes, hipStream_t st) {
+                            void* k, void* v, const int32_t* kv_row, int64_t kv_rows, void* ws,
+                            size_t ws_bytes, hipStream_t st) {
   GemmArgs a{};
+  a.kv_row = kv_row;
+  a.kv_rows = kv_rows;
   a.x = x;
   a.x_rows = x_rows;
   a.row_src = row_src;

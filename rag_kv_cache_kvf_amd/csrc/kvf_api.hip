@@ -260,7 +260,8 @@ kvf_status kvf_recompute_qkv(const kvf_layer_desc* layer, const void* x, int64_t
                              const int32_t* row_src, const int32_t* row_pos, int32_t M,
                              const void* w_qkv, uint32_t out_mask, const float* rope_cos,
                              const float* rope_sin, int32_t rope_n_pos, void* q_out,
-                             void* k_out, void* v_out, void* workspace, size_t ws_bytes,
+                             void* k_out, void* v_out, const int32_t* kv_out_row,
+                             int64_t kv_out_rows, void* workspace, size_t ws_bytes,
                              void* stream) {
   KVF_GUARD_BEGIN
   kvf_status st = check_layer(layer);
@@ -270,6 +271,8 @@ kvf_status kvf_recompute_qkv(const kvf_layer_desc* layer, const void* x, int64_t
   if (M == 0 || out_mask == 0) return KVF_OK;
   KVF_CHECK(x && w_qkv && row_pos, KVF_ERR_INVALID_ARG, "required pointer is NULL");
   KVF_CHECK(x_rows > 0, KVF_ERR_INVALID_ARG, "x has no rows");
+  KVF_CHECK(kv_out_row == nullptr || kv_out_rows > 0, KVF_ERR_INVALID_ARG,
+            "kv_out_row needs kv_out_rows > 0");
   KVF_CHECK(row_src != nullptr || M <= x_rows, KVF_ERR_INVALID_ARG,
             "identity row map needs M <= x_rows");
   KVF_CHECK(!(out_mask & KVF_OUT_Q) || q_out, KVF_ERR_INVALID_ARG, "q_out is NULL");
@@ -286,7 +289,8 @@ kvf_status kvf_recompute_qkv(const kvf_layer_desc* layer, const void* x, int64_t
             "workspace of %zu bytes given, %zu needed", ws_bytes, need);
   return from_hip(kvf::launch_recompute(*layer, x, x_rows, row_src, row_pos, M, w_qkv, out_mask,
                                         rope_cos, rope_sin, rope_n_pos, q_out, k_out, v_out,
-                                        workspace, ws_bytes, as_stream(stream)),
+                                        kv_out_row, kv_out_rows, workspace, ws_bytes,
+                                        as_stream(stream)),
                   "kvf_recompute_qkv");
   KVF_GUARD_END
 }

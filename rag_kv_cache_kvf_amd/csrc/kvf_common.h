@@ -148,8 +148,8 @@ hipError_t launch_topk(const float* scores, const BatchArgs& B, const int32_t* k
 hipError_t launch_recompute(const kvf_layer_desc& L, const void* x, int64_t x_rows,
                             const int32_t* row_src, const int32_t* row_pos, int M,
                             const void* w, uint32_t mask, const float* rc, const float* rs,
-                            int rope_n, void* q, void* k, void* v, void* ws, size_t ws_bytes,
-                            hipStream_t st);
+                            int rope_n, void* q, void* k, void* v, const int32_t* kv_row,
+                            int64_t kv_rows, void* ws, size_t ws_bytes, hipStream_t st);
 size_t recompute_workspace(const kvf_layer_desc& L, int M, uint32_t mask);
 hipError_t launch_scatter(const kvf_layer_desc& L, const void* ks, const int32_t* ksr,
                           int64_t ks_rows, const void* vs, const int32_t* vsr, int64_t vs_rows,

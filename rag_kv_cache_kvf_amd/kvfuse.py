@@ -77,7 +77,7 @@ _SIGS = {
     "kvf_select_topk": (_I32, [_P, _BP, _IP, _P, _P, _P, _P, _SZ, _P]),
     "kvf_select_workspace_size": (_SZ, [_BP]),
     "kvf_recompute_qkv": (_I32, [_LP, _P, _I64, _P, _P, _I32, _P, ctypes.c_uint32, _P, _P, _I32,
-                                 _P, _P, _P, _P, _SZ, _P]),
+                                 _P, _P, _P, _P, _I64, _P, _SZ, _P]),
     "kvf_recompute_workspace_size": (_SZ, [_LP, _I32, ctypes.c_uint32]),
     "kvf_scatter_kv": (_I32, [_LP, _P, _P, _I64, _P, _P, _I64, _P, _I32, _P, _P, _I64, _P]),
     "kvf_sparse_q_attention": (_I32, [_LP, _BP, _P, _P, _IP, _P, _P, ctypes.c_float, _P, _P, _P]),
@@ -234,9 +234,11 @@ def recompute_qkv(layer: Layer, x: torch.Tensor, row_src: Optional[torch.Tensor]
                   rope_cos: torch.Tensor, rope_sin: torch.Tensor,
                   q_out: Optional[torch.Tensor] = None, k_out: Optional[torch.Tensor] = None,
                   v_out: Optional[torch.Tensor] = None, M: Optional[int] = None,
-                  workspace: Optional[torch.Tensor] = None, stream=None):
+                  workspace: Optional[torch.Tensor] = None, kv_out_row: Optional[torch.Tensor] = None,
+                  stream=None):
     """workspace: kvf_recompute_workspace_size bytes; allocated here when
-    omitted and needed (pass one to keep the call allocation-free)."""
+    omitted and needed (pass one to keep the call allocation-free).
+    kv_out_row: destination rows of K/V in k_out / v_out (e.g. the fused cache)."""
     d = layer.desc()
     M = int(row_pos.shape[0]) if M is None else M
     if workspace is None:
@@ -244,10 +246,14 @@ def recompute_qkv(layer: Layer, x: torch.Tensor, row_src: Optional[torch.Tensor]
         if need:
             workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    kv_rows = 0
+    if kv_out_row is not None:
+        kv_rows = min(_rows(t) for t in (k_out, v_out) if t is not None)
     _check(_lib.kvf_recompute_qkv(ctypes.byref(d), _ptr(x), _rows(x), _ptr(row_src), _ptr(row_pos),
                                   M, _ptr(w_qkv), out_mask, _ptr(rope_cos), _ptr(rope_sin),
                                   _rows(rope_cos), _ptr(q_out), _ptr(k_out), _ptr(v_out),
-                                  _ptr(workspace), ws_bytes, _stream(stream)), "kvf_recompute_qkv")
+                                  _ptr(kv_out_row), kv_rows, _ptr(workspace), ws_bytes,
+                                  _stream(stream)), "kvf_recompute_qkv")
 
 
 def recompute_workspace_size(layer: Layer, M: int, out_mask: int) -> int:

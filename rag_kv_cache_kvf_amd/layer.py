@@ -6,12 +6,15 @@ itself.  Order (all on one stream, no host synchronisation):
 
   deviation mode (KVBoost page, section 4.6.2, Algorithm 2 at one layer)
     kvf_rerotate -> kvf_recompute_qkv(all rows, K: probe K~) ->
-    kvf_score(DEVIATION) -> kvf_select_topk -> kvf_recompute_qkv(P+U, Q|V) ->
-    kvf_scatter_kv(K from the probe, V new) -> kvf_sparse_q_attention
+    kvf_score(DEVIATION) -> kvf_select_topk ->
+    kvf_recompute_qkv(P+U, Q|V; V straight into the fused cache) ->
+    kvf_scatter_kv(K of P+U from the probe) -> kvf_sparse_q_attention
   attention-mass mode (QCFuse page, section 3.2.1 at one layer)
-    kvf_rerotate -> kvf_recompute_qkv(U, Q|K|V) -> kvf_scatter_kv(U) ->
-    kvf_score(ATTN_MASS) -> kvf_select_topk -> kvf_recompute_qkv(P+U, Q|K|V)
-    -> kvf_scatter_kv(P+U) -> kvf_sparse_q_attention
+    kvf_rerotate -> kvf_recompute_qkv(U, Q|K|V; K/V into the fused cache) ->
+    kvf_score(ATTN_MASS) -> kvf_select_topk ->
+    kvf_recompute_qkv(P+U, Q|K|V; K/V into the fused cache) ->
+    kvf_sparse_q_attention
+  (the recompute call's destination-row output is the scatter of Eq. 7)
 
 The per-chunk caches are built ahead of serving (QCFuse page, section 2.1.2,
 Eq. 3) either by the caller (`pic=`) or on the GPU by this library's own
@@ -117,8 +120,6 @@ class FusedLayerGPU:
         self.rows = torch.zeros(max(M, 1), dtype=torch.int32, device=dev)
         self.pos = torch.zeros(max(M, 1), dtype=torch.int32, device=dev)
         self.q = torch.zeros((max(M, 1), hq, d), dtype=td, device=dev)
-        self.k_new = torch.zeros((max(M, 1), hkv, d), dtype=td, device=dev)
-        self.v_new = torch.zeros_like(self.k_new)
         self.out = torch.zeros((max(M, 1), hq, d), dtype=td, device=dev)
         self.lse = torch.zeros((max(M, 1), hq), dtype=torch.float32, device=dev)
         self.sm_scale = 1.0 / math.sqrt(d)
@@ -131,8 +132,6 @@ class FusedLayerGPU:
             self.k_probe = torch.zeros((T_total, hkv, d), dtype=td, device=dev)
         else:
             self.q_u = torch.zeros((max(nU, 1), hq, d), dtype=td, device=dev)
-            self.k_u = torch.zeros((max(nU, 1), hkv, d), dtype=td, device=dev)
-            self.v_u = torch.zeros_like(self.k_u)
             nbytes = kvf.score_workspace_size(kvf.KVF_SCORE_ATTN_MASS, L, self.kb, n_last_q)
             self.ws = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=dev)
         # one projection workspace for every recompute call (they are ordered
@@ -157,12 +156,8 @@ class FusedLayerGPU:
     def _u_probe(self):
         kvf.recompute_qkv(self.layer, self.x, self.u_rows, self.u_pos, self.w,
                           kvf.KVF_OUT_Q | kvf.KVF_OUT_K | kvf.KVF_OUT_V, self.rope_cos,
-                          self.rope_sin, q_out=self.q_u, k_out=self.k_u, v_out=self.v_u,
-                          workspace=self.gemm_ws)
-
-    def _u_scatter(self):
-        kvf.scatter_kv(self.layer, self.k_u, None, self.v_u, None, self.u_rows, self.fused_k,
-                       self.fused_v)
+                          self.rope_sin, q_out=self.q_u, k_out=self.fused_k, v_out=self.fused_v,
+                          kv_out_row=self.u_rows, workspace=self.gemm_ws)
 
     def _score(self):
         if self.mode == "deviation":
@@ -182,22 +177,21 @@ class FusedLayerGPU:
             # K of these rows is already in the probe
             kvf.recompute_qkv(self.layer, self.x, self.rows, self.pos, self.w,
                               kvf.KVF_OUT_Q | kvf.KVF_OUT_V, self.rope_cos, self.rope_sin,
-                              q_out=self.q, v_out=self.v_new, M=self.M, workspace=self.gemm_ws)
+                              q_out=self.q, v_out=self.fused_v, kv_out_row=self.rows, M=self.M,
+                              workspace=self.gemm_ws)
         else:
             kvf.recompute_qkv(self.layer, self.x, self.rows, self.pos, self.w,
                               kvf.KVF_OUT_Q | kvf.KVF_OUT_K | kvf.KVF_OUT_V, self.rope_cos,
-                              self.rope_sin, q_out=self.q, k_out=self.k_new, v_out=self.v_new,
+                              self.rope_sin, q_out=self.q, k_out=self.fused_k, v_out=self.fused_v,
+                              kv_out_row=self.rows,
                               M=self.M, workspace=self.gemm_ws)
 
     def _scatter(self):
+        # deviation mode: K of the recomputed rows is the probe's
         if self.M == 0:
             return
-        if self.mode == "deviation":
-            kvf.scatter_kv(self.layer, self.k_probe, self.rows, self.v_new, None, self.rows,
-                           self.fused_k, self.fused_v, M=self.M)
-        else:
-            kvf.scatter_kv(self.layer, self.k_new, None, self.v_new, None, self.rows, self.fused_k,
-                           self.fused_v, M=self.M)
+        kvf.scatter_kv(self.layer, self.k_probe, self.rows, None, None, self.rows, self.fused_k,
+                       self.fused_v, M=self.M)
 
     def _attention(self):
         if self.M == 0:
@@ -210,14 +204,14 @@ class FusedLayerGPU:
         stage is one of rerotate / score / select / recompute_fuse / attention."""
         if self.mode == "deviation":
             score = [("k_probe", "score", self._k_probe), ("score", "score", self._score)]
+            fuse = [("recompute", "recompute_fuse", self._recompute),
+                    ("scatter", "recompute_fuse", self._scatter)]
         else:
-            score = [("u_probe", "score", self._u_probe), ("u_scatter", "score", self._u_scatter),
-                     ("score", "score", self._score)]
+            score = [("u_probe", "score", self._u_probe), ("score", "score", self._score)]
+            fuse = [("recompute", "recompute_fuse", self._recompute)]
         return ([("rerotate", "rerotate", self._rerotate)] + score +
-                [("select", "select", self._select),
-                 ("recompute", "recompute_fuse", self._recompute),
-                 ("scatter", "recompute_fuse", self._scatter),
-                 ("attention", "attention", self._attention)])
+                [("select", "select", self._select)] + fuse +
+                [("attention", "attention", self._attention)])
 
     def _stage(self, stage):
         for _, st, fn in self.calls():

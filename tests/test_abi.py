@@ -28,7 +28,7 @@ def lib():
     lib = ctypes.CDLL(LIB)
     P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
     lib.kvf_recompute_qkv.argtypes = [P, P, I64, P, P, I32, P, ctypes.c_uint32, P, P, I32,
-                                      P, P, P, P, ctypes.c_size_t, P]
+                                      P, P, P, P, I64, P, ctypes.c_size_t, P]
     lib.kvf_recompute_workspace_size.argtypes = [P, I32, ctypes.c_uint32]
     lib.kvf_recompute_workspace_size.restype = ctypes.c_size_t
     return lib
@@ -48,7 +48,7 @@ def test_status_strings_and_version(lib):
     lib.kvf_status_string.restype = ctypes.c_char_p
     assert lib.kvf_status_string(0) == b"KVF_OK"
     assert lib.kvf_status_string(2) == b"KVF_ERR_UNSUPPORTED"
-    assert lib.kvf_abi_version() == 2
+    assert lib.kvf_abi_version() == 3
 
 
 def test_budget_matches_oracle(lib):
@@ -85,31 +85,34 @@ def test_validation_errors(lib):
     ok = Layer(256, 4, 4, 64, 0)
     # head_dim and GQA shape
     assert lib.kvf_recompute_qkv(ctypes.byref(Layer(256, 4, 4, 96, 0)), FAKE, 10, None, FAKE, 1,
-                                 FAKE, 7, FAKE, FAKE, 4, FAKE, FAKE, FAKE, None, 0, None) == 2
+                                 FAKE, 7, FAKE, FAKE, 4, FAKE, FAKE, FAKE, None, 0, None, 0, None) == 2
     assert lib.kvf_recompute_qkv(ctypes.byref(Layer(256, 6, 4, 64, 0)), FAKE, 10, None, FAKE, 1,
-                                 FAKE, 7, FAKE, FAKE, 4, FAKE, FAKE, FAKE, None, 0, None) == 2
+                                 FAKE, 7, FAKE, FAKE, 4, FAKE, FAKE, FAKE, None, 0, None, 0, None) == 2
     assert b"multiple" in lib.kvf_last_error()
     # bad dtype, NULL layer, bad mask
     assert lib.kvf_recompute_qkv(ctypes.byref(Layer(256, 4, 4, 64, 7)), FAKE, 10, None, FAKE, 1,
-                                 FAKE, 7, FAKE, FAKE, 4, FAKE, FAKE, FAKE, None, 0, None) == 1
+                                 FAKE, 7, FAKE, FAKE, 4, FAKE, FAKE, FAKE, None, 0, None, 0, None) == 1
     assert lib.kvf_recompute_qkv(None, FAKE, 10, None, FAKE, 1, FAKE, 7, FAKE, FAKE, 4, FAKE, FAKE,
-                                 FAKE, None, 0, None) == 1
+                                 FAKE, None, 0, None, 0, None) == 1
     assert lib.kvf_recompute_qkv(ctypes.byref(ok), FAKE, 10, None, FAKE, 1, FAKE, 8, FAKE, FAKE, 4,
-                                 FAKE, FAKE, FAKE, None, 0, None) == 1
+                                 FAKE, FAKE, FAKE, None, 0, None, 0, None) == 1
     # identity row map larger than x
     assert lib.kvf_recompute_qkv(ctypes.byref(ok), FAKE, 10, None, FAKE, 11, FAKE, 1, FAKE, FAKE, 4,
-                                 FAKE, FAKE, FAKE, None, 0, None) == 1
+                                 FAKE, FAKE, FAKE, None, 0, None, 0, None) == 1
     # bf16 projection with Hkv * d not a multiple of 128
     assert lib.kvf_recompute_qkv(ctypes.byref(Layer(256, 3, 1, 64, 1)), FAKE, 10, None, FAKE, 1,
-                                 FAKE, 7, FAKE, FAKE, 4, FAKE, FAKE, FAKE, None, 0, None) == 2
+                                 FAKE, 7, FAKE, FAKE, 4, FAKE, FAKE, FAKE, None, 0, None, 0, None) == 2
     # bf16 projection of few rows splits K and needs its workspace
     bf = Layer(4096, 32, 8, 128, 1)
     need = lib.kvf_recompute_workspace_size(ctypes.byref(bf), 64, 7)
     assert need == 8 * 64 * (32 + 16) * 128 * 4
     assert lib.kvf_recompute_qkv(ctypes.byref(bf), FAKE, 64, None, FAKE, 64, FAKE, 7, FAKE, FAKE, 4,
-                                 FAKE, FAKE, FAKE, None, 0, None) == 3
+                                 FAKE, FAKE, FAKE, None, 0, None, 0, None) == 3
     assert lib.kvf_recompute_qkv(ctypes.byref(bf), FAKE, 64, None, FAKE, 64, FAKE, 7, FAKE, FAKE, 4,
-                                 FAKE, FAKE, FAKE, FAKE, need - 1, None) == 3
+                                 FAKE, FAKE, FAKE, None, 0, FAKE, need - 1, None) == 3
+    # destination rows need their count
+    assert lib.kvf_recompute_qkv(ctypes.byref(ok), FAKE, 10, None, FAKE, 1, FAKE, 7, FAKE, FAKE, 4,
+                                 FAKE, FAKE, FAKE, FAKE, 0, None, 0, None) == 1
     # many rows or fp32: no workspace
     assert lib.kvf_recompute_workspace_size(ctypes.byref(bf), 5000, 7) == 0
     assert lib.kvf_recompute_workspace_size(ctypes.byref(Layer(4096, 32, 8, 128, 0)), 64, 7) == 0
@@ -146,6 +149,6 @@ def test_empty_calls_are_noops(lib):
     ok = Layer(256, 4, 4, 64, 0)
     assert lib.kvf_rope_table(ctypes.c_double(1e4), 64, 0, None, None, None) == 0
     assert lib.kvf_recompute_qkv(ctypes.byref(ok), None, 0, None, None, 0, None, 7, None, None, 0,
-                                 None, None, None, None, 0, None) == 0
+                                 None, None, None, None, 0, None, 0, None) == 0
     assert lib.kvf_scatter_kv(ctypes.byref(ok), None, None, 0, None, None, 0, None, 0, None, None, 0,
                               None) == 0

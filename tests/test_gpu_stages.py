@@ -368,6 +368,38 @@ def test_recompute_skips_rows_outside_tables(kvf, dtype, hidden, M):
             assert not np.all(got[bad_src[1]] == 7.0)
 
 
+@pytest.mark.parametrize("dtype,hidden,M", [("bf16", 1024, 40), ("bf16", 256, 300), ("f32", 128, 50)])
+def test_recompute_kv_destination_rows(kvf, dtype, hidden, M):
+    """K/V written straight into a larger cache at given rows (the scatter of
+    Eq. 7 fused into the projection); other rows untouched, Q dense."""
+    import torch
+    hq, hkv, d, xr, n_dst = 4, 2, 64, 350, 700
+    x_s = encode(_randn((xr, hidden), 12, "x"), dtype)
+    w_s = encode(_randn(((hq + 2 * hkv) * d, hidden), 12, "w", std=1 / math.sqrt(hidden)), dtype)
+    rows = synth.random_rows(xr, M, 13)
+    pos = synth.random_rows(600, M, 14)
+    dst = synth.random_rows(n_dst, M, 15)
+    dst[2] = -1                     # skipped
+    dst[M - 1] = n_dst              # outside: skipped
+    L = _layer(kvf, hidden, hq, hkv, d, dtype)
+    c, s = _rope_tables(kvf, 1e4, d, 600)
+    td = L.torch_dtype
+    q = torch.full((M, hq, d), 7.0, dtype=td, device="cuda")
+    kc = torch.full((n_dst, hkv, d), 7.0, dtype=td, device="cuda")
+    vc = torch.full((n_dst, hkv, d), 7.0, dtype=td, device="cuda")
+    kvf.recompute_qkv(L, to_gpu(x_s, dtype), to_gpu(rows), to_gpu(pos), to_gpu(w_s, dtype), 7, c, s,
+                      q_out=q, k_out=kc, v_out=vc, kv_out_row=to_gpu(dst))
+    lo = fusion.Layer(hidden, hq, hkv, d, 1e4)
+    ref = fusion.recompute(decode(x_s, dtype)[rows], pos, decode(w_s, dtype), lo)
+    assert_close(from_gpu(q), ref["q"], dtype, "recompute q (dense)")
+    ok = np.array([i for i in range(M) if 0 <= dst[i] < n_dst])
+    for name, t in (("k", kc), ("v", vc)):
+        got = from_gpu(t)
+        assert_close(got[dst[ok]], ref[name][ok], dtype, f"recompute {name} at destination rows")
+        untouched = np.setdiff1d(np.arange(n_dst), dst[ok])
+        assert np.all(got[untouched] == 7.0), name
+
+
 @pytest.mark.parametrize("wl_name,kind", [("qwen3_8b_mass", "p_and_u"), ("qwen3_8b_mass", "u_probe"),
                                           ("llama3_70b_mass", "p_and_u"),
                                           ("qwen25_3b_kivi8", "probe_all")])
