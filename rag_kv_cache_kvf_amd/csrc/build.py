@@ -12,6 +12,7 @@ import argparse
 import concurrent.futures as cf
 import glob
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -30,7 +31,27 @@ CFLAGS = [
     # packed fp32 instructions stay off (plain scalar fp32 code only)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", INCLUDE, "-I", HERE,
+    # per-kernel register / scratch report, checked below
+    "-Rpass-analysis=kernel-resource-usage",
 ]
+
+# A kernel whose private arrays the compiler could not keep in registers runs
+# them through scratch memory, an order of magnitude slower; a few spilled
+# dwords are tolerable, a demoted accumulator array is not.
+MAX_SCRATCH_BYTES = 64
+_REMARK = re.compile(r"remark:\s+(Function Name|VGPRs|AGPRs|ScratchSize \[bytes/lane\]|Occupancy \[waves/SIMD\]):\s+(\S+)")
+
+
+def _resources(stderr: str) -> dict:
+    """kernel name -> {VGPRs, AGPRs, ScratchSize, Occupancy} from the remarks."""
+    out, cur = {}, None
+    for m in _REMARK.finditer(stderr):
+        key, val = m.group(1).split(" ")[0], m.group(2)
+        if key == "Function":
+            cur = out.setdefault(val, {})
+        elif cur is not None:
+            cur[key] = int(val)
+    return out
 
 
 def sources():
@@ -44,9 +65,28 @@ def _compile(src: str) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
-    # keep real diagnostics, drop the host pass's note about the GPU-only feature
+    res = _resources(r.stderr)
+    bad = {k: v for k, v in res.items() if v.get("ScratchSize", 0) > MAX_SCRATCH_BYTES}
+    if bad:
+        raise RuntimeError(f"kernels in {src} use scratch memory beyond {MAX_SCRATCH_BYTES} B/lane: {bad}")
+    with open(obj[:-2] + ".resources.txt", "w") as f:
+        for k, v in sorted(res.items()):
+            f.write(f"{k} {v}\n")
+    # keep real diagnostics, drop the resource remarks and the host pass's
+    # note about the GPU-only feature
     noise = "'-packed-fp32-ops' is not a recognized feature"
-    warn = "\n".join(l for l in r.stderr.splitlines() if noise not in l).strip()
+    lines = r.stderr.splitlines()
+    keep, skip = [], False
+    for l in lines:
+        if "remark:" in l:
+            skip = True          # the remark and its source-excerpt lines
+            continue
+        if skip and (l.startswith(" ") or l.strip() == ""):
+            continue
+        skip = False
+        if noise not in l and "warning generated" not in l and "warnings generated" not in l:
+            keep.append(l)
+    warn = "\n".join(keep).strip()
     if warn:
         print(warn, file=sys.stderr)
     return obj

@@ -21,10 +21,9 @@
 //    row-major V tile through transposing LDS reads (ds_read_b64_tr_b16).
 //  * The causal mask uses each row's own position; keys beyond the tile's
 //    last position are never loaded.
-// The mass score runs the same loop in "statistics only" mode over key
-// splits (pass 1: per-row log-sum-exp), combines the splits, then a second
-// MFMA pass (S = Q K^T, query vectors on the MFMA rows) sums the normalised
-// probabilities per key lane-locally and a last pass adds the kv heads in a
+// The mass score (see the section below) takes per-chunk softmax statistics
+// of the query rows, combines them into log-sum-exps, sums the normalised
+// probabilities per key in a second MFMA pass and adds the kv heads in a
 // fixed order, so the result is deterministic.
 //
 // fp32 path: one wave per (row, head) with lane-parallel keys; used by the
@@ -101,7 +100,7 @@ __device__ __forceinline__ int chunk_xor(int row) {
   }
 }
 
-template <int D, bool STATS_ONLY>
+template <int D>
 __global__ void __launch_bounds__(kAThreads) attn_bf16_kernel(AttnArgs a) {
   constexpr int KS = D / 16;       // MFMA k-steps over the head dimension
   constexpr int DB = D / 32;       // 32-channel output blocks
@@ -111,8 +110,8 @@ __global__ void __launch_bounds__(kAThreads) attn_bf16_kernel(AttnArgs a) {
   constexpr int TILE = kAT * D;
   __shared__ __attribute__((aligned(16))) bf16_t k0s[TILE];
   __shared__ __attribute__((aligned(16))) bf16_t k1s[TILE];
-  __shared__ __attribute__((aligned(16))) bf16_t v0s[STATS_ONLY ? 8 : TILE];
-  __shared__ __attribute__((aligned(16))) bf16_t v1s[STATS_ONLY ? 8 : TILE];
+  __shared__ __attribute__((aligned(16))) bf16_t v0s[TILE];
+  __shared__ __attribute__((aligned(16))) bf16_t v1s[TILE];
   __shared__ int s_pos[2];
 
   const int hkv = a.hkv;
@@ -152,11 +151,7 @@ __global__ void __launch_bounds__(kAThreads) attn_bf16_kernel(AttnArgs a) {
   const int kend = s_pos[0] + 1;                  // keys [0, kend) are visible to someone
   const int pmin = s_pos[1];                      // keys <= pmin are visible to everyone
 
-  int kbeg = 0, klim = kend;
-  if constexpr (STATS_ONLY) {
-    kbeg = blockIdx.y * a.split_keys;
-    klim = min(kend, kbeg + a.split_keys);
-  }
+  const int kbeg = 0, klim = kend;
 
   const bf16_t* Q = static_cast<const bf16_t*>(a.q);
   bf16x8_t qf[KS];
@@ -184,7 +179,7 @@ __global__ void __launch_bounds__(kAThreads) attn_bf16_kernel(AttnArgs a) {
   // this lane's DMA slot: row lane / CPR of each group, physical chunk lane % CPR
   const int dma_rr = lane / CPR, dma_p = lane % CPR;
 
-  auto dma_tile = [&](const bf16_t* src_req, bf16_t* dst, int kb0) {
+  auto dma_tile = [&](const bf16_t* src_req, bf16_t* dst, int kb0) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < NDMA; ++j) {
       const int grp = w * NDMA + j;
@@ -229,7 +224,7 @@ __global__ void __launch_bounds__(kAThreads) attn_bf16_kernel(AttnArgs a) {
 
   // One 128-key tile computed from (ks, vs).  MASK selects the variant that
   // applies the causal and range mask (only the last tiles need it).
-  auto step = [&](const bf16_t* ks_, const bf16_t* vs_, int kb0, auto mask_tag) {
+  auto step = [&](const bf16_t* ks_, const bf16_t* vs_, int kb0, auto mask_tag) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
     const int k_half = kb0 + 64 * kg;             // first key of this wave's half
     if (k_half >= klim) return;                   // wave-uniform
@@ -265,22 +260,15 @@ __global__ void __launch_bounds__(kAThreads) attn_bf16_kernel(AttnArgs a) {
       const float m_new = fmaxf(m_run, mx);
       const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
-      if constexpr (!STATS_ONLY) {
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
-      }
+        for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
       m_run = m_new;
     }
     const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
     float rs = 0.f;
-    if constexpr (STATS_ONLY) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) rs += __builtin_amdgcn_exp2f(fmaf(s[kb][i], c_scale, neg_m));
-    } else {
+    {
       uint32_t pk[2][8];                          // bf16 probability pairs
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -320,7 +308,7 @@ __global__ void __launch_bounds__(kAThreads) attn_bf16_kernel(AttnArgs a) {
   // leading tiles every row sees completely need no mask
   int n_plain = 0;
   if (pmin >= kbeg) n_plain = min(min(ntiles, (pmin + 1 - kbeg) / kAT), (klim - kbeg) / kAT);
-  auto run_tile = [&](int t, const bf16_t* ks_, const bf16_t* vs_) {
+  auto run_tile = [&](int t, const bf16_t* ks_, const bf16_t* vs_) __attribute__((always_inline)) {
     if (t < n_plain)
       step(ks_, vs_, kbeg + t * kAT, std::false_type{});
     else
@@ -328,21 +316,21 @@ __global__ void __launch_bounds__(kAThreads) attn_bf16_kernel(AttnArgs a) {
   };
   if (ntiles > 0) {
     dma_tile(Kreq, k0s, kbeg);
-    if constexpr (!STATS_ONLY) dma_tile(Vreq, v0s, kbeg);
+    dma_tile(Vreq, v0s, kbeg);
   }
   __syncthreads();                                // waits for the DMA (vmcnt) too
   // two tiles per trip so every buffer is a distinct static array
   for (int t = 0; t < ntiles; t += 2) {
     if (t + 1 < ntiles) {
       dma_tile(Kreq, k1s, kbeg + (t + 1) * kAT);
-      if constexpr (!STATS_ONLY) dma_tile(Vreq, v1s, kbeg + (t + 1) * kAT);
+      dma_tile(Vreq, v1s, kbeg + (t + 1) * kAT);
     }
     run_tile(t, k0s, v0s);
     __syncthreads();
     if (t + 1 >= ntiles) break;
     if (t + 2 < ntiles) {
       dma_tile(Kreq, k0s, kbeg + (t + 2) * kAT);
-      if constexpr (!STATS_ONLY) dma_tile(Vreq, v0s, kbeg + (t + 2) * kAT);
+      dma_tile(Vreq, v0s, kbeg + (t + 2) * kAT);
     }
     run_tile(t + 1, k1s, v1s);
     __syncthreads();
@@ -352,20 +340,18 @@ __global__ void __launch_bounds__(kAThreads) attn_bf16_kernel(AttnArgs a) {
   const int slot = qg * 64 + lane;
   float* xo0 = reinterpret_cast<float*>(k0s);     // O blocks [0, DB/2)
   float* xo1 = reinterpret_cast<float*>(k1s);     // O blocks [DB/2, DB)
-  float* xml = STATS_ONLY ? reinterpret_cast<float*>(k1s) : reinterpret_cast<float*>(v0s);
+  float* xml = reinterpret_cast<float*>(v0s);
   constexpr int HO = 8 * DB;                      // floats per lane in each O half
   if (kg == 1) {
     xml[2 * slot] = m_run;
     xml[2 * slot + 1] = l_run;
-    if constexpr (!STATS_ONLY) {
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float* dstp = db < DB / 2 ? xo0 : xo1;
-          dstp[slot * HO + (db % (DB / 2)) * 16 + i] = o[db][i];
-        }
-    }
+      for (int i = 0; i < 16; ++i) {
+        float* dstp = db < DB / 2 ? xo0 : xo1;
+        dstp[slot * HO + (db % (DB / 2)) * 16 + i] = o[db][i];
+      }
   }
   __syncthreads();
   if (kg == 1) return;
@@ -377,45 +363,35 @@ __global__ void __launch_bounds__(kAThreads) attn_bf16_kernel(AttnArgs a) {
     const float a1 = __builtin_amdgcn_exp2f(m_run - mu), a2 = __builtin_amdgcn_exp2f(m2 - mu);
     l_run = l_run * a1 + l2 * a2;
     m_run = mm;
-    if constexpr (!STATS_ONLY) {
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float* srcp = db < DB / 2 ? xo0 : xo1;
-          o[db][i] = o[db][i] * a1 + srcp[slot * HO + (db % (DB / 2)) * 16 + i] * a2;
-        }
-    }
+      for (int i = 0; i < 16; ++i) {
+        const float* srcp = db < DB / 2 ? xo0 : xo1;
+        o[db][i] = o[db][i] * a1 + srcp[slot * HO + (db % (DB / 2)) * 16 + i] * a2;
+      }
   }
 
   if (!valid || pos < 0) return;
   const int64_t orow = static_cast<int64_t>(a.orow0[r]) + lrow0 + row_l;
-  if constexpr (STATS_ONLY) {
-    if (hf == 0) {
-      const int64_t idx = static_cast<int64_t>(blockIdx.y) * a.plane + orow * a.hq + h;
-      a.part_m[idx] = m_run;
-      a.part_l[idx] = l_run;
+  const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+  bf16_t* O = static_cast<bf16_t*>(a.out) + (orow * a.hq + h) * D;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int d0 = db * 32 + 8 * i + 4 * hf;
+      u32x2_t pk2;
+      pk2[0] = pack_bf16x2(o[db][4 * i] * inv, o[db][4 * i + 1] * inv);
+      pk2[1] = pack_bf16x2(o[db][4 * i + 2] * inv, o[db][4 * i + 3] * inv);
+      *reinterpret_cast<u32x2_t*>(O + d0) = pk2;
     }
-  } else {
-    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-    bf16_t* O = static_cast<bf16_t*>(a.out) + (orow * a.hq + h) * D;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int d0 = db * 32 + 8 * i + 4 * hf;
-        u32x2_t pk2;
-        pk2[0] = pack_bf16x2(o[db][4 * i] * inv, o[db][4 * i + 1] * inv);
-        pk2[1] = pack_bf16x2(o[db][4 * i + 2] * inv, o[db][4 * i + 3] * inv);
-        *reinterpret_cast<u32x2_t*>(O + d0) = pk2;
-      }
-    if (a.lse && hf == 0) a.lse[orow * a.hq + h] = (m_run + log2f(l_run)) * kLn2;
-  }
+  if (a.lse && hf == 0) a.lse[orow * a.hq + h] = (m_run + log2f(l_run)) * kLn2;
 }
 
-template <int D, bool STATS_ONLY>
+template <int D>
 static hipError_t launch_attn_bf16(const AttnArgs& a, dim3 grid, hipStream_t st) {
-  hipLaunchKernelGGL((attn_bf16_kernel<D, STATS_ONLY>), grid, dim3(kAThreads), 0, st, a);
+  hipLaunchKernelGGL((attn_bf16_kernel<D>), grid, dim3(kAThreads), 0, st, a);
   return hipGetLastError();
 }
 
@@ -530,8 +506,8 @@ hipError_t launch_attention(const kvf_layer_desc& L, const BatchArgs& B, const v
     const int64_t blocks = static_cast<int64_t>(a.total_tiles) * a.hkv;
     if (blocks == 0) return hipSuccess;
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-    const hipError_t e = L.head_dim == 128 ? launch_attn_bf16<128, false>(a, dim3(blocks), st)
-                                           : launch_attn_bf16<64, false>(a, dim3(blocks), st);
+    const hipError_t e = L.head_dim == 128 ? launch_attn_bf16<128>(a, dim3(blocks), st)
+                                           : launch_attn_bf16<64>(a, dim3(blocks), st);
     if (e != hipSuccess) return e;
   } else {
     const int total_rows = cu_q[B.n_req];
@@ -545,8 +521,22 @@ hipError_t launch_attention(const kvf_layer_desc& L, const BatchArgs& B, const v
 // ---------------------------------------------------------------------------
 // attention mass
 // ---------------------------------------------------------------------------
+// Three launches (bf16):
+//  1. mass_stats_bf16_kernel: per (128-key chunk, kv head), the softmax
+//     statistics (max, sum) of every used query vector over the chunk's
+//     visible keys.  S^T = K Q^T with the chunk's keys held in registers as
+//     the MFMA A operand and query vectors staged in LDS as B, so each lane
+//     owns one query vector's scores.
+//  2. lse_combine_kernel: chunk statistics -> log2-domain LSE per (row, head).
+//  3. mass_colsum_bf16_kernel: per (128-key tile, kv head), S = Q K^T again
+//     (query vectors on the MFMA rows, keys on the lanes), exp(s - lse)
+//     summed over the query vectors of the group.
+//  4. head_sum_kernel: the kv heads added in a fixed order (deterministic).
+// fp32: statistics by the fp32 attention kernel, column sums by one wave per
+// (key, kv head).
+
 // combine split statistics into log2-domain LSE per (row, head): one wave per
-// entry, one lane per split (n_splits <= 64)
+// entry, lanes over splits
 __global__ void __launch_bounds__(256) lse_combine_kernel(const float* __restrict__ pm,
                                                           const float* __restrict__ pl, int n_splits,
                                                           int64_t plane, int64_t n,
@@ -554,43 +544,192 @@ __global__ void __launch_bounds__(256) lse_combine_kernel(const float* __restric
   const int64_t i = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) / kWave;
   const int lane = threadIdx.x & (kWave - 1);
   if (i >= n) return;
-  const float ms = lane < n_splits ? pm[lane * plane + i] : -INFINITY;
-  const float ls = lane < n_splits ? pl[lane * plane + i] : 0.f;
-  const float m = wave_max(ms);
-  const float l = wave_sum(ms > -INFINITY ? ls * exp2f(ms - m) : 0.f);
-  if (lane == 0) lse2[i] = l > 0.f ? m + log2f(l) : INFINITY;     // INFINITY: contributes nothing
+  float m = -INFINITY, l = 0.f;
+  for (int sp = lane; sp < n_splits; sp += kWave) {
+    const float ms = pm[sp * plane + i], ls = pl[sp * plane + i];
+    if (ms > m) {
+      l = l * (m == -INFINITY ? 0.f : exp2f(m - ms)) + ls;
+      m = ms;
+    } else if (ms > -INFINITY) {
+      l += ls * exp2f(ms - m);
+    }
+  }
+  const float mw = wave_max(m);
+  const float lw = wave_sum(m > -INFINITY ? l * exp2f(m - mw) : 0.f);
+  if (lane == 0) lse2[i] = lw > 0.f ? mw + log2f(lw) : INFINITY;   // INFINITY: contributes nothing
 }
 
 struct MassArgs {
   BatchArgs b;
   int qrow0[KVF_MAX_REQ];        // first q_u row used by each request
   int nq[KVF_MAX_REQ];           // query rows used
-  int orow0[KVF_MAX_REQ];        // their rows in lse2
+  int pos0[KVF_MAX_REQ];         // position of the first used query row
+  int orow0[KVF_MAX_REQ];        // their rows in lse2 / the statistics planes
   int cu_ktiles[KVF_MAX_REQ + 1];
   int total_ktiles;
   const void* q;
   const void* k;
   const float* lse2;             // [rows, Hq]
   float* part;                   // [Hkv, sum N]
+  float* part_m;                 // [chunks, rows, Hq] (statistics pass)
+  float* part_l;
+  int64_t plane;                 // rows * Hq
   int hq, hkv, G;
   float scale_log2;
 };
 
-constexpr int kMK = 128;         // context keys per workgroup (4 waves x 32)
+constexpr int kMK = 128;         // keys per workgroup (4 waves x 32)
+constexpr int kMQS = 256;        // query vectors staged per round (LDS)
+
+template <int D>
+__global__ void __launch_bounds__(256) mass_stats_bf16_kernel(MassArgs a) {
+  constexpr int KS = D / 16;
+  constexpr int LDQ = D + 8;     // padded rows: B-fragment reads hit distinct banks
+  constexpr int VPR = D / 8;
+  __shared__ __attribute__((aligned(16))) bf16_t Qs[kMQS][LDQ];
+  __shared__ float2 st[4][kMQS];
+  const int hkv = a.hkv;
+  const int g = blockIdx.x % hkv;
+  const int chunk = static_cast<int>(blockIdx.x / hkv);
+  const int r = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c = lane & 31, hf = lane >> 5;
+  const int T = a.b.cu_T[r + 1] - a.b.cu_T[r];
+  const int64_t krow0 = a.b.cu_T[r];
+  const int nqv = a.nq[r] * a.G;
+  const int key0 = chunk * kMK;
+  const int64_t out0 = static_cast<int64_t>(chunk) * a.plane;
+  if (key0 >= T) {          // past this request's keys: an empty chunk
+    for (int qv = tid; qv < nqv; qv += 256) {
+      const int row = qv / a.G, hl = qv - row * a.G;
+      const int64_t idx = out0 + (static_cast<int64_t>(a.orow0[r]) + row) * a.hq + g * a.G + hl;
+      a.part_m[idx] = -INFINITY;
+      a.part_l[idx] = 0.f;
+    }
+    return;
+  }
+  // this wave's 32 keys as the A operand: row = key, k = 8 hf + e
+  const bf16_t* Kg = static_cast<const bf16_t*>(a.k);
+  const int key_a = key0 + 32 * w + c;
+  bf16x8_t kf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    if (key_a < T) {
+      kf[ks] = *reinterpret_cast<const bf16x8_t*>(Kg + ((krow0 + key_a) * hkv + g) * D + ks * 16 + hf * 8);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) kf[ks][e] = static_cast<__bf16>(0.f);
+    }
+  }
+  const bf16_t* Qg = static_cast<const bf16_t*>(a.q);
+  const float cs = a.scale_log2;
+  for (int qs = 0; qs < nqv; qs += kMQS) {
+    const int qe = min(nqv, qs + kMQS);
+    // stage this round's query vectors (zero rows past the end): all loads
+    // in flight together, then the stores
+    constexpr int NV = kMQS * VPR / 256;
+    u32x4_t v4[NV];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int idx = tid + 256 * j;
+      const int qq = idx / VPR, vc = idx - qq * VPR;
+      const int qi = qs + qq;
+      v4[j] = u32x4_t{0u, 0u, 0u, 0u};
+      if (qi < qe) {
+        const int row = qi / a.G, hl = qi - row * a.G;
+        v4[j] = *reinterpret_cast<const u32x4_t*>(
+            Qg + ((static_cast<int64_t>(a.qrow0[r]) + row) * a.hq + g * a.G + hl) * D + vc * 8);
+      }
+    }
+    if (qs == 0) {          // the K fragments have been in flight alongside
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(kf[ks]));
+    }
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int idx = tid + 256 * j;
+      const int qq = idx / VPR, vc = idx - qq * VPR;
+      *reinterpret_cast<u32x4_t*>(&Qs[qq][vc * 8]) = v4[j];
+    }
+    __syncthreads();
+    // four independent 32-vector blocks at a time (four MFMA chains in flight)
+#pragma unroll 1
+    for (int b0 = 0; b0 < qe - qs; b0 += 128) {
+      f32x16_t s[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[j][i] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const bf16x8_t qfrag = *reinterpret_cast<const bf16x8_t*>(&Qs[b0 + 32 * j + c][ks * 16 + hf * 8]);
+          s[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qfrag, s[j], 0, 0, 0);
+        }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        // lane c: query vector qs + b0 + 32 j + c; keys key0 + 32 w + 8 (i/4) + 4 hf + (i%4)
+        const int qv = qs + b0 + 32 * j + c;
+        const int pos = a.pos0[r] + qv / a.G;
+        const int lim = min(pos, T - 1) - (key0 + 32 * w + 4 * hf);
+        float sv[16];
+        float m = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          sv[i] = 8 * (i >> 2) + (i & 3) <= lim ? s[j][i] * cs : -INFINITY;
+          m = fmaxf(m, sv[i]);
+        }
+        m = fmaxf(m, __shfl_xor(m, 32, kWave));
+        float l = 0.f;
+        if (m > -INFINITY) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) l += __builtin_amdgcn_exp2f(sv[i] - m);
+        }
+        l += __shfl_xor(l, 32, kWave);
+        if (hf == 0) st[w][b0 + 32 * j + c] = make_float2(m, l);
+      }
+    }
+    __syncthreads();
+    for (int qv = qs + tid; qv < qe; qv += 256) {
+      float m = -INFINITY, l = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < 4; ++ww) {
+        const float2 x = st[ww][qv - qs];
+        if (x.x > m) {
+          l = l * (m == -INFINITY ? 0.f : exp2f(m - x.x)) + x.y;
+          m = x.x;
+        } else if (x.x > -INFINITY) {
+          l += x.y * exp2f(x.x - m);
+        }
+      }
+      const int row = qv / a.G, hl = qv - row * a.G;
+      const int64_t idx = out0 + (static_cast<int64_t>(a.orow0[r]) + row) * a.hq + g * a.G + hl;
+      a.part_m[idx] = m;
+      a.part_l[idx] = l;
+    }
+    __syncthreads();
+  }
+}
+
+constexpr int kMQB = 128;        // query vectors staged per column-sum round
 
 template <int D>
 __global__ void __launch_bounds__(256) mass_colsum_bf16_kernel(MassArgs a) {
   constexpr int KS = D / 16;
   constexpr int LDQ = D + 8;
-  __shared__ __attribute__((aligned(16))) bf16_t Qs[32][LDQ];
-  __shared__ float Ls[32];
+  constexpr int VPR = D / 8;
+  __shared__ __attribute__((aligned(16))) bf16_t Qs[kMQB][LDQ];
+  __shared__ float Ls[kMQB];
   const int g = blockIdx.x % a.hkv;
   const int kt = static_cast<int>(blockIdx.x / a.hkv);
   const int r = find_segment(a.cu_ktiles, a.b.n_req, kt);
   const int key0 = (kt - a.cu_ktiles[r]) * kMK;
   const int N = a.b.n_ctx[r];
   const int64_t krow0 = a.b.cu_T[r];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c = lane & 31, hf = lane >> 5;
   const int key = key0 + 32 * w + c;
   const bool kvalid = key < N;
@@ -610,46 +749,67 @@ __global__ void __launch_bounds__(256) mass_colsum_bf16_kernel(MassArgs a) {
   const bf16_t* Qg = static_cast<const bf16_t*>(a.q);
   const int nqv = a.nq[r] * a.G;
   float colsum = 0.f;
-  constexpr int VPR = D / 8;
-  for (int q0 = 0; q0 < nqv; q0 += 32) {
-    __syncthreads();
-    for (int idx = tid; idx < 32 * VPR; idx += 256) {
+  for (int q0 = 0; q0 < nqv; q0 += kMQB) {
+    // this round's query vectors and LSEs: all loads in flight together
+    constexpr int NV = kMQB * VPR / 256;
+    u32x4_t v4[NV];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int idx = tid + 256 * j;
       const int qq = idx / VPR, vc = idx - qq * VPR;
       const int qi = q0 + qq;
-      u32x4_t v4 = {0u, 0u, 0u, 0u};
+      v4[j] = u32x4_t{0u, 0u, 0u, 0u};
       if (qi < nqv) {
         const int row = qi / a.G, hl = qi - row * a.G;
-        v4 = *reinterpret_cast<const u32x4_t*>(
+        v4[j] = *reinterpret_cast<const u32x4_t*>(
             Qg + ((static_cast<int64_t>(a.qrow0[r]) + row) * a.hq + g * a.G + hl) * D + vc * 8);
       }
-      *reinterpret_cast<u32x4_t*>(&Qs[qq][vc * 8]) = v4;
     }
-    if (tid < 32) {
+    float l2 = INFINITY;
+    if (tid < kMQB) {
       const int qi = q0 + tid;
-      float l2 = INFINITY;
       if (qi < nqv) {
         const int row = qi / a.G, hl = qi - row * a.G;
         l2 = a.lse2[(static_cast<int64_t>(a.orow0[r]) + row) * a.hq + g * a.G + hl];
       }
-      Ls[tid] = l2;
     }
+    if (q0 == 0) {          // the K fragments have been in flight alongside
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(kf[ks]));
+    }
+    __syncthreads();        // previous round's reads of Qs and Ls are done
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int idx = tid + 256 * j;
+      const int qq = idx / VPR, vc = idx - qq * VPR;
+      *reinterpret_cast<u32x4_t*>(&Qs[qq][vc * 8]) = v4[j];
+    }
+    if (tid < kMQB) Ls[tid] = l2;
     __syncthreads();
-    f32x16_t s;
+    // the four 32-vector blocks as four independent MFMA chains
+    f32x16_t s[4];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) s[i] = 0.f;
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8_t qfrag = *reinterpret_cast<const bf16x8_t*>(&Qs[c][ks * 16 + hf * 8]);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qfrag, kf[ks], s, 0, 0, 0);
-    }
+      for (int i = 0; i < 16; ++i) s[j][i] = 0.f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int qq = 8 * (i >> 2) + 4 * hf + (i & 3);
-      colsum += exp2f(s[i] * a.scale_log2 - Ls[qq]);    // Ls = +inf for padding rows -> 0
-    }
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bf16x8_t qfrag = *reinterpret_cast<const bf16x8_t*>(&Qs[32 * j + c][ks * 16 + hf * 8]);
+        s[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qfrag, kf[ks], s[j], 0, 0, 0);
+      }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int qq = 32 * j + 8 * (i >> 2) + 4 * hf + (i & 3);
+        colsum += __builtin_amdgcn_exp2f(s[j][i] * a.scale_log2 - Ls[qq]);   // Ls = +inf: padding -> 0
+      }
   }
   colsum += __shfl_xor(colsum, 32, kWave);
-  if (hf == 0 && kvalid) a.part[static_cast<int64_t>(g) * a.b.cu_N[a.b.n_req] + a.b.cu_N[r] + key] = colsum;
+  if (hf == 0 && kvalid)
+    a.part[static_cast<int64_t>(g) * a.b.cu_N[a.b.n_req] + a.b.cu_N[r] + key] = colsum;
 }
 
 // fp32: one wave per (context key, kv head)
@@ -697,24 +857,25 @@ struct MassLayout {
 MassLayout mass_layout(const kvf_layer_desc& L, const BatchArgs& B, int n_last_q) {
   MassLayout m{};
   int max_T = 0;
-  int64_t tiles = 0;
-  const int G = L.n_q_heads / L.n_kv_heads;
-  const int R = L.dtype == KVF_BF16 ? rows_per_tile(G) : 1;
   for (int r = 0; r < B.n_req; ++r) {
     const int U = B.cu_T[r + 1] - B.cu_T[r] - B.n_ctx[r];
     const int nq = n_last_q > 0 ? std::min(n_last_q, U) : U;
     m.rows += nq;
-    tiles += ceil_div(nq, R);
     max_T = std::max(max_T, B.cu_T[r + 1] - B.cu_T[r]);
   }
-  // enough workgroups in the statistics pass to cover the chip twice
-  const int64_t base = std::max<int64_t>(1, L.dtype == KVF_BF16 ? tiles * L.n_kv_heads
-                                                                : m.rows * L.n_q_heads / 4);
-  const int key_tiles = std::max(1, ceil_div(max_T, kAT));
-  int splits = static_cast<int>(std::min<int64_t>(key_tiles, ceil_div(512, static_cast<int>(std::min<int64_t>(base, 512)))));
-  splits = std::max(1, std::min(splits, 64));
-  m.split_keys = ceil_div(key_tiles, splits) * kAT;
-  m.n_splits = ceil_div(std::max(max_T, 1), m.split_keys);
+  if (L.dtype == KVF_BF16) {
+    // statistics per 128-key chunk
+    m.split_keys = kMK;
+    m.n_splits = std::max(1, ceil_div(max_T, kMK));
+  } else {
+    // fp32 statistics kernel: enough splits to cover the chip twice
+    const int64_t base = std::max<int64_t>(1, m.rows * L.n_q_heads / 4);
+    const int key_tiles = std::max(1, ceil_div(max_T, kAT));
+    int splits = static_cast<int>(std::min<int64_t>(key_tiles, ceil_div(512, static_cast<int>(std::min<int64_t>(base, 512)))));
+    splits = std::max(1, std::min(splits, 64));
+    m.split_keys = ceil_div(key_tiles, splits) * kAT;
+    m.n_splits = ceil_div(std::max(max_T, 1), m.split_keys);
+  }
   const int64_t plane = m.rows * L.n_q_heads;
   auto align = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
   m.off_pm = 0;
@@ -745,58 +906,17 @@ hipError_t launch_attn_mass(const kvf_layer_desc& L, const BatchArgs& B, const v
   const int64_t plane = lay.rows * L.n_q_heads;
   if (plane > 0x7fffffff) return hipErrorInvalidValue;
 
-  // pass 1: per-split softmax statistics of the used query rows
-  AttnArgs a{};
-  a.b = B;
+  MassArgs m{};
+  m.b = B;
   int orow = 0;
   for (int r = 0; r < B.n_req; ++r) {
     const int U = B.cu_T[r + 1] - B.cu_T[r] - B.n_ctx[r];
     const int nq = n_last_q > 0 ? std::min(n_last_q, U) : U;
-    a.qrow0[r] = B.cu_U[r] + (U - nq);
-    a.nrows[r] = nq;
-    a.pos0[r] = B.n_ctx[r] + (U - nq);
-    a.orow0[r] = orow;
+    m.qrow0[r] = B.cu_U[r] + (U - nq);
+    m.nq[r] = nq;
+    m.pos0[r] = B.n_ctx[r] + (U - nq);
+    m.orow0[r] = orow;
     orow += nq;
-  }
-  a.plane = plane;
-  a.q = q_u;
-  a.q_pos = nullptr;
-  a.k = fk;
-  a.part_m = pm;
-  a.part_l = pl;
-  a.n_splits = lay.n_splits;
-  a.split_keys = lay.split_keys;
-  a.hq = L.n_q_heads;
-  a.hkv = L.n_kv_heads;
-  a.G = G;
-  a.scale_log2 = scale_log2;
-  if (plane > 0) {
-    if (L.dtype == KVF_BF16) {
-      fill_tiles(a, rows_per_tile(G));
-      const dim3 grid(a.total_tiles * a.hkv, lay.n_splits);
-      const hipError_t e1 = L.head_dim == 128 ? launch_attn_bf16<128, true>(a, grid, st)
-                                              : launch_attn_bf16<64, true>(a, grid, st);
-      if (e1 != hipSuccess) return e1;
-    } else {
-      const dim3 grid(ceil_div(static_cast<int>(plane), 4), lay.n_splits);
-      hipLaunchKernelGGL((attn_f32_kernel<true>), grid, dim3(256), 0, st, a, L.head_dim,
-                         static_cast<int>(lay.rows));
-    }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(lse_combine_kernel, dim3(ceil_div(static_cast<int>(plane), 256 / kWave)),
-                       dim3(256), 0, st, pm, pl, lay.n_splits, plane, plane, lse2);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-
-  // pass 2: normalised probabilities summed per context key and kv head
-  MassArgs m{};
-  m.b = B;
-  for (int r = 0; r < B.n_req; ++r) {
-    m.qrow0[r] = a.qrow0[r];
-    m.nq[r] = a.nrows[r];
-    m.orow0[r] = a.orow0[r];
     m.cu_ktiles[r + 1] = m.cu_ktiles[r] + ceil_div(B.n_ctx[r], kMK);
   }
   m.total_ktiles = m.cu_ktiles[B.n_req];
@@ -804,11 +924,64 @@ hipError_t launch_attn_mass(const kvf_layer_desc& L, const BatchArgs& B, const v
   m.k = fk;
   m.lse2 = lse2;
   m.part = part;
+  m.part_m = pm;
+  m.part_l = pl;
+  m.plane = plane;
   m.hq = L.n_q_heads;
   m.hkv = L.n_kv_heads;
   m.G = G;
   m.scale_log2 = scale_log2;
   const int n = B.cu_N[B.n_req];
+  if (plane == 0) {
+    // no query rows: every key gets zero mass
+    if (n > 0) {
+      hipLaunchKernelGGL(head_sum_kernel, dim3(ceil_div(n, 256)), dim3(256), 0, st, part, 0, n,
+                         scores);
+    }
+    return hipGetLastError();
+  }
+
+  // pass 1: softmax statistics of the used query rows
+  if (L.dtype == KVF_BF16) {
+    const dim3 grid(lay.n_splits * m.hkv, B.n_req);
+    if (L.head_dim == 128)
+      hipLaunchKernelGGL(mass_stats_bf16_kernel<128>, grid, dim3(256), 0, st, m);
+    else
+      hipLaunchKernelGGL(mass_stats_bf16_kernel<64>, grid, dim3(256), 0, st, m);
+  } else {
+    AttnArgs a{};
+    a.b = B;
+    for (int r = 0; r < B.n_req; ++r) {
+      a.qrow0[r] = m.qrow0[r];
+      a.nrows[r] = m.nq[r];
+      a.pos0[r] = m.pos0[r];
+      a.orow0[r] = m.orow0[r];
+    }
+    a.plane = plane;
+    a.q = q_u;
+    a.q_pos = nullptr;
+    a.k = fk;
+    a.part_m = pm;
+    a.part_l = pl;
+    a.n_splits = lay.n_splits;
+    a.split_keys = lay.split_keys;
+    a.hq = L.n_q_heads;
+    a.hkv = L.n_kv_heads;
+    a.G = G;
+    a.scale_log2 = scale_log2;
+    const dim3 grid(ceil_div(static_cast<int>(plane), 4), lay.n_splits);
+    hipLaunchKernelGGL((attn_f32_kernel<true>), grid, dim3(256), 0, st, a, L.head_dim,
+                       static_cast<int>(lay.rows));
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(lse_combine_kernel, dim3(ceil_div(static_cast<int>(plane), 256 / kWave)),
+                     dim3(256), 0, st, pm, pl, lay.n_splits, plane, plane, lse2);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  // pass 2: normalised probabilities summed per context key and kv head
+  if (n == 0) return hipSuccess;
   if (L.dtype == KVF_BF16) {
     const int64_t blocks = static_cast<int64_t>(m.total_ktiles) * m.hkv;
     if (L.head_dim == 128)
@@ -817,10 +990,10 @@ hipError_t launch_attn_mass(const kvf_layer_desc& L, const BatchArgs& B, const v
       hipLaunchKernelGGL(mass_colsum_bf16_kernel<64>, dim3(blocks), dim3(256), 0, st, m);
   } else {
     const int64_t waves = static_cast<int64_t>(n) * m.hkv;
-    hipLaunchKernelGGL(mass_colsum_f32_kernel, dim3(ceil_div(static_cast<int>(waves), 4)), dim3(256),
-                       0, st, m, L.head_dim);
+    hipLaunchKernelGGL(mass_colsum_f32_kernel, dim3(ceil_div(static_cast<int>(waves), 4)),
+                       dim3(256), 0, st, m, L.head_dim);
   }
-  hipError_t e = hipGetLastError();
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(head_sum_kernel, dim3(ceil_div(n, 256)), dim3(256), 0, st, part, L.n_kv_heads,
                      n, scores);
