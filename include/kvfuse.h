@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define KVF_ABI_VERSION 3
+#define KVF_ABI_VERSION 4
 #define KVF_MAX_REQ 64      /* requests per call (batch metadata is passed by value) */
 
 typedef enum {
@@ -264,7 +264,21 @@ kvf_status kvf_sparse_q_attention(const kvf_layer_desc* layer,
                                   const int32_t* q_pos, const int32_t* cu_q,
                                   const void* fused_k, const void* fused_v,
                                   float sm_scale, void* out, float* lse,
+                                  void* workspace, size_t workspace_bytes,
                                   void* stream);
+
+/* Workspace bytes kvf_sparse_q_attention can use for the same layer, batch
+ * and cu_q (HOST).  0 when the call would not use one (fp32, or a grid large
+ * enough to balance by itself).  With a workspace, the row tiles of long
+ * rows split their keys over two workgroups and merge (same result up to
+ * fp32 rounding order); with workspace NULL the call runs unsplit.  The
+ * workspace ends in per-tile arrival counters that must be zero before its
+ * first use (zero-fill it once when allocating it); every completed call
+ * leaves them zero again.  Calls that share a workspace must not overlap.
+ * A non-NULL workspace smaller than this size gives KVF_ERR_WORKSPACE. */
+size_t kvf_attention_workspace_size(const kvf_layer_desc* layer,
+                                    const kvf_batch* batch,
+                                    const int32_t* cu_q);
 
 /* ---------------------------------------------------------------------------
  * kvf_kivi8_encode - offline encoder of a dense bf16 per-chunk cache into the

@@ -54,6 +54,15 @@ def _resources(stderr: str) -> dict:
     return out
 
 
+# per-file code-generation options
+FILE_FLAGS = {
+    # the attention kernel runs one wave per SIMD with its score accumulators
+    # feeding VALU softmax: keep MFMA results in VGPRs instead of AGPRs (no
+    # accumulator copies); spills go to the otherwise unused AGPRs
+    "attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
+
+
 def sources():
     return sorted(glob.glob(os.path.join(HERE, "*.hip")) + glob.glob(os.path.join(HERE, "kernels", "*.hip")))
 
@@ -61,7 +70,7 @@ def sources():
 def _compile(src: str) -> str:
     rel = os.path.relpath(src, HERE).replace(os.sep, "_")
     obj = os.path.join(BUILD_DIR, rel[:-4] + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *CFLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
@@ -105,6 +114,14 @@ def build(jobs: int | None = None, verbose: bool = True) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    # A kernel template whose host-side instantiation fails (for instance a
+    # device builtin called with an implicit narrowing conversion) loses its
+    # launch stub without any diagnostic; the library would then not load.
+    r = subprocess.run(["nm", "-D", "--undefined-only", tmp], capture_output=True, text=True)
+    missing = [l.split()[-1] for l in r.stdout.splitlines() if "__device_stub__" in l]
+    if missing:
+        os.remove(tmp)
+        raise RuntimeError(f"kernel launch stubs missing from the library: {missing}")
     shutil.move(tmp, OUT_LIB)
     if verbose:
         print(f"built {OUT_LIB} from {len(srcs)} sources")

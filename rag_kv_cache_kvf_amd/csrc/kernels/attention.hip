@@ -46,6 +46,11 @@ struct AttnArgs {
   int orow0[KVF_MAX_REQ];        // first output row of each request
   int cu_tiles[KVF_MAX_REQ + 1]; // row-tile prefix
   int total_tiles;
+  int fold_from;                 // dispatch slots at or past this run smallest-first
+  int parts;                     // 2: long row tiles split their keys over two workgroups
+  int split_min;                 // key tiles from which a row tile is split
+  float* ws_part;                // [tiles * Hkv, 2 parts, partial values, threads]
+  int* ws_cnt;                   // [tiles * Hkv] arrivals; zero between calls
   int rows_per_tile;             // R
   const void* q;
   const int32_t* q_pos;
@@ -65,21 +70,38 @@ struct AttnArgs {
 // ---------------------------------------------------------------------------
 // bf16 MFMA kernel
 // ---------------------------------------------------------------------------
-// 8 waves: wave w owns query vectors [32*(w%4), +32) and key half w/4 of every
-// 128-key tile.  K and V tiles are copied global -> LDS by the DMA path
-// (global_load_lds, 16 bytes per lane, no registers involved) into two
-// static buffers: tile t+1 streams in while tile t is computed.  Both tiles
-// are row-major with the 16-byte chunks of row r XOR-swizzled (chunk_xor), so
-// the key-row reads of the score MFMA and the transposing reads of V
-// (ds_read_b64_tr_b16, one 4-key x 4-channel transpose per 16 lanes) hit
-// distinct banks.
-constexpr int kAT = 128;         // keys per tile (two halves of 64)
-constexpr int kAThreads = 512;
+// A workgroup owns 128 query vectors; each of its waves owns kQB blocks of
+// 32 of them (every K or V fragment read from LDS feeds kQB MFMAs).  Two
+// workgroups share a CU (64 KB of LDS each), so their waves interleave on
+// every SIMD without sharing barriers, and each wave accumulates the next
+// key block's scores while this block's softmax runs.
+//
+// Keys advance in tiles of 64 (two 32-key blocks).  K and V tiles are copied
+// global -> LDS by the DMA path (global_load_lds, 16 bytes per lane) into two
+// K buffers and two V buffers, each a distinct static array so the compiler
+// can tell the outstanding copies apart.  Per tile t, with barriers A and B:
+//   A: V_t has landed; all waves are done with V_{t-1}  -> copy V_{t+1}
+//      S(t, block 1) from K_t, overlapped with softmax(t, block 0)
+//      O += P(t, block 0) V_t
+//   B: K_{t+1} has landed; all waves are done with K_t  -> copy K_{t+2}
+//      S(t+1, block 0) from K_{t+1}, overlapped with softmax(t, block 1)
+//      O += P(t, block 1) V_t
+// so every copy has a whole tile of compute to land.  Tiles are row-major
+// with the 16-byte chunks of row r XOR-swizzled (chunk_xor): the key-row reads
+// of the score MFMA and the transposing reads of V (ds_read_b64_tr_b16, one
+// 4-key x 4-channel transpose per 16 lanes) hit distinct banks.
+constexpr int kAT = 64;          // keys per tile (two 32-key blocks)
+constexpr int kQB = 1;           // 32-vector query blocks per wave
+constexpr int kAWaves = 4 / kQB; // 128 query vectors per workgroup
+constexpr int kAThreads = 64 * kAWaves;
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) const void global_cvoid_t;
+// Word 3 of a gfx9-family buffer descriptor for raw byte addressing
+// (stride 0): 32-bit data format, no swizzle; accesses at or past the
+// descriptor's byte range read as zero.
+constexpr int kBufferRsrcWord3 = 0x00020000;
 
 // XOR applied to the 16-byte chunk index of tile row `row`.  LDS serves a
 // wide read over 64 banks (256 B) per cycle: 16 lanes of a 16-byte read or
@@ -100,14 +122,26 @@ __device__ __forceinline__ int chunk_xor(int row) {
   }
 }
 
+// Workgroup barrier after this wave's tile copies older than the newest N
+// have landed (vmcnt counts only those copies here) and its LDS reads have
+// returned.  One asm statement with a memory clobber, so the compiler moves
+// no LDS access across the barrier.
+template <int N>
+__device__ __forceinline__ void copies_landed_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
 template <int D>
-__global__ void __launch_bounds__(kAThreads) attn_bf16_kernel(AttnArgs a) {
+__global__ void __launch_bounds__(kAThreads) __attribute__((amdgpu_waves_per_eu(2 / kQB, 2 / kQB)))
+attn_bf16_kernel(AttnArgs a) {
   constexpr int KS = D / 16;       // MFMA k-steps over the head dimension
   constexpr int DB = D / 32;       // 32-channel output blocks
   constexpr int CPR = D / 8;       // 16-byte chunks per row
   constexpr int RPI = 64 / CPR;    // rows per DMA instruction (64 lanes x 16 B)
-  constexpr int NDMA = kAT / RPI / 8;   // DMA instructions per wave per tile and tensor
+  constexpr int NDMA = kAT / RPI / kAWaves;   // DMA instructions per wave per tile and tensor
   constexpr int TILE = kAT * D;
+  static_assert(NDMA >= 1 && NDMA * RPI * kAWaves == kAT, "tile copy split");
   __shared__ __attribute__((aligned(16))) bf16_t k0s[TILE];
   __shared__ __attribute__((aligned(16))) bf16_t k1s[TILE];
   __shared__ __attribute__((aligned(16))) bf16_t v0s[TILE];
@@ -116,7 +150,16 @@ __global__ void __launch_bounds__(kAThreads) attn_bf16_kernel(AttnArgs a) {
 
   const int hkv = a.hkv;
   const int g = blockIdx.x % hkv;
-  const int tile = a.total_tiles - 1 - static_cast<int>(blockIdx.x / hkv);
+  // Row tiles are numbered by position, so a higher tile has more keys.
+  // Dispatch runs largest-first; when the whole grid is resident at once
+  // (two workgroups per CU), the second round of slots runs smallest-first
+  // so each CU pairs a long tile with a short one.
+  // With key splitting, the two parts of a row tile are adjacent slots.
+  const int slot = static_cast<int>(blockIdx.x / hkv);
+  const int rank0 = a.parts == 2 ? slot >> 1 : slot;
+  const int part = a.parts == 2 ? slot & 1 : 0;
+  const int rank = rank0 < a.fold_from ? rank0 : a.total_tiles - 1 - (rank0 - a.fold_from);
+  const int tile = a.total_tiles - 1 - rank;
   const int r = find_segment(a.cu_tiles, a.b.n_req, tile);
   const int tr = tile - a.cu_tiles[r];
   const int R = a.rows_per_tile;
@@ -125,92 +168,127 @@ __global__ void __launch_bounds__(kAThreads) attn_bf16_kernel(AttnArgs a) {
   const int T = a.b.cu_T[r + 1] - a.b.cu_T[r];
   const int64_t krow0 = a.b.cu_T[r];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int qg = w & 3, kg = w >> 2;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c = lane & 31, hf = lane >> 5;
-  const int qv = 32 * qg + c;
-  const int row_l = qv % R, head_l = qv / R;
-  const bool valid = head_l < a.G && row_l < nrows;
-  const int64_t qrow = static_cast<int64_t>(a.qrow0[r]) + lrow0 + row_l;
-  const int h = g * a.G + head_l;
-  int pos = -1;
-  if (valid) {
-    pos = a.q_pos ? a.q_pos[qrow] : a.pos0[r] + lrow0 + row_l;
-    if (pos < 0 || pos >= T) pos = -1;
+  int pos[kQB], row_l[kQB], h[kQB];
+  int64_t qrow[kQB];
+  bool valid[kQB];
+#pragma unroll
+  for (int qb = 0; qb < kQB; ++qb) {
+    const int qv = 32 * (kQB * w + qb) + c;
+    row_l[qb] = qv % R;
+    const int head_l = qv / R;
+    valid[qb] = head_l < a.G && row_l[qb] < nrows;
+    qrow[qb] = static_cast<int64_t>(a.qrow0[r]) + lrow0 + row_l[qb];
+    h[qb] = g * a.G + head_l;
+    pos[qb] = -1;
+    if (valid[qb]) {
+      int p = a.q_pos ? a.q_pos[qrow[qb]] : a.pos0[r] + lrow0 + row_l[qb];
+      pos[qb] = (p < 0 || p >= T) ? -1 : p;
+    }
   }
   if (tid == 0) {
     s_pos[0] = -1;                 // max position
     s_pos[1] = 0x7fffffff;         // min position
   }
   __syncthreads();
-  if (pos >= 0) {
-    atomicMax(&s_pos[0], pos);
-    atomicMin(&s_pos[1], pos);
-  }
-  __syncthreads();
-  const int kend = s_pos[0] + 1;                  // keys [0, kend) are visible to someone
-  const int pmin = s_pos[1];                      // keys <= pmin are visible to everyone
-
-  const int kbeg = 0, klim = kend;
-
-  const bf16_t* Q = static_cast<const bf16_t*>(a.q);
-  bf16x8_t qf[KS];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    if (pos >= 0) {
-      qf[ks] = *reinterpret_cast<const bf16x8_t*>(Q + (qrow * a.hq + h) * D + ks * 16 + hf * 8);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qf[ks][e] = static_cast<__bf16>(0.f);
+  for (int qb = 0; qb < kQB; ++qb) {
+    if (pos[qb] >= 0) {
+      atomicMax(&s_pos[0], pos[qb]);
+      atomicMin(&s_pos[1], pos[qb]);
     }
   }
+  __syncthreads();
+  // (uniform values: read once into scalar registers)
+  const int klim = __builtin_amdgcn_readfirstlane(s_pos[0] + 1);   // keys [0, klim) are visible to someone
+  const int pmin = __builtin_amdgcn_readfirstlane(s_pos[1]);       // keys <= pmin are visible to everyone
+  const int n = klim > 0 ? ceil_div(klim, kAT) : 0;
+  // leading tiles that every row sees completely need no mask
+  const int n_plain = klim > 0 ? min(n, (pmin + 1) / kAT) : 0;
+  // A long row tile is split: part 0 takes key tiles [0, n/2), part 1 the
+  // rest; whichever finishes second merges the two (m, l, O) and writes.
+  const bool split = a.parts == 2 && n >= a.split_min;
+  if (part == 1 && !split) return;                // whole workgroup: s_pos is uniform
+  const int t0 = part == 1 ? n / 2 : 0;
+  const int t1 = split && part == 0 ? n / 2 : n;
 
-  f32x16_t o[DB];
+  const bf16_t* Q = static_cast<const bf16_t*>(a.q);
+  bf16x8_t qf[kQB][KS];
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
+  for (int qb = 0; qb < kQB; ++qb)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
+    for (int ks = 0; ks < KS; ++ks) {
+      if (pos[qb] >= 0) {
+        qf[qb][ks] = *reinterpret_cast<const bf16x8_t*>(Q + (qrow[qb] * a.hq + h[qb]) * D + ks * 16 + hf * 8);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qf[qb][ks][e] = static_cast<__bf16>(0.f);
+      }
+    }
 
-  // per-request base of this kv head; rows are row_stride elements apart
+  f32x16_t o[kQB][DB];
+#pragma unroll
+  for (int qb = 0; qb < kQB; ++qb)
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[qb][db][i] = 0.f;
+  float m_run[kQB], l_lane[kQB];                  // l_lane: this lane's half of the row sums
+#pragma unroll
+  for (int qb = 0; qb < kQB; ++qb) {
+    m_run[qb] = -INFINITY;
+    l_lane[qb] = 0.f;
+  }
+
   const int64_t row_stride = static_cast<int64_t>(hkv) * D;
   const bf16_t* Kreq = static_cast<const bf16_t*>(a.k) + krow0 * row_stride + static_cast<int64_t>(g) * D;
   const bf16_t* Vreq = static_cast<const bf16_t*>(a.v) + krow0 * row_stride + static_cast<int64_t>(g) * D;
-  // this lane's DMA slot: row lane / CPR of each group, physical chunk lane % CPR
-  const int dma_rr = lane / CPR, dma_p = lane % CPR;
-
-  auto dma_tile = [&](const bf16_t* src_req, bf16_t* dst, int kb0) __attribute__((always_inline)) {
+  // Tile copies go through buffer resources whose range ends at key klim:
+  // rows past it read as zeros (those keys are masked for every row), so no
+  // per-row clamp is needed.  A lane's byte offset within a tile is fixed
+  // per copy instruction; the tile adds kb0 rows.
+  const int rs2 = static_cast<int>(row_stride) * 2;        // bytes per key row
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16_t*>(Kreq), 0, klim > 0 ? klim * rs2 : 0, kBufferRsrcWord3);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16_t*>(Vreq), 0, klim > 0 ? klim * rs2 : 0, kBufferRsrcWord3);
+  int dvo[NDMA];
+  {
+    const int dma_rr = lane / CPR, dma_p = lane % CPR;
 #pragma unroll
     for (int j = 0; j < NDMA; ++j) {
-      const int grp = w * NDMA + j;
-      const int row = grp * RPI + dma_rr;
-      const int q = dma_p ^ chunk_xor<D>(row);            // logical chunk held by this slot
-      const int key = min(kb0 + row, klim - 1);           // tail rows repeat a valid key
-      const bf16_t* src = src_req + static_cast<int64_t>(key) * row_stride + q * 8;
-      __builtin_amdgcn_global_load_lds((global_cvoid_t*)(src), (lds_void_t*)(dst + grp * RPI * D), 16, 0, 0);
+      const int row = (w * NDMA + j) * RPI + dma_rr;
+      dvo[j] = row * rs2 + ((dma_p ^ chunk_xor<D>(row)) << 4);   // slot holds logical chunk p ^ x
     }
+  }
+  auto dma_tile = [&](__amdgpu_buffer_rsrc_t rs, bf16_t* dst, int kb0) __attribute__((always_inline)) {
+    const int toff = kb0 * rs2;
+#pragma unroll
+    for (int j = 0; j < NDMA; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(dst + (w * NDMA + j) * RPI * D), 16u,
+                                               static_cast<unsigned>(dvo[j] + toff), 0u, 0u, 0u);
   };
 
   // Softmax state in the log2 domain: scores enter as s * c with
-  // c = sm_scale * log2(e).  The running max m_run is raised only when a
-  // tile's max exceeds it by more than kSlack (then O and l are rescaled);
-  // otherwise probabilities are taken against the old max and may exceed 1
-  // by at most 2^kSlack, which fp32 sums and bf16 operands carry exactly as
-  // well.  The result is the same softmax, with far fewer rescales.
-  constexpr float kSlack = 8.f;
+  // c = sm_scale * log2(e).  Probabilities are taken against a running max
+  // m_run that is raised only when a block's probabilities would exceed
+  // 2^8 (then O and l are rescaled); fp32 sums and bf16 operands carry such
+  // values exactly as well, so the result is the same softmax with far
+  // fewer rescales.
+  constexpr float kSlackSum = 256.f;                // 2^8
   const float c_scale = a.scale_log2;
   const f32x16_t zero16 = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   const bf16x2_t ones2 = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
-  // LDS element offsets of this lane's operand reads, with the XOR swizzle
-  // resolved once: the swizzle term depends only on row mod 16, which the
-  // 32-key and 16-key block steps (multiples of 16 rows) do not change.
-  // K rows 64 kg + 32 kb + c, channel chunk 2 kk + hf:
+  // LDS element offsets of this lane's operand reads with the swizzle
+  // resolved once (it depends on row mod 16 only).
+  // K: row c of a 32-key block, channel chunk 2 ks + hf
   int koff[KS];
 #pragma unroll
-  for (int kk = 0; kk < KS; ++kk)
-    koff[kk] = (64 * kg + c) * D + (((2 * kk + hf) ^ chunk_xor<D>(c)) << 3);
+  for (int ks = 0; ks < KS; ++ks) koff[ks] = c * D + (((2 * ks + hf) ^ chunk_xor<D>(c)) << 3);
   // transposed V reads: lane i of 16-lane group G reads keys 4 hf + i/4 (+8)
-  // and channels 32 db + 16 (G%2) + 4 (i%4) .. +3
+  // and channels 32 db + 16 (G%2) + 4 (i%4) .. +3 of a 16-key group
   const int tr_key = 4 * hf + ((lane & 15) >> 2);
   const int tr_d = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
   int voff[2][DB];
@@ -219,174 +297,242 @@ __global__ void __launch_bounds__(kAThreads) attn_bf16_kernel(AttnArgs a) {
     const int row = tr_key + 8 * hl;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
-      voff[hl][db] = (64 * kg + row) * D + ((((4 * db + (tr_d >> 3)) ^ chunk_xor<D>(row))) << 3) + (tr_d & 7);
+      voff[hl][db] = row * D + ((((4 * db + (tr_d >> 3)) ^ chunk_xor<D>(row))) << 3) + (tr_d & 7);
   }
 
-  // One 128-key tile computed from (ks, vs).  MASK selects the variant that
-  // applies the causal and range mask (only the last tiles need it).
-  auto step = [&](const bf16_t* ks_, const bf16_t* vs_, int kb0, auto mask_tag) __attribute__((always_inline)) {
-    constexpr bool MASK = decltype(mask_tag)::value;
-    const int k_half = kb0 + 64 * kg;             // first key of this wave's half
-    if (k_half >= klim) return;                   // wave-uniform
-    f32x16_t s[2];
+  // S^T for one 32-key block (keys on the MFMA rows, query vectors on lanes):
+  // lane (c, hf) value i is key 8 (i/4) + 4 hf + (i%4) of the block
+  auto scores = [&](const bf16_t* kt, int kb, f32x16_t (&s)[kQB]) __attribute__((always_inline)) {
+    const bf16_t* kr = kt + kb * 32 * D;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const bf16_t* krow = ks_ + kb * 32 * D;      // + koff: row 64 kg + 32 kb + c
-      const bf16x8_t k0 = *reinterpret_cast<const bf16x8_t*>(krow + koff[0]);
-      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[0], zero16, 0, 0, 0);
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(kr + koff[ks]);
 #pragma unroll
-      for (int kk = 1; kk < KS; ++kk) {
-        const bf16x8_t kfrag = *reinterpret_cast<const bf16x8_t*>(krow + koff[kk]);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag, qf[kk], s[kb], 0, 0, 0);
+      for (int qb = 0; qb < kQB; ++qb)
+        s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][ks], ks == 0 ? zero16 : s[qb], 0, 0, 0);
+    }
+  };
+  // masked keys -> -inf (keys past a row's position; kb0 = block's first key)
+  auto apply_mask = [&](f32x16_t (&s)[kQB], int kb0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) {
+      const int lim = pos[qb] - kb0 - 4 * hf;
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (8 * (i >> 2) + (i & 3) > lim) s[qb][i] = -INFINITY;
+    }
+  };
+  // probabilities as bf16 pairs against the running max; the row sum is
+  // taken over exactly the bf16 values the V product consumes.  Returns this
+  // block's lane-local sums.
+  auto probs = [&](const f32x16_t (&s)[kQB], uint32_t (&pk)[kQB][8], float (&lb)[kQB]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) {
+      const float neg_m = m_run[qb] == -INFINITY ? 0.f : -m_run[qb];
+      lb[qb] = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[qb][2 * i], c_scale, neg_m));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[qb][2 * i + 1], c_scale, neg_m));
+        pk[qb][i] = pack_bf16x2(p0, p1);
+        lb[qb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[qb][i]), ones2, lb[qb], false);
       }
     }
-    if constexpr (MASK) {
-      // key = k_half + 32 kb + 8 (i/4) + 4 hf + (i%4) is visible iff key <= lim
-      const int lim = min(pos, klim - 1) - k_half - 4 * hf;
+  };
+  // Raise the running max to the exact max of block s, rescaling O and l.
+  auto raise_max = [&](const f32x16_t (&s)[kQB]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+    for (int qb = 0; qb < kQB; ++qb) {
+      float m = fmaxf(s[qb][0], s[qb][1]);
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (kb * 32 + 8 * (i >> 2) + (i & 3) > lim) s[kb][i] = -INFINITY;
-    }
-    float mx = fmaxf(s[0][0], s[0][1]);
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = (kb == 0 ? 2 : 0); i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave)) * c_scale;     // tile max, log2 domain
-    if (__builtin_expect(__any(mx > m_run + kSlack), 0)) {
-      asm volatile("; rescale");                  // keeps this rare path a branch
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= alpha;
+      for (int i = 2; i < 16; ++i) m = fmaxf(m, s[qb][i]);
+      const float mx = fmaxf(m, __shfl_xor(m, 32, kWave)) * c_scale;
+      const float m_new = fmaxf(m_run[qb], mx);
+      const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run[qb] - m_new);
+      l_lane[qb] *= alpha;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
-      m_run = m_new;
+        for (int i = 0; i < 16; ++i) o[qb][db][i] *= alpha;
+      m_run[qb] = m_new;
     }
-    const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
-    float rs = 0.f;
-    {
-      uint32_t pk[2][8];                          // bf16 probability pairs
+  };
+  // O^T += V^T P^T for one 32-key block of tile vt
+  auto pv = [&](const bf16_t* vt, int kb, const uint32_t (&pk)[kQB][8]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+    for (int st = 0; st < 2; ++st) {
+      bf16x8_t pb[kQB];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kb][2 * i], c_scale, neg_m));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kb][2 * i + 1], c_scale, neg_m));
-          pk[kb][i] = pack_bf16x2(p0, p1);
-          // normalise by the sum of the bf16 values the V product consumes
-          rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[kb][i]), ones2, rs, false);
-        }
+      for (int qb = 0; qb < kQB; ++qb) {
+        const u32x4_t pw = {pk[qb][4 * st], pk[qb][4 * st + 1], pk[qb][4 * st + 2], pk[qb][4 * st + 3]};
+        pb[qb] = __builtin_bit_cast(bf16x8_t, pw);
+      }
+      const bf16_t* vblk = vt + (kb * 32 + 16 * st) * D;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int db = 0; db < DB; ++db) {
+        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vblk + voff[0][db]));
+        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vblk + voff[1][db]));
+        const s16x4_t vv[2] = {lo, hi};
+        const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, vv);
 #pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          const u32x4_t pw = {pk[kb][4 * st], pk[kb][4 * st + 1], pk[kb][4 * st + 2], pk[kb][4 * st + 3]};
-          const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pw);
-          const bf16_t* vblk = vs_ + (kb * 32 + 16 * st) * D;   // + voff: this lane's rows
-          // keep each 16-key group's V reads next to its MFMAs (register pressure)
-          __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vblk + voff[0][db]));
-            const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vblk + voff[1][db]));
-            const s16x4_t vv[2] = {lo, hi};
-            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, vv), pb,
-                                                            o[db], 0, 0, 0);
-          }
-        }
+        for (int qb = 0; qb < kQB; ++qb)
+          o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[qb], o[qb][db], 0, 0, 0);
       }
     }
-    rs += __shfl_xor(rs, 32, kWave);
-    l_run += rs;
   };
 
-  const int ntiles = klim > kbeg ? ceil_div(klim - kbeg, kAT) : 0;
-  // leading tiles every row sees completely need no mask
-  int n_plain = 0;
-  if (pmin >= kbeg) n_plain = min(min(ntiles, (pmin + 1 - kbeg) / kAT), (klim - kbeg) / kAT);
-  auto run_tile = [&](int t, const bf16_t* ks_, const bf16_t* vs_) __attribute__((always_inline)) {
-    if (t < n_plain)
-      step(ks_, vs_, kbeg + t * kAT, std::false_type{});
-    else
-      step(ks_, vs_, kbeg + t * kAT, std::true_type{});
+  // Software pipeline over 32-key blocks b: one half step runs the score
+  // MFMAs of block b+1, the softmax of block b and the V product of block
+  // b-1 in one branch-free stretch (the V product lags by a block so that
+  // its MFMAs never wait for this block's exponentials).  Per tile t there is
+  // one barrier (B), after which K_{t+2} and V_{t+1} are copied into the
+  // buffers of K_t and V_{t-1}: the half step before B still reads those,
+  // the one after B reads K_{t+1} and V_t, which the barrier waited for.
+  f32x16_t s_a[kQB], s_b[kQB];                     // scores of blocks 0 and 1 of a tile
+  uint32_t pk_a[kQB][8], pk_b[kQB][8];             // probabilities of blocks 0 and 1
+#pragma unroll
+  for (int qb = 0; qb < kQB; ++qb)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) pk_b[qb][i] = 0u;  // "block -1": contributes nothing
+  // sc: scores of block b (first key kb0); kt/kbs: K tile and block of b+1
+  // into sn; vt/kbp/pkp: V tile, block and probabilities of b-1; pkc gets b's.
+  // Lazy rescaling without a per-element max: a block whose lane-local
+  // probability sums stay within 2^8 has no probability above 2^8, so it is
+  // used as computed; otherwise the exact block max is taken, O and l are
+  // rescaled to it and the block's probabilities are recomputed.
+  auto half_step = [&](f32x16_t (&sc)[kQB], int kb0, bool masked, const bf16_t* kt, int kbs,
+                       f32x16_t (&sn)[kQB], const bf16_t* vt, int kbp, const uint32_t (&pkp)[kQB][8],
+                       uint32_t (&pkc)[kQB][8]) __attribute__((always_inline)) {
+    if (masked) apply_mask(sc, kb0);
+    float lb[kQB];
+    scores(kt, kbs, sn);
+    probs(sc, pkc, lb);
+    pv(vt, kbp, pkp);
+    bool big = false;
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) big = big || lb[qb] > kSlackSum;
+    if (__builtin_expect(__any(big), 0)) {
+      asm volatile("; rescale");                  // keeps this rare path a branch
+      raise_max(sc);
+      probs(sc, pkc, lb);
+    }
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) l_lane[qb] += lb[qb];
   };
-  if (ntiles > 0) {
-    dma_tile(Kreq, k0s, kbeg);
-    dma_tile(Vreq, v0s, kbeg);
+  // tile t: kc holds K_t, kn K_{t+1}; vc holds V_t, vp V_{t-1}
+  auto tile_step = [&](int t, bf16_t* kc, const bf16_t* kn, const bf16_t* vc, bf16_t* vp)
+      __attribute__((always_inline)) {
+    const bool masked = t >= n_plain;
+    // S(2t+1) from K_t, softmax(2t), P(2t-1) V_{t-1}
+    half_step(s_a, t * kAT, masked, kc, 1, s_b, vp, 1, pk_b, pk_a);
+    // B: K_{t+1} and V_t landed everywhere; K_t and V_{t-1} free
+    copies_landed_barrier<0>();
+    if (t + 2 < t1) dma_tile(krs, kc, (t + 2) * kAT);
+    if (t + 1 < t1) dma_tile(vrs, vp, (t + 1) * kAT);
+    // S(2t+2) from K_{t+1} (unused after the last tile), softmax(2t+1), P(2t) V_t
+    half_step(s_b, t * kAT + 32, masked, kn, 0, s_a, vc, 0, pk_a, pk_b);
+  };
+
+  if (t1 > t0) {
+    dma_tile(krs, k0s, t0 * kAT);
+    dma_tile(vrs, v0s, t0 * kAT);
+    if (t0 + 1 < t1) dma_tile(krs, k1s, (t0 + 1) * kAT);
+    // the first half step multiplies zero probabilities with "V_{t0-1}"
+    for (int i = tid; i < TILE / 8; i += kAThreads)
+      *reinterpret_cast<u32x4_t*>(v1s + 8 * i) = u32x4_t{0u, 0u, 0u, 0u};
+    copies_landed_barrier<0>();
+    scores(k0s, 0, s_a);
+    if (t0 >= n_plain) apply_mask(s_a, t0 * kAT);
+    raise_max(s_a);                                 // the first block sets the max exactly
   }
-  __syncthreads();                                // waits for the DMA (vmcnt) too
   // two tiles per trip so every buffer is a distinct static array
-  for (int t = 0; t < ntiles; t += 2) {
-    if (t + 1 < ntiles) {
-      dma_tile(Kreq, k1s, kbeg + (t + 1) * kAT);
-      dma_tile(Vreq, v1s, kbeg + (t + 1) * kAT);
-    }
-    run_tile(t, k0s, v0s);
-    __syncthreads();
-    if (t + 1 >= ntiles) break;
-    if (t + 2 < ntiles) {
-      dma_tile(Kreq, k0s, kbeg + (t + 2) * kAT);
-      dma_tile(Vreq, v0s, kbeg + (t + 2) * kAT);
-    }
-    run_tile(t + 1, k1s, v1s);
-    __syncthreads();
+  int tl = t0;                                      // last tile processed
+  for (int t = t0; t < t1; t += 2) {
+    tile_step(t, k0s, k1s, v0s, v1s);
+    tl = t;
+    if (t + 1 >= t1) break;
+    tile_step(t + 1, k1s, k0s, v1s, v0s);
+    tl = t + 1;
+  }
+  // P(last block) V_{last tile}
+  if (t1 > t0) {
+    if (((tl - t0) & 1) == 0) pv(v0s, 1, pk_b);
+    else pv(v1s, 1, pk_b);
   }
 
-  // merge the two key halves: waves 4..7 hand (m, l, O) to waves 0..3
-  const int slot = qg * 64 + lane;
-  float* xo0 = reinterpret_cast<float*>(k0s);     // O blocks [0, DB/2)
-  float* xo1 = reinterpret_cast<float*>(k1s);     // O blocks [DB/2, DB)
-  float* xml = reinterpret_cast<float*>(v0s);
-  constexpr int HO = 8 * DB;                      // floats per lane in each O half
-  if (kg == 1) {
-    xml[2 * slot] = m_run;
-    xml[2 * slot + 1] = l_run;
+  if (split) {
+    // Partial state of this part, value-major so a store is one coalesced
+    // row per value: O (unnormalised), then m and the lane's half of l.
+    // Every partial value is stored and loaded as a relaxed device-scope
+    // atomic, which is coherent across the XCDs' L2 caches, and the arrival
+    // counter is bumped only after the barrier has waited for all of the
+    // workgroup's stores to complete.  Device-scope fences would do the same
+    // by writing back and invalidating the whole L2, evicting the K/V tiles
+    // the other workgroups on this XCD are streaming.
+    constexpr int NV = kQB * (DB * 16 + 2);
+    const int64_t item = static_cast<int64_t>(tile) * hkv + g;
+    float* mine = a.ws_part + ((item * 2 + part) * NV) * kAThreads + tid;
+    auto put = [&](int e, float x) __attribute__((always_inline)) {
+      __hip_atomic_store(mine + e * kAThreads, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    int e = 0;
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) put(e++, o[qb][db][i]);
+      put(e++, m_run[qb]);
+      put(e++, l_lane[qb]);
+    }
+    __syncthreads();                              // waits for this workgroup's stores
+    if (tid == 0)
+      s_pos[0] = __hip_atomic_fetch_add(&a.ws_cnt[item], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (s_pos[0] == 0) return;                    // first to finish: the other part merges
+    const float* other = a.ws_part + ((item * 2 + (part ^ 1)) * NV) * kAThreads + tid;
+    auto get = [&](int e) __attribute__((always_inline)) {
+      return __hip_atomic_load(other + e * kAThreads, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    e = 0;
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) {
+      const float m2 = get(e + DB * 16);
+      const float l2 = get(e + DB * 16 + 1);
+      const float mm = fmaxf(m_run[qb], m2);
+      const float mu = mm == -INFINITY ? 0.f : mm;
+      const float a1 = __builtin_amdgcn_exp2f(m_run[qb] - mu), a2 = __builtin_amdgcn_exp2f(m2 - mu);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[qb][db][i] = o[qb][db][i] * a1 + get(e++) * a2;
+      e += 2;
+      l_lane[qb] = l_lane[qb] * a1 + l2 * a2;
+      m_run[qb] = mm;
+    }
+    // both parts have arrived: leave the counter zero for the next call
+    if (tid == 0) __hip_atomic_store(&a.ws_cnt[item], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+
+#pragma unroll
+  for (int qb = 0; qb < kQB; ++qb) {
+    if (!valid[qb] || pos[qb] < 0) continue;
+    const float l = l_lane[qb] + __shfl_xor(l_lane[qb], 32, kWave);
+    const int64_t orow = static_cast<int64_t>(a.orow0[r]) + lrow0 + row_l[qb];
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    bf16_t* O = static_cast<bf16_t*>(a.out) + (orow * a.hq + h[qb]) * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float* dstp = db < DB / 2 ? xo0 : xo1;
-        dstp[slot * HO + (db % (DB / 2)) * 16 + i] = o[db][i];
+      for (int i = 0; i < 4; ++i) {
+        const int d0 = db * 32 + 8 * i + 4 * hf;
+        u32x2_t pk2;
+        pk2[0] = pack_bf16x2(o[qb][db][4 * i] * inv, o[qb][db][4 * i + 1] * inv);
+        pk2[1] = pack_bf16x2(o[qb][db][4 * i + 2] * inv, o[qb][db][4 * i + 3] * inv);
+        *reinterpret_cast<u32x2_t*>(O + d0) = pk2;
       }
+    if (a.lse && hf == 0) a.lse[orow * a.hq + h[qb]] = (m_run[qb] + log2f(l)) * kLn2;
   }
-  __syncthreads();
-  if (kg == 1) return;
-  {
-    const float m2 = xml[2 * slot];
-    const float l2 = xml[2 * slot + 1];
-    const float mm = fmaxf(m_run, m2);
-    const float mu = mm == -INFINITY ? 0.f : mm;
-    const float a1 = __builtin_amdgcn_exp2f(m_run - mu), a2 = __builtin_amdgcn_exp2f(m2 - mu);
-    l_run = l_run * a1 + l2 * a2;
-    m_run = mm;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float* srcp = db < DB / 2 ? xo0 : xo1;
-        o[db][i] = o[db][i] * a1 + srcp[slot * HO + (db % (DB / 2)) * 16 + i] * a2;
-      }
-  }
-
-  if (!valid || pos < 0) return;
-  const int64_t orow = static_cast<int64_t>(a.orow0[r]) + lrow0 + row_l;
-  const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-  bf16_t* O = static_cast<bf16_t*>(a.out) + (orow * a.hq + h) * D;
-#pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int d0 = db * 32 + 8 * i + 4 * hf;
-      u32x2_t pk2;
-      pk2[0] = pack_bf16x2(o[db][4 * i] * inv, o[db][4 * i + 1] * inv);
-      pk2[1] = pack_bf16x2(o[db][4 * i + 2] * inv, o[db][4 * i + 3] * inv);
-      *reinterpret_cast<u32x2_t*>(O + d0) = pk2;
-    }
-  if (a.lse && hf == 0) a.lse[orow * a.hq + h] = (m_run + log2f(l_run)) * kLn2;
 }
 
 template <int D>
@@ -398,6 +544,8 @@ static hipError_t launch_attn_bf16(const AttnArgs& a, dim3 grid, hipStream_t st)
 // ---------------------------------------------------------------------------
 // fp32 kernel: one wave per (row, head)
 // ---------------------------------------------------------------------------
+constexpr int kFT = 128;         // key granularity of the fp32 statistics splits
+
 template <bool STATS_ONLY>
 __global__ void __launch_bounds__(256) attn_f32_kernel(AttnArgs a, int d, int total_rows) {
   const int wid = (blockIdx.x * blockDim.x + threadIdx.x) / kWave;
@@ -478,10 +626,42 @@ static void fill_tiles(AttnArgs& a, int R) {
 
 static int rows_per_tile(int G) { return G >= kAQ ? 1 : kAQ / G; }
 
+// Key splitting: only grids that one dispatch round holds (two workgroups
+// per CU) have too few workgroups to even out tiles of unequal length, so
+// only they get the workspace; row tiles of at least kSplitMinTiles key
+// tiles are split.
+constexpr int kSplitMaxItems = 2 * kCUs;
+constexpr int kSplitMinTiles = 24;
+
+struct AttnSplitLayout {
+  int64_t items = 0;             // row tiles x kv heads
+  size_t off_cnt = 0, bytes = 0;
+};
+
+static AttnSplitLayout attn_split_layout(const kvf_layer_desc& L, const BatchArgs& B,
+                                         const int32_t* cu_q) {
+  AttnSplitLayout s;
+  if (L.dtype != KVF_BF16) return s;
+  const int R = rows_per_tile(L.n_q_heads / L.n_kv_heads);
+  int64_t tiles = 0;
+  for (int r = 0; r < B.n_req; ++r) tiles += ceil_div(cu_q[r + 1] - cu_q[r], R);
+  const int64_t items = tiles * L.n_kv_heads;
+  if (items == 0 || items > kSplitMaxItems) return s;
+  const int64_t nv = kQB * (L.head_dim / 32 * 16 + 2);
+  s.items = items;
+  s.off_cnt = static_cast<size_t>(items * 2 * nv * kAThreads) * sizeof(float);
+  s.bytes = s.off_cnt + static_cast<size_t>(items) * sizeof(int);
+  return s;
+}
+
+size_t attention_workspace(const kvf_layer_desc& L, const BatchArgs& B, const int32_t* cu_q) {
+  return attn_split_layout(L, B, cu_q).bytes;
+}
+
 hipError_t launch_attention(const kvf_layer_desc& L, const BatchArgs& B, const void* q,
                             const int32_t* q_pos, const int32_t* cu_q, const void* fk,
-                            const void* fv, float sm_scale, void* out, float* lse,
-                            hipStream_t st) {
+                            const void* fv, float sm_scale, void* out, float* lse, void* ws,
+                            size_t ws_bytes, hipStream_t st) {
   AttnArgs a{};
   a.b = B;
   for (int r = 0; r < B.n_req; ++r) {
@@ -501,11 +681,23 @@ hipError_t launch_attention(const kvf_layer_desc& L, const BatchArgs& B, const v
   a.G = L.n_q_heads / L.n_kv_heads;
   a.scale_log2 = sm_scale * kLog2e;
   a.n_splits = 1;
+  a.parts = 1;
   if (L.dtype == KVF_BF16) {
     fill_tiles(a, rows_per_tile(a.G));
-    const int64_t blocks = static_cast<int64_t>(a.total_tiles) * a.hkv;
-    if (blocks == 0) return hipSuccess;
+    const int64_t tiles = static_cast<int64_t>(a.total_tiles) * a.hkv;
+    if (tiles == 0) return hipSuccess;
+    const AttnSplitLayout sl = attn_split_layout(L, B, cu_q);
+    if (sl.bytes > 0 && ws != nullptr && ws_bytes >= sl.bytes) {
+      a.parts = 2;
+      a.split_min = kSplitMinTiles;
+      a.ws_part = static_cast<float*>(ws);
+      a.ws_cnt = reinterpret_cast<int*>(static_cast<char*>(ws) + sl.off_cnt);
+    }
+    const int64_t blocks = tiles * a.parts;
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+    // without splitting, a grid that one dispatch round holds runs its second
+    // round smallest-first, pairing long and short tiles on a CU
+    a.fold_from = a.parts == 1 && blocks <= 2 * kCUs ? std::max(1, kCUs / a.hkv) : a.total_tiles;
     const hipError_t e = L.head_dim == 128 ? launch_attn_bf16<128>(a, dim3(blocks), st)
                                            : launch_attn_bf16<64>(a, dim3(blocks), st);
     if (e != hipSuccess) return e;
@@ -870,10 +1062,10 @@ MassLayout mass_layout(const kvf_layer_desc& L, const BatchArgs& B, int n_last_q
   } else {
     // fp32 statistics kernel: enough splits to cover the chip twice
     const int64_t base = std::max<int64_t>(1, m.rows * L.n_q_heads / 4);
-    const int key_tiles = std::max(1, ceil_div(max_T, kAT));
+    const int key_tiles = std::max(1, ceil_div(max_T, kFT));
     int splits = static_cast<int>(std::min<int64_t>(key_tiles, ceil_div(512, static_cast<int>(std::min<int64_t>(base, 512)))));
     splits = std::max(1, std::min(splits, 64));
-    m.split_keys = ceil_div(key_tiles, splits) * kAT;
+    m.split_keys = ceil_div(key_tiles, splits) * kFT;
     m.n_splits = ceil_div(std::max(max_T, 1), m.split_keys);
   }
   const int64_t plane = m.rows * L.n_q_heads;

@@ -319,26 +319,51 @@ kvf_status kvf_scatter_kv(const kvf_layer_desc* layer, const void* k_src,
   KVF_GUARD_END
 }
 
+static kvf_status check_cu_q(const kvf::BatchArgs& B, const int32_t* cu_q) {
+  KVF_CHECK(cu_q != nullptr, KVF_ERR_INVALID_ARG, "cu_q is NULL");
+  KVF_CHECK(cu_q[0] == 0, KVF_ERR_INVALID_ARG, "cu_q[0] must be 0");
+  for (int r = 0; r < B.n_req; ++r)
+    KVF_CHECK(cu_q[r + 1] >= cu_q[r], KVF_ERR_INVALID_ARG, "cu_q decreases at %d", r);
+  return KVF_OK;
+}
+
+size_t kvf_attention_workspace_size(const kvf_layer_desc* layer, const kvf_batch* batch,
+                                    const int32_t* cu_q) {
+  try {
+    if (check_layer(layer) != KVF_OK) return 0;
+    kvf::BatchArgs B;
+    if (check_batch(batch, &B) != KVF_OK || check_cu_q(B, cu_q) != KVF_OK) return 0;
+    return kvf::attention_workspace(*layer, B, cu_q);
+  } catch (...) {
+    return 0;
+  }
+}
+
 kvf_status kvf_sparse_q_attention(const kvf_layer_desc* layer, const kvf_batch* batch,
                                   const void* q, const int32_t* q_pos, const int32_t* cu_q,
                                   const void* fused_k, const void* fused_v, float sm_scale,
-                                  void* out, float* lse, void* stream) {
+                                  void* out, float* lse, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
   KVF_GUARD_BEGIN
   kvf_status st = check_layer(layer);
   if (st != KVF_OK) return st;
   kvf::BatchArgs B;
   st = check_batch(batch, &B);
   if (st != KVF_OK) return st;
-  KVF_CHECK(cu_q != nullptr, KVF_ERR_INVALID_ARG, "cu_q is NULL");
-  KVF_CHECK(cu_q[0] == 0, KVF_ERR_INVALID_ARG, "cu_q[0] must be 0");
-  for (int r = 0; r < B.n_req; ++r)
-    KVF_CHECK(cu_q[r + 1] >= cu_q[r], KVF_ERR_INVALID_ARG, "cu_q decreases at %d", r);
+  st = check_cu_q(B, cu_q);
+  if (st != KVF_OK) return st;
   KVF_CHECK(sm_scale > 0.f && sm_scale < 1e30f, KVF_ERR_INVALID_ARG, "bad sm_scale");
   if (cu_q[B.n_req] == 0) return KVF_OK;
   KVF_CHECK(q && q_pos && fused_k && fused_v && out, KVF_ERR_INVALID_ARG,
             "required pointer is NULL");
+  if (workspace != nullptr) {
+    const size_t need = kvf::attention_workspace(*layer, B, cu_q);
+    KVF_CHECK(workspace_bytes >= need, KVF_ERR_WORKSPACE,
+              "attention workspace %zu bytes, needs %zu", workspace_bytes, need);
+  }
   return from_hip(kvf::launch_attention(*layer, B, q, q_pos, cu_q, fused_k, fused_v, sm_scale,
-                                        out, lse, as_stream(stream)), "kvf_sparse_q_attention");
+                                        out, lse, workspace, workspace_bytes, as_stream(stream)),
+                  "kvf_sparse_q_attention");
   KVF_GUARD_END
 }
 

@@ -12,6 +12,7 @@ namespace kvf {
 
 constexpr int kWave = 64;
 constexpr int kXcds = 8;          // MI355X: 8 accelerator complex dies, one L2 each
+constexpr int kCUs = 256;         // MI355X: 32 compute units per XCD
 
 using bf16_t = uint16_t;          // storage form of bf16 values
 
@@ -157,6 +158,7 @@ hipError_t launch_scatter(const kvf_layer_desc& L, const void* ks, const int32_t
                           hipStream_t st);
 hipError_t launch_attention(const kvf_layer_desc& L, const BatchArgs& B, const void* q,
                             const int32_t* q_pos, const int32_t* cu_q_host, const void* fk,
-                            const void* fv, float sm_scale, void* out, float* lse,
-                            hipStream_t st);
+                            const void* fv, float sm_scale, void* out, float* lse, void* ws,
+                            size_t ws_bytes, hipStream_t st);
+size_t attention_workspace(const kvf_layer_desc& L, const BatchArgs& B, const int32_t* cu_q_host);
 }  // namespace kvf

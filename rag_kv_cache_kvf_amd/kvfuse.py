@@ -80,7 +80,9 @@ _SIGS = {
                                  _P, _P, _P, _P, _I64, _P, _SZ, _P]),
     "kvf_recompute_workspace_size": (_SZ, [_LP, _I32, ctypes.c_uint32]),
     "kvf_scatter_kv": (_I32, [_LP, _P, _P, _I64, _P, _P, _I64, _P, _I32, _P, _P, _I64, _P]),
-    "kvf_sparse_q_attention": (_I32, [_LP, _BP, _P, _P, _IP, _P, _P, ctypes.c_float, _P, _P, _P]),
+    "kvf_sparse_q_attention": (_I32, [_LP, _BP, _P, _P, _IP, _P, _P, ctypes.c_float, _P, _P, _P,
+                                      _SZ, _P]),
+    "kvf_attention_workspace_size": (_SZ, [_LP, _BP, _IP]),
     "kvf_kivi8_encode": (_I32, [_LP, _P, _P, _P, _I32, _I64, _I32, ctypes.POINTER(Kivi8Desc), _P]),
     "kvf_recompute_budget": (_I32, [_I32, _I32]),
     "kvf_status_string": (ctypes.c_char_p, [_I32]),
@@ -273,15 +275,25 @@ def scatter_kv(layer: Layer, k_src: Optional[torch.Tensor], k_src_row: Optional[
            "kvf_scatter_kv")
 
 
+def attention_workspace_size(layer: Layer, batch: Batch, cu_q: Sequence[int]) -> int:
+    d = layer.desc()
+    return int(_lib.kvf_attention_workspace_size(ctypes.byref(d), ctypes.byref(batch.desc),
+                                                 _int_array(cu_q)))
+
+
 def sparse_q_attention(layer: Layer, batch: Batch, q: torch.Tensor, q_pos: torch.Tensor,
                        cu_q: Sequence[int], fused_k: torch.Tensor, fused_v: torch.Tensor,
                        sm_scale: float, out: torch.Tensor, lse: Optional[torch.Tensor] = None,
-                       stream=None):
+                       workspace: Optional[torch.Tensor] = None, stream=None):
+    """workspace: attention_workspace_size bytes, zero-filled when allocated
+    (the call leaves it zeroed); None runs without key splitting."""
     d = layer.desc()
     cq = _int_array(cu_q)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_lib.kvf_sparse_q_attention(ctypes.byref(d), ctypes.byref(batch.desc), _ptr(q),
                                        _ptr(q_pos), cq, _ptr(fused_k), _ptr(fused_v),
-                                       float(sm_scale), _ptr(out), _ptr(lse), _stream(stream)),
+                                       float(sm_scale), _ptr(out), _ptr(lse), _ptr(workspace),
+                                       ws_bytes, _stream(stream)),
            "kvf_sparse_q_attention")
 
 

@@ -143,6 +143,11 @@ class FusedLayerGPU:
         else:
             need.append(kvf.recompute_workspace_size(L, nU, QKV))
         self.gemm_ws = torch.empty(max(max(need), 1), dtype=torch.uint8, device=dev)
+        # key-split workspace of the attention call: zero-filled once, every
+        # call leaves it zeroed
+        attn_need = kvf.attention_workspace_size(self.layer, self.kb, self.cu_q)
+        self.attn_ws = (torch.zeros(attn_need, dtype=torch.uint8, device=dev)
+                        if attn_need > 0 else None)
 
     # ------------------------------------------------------------------ calls
     def _rerotate(self):
@@ -197,7 +202,8 @@ class FusedLayerGPU:
         if self.M == 0:
             return
         kvf.sparse_q_attention(self.layer, self.kb, self.q, self.pos, self.cu_q, self.fused_k,
-                               self.fused_v, self.sm_scale, self.out, self.lse)
+                               self.fused_v, self.sm_scale, self.out, self.lse,
+                               workspace=self.attn_ws)
 
     def calls(self):
         """The library calls of one pass, in order, as (name, stage, fn):

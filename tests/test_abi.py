@@ -48,7 +48,7 @@ def test_status_strings_and_version(lib):
     lib.kvf_status_string.restype = ctypes.c_char_p
     assert lib.kvf_status_string(0) == b"KVF_OK"
     assert lib.kvf_status_string(2) == b"KVF_ERR_UNSUPPORTED"
-    assert lib.kvf_abi_version() == 3
+    assert lib.kvf_abi_version() == 4
 
 
 def test_budget_matches_oracle(lib):
@@ -128,6 +128,25 @@ def test_validation_errors(lib):
     b, keep = _batch([0, 10], [6])
     assert lib.kvf_score(1, ctypes.byref(ok), ctypes.byref(b), FAKE, None, FAKE, 0, FAKE, None, 0,
                          None) == 3
+    # attention: the key-split workspace exists only for small bf16 grids and
+    # a non-NULL workspace must be large enough
+    lib.kvf_attention_workspace_size.restype = ctypes.c_size_t
+    lib.kvf_sparse_q_attention.argtypes = [ctypes.c_void_p] * 7 + [ctypes.c_float] + \
+        [ctypes.c_void_p] * 3 + [ctypes.c_size_t, ctypes.c_void_p]
+    bq = Layer(4096, 32, 8, 128, 1)
+    ba, keep_a = _batch([0, 5184], [5120])
+    cq = (ctypes.c_int32 * 2)(0, 1600)
+    need = lib.kvf_attention_workspace_size(ctypes.byref(bq), ctypes.byref(ba), cq)
+    assert need == 50 * 8 * (2 * (4 * 16 + 2) * 256 * 4 + 4)
+    assert lib.kvf_sparse_q_attention(ctypes.byref(bq), ctypes.byref(ba), FAKE, FAKE, cq, FAKE, FAKE,
+                                      0.088, FAKE, None, FAKE, need - 1, None) == 3
+    big = (ctypes.c_int32 * 2)(0, 5184)
+    assert lib.kvf_attention_workspace_size(ctypes.byref(bq), ctypes.byref(ba), big) == 0
+    assert lib.kvf_attention_workspace_size(ctypes.byref(Layer(4096, 32, 8, 128, 0)),
+                                            ctypes.byref(ba), cq) == 0
+    bad = (ctypes.c_int32 * 2)(1, 1600)
+    assert lib.kvf_sparse_q_attention(ctypes.byref(bq), ctypes.byref(ba), FAKE, FAKE, bad, FAKE,
+                                      FAKE, 0.088, FAKE, None, None, 0, None) == 1
     # top-k: k > N
     k = (ctypes.c_int32 * 1)(7)
     assert lib.kvf_select_topk(FAKE, ctypes.byref(b), k, FAKE, None, None, None, 0, None) == 1

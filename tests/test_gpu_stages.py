@@ -479,6 +479,9 @@ ATTN_CASES = [
     ("bf16", 16, 2, 128, [700, 33], [199, 33]),
     ("bf16", 4, 2, 64, [500], [150]),
     ("bf16", 64, 8, 128, [300], [40]),
+    # long rows in a small grid: with a workspace their keys split in two
+    ("bf16", 32, 8, 128, [3000, 2000], [400, 700]),
+    ("bf16", 8, 2, 64, [2500], [300]),
     ("f32", 4, 4, 64, [288], [108]),
     ("f32", 4, 2, 64, [150, 140], [70, 39]),
 ]
@@ -498,10 +501,21 @@ def test_attention(kvf, case):
     k_s, v_s, q_s = encode(K, dtype), encode(V, dtype), encode(Q, dtype)
     L = _layer(kvf, 256, hq, hkv, d, dtype)
     kb = _kbatch(kvf, cu_T, [t for t in Ts])
-    out = torch.zeros((cu_q[-1], hq, d), dtype=L.torch_dtype, device="cuda")
-    lse = torch.zeros((cu_q[-1], hq), dtype=torch.float32, device="cuda")
-    kvf.sparse_q_attention(L, kb, to_gpu(q_s, dtype), to_gpu(pos), cu_q, to_gpu(k_s, dtype),
-                           to_gpu(v_s, dtype), 1 / math.sqrt(d), out, lse)
+    # without a workspace, then twice with one (the second call checks that
+    # the first left the arrival counters zeroed)
+    need = kvf.attention_workspace_size(L, kb, cu_q)
+    ws = torch.zeros(max(need, 1), dtype=torch.uint8, device="cuda") if need > 0 else None
+    runs = []
+    for w in [None] + ([ws, ws] if ws is not None else []):
+        out = torch.zeros((cu_q[-1], hq, d), dtype=L.torch_dtype, device="cuda")
+        lse = torch.zeros((cu_q[-1], hq), dtype=torch.float32, device="cuda")
+        kvf.sparse_q_attention(L, kb, to_gpu(q_s, dtype), to_gpu(pos), cu_q, to_gpu(k_s, dtype),
+                               to_gpu(v_s, dtype), 1 / math.sqrt(d), out, lse, workspace=w)
+        runs.append((from_gpu(out), from_gpu(lse)))
+    if ws is not None:
+        # the workspace ends in one int32 arrival counter per (row tile, kv head)
+        items = need // (2 * (d // 32 * 16 + 2) * 256 * 4 + 4)
+        assert not bool(ws[need - 4 * items:need].view(torch.int32).any()), "arrival counters not reset"
     lo = fusion.Layer(256, hq, hkv, d, 1e4)
     dk, dv, dq = decode(k_s, dtype), decode(v_s, dtype), decode(q_s, dtype)
     refs, lses = [], []
@@ -510,9 +524,18 @@ def test_attention(kvf, case):
                                        dk[cu_T[r]:cu_T[r + 1]], dv[cu_T[r]:cu_T[r + 1]], lo)
         refs.append(o)
         lses.append(l)
-    assert_close_vectors(from_gpu(out), np.concatenate(refs), dtype, f"attention {case[:4]}")
-    assert_close(from_gpu(lse), np.concatenate(lses), "f32" if dtype == "f32" else "bf16",
-                 f"attention lse {case[:4]}", tol=1e-4 if dtype == "f32" else 1e-3)
+    # Rows that see over 2000 keys average so many values that their output
+    # vectors are small, and the bf16 rounding of the probabilities (the
+    # serving precision of the P V product) then reaches about 2e-2 of a
+    # vector's RMS at its worst element: a CPU emulation of the kernel's
+    # arithmetic on this case gives 2.06e-2, the same emulation with exact
+    # running maxima 1.4e-2.  Those cases are held to 3e-2 per vector.
+    long_rows = max(Ts) > 2000
+    for i, (go, gl) in enumerate(runs):
+        tag = f"attention {case[:4]} run {i} ({'split' if i else 'unsplit'})"
+        assert_close_vectors(go, np.concatenate(refs), dtype, tag, tol=3e-2 if long_rows else None)
+        assert_close(gl, np.concatenate(lses), "f32" if dtype == "f32" else "bf16",
+                     tag + " lse", tol=1e-4 if dtype == "f32" else 1e-3)
 
 
 @pytest.mark.parametrize("wl_name", ["qwen3_8b_mass", "llama3_70b_mass", "qwen3_8b_dev_pool"])
@@ -538,8 +561,12 @@ def test_attention_full_size_sampled(kvf, wl_name):
     kb = _kbatch(kvf, cu_T, [N] * n_req)
     out = torch.zeros((cu_q[-1], hq, d), dtype=torch.bfloat16, device="cuda")
     lse = torch.zeros((cu_q[-1], hq), dtype=torch.float32, device="cuda")
+    # the launch configuration of the fused layer: with its workspace (key
+    # splitting where the grid is small)
+    need = kvf.attention_workspace_size(L, kb, cu_q)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda") if need > 0 else None
     kvf.sparse_q_attention(L, kb, to_gpu(q_s, "bf16"), to_gpu(pos), cu_q, to_gpu(k_s, "bf16"),
-                           to_gpu(v_s, "bf16"), 1 / math.sqrt(d), out, lse)
+                           to_gpu(v_s, "bf16"), 1 / math.sqrt(d), out, lse, workspace=ws)
     go, gl = from_gpu(out), from_gpu(lse)
     lo = fusion.Layer(wl.hidden, hq, hkv, d, wl.rope_base)
     samp = np.unique(np.concatenate([synth.random_rows(cu_q[-1], 24, 22), [0, cu_q[-1] - 1]]))
