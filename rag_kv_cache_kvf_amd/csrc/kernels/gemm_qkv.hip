@@ -239,6 +239,15 @@ gemm_qkv_bf16_kernel(GemmArgs a) {
 #pragma unroll
     for (int i = 0; i < BGW; ++i) dma16(bsrc[i] + k0, bs + (w + 4 * i) * 8 * kBK);
   };
+  // copies [i0, i1) of a stage (A copies first, then B)
+  auto dma_part = [&](bf16_t* as, bf16_t* bs, int k0, auto i0c, auto i1c) {
+    constexpr int I0 = decltype(i0c)::value, I1 = decltype(i1c)::value;
+#pragma unroll
+    for (int i = I0; i < I1; ++i) {
+      if (i < AGW) dma16(asrc[i] + k0, as + (w + 4 * i) * 8 * kBK);
+      else dma16(bsrc[i - AGW] + k0, bs + (w + 4 * (i - AGW)) * 8 * kBK);
+    }
+  };
 
   // The epilogue's rows (thread tid handles units tid + 256 i of each round;
   // a unit is 8 low channels of a head plus their partners in one row): read
@@ -307,11 +316,12 @@ gemm_qkv_bf16_kernel(GemmArgs a) {
         acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[slot][mi], bfr[slot][ni], acc[mi][ni], 0, 0, 0);
   };
 
-  // Ring of NST stage buffers; stage k lives in buffer k % NST and all NST
-  // are in flight.  During stage k, once every wave holds the fragments of
-  // its last k-step, the waves meet (which also means stage k+1 has landed),
-  // buffer k % NST is refilled with stage k+NST and the first fragments of
-  // stage k+1 are read; then the last MFMAs of stage k run.
+  // Ring of NST stage buffers; stage k lives in buffer k % NST.  Once every
+  // wave holds the fragments of stage k's last k-step, the waves meet (which
+  // also means stage k+1 has landed) and buffer k % NST is free; its refill
+  // with stage k+NST is issued during the first k-steps of stage k+1, a
+  // few copies between MFMA groups, so the copy instructions never pile up
+  // in the memory pipeline ahead of the MFMAs.
   const int nk = a.k_len / kBK;
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
@@ -330,12 +340,23 @@ gemm_qkv_bf16_kernel(GemmArgs a) {
     else dma_wait_barrier<0>();
   }
   load_frags(abuf(I0{}), bbuf(I0{}), 0, 0);
-  auto stage = [&](int k, auto cur, auto next) {
-#pragma unroll
-    for (int kk = 0; kk + 1 < KK; ++kk) {
+  constexpr int CPS = (PER + KK - 2) / (KK - 1);       // copies per k-step
+  auto stage = [&](int k, auto cur, auto next, auto prev) {
+    // buffer of stage k-1 gets stage k-1+NST
+    const bool refill = k >= 1 && k - 1 + NST < nk;
+    const int k0 = (k - 1 + NST) * kBK;
+    auto step = [&](auto kkc) {
+      constexpr int kk = decltype(kkc)::value;
       load_frags(abuf(cur), bbuf(cur), (kk + 1) & 1, kk + 1);
+      if (refill)
+        dma_part(abuf(prev), bbuf(prev), k0, std::integral_constant<int, kk * CPS>{},
+                 std::integral_constant<int, (kk + 1) * CPS < PER ? (kk + 1) * CPS : PER>{});
       mfmas(kk & 1);
-    }
+    };
+    step(I0{});
+    if constexpr (KK > 2) step(I1{});
+    if constexpr (KK > 3) step(I2{});
+    static_assert(KK == 4, "k-steps per stage");
     // issue order: reads of k-step kk+1, then the MFMAs of kk
 #pragma unroll
     for (int kk = 0; kk + 1 < KK; ++kk) {
@@ -348,7 +369,6 @@ gemm_qkv_bf16_kernel(GemmArgs a) {
       if (pend >= 2) lds_dma_wait_barrier<2 * PER>();
       else if (pend == 1) lds_dma_wait_barrier<PER>();
       else lds_dma_wait_barrier<0>();
-      if (k + NST < nk) dma_stage(abuf(cur), bbuf(cur), (k + NST) * kBK);
     }
     // after the last stage these reads are unused (their buffer is settled:
     // no copy is in flight); one unconditional path keeps the compiler's
@@ -360,17 +380,17 @@ gemm_qkv_bf16_kernel(GemmArgs a) {
   };
   for (int kt = 0; kt < nk; kt += NST) {
     if constexpr (NST == 4) {
-      stage(kt, I0{}, I1{});
-      if (kt + 1 < nk) stage(kt + 1, I1{}, I2{});
-      if (kt + 2 < nk) stage(kt + 2, I2{}, I3{});
-      if (kt + 3 < nk) stage(kt + 3, I3{}, I0{});
+      stage(kt, I0{}, I1{}, I3{});
+      if (kt + 1 < nk) stage(kt + 1, I1{}, I2{}, I0{});
+      if (kt + 2 < nk) stage(kt + 2, I2{}, I3{}, I1{});
+      if (kt + 3 < nk) stage(kt + 3, I3{}, I0{}, I2{});
     } else if constexpr (NST == 2) {
-      stage(kt, I0{}, I1{});
-      if (kt + 1 < nk) stage(kt + 1, I1{}, I0{});
+      stage(kt, I0{}, I1{}, I1{});
+      if (kt + 1 < nk) stage(kt + 1, I1{}, I0{}, I0{});
     } else {
-      stage(kt, I0{}, I1{});
-      if (kt + 1 < nk) stage(kt + 1, I1{}, I2{});
-      if (kt + 2 < nk) stage(kt + 2, I2{}, I0{});
+      stage(kt, I0{}, I1{}, I2{});
+      if (kt + 1 < nk) stage(kt + 1, I1{}, I2{}, I0{});
+      if (kt + 2 < nk) stage(kt + 2, I2{}, I0{}, I1{});
     }
   }
 

@@ -17,6 +17,7 @@ namespace kvf {
 
 constexpr int kTopkThreads = 1024;
 constexpr int kTopkWaves = kTopkThreads / kWave;
+constexpr int kTopkCache = 36864;   // keys cached in LDS (144 KB)
 
 struct TopkArgs {
   BatchArgs b;
@@ -65,9 +66,17 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(TopkArgs a, const fl
                                                             int32_t* __restrict__ out_idx,
                                                             int32_t* __restrict__ out_rows,
                                                             int32_t* __restrict__ out_pos) {
-  __shared__ uint32_t hist[256];
+  // kCopies interleaved copies of the 256-bin histogram: lane l adds into
+  // copy l % kCopies, and the stride kCopies + 1 puts the copies of one bin
+  // in distinct LDS banks, so a wave whose keys share a bin (scores of one
+  // request mostly share their top bits) costs a few conflict cycles instead
+  // of 64 serialised atomics on one word.
+  constexpr int kCopies = 8;
+  __shared__ uint32_t hist[256 * (kCopies + 1)];
   __shared__ uint32_t s_sel[2];
   __shared__ int s_wave[kTopkWaves + 1];
+  // the request's order keys, read from global memory once when they fit
+  __shared__ uint32_t s_keys[kTopkCache];
   const int r = blockIdx.x;
   const int N = a.b.n_ctx[r];
   const int k = a.k[r];
@@ -75,6 +84,12 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(TopkArgs a, const fl
   const int U = T - N;
   const float* sc = scores + a.b.cu_N[r];
   const int tid = threadIdx.x;
+  const bool cached = N <= kTopkCache;
+  if (cached && k > 0 && k < N)
+    for (int i = tid; i < N; i += kTopkThreads) s_keys[i] = order_key(sc[i]);
+  auto key_at = [&](int i) __attribute__((always_inline)) {
+    return cached ? s_keys[i] : order_key(sc[i]);
+  };
 
   uint32_t tau = 0u;        // keys > tau are taken; `need` keys == tau in index order
   int need = 0;
@@ -82,11 +97,20 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(TopkArgs a, const fl
     uint32_t prefix = 0u, mask = 0u;
     int krem = k;
     for (int shift = 24; shift >= 0; shift -= 8) {
-      for (int i = tid; i < 256; i += kTopkThreads) hist[i] = 0u;
+      for (int i = tid; i < 256 * (kCopies + 1); i += kTopkThreads) hist[i] = 0u;
       __syncthreads();
+      const uint32_t copy = tid % kCopies;
       for (int i = tid; i < N; i += kTopkThreads) {
-        const uint32_t key = order_key(sc[i]);
-        if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+        const uint32_t key = key_at(i);
+        if ((key & mask) == prefix) atomicAdd(&hist[((key >> shift) & 255u) * (kCopies + 1) + copy], 1u);
+      }
+      __syncthreads();
+      // fold the copies into copy 0 of each bin
+      for (int b = tid; b < 256; b += kTopkThreads) {
+        uint32_t t = 0u;
+#pragma unroll
+        for (int c = 0; c < kCopies; ++c) t += hist[b * (kCopies + 1) + c];
+        hist[b * (kCopies + 1)] = t;
       }
       __syncthreads();
       if (tid < kWave) {
@@ -96,7 +120,7 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(TopkArgs a, const fl
         uint32_t sum4 = 0u;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          c4[j] = hist[b0 - j];
+          c4[j] = hist[(b0 - j) * (kCopies + 1)];
           sum4 += c4[j];
         }
         uint32_t incl = sum4;
@@ -137,7 +161,7 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(TopkArgs a, const fl
     n_gt = s1 - s0;
   } else if (k > 0) {
     for (int i = s0; i < s1; ++i) {
-      const uint32_t key = order_key(sc[i]);
+      const uint32_t key = key_at(i);
       n_gt += key > tau;
       n_eq += key == tau;
     }
@@ -158,7 +182,7 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(TopkArgs a, const fl
       if (k == N) {
         sel = true;
       } else {
-        const uint32_t key = order_key(sc[i]);
+        const uint32_t key = key_at(i);
         sel = key > tau;
         if (key == tau) {
           sel = eq_seen < take;
