@@ -171,7 +171,11 @@ kvf_status kvf_rerotate(const kvf_layer_desc* layer, const kvf_chunk* chunks,
  *   keys 0..N+i; each (i, head) softmax is over that whole row, and
  *   score_t = sum over the last n_last_q query tokens (all when <= 0) and all
  *   query heads of the probability at context position t.  Softmax scale is
- *   1/sqrt(d).  Needs a workspace of kvf_score_workspace_size() bytes.
+ *   1/sqrt(d).  Needs a workspace of kvf_score_workspace_size() bytes; it
+ *   ends in arrival counters that must be zero before its first use
+ *   (zero-fill it once when allocating it); every completed call leaves them
+ *   zero.  Calls that share a workspace must not overlap.  The scores are
+ *   deterministic (fixed summation order).
  */
 kvf_status kvf_score(kvf_score_mode mode, const kvf_layer_desc* layer,
                      const kvf_batch* batch, const void* fused_k,

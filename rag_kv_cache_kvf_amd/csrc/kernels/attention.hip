@@ -713,7 +713,7 @@ hipError_t launch_attention(const kvf_layer_desc& L, const BatchArgs& B, const v
 // ---------------------------------------------------------------------------
 // attention mass
 // ---------------------------------------------------------------------------
-// Three launches (bf16):
+// Three launches for bf16:
 //  1. mass_stats_bf16_kernel: per (128-key chunk, kv head), the softmax
 //     statistics (max, sum) of every used query vector over the chunk's
 //     visible keys.  S^T = K Q^T with the chunk's keys held in registers as
@@ -722,8 +722,10 @@ hipError_t launch_attention(const kvf_layer_desc& L, const BatchArgs& B, const v
 //  2. lse_combine_kernel: chunk statistics -> log2-domain LSE per (row, head).
 //  3. mass_colsum_bf16_kernel: per (128-key tile, kv head), S = Q K^T again
 //     (query vectors on the MFMA rows, keys on the lanes), exp(s - lse)
-//     summed over the query vectors of the group.
-//  4. head_sum_kernel: the kv heads added in a fixed order (deterministic).
+//     summed over the query vectors of the group; the last kv head of a key
+//     tile to finish adds the heads in a fixed order (deterministic).
+// The "last to finish" hand-off counts arrivals in the workspace, which must
+// be zero before the first call; each call leaves the counters zero.
 // fp32: statistics by the fp32 attention kernel, column sums by one wave per
 // (key, kv head).
 
@@ -768,7 +770,35 @@ struct MassArgs {
   int64_t plane;                 // rows * Hq
   int hq, hkv, G;
   float scale_log2;
+  // Arrival counters (zero between calls): the last column-sum workgroup of
+  // a key tile adds the kv heads.
+  int* cnt_cols;                 // [total_ktiles]
+  float* scores;                 // [sum N]
 };
+
+// Relaxed device-scope atomics: coherent across the XCDs' L2 caches without
+// the whole-cache write-back/invalidate of a device-scope fence.  A
+// workgroup stores its partial results this way, the barrier waits for the
+// stores, then one arrival counter is bumped; the last arrival reads the
+// others' results the same way.
+__device__ __forceinline__ void put_dev(float* p, float x) {
+  __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float get_dev(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// all threads: returns true in the workgroup that arrived last of n
+__device__ __forceinline__ bool arrive_last(int* cnt, int n, int* s_flag) {
+  __syncthreads();                                // this workgroup's stores have completed
+  if (threadIdx.x == 0) {
+    const int old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = old == n - 1;
+    if (last) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // next call
+    *s_flag = last;
+  }
+  __syncthreads();
+  return *s_flag != 0;
+}
 
 constexpr int kMK = 128;         // keys per workgroup (4 waves x 32)
 constexpr int kMQS = 256;        // query vectors staged per round (LDS)
@@ -1000,8 +1030,24 @@ __global__ void __launch_bounds__(256) mass_colsum_bf16_kernel(MassArgs a) {
       }
   }
   colsum += __shfl_xor(colsum, 32, kWave);
-  if (hf == 0 && kvalid)
-    a.part[static_cast<int64_t>(g) * a.b.cu_N[a.b.n_req] + a.b.cu_N[r] + key] = colsum;
+  const int64_t n_all = a.b.cu_N[a.b.n_req];
+  if (hf == 0 && kvalid) put_dev(a.part + static_cast<int64_t>(g) * n_all + a.b.cu_N[r] + key, colsum);
+  // the last kv head of this key tile adds the heads in a fixed order
+  __shared__ int s_flag;
+  if (!arrive_last(a.cnt_cols + kt, a.hkv, &s_flag)) return;
+  if (tid < kMK && key0 + tid < N) {
+    const int64_t j = a.b.cu_N[r] + key0 + tid;
+    float sum = 0.f;
+    for (int g0 = 0; g0 < a.hkv; g0 += 8) {
+      float pv8[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) pv8[u] = get_dev(a.part + min(g0 + u, a.hkv - 1) * n_all + j);
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (g0 + u < a.hkv) sum += pv8[u];
+    }
+    a.scores[j] = sum;
+  }
 }
 
 // fp32: one wave per (context key, kv head)
@@ -1043,7 +1089,8 @@ struct MassLayout {
   int64_t rows;          // query rows used (sum over requests)
   int n_splits;
   int split_keys;
-  size_t off_pm, off_pl, off_lse, off_part, total;
+  size_t off_pm, off_pl, off_lse, off_part, off_cnt, total;
+  int64_t n_cnt;         // arrival counters: one per key tile
 };
 
 MassLayout mass_layout(const kvf_layer_desc& L, const BatchArgs& B, int n_last_q) {
@@ -1074,7 +1121,11 @@ MassLayout mass_layout(const kvf_layer_desc& L, const BatchArgs& B, int n_last_q
   m.off_pl = align(m.off_pm + sizeof(float) * plane * m.n_splits);
   m.off_lse = align(m.off_pl + sizeof(float) * plane * m.n_splits);
   m.off_part = align(m.off_lse + sizeof(float) * plane);
-  m.total = align(m.off_part + sizeof(float) * static_cast<size_t>(L.n_kv_heads) * B.cu_N[B.n_req]);
+  m.off_cnt = align(m.off_part + sizeof(float) * static_cast<size_t>(L.n_kv_heads) * B.cu_N[B.n_req]);
+  int64_t ktiles = 0;
+  for (int r = 0; r < B.n_req; ++r) ktiles += ceil_div(B.n_ctx[r], kMK);
+  m.n_cnt = ktiles;
+  m.total = align(m.off_cnt + sizeof(int) * m.n_cnt);
   return m;
 }
 }  // namespace
@@ -1093,6 +1144,7 @@ hipError_t launch_attn_mass(const kvf_layer_desc& L, const BatchArgs& B, const v
   float* pl = reinterpret_cast<float*>(base + lay.off_pl);
   float* lse2 = reinterpret_cast<float*>(base + lay.off_lse);
   float* part = reinterpret_cast<float*>(base + lay.off_part);
+  int* cnt = reinterpret_cast<int*>(base + lay.off_cnt);
   const int G = L.n_q_heads / L.n_kv_heads;
   const float scale_log2 = kLog2e / sqrtf(static_cast<float>(L.head_dim));
   const int64_t plane = lay.rows * L.n_q_heads;
@@ -1123,6 +1175,8 @@ hipError_t launch_attn_mass(const kvf_layer_desc& L, const BatchArgs& B, const v
   m.hkv = L.n_kv_heads;
   m.G = G;
   m.scale_log2 = scale_log2;
+  m.cnt_cols = cnt;
+  m.scores = scores;
   const int n = B.cu_N[B.n_req];
   if (plane == 0) {
     // no query rows: every key gets zero mass
@@ -1187,8 +1241,10 @@ hipError_t launch_attn_mass(const kvf_layer_desc& L, const BatchArgs& B, const v
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(head_sum_kernel, dim3(ceil_div(n, 256)), dim3(256), 0, st, part, L.n_kv_heads,
-                     n, scores);
+  // (bf16: the column-sum pass added the heads)
+  if (L.dtype != KVF_BF16)
+    hipLaunchKernelGGL(head_sum_kernel, dim3(ceil_div(n, 256)), dim3(256), 0, st, part, L.n_kv_heads,
+                       n, scores);
   return hipGetLastError();
 }
 

@@ -193,6 +193,8 @@ MASS_CASES = [
     ("bf16", 16, 2, 128, [0, 3136, 6272], [3072, 3072], 0),
     ("bf16", 4, 2, 64, [0, 233], [188], 0),
     ("bf16", 32, 8, 128, [0, 5184], [5120], 0),
+    # long context with many query vectors (71 key chunks, 2048 vectors)
+    ("bf16", 16, 2, 128, [0, 9000], [8744], 0),
     ("f32", 4, 2, 64, [0, 150, 290], [127, 100], 0),
 ]
 
@@ -210,10 +212,16 @@ def test_attention_mass(kvf, case):
     L = _layer(kvf, 256, hq, hkv, d, dtype)
     kb = _kbatch(kvf, cu_T, n_ctx)
     ws_n = kvf.score_workspace_size(kvf.KVF_SCORE_ATTN_MASS, L, kb, nlq)
-    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device="cuda")
-    sc = torch.zeros(sum(n_ctx), dtype=torch.float32, device="cuda")
-    kvf.score(kvf.KVF_SCORE_ATTN_MASS, L, kb, to_gpu(k_s, dtype), None, to_gpu(q_s, dtype), sc, ws,
-              n_last_q=nlq)
+    ws = torch.zeros(max(ws_n, 1), dtype=torch.uint8, device="cuda")   # counters start at zero
+    # two calls on one workspace: the arrival counters the first call leaves
+    # behind must be zero again, and the result is deterministic
+    runs = []
+    for _ in range(2):
+        sc = torch.zeros(sum(n_ctx), dtype=torch.float32, device="cuda")
+        kvf.score(kvf.KVF_SCORE_ATTN_MASS, L, kb, to_gpu(k_s, dtype), None, to_gpu(q_s, dtype), sc,
+                  ws, n_last_q=nlq)
+        runs.append(from_gpu(sc))
+    assert np.array_equal(runs[0], runs[1]), "attention mass differs between two calls"
     dk, dq = decode(k_s, dtype), decode(q_s, dtype)
     lo = fusion.Layer(256, hq, hkv, d, 1e4)
     ref, uoff = [], 0
@@ -223,7 +231,7 @@ def test_attention_mass(kvf, case):
                                          n_last_q=nlq))
         uoff += U
     ref = np.concatenate(ref)
-    assert_close(from_gpu(sc), ref, dtype, f"attention mass {case[:4]}")
+    assert_close(runs[1], ref, dtype, f"attention mass {case[:4]}")
 
 
 # ----------------------------------------------------------------------------
