@@ -47,7 +47,7 @@ struct AttnArgs {
   int cu_tiles[KVF_MAX_REQ + 1]; // row-tile prefix
   int total_tiles;
   int fold_from;                 // dispatch slots at or past this run smallest-first
-  int parts;                     // 2: long row tiles split their keys over two workgroups
+  int parts;                     // > 1: long row tiles split their keys over up to this many workgroups
   int split_min;                 // key tiles from which a row tile is split
   float* ws_part;                // [tiles * Hkv, 2 parts, partial values, threads]
   int* ws_cnt;                   // [tiles * Hkv] arrivals; zero between calls
@@ -154,10 +154,10 @@ attn_bf16_kernel(AttnArgs a) {
   // Dispatch runs largest-first; when the whole grid is resident at once
   // (two workgroups per CU), the second round of slots runs smallest-first
   // so each CU pairs a long tile with a short one.
-  // With key splitting, the two parts of a row tile are adjacent slots.
+  // With key splitting, the parts of a row tile are adjacent slots.
   const int slot = static_cast<int>(blockIdx.x / hkv);
-  const int rank0 = a.parts == 2 ? slot >> 1 : slot;
-  const int part = a.parts == 2 ? slot & 1 : 0;
+  const int rank0 = slot / a.parts;
+  const int part = slot - rank0 * a.parts;
   const int rank = rank0 < a.fold_from ? rank0 : a.total_tiles - 1 - (rank0 - a.fold_from);
   const int tile = a.total_tiles - 1 - rank;
   const int r = find_segment(a.cu_tiles, a.b.n_req, tile);
@@ -207,12 +207,14 @@ attn_bf16_kernel(AttnArgs a) {
   const int n = klim > 0 ? ceil_div(klim, kAT) : 0;
   // leading tiles that every row sees completely need no mask
   const int n_plain = klim > 0 ? min(n, (pmin + 1) / kAT) : 0;
-  // A long row tile is split: part 0 takes key tiles [0, n/2), part 1 the
-  // rest; whichever finishes second merges the two (m, l, O) and writes.
-  const bool split = a.parts == 2 && n >= a.split_min;
-  if (part == 1 && !split) return;                // whole workgroup: s_pos is uniform
-  const int t0 = part == 1 ? n / 2 : 0;
-  const int t1 = split && part == 0 ? n / 2 : n;
+  // A long row tile is split into np parts of at least split_min key tiles
+  // (at most a.parts); part p takes key tiles [p n / np, (p + 1) n / np) and
+  // whichever part finishes last merges every part's (m, l, O) and writes.
+  const int np = a.parts > 1 ? max(1, min(a.parts, n / a.split_min)) : 1;
+  if (part >= np) return;                         // whole workgroup: s_pos is uniform
+  const bool split = np > 1;
+  const int t0 = part * n / np;
+  const int t1 = (part + 1) * n / np;
 
   const bf16_t* Q = static_cast<const bf16_t*>(a.q);
   bf16x8_t qf[kQB][KS];
@@ -471,7 +473,7 @@ attn_bf16_kernel(AttnArgs a) {
     // the other workgroups on this XCD are streaming.
     constexpr int NV = kQB * (DB * 16 + 2);
     const int64_t item = static_cast<int64_t>(tile) * hkv + g;
-    float* mine = a.ws_part + ((item * 2 + part) * NV) * kAThreads + tid;
+    float* mine = a.ws_part + ((item * a.parts + part) * NV) * kAThreads + tid;
     auto put = [&](int e, float x) __attribute__((always_inline)) {
       __hip_atomic_store(mine + e * kAThreads, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     };
@@ -489,28 +491,31 @@ attn_bf16_kernel(AttnArgs a) {
     if (tid == 0)
       s_pos[0] = __hip_atomic_fetch_add(&a.ws_cnt[item], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
-    if (s_pos[0] == 0) return;                    // first to finish: the other part merges
-    const float* other = a.ws_part + ((item * 2 + (part ^ 1)) * NV) * kAThreads + tid;
-    auto get = [&](int e) __attribute__((always_inline)) {
-      return __hip_atomic_load(other + e * kAThreads, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    };
-    e = 0;
+    if (s_pos[0] != np - 1) return;               // not the last to finish: it merges
+    for (int op = 0; op < np; ++op) {
+      if (op == part) continue;
+      const float* other = a.ws_part + ((item * a.parts + op) * NV) * kAThreads + tid;
+      auto get = [&](int e) __attribute__((always_inline)) {
+        return __hip_atomic_load(other + e * kAThreads, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      };
+      e = 0;
 #pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) {
-      const float m2 = get(e + DB * 16);
-      const float l2 = get(e + DB * 16 + 1);
-      const float mm = fmaxf(m_run[qb], m2);
-      const float mu = mm == -INFINITY ? 0.f : mm;
-      const float a1 = __builtin_amdgcn_exp2f(m_run[qb] - mu), a2 = __builtin_amdgcn_exp2f(m2 - mu);
+      for (int qb = 0; qb < kQB; ++qb) {
+        const float m2 = get(e + DB * 16);
+        const float l2 = get(e + DB * 16 + 1);
+        const float mm = fmaxf(m_run[qb], m2);
+        const float mu = mm == -INFINITY ? 0.f : mm;
+        const float a1 = __builtin_amdgcn_exp2f(m_run[qb] - mu), a2 = __builtin_amdgcn_exp2f(m2 - mu);
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) o[qb][db][i] = o[qb][db][i] * a1 + get(e++) * a2;
-      e += 2;
-      l_lane[qb] = l_lane[qb] * a1 + l2 * a2;
-      m_run[qb] = mm;
+          for (int i = 0; i < 16; ++i) o[qb][db][i] = o[qb][db][i] * a1 + get(e++) * a2;
+        e += 2;
+        l_lane[qb] = l_lane[qb] * a1 + l2 * a2;
+        m_run[qb] = mm;
+      }
     }
-    // both parts have arrived: leave the counter zero for the next call
+    // every part has arrived: leave the counter zero for the next call
     if (tid == 0) __hip_atomic_store(&a.ws_cnt[item], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
@@ -628,10 +633,11 @@ static int rows_per_tile(int G) { return G >= kAQ ? 1 : kAQ / G; }
 
 // Key splitting: only grids that one dispatch round holds (two workgroups
 // per CU) have too few workgroups to even out tiles of unequal length, so
-// only they get the workspace; row tiles of at least kSplitMinTiles key
-// tiles are split.
+// only they get the workspace; a row tile is cut into parts of at least
+// kSplitMinTiles key tiles, at most kSplitParts of them.
 constexpr int kSplitMaxItems = 2 * kCUs;
-constexpr int kSplitMinTiles = 24;
+constexpr int kSplitMinTiles = 12;
+constexpr int kSplitParts = 2;
 
 struct AttnSplitLayout {
   int64_t items = 0;             // row tiles x kv heads
@@ -649,7 +655,7 @@ static AttnSplitLayout attn_split_layout(const kvf_layer_desc& L, const BatchArg
   if (items == 0 || items > kSplitMaxItems) return s;
   const int64_t nv = kQB * (L.head_dim / 32 * 16 + 2);
   s.items = items;
-  s.off_cnt = static_cast<size_t>(items * 2 * nv * kAThreads) * sizeof(float);
+  s.off_cnt = static_cast<size_t>(items * kSplitParts * nv * kAThreads) * sizeof(float);
   s.bytes = s.off_cnt + static_cast<size_t>(items) * sizeof(int);
   return s;
 }
@@ -688,7 +694,7 @@ hipError_t launch_attention(const kvf_layer_desc& L, const BatchArgs& B, const v
     if (tiles == 0) return hipSuccess;
     const AttnSplitLayout sl = attn_split_layout(L, B, cu_q);
     if (sl.bytes > 0 && ws != nullptr && ws_bytes >= sl.bytes) {
-      a.parts = 2;
+      a.parts = kSplitParts;
       a.split_min = kSplitMinTiles;
       a.ws_part = static_cast<float*>(ws);
       a.ws_cnt = reinterpret_cast<int*>(static_cast<char*>(ws) + sl.off_cnt);
