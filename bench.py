@@ -50,6 +50,7 @@ CALL_KERNEL = {
     "k_probe": ("gemm_qkv_bf16_kernel", "kernels/gemm_qkv.hip"),
     "u_probe": ("gemm_qkv_bf16_kernel", "kernels/gemm_qkv.hip"),
     "score": ("mass_colsum_bf16_kernel", "kernels/attention.hip"),
+    "static_mask": ("static_mask_kernel", "kernels/static_mask.hip"),
     "select": ("topk_kernel", "kernels/topk.hip"),
     "recompute": ("gemm_qkv_bf16_kernel", "kernels/gemm_qkv.hip"),
     "scatter": ("scatter_kernel", "kernels/scatter_deviation.hip"),
@@ -93,7 +94,12 @@ def call_work(g):
                             + n_chunks * 8 * hkv * d)
     else:
         work["rerotate"] = ("hbm", n_ctx * 4 * krow)      # read pool K,V; write fused K,V
-    if g.mode == "deviation":
+    if g.selector == "static":
+        work["recompute"] = ("mfma", 2.0 * hid * d * (hq + 2 * hkv) * M)
+    elif g.selector == "anchor":
+        work["score"] = ("hbm", n_ctx * (krow + 4))       # fused K -> one fp32 norm
+        work["recompute"] = ("mfma", 2.0 * hid * d * (hq + 2 * hkv) * M)
+    elif g.mode == "deviation":
         work["k_probe"] = ("mfma", 2.0 * hid * hkv * d * total)
         work["score"] = ("hbm", n_ctx * (2 * krow + 4))   # fused K, probe K -> one fp32
         work["recompute"] = ("mfma", 2.0 * hid * d * (hq + hkv) * M)
@@ -107,8 +113,14 @@ def call_work(g):
             flops += 2.0 * d * hq * keys + 2.0 * d * hq * U * N   # then Q K^T over the context
         work["score"] = ("mfma", flops)
         work["recompute"] = ("mfma", 2.0 * hid * d * (hq + 2 * hkv) * M)
-    work["select"] = ("hbm", n_ctx * 4 + M * 8)       # scores in; row ids + positions out
-    if g.mode == "deviation":
+    # scores in (none for static selection), forced mask in; picks, row ids
+    # and positions out
+    k_sum = int(sum(g.k_per_req))
+    work["select"] = ("hbm", (0 if g.selector == "static" else n_ctx * 4)
+                      + (n_ctx if g.static_mask is not None else 0) + k_sum * 4 + M * 8)
+    if g.static_mask is not None:
+        work["static_mask"] = ("hbm", n_ctx + b.chunk_table.shape[0] * 32)   # mask out, table in
+    if g.probe:
         work["scatter"] = ("hbm", M * 2 * krow)       # probe K in; fused K rows out
     work["attention"] = ("mfma", 4.0 * d * hq * float((pos + 1).sum()))   # QK^T + PV, causal
     return work
@@ -181,11 +193,33 @@ def _traffic(kernel, src, workload):
     return float(m_b.group(1))
 
 
+def _oracle_selection(batch, lo, pk, pv, fusion, selectors):
+    """The oracle's selection for the static and anchor selectors."""
+    import numpy as np
+    wl = batch.wl
+    sels = []
+    if wl.selector == "static":
+        for r in range(batch.n_req):
+            spans = batch.chunk_spans(r)
+            m = selectors.static_mask(int(batch.n_ctx[r]), [p for p, _ in spans], *wl.static_rules)
+            sels.append(np.flatnonzero(m).astype(np.int32))
+        return sels
+    fk, _ = fusion.rerotate_stitch(pk, pv, batch.chunk_table, batch.total_rows, lo)
+    for r in range(batch.n_req):
+        spans = batch.chunk_spans(r)
+        a = int(batch.cu_T[r])
+        s = selectors.key_norm(fk[a:a + int(batch.n_ctx[r])])
+        sels.append(selectors.select_topk_segmented(
+            s, [p for p, _ in spans], [n for _, n in spans],
+            [selectors.anchor_budget(n, wl.anchor_pct, 100) for _, n in spans]))
+    return sels
+
+
 def cpu_baseline(batch, ratio, min_seconds=10.0):
     """The float64 oracle on the same batch (one full pass of every stage of
     the layer), repeated until at least `min_seconds` of host time."""
     import numpy as np
-    from oracle import fusion, storage
+    from oracle import fusion, selectors, storage
     wl = batch.wl
     lo = fusion.Layer(wl.hidden, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.rope_base)
     x = storage.decode(batch.x, wl.dtype)
@@ -200,8 +234,13 @@ def cpu_baseline(batch, ratio, min_seconds=10.0):
         threads = len(os.sched_getaffinity(0))
     runs, t0 = 0, time.perf_counter()
     while True:
-        fusion.fused_layer(x, w, pk, pv, batch.chunk_table, batch.cu_T, batch.n_ctx, lo, wl.score,
-                           ks)
+        if wl.selector == "score":
+            fusion.fused_layer(x, w, pk, pv, batch.chunk_table, batch.cu_T, batch.n_ctx, lo,
+                               wl.score, ks)
+        else:
+            sel = _oracle_selection(batch, lo, pk, pv, fusion, selectors)
+            fusion.fused_layer(x, w, pk, pv, batch.chunk_table, batch.cu_T, batch.n_ctx, lo,
+                               "none", [len(s) for s in sel], forced_sel=sel)
         runs += 1
         dt = time.perf_counter() - t0
         if dt >= min_seconds:
@@ -271,8 +310,12 @@ def main():
                        "tokens_per_s": round(n_ctx / (ms * 1e-3), 1)}
     dom = max(per_call, key=per_call.get)
     kname, ksrc = CALL_KERNEL[dom]
-    if dom == "score" and g.mode == "deviation":
+    if dom == "score" and g.selector == "anchor":
+        kname, ksrc = "key_norm_kernel", "kernels/scatter_deviation.hip"
+    elif dom == "score" and g.mode == "deviation":
         kname, ksrc = "deviation_kernel", "kernels/scatter_deviation.hip"
+    if dom == "select" and g.selector == "anchor":
+        kname = "topk_segmented_kernel"
     kind, amount = work[dom]
     c = calls[dom]
     roofline = {"kernel": kname, "call": dom, "bound": kind, "achieved": c["achieved"],
@@ -295,7 +338,12 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "description": wl.description, "requests": batch.n_req,
                    "context_tokens": n_ctx, "query_tokens": batch.total_rows - n_ctx,
-                   "recompute_ratio_pct": ratio, "score": g.mode, "graph": bool(args.graph)},
+                   "recompute_ratio_pct": ratio if wl.selector == "score" else None,
+                   "selector": wl.selector,
+                   "score": g.mode if wl.selector == "score" else
+                   ("key_norm" if wl.selector == "anchor" else None),
+                   "recomputed_context_tokens": int(sum(g.k_per_req)),
+                   "graph": bool(args.graph)},
         "roofline": roofline,
         "calls": calls,
         "ms_per_step_with_call_events": round(wall_events * 1e3, 5),

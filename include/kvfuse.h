@@ -6,12 +6,14 @@
  *   [QCF] "QCFuse: Query-Aware Cache Fusion via Compressed View for Efficient
  *         RAG Serving": 2.1.1 (Eq. 1, context C and query U), 2.1.2 (Eq. 3-5,
  *         per-chunk caches and their re-positioning), 2.1.3 (Eq. 6-7,
- *         selective recomputation and the fused cache), 3.2.1 (Eq. 9-11,
- *         query-to-context attention mass and TopK).
+ *         selective recomputation and the fused cache), 2.2.1 (EPIC's
+ *         boundary tokens), 3.2.1 (Eq. 9-11, query-to-context attention mass
+ *         and TopK), 3.3.1 (Eq. 14, per-chunk anchors, Knorm ranking).
  *   [KVB] "KVBoost: Chunk-Level Key-Value Cache Reuse with Deviation-Guided
  *         Recomputation for Efficient Large Language Model Inference":
  *         3.1 (Eq. 1-2, projections, attention, cache layout), 3.2 (Eq. 3,
- *         RoPE and the rotation correction), 4.5 (Eq. 7, KIVI int8/int4),
+ *         RoPE and the rotation correction), 4.1 (attention-sink tokens),
+ *         4.5 (Eq. 7, KIVI int8/int4), 4.6.1 (Algorithm 1, seam windows),
  *         4.6.2 (Algorithm 2, key-deviation scoring).
  *
  * One layer, per request:  N context tokens (stitched chunks) then U query
@@ -19,7 +21,11 @@
  *   kvf_rerotate -> kvf_score -> kvf_select_topk -> kvf_recompute_qkv
  *   -> kvf_scatter_kv -> kvf_sparse_q_attention
  * every call enqueues HIP kernels on the caller's stream and returns; there
- * is no host synchronisation inside the library.
+ * is no host synchronisation inside the library.  Other selectors feed the
+ * same recompute path: kvf_select_static builds a mask of static positions
+ * (attention sinks, chunk boundary tokens, seam windows) that kvf_select_topk
+ * takes as a forced set, and kvf_select_topk_segmented selects per chunk
+ * (e.g. over kvf_score's KVF_SCORE_KEY_NORM scores).
  *
  * Conventions for every call:
  *  - Pointers are DEVICE pointers unless the comment says "host".
@@ -58,7 +64,7 @@
 extern "C" {
 #endif
 
-#define KVF_ABI_VERSION 4
+#define KVF_ABI_VERSION 5
 #define KVF_MAX_REQ 64      /* requests per call (batch metadata is passed by value) */
 
 typedef enum {
@@ -73,7 +79,8 @@ typedef enum { KVF_F32 = 0, KVF_BF16 = 1 } kvf_dtype;
 
 typedef enum {
   KVF_SCORE_DEVIATION = 0,   /* [KVB] 4.6.2 Algorithm 2: 1 - mean_h cos(K, K~) */
-  KVF_SCORE_ATTN_MASS = 1    /* [QCF] 3.2.1 Eq. 9-10: query-to-context mass  */
+  KVF_SCORE_ATTN_MASS = 1,   /* [QCF] 3.2.1 Eq. 9-10: query-to-context mass  */
+  KVF_SCORE_KEY_NORM = 2     /* [QCF] 3.3.1 Knorm: L2 norm of the cached key  */
 } kvf_score_mode;
 
 enum { KVF_OUT_Q = 1, KVF_OUT_K = 2, KVF_OUT_V = 4 };
@@ -123,6 +130,33 @@ typedef struct {
   const float* v_scale;      /* [pool_rows, Hkv] */
   int32_t n_pool_chunks;
 } kvf_kivi8;
+
+/* Static recompute rules (host struct); every field >= 0, 0 turns a rule off.
+ *   sink:     request positions 0 .. sink-1 ([KVB] 4.1, attention-sink
+ *             tokens always kept live);
+ *   boundary: the first `boundary` positions of every stitched chunk
+ *             ([QCF] 2.2.1, EPIC's boundary tokens);
+ *   seam:     R of [KVB] 4.6.1 Algorithm 1: positions max(0, p - R) .. p - 1
+ *             before every chunk start p > 0.
+ * Every range is clipped to the request's context [0, N). */
+typedef struct {
+  int32_t sink;
+  int32_t boundary;
+  int32_t seam;
+} kvf_static_rules;
+
+/* One selection segment of kvf_select_topk_segmented (device array element,
+ * 32 bytes): scores req's context positions pos0 .. pos0+len-1 and keeps k of
+ * them; its picks land at slots out_off .. out_off+k-1 of the request's k_r
+ * picks ([QCF] 3.3.1 Eq. 14: A_i = TopK(G_i, ceil(r_a |c_i|)) per chunk). */
+typedef struct {
+  int32_t req;
+  int32_t pos0;
+  int32_t len;
+  int32_t k;
+  int32_t out_off;
+  int32_t reserved[3];
+} kvf_segment;
 
 /* ---------------------------------------------------------------------------
  * kvf_rope_table - cos/sin of the rotation angles p * theta_j for positions
@@ -176,6 +210,11 @@ kvf_status kvf_rerotate(const kvf_layer_desc* layer, const kvf_chunk* chunks,
  *   (zero-fill it once when allocating it); every completed call leaves them
  *   zero.  Calls that share a workspace must not overlap.  The scores are
  *   deterministic (fixed summation order).
+ * KVF_SCORE_KEY_NORM ([QCF] 3.3.1, the Knorm ranking rule):
+ *   score_t = sqrt(sum over heads h and channels j of fused_k[t, h, j]^2),
+ *   fp32 accumulation.  The norm is rotation invariant, so the re-positioned
+ *   fused cache gives the per-chunk cache's score.  k_fresh and q_u unused.
+ *   Rank the negated scores for "smallest norm first".
  */
 kvf_status kvf_score(kvf_score_mode mode, const kvf_layer_desc* layer,
                      const kvf_batch* batch, const void* fused_k,
@@ -189,6 +228,11 @@ size_t kvf_score_workspace_size(kvf_score_mode mode, const kvf_layer_desc* layer
  * kvf_select_topk - S3: P_r = TopK(score, k_r) per request ([QCF] 3.2.1
  * Eq. 11).  Order: larger score first; ties to the lower position; -0 == +0;
  * NaN ranks below every number.  k_per_req: HOST [n_req], 0 <= k_r <= N_r.
+ * scores: [sum N] request-major, or NULL to rank every position equal.
+ * forced: [sum N] uint8 (may be NULL): positions with a nonzero byte rank
+ *   above every score, so with f_r forced positions P_r holds all of them
+ *   when f_r <= k_r (the rest by score) and the f_r lowest otherwise.  With
+ *   scores NULL and k_r = f_r, P_r is exactly the forced set.
  *   out_idx  [sum k_r]: P_r ascending, positions within the request.
  *   out_rows [sum (k_r + U_r)] (may be NULL): flat rows (cu_T[r] + p) of
  *            P_r followed by the request's query rows, i.e. the rows to
@@ -197,11 +241,52 @@ size_t kvf_score_workspace_size(kvf_score_mode mode, const kvf_layer_desc* layer
  * Needs kvf_select_workspace_size() bytes of workspace (0 today; the
  * argument is reserved).
  */
-kvf_status kvf_select_topk(const float* scores, const kvf_batch* batch,
+kvf_status kvf_select_topk(const float* scores, const uint8_t* forced,
+                           const kvf_batch* batch,
                            const int32_t* k_per_req, int32_t* out_idx,
                            int32_t* out_rows, int32_t* out_pos,
                            void* workspace, size_t ws_bytes, void* stream);
 size_t kvf_select_workspace_size(const kvf_batch* batch);
+
+/* ---------------------------------------------------------------------------
+ * kvf_select_topk_segmented - per-segment TopK ([QCF] 3.3.1 Eq. 14): every
+ * segment g keeps the g.k best of its positions by kvf_select_topk's order
+ * (and forced rule), written ascending as request positions at
+ * out_idx[sum_{r' < g.req} k_r' + g.out_off ..].  k_per_req: HOST [n_req],
+ * the number of picks of each request (the sum of its segments' k).
+ * out_rows / out_pos (both or neither): as in kvf_select_topk, the picks'
+ * flat rows and positions at the same slots of each request's k_r + U_r
+ * list, then the U_r query rows.  A request's picks come out ascending when
+ * its segments are ascending, disjoint and take consecutive output slots in
+ * that order.  segs: device [n_segs].  A segment whose request, range
+ * (pos0 + len <= N_req), k (<= len) or slots (out_off + k <= k_req) is out
+ * of bounds writes nothing.
+ */
+kvf_status kvf_select_topk_segmented(const float* scores, const uint8_t* forced,
+                                     const kvf_batch* batch, const kvf_segment* segs,
+                                     int32_t n_segs, const int32_t* k_per_req,
+                                     int32_t* out_idx, int32_t* out_rows,
+                                     int32_t* out_pos, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * kvf_select_static - mask[cu_N[r] + t] = 1 if a static rule picks context
+ * position t of request r, else 0 (kvf_static_rules; [KVB] 4.1, 4.6.1
+ * Algorithm 1; [QCF] 2.2.1).  mask: device [sum N] uint8, every byte
+ * written.  The chunk starts are read from the chunk table kvf_rerotate
+ * takes (device [n_chunks]): chunk c starts at context position
+ * dst_row - cu_T[r] of the request r whose context rows hold dst_row;
+ * chunks whose dst_row lies in no request's context are ignored.
+ */
+kvf_status kvf_select_static(const kvf_batch* batch, const kvf_chunk* chunks,
+                             int32_t n_chunks, const kvf_static_rules* rules,
+                             uint8_t* mask, void* stream);
+
+/* Host-side count of the positions kvf_select_static marks per request, from
+ * a HOST copy of the same chunk table: counts HOST [n_req].  Sizes the
+ * kvf_select_topk call that turns the mask into a position list. */
+kvf_status kvf_static_counts(const kvf_batch* batch, const kvf_chunk* chunks_host,
+                             int32_t n_chunks, const kvf_static_rules* rules,
+                             int32_t* counts);
 
 /* ---------------------------------------------------------------------------
  * kvf_recompute_qkv - S4: fresh Q/K/V of M rows ([QCF] 2.1.3 KV^New;
@@ -274,8 +359,9 @@ kvf_status kvf_sparse_q_attention(const kvf_layer_desc* layer,
 /* Workspace bytes kvf_sparse_q_attention can use for the same layer, batch
  * and cu_q (HOST).  0 when the call would not use one (fp32, or a grid large
  * enough to balance by itself).  With a workspace, the row tiles of long
- * rows split their keys over two workgroups and merge (same result up to
- * fp32 rounding order); with workspace NULL the call runs unsplit.  The
+ * rows split their keys over several workgroups (2 to 8, more when the grid
+ * has fewer row tiles) and merge (same result up to fp32 rounding order);
+ * with workspace NULL the call runs unsplit.  The
  * workspace ends in per-tile arrival counters that must be zero before its
  * first use (zero-fill it once when allocating it); every completed call
  * leaves them zero again.  Calls that share a workspace must not overlap.
@@ -305,6 +391,11 @@ kvf_status kvf_kivi8_encode(const kvf_layer_desc* layer, const void* pool_k,
  * |P| = floor(rho N) of [QCF] 3.2.1 Eq. 11.  Returns -1 for negative input
  * or ratio_pct > 100. */
 int32_t kvf_recompute_budget(int32_t n_ctx, int32_t ratio_pct);
+
+/* ceil(len * ra_num / ra_den) in integer arithmetic: the anchor budget
+ * ceil(r_a |c_i|) of [QCF] 3.3.1 Eq. 14 with r_a = ra_num / ra_den.  Returns
+ * -1 for len < 0, ra_den <= 0, ra_num < 0 or ra_num > ra_den. */
+int32_t kvf_anchor_budget(int32_t len, int32_t ra_num, int32_t ra_den);
 
 const char* kvf_status_string(kvf_status status);
 const char* kvf_last_error(void);

@@ -266,6 +266,11 @@ def fused_layer(x: np.ndarray, w_qkv: np.ndarray, pool_k: np.ndarray, pool_v: np
     attention mass, select, recompute Q/K/V of the selected and query rows,
     fuse, attend.
 
+    mode "none": no scoring; the selection is `forced_sel` (a selector that
+    needs no query-time score, e.g. static positions or per-chunk anchors),
+    and Q/K/V of the selected and query rows are recomputed as in
+    "attn_mass".
+
     `forced_sel` replaces the selection with given per-request positions
     (used to evaluate the rest of the layer on another selection).
 
@@ -296,14 +301,18 @@ def fused_layer(x: np.ndarray, w_qkv: np.ndarray, pool_k: np.ndarray, pool_v: np
         allpos = np.concatenate([np.arange(cu_T[r + 1] - cu_T[r]) for r in range(n_req)])
         k_probe = S(recompute(x, allpos, w_qkv, layer, want=("k",))["k"])
         res["k_probe"] = k_probe
-    elif mode != "attn_mass":
+    elif mode not in ("attn_mass", "none"):
         raise ValueError(mode)
+    if mode == "none" and forced_sel is None:
+        raise ValueError("mode 'none' takes its selection from forced_sel")
 
     q_u_all = []
     for r in range(n_req):
         a, b, N = cu_T[r], cu_T[r + 1], int(n_ctx[r])
         if mode == "deviation":
             s = deviation(fk[a:a + N], k_probe[a:a + N])
+        elif mode == "none":
+            s = None
         else:
             qr = np.arange(a + N, b)
             qpos = np.arange(N, b - a)

@@ -48,7 +48,8 @@ def key_norm(keys: np.ndarray) -> np.ndarray:
     Pin: explicit loops on tiny inputs, invariance under any RoPE rotation of
     the keys, zero keys give zero."""
     k = np.asarray(keys, dtype=np.float64)
-    return np.sqrt(np.sum(k.reshape(k.shape[0], -1) ** 2, axis=1))
+    flat = k.reshape(k.shape[0], int(np.prod(k.shape[1:], dtype=np.int64)))
+    return np.sqrt(np.sum(flat * flat, axis=1))
 
 
 def anchor_budget(chunk_len: int, ra_num: int, ra_den: int) -> int:

@@ -633,14 +633,19 @@ static int rows_per_tile(int G) { return G >= kAQ ? 1 : kAQ / G; }
 
 // Key splitting: only grids that one dispatch round holds (two workgroups
 // per CU) have too few workgroups to even out tiles of unequal length, so
-// only they get the workspace; a row tile is cut into parts of at least
-// kSplitMinTiles key tiles, at most kSplitParts of them.
+// only they get the workspace.  The part count fills one dispatch round: two
+// parts when the row tiles nearly fill it, up to kSplitMaxParts for the few
+// row tiles of a small recompute set (a handful of seam windows, say).  A
+// row tile is cut into parts of at least kSplitMinTiles key tiles, or
+// kSplitMinTilesSmall when the grid is that small.
 constexpr int kSplitMaxItems = 2 * kCUs;
 constexpr int kSplitMinTiles = 12;
-constexpr int kSplitParts = 2;
+constexpr int kSplitMinTilesSmall = 6;
+constexpr int kSplitMaxParts = 8;
 
 struct AttnSplitLayout {
   int64_t items = 0;             // row tiles x kv heads
+  int parts = 1;
   size_t off_cnt = 0, bytes = 0;
 };
 
@@ -655,7 +660,9 @@ static AttnSplitLayout attn_split_layout(const kvf_layer_desc& L, const BatchArg
   if (items == 0 || items > kSplitMaxItems) return s;
   const int64_t nv = kQB * (L.head_dim / 32 * 16 + 2);
   s.items = items;
-  s.off_cnt = static_cast<size_t>(items * kSplitParts * nv * kAThreads) * sizeof(float);
+  s.parts = static_cast<int>(std::min<int64_t>(
+      kSplitMaxParts, std::max<int64_t>(2, (kSplitMaxItems + items - 1) / items)));
+  s.off_cnt = static_cast<size_t>(items * s.parts * nv * kAThreads) * sizeof(float);
   s.bytes = s.off_cnt + static_cast<size_t>(items) * sizeof(int);
   return s;
 }
@@ -694,8 +701,8 @@ hipError_t launch_attention(const kvf_layer_desc& L, const BatchArgs& B, const v
     if (tiles == 0) return hipSuccess;
     const AttnSplitLayout sl = attn_split_layout(L, B, cu_q);
     if (sl.bytes > 0 && ws != nullptr && ws_bytes >= sl.bytes) {
-      a.parts = kSplitParts;
-      a.split_min = kSplitMinTiles;
+      a.parts = sl.parts;
+      a.split_min = sl.parts > 2 ? kSplitMinTilesSmall : kSplitMinTiles;
       a.ws_part = static_cast<float*>(ws);
       a.ws_cnt = reinterpret_cast<int*>(static_cast<char*>(ws) + sl.off_cnt);
     }

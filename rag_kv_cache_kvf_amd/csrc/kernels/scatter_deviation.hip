@@ -1,4 +1,5 @@
-// S5 in-place K/V scatter into the fused cache and S2 key-deviation score.
+// S5 in-place K/V scatter into the fused cache, S2 key-deviation score and
+// the key-norm ranking score.
 //
 // Scatter: QCFuse page, section 2.1.3, Eq. 7 - the fused cache takes the
 // recomputed entry at every selected position and keeps the reused one
@@ -6,10 +7,13 @@
 // Deviation: KVBoost page, section 4.6.2, Algorithm 2 - delta_t = 1 minus the
 // mean over heads of cos(K_t, K~_t), here for one layer and the key heads.
 //
-// Both are HBM streams.  Scatter moves 16-byte vectors with a grid-stride
-// loop over (row, vector); deviation gives each context token one wave that
-// reads the two key rows with 16-byte loads and reduces per head with
-// cross-lane shuffles.
+// Key norm: QCFuse page, section 3.3.1 - the Knorm rule ranks a chunk's
+// positions by the norm of their cached keys (one norm over all kv heads).
+//
+// All three are HBM streams.  Scatter moves 16-byte vectors with a
+// grid-stride loop over (row, vector); deviation and key norm give each
+// context token one wave that reads the key rows with 16-byte loads and
+// reduces with cross-lane shuffles.
 #include "../kvf_common.h"
 
 namespace kvf {
@@ -135,6 +139,44 @@ hipError_t launch_deviation(const kvf_layer_desc& L, const BatchArgs& B, const v
     hipLaunchKernelGGL(deviation_kernel<float>, dim3(blocks), dim3(256), 0, st, B,
                        static_cast<const float*>(fk), static_cast<const float*>(kf),
                        L.n_kv_heads, L.head_dim, scores);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// key norm
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ void __launch_bounds__(256) key_norm_kernel(BatchArgs B, const T* __restrict__ fk,
+                                                       int row_elems, float* __restrict__ scores) {
+  const int wave = (blockIdx.x * blockDim.x + threadIdx.x) / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int total = B.cu_N[B.n_req];
+  if (wave >= total) return;
+  const int r = find_segment(B.cu_N, B.n_req, wave);
+  const int64_t row = B.cu_T[r] + (wave - B.cu_N[r]);
+  const T* a = fk + row * row_elems;
+  float ss = 0.f;
+  for (int e0 = lane * 8; e0 < row_elems; e0 += kWave * 8) {
+    float x[8];
+    Elem<T>::load8(a + e0, x);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ss = fmaf(x[i], x[i], ss);
+  }
+  ss = wave_sum(ss);
+  if (lane == 0) scores[wave] = sqrtf(ss);
+}
+
+hipError_t launch_key_norm(const kvf_layer_desc& L, const BatchArgs& B, const void* fk,
+                           float* scores, hipStream_t st) {
+  const int total = B.cu_N[B.n_req];
+  const int blocks = ceil_div(total, 256 / kWave);
+  const int row_elems = L.n_kv_heads * L.head_dim;
+  if (L.dtype == KVF_BF16)
+    hipLaunchKernelGGL(key_norm_kernel<bf16_t>, dim3(blocks), dim3(256), 0, st, B,
+                       static_cast<const bf16_t*>(fk), row_elems, scores);
+  else
+    hipLaunchKernelGGL(key_norm_kernel<float>, dim3(blocks), dim3(256), 0, st, B,
+                       static_cast<const float*>(fk), row_elems, scores);
   return hipGetLastError();
 }
 

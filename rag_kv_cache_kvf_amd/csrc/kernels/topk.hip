@@ -1,23 +1,33 @@
-// S3: per-request top-k selection of context positions.
+// S3: top-k selection of context positions, whole-request and per-segment.
 //
 // QCFuse page, section 3.2.1, Eq. 11: P = TopK(I(t), floor(rho N)).  The order
 // is larger score first, ties to the lower position (-0 == +0, NaN below
 // every number); P is written ascending, followed (optionally) by the
 // request's query rows so the caller gets the full recompute row list.
+// A forced mask (positions every selection keeps: attention-sink tokens,
+// KVBoost page, section 4.1; seam windows, section 4.6.1; EPIC's boundary
+// tokens, QCFuse page, section 2.2.1) ranks its positions above every score,
+// so they take the budget first, lowest positions first when they overflow it.
+// The segmented form runs one selection per segment - the per-chunk anchors
+// A_i = TopK(G_i, ceil(r_a |c_i|)) of QCFuse, section 3.3.1, Eq. 14 - so no
+// chunk can take another chunk's budget.
 //
-// One 1024-thread workgroup per request.  Scores map to order-preserving
-// uint32 keys; an MSB-first 8-bit radix select (four LDS histogram passes)
-// finds the k-th largest key tau and how many keys equal to tau are still
-// needed.  A block-wide scan over per-thread contiguous segments then keeps
-// every key above tau plus the first needed ties in index order and writes
-// them in ascending order - no sort, and the result is exact.
+// One workgroup per selection.  Scores map to order-preserving uint32 keys;
+// an MSB-first 8-bit radix select (four LDS histogram passes) finds the k-th
+// largest key tau and how many keys equal to tau are still needed.  A
+// block-wide scan over per-thread contiguous segments then keeps every key
+// above tau plus the first needed ties in index order and writes them in
+// ascending order - no sort, and the result is exact.
 #include "../kvf_common.h"
 
 namespace kvf {
 
 constexpr int kTopkThreads = 1024;
-constexpr int kTopkWaves = kTopkThreads / kWave;
-constexpr int kTopkCache = 36864;   // keys cached in LDS (144 KB)
+constexpr int kTopkCache = 36864;     // keys cached in LDS (144 KB)
+constexpr int kSegThreads = 256;
+constexpr int kSegCache = 8192;       // 32 KB: several segment workgroups per CU
+constexpr int kHistCopies = 8;
+constexpr uint32_t kForcedKey = 0xffffffffu;   // above the key of +inf (0xff800000)
 
 struct TopkArgs {
   BatchArgs b;
@@ -34,7 +44,9 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 }
 
 // exclusive block scan of one int per thread; also returns the block total
+template <int NT>
 __device__ __forceinline__ int block_exclusive_scan(int v, int* s_wave, int* total) {
+  constexpr int kWaves = NT / kWave;
   const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
   int incl = v;
 #pragma unroll
@@ -45,72 +57,84 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* s_wave, int* tot
   if (lane == kWave - 1) s_wave[w] = incl;
   __syncthreads();
   if (w == 0) {
-    int x = lane < kTopkWaves ? s_wave[lane] : 0;
+    int x = lane < kWaves ? s_wave[lane] : 0;
     int xi = x;
 #pragma unroll
     for (int o = 1; o < kWave; o <<= 1) {
       const int t = __shfl_up(xi, o, kWave);
       if (lane >= o) xi += t;
     }
-    if (lane < kTopkWaves) s_wave[lane] = xi - x;      // exclusive wave offsets
-    if (lane == kTopkWaves - 1) s_wave[kTopkWaves] = xi;
+    if (lane < kWaves) s_wave[lane] = xi - x;      // exclusive wave offsets
+    if (lane == kWaves - 1) s_wave[kWaves] = xi;
   }
   __syncthreads();
   const int res = s_wave[w] + incl - v;
-  *total = s_wave[kTopkWaves];
+  *total = s_wave[kWaves];
   __syncthreads();
   return res;
 }
 
-__global__ void __launch_bounds__(kTopkThreads) topk_kernel(TopkArgs a, const float* __restrict__ scores,
-                                                            int32_t* __restrict__ out_idx,
-                                                            int32_t* __restrict__ out_rows,
-                                                            int32_t* __restrict__ out_pos) {
-  // kCopies interleaved copies of the 256-bin histogram: lane l adds into
-  // copy l % kCopies, and the stride kCopies + 1 puts the copies of one bin
-  // in distinct LDS banks, so a wave whose keys share a bin (scores of one
-  // request mostly share their top bits) costs a few conflict cycles instead
-  // of 64 serialised atomics on one word.
-  constexpr int kCopies = 8;
-  __shared__ uint32_t hist[256 * (kCopies + 1)];
-  __shared__ uint32_t s_sel[2];
-  __shared__ int s_wave[kTopkWaves + 1];
-  // the request's order keys, read from global memory once when they fit
-  __shared__ uint32_t s_keys[kTopkCache];
-  const int r = blockIdx.x;
-  const int N = a.b.n_ctx[r];
-  const int k = a.k[r];
-  const int T = a.b.cu_T[r + 1] - a.b.cu_T[r];
-  const int U = T - N;
-  const float* sc = scores + a.b.cu_N[r];
+// LDS of one selecting workgroup.  kHistCopies interleaved copies of the
+// 256-bin histogram: lane l adds into copy l % kHistCopies, and the stride
+// kHistCopies + 1 puts the copies of one bin in distinct LDS banks, so a wave
+// whose keys share a bin (scores of one request mostly share their top bits)
+// costs a few conflict cycles instead of 64 serialised atomics on one word.
+template <int NT, int CACHE>
+struct SelectLds {
+  uint32_t hist[256 * (kHistCopies + 1)];
+  uint32_t sel[2];
+  int wave[NT / kWave + 1];
+  uint32_t keys[CACHE];     // the selection's keys, read from HBM once when they fit
+};
+
+// The k largest keys of positions [0, N) with ties to the lower position;
+// emit(o, i) is called for the o-th chosen position i, o ascending with i.
+// sc == nullptr ranks every unforced position equal (lowest positions win).
+template <int NT, int CACHE, typename Emit>
+__device__ __forceinline__ void select_block(const float* __restrict__ sc,
+                                             const uint8_t* __restrict__ forced, int N, int k,
+                                             SelectLds<NT, CACHE>& s, Emit emit) {
   const int tid = threadIdx.x;
-  const bool cached = N <= kTopkCache;
+  auto key_of = [&](int i) __attribute__((always_inline)) -> uint32_t {
+    if (forced && forced[i]) return kForcedKey;
+    return sc ? order_key(sc[i]) : 0u;
+  };
+  const bool cached = N <= CACHE;
   if (cached && k > 0 && k < N)
-    for (int i = tid; i < N; i += kTopkThreads) s_keys[i] = order_key(sc[i]);
+    for (int i = tid; i < N; i += NT) s.keys[i] = key_of(i);
   auto key_at = [&](int i) __attribute__((always_inline)) {
-    return cached ? s_keys[i] : order_key(sc[i]);
+    return cached ? s.keys[i] : key_of(i);
   };
 
   uint32_t tau = 0u;        // keys > tau are taken; `need` keys == tau in index order
   int need = 0;
-  if (k > 0 && k < N) {
+  if (k > 0 && k < N && !sc) {
+    // two key values only (forced, 0): one counting pass instead of the radix
+    int f = 0;
+    for (int i = tid; i < N; i += NT) f += key_at(i) == kForcedKey;
+    int n_forced;
+    block_exclusive_scan<NT>(f, s.wave, &n_forced);
+    tau = k <= n_forced ? kForcedKey : 0u;
+    need = k <= n_forced ? k : k - n_forced;
+  } else if (k > 0 && k < N) {
     uint32_t prefix = 0u, mask = 0u;
     int krem = k;
     for (int shift = 24; shift >= 0; shift -= 8) {
-      for (int i = tid; i < 256 * (kCopies + 1); i += kTopkThreads) hist[i] = 0u;
+      for (int i = tid; i < 256 * (kHistCopies + 1); i += NT) s.hist[i] = 0u;
       __syncthreads();
-      const uint32_t copy = tid % kCopies;
-      for (int i = tid; i < N; i += kTopkThreads) {
+      const uint32_t copy = tid % kHistCopies;
+      for (int i = tid; i < N; i += NT) {
         const uint32_t key = key_at(i);
-        if ((key & mask) == prefix) atomicAdd(&hist[((key >> shift) & 255u) * (kCopies + 1) + copy], 1u);
+        if ((key & mask) == prefix)
+          atomicAdd(&s.hist[((key >> shift) & 255u) * (kHistCopies + 1) + copy], 1u);
       }
       __syncthreads();
       // fold the copies into copy 0 of each bin
-      for (int b = tid; b < 256; b += kTopkThreads) {
+      for (int b = tid; b < 256; b += NT) {
         uint32_t t = 0u;
 #pragma unroll
-        for (int c = 0; c < kCopies; ++c) t += hist[b * (kCopies + 1) + c];
-        hist[b * (kCopies + 1)] = t;
+        for (int c = 0; c < kHistCopies; ++c) t += s.hist[b * (kHistCopies + 1) + c];
+        s.hist[b * (kHistCopies + 1)] = t;
       }
       __syncthreads();
       if (tid < kWave) {
@@ -120,7 +144,7 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(TopkArgs a, const fl
         uint32_t sum4 = 0u;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          c4[j] = hist[(b0 - j) * (kCopies + 1)];
+          c4[j] = s.hist[(b0 - j) * (kHistCopies + 1)];
           sum4 += c4[j];
         }
         uint32_t incl = sum4;
@@ -135,8 +159,8 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(TopkArgs a, const fl
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             if (c + c4[j] >= static_cast<uint32_t>(krem)) {
-              s_sel[0] = prefix | (static_cast<uint32_t>(b0 - j) << shift);
-              s_sel[1] = static_cast<uint32_t>(krem) - c;
+              s.sel[0] = prefix | (static_cast<uint32_t>(b0 - j) << shift);
+              s.sel[1] = static_cast<uint32_t>(krem) - c;
               break;
             }
             c += c4[j];
@@ -144,8 +168,8 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(TopkArgs a, const fl
         }
       }
       __syncthreads();
-      prefix = s_sel[0];
-      krem = static_cast<int>(s_sel[1]);
+      prefix = s.sel[0];
+      krem = static_cast<int>(s.sel[1]);
       mask |= 255u << shift;
       __syncthreads();
     }
@@ -154,7 +178,7 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(TopkArgs a, const fl
   }
 
   // compaction over contiguous per-thread segments
-  const int seg = ceil_div(N, kTopkThreads);
+  const int seg = ceil_div(N, NT);
   const int s0 = min(N, tid * seg), s1 = min(N, s0 + seg);
   int n_gt = 0, n_eq = 0;
   if (k == N) {
@@ -167,14 +191,9 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(TopkArgs a, const fl
     }
   }
   int tot;
-  const int eq_base = block_exclusive_scan(n_eq, s_wave, &tot);
+  const int eq_base = block_exclusive_scan<NT>(n_eq, s.wave, &tot);
   const int take = max(0, min(n_eq, need - eq_base));
-  const int out_base = block_exclusive_scan(n_gt + take, s_wave, &tot);
-
-  int32_t* oi = out_idx ? out_idx + a.cu_k[r] : nullptr;
-  int32_t* orow = out_rows ? out_rows + a.cu_m[r] : nullptr;
-  int32_t* opos = out_pos ? out_pos + a.cu_m[r] : nullptr;
-  const int row0 = a.b.cu_T[r];
+  const int out_base = block_exclusive_scan<NT>(n_gt + take, s.wave, &tot);
   if (k > 0) {
     int o = out_base, eq_seen = 0;
     for (int i = s0; i < s1; ++i) {
@@ -189,26 +208,86 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(TopkArgs a, const fl
           ++eq_seen;
         }
       }
-      if (sel) {
+      if (sel) emit(o++, i);
+    }
+  }
+}
+
+__global__ void __launch_bounds__(kTopkThreads) topk_kernel(TopkArgs a, const float* __restrict__ scores,
+                                                            const uint8_t* __restrict__ forced,
+                                                            int32_t* __restrict__ out_idx,
+                                                            int32_t* __restrict__ out_rows,
+                                                            int32_t* __restrict__ out_pos) {
+  __shared__ SelectLds<kTopkThreads, kTopkCache> lds;
+  const int r = blockIdx.x;
+  const int N = a.b.n_ctx[r];
+  const int k = a.k[r];
+  const int T = a.b.cu_T[r + 1] - a.b.cu_T[r];
+  const int U = T - N;
+  const int row0 = a.b.cu_T[r];
+  int32_t* oi = out_idx ? out_idx + a.cu_k[r] : nullptr;
+  int32_t* orow = out_rows ? out_rows + a.cu_m[r] : nullptr;
+  int32_t* opos = out_pos ? out_pos + a.cu_m[r] : nullptr;
+  select_block<kTopkThreads, kTopkCache>(
+      scores ? scores + a.b.cu_N[r] : nullptr, forced ? forced + a.b.cu_N[r] : nullptr, N, k, lds,
+      [&](int o, int i) __attribute__((always_inline)) {
         if (oi) oi[o] = i;
         if (orow) {
           orow[o] = row0 + i;
           opos[o] = i;
         }
-        ++o;
-      }
-    }
-  }
+      });
   if (orow) {
-    for (int u = tid; u < U; u += kTopkThreads) {
+    for (int u = threadIdx.x; u < U; u += kTopkThreads) {
       orow[k + u] = row0 + N + u;
       opos[k + u] = N + u;
     }
   }
 }
 
-hipError_t launch_topk(const float* scores, const BatchArgs& B, const int32_t* k_host,
-                       int32_t* out_idx, int32_t* out_rows, int32_t* out_pos, hipStream_t st) {
+// Blocks [0, n_segs) select one segment each; block n_segs + r writes the
+// query rows of request r behind its picks.  A segment that breaks its
+// contract (request, range, k or output slots out of bounds) writes nothing.
+__global__ void __launch_bounds__(kSegThreads) topk_segmented_kernel(
+    TopkArgs a, const float* __restrict__ scores, const uint8_t* __restrict__ forced,
+    const kvf_segment* __restrict__ segs, int n_segs, int32_t* __restrict__ out_idx,
+    int32_t* __restrict__ out_rows, int32_t* __restrict__ out_pos) {
+  __shared__ SelectLds<kSegThreads, kSegCache> lds;
+  if (static_cast<int>(blockIdx.x) >= n_segs) {
+    const int r = blockIdx.x - n_segs;
+    if (!out_rows) return;
+    const int N = a.b.n_ctx[r];
+    const int U = a.b.cu_T[r + 1] - a.b.cu_T[r] - N;
+    for (int u = threadIdx.x; u < U; u += kSegThreads) {
+      out_rows[a.cu_m[r] + a.k[r] + u] = a.b.cu_T[r] + N + u;
+      out_pos[a.cu_m[r] + a.k[r] + u] = N + u;
+    }
+    return;
+  }
+  const kvf_segment g = segs[blockIdx.x];
+  const int r = g.req;
+  if (r < 0 || r >= a.b.n_req) return;
+  const int N = a.b.n_ctx[r];
+  if (g.pos0 < 0 || g.len < 0 || g.pos0 > N - g.len || g.k < 0 || g.k > g.len ||
+      g.out_off < 0 || g.out_off > a.k[r] - g.k)
+    return;
+  const int base = a.b.cu_N[r] + g.pos0;
+  const int row0 = a.b.cu_T[r] + g.pos0;
+  int32_t* oi = out_idx ? out_idx + a.cu_k[r] + g.out_off : nullptr;
+  int32_t* orow = out_rows ? out_rows + a.cu_m[r] + g.out_off : nullptr;
+  int32_t* opos = out_pos ? out_pos + a.cu_m[r] + g.out_off : nullptr;
+  select_block<kSegThreads, kSegCache>(
+      scores ? scores + base : nullptr, forced ? forced + base : nullptr, g.len, g.k, lds,
+      [&](int o, int i) __attribute__((always_inline)) {
+        if (oi) oi[o] = g.pos0 + i;
+        if (orow) {
+          orow[o] = row0 + i;
+          opos[o] = g.pos0 + i;
+        }
+      });
+}
+
+static TopkArgs topk_args(const BatchArgs& B, const int32_t* k_host) {
   TopkArgs a{};
   a.b = B;
   for (int r = 0; r < B.n_req; ++r) {
@@ -216,8 +295,24 @@ hipError_t launch_topk(const float* scores, const BatchArgs& B, const int32_t* k
     a.cu_k[r + 1] = a.cu_k[r] + k_host[r];
     a.cu_m[r + 1] = a.cu_m[r] + k_host[r] + (B.cu_T[r + 1] - B.cu_T[r] - B.n_ctx[r]);
   }
-  hipLaunchKernelGGL(topk_kernel, dim3(B.n_req), dim3(kTopkThreads), 0, st, a, scores, out_idx,
-                     out_rows, out_pos);
+  return a;
+}
+
+hipError_t launch_topk(const float* scores, const uint8_t* forced, const BatchArgs& B,
+                       const int32_t* k_host, int32_t* out_idx, int32_t* out_rows,
+                       int32_t* out_pos, hipStream_t st) {
+  hipLaunchKernelGGL(topk_kernel, dim3(B.n_req), dim3(kTopkThreads), 0, st, topk_args(B, k_host),
+                     scores, forced, out_idx, out_rows, out_pos);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_segmented(const float* scores, const uint8_t* forced, const BatchArgs& B,
+                                 const kvf_segment* segs, int n_segs, const int32_t* k_host,
+                                 int32_t* out_idx, int32_t* out_rows, int32_t* out_pos,
+                                 hipStream_t st) {
+  hipLaunchKernelGGL(topk_segmented_kernel, dim3(n_segs + B.n_req), dim3(kSegThreads), 0, st,
+                     topk_args(B, k_host), scores, forced, segs, n_segs, out_idx, out_rows,
+                     out_pos);
   return hipGetLastError();
 }
 

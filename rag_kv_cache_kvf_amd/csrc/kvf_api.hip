@@ -112,6 +112,12 @@ int32_t kvf_recompute_budget(int32_t n_ctx, int32_t ratio_pct) {
   return static_cast<int32_t>((static_cast<int64_t>(n_ctx) * ratio_pct) / 100);
 }
 
+int32_t kvf_anchor_budget(int32_t len, int32_t ra_num, int32_t ra_den) {
+  if (len < 0 || ra_den <= 0 || ra_num < 0 || ra_num > ra_den) return -1;
+  const int64_t num = static_cast<int64_t>(len) * ra_num;
+  return static_cast<int32_t>((num + ra_den - 1) / ra_den);
+}
+
 kvf_status kvf_rope_table(double base, int32_t head_dim, int32_t n_pos, float* cos_tab,
                           float* sin_tab, void* stream) {
   KVF_GUARD_BEGIN
@@ -206,6 +212,9 @@ kvf_status kvf_score(kvf_score_mode mode, const kvf_layer_desc* layer, const kvf
     return from_hip(kvf::launch_deviation(*layer, B, fused_k, k_fresh, scores,
                                           as_stream(stream)), "kvf_score(deviation)");
   }
+  if (mode == KVF_SCORE_KEY_NORM)
+    return from_hip(kvf::launch_key_norm(*layer, B, fused_k, scores, as_stream(stream)),
+                    "kvf_score(key_norm)");
   KVF_CHECK(mode == KVF_SCORE_ATTN_MASS, KVF_ERR_INVALID_ARG, "unknown score mode %d", mode);
   KVF_CHECK(q_u != nullptr, KVF_ERR_INVALID_ARG, "q_u is NULL");
   const size_t need = kvf::attn_mass_workspace(*layer, B, n_last_q);
@@ -221,9 +230,9 @@ size_t kvf_select_workspace_size(const kvf_batch* batch) {
   return 0;
 }
 
-kvf_status kvf_select_topk(const float* scores, const kvf_batch* batch, const int32_t* k_per_req,
-                           int32_t* out_idx, int32_t* out_rows, int32_t* out_pos,
-                           void* workspace, size_t ws_bytes, void* stream) {
+kvf_status kvf_select_topk(const float* scores, const uint8_t* forced, const kvf_batch* batch,
+                           const int32_t* k_per_req, int32_t* out_idx, int32_t* out_rows,
+                           int32_t* out_pos, void* workspace, size_t ws_bytes, void* stream) {
   KVF_GUARD_BEGIN
   (void)workspace;
   (void)ws_bytes;
@@ -239,11 +248,82 @@ kvf_status kvf_select_topk(const float* scores, const kvf_batch* batch, const in
     total_m += k_per_req[r] + (B.cu_T[r + 1] - B.cu_T[r] - B.n_ctx[r]);
   }
   if (total_m == 0) return KVF_OK;
-  KVF_CHECK(total_k == 0 || (scores && out_idx), KVF_ERR_INVALID_ARG, "required pointer is NULL");
+  KVF_CHECK(total_k == 0 || out_idx, KVF_ERR_INVALID_ARG, "out_idx is NULL");
   KVF_CHECK((out_rows == nullptr) == (out_pos == nullptr), KVF_ERR_INVALID_ARG,
             "out_rows and out_pos must both be given or both be NULL");
-  return from_hip(kvf::launch_topk(scores, B, k_per_req, out_idx, out_rows, out_pos,
+  return from_hip(kvf::launch_topk(scores, forced, B, k_per_req, out_idx, out_rows, out_pos,
                                    as_stream(stream)), "kvf_select_topk");
+  KVF_GUARD_END
+}
+
+kvf_status kvf_select_topk_segmented(const float* scores, const uint8_t* forced,
+                                     const kvf_batch* batch, const kvf_segment* segs,
+                                     int32_t n_segs, const int32_t* k_per_req, int32_t* out_idx,
+                                     int32_t* out_rows, int32_t* out_pos, void* stream) {
+  KVF_GUARD_BEGIN
+  kvf::BatchArgs B;
+  kvf_status st = check_batch(batch, &B);
+  if (st != KVF_OK) return st;
+  KVF_CHECK(k_per_req != nullptr, KVF_ERR_INVALID_ARG, "k_per_req is NULL");
+  KVF_CHECK(n_segs >= 0 && n_segs <= (1 << 24), KVF_ERR_INVALID_ARG, "n_segs %d out of range",
+            n_segs);
+  int64_t total_k = 0, total_m = 0;
+  for (int r = 0; r < B.n_req; ++r) {
+    KVF_CHECK(k_per_req[r] >= 0 && k_per_req[r] <= B.n_ctx[r], KVF_ERR_INVALID_ARG,
+              "k_per_req[%d] = %d outside [0, %d]", r, k_per_req[r], B.n_ctx[r]);
+    total_k += k_per_req[r];
+    total_m += k_per_req[r] + (B.cu_T[r + 1] - B.cu_T[r] - B.n_ctx[r]);
+  }
+  KVF_CHECK((out_rows == nullptr) == (out_pos == nullptr), KVF_ERR_INVALID_ARG,
+            "out_rows and out_pos must both be given or both be NULL");
+  if (out_rows == nullptr && (total_k == 0 || n_segs == 0)) return KVF_OK;
+  if (total_m == 0) return KVF_OK;
+  KVF_CHECK(total_k == 0 || out_idx, KVF_ERR_INVALID_ARG, "out_idx is NULL");
+  KVF_CHECK(n_segs == 0 || segs, KVF_ERR_INVALID_ARG, "segs is NULL");
+  return from_hip(kvf::launch_topk_segmented(scores, forced, B, segs, n_segs, k_per_req, out_idx,
+                                             out_rows, out_pos, as_stream(stream)),
+                  "kvf_select_topk_segmented");
+  KVF_GUARD_END
+}
+
+static kvf_status check_rules(const kvf_static_rules* rules) {
+  KVF_CHECK(rules != nullptr, KVF_ERR_INVALID_ARG, "rules is NULL");
+  KVF_CHECK(rules->sink >= 0 && rules->boundary >= 0 && rules->seam >= 0, KVF_ERR_INVALID_ARG,
+            "static rules must be >= 0");
+  return KVF_OK;
+}
+
+kvf_status kvf_select_static(const kvf_batch* batch, const kvf_chunk* chunks, int32_t n_chunks,
+                             const kvf_static_rules* rules, uint8_t* mask, void* stream) {
+  KVF_GUARD_BEGIN
+  kvf::BatchArgs B;
+  kvf_status st = check_batch(batch, &B);
+  if (st != KVF_OK) return st;
+  st = check_rules(rules);
+  if (st != KVF_OK) return st;
+  KVF_CHECK(n_chunks >= 0, KVF_ERR_INVALID_ARG, "n_chunks negative");
+  if (B.cu_N[B.n_req] == 0) return KVF_OK;
+  KVF_CHECK(mask != nullptr, KVF_ERR_INVALID_ARG, "mask is NULL");
+  KVF_CHECK(n_chunks == 0 || chunks, KVF_ERR_INVALID_ARG, "chunks is NULL");
+  return from_hip(kvf::launch_static_mask(B, chunks, n_chunks, *rules, mask, as_stream(stream)),
+                  "kvf_select_static");
+  KVF_GUARD_END
+}
+
+kvf_status kvf_static_counts(const kvf_batch* batch, const kvf_chunk* chunks_host,
+                             int32_t n_chunks, const kvf_static_rules* rules, int32_t* counts) {
+  KVF_GUARD_BEGIN
+  kvf::BatchArgs B;
+  kvf_status st = check_batch(batch, &B);
+  if (st != KVF_OK) return st;
+  st = check_rules(rules);
+  if (st != KVF_OK) return st;
+  KVF_CHECK(n_chunks >= 0, KVF_ERR_INVALID_ARG, "n_chunks negative");
+  KVF_CHECK(counts != nullptr, KVF_ERR_INVALID_ARG, "counts is NULL");
+  KVF_CHECK(n_chunks == 0 || chunks_host, KVF_ERR_INVALID_ARG, "chunks_host is NULL");
+  kvf::static_counts_host(B, chunks_host, n_chunks, *rules, counts);
+  g_err[0] = '\0';
+  return KVF_OK;
   KVF_GUARD_END
 }
 

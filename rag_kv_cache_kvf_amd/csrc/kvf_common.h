@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <vector>
 
 #include "kvfuse.h"
 
@@ -144,8 +145,19 @@ hipError_t launch_attn_mass(const kvf_layer_desc& L, const BatchArgs& B, const v
                             const void* q_u, int n_last_q, float* scores, void* ws,
                             size_t ws_bytes, hipStream_t st);
 size_t attn_mass_workspace(const kvf_layer_desc& L, const BatchArgs& B, int n_last_q);
-hipError_t launch_topk(const float* scores, const BatchArgs& B, const int32_t* k_host,
-                       int32_t* out_idx, int32_t* out_rows, int32_t* out_pos, hipStream_t st);
+hipError_t launch_key_norm(const kvf_layer_desc& L, const BatchArgs& B, const void* fk,
+                           float* scores, hipStream_t st);
+hipError_t launch_topk(const float* scores, const uint8_t* forced, const BatchArgs& B,
+                       const int32_t* k_host, int32_t* out_idx, int32_t* out_rows,
+                       int32_t* out_pos, hipStream_t st);
+hipError_t launch_topk_segmented(const float* scores, const uint8_t* forced, const BatchArgs& B,
+                                 const kvf_segment* segs, int n_segs, const int32_t* k_host,
+                                 int32_t* out_idx, int32_t* out_rows, int32_t* out_pos,
+                                 hipStream_t st);
+hipError_t launch_static_mask(const BatchArgs& B, const kvf_chunk* chunks, int n_chunks,
+                              const kvf_static_rules& rules, uint8_t* mask, hipStream_t st);
+void static_counts_host(const BatchArgs& B, const kvf_chunk* chunks, int n_chunks,
+                        const kvf_static_rules& rules, int32_t* counts);
 hipError_t launch_recompute(const kvf_layer_desc& L, const void* x, int64_t x_rows,
                             const int32_t* row_src, const int32_t* row_pos, int M,
                             const void* w, uint32_t mask, const float* rc, const float* rs,

@@ -19,7 +19,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvfuse.
 
 KVF_OK, KVF_ERR_INVALID_ARG, KVF_ERR_UNSUPPORTED, KVF_ERR_WORKSPACE, KVF_ERR_HIP = range(5)
 KVF_F32, KVF_BF16 = 0, 1
-KVF_SCORE_DEVIATION, KVF_SCORE_ATTN_MASS = 0, 1
+KVF_SCORE_DEVIATION, KVF_SCORE_ATTN_MASS, KVF_SCORE_KEY_NORM = 0, 1, 2
 KVF_OUT_Q, KVF_OUT_K, KVF_OUT_V = 1, 2, 4
 KVF_MAX_REQ = 64
 
@@ -60,6 +60,10 @@ class Kivi8Desc(ctypes.Structure):
                 ("n_pool_chunks", ctypes.c_int32)]
 
 
+class StaticRules(ctypes.Structure):
+    _fields_ = [("sink", ctypes.c_int32), ("boundary", ctypes.c_int32), ("seam", ctypes.c_int32)]
+
+
 _P = ctypes.c_void_p
 _I32 = ctypes.c_int32
 _I64 = ctypes.c_int64
@@ -74,7 +78,10 @@ _SIGS = {
                             _I32, _P, _P, _I64, _P]),
     "kvf_score": (_I32, [_I32, _LP, _BP, _P, _P, _P, _I32, _P, _P, _SZ, _P]),
     "kvf_score_workspace_size": (_SZ, [_I32, _LP, _BP, _I32]),
-    "kvf_select_topk": (_I32, [_P, _BP, _IP, _P, _P, _P, _P, _SZ, _P]),
+    "kvf_select_topk": (_I32, [_P, _P, _BP, _IP, _P, _P, _P, _P, _SZ, _P]),
+    "kvf_select_topk_segmented": (_I32, [_P, _P, _BP, _P, _I32, _IP, _P, _P, _P, _P]),
+    "kvf_select_static": (_I32, [_BP, _P, _I32, ctypes.POINTER(StaticRules), _P, _P]),
+    "kvf_static_counts": (_I32, [_BP, _P, _I32, ctypes.POINTER(StaticRules), _IP]),
     "kvf_select_workspace_size": (_SZ, [_BP]),
     "kvf_recompute_qkv": (_I32, [_LP, _P, _I64, _P, _P, _I32, _P, ctypes.c_uint32, _P, _P, _I32,
                                  _P, _P, _P, _P, _I64, _P, _SZ, _P]),
@@ -85,6 +92,7 @@ _SIGS = {
     "kvf_attention_workspace_size": (_SZ, [_LP, _BP, _IP]),
     "kvf_kivi8_encode": (_I32, [_LP, _P, _P, _P, _I32, _I64, _I32, ctypes.POINTER(Kivi8Desc), _P]),
     "kvf_recompute_budget": (_I32, [_I32, _I32]),
+    "kvf_anchor_budget": (_I32, [_I32, _I32, _I32]),
     "kvf_status_string": (ctypes.c_char_p, [_I32]),
     "kvf_last_error": (ctypes.c_char_p, []),
     "kvf_abi_version": (_I32, []),
@@ -109,6 +117,10 @@ def abi_version() -> int:
 
 def recompute_budget(n_ctx: int, ratio_pct: int) -> int:
     return _lib.kvf_recompute_budget(n_ctx, ratio_pct)
+
+
+def anchor_budget(length: int, ra_num: int, ra_den: int) -> int:
+    return _lib.kvf_anchor_budget(length, ra_num, ra_den)
 
 
 def _check(status: int, func: str):
@@ -222,13 +234,52 @@ def score(mode: int, layer: Layer, batch: Batch, fused_k: torch.Tensor,
                           ws_bytes, _stream(stream)), "kvf_score")
 
 
-def select_topk(scores: torch.Tensor, batch: Batch, k_per_req: Sequence[int],
+def select_topk(scores: Optional[torch.Tensor], batch: Batch, k_per_req: Sequence[int],
                 out_idx: torch.Tensor, out_rows: Optional[torch.Tensor] = None,
-                out_pos: Optional[torch.Tensor] = None, stream=None):
+                out_pos: Optional[torch.Tensor] = None, forced: Optional[torch.Tensor] = None,
+                stream=None):
+    """forced: uint8 [sum N] mask of positions ranked above every score."""
     ka = _int_array(k_per_req)
-    _check(_lib.kvf_select_topk(_ptr(scores), ctypes.byref(batch.desc), ka, _ptr(out_idx),
-                                _ptr(out_rows), _ptr(out_pos), None, 0, _stream(stream)),
+    _check(_lib.kvf_select_topk(_ptr(scores), _ptr(forced), ctypes.byref(batch.desc), ka,
+                                _ptr(out_idx), _ptr(out_rows), _ptr(out_pos), None, 0,
+                                _stream(stream)),
            "kvf_select_topk")
+
+
+def select_topk_segmented(scores: Optional[torch.Tensor], batch: Batch, segs: torch.Tensor,
+                          k_per_req: Sequence[int], out_idx: torch.Tensor,
+                          out_rows: Optional[torch.Tensor] = None,
+                          out_pos: Optional[torch.Tensor] = None,
+                          forced: Optional[torch.Tensor] = None, stream=None):
+    """segs: int32 [n_segs, 8] device tensor (kvf_segment rows)."""
+    ka = _int_array(k_per_req)
+    _check(_lib.kvf_select_topk_segmented(_ptr(scores), _ptr(forced), ctypes.byref(batch.desc),
+                                          _ptr(segs), int(segs.shape[0]), ka, _ptr(out_idx),
+                                          _ptr(out_rows), _ptr(out_pos), _stream(stream)),
+           "kvf_select_topk_segmented")
+
+
+def select_static(batch: Batch, chunks: torch.Tensor, rules: Sequence[int], mask: torch.Tensor,
+                  stream=None):
+    """rules: (sink, boundary, seam); chunks: int32 [n_chunks, 8] device tensor."""
+    r = StaticRules(*[int(v) for v in rules])
+    _check(_lib.kvf_select_static(ctypes.byref(batch.desc), _ptr(chunks), int(chunks.shape[0]),
+                                  ctypes.byref(r), _ptr(mask), _stream(stream)),
+           "kvf_select_static")
+
+
+def static_counts(batch: Batch, chunks_host, rules: Sequence[int]) -> list:
+    """Per-request count of kvf_select_static's marks; chunks_host: int32
+    [n_chunks, 8] host array (numpy or CPU tensor)."""
+    import numpy as np
+    ch = np.ascontiguousarray(np.asarray(chunks_host, dtype=np.int32))
+    if ch.ndim != 2 or ch.shape[1] != 8:
+        raise ValueError("chunks_host must be int32 [n_chunks, 8]")
+    r = StaticRules(*[int(v) for v in rules])
+    out = (ctypes.c_int32 * max(batch.n_req, 1))()
+    _check(_lib.kvf_static_counts(ctypes.byref(batch.desc), ch.ctypes.data, int(ch.shape[0]),
+                                  ctypes.byref(r), out), "kvf_static_counts")
+    return [int(out[i]) for i in range(batch.n_req)]
 
 
 def recompute_qkv(layer: Layer, x: torch.Tensor, row_src: Optional[torch.Tensor],

@@ -15,6 +15,15 @@ itself.  Order (all on one stream, no host synchronisation):
     kvf_recompute_qkv(P+U, Q|K|V; K/V into the fused cache) ->
     kvf_sparse_q_attention
   (the recompute call's destination-row output is the scatter of Eq. 7)
+  static selection (KVBoost page, sections 4.1 and 4.6.1; QCFuse page,
+  section 2.2.1)
+    kvf_rerotate -> kvf_select_static -> kvf_select_topk(forced set only) ->
+    kvf_recompute_qkv(P+U, Q|K|V into the fused cache) -> kvf_sparse_q_attention
+  per-chunk key-norm anchors (QCFuse page, section 3.3.1, Eq. 14)
+    kvf_rerotate -> kvf_score(KEY_NORM) -> kvf_select_topk_segmented ->
+    kvf_recompute_qkv(P+U, Q|K|V into the fused cache) -> kvf_sparse_q_attention
+  A score selector with static rules takes their positions as a forced set
+  (kvf_select_static before kvf_select_topk).
 
 The per-chunk caches are built ahead of serving (QCFuse page, section 2.1.2,
 Eq. 3) either by the caller (`pic=`) or on the GPU by this library's own
@@ -50,6 +59,13 @@ class FusedLayerGPU:
         self.wl = wl
         self.batch = batch
         self.mode = mode or wl.score
+        self.selector = wl.selector
+        self.rules = tuple(int(v) for v in wl.static_rules)
+        if self.selector not in ("score", "static", "anchor"):
+            raise ValueError(f"unknown selector {self.selector!r}")
+        # the key probe of deviation scoring; other selectors project P+U only
+        self.probe = self.selector == "score" and self.mode == "deviation"
+        self.mass = self.selector == "score" and self.mode != "deviation"
         self.n_last_q = n_last_q
         self.device = torch.device(device)
         dev = self.device
@@ -106,7 +122,26 @@ class FusedLayerGPU:
             del pool_hidden
 
         # budgets and buffers
-        self.k_per_req = [kvf.recompute_budget(int(n), ratio_pct) for n in batch.n_ctx]
+        self.static_mask = None
+        self.segs = None
+        if self.selector == "static":
+            self.k_per_req = kvf.static_counts(self.kb, batch.chunk_table, self.rules)
+        elif self.selector == "anchor":
+            segs, ks = [], []
+            for r in range(R):
+                kr = 0
+                for p0, ln in batch.chunk_spans(r):
+                    kc = kvf.anchor_budget(ln, wl.anchor_pct, 100)
+                    segs.append([r, p0, ln, kc, kr, 0, 0, 0])
+                    kr += kc
+                ks.append(kr)
+            self.k_per_req = ks
+            self.segs = _i32(np.asarray(segs, dtype=np.int32).reshape(-1, 8), dev)
+        else:
+            self.k_per_req = [kvf.recompute_budget(int(n), ratio_pct) for n in batch.n_ctx]
+        if self.selector == "static" or any(self.rules):
+            self.static_mask = torch.zeros(max(int(np.sum(batch.n_ctx)), 1), dtype=torch.uint8,
+                                           device=dev)
         self.U = [self.kb.n_query(r) for r in range(R)]
         self.M_per_req = [k + u for k, u in zip(self.k_per_req, self.U)]
         self.cu_q = [0] + list(np.cumsum(self.M_per_req).astype(int))
@@ -127,10 +162,10 @@ class FusedLayerGPU:
         self.u_pos = _i32(batch.query_pos(), dev)
         nU = int(self.u_rows.shape[0])
         self.ws = None
-        if self.mode == "deviation":
+        if self.probe:
             self.all_pos = _i32(batch.all_pos(), dev)
             self.k_probe = torch.zeros((T_total, hkv, d), dtype=td, device=dev)
-        else:
+        elif self.mass:
             self.q_u = torch.zeros((max(nU, 1), hq, d), dtype=td, device=dev)
             nbytes = kvf.score_workspace_size(kvf.KVF_SCORE_ATTN_MASS, L, self.kb, n_last_q)
             self.ws = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=dev)
@@ -138,9 +173,9 @@ class FusedLayerGPU:
         # on the stream), so the stages allocate nothing
         QKV = kvf.KVF_OUT_Q | kvf.KVF_OUT_K | kvf.KVF_OUT_V
         need = [kvf.recompute_workspace_size(L, M, QKV)]
-        if self.mode == "deviation":
+        if self.probe:
             need.append(kvf.recompute_workspace_size(L, T_total, kvf.KVF_OUT_K))
-        else:
+        elif self.mass:
             need.append(kvf.recompute_workspace_size(L, nU, QKV))
         self.gemm_ws = torch.empty(max(max(need), 1), dtype=torch.uint8, device=dev)
         # key-split workspace of the attention call: zero-filled once, every
@@ -164,8 +199,14 @@ class FusedLayerGPU:
                           self.rope_sin, q_out=self.q_u, k_out=self.fused_k, v_out=self.fused_v,
                           kv_out_row=self.u_rows, workspace=self.gemm_ws)
 
+    def _static_mask(self):
+        kvf.select_static(self.kb, self.chunks, self.rules, self.static_mask)
+
     def _score(self):
-        if self.mode == "deviation":
+        if self.selector == "anchor":
+            kvf.score(kvf.KVF_SCORE_KEY_NORM, self.layer, self.kb, self.fused_k, None, None,
+                      self.scores)
+        elif self.mode == "deviation":
             kvf.score(kvf.KVF_SCORE_DEVIATION, self.layer, self.kb, self.fused_k, self.k_probe,
                       None, self.scores)
         else:
@@ -173,12 +214,18 @@ class FusedLayerGPU:
                       self.scores, self.ws, n_last_q=self.n_last_q)
 
     def _select(self):
-        kvf.select_topk(self.scores, self.kb, self.k_per_req, self.sel, self.rows, self.pos)
+        if self.selector == "anchor":
+            kvf.select_topk_segmented(self.scores, self.kb, self.segs, self.k_per_req, self.sel,
+                                      self.rows, self.pos)
+        else:
+            kvf.select_topk(None if self.selector == "static" else self.scores, self.kb,
+                            self.k_per_req, self.sel, self.rows, self.pos,
+                            forced=self.static_mask)
 
     def _recompute(self):
         if self.M == 0:
             return
-        if self.mode == "deviation":
+        if self.probe:
             # K of these rows is already in the probe
             kvf.recompute_qkv(self.layer, self.x, self.rows, self.pos, self.w,
                               kvf.KVF_OUT_Q | kvf.KVF_OUT_V, self.rope_cos, self.rope_sin,
@@ -208,15 +255,20 @@ class FusedLayerGPU:
     def calls(self):
         """The library calls of one pass, in order, as (name, stage, fn):
         stage is one of rerotate / score / select / recompute_fuse / attention."""
-        if self.mode == "deviation":
+        fuse = [("recompute", "recompute_fuse", self._recompute)]
+        if self.probe:
             score = [("k_probe", "score", self._k_probe), ("score", "score", self._score)]
-            fuse = [("recompute", "recompute_fuse", self._recompute),
-                    ("scatter", "recompute_fuse", self._scatter)]
-        else:
+            fuse.append(("scatter", "recompute_fuse", self._scatter))
+        elif self.mass:
             score = [("u_probe", "score", self._u_probe), ("score", "score", self._score)]
-            fuse = [("recompute", "recompute_fuse", self._recompute)]
-        return ([("rerotate", "rerotate", self._rerotate)] + score +
-                [("select", "select", self._select)] + fuse +
+        elif self.selector == "anchor":
+            score = [("score", "score", self._score)]
+        else:
+            score = []
+        select = [("select", "select", self._select)]
+        if self.static_mask is not None:
+            select.insert(0, ("static_mask", "select", self._static_mask))
+        return ([("rerotate", "rerotate", self._rerotate)] + score + select + fuse +
                 [("attention", "attention", self._attention)])
 
     def _stage(self, stage):
@@ -261,11 +313,13 @@ class FusedLayerGPU:
             for _, _, fn in self.calls():
                 fn()
             return
+        forced = False
         for _, st, fn in self.calls():
-            if st == "select":
-                self.force_selection(forced_sel)
-            else:
+            if st != "select":
                 fn()
+            elif not forced:
+                self.force_selection(forced_sel)
+                forced = True
 
     # ------------------------------------------------------------------ readback
     def selection(self):

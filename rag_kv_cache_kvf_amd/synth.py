@@ -50,6 +50,13 @@ class Workload:
     kivi8: bool = False        # cached K/V stored as int8 codes
     seed: int = 0
     description: str = ""
+    # selector feeding the recompute path: "score" (top-k of `score`, with
+    # static_rules as a forced set when any is nonzero), "static" (exactly the
+    # static_rules positions) or "anchor" (per-chunk top-k of the key norm,
+    # ceil(anchor_pct / 100 * chunk length) per chunk)
+    selector: str = "score"
+    static_rules: tuple = (0, 0, 0)     # (sink, boundary, seam)
+    anchor_pct: int = 0
 
     @property
     def n_chunks(self) -> int:
@@ -90,6 +97,23 @@ WORKLOADS = {
         n_query=(256,), hidden=8192, n_q_heads=64, n_kv_heads=8, head_dim=128,
         rope_base=5e5, score="attn_mass", ratio_pct=(20,), sigma=0.05,
         description="Llama-3-70B-shaped layer, bf16, 1 request of 32x1024 + 256 query"),
+    # The Qwen3-8B-shaped request with static selection: KVBoost's seam
+    # windows (R = 16) plus 4 attention-sink tokens.
+    "qwen3_8b_seam": _wl(
+        name="qwen3_8b_seam", dtype="bf16", n_req=1, chunk_lens=(512,) * 10,
+        n_query=(64,), hidden=4096, n_q_heads=32, n_kv_heads=8, head_dim=128,
+        rope_base=1e6, score="attn_mass", ratio_pct=(0,), sigma=0.1,
+        selector="static", static_rules=(4, 0, 16),
+        description="Qwen3-8B-shaped layer, bf16, 1 request of 10x512 + 64 query, "
+                    "static selection (seam windows R=16, 4 sink tokens)"),
+    # The same request with per-chunk key-norm anchors, r_a = 10%.
+    "qwen3_8b_anchor": _wl(
+        name="qwen3_8b_anchor", dtype="bf16", n_req=1, chunk_lens=(512,) * 10,
+        n_query=(64,), hidden=4096, n_q_heads=32, n_kv_heads=8, head_dim=128,
+        rope_base=1e6, score="attn_mass", ratio_pct=(0,), sigma=0.1,
+        selector="anchor", anchor_pct=10,
+        description="Qwen3-8B-shaped layer, bf16, 1 request of 10x512 + 64 query, "
+                    "per-chunk key-norm anchors (r_a = 10%) as the recompute set"),
     # Qwen2.5-3B-shaped layer, int8 KIVI cache, 16 requests of 24 x 128 + 64.
     "qwen25_3b_kivi8": _wl(
         name="qwen25_3b_kivi8", dtype="bf16", n_req=16, chunk_lens=(128,) * 24,
@@ -120,6 +144,21 @@ MINI_WORKLOADS = {
         name="mini_bf16_d64_mass", dtype="bf16", n_req=1, chunk_lens=(50, 77, 61),
         n_query=(45,), hidden=256, n_q_heads=4, n_kv_heads=2, head_dim=64,
         rope_base=1e4, score="attn_mass", ratio_pct=(20,), sigma=0.1),
+    "mini_bf16_seam": _wl(
+        name="mini_bf16_seam", dtype="bf16", n_req=2, chunk_lens=(97, 130, 64, 33),
+        n_query=(19, 40), hidden=512, n_q_heads=8, n_kv_heads=2, head_dim=128,
+        rope_base=1e6, score="attn_mass", ratio_pct=(0,), sigma=0.1,
+        selector="static", static_rules=(3, 2, 16)),
+    "mini_bf16_anchor": _wl(
+        name="mini_bf16_anchor", dtype="bf16", n_req=2, chunk_lens=(97, 130, 64, 33),
+        n_query=(19, 40), hidden=512, n_q_heads=8, n_kv_heads=2, head_dim=128,
+        rope_base=1e6, score="attn_mass", ratio_pct=(0,), sigma=0.1,
+        selector="anchor", anchor_pct=15),
+    "mini_bf16_dev_sink": _wl(
+        name="mini_bf16_dev_sink", dtype="bf16", n_req=3, chunk_lens=(70, 70, 70, 70),
+        n_query=(21,), hidden=384, n_q_heads=4, n_kv_heads=4, head_dim=128,
+        rope_base=1e6, score="deviation", ratio_pct=(30,), sigma=0.1,
+        pool_chunks=6, static_rules=(4, 1, 0)),
     "mini_f32_mass": _wl(
         name="mini_f32_mass", dtype="f32", n_req=2, chunk_lens=(40, 23, 64),
         n_query=(9, 30), hidden=128, n_q_heads=4, n_kv_heads=2, head_dim=64,
@@ -228,6 +267,14 @@ class Batch:
     def all_pos(self) -> np.ndarray:
         return np.concatenate([np.arange(self.cu_T[r + 1] - self.cu_T[r], dtype=np.int32)
                                for r in range(self.n_req)])
+
+    def chunk_spans(self, r: int):
+        """(start position, length) of every stitched chunk of request r,
+        ascending."""
+        t = self.chunk_table
+        mine = t[(t[:, 1] >= self.cu_T[r]) & (t[:, 1] < self.cu_T[r] + self.n_ctx[r])]
+        mine = mine[np.argsort(mine[:, 1], kind="stable")]
+        return [(int(row[1] - self.cu_T[r]), int(row[3])) for row in mine]
 
 
 def _chunk_ids(wl: Workload, r: int) -> List[int]:

@@ -8,7 +8,7 @@ import re
 import numpy as np
 import pytest
 
-from oracle import fusion
+from oracle import fusion, selectors
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "kvfuse.h")
@@ -48,7 +48,7 @@ def test_status_strings_and_version(lib):
     lib.kvf_status_string.restype = ctypes.c_char_p
     assert lib.kvf_status_string(0) == b"KVF_OK"
     assert lib.kvf_status_string(2) == b"KVF_ERR_UNSUPPORTED"
-    assert lib.kvf_abi_version() == 4
+    assert lib.kvf_abi_version() == 5
 
 
 def test_budget_matches_oracle(lib):
@@ -75,6 +75,10 @@ def _batch(cu, nc):
     b = (ctypes.c_int32 * len(nc))(*nc)
     return Batch(len(nc), ctypes.cast(a, ctypes.POINTER(ctypes.c_int32)),
                  ctypes.cast(b, ctypes.POINTER(ctypes.c_int32))), (a, b)
+
+
+class StaticRules(ctypes.Structure):
+    _fields_ = [("sink", ctypes.c_int32), ("boundary", ctypes.c_int32), ("seam", ctypes.c_int32)]
 
 
 FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
@@ -149,7 +153,26 @@ def test_validation_errors(lib):
                                       FAKE, 0.088, FAKE, None, None, 0, None) == 1
     # top-k: k > N
     k = (ctypes.c_int32 * 1)(7)
-    assert lib.kvf_select_topk(FAKE, ctypes.byref(b), k, FAKE, None, None, None, 0, None) == 1
+    assert lib.kvf_select_topk(FAKE, None, ctypes.byref(b), k, FAKE, None, None, None, 0, None) == 1
+    assert lib.kvf_select_topk(FAKE, FAKE, ctypes.byref(b), k, FAKE, None, None, None, 0, None) == 1
+    assert lib.kvf_select_topk_segmented(FAKE, None, ctypes.byref(b), FAKE, 1, k, FAKE, None,
+                                         None, None) == 1
+    k = (ctypes.c_int32 * 1)(3)
+    assert lib.kvf_select_topk(FAKE, None, ctypes.byref(b), k, None, None, None, None, 0,
+                               None) == 1                         # out_idx NULL
+    assert lib.kvf_select_topk_segmented(FAKE, None, ctypes.byref(b), FAKE, 1, k, FAKE, FAKE,
+                                         None, None) == 1         # rows without pos
+    assert lib.kvf_select_topk_segmented(FAKE, None, ctypes.byref(b), None, 1, k, FAKE, None,
+                                         None, None) == 1         # segs NULL
+    assert lib.kvf_select_topk_segmented(FAKE, None, ctypes.byref(b), FAKE, -1, k, FAKE, None,
+                                         None, None) == 1
+    # static selection: negative rules, missing mask
+    neg = StaticRules(-1, 0, 0)
+    assert lib.kvf_select_static(ctypes.byref(b), FAKE, 1, ctypes.byref(neg), FAKE, None) == 1
+    good = StaticRules(1, 1, 1)
+    assert lib.kvf_select_static(ctypes.byref(b), FAKE, 1, ctypes.byref(good), None, None) == 1
+    assert lib.kvf_select_static(ctypes.byref(b), None, 1, ctypes.byref(good), FAKE, None) == 1
+    assert lib.kvf_select_static(ctypes.byref(b), FAKE, 1, None, FAKE, None) == 1
     # too many requests
     cu = list(range(0, 66))
     b, keep = _batch(cu, [0] * 65)
@@ -171,3 +194,51 @@ def test_empty_calls_are_noops(lib):
                                  None, None, None, None, 0, None, 0, None) == 0
     assert lib.kvf_scatter_kv(ctypes.byref(ok), None, None, 0, None, None, 0, None, 0, None, None, 0,
                               None) == 0
+
+
+def test_anchor_budget_matches_oracle(lib):
+    for n in (0, 1, 5, 37, 64, 128, 512, 1000, 1024):
+        for num, den in ((1, 10), (15, 100), (1, 3), (0, 7), (7, 7), (333, 1000)):
+            assert lib.kvf_anchor_budget(n, num, den) == selectors.anchor_budget(n, num, den)
+    for args in ((-1, 1, 4), (5, 1, 0), (5, -1, 4), (5, 5, 4)):
+        assert lib.kvf_anchor_budget(*args) == -1
+
+
+def _chunk_rows(cu_T, starts_per_req, pos_shift=0):
+    rows = []
+    for r, starts in enumerate(starts_per_req):
+        for p in starts:
+            rows.append([0, cu_T[r] + p, p + pos_shift, 1, 0, 0, 0, 0])
+    return np.array(rows, dtype=np.int32).reshape(-1, 8)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_static_counts_match_oracle(lib, seed):
+    """The host count the library sizes static selections with equals the
+    number of positions in the oracle's static mask (host code only)."""
+    g = np.random.default_rng(500 + seed)
+    n_req = int(g.integers(1, 5))
+    ns = [int(g.integers(0, 300)) for _ in range(n_req)]
+    us = [int(g.integers(0, 20)) for _ in range(n_req)]
+    cu = [0]
+    for n, u in zip(ns, us):
+        cu.append(cu[-1] + n + u)
+    starts = []
+    for n in ns:
+        st = sorted(set([0] + g.integers(0, max(n, 1), size=int(g.integers(0, 6))).tolist()))
+        starts.append([p for p in st if p < n] if n else [])
+    ch = _chunk_rows(cu, starts)
+    # chunks of other requests and a chunk starting in the query rows are ignored
+    if n_req and us[0]:
+        ch = np.concatenate([ch, np.array([[0, cu[0] + ns[0], 0, 1, 0, 0, 0, 0]], np.int32)])
+    g.shuffle(ch)
+    sink, boundary, seam = (int(v) for v in g.integers(0, 20, size=3))
+    b, keep = _batch(cu, ns)
+    out = (ctypes.c_int32 * n_req)()
+    rules = StaticRules(sink, boundary, seam)
+    assert lib.kvf_static_counts(ctypes.byref(b), ch.ctypes.data_as(ctypes.c_void_p),
+                                 ch.shape[0], ctypes.byref(rules), out) == 0
+    for r in range(n_req):
+        want = int(selectors.static_mask(ns[r], starts[r] or [0], sink, boundary, seam).sum()) \
+            if ns[r] else 0
+        assert out[r] == want

@@ -13,7 +13,7 @@ KIVI), then fed to both sides.  Checks:
 import numpy as np
 import pytest
 
-from oracle import fusion, kivi
+from oracle import fusion, kivi, selectors
 from rag_kv_cache_kvf_amd import synth
 from tests.gpu_util import TOL, assert_close, assert_close_vectors, decode, encode, from_gpu, raw
 
@@ -162,3 +162,95 @@ def test_deterministic_and_graph_replay(layer_mod):
         torch.cuda.synchronize()
         for k, v in first.items():
             assert np.array_equal(raw(getattr(g, k)), v), f"replay {rep}: {k} differs"
+
+
+# ----------------------------------------------------------------------------
+# other selectors feeding the same path
+# ----------------------------------------------------------------------------
+SEL_E2E = ["mini_bf16_seam", "mini_bf16_anchor", "mini_bf16_dev_sink"]
+
+
+def _static_masks(b, wl):
+    return [selectors.static_mask(int(b.n_ctx[r]), [p for p, _ in b.chunk_spans(r)],
+                                  *wl.static_rules) for r in range(b.n_req)]
+
+
+@pytest.mark.parametrize("name", SEL_E2E)
+def test_selector_end_to_end(layer_mod, name):
+    """Static selection (KVBoost sections 4.1 and 4.6.1, EPIC's boundary
+    tokens), per-chunk key-norm anchors (QCFuse section 3.3.1, Eq. 14) and a
+    deviation score with a forced static set, each through the whole layer:
+    the selection against the oracle's (bit-exact where no floating point
+    decides it), then the fused cache and attention with the oracle's
+    selection forced in."""
+    import torch
+    b, wl, lo, x, w, pic, opk, opv, pct, ks = _oracle_inputs(name)
+    print(f"[case] {name}", flush=True)
+    g = layer_mod.FusedLayerGPU(b, pct, pic=pic)
+    g.run()
+    torch.cuda.synchronize()
+    sel_gpu = g.selection()
+    nsum = int(np.sum(b.n_ctx))
+    offs = np.concatenate([[0], np.cumsum(b.n_ctx)]).astype(int)
+    masks = None
+    if wl.selector == "static" or any(wl.static_rules):
+        masks = _static_masks(b, wl)
+        assert np.array_equal(raw(g.static_mask)[:nsum], np.concatenate(masks))
+    if wl.selector == "static":
+        sel = [np.flatnonzero(m).astype(np.int32) for m in masks]
+        for r in range(b.n_req):
+            assert np.array_equal(sel_gpu[r], sel[r]), f"request {r}"
+        mode = "none"
+    elif wl.selector == "anchor":
+        fk, _ = fusion.rerotate_stitch(opk, opv, b.chunk_table, b.total_rows, lo)
+        fk = decode(encode(fk, wl.dtype), wl.dtype)
+        gs = from_gpu(g.scores)[:nsum]
+        sel = []
+        for r in range(b.n_req):
+            a, n = int(b.cu_T[r]), int(b.n_ctx[r])
+            s = selectors.key_norm(fk[a:a + n])
+            rel = np.abs(gs[offs[r]:offs[r] + n] - s) / s
+            print(f"[parity] {name} req {r} key norm: max rel {float(rel.max()):.3e}", flush=True)
+            assert rel.max() <= 4e-3
+            spans = b.chunk_spans(r)
+            kk = [selectors.anchor_budget(ln, wl.anchor_pct, 100) for _, ln in spans]
+            sel.append(selectors.select_topk_segmented(s, [p for p, _ in spans],
+                                                       [ln for _, ln in spans], kk))
+            for (p0, ln), kc in zip(spans, kk):
+                mine = sel_gpu[r][(sel_gpu[r] >= p0) & (sel_gpu[r] < p0 + ln)] - p0
+                assert len(mine) == kc
+                _check_selection_valid(mine, s[p0:p0 + ln], 4e-3 * float(s.max()),
+                                       f"{name} req {r} chunk at {p0}")
+        mode = "none"
+    else:
+        ref0 = fusion.fused_layer(x, w, opk, opv, b.chunk_table, b.cu_T, b.n_ctx, lo, wl.score,
+                                  ks, store=wl.dtype)
+        rs = np.concatenate(ref0["scores"])
+        assert_close(from_gpu(g.scores)[:nsum], rs, wl.dtype, f"{name} scores")
+        rms = float(np.sqrt(np.mean(rs * rs)))
+        sel = []
+        for r in range(b.n_req):
+            s = ref0["scores"][r]
+            sel.append(selectors.select_topk_forced(s.astype(np.float32), ks[r], masks[r]))
+            f = np.flatnonzero(masks[r])
+            assert len(f) <= ks[r] and np.isin(f, sel_gpu[r]).all(), f"request {r}: forced set"
+            ranked = s.astype(np.float64).copy()
+            ranked[f] = np.inf
+            _check_selection_valid(sel_gpu[r], ranked, 2 * TOL[wl.dtype] * rms, f"{name} req {r}")
+        mode = wl.score
+    for r in range(b.n_req):
+        assert len(sel_gpu[r]) == g.k_per_req[r] and np.all(np.diff(sel_gpu[r]) > 0)
+
+    kk = [len(s) for s in sel]
+    ref = fusion.fused_layer(x, w, opk, opv, b.chunk_table, b.cu_T, b.n_ctx, lo, mode, kk,
+                             forced_sel=sel, store=wl.dtype)
+    exact = fusion.fused_layer(x, w, opk, opv, b.chunk_table, b.cu_T, b.n_ctx, lo, mode, kk,
+                               forced_sel=sel)
+    g.run(forced_sel=sel)
+    torch.cuda.synchronize()
+    assert np.array_equal(raw(g.rows)[: g.M], ref["rows"])
+    assert_close(from_gpu(g.fused_k), exact["fused_k"], wl.dtype, f"{name} fused K")
+    assert_close(from_gpu(g.fused_v), exact["fused_v"], wl.dtype, f"{name} fused V")
+    assert_close(from_gpu(g.q)[: g.M], exact["q"], wl.dtype, f"{name} recomputed Q")
+    assert_close_vectors(from_gpu(g.out)[: g.M], ref["out"], wl.dtype, f"{name} attention output")
+    assert_close(from_gpu(g.lse)[: g.M], ref["lse"], wl.dtype, f"{name} lse", tol=1e-3)

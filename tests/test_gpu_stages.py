@@ -490,6 +490,9 @@ ATTN_CASES = [
     # long rows in a small grid: with a workspace their keys split in two
     ("bf16", 32, 8, 128, [3000, 2000], [400, 700]),
     ("bf16", 8, 2, 64, [2500], [300]),
+    # a few long row tiles (a seam-window recompute set): up to 8 parts
+    ("bf16", 32, 8, 128, [5184], [212]),
+    ("bf16", 8, 2, 64, [6000, 300], [40, 3]),
     ("f32", 4, 4, 64, [288], [108]),
     ("f32", 4, 2, 64, [150, 140], [70, 39]),
 ]
@@ -522,7 +525,8 @@ def test_attention(kvf, case):
         runs.append((from_gpu(out), from_gpu(lse)))
     if ws is not None:
         # the workspace ends in one int32 arrival counter per (row tile, kv head)
-        items = need // (2 * (d // 32 * 16 + 2) * 256 * 4 + 4)
+        rows_per_tile = 128 // (hq // hkv)
+        items = sum(-(-m // rows_per_tile) for m in Ms) * hkv
         assert not bool(ws[need - 4 * items:need].view(torch.int32).any()), "arrival counters not reset"
     lo = fusion.Layer(256, hq, hkv, d, 1e4)
     dk, dv, dq = decode(k_s, dtype), decode(v_s, dtype), decode(q_s, dtype)

@@ -138,3 +138,26 @@ def test_serving_precision_mode(name):
         assert 0 < e < 2e-2, (key, e)
     e = np.max(np.abs(bf["out"] - exact["out"])) / rms
     assert 0 < e < 0.1
+
+
+@pytest.mark.parametrize("name", ["mini_bf16_mass", "mini_bf16_dev_pool"])
+def test_given_selection_mode(name):
+    """mode "none" (selection handed in, no scoring) builds the same fused
+    cache and outputs as the scored modes run on that selection, and with
+    every context position selected it reproduces full prefill."""
+    wl, b, layer, x, w, pk, pv = _setup(name)
+    ref = _run(wl, b, layer, x, w, pk, pv, 30)
+    sel = ref["sel"]
+    ks = [len(s) for s in sel]
+    got = fusion.fused_layer(x, w, pk, pv, b.chunk_table, b.cu_T, b.n_ctx, layer, "none", ks,
+                             forced_sel=sel)
+    for key in ("fused_k", "fused_v", "out", "lse", "q", "rows", "pos"):
+        np.testing.assert_allclose(got[key], ref[key], rtol=1e-10, atol=1e-10, err_msg=key)
+    assert all(s is None for s in got["scores"])
+    every = [np.arange(int(n), dtype=np.int32) for n in b.n_ctx]
+    allr = fusion.fused_layer(x, w, pk, pv, b.chunk_table, b.cu_T, b.n_ctx, layer, "none",
+                              [len(s) for s in every], forced_sel=every)
+    full = fusion.full_prefill(x, w, b.cu_T, layer)
+    np.testing.assert_allclose(allr["fused_k"], full["k"], rtol=1e-9, atol=1e-9)
+    with pytest.raises(ValueError):
+        fusion.fused_layer(x, w, pk, pv, b.chunk_table, b.cu_T, b.n_ctx, layer, "none", ks)

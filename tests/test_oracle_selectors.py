@@ -50,6 +50,7 @@ def test_key_norm_rotation_invariant():
 
 def test_key_norm_zero_and_scale():
     assert np.all(selectors.key_norm(np.zeros((3, 2, 8))) == 0.0)
+    assert selectors.key_norm(np.zeros((0, 2, 8))).shape == (0,)
     k = np.zeros((1, 2, 4))
     k[0, 0, 0], k[0, 1, 3] = 3.0, 4.0
     assert selectors.key_norm(k)[0] == 5.0

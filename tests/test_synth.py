@@ -44,3 +44,22 @@ def test_bf16_encoding_rounds_to_nearest_even():
     back = (bits.astype(np.uint32) << 16).view(np.float32)
     # 1 + 2^-8 is a tie between 1 and 1 + 2^-7: even mantissa (1.0) wins
     assert back.tolist() == [1.0, 1.0, 1.0078125, 1.0, -2.5]
+
+
+@pytest.mark.parametrize("name", ["mini_bf16_seam", "mini_bf16_dev_pool", "qwen3_8b_anchor"])
+def test_chunk_spans_tile_the_context(name):
+    b = synth.make_batch(name) if name.startswith("mini") else None
+    if b is None:
+        wl = synth.get_workload(name)
+        # layout only: the spans follow the workload's chunk lengths
+        import dataclasses
+        b = synth.make_batch(dataclasses.replace(wl, hidden=64, n_q_heads=1, n_kv_heads=1,
+                                                 head_dim=64))
+    for r in range(b.n_req):
+        spans = b.chunk_spans(r)
+        assert [ln for _, ln in spans] == list(b.wl.chunk_lens)
+        pos = 0
+        for p, ln in spans:
+            assert p == pos
+            pos += ln
+        assert pos == int(b.n_ctx[r])
