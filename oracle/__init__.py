@@ -10,7 +10,7 @@ inputs reach it as plain numpy arrays.
 Sources (cited by page title and section / equation):
   [QCF] "QCFuse: Query-Aware Cache Fusion via Compressed View for Efficient
         RAG Serving" - sections 2.1.1-2.1.3 (Eq. 1-7), 2.2 (2.2.1), 3.2.1
-        (Eq. 9-11), 3.3.1 (Eq. 14).
+        (Eq. 9-11), 3.3.1 (Eq. 14), 3.4.2 (Eq. 20).
   [KVB] "KVBoost: Chunk-Level Key-Value Cache Reuse with Deviation-Guided
         Recomputation for Efficient Large Language Model Inference" -
         section 3.1 (Eq. 1-2), 3.2 (Eq. 3), 4.1, 4.5 (Eq. 7), 4.6.1
@@ -22,4 +22,4 @@ closed forms, invariants, brute force on tiny inputs or special cases
 package is "parity unpinned"; the quality of the selected set on real text
 (which needs trained weights and datasets) is not claimed anywhere.
 """
-from . import storage, rope, kivi, fusion, selectors  # noqa: F401
+from . import storage, rope, kivi, fusion, selectors, multilayer  # noqa: F401
