@@ -41,8 +41,10 @@ if ROOT not in sys.path:
 DEFAULT_WORKLOAD = "qwen3_8b_mass"
 METRIC = "fused context tokens/s per layer @r=30% on 1 MI355X; % MFMA/HBM roofline"
 UNIT = "fused context tokens/s per layer"
-# MI355X published peaks: HBM3E bandwidth, dense MFMA bf16, fp32 vector
-PEAK = {"hbm": 8000.0, "bf16": 2500.0, "f32": 157.3}
+# MI355X published peaks: HBM3E bandwidth, dense MFMA bf16, fp32 vector, and
+# the host link
+PEAK = {"hbm": 8000.0, "bf16": 2500.0, "f32": 157.3,
+        "pcie": 64.0}    # host link: PCIe 5.0 x16, one direction, GB/s
 KDIR = os.path.join(ROOT, "rag_kv_cache_kvf_amd", "csrc")
 # library call -> (kernel that dominates it, its source file)
 CALL_KERNEL = {
@@ -252,6 +254,210 @@ def cpu_baseline(batch, ratio, min_seconds=10.0):
                       f"({batch.n_req} request(s), {n_ctx} context tokens), float64 numpy"}
 
 
+def cpu_baseline_multilayer(batches, pcts, min_seconds=10.0):
+    """The float64 oracle over every layer of a multi-layer pass (selection
+    signal included), repeated until at least `min_seconds` of host time."""
+    import numpy as np
+    from oracle import fusion, multilayer, storage
+    wl = batches[0].wl
+    lo = fusion.Layer(wl.hidden, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.rope_base)
+    prep = []
+    for b in batches:
+        x = storage.decode(b.x, wl.dtype)
+        w = storage.decode(b.w_qkv, wl.dtype)
+        pk, pv = fusion.pic_encode(storage.decode(b.pool_hidden, wl.dtype), b.pool_pos, w, lo)
+        prep.append((b, x, w, pk, pv))
+    L = len(batches)
+
+    def one_pass():
+        def layer(l, mode, ks, sel=None):
+            b, x, w, pk, pv = prep[l]
+            return fusion.fused_layer(x, w, pk, pv, b.chunk_table, b.cu_T, b.n_ctx, lo, mode, ks,
+                                      forced_sel=sel)
+        n = [int(v) for v in batches[0].n_ctx]
+        if wl.signal == "sum":
+            ks = [fusion.budget(v, pcts[0]) for v in n]
+            layers = list(wl.score_layers) or list(range(L))
+            per = [layer(l, "attn_mass", ks)["scores"] for l in layers]
+            sel = [fusion.select_topk(multilayer.layer_sum([p[r] for p in per]).astype(np.float32),
+                                      ks[r]) for r in range(len(n))]
+            for l in range(L):
+                layer(l, "none", ks, sel)
+        elif wl.signal == "progressive":
+            cand = [None] * len(n)
+            for l in range(L):
+                ks = [fusion.budget(v, pcts[l]) for v in n]
+                dev = layer(l, "deviation", ks)["scores"]
+                sel = []
+                for r in range(len(n)):
+                    s = dev[r] if cand[r] is None else multilayer.restrict(dev[r], cand[r])
+                    sel.append(fusion.select_topk(np.asarray(s, dtype=np.float32), ks[r]))
+                    cand[r] = np.isin(np.arange(n[r]), sel[-1])
+                layer(l, "deviation", ks, sel)
+        else:
+            for l in range(L):
+                layer(l, wl.score, [fusion.budget(v, pcts[l]) for v in n])
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    runs, t0 = 0, time.perf_counter()
+    while True:
+        one_pass()
+        runs += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
+    n_ctx = int(np.sum(batches[0].n_ctx))
+    return {"value": round(n_ctx * L * runs / dt, 1), "unit": UNIT, "cores": int(threads),
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": f"{runs} full pass(es) over all {L} layers of the {wl.name} batch "
+                      f"({len(batches[0].n_ctx)} request(s), {n_ctx} context tokens), float64 numpy"}
+
+
+def multilayer_work(m):
+    """(name, layer) -> algorithmic work of every call of one multi-layer pass."""
+    out = {}
+    for name, l, _ in m.calls():
+        ly = m.layers[l]
+        w = call_work(ly)
+        if name == "k_probe" and l > 0:            # probe of the previous picks only
+            wl = ly.wl
+            w[name] = ("mfma", 2.0 * wl.hidden * wl.n_kv_heads * wl.head_dim * m.layers[l - 1].M)
+        out[(name, l)] = w[name]
+    return out
+
+
+def _timed_calls_ml(m, steps):
+    """Average duration (ms) of every (call, layer) of a multi-layer pass."""
+    import torch
+    torch.cuda.synchronize()
+    acc = {}
+    for _ in range(steps):
+        m._begin_pass()
+        evs = []
+        for name, l, fn in m.calls():
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            evs.append(((name, l), e0, e1))
+        torch.cuda.synchronize()
+        for key, e0, e1 in evs:
+            acc[key] = acc.get(key, 0.0) + e0.elapsed_time(e1)
+    return {k: v / steps for k, v in acc.items()}
+
+
+def _time_passes(fn, steps):
+    import torch
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
+def main_multilayer(args, wl, ratio):
+    """Several layers per step: `value` is (sum N) x layers / step time."""
+    import numpy as np
+    import torch
+    from rag_kv_cache_kvf_amd import synth
+    from rag_kv_cache_kvf_amd.multilayer import MultiLayerGPU
+    batches = synth.make_layer_batches(wl)
+    m = MultiLayerGPU(batches, ratio)
+    # a streamed pipeline's first passes run slower (about 5 ms instead of
+    # 1.6 ms for 4 layers over the first eight passes): it gets 12 warm-up
+    # passes at least
+    warmup = max(args.warmup, 12 if m.stream_pools else 1)
+    for _ in range(warmup):
+        m.run()
+    torch.cuda.synchronize()
+    sec = _time_passes(m.run, args.steps)
+    pipeline = None
+    if m.stream_pools:
+        # the same layers with the caches resident, and the copies alone; the
+        # per-call kernel times below are taken resident, so that a
+        # re-position call does not include its wait for the copy
+        copy_s = _time_passes(m.run_copies_only, args.steps)
+        m.set_streaming(False)
+        for _ in range(3):
+            m.run()
+        resident = _time_passes(m.run, args.steps)
+        nbytes = m.cache_bytes()
+        pipeline = {
+            "streamed_ms": round(sec * 1e3, 4), "resident_ms": round(resident * 1e3, 4),
+            "copies_ms": round(copy_s * 1e3, 4), "cache_bytes_per_pass": nbytes,
+            "bound": "host link", "achieved_GBps": round(nbytes / sec / 1e9, 2),
+            "copy_only_GBps": round(nbytes / copy_s / 1e9, 2),
+            "peak_GBps": PEAK["pcie"],
+            "frac": round(nbytes / sec / 1e9 / PEAK["pcie"], 4),
+            "hidden_fraction": round(max(0.0, resident + copy_s - sec) / min(resident, copy_s), 4)}
+    per = _timed_calls_ml(m, args.steps)
+    work = multilayer_work(m)
+    n_ctx = int(np.sum(batches[0].n_ctx))
+    L = m.n_layers
+    peak_mfma = PEAK["bf16"] if wl.dtype == "bf16" else PEAK["f32"]
+    # per call name: summed over layers
+    by_name = {}
+    for (name, l), ms in per.items():
+        kind, amount = work[(name, l)]
+        t = by_name.setdefault(name, {"ms": 0.0, "kind": kind, "amount": 0.0, "layers": 0})
+        t["ms"] += ms
+        t["amount"] += amount
+        t["layers"] += 1
+    calls = {}
+    for name, t in by_name.items():
+        ms = t["ms"]
+        if t["kind"] == "hbm":
+            ach, peak, unit = t["amount"] / (ms * 1e-3) / 1e9, PEAK["hbm"], "GB/s"
+        else:
+            ach, peak, unit = t["amount"] / (ms * 1e-3) / 1e12, peak_mfma, "TFLOP/s"
+        calls[name] = {"ms_all_layers": round(ms, 5), "launches": t["layers"], "bound": t["kind"],
+                       "achieved": round(ach, 2), "unit": unit, "frac": round(ach / peak, 4)}
+    dom = max(by_name, key=lambda n: by_name[n]["ms"])
+    kname, ksrc = CALL_KERNEL[dom]
+    if dom == "score" and wl.score == "deviation":
+        kname, ksrc = "deviation_kernel", "kernels/scatter_deviation.hip"
+    c = calls[dom]
+    t = by_name[dom]
+    roofline = {"kernel": kname, "call": dom, "bound": t["kind"], "achieved": c["achieved"],
+                "peak": PEAK["hbm"] if t["kind"] == "hbm" else peak_mfma, "unit": c["unit"],
+                "frac": c["frac"], "avg_ms": round(t["ms"] / t["layers"], 5),
+                "algorithmic_per_launch": t["amount"] / t["layers"],
+                "traffic": _traffic(kname, ksrc, wl.name)}
+    out = {
+        "metric": METRIC,
+        "value": round(n_ctx * L / sec, 1),
+        "unit": UNIT,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": warmup,
+        "ms_per_step": round(sec * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": wl.name, "description": wl.description,
+                   "requests": batches[0].n_req, "context_tokens": n_ctx, "layers": L,
+                   "query_tokens": batches[0].total_rows - n_ctx, "signal": wl.signal or "per-layer",
+                   "score": wl.score, "recompute_ratio_pct": m.pcts,
+                   "score_layers": getattr(m, "score_layers", None),
+                   "streamed_caches": bool(wl.stream_pools)},
+        "roofline": roofline,
+        "calls": calls,
+    }
+    if pipeline is not None:
+        out["pipeline"] = pipeline
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_multilayer(batches, m.pcts)
+    print(json.dumps(out), flush=True)
+
+
 def copy_calibration():
     """A plain 1 GiB device-to-device copy, three times: the HBM byte
     counters read for it scale the counters of the kernels."""
@@ -286,6 +492,9 @@ def main():
 
     wl = synth.get_workload(args.workload)
     ratio = args.ratio if args.ratio is not None else wl.ratio_pct[-1]
+    if wl.n_layers > 1:
+        main_multilayer(args, wl, ratio)
+        return
     batch = synth.make_batch(wl)
     g = FusedLayerGPU(batch, ratio)
     for _ in range(max(args.warmup, 1)):

@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define KVF_ABI_VERSION 5
+#define KVF_ABI_VERSION 6
 #define KVF_MAX_REQ 64      /* requests per call (batch metadata is passed by value) */
 
 typedef enum {
@@ -80,7 +80,11 @@ typedef enum { KVF_F32 = 0, KVF_BF16 = 1 } kvf_dtype;
 typedef enum {
   KVF_SCORE_DEVIATION = 0,   /* [KVB] 4.6.2 Algorithm 2: 1 - mean_h cos(K, K~) */
   KVF_SCORE_ATTN_MASS = 1,   /* [QCF] 3.2.1 Eq. 9-10: query-to-context mass  */
-  KVF_SCORE_KEY_NORM = 2     /* [QCF] 3.3.1 Knorm: L2 norm of the cached key  */
+  KVF_SCORE_KEY_NORM = 2,    /* [QCF] 3.3.1 Knorm: L2 norm of the cached key  */
+  /* flag OR-ed into the mode: add this layer's score to `scores` instead of
+   * overwriting them - I(t) = sum over layers of the per-layer score
+   * ([QCF] 3.2.1 Eq. 10 over all layers, 3.4.2 Eq. 20 over a layer set) */
+  KVF_SCORE_ACCUMULATE = 0x100
 } kvf_score_mode;
 
 enum { KVF_OUT_Q = 1, KVF_OUT_K = 2, KVF_OUT_V = 4 };
@@ -193,7 +197,13 @@ kvf_status kvf_rerotate(const kvf_layer_desc* layer, const kvf_chunk* chunks,
 
 /* ---------------------------------------------------------------------------
  * kvf_score - S2: one fp32 score per context token; scores [sum_r n_ctx[r]]
- * request-major.
+ * request-major.  mode: one of the modes below, optionally OR KVF_SCORE_ACCUMULATE
+ * (scores[t] += this layer's score; a NaN already there stays NaN).
+ * eligible: [sum N] uint8 or NULL.  A position whose byte is 0 is not scored:
+ *   its score is set to NaN, which every selection ranks below all numbers -
+ *   the candidate set of CacheBlend's layer-by-layer filtering ([QCF] 2.2.1):
+ *   only the previous layer's picks stay in play.  Deviation and key norm
+ *   skip the ineligible rows' loads (their k_fresh rows need not exist).
  * KVF_SCORE_DEVIATION ([KVB] 4.6.2 Algorithm 2, one layer):
  *   score_t = 1 - (1/Hkv) sum_h cos(fused_k[t, h], k_fresh[t, h]),
  *   cos := 0 when either norm is 0.  fused_k and k_fresh are [sum T, Hkv, d]
@@ -219,8 +229,8 @@ kvf_status kvf_rerotate(const kvf_layer_desc* layer, const kvf_chunk* chunks,
 kvf_status kvf_score(kvf_score_mode mode, const kvf_layer_desc* layer,
                      const kvf_batch* batch, const void* fused_k,
                      const void* k_fresh, const void* q_u, int32_t n_last_q,
-                     float* scores, void* workspace, size_t ws_bytes,
-                     void* stream);
+                     const uint8_t* eligible, float* scores, void* workspace,
+                     size_t ws_bytes, void* stream);
 size_t kvf_score_workspace_size(kvf_score_mode mode, const kvf_layer_desc* layer,
                                 const kvf_batch* batch, int32_t n_last_q);
 
@@ -238,13 +248,16 @@ size_t kvf_score_workspace_size(kvf_score_mode mode, const kvf_layer_desc* layer
  *            P_r followed by the request's query rows, i.e. the rows to
  *            recompute, ascending per request.
  *   out_pos  [sum (k_r + U_r)] (may be NULL): the matching positions.
+ *   out_mask [sum N] uint8 (may be NULL): 1 at the picks, 0 at every other
+ *            context position (the next layer's `eligible` set in
+ *            kvf_score).
  * Needs kvf_select_workspace_size() bytes of workspace (0 today; the
  * argument is reserved).
  */
 kvf_status kvf_select_topk(const float* scores, const uint8_t* forced,
                            const kvf_batch* batch,
                            const int32_t* k_per_req, int32_t* out_idx,
-                           int32_t* out_rows, int32_t* out_pos,
+                           int32_t* out_rows, int32_t* out_pos, uint8_t* out_mask,
                            void* workspace, size_t ws_bytes, void* stream);
 size_t kvf_select_workspace_size(const kvf_batch* batch);
 

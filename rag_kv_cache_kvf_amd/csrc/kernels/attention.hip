@@ -786,7 +786,7 @@ struct MassArgs {
   // Arrival counters (zero between calls): the last column-sum workgroup of
   // a key tile adds the kv heads.
   int* cnt_cols;                 // [total_ktiles]
-  float* scores;                 // [sum N]
+  ScoreOut out;                  // scores [sum N]
 };
 
 // Relaxed device-scope atomics: coherent across the XCDs' L2 caches without
@@ -1059,7 +1059,7 @@ __global__ void __launch_bounds__(256) mass_colsum_bf16_kernel(MassArgs a) {
       for (int u = 0; u < 8; ++u)
         if (g0 + u < a.hkv) sum += pv8[u];
     }
-    a.scores[j] = sum;
+    store_score(a.out, j, sum);
   }
 }
 
@@ -1089,12 +1089,12 @@ __global__ void __launch_bounds__(256) mass_colsum_f32_kernel(MassArgs a, int d)
 }
 
 __global__ void __launch_bounds__(256) head_sum_kernel(const float* __restrict__ part, int hkv,
-                                                       int n, float* __restrict__ scores) {
+                                                       int n, ScoreOut out) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n) return;
   float s = 0.f;
   for (int g = 0; g < hkv; ++g) s += part[static_cast<int64_t>(g) * n + i];
-  scores[i] = s;
+  store_score(out, i, s);
 }
 
 namespace {
@@ -1148,7 +1148,7 @@ size_t attn_mass_workspace(const kvf_layer_desc& L, const BatchArgs& B, int n_la
 }
 
 hipError_t launch_attn_mass(const kvf_layer_desc& L, const BatchArgs& B, const void* fk,
-                            const void* q_u, int n_last_q, float* scores, void* ws,
+                            const void* q_u, int n_last_q, const ScoreOut& out, void* ws,
                             size_t ws_bytes, hipStream_t st) {
   const MassLayout lay = mass_layout(L, B, n_last_q);
   if (ws_bytes < lay.total) return hipErrorInvalidValue;
@@ -1189,13 +1189,13 @@ hipError_t launch_attn_mass(const kvf_layer_desc& L, const BatchArgs& B, const v
   m.G = G;
   m.scale_log2 = scale_log2;
   m.cnt_cols = cnt;
-  m.scores = scores;
+  m.out = out;
   const int n = B.cu_N[B.n_req];
   if (plane == 0) {
     // no query rows: every key gets zero mass
     if (n > 0) {
       hipLaunchKernelGGL(head_sum_kernel, dim3(ceil_div(n, 256)), dim3(256), 0, st, part, 0, n,
-                         scores);
+                         out);
     }
     return hipGetLastError();
   }
@@ -1257,7 +1257,7 @@ hipError_t launch_attn_mass(const kvf_layer_desc& L, const BatchArgs& B, const v
   // (bf16: the column-sum pass added the heads)
   if (L.dtype != KVF_BF16)
     hipLaunchKernelGGL(head_sum_kernel, dim3(ceil_div(n, 256)), dim3(256), 0, st, part, L.n_kv_heads,
-                       n, scores);
+                       n, out);
   return hipGetLastError();
 }
 

@@ -93,11 +93,15 @@ hipError_t launch_scatter(const kvf_layer_desc& L, const void* ks, const int32_t
 template <typename T>
 __global__ void __launch_bounds__(256) deviation_kernel(BatchArgs B, const T* __restrict__ fk,
                                                         const T* __restrict__ kf, int hkv, int d,
-                                                        float* __restrict__ scores) {
+                                                        ScoreOut out) {
   const int wave = (blockIdx.x * blockDim.x + threadIdx.x) / kWave;
   const int lane = threadIdx.x & (kWave - 1);
   const int total = B.cu_N[B.n_req];
   if (wave >= total) return;
+  if (!score_eligible(out, wave)) {             // the whole wave: one token
+    if (lane == 0) store_score(out, wave, 0.f);
+    return;
+  }
   const int r = find_segment(B.cu_N, B.n_req, wave);
   const int64_t row = B.cu_T[r] + (wave - B.cu_N[r]);
   const int row_elems = hkv * d;
@@ -124,21 +128,21 @@ __global__ void __launch_bounds__(256) deviation_kernel(BatchArgs B, const T* __
   }
   // lanes past the row end still take part in the shuffles above with zeros
   cos_acc = wave_sum(cos_acc);
-  if (lane == 0) scores[wave] = 1.f - cos_acc / static_cast<float>(hkv);
+  if (lane == 0) store_score(out, wave, 1.f - cos_acc / static_cast<float>(hkv));
 }
 
 hipError_t launch_deviation(const kvf_layer_desc& L, const BatchArgs& B, const void* fk,
-                            const void* kf, float* scores, hipStream_t st) {
+                            const void* kf, const ScoreOut& out, hipStream_t st) {
   const int total = B.cu_N[B.n_req];
   const int blocks = ceil_div(total, 256 / kWave);
   if (L.dtype == KVF_BF16)
     hipLaunchKernelGGL(deviation_kernel<bf16_t>, dim3(blocks), dim3(256), 0, st, B,
                        static_cast<const bf16_t*>(fk), static_cast<const bf16_t*>(kf),
-                       L.n_kv_heads, L.head_dim, scores);
+                       L.n_kv_heads, L.head_dim, out);
   else
     hipLaunchKernelGGL(deviation_kernel<float>, dim3(blocks), dim3(256), 0, st, B,
                        static_cast<const float*>(fk), static_cast<const float*>(kf),
-                       L.n_kv_heads, L.head_dim, scores);
+                       L.n_kv_heads, L.head_dim, out);
   return hipGetLastError();
 }
 
@@ -147,11 +151,15 @@ hipError_t launch_deviation(const kvf_layer_desc& L, const BatchArgs& B, const v
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ void __launch_bounds__(256) key_norm_kernel(BatchArgs B, const T* __restrict__ fk,
-                                                       int row_elems, float* __restrict__ scores) {
+                                                       int row_elems, ScoreOut out) {
   const int wave = (blockIdx.x * blockDim.x + threadIdx.x) / kWave;
   const int lane = threadIdx.x & (kWave - 1);
   const int total = B.cu_N[B.n_req];
   if (wave >= total) return;
+  if (!score_eligible(out, wave)) {
+    if (lane == 0) store_score(out, wave, 0.f);
+    return;
+  }
   const int r = find_segment(B.cu_N, B.n_req, wave);
   const int64_t row = B.cu_T[r] + (wave - B.cu_N[r]);
   const T* a = fk + row * row_elems;
@@ -163,20 +171,20 @@ __global__ void __launch_bounds__(256) key_norm_kernel(BatchArgs B, const T* __r
     for (int i = 0; i < 8; ++i) ss = fmaf(x[i], x[i], ss);
   }
   ss = wave_sum(ss);
-  if (lane == 0) scores[wave] = sqrtf(ss);
+  if (lane == 0) store_score(out, wave, sqrtf(ss));
 }
 
 hipError_t launch_key_norm(const kvf_layer_desc& L, const BatchArgs& B, const void* fk,
-                           float* scores, hipStream_t st) {
+                           const ScoreOut& out, hipStream_t st) {
   const int total = B.cu_N[B.n_req];
   const int blocks = ceil_div(total, 256 / kWave);
   const int row_elems = L.n_kv_heads * L.head_dim;
   if (L.dtype == KVF_BF16)
     hipLaunchKernelGGL(key_norm_kernel<bf16_t>, dim3(blocks), dim3(256), 0, st, B,
-                       static_cast<const bf16_t*>(fk), row_elems, scores);
+                       static_cast<const bf16_t*>(fk), row_elems, out);
   else
     hipLaunchKernelGGL(key_norm_kernel<float>, dim3(blocks), dim3(256), 0, st, B,
-                       static_cast<const float*>(fk), row_elems, scores);
+                       static_cast<const float*>(fk), row_elems, out);
   return hipGetLastError();
 }
 

@@ -90,10 +90,12 @@ struct SelectLds {
 // The k largest keys of positions [0, N) with ties to the lower position;
 // emit(o, i) is called for the o-th chosen position i, o ascending with i.
 // sc == nullptr ranks every unforced position equal (lowest positions win).
+// mask (optional): mask[i] = 1 for chosen positions, 0 for the others.
 template <int NT, int CACHE, typename Emit>
 __device__ __forceinline__ void select_block(const float* __restrict__ sc,
                                              const uint8_t* __restrict__ forced, int N, int k,
-                                             SelectLds<NT, CACHE>& s, Emit emit) {
+                                             SelectLds<NT, CACHE>& s, uint8_t* __restrict__ mask,
+                                             Emit emit) {
   const int tid = threadIdx.x;
   auto key_of = [&](int i) __attribute__((always_inline)) -> uint32_t {
     if (forced && forced[i]) return kForcedKey;
@@ -194,11 +196,13 @@ __device__ __forceinline__ void select_block(const float* __restrict__ sc,
   const int eq_base = block_exclusive_scan<NT>(n_eq, s.wave, &tot);
   const int take = max(0, min(n_eq, need - eq_base));
   const int out_base = block_exclusive_scan<NT>(n_gt + take, s.wave, &tot);
-  if (k > 0) {
+  if (k > 0 || mask) {
     int o = out_base, eq_seen = 0;
     for (int i = s0; i < s1; ++i) {
       bool sel;
-      if (k == N) {
+      if (k == 0) {
+        sel = false;
+      } else if (k == N) {
         sel = true;
       } else {
         const uint32_t key = key_at(i);
@@ -208,6 +212,7 @@ __device__ __forceinline__ void select_block(const float* __restrict__ sc,
           ++eq_seen;
         }
       }
+      if (mask) mask[i] = sel ? 1 : 0;
       if (sel) emit(o++, i);
     }
   }
@@ -217,7 +222,8 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(TopkArgs a, const fl
                                                             const uint8_t* __restrict__ forced,
                                                             int32_t* __restrict__ out_idx,
                                                             int32_t* __restrict__ out_rows,
-                                                            int32_t* __restrict__ out_pos) {
+                                                            int32_t* __restrict__ out_pos,
+                                                            uint8_t* __restrict__ out_mask) {
   __shared__ SelectLds<kTopkThreads, kTopkCache> lds;
   const int r = blockIdx.x;
   const int N = a.b.n_ctx[r];
@@ -230,7 +236,7 @@ __global__ void __launch_bounds__(kTopkThreads) topk_kernel(TopkArgs a, const fl
   int32_t* opos = out_pos ? out_pos + a.cu_m[r] : nullptr;
   select_block<kTopkThreads, kTopkCache>(
       scores ? scores + a.b.cu_N[r] : nullptr, forced ? forced + a.b.cu_N[r] : nullptr, N, k, lds,
-      [&](int o, int i) __attribute__((always_inline)) {
+      out_mask ? out_mask + a.b.cu_N[r] : nullptr, [&](int o, int i) __attribute__((always_inline)) {
         if (oi) oi[o] = i;
         if (orow) {
           orow[o] = row0 + i;
@@ -277,7 +283,7 @@ __global__ void __launch_bounds__(kSegThreads) topk_segmented_kernel(
   int32_t* orow = out_rows ? out_rows + a.cu_m[r] + g.out_off : nullptr;
   int32_t* opos = out_pos ? out_pos + a.cu_m[r] + g.out_off : nullptr;
   select_block<kSegThreads, kSegCache>(
-      scores ? scores + base : nullptr, forced ? forced + base : nullptr, g.len, g.k, lds,
+      scores ? scores + base : nullptr, forced ? forced + base : nullptr, g.len, g.k, lds, nullptr,
       [&](int o, int i) __attribute__((always_inline)) {
         if (oi) oi[o] = g.pos0 + i;
         if (orow) {
@@ -300,9 +306,9 @@ static TopkArgs topk_args(const BatchArgs& B, const int32_t* k_host) {
 
 hipError_t launch_topk(const float* scores, const uint8_t* forced, const BatchArgs& B,
                        const int32_t* k_host, int32_t* out_idx, int32_t* out_rows,
-                       int32_t* out_pos, hipStream_t st) {
+                       int32_t* out_pos, uint8_t* out_mask, hipStream_t st) {
   hipLaunchKernelGGL(topk_kernel, dim3(B.n_req), dim3(kTopkThreads), 0, st, topk_args(B, k_host),
-                     scores, forced, out_idx, out_rows, out_pos);
+                     scores, forced, out_idx, out_rows, out_pos, out_mask);
   return hipGetLastError();
 }
 

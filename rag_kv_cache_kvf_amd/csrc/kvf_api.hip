@@ -187,7 +187,7 @@ kvf_status kvf_kivi8_encode(const kvf_layer_desc* layer, const void* pool_k, con
 size_t kvf_score_workspace_size(kvf_score_mode mode, const kvf_layer_desc* layer,
                                 const kvf_batch* batch, int32_t n_last_q) {
   try {
-    if (mode != KVF_SCORE_ATTN_MASS) return 0;
+    if ((static_cast<int>(mode) & ~KVF_SCORE_ACCUMULATE) != KVF_SCORE_ATTN_MASS) return 0;
     kvf::BatchArgs B;
     if (check_layer(layer) != KVF_OK || check_batch(batch, &B) != KVF_OK) return 0;
     return kvf::attn_mass_workspace(*layer, B, n_last_q);
@@ -196,31 +196,38 @@ size_t kvf_score_workspace_size(kvf_score_mode mode, const kvf_layer_desc* layer
   }
 }
 
-kvf_status kvf_score(kvf_score_mode mode, const kvf_layer_desc* layer, const kvf_batch* batch,
-                     const void* fused_k, const void* k_fresh, const void* q_u, int32_t n_last_q,
-                     float* scores, void* workspace, size_t ws_bytes, void* stream) {
+kvf_status kvf_score(kvf_score_mode mode_flags, const kvf_layer_desc* layer,
+                     const kvf_batch* batch, const void* fused_k, const void* k_fresh,
+                     const void* q_u, int32_t n_last_q, const uint8_t* eligible, float* scores,
+                     void* workspace, size_t ws_bytes, void* stream) {
   KVF_GUARD_BEGIN
   kvf_status st = check_layer(layer);
   if (st != KVF_OK) return st;
   kvf::BatchArgs B;
   st = check_batch(batch, &B);
   if (st != KVF_OK) return st;
+  const int flags = static_cast<int>(mode_flags);
+  KVF_CHECK((flags & ~(0xff | KVF_SCORE_ACCUMULATE)) == 0, KVF_ERR_INVALID_ARG,
+            "unknown score flags 0x%x", flags);
+  const int mode = flags & 0xff;
+  KVF_CHECK(mode == KVF_SCORE_DEVIATION || mode == KVF_SCORE_ATTN_MASS ||
+                mode == KVF_SCORE_KEY_NORM, KVF_ERR_INVALID_ARG, "unknown score mode %d", mode);
   if (B.cu_N[B.n_req] == 0) return KVF_OK;
   KVF_CHECK(fused_k && scores, KVF_ERR_INVALID_ARG, "required pointer is NULL");
+  const kvf::ScoreOut out{scores, eligible, (flags & KVF_SCORE_ACCUMULATE) ? 1 : 0};
   if (mode == KVF_SCORE_DEVIATION) {
     KVF_CHECK(k_fresh != nullptr, KVF_ERR_INVALID_ARG, "k_fresh is NULL");
-    return from_hip(kvf::launch_deviation(*layer, B, fused_k, k_fresh, scores,
-                                          as_stream(stream)), "kvf_score(deviation)");
+    return from_hip(kvf::launch_deviation(*layer, B, fused_k, k_fresh, out, as_stream(stream)),
+                    "kvf_score(deviation)");
   }
   if (mode == KVF_SCORE_KEY_NORM)
-    return from_hip(kvf::launch_key_norm(*layer, B, fused_k, scores, as_stream(stream)),
+    return from_hip(kvf::launch_key_norm(*layer, B, fused_k, out, as_stream(stream)),
                     "kvf_score(key_norm)");
-  KVF_CHECK(mode == KVF_SCORE_ATTN_MASS, KVF_ERR_INVALID_ARG, "unknown score mode %d", mode);
   KVF_CHECK(q_u != nullptr, KVF_ERR_INVALID_ARG, "q_u is NULL");
   const size_t need = kvf::attn_mass_workspace(*layer, B, n_last_q);
   KVF_CHECK(ws_bytes >= need, KVF_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);
   KVF_CHECK(need == 0 || workspace != nullptr, KVF_ERR_WORKSPACE, "workspace is NULL");
-  return from_hip(kvf::launch_attn_mass(*layer, B, fused_k, q_u, n_last_q, scores, workspace,
+  return from_hip(kvf::launch_attn_mass(*layer, B, fused_k, q_u, n_last_q, out, workspace,
                                         ws_bytes, as_stream(stream)), "kvf_score(attn_mass)");
   KVF_GUARD_END
 }
@@ -232,7 +239,8 @@ size_t kvf_select_workspace_size(const kvf_batch* batch) {
 
 kvf_status kvf_select_topk(const float* scores, const uint8_t* forced, const kvf_batch* batch,
                            const int32_t* k_per_req, int32_t* out_idx, int32_t* out_rows,
-                           int32_t* out_pos, void* workspace, size_t ws_bytes, void* stream) {
+                           int32_t* out_pos, uint8_t* out_mask, void* workspace, size_t ws_bytes,
+                           void* stream) {
   KVF_GUARD_BEGIN
   (void)workspace;
   (void)ws_bytes;
@@ -247,12 +255,12 @@ kvf_status kvf_select_topk(const float* scores, const uint8_t* forced, const kvf
     total_k += k_per_req[r];
     total_m += k_per_req[r] + (B.cu_T[r + 1] - B.cu_T[r] - B.n_ctx[r]);
   }
-  if (total_m == 0) return KVF_OK;
+  if (total_m == 0 && (out_mask == nullptr || B.cu_N[B.n_req] == 0)) return KVF_OK;
   KVF_CHECK(total_k == 0 || out_idx, KVF_ERR_INVALID_ARG, "out_idx is NULL");
   KVF_CHECK((out_rows == nullptr) == (out_pos == nullptr), KVF_ERR_INVALID_ARG,
             "out_rows and out_pos must both be given or both be NULL");
   return from_hip(kvf::launch_topk(scores, forced, B, k_per_req, out_idx, out_rows, out_pos,
-                                   as_stream(stream)), "kvf_select_topk");
+                                   out_mask, as_stream(stream)), "kvf_select_topk");
   KVF_GUARD_END
 }
 

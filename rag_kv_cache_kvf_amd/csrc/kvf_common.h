@@ -125,6 +125,25 @@ __device__ __forceinline__ int find_segment(const int* cu, int n, int i) {
 
 __host__ __device__ constexpr int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
+// Where a score kernel writes.  A position whose eligibility byte is 0 gets
+// NaN (ranked below every score by the selection); with `acc` the score is
+// added to the value already there (scores summed over layers).
+struct ScoreOut {
+  float* scores;                // [sum N]
+  const uint8_t* elig;          // [sum N] or nullptr (every position eligible)
+  int acc;
+};
+__device__ __forceinline__ bool score_eligible(const ScoreOut& o, int64_t j) {
+  return o.elig == nullptr || o.elig[j] != 0;
+}
+__device__ __forceinline__ void store_score(const ScoreOut& o, int64_t j, float v) {
+  if (!score_eligible(o, j)) {
+    o.scores[j] = __builtin_nanf("");
+    return;
+  }
+  o.scores[j] = o.acc ? o.scores[j] + v : v;
+}
+
 }  // namespace kvf
 
 // ---------------------------------------------------------------------------
@@ -140,16 +159,16 @@ hipError_t launch_kivi8_encode(const kvf_layer_desc& L, const void* pk, const vo
                                const int32_t* pool_cu, int n_pool, int64_t pool_rows,
                                int max_len, const kvf_kivi8& out, hipStream_t st);
 hipError_t launch_deviation(const kvf_layer_desc& L, const BatchArgs& B, const void* fk,
-                            const void* kf, float* scores, hipStream_t st);
+                            const void* kf, const ScoreOut& out, hipStream_t st);
 hipError_t launch_attn_mass(const kvf_layer_desc& L, const BatchArgs& B, const void* fk,
-                            const void* q_u, int n_last_q, float* scores, void* ws,
+                            const void* q_u, int n_last_q, const ScoreOut& out, void* ws,
                             size_t ws_bytes, hipStream_t st);
 size_t attn_mass_workspace(const kvf_layer_desc& L, const BatchArgs& B, int n_last_q);
 hipError_t launch_key_norm(const kvf_layer_desc& L, const BatchArgs& B, const void* fk,
-                           float* scores, hipStream_t st);
+                           const ScoreOut& out, hipStream_t st);
 hipError_t launch_topk(const float* scores, const uint8_t* forced, const BatchArgs& B,
                        const int32_t* k_host, int32_t* out_idx, int32_t* out_rows,
-                       int32_t* out_pos, hipStream_t st);
+                       int32_t* out_pos, uint8_t* out_mask, hipStream_t st);
 hipError_t launch_topk_segmented(const float* scores, const uint8_t* forced, const BatchArgs& B,
                                  const kvf_segment* segs, int n_segs, const int32_t* k_host,
                                  int32_t* out_idx, int32_t* out_rows, int32_t* out_pos,

@@ -20,6 +20,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvfuse.
 KVF_OK, KVF_ERR_INVALID_ARG, KVF_ERR_UNSUPPORTED, KVF_ERR_WORKSPACE, KVF_ERR_HIP = range(5)
 KVF_F32, KVF_BF16 = 0, 1
 KVF_SCORE_DEVIATION, KVF_SCORE_ATTN_MASS, KVF_SCORE_KEY_NORM = 0, 1, 2
+KVF_SCORE_ACCUMULATE = 0x100
 KVF_OUT_Q, KVF_OUT_K, KVF_OUT_V = 1, 2, 4
 KVF_MAX_REQ = 64
 
@@ -76,9 +77,9 @@ _SIGS = {
     "kvf_rope_table": (_I32, [ctypes.c_double, _I32, _I32, _P, _P, _P]),
     "kvf_rerotate": (_I32, [_LP, _P, _I32, _I32, _P, _P, ctypes.POINTER(Kivi8Desc), _I64, _P, _P,
                             _I32, _P, _P, _I64, _P]),
-    "kvf_score": (_I32, [_I32, _LP, _BP, _P, _P, _P, _I32, _P, _P, _SZ, _P]),
+    "kvf_score": (_I32, [_I32, _LP, _BP, _P, _P, _P, _I32, _P, _P, _P, _SZ, _P]),
     "kvf_score_workspace_size": (_SZ, [_I32, _LP, _BP, _I32]),
-    "kvf_select_topk": (_I32, [_P, _P, _BP, _IP, _P, _P, _P, _P, _SZ, _P]),
+    "kvf_select_topk": (_I32, [_P, _P, _BP, _IP, _P, _P, _P, _P, _P, _SZ, _P]),
     "kvf_select_topk_segmented": (_I32, [_P, _P, _BP, _P, _I32, _IP, _P, _P, _P, _P]),
     "kvf_select_static": (_I32, [_BP, _P, _I32, ctypes.POINTER(StaticRules), _P, _P]),
     "kvf_static_counts": (_I32, [_BP, _P, _I32, ctypes.POINTER(StaticRules), _IP]),
@@ -226,23 +227,27 @@ def score_workspace_size(mode: int, layer: Layer, batch: Batch, n_last_q: int = 
 
 def score(mode: int, layer: Layer, batch: Batch, fused_k: torch.Tensor,
           k_fresh: Optional[torch.Tensor], q_u: Optional[torch.Tensor], scores: torch.Tensor,
-          workspace: Optional[torch.Tensor] = None, n_last_q: int = 0, stream=None):
+          workspace: Optional[torch.Tensor] = None, n_last_q: int = 0,
+          eligible: Optional[torch.Tensor] = None, accumulate: bool = False, stream=None):
+    """eligible: uint8 [sum N] (0 = not scored, NaN); accumulate: add to scores."""
     d = layer.desc()
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(_lib.kvf_score(mode, ctypes.byref(d), ctypes.byref(batch.desc), _ptr(fused_k),
-                          _ptr(k_fresh), _ptr(q_u), n_last_q, _ptr(scores), _ptr(workspace),
-                          ws_bytes, _stream(stream)), "kvf_score")
+    flags = mode | (KVF_SCORE_ACCUMULATE if accumulate else 0)
+    _check(_lib.kvf_score(flags, ctypes.byref(d), ctypes.byref(batch.desc), _ptr(fused_k),
+                          _ptr(k_fresh), _ptr(q_u), n_last_q, _ptr(eligible), _ptr(scores),
+                          _ptr(workspace), ws_bytes, _stream(stream)), "kvf_score")
 
 
 def select_topk(scores: Optional[torch.Tensor], batch: Batch, k_per_req: Sequence[int],
                 out_idx: torch.Tensor, out_rows: Optional[torch.Tensor] = None,
                 out_pos: Optional[torch.Tensor] = None, forced: Optional[torch.Tensor] = None,
-                stream=None):
-    """forced: uint8 [sum N] mask of positions ranked above every score."""
+                out_mask: Optional[torch.Tensor] = None, stream=None):
+    """forced: uint8 [sum N] mask of positions ranked above every score;
+    out_mask: uint8 [sum N], 1 at the picks."""
     ka = _int_array(k_per_req)
     _check(_lib.kvf_select_topk(_ptr(scores), _ptr(forced), ctypes.byref(batch.desc), ka,
-                                _ptr(out_idx), _ptr(out_rows), _ptr(out_pos), None, 0,
-                                _stream(stream)),
+                                _ptr(out_idx), _ptr(out_rows), _ptr(out_pos), _ptr(out_mask),
+                                None, 0, _stream(stream)),
            "kvf_select_topk")
 
 

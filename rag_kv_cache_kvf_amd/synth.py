@@ -57,6 +57,18 @@ class Workload:
     selector: str = "score"
     static_rules: tuple = (0, 0, 0)     # (sink, boundary, seam)
     anchor_pct: int = 0
+    # several layers, each with its own weights, hidden states and per-chunk
+    # caches (drawn independently).  signal: "" (every layer selects on its
+    # own score), "sum" (one selection for all layers from the score summed
+    # over score_layers, all layers when empty) or "progressive" (layer l
+    # keeps progressive_pct[l] % of N out of layer l-1's picks).
+    # stream_pools: the per-chunk caches stay in pinned host memory and every
+    # layer's cache is copied in on a second stream while earlier layers run.
+    n_layers: int = 1
+    signal: str = ""
+    score_layers: tuple = ()
+    progressive_pct: tuple = ()
+    stream_pools: bool = False
 
     @property
     def n_chunks(self) -> int:
@@ -114,6 +126,38 @@ WORKLOADS = {
         selector="anchor", anchor_pct=10,
         description="Qwen3-8B-shaped layer, bf16, 1 request of 10x512 + 64 query, "
                     "per-chunk key-norm anchors (r_a = 10%) as the recompute set"),
+    # Several Qwen3-8B-shaped layers over the headline request: the attention
+    # mass summed over all 4 layers (ProphetKV's full view), over 3 of 8
+    # layers (QCFuse's critical set), CacheBlend's filtering over 3 layers,
+    # and 4 independent layers whose caches stream in from host memory.
+    "qwen3_8b_prophet4": _wl(
+        name="qwen3_8b_prophet4", dtype="bf16", n_req=1, chunk_lens=(512,) * 10,
+        n_query=(64,), hidden=4096, n_q_heads=32, n_kv_heads=8, head_dim=128,
+        rope_base=1e6, score="attn_mass", ratio_pct=(30,), sigma=0.1,
+        n_layers=4, signal="sum",
+        description="4 Qwen3-8B-shaped layers, bf16, 1 request of 10x512 + 64 query, "
+                    "one selection from the attention mass summed over all 4 layers"),
+    "qwen3_8b_critical3": _wl(
+        name="qwen3_8b_critical3", dtype="bf16", n_req=1, chunk_lens=(512,) * 10,
+        n_query=(64,), hidden=4096, n_q_heads=32, n_kv_heads=8, head_dim=128,
+        rope_base=1e6, score="attn_mass", ratio_pct=(30,), sigma=0.1,
+        n_layers=8, signal="sum", score_layers=(3, 4, 5),
+        description="8 Qwen3-8B-shaped layers, bf16, 1 request of 10x512 + 64 query, "
+                    "one selection from the attention mass summed over layers 3-5"),
+    "qwen3_8b_dev_progressive": _wl(
+        name="qwen3_8b_dev_progressive", dtype="bf16", n_req=1, chunk_lens=(512,) * 10,
+        n_query=(64,), hidden=4096, n_q_heads=32, n_kv_heads=8, head_dim=128,
+        rope_base=1e6, score="deviation", ratio_pct=(30,), sigma=0.1,
+        n_layers=3, signal="progressive", progressive_pct=(50, 40, 30),
+        description="3 Qwen3-8B-shaped layers, bf16, 1 request of 10x512 + 64 query, "
+                    "deviation candidates narrowed 50% -> 40% -> 30% layer by layer"),
+    "qwen3_8b_mass_stream4": _wl(
+        name="qwen3_8b_mass_stream4", dtype="bf16", n_req=1, chunk_lens=(512,) * 10,
+        n_query=(64,), hidden=4096, n_q_heads=32, n_kv_heads=8, head_dim=128,
+        rope_base=1e6, score="attn_mass", ratio_pct=(30,), sigma=0.1,
+        n_layers=4, stream_pools=True,
+        description="4 Qwen3-8B-shaped layers, bf16, 1 request of 10x512 + 64 query, "
+                    "per-chunk caches streamed from pinned host memory layer by layer"),
     # Qwen2.5-3B-shaped layer, int8 KIVI cache, 16 requests of 24 x 128 + 64.
     "qwen25_3b_kivi8": _wl(
         name="qwen25_3b_kivi8", dtype="bf16", n_req=16, chunk_lens=(128,) * 24,
@@ -159,6 +203,21 @@ MINI_WORKLOADS = {
         n_query=(21,), hidden=384, n_q_heads=4, n_kv_heads=4, head_dim=128,
         rope_base=1e6, score="deviation", ratio_pct=(30,), sigma=0.1,
         pool_chunks=6, static_rules=(4, 1, 0)),
+    "mini_bf16_mass_sum3": _wl(
+        name="mini_bf16_mass_sum3", dtype="bf16", n_req=2, chunk_lens=(97, 130, 64, 33),
+        n_query=(19, 40), hidden=512, n_q_heads=8, n_kv_heads=2, head_dim=128,
+        rope_base=1e6, score="attn_mass", ratio_pct=(30,), sigma=0.1,
+        n_layers=4, signal="sum", score_layers=(1, 3)),
+    "mini_bf16_dev_progressive": _wl(
+        name="mini_bf16_dev_progressive", dtype="bf16", n_req=3, chunk_lens=(70, 70, 70, 70),
+        n_query=(21,), hidden=384, n_q_heads=4, n_kv_heads=4, head_dim=128,
+        rope_base=1e6, score="deviation", ratio_pct=(30,), sigma=0.1,
+        pool_chunks=6, n_layers=3, signal="progressive", progressive_pct=(60, 45, 30)),
+    "mini_bf16_mass_stream": _wl(
+        name="mini_bf16_mass_stream", dtype="bf16", n_req=2, chunk_lens=(97, 130, 64, 33),
+        n_query=(19, 40), hidden=512, n_q_heads=8, n_kv_heads=2, head_dim=128,
+        rope_base=1e6, score="attn_mass", ratio_pct=(30,), sigma=0.1,
+        n_layers=5, stream_pools=True),
     "mini_f32_mass": _wl(
         name="mini_f32_mass", dtype="f32", n_req=2, chunk_lens=(40, 23, 64),
         n_query=(9, 30), hidden=128, n_q_heads=4, n_kv_heads=2, head_dim=64,
@@ -283,6 +342,20 @@ def _chunk_ids(wl: Workload, r: int) -> List[int]:
         perm = _rng(wl.seed, "pool_permutation", r).permutation(wl.pool_chunks)
         return [int(c) for c in perm[: wl.n_chunks]]
     return [r * wl.n_chunks + s for s in range(wl.n_chunks)]
+
+
+def layer_seed(wl: Workload, layer: int) -> int:
+    """Seed of layer `layer` of a multi-layer workload (layer 0 keeps the
+    workload's own seed, so it is the one-layer batch)."""
+    return wl.seed + 1000003 * layer
+
+
+def make_layer_batches(wl: Workload | str) -> List["Batch"]:
+    """One batch per layer: the same request layout, independent weights,
+    hidden states and per-chunk caches."""
+    if isinstance(wl, str):
+        wl = get_workload(wl)
+    return [make_batch(wl, seed=layer_seed(wl, l)) for l in range(wl.n_layers)]
 
 
 def make_batch(wl: Workload | str, seed: Optional[int] = None) -> Batch:

@@ -48,7 +48,7 @@ def test_status_strings_and_version(lib):
     lib.kvf_status_string.restype = ctypes.c_char_p
     assert lib.kvf_status_string(0) == b"KVF_OK"
     assert lib.kvf_status_string(2) == b"KVF_ERR_UNSUPPORTED"
-    assert lib.kvf_abi_version() == 5
+    assert lib.kvf_abi_version() == 6
 
 
 def test_budget_matches_oracle(lib):
@@ -123,14 +123,24 @@ def test_validation_errors(lib):
     assert lib.kvf_recompute_workspace_size(None, 64, 7) == 0
     # batch checks
     b, keep = _batch([0, 10, 5], [4, 2])
-    assert lib.kvf_score(0, ctypes.byref(ok), ctypes.byref(b), FAKE, FAKE, None, 0, FAKE, None, 0,
+    assert lib.kvf_score(0, ctypes.byref(ok), ctypes.byref(b), FAKE, FAKE, None, 0, None, FAKE, None, 0,
                          None) == 1
     b, keep = _batch([0, 10], [11])
-    assert lib.kvf_score(0, ctypes.byref(ok), ctypes.byref(b), FAKE, FAKE, None, 0, FAKE, None, 0,
+    assert lib.kvf_score(0, ctypes.byref(ok), ctypes.byref(b), FAKE, FAKE, None, 0, None, FAKE, None, 0,
                          None) == 1
-    # attention mass needs a workspace
+    # unknown score modes and flag bits
     b, keep = _batch([0, 10], [6])
-    assert lib.kvf_score(1, ctypes.byref(ok), ctypes.byref(b), FAKE, None, FAKE, 0, FAKE, None, 0,
+    for mode in (3, 0x200, 0x101 | 0x1000):
+        assert lib.kvf_score(mode, ctypes.byref(ok), ctypes.byref(b), FAKE, FAKE, FAKE, 0, None,
+                             FAKE, None, 0, None) == 1
+    lib.kvf_score_workspace_size.restype = ctypes.c_size_t
+    assert lib.kvf_score_workspace_size(1 | 0x100, ctypes.byref(ok), ctypes.byref(b), 0) == \
+        lib.kvf_score_workspace_size(1, ctypes.byref(ok), ctypes.byref(b), 0) > 0
+    assert lib.kvf_score_workspace_size(0 | 0x100, ctypes.byref(ok), ctypes.byref(b), 0) == 0
+    # attention mass needs a workspace (also when accumulating)
+    assert lib.kvf_score(1 | 0x100, ctypes.byref(ok), ctypes.byref(b), FAKE, None, FAKE, 0, None,
+                         FAKE, None, 0, None) == 3
+    assert lib.kvf_score(1, ctypes.byref(ok), ctypes.byref(b), FAKE, None, FAKE, 0, None, FAKE, None, 0,
                          None) == 3
     # attention: the key-split workspace exists only for small bf16 grids and
     # a non-NULL workspace must be large enough
@@ -153,12 +163,12 @@ def test_validation_errors(lib):
                                       FAKE, 0.088, FAKE, None, None, 0, None) == 1
     # top-k: k > N
     k = (ctypes.c_int32 * 1)(7)
-    assert lib.kvf_select_topk(FAKE, None, ctypes.byref(b), k, FAKE, None, None, None, 0, None) == 1
-    assert lib.kvf_select_topk(FAKE, FAKE, ctypes.byref(b), k, FAKE, None, None, None, 0, None) == 1
+    assert lib.kvf_select_topk(FAKE, None, ctypes.byref(b), k, FAKE, None, None, None, None, 0, None) == 1
+    assert lib.kvf_select_topk(FAKE, FAKE, ctypes.byref(b), k, FAKE, None, None, None, None, 0, None) == 1
     assert lib.kvf_select_topk_segmented(FAKE, None, ctypes.byref(b), FAKE, 1, k, FAKE, None,
                                          None, None) == 1
     k = (ctypes.c_int32 * 1)(3)
-    assert lib.kvf_select_topk(FAKE, None, ctypes.byref(b), k, None, None, None, None, 0,
+    assert lib.kvf_select_topk(FAKE, None, ctypes.byref(b), k, None, None, None, None, None, 0,
                                None) == 1                         # out_idx NULL
     assert lib.kvf_select_topk_segmented(FAKE, None, ctypes.byref(b), FAKE, 1, k, FAKE, FAKE,
                                          None, None) == 1         # rows without pos
@@ -176,7 +186,7 @@ def test_validation_errors(lib):
     # too many requests
     cu = list(range(0, 66))
     b, keep = _batch(cu, [0] * 65)
-    assert lib.kvf_score(0, ctypes.byref(ok), ctypes.byref(b), FAKE, FAKE, None, 0, FAKE, None, 0,
+    assert lib.kvf_score(0, ctypes.byref(ok), ctypes.byref(b), FAKE, FAKE, None, 0, None, FAKE, None, 0,
                          None) == 1
     # rerotate: int8 caches need bf16 output
     class Kivi(ctypes.Structure):
