@@ -88,11 +88,11 @@ def call_work(g):
     M = g.M
     pos = g.pos.cpu().numpy()[:M].astype("int64")
     work = {}
-    if wl.kivi8:
-        # read K/V codes (1 B each) + V per-token stats (min, scale) + K
-        # per-channel stats once per chunk; write bf16 K and V
+    if wl.kivi_bits:
+        # read K/V codes (bits / 8 B each) + V per-token stats (min, scale) +
+        # K per-channel stats once per chunk; write bf16 K and V
         n_chunks = b.chunk_table.shape[0]
-        work["rerotate"] = ("hbm", n_ctx * (2 * hkv * d + 8 * hkv + 2 * krow)
+        work["rerotate"] = ("hbm", n_ctx * (2 * hkv * d * wl.kivi_bits // 8 + 8 * hkv + 2 * krow)
                             + n_chunks * 8 * hkv * d)
     else:
         work["rerotate"] = ("hbm", n_ctx * 4 * krow)      # read pool K,V; write fused K,V

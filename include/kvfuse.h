@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define KVF_ABI_VERSION 6
+#define KVF_ABI_VERSION 7
 #define KVF_MAX_REQ 64      /* requests per call (batch metadata is passed by value) */
 
 typedef enum {
@@ -122,18 +122,21 @@ typedef struct {
   int32_t reserved[3];
 } kvf_chunk;
 
-/* KIVI int8 cache ([KVB] 4.5 Eq. 7, b = 8): value = min + code * scale.
- * Keys: per (pool chunk, kv head, channel) statistics; values: per
- * (pool row, kv head). */
+/* KIVI quantised cache ([KVB] 4.5 Eq. 7, b = 8 or 4): value = min + code *
+ * scale.  Keys: per (pool chunk, kv head, channel) statistics; values: per
+ * (pool row, kv head).  b = 8: one code per byte.  b = 4: two codes per byte,
+ * channel 2i in bits 0-3 and channel 2i + 1 in bits 4-7 of byte i of the
+ * row, so a [pool_rows, Hkv, d] cache takes [pool_rows, Hkv, d / 2] bytes. */
 typedef struct {
-  const uint8_t* k_codes;    /* [pool_rows, Hkv, d] */
-  const uint8_t* v_codes;    /* [pool_rows, Hkv, d] */
+  const uint8_t* k_codes;    /* [pool_rows, Hkv, d * bits / 8] */
+  const uint8_t* v_codes;    /* [pool_rows, Hkv, d * bits / 8] */
   const float* k_min;        /* [n_pool_chunks, Hkv, d] */
   const float* k_scale;      /* [n_pool_chunks, Hkv, d] */
   const float* v_min;        /* [pool_rows, Hkv] */
   const float* v_scale;      /* [pool_rows, Hkv] */
   int32_t n_pool_chunks;
-} kvf_kivi8;
+  int32_t bits;              /* 8 or 4 */
+} kvf_kivi;
 
 /* Static recompute rules (host struct); every field >= 0, 0 turns a rule off.
  *   sink:     request positions 0 .. sink-1 ([KVB] 4.1, attention-sink
@@ -180,9 +183,9 @@ kvf_status kvf_rope_table(double base, int32_t head_dim, int32_t n_pos,
  *                          R(pos0) R(t) = R(pos0 + t))
  *   fused_v[dst_row + t] = V_pool[src_row + t]
  * Dense caches: pool_k, pool_v [pool_rows, Hkv, d] in dtype, kivi = NULL.
- * int8 caches: pool_k = pool_v = NULL and kivi != NULL; codes are decoded
- * (min + code * scale, fp32) before the rotation (dequant-on-load).
- * Output dtype must be bf16 for int8 caches.
+ * KIVI caches (8 or 4 bits): pool_k = pool_v = NULL and kivi != NULL; codes
+ * are decoded (min + code * scale, fp32) before the rotation
+ * (dequant-on-load).  Output dtype must be bf16 for KIVI caches.
  * chunks: device [n_chunks]; max_chunk_len (host) bounds every len.
  * rope tables cover positions [0, rope_n_pos); pos0 >= rope_n_pos skips the
  * chunk.  Fused rows no chunk covers are not written.
@@ -190,7 +193,7 @@ kvf_status kvf_rope_table(double base, int32_t head_dim, int32_t n_pos,
 kvf_status kvf_rerotate(const kvf_layer_desc* layer, const kvf_chunk* chunks,
                         int32_t n_chunks, int32_t max_chunk_len,
                         const void* pool_k, const void* pool_v,
-                        const kvf_kivi8* kivi, int64_t pool_rows,
+                        const kvf_kivi* kivi, int64_t pool_rows,
                         const float* rope_cos, const float* rope_sin,
                         int32_t rope_n_pos, void* fused_k, void* fused_v,
                         int64_t fused_rows, void* stream);
@@ -384,21 +387,22 @@ size_t kvf_attention_workspace_size(const kvf_layer_desc* layer,
                                     const int32_t* cu_q);
 
 /* ---------------------------------------------------------------------------
- * kvf_kivi8_encode - offline encoder of a dense bf16 per-chunk cache into the
- * int8 KIVI form read by kvf_rerotate ([KVB] 4.5 Eq. 7, b = 8).  Runs ahead
- * of serving, not on the fused-layer path.  fp32 arithmetic, in this order:
- * range = max - min; scale = range / 255; inv = 255 / range;
- * code = round-half-even((x - min) * inv) clamped to [0, 255]; range 0 gives
- * scale 0 and code 0.  Keys: statistics per (pool chunk, head, channel) over
- * the chunk's rows pool_cu[c]..pool_cu[c+1]-1 (pool_cu: device
+ * kvf_kivi_encode - offline encoder of a dense bf16 per-chunk cache into the
+ * KIVI form read by kvf_rerotate ([KVB] 4.5 Eq. 7), b = out->bits (8 or 4).
+ * Runs ahead of serving, not on the fused-layer path.  With
+ * levels = 2^b - 1, fp32 arithmetic in this order: range = max - min;
+ * scale = range / levels; inv = levels / range;
+ * code = round-half-even((x - min) * inv) clamped to [0, levels]; range 0
+ * gives scale 0 and code 0.  Keys: statistics per (pool chunk, head,
+ * channel) over the chunk's rows pool_cu[c]..pool_cu[c+1]-1 (pool_cu: device
  * [n_pool_chunks + 1]); values: per (row, head) over the channels.
  * out must point at writable arrays (the const members are written).
  */
-kvf_status kvf_kivi8_encode(const kvf_layer_desc* layer, const void* pool_k,
-                            const void* pool_v, const int32_t* pool_cu,
-                            int32_t n_pool_chunks, int64_t pool_rows,
-                            int32_t max_chunk_len, const kvf_kivi8* out,
-                            void* stream);
+kvf_status kvf_kivi_encode(const kvf_layer_desc* layer, const void* pool_k,
+                           const void* pool_v, const int32_t* pool_cu,
+                           int32_t n_pool_chunks, int64_t pool_rows,
+                           int32_t max_chunk_len, const kvf_kivi* out,
+                           void* stream);
 
 /* floor(ratio_pct * n_ctx / 100) in integer arithmetic: the recompute budget
  * |P| = floor(rho N) of [QCF] 3.2.1 Eq. 11.  Returns -1 for negative input

@@ -1,12 +1,13 @@
-// RoPE tables, S1 re-position + stitch of per-chunk caches (dense and int8
-// KIVI dequant-on-load), and the offline KIVI int8 encoder.
+// RoPE tables, S1 re-position + stitch of per-chunk caches (dense, and KIVI
+// int8 / int4 dequant-on-load), and the offline KIVI encoder.
 //
 // QCFuse page, section 2.1.2 (Eq. 3-4): chunk caches are built in isolation
 // with keys at chunk-local positions from zero; serving remaps keys to request
 // positions and stitches values in the same token order.  KVBoost page,
 // section 3.2 (Eq. 3): the correction is the delta rotation R^(pos0).
-// KVBoost page, section 4.5 (Eq. 7): KIVI int8, keys per channel, values per
-// token.
+// KVBoost page, section 4.5 (Eq. 7): KIVI with b = 8 or 4 bits, keys per
+// channel, values per token; 4-bit codes two to a byte, channel 2i in the
+// low nibble.
 //
 // All kernels here are HBM-bound streams: 16-byte vector loads/stores, one
 // chunk tile per workgroup so the chunk descriptor and its rotation row are
@@ -69,9 +70,27 @@ struct RotArgs {
   int d;
 };
 
+// the 8 codes of channels e..e+7 (e a multiple of 8), `codes` pointing at
+// their first byte: 8 bytes for b = 8, 4 bytes for b = 4 (channel i of the
+// eight in bits 4i..4i+3 of the little-endian word)
+template <int BITS>
+__device__ __forceinline__ void codes8(const uint8_t* codes, uint32_t (&q)[8]) {
+  if constexpr (BITS == 8) {
+    const u32x2_t c = *reinterpret_cast<const u32x2_t*>(codes);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) q[i] = (c[i >> 2] >> (8 * (i & 3))) & 0xffu;
+  } else {
+    const uint32_t c = *reinterpret_cast<const uint32_t*>(codes);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) q[i] = (c >> (4 * i)) & 0xfu;
+  }
+}
+
+template <int BITS>
 __device__ __forceinline__ void decode8(const uint8_t* codes, const float* mn, const float* sc,
                                         float (&v)[8]) {
-  const u32x2_t c = *reinterpret_cast<const u32x2_t*>(codes);
+  uint32_t q[8];
+  codes8<BITS>(codes, q);
   const float4 m0 = *reinterpret_cast<const float4*>(mn);
   const float4 m1 = *reinterpret_cast<const float4*>(mn + 4);
   const float4 s0 = *reinterpret_cast<const float4*>(sc);
@@ -79,14 +98,13 @@ __device__ __forceinline__ void decode8(const uint8_t* codes, const float* mn, c
   const float m[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
   const float s[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint32_t q = (c[i >> 2] >> (8 * (i & 3))) & 0xffu;
-    v[i] = fmaf(static_cast<float>(q), s[i], m[i]);
-  }
+  for (int i = 0; i < 8; ++i) v[i] = fmaf(static_cast<float>(q[i]), s[i], m[i]);
 }
 
-template <typename T, bool KIVI>
+// KB: 0 for a dense cache in T, else the KIVI code width (8 or 4)
+template <typename T, int KB>
 __global__ void __launch_bounds__(256) rerotate_kernel(RotArgs a) {
+  constexpr bool KIVI = KB != 0;
   const kvf_chunk ch = a.chunks[blockIdx.x];
   const int t0 = blockIdx.y * kRotRows;
   if (ch.len <= 0 || t0 >= ch.len) return;
@@ -115,8 +133,9 @@ __global__ void __launch_bounds__(256) rerotate_kernel(RotArgs a) {
     float lo[8], hi[8];
     if constexpr (KIVI) {
       const int64_t st = (static_cast<int64_t>(ch.pool_chunk) * hkv + h) * d;
-      decode8(a.k_codes + src + j0, a.k_min + st + j0, a.k_scale + st + j0, lo);
-      decode8(a.k_codes + src + half + j0, a.k_min + st + half + j0, a.k_scale + st + half + j0, hi);
+      decode8<KB>(a.k_codes + (src + j0) * KB / 8, a.k_min + st + j0, a.k_scale + st + j0, lo);
+      decode8<KB>(a.k_codes + (src + half + j0) * KB / 8, a.k_min + st + half + j0,
+                  a.k_scale + st + half + j0, hi);
     } else {
       const T* pk = static_cast<const T*>(a.pool_k);
       Elem<T>::load8(pk + src + j0, lo);
@@ -147,10 +166,10 @@ __global__ void __launch_bounds__(256) rerotate_kernel(RotArgs a) {
       const int h = e0 / d;
       const float m = a.v_min[srow * hkv + h];
       const float sc = a.v_scale[srow * hkv + h];
-      const u32x2_t cq = *reinterpret_cast<const u32x2_t*>(a.v_codes + src);
+      uint32_t q[8];
+      codes8<KB>(a.v_codes + src * KB / 8, q);
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        v[i] = fmaf(static_cast<float>((cq[i >> 2] >> (8 * (i & 3))) & 0xffu), sc, m);
+      for (int i = 0; i < 8; ++i) v[i] = fmaf(static_cast<float>(q[i]), sc, m);
     } else {
       Elem<T>::load8(static_cast<const T*>(a.pool_v) + src, v);
     }
@@ -159,7 +178,7 @@ __global__ void __launch_bounds__(256) rerotate_kernel(RotArgs a) {
 }
 
 hipError_t launch_rerotate(const kvf_layer_desc& L, const kvf_chunk* chunks, int n_chunks,
-                           int max_len, const void* pk, const void* pv, const kvf_kivi8* q,
+                           int max_len, const void* pk, const void* pv, const kvf_kivi* q,
                            int64_t pool_rows, const float* rc, const float* rs, int rope_n,
                            void* fk, void* fv, int64_t fused_rows, hipStream_t st) {
   RotArgs a{};
@@ -186,66 +205,96 @@ hipError_t launch_rerotate(const kvf_layer_desc& L, const kvf_chunk* chunks, int
   a.d = L.head_dim;
   const dim3 grid(n_chunks, ceil_div(max_len, kRotRows));
   if (grid.y > 65535) return hipErrorInvalidValue;
-  if (q)
-    hipLaunchKernelGGL((rerotate_kernel<bf16_t, true>), grid, dim3(256), 0, st, a);
+  if (q && q->bits == 4)
+    hipLaunchKernelGGL((rerotate_kernel<bf16_t, 4>), grid, dim3(256), 0, st, a);
+  else if (q)
+    hipLaunchKernelGGL((rerotate_kernel<bf16_t, 8>), grid, dim3(256), 0, st, a);
   else if (L.dtype == KVF_BF16)
-    hipLaunchKernelGGL((rerotate_kernel<bf16_t, false>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((rerotate_kernel<bf16_t, 0>), grid, dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL((rerotate_kernel<float, false>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((rerotate_kernel<float, 0>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
-// offline KIVI int8 encoder (not on the fused-layer path)
+// offline KIVI encoder (not on the fused-layer path)
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint8_t kivi_code(float x, float mn, float inv) {
+template <int BITS>
+__device__ __forceinline__ uint32_t kivi_code(float x, float mn, float inv) {
+  constexpr float kTop = static_cast<float>((1 << BITS) - 1);
   const float t = (x - mn) * inv;
-  return static_cast<uint8_t>(fminf(fmaxf(rintf(t), 0.f), 255.f));
+  return static_cast<uint32_t>(fminf(fmaxf(rintf(t), 0.f), kTop));
 }
 
-// keys: one thread per (pool chunk, head, channel); two passes over the chunk
+template <int BITS>
+__device__ __forceinline__ void kivi_stats(float mn, float mx, float& sc, float& inv) {
+  constexpr float kTop = static_cast<float>((1 << BITS) - 1);
+  const float rng = mx - mn;
+  sc = rng > 0.f ? rng / kTop : 0.f;
+  inv = rng > 0.f ? kTop / rng : 0.f;
+}
+
+// keys: one thread per (pool chunk, head, code byte) - one channel for
+// b = 8, the channel pair (2i, 2i+1) for b = 4; two passes over the chunk
+template <int BITS>
 __global__ void __launch_bounds__(256) kivi_keys_kernel(const bf16_t* __restrict__ pk,
                                                         const int32_t* __restrict__ pool_cu,
                                                         int n_pool, int64_t pool_rows, int hkv,
                                                         int d, uint8_t* __restrict__ codes,
                                                         float* __restrict__ kmin,
                                                         float* __restrict__ kscale) {
+  constexpr int CPB = 8 / BITS;                            // channels per code byte
   const int c = blockIdx.y;
-  const int ch = blockIdx.x * blockDim.x + threadIdx.x;   // head * d + channel
-  if (c >= n_pool || ch >= hkv * d) return;
+  const int byte = blockIdx.x * blockDim.x + threadIdx.x;  // code byte within a row
+  const int row = hkv * d;
+  const int row_bytes = row / CPB;
+  if (c >= n_pool || byte >= row_bytes) return;
   const int a = pool_cu[c], b = pool_cu[c + 1];
   if (a < 0 || b < a || b > pool_rows) return;
-  const int row = hkv * d;
-  float mn = INFINITY, mx = -INFINITY;
-  for (int t = a; t < b; ++t) {
-    const float x = bf16_to_f32(pk[static_cast<int64_t>(t) * row + ch]);
-    mn = fminf(mn, x);
-    mx = fmaxf(mx, x);
+  const int ch0 = byte * CPB;                              // head * d + channel
+  float mn[CPB], mx[CPB], sc[CPB], inv[CPB];
+#pragma unroll
+  for (int q = 0; q < CPB; ++q) {
+    mn[q] = INFINITY;
+    mx[q] = -INFINITY;
   }
-  float sc = 0.f, inv = 0.f;
-  if (b > a) {
-    const float rng = mx - mn;
-    if (rng > 0.f) {
-      sc = rng / 255.f;
-      inv = 255.f / rng;
+  for (int t = a; t < b; ++t)
+#pragma unroll
+    for (int q = 0; q < CPB; ++q) {
+      const float x = bf16_to_f32(pk[static_cast<int64_t>(t) * row + ch0 + q]);
+      mn[q] = fminf(mn[q], x);
+      mx[q] = fmaxf(mx[q], x);
     }
-  } else {
-    mn = 0.f;
+#pragma unroll
+  for (int q = 0; q < CPB; ++q) {
+    if (b > a) {
+      kivi_stats<BITS>(mn[q], mx[q], sc[q], inv[q]);
+    } else {
+      mn[q] = 0.f;
+      sc[q] = inv[q] = 0.f;
+    }
+    kmin[static_cast<int64_t>(c) * row + ch0 + q] = mn[q];
+    kscale[static_cast<int64_t>(c) * row + ch0 + q] = sc[q];
   }
-  kmin[static_cast<int64_t>(c) * row + ch] = mn;
-  kscale[static_cast<int64_t>(c) * row + ch] = sc;
   for (int t = a; t < b; ++t) {
-    const int64_t i = static_cast<int64_t>(t) * row + ch;
-    codes[i] = kivi_code(bf16_to_f32(pk[i]), mn, inv);
+    uint32_t v = 0;
+#pragma unroll
+    for (int q = 0; q < CPB; ++q) {
+      const float x = bf16_to_f32(pk[static_cast<int64_t>(t) * row + ch0 + q]);
+      v |= kivi_code<BITS>(x, mn[q], inv[q]) << (BITS * q);
+    }
+    codes[static_cast<int64_t>(t) * row_bytes + byte] = static_cast<uint8_t>(v);
   }
 }
 
-// values: one wave per (row, head)
+// values: one wave per (row, head); a lane writes whole code bytes
+template <int BITS>
 __global__ void __launch_bounds__(256) kivi_values_kernel(const bf16_t* __restrict__ pv,
                                                           int64_t n_groups, int d,
                                                           uint8_t* __restrict__ codes,
                                                           float* __restrict__ vmin,
                                                           float* __restrict__ vscale) {
+  constexpr int CPB = 8 / BITS;
   const int64_t g = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) / kWave;
   const int lane = threadIdx.x & (kWave - 1);
   if (g >= n_groups) return;
@@ -261,24 +310,30 @@ __global__ void __launch_bounds__(256) kivi_values_kernel(const bf16_t* __restri
     mn = fminf(mn, __shfl_xor(mn, o, kWave));
     mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
   }
-  const float rng = mx - mn;
-  const float sc = rng > 0.f ? rng / 255.f : 0.f;
-  const float inv = rng > 0.f ? 255.f / rng : 0.f;
+  float sc, inv;
+  kivi_stats<BITS>(mn, mx, sc, inv);
   if (lane == 0) {
     vmin[g] = mn;
     vscale[g] = sc;
   }
-  for (int j = lane; j < d; j += kWave) codes[g * d + j] = kivi_code(bf16_to_f32(src[j]), mn, inv);
+  const int gb = d / CPB;                                  // code bytes per group
+  for (int k = lane; k < gb; k += kWave) {
+    uint32_t v = 0;
+#pragma unroll
+    for (int q = 0; q < CPB; ++q)
+      v |= kivi_code<BITS>(bf16_to_f32(src[k * CPB + q]), mn, inv) << (BITS * q);
+    codes[g * gb + k] = static_cast<uint8_t>(v);
+  }
 }
 
-hipError_t launch_kivi8_encode(const kvf_layer_desc& L, const void* pk, const void* pv,
-                               const int32_t* pool_cu, int n_pool, int64_t pool_rows, int max_len,
-                               const kvf_kivi8& out, hipStream_t st) {
-  (void)max_len;
+template <int BITS>
+static hipError_t kivi_encode_bits(const kvf_layer_desc& L, const void* pk, const void* pv,
+                                   const int32_t* pool_cu, int n_pool, int64_t pool_rows,
+                                   const kvf_kivi& out, hipStream_t st) {
   const int hkv = L.n_kv_heads, d = L.head_dim;
-  if (n_pool > 65535) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(kivi_keys_kernel, dim3(ceil_div(hkv * d, 256), n_pool), dim3(256), 0, st,
-                     static_cast<const bf16_t*>(pk), pool_cu, n_pool, pool_rows, hkv, d,
+  const int row_bytes = hkv * d * BITS / 8;
+  hipLaunchKernelGGL(kivi_keys_kernel<BITS>, dim3(ceil_div(row_bytes, 256), n_pool), dim3(256), 0,
+                     st, static_cast<const bf16_t*>(pk), pool_cu, n_pool, pool_rows, hkv, d,
                      const_cast<uint8_t*>(out.k_codes), const_cast<float*>(out.k_min),
                      const_cast<float*>(out.k_scale));
   hipError_t e = hipGetLastError();
@@ -286,10 +341,20 @@ hipError_t launch_kivi8_encode(const kvf_layer_desc& L, const void* pk, const vo
   const int64_t groups = pool_rows * hkv;
   const int64_t blocks = (groups * kWave + 255) / 256;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(kivi_values_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st,
-                     static_cast<const bf16_t*>(pv), groups, d, const_cast<uint8_t*>(out.v_codes),
-                     const_cast<float*>(out.v_min), const_cast<float*>(out.v_scale));
+  hipLaunchKernelGGL(kivi_values_kernel<BITS>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
+                     st, static_cast<const bf16_t*>(pv), groups, d,
+                     const_cast<uint8_t*>(out.v_codes), const_cast<float*>(out.v_min),
+                     const_cast<float*>(out.v_scale));
   return hipGetLastError();
+}
+
+hipError_t launch_kivi_encode(const kvf_layer_desc& L, const void* pk, const void* pv,
+                              const int32_t* pool_cu, int n_pool, int64_t pool_rows, int max_len,
+                              const kvf_kivi& out, hipStream_t st) {
+  (void)max_len;
+  if (n_pool > 65535) return hipErrorInvalidValue;
+  return out.bits == 4 ? kivi_encode_bits<4>(L, pk, pv, pool_cu, n_pool, pool_rows, out, st)
+                       : kivi_encode_bits<8>(L, pk, pv, pool_cu, n_pool, pool_rows, out, st);
 }
 
 }  // namespace kvf

@@ -134,7 +134,7 @@ kvf_status kvf_rope_table(double base, int32_t head_dim, int32_t n_pos, float* c
 
 kvf_status kvf_rerotate(const kvf_layer_desc* layer, const kvf_chunk* chunks, int32_t n_chunks,
                         int32_t max_chunk_len, const void* pool_k, const void* pool_v,
-                        const kvf_kivi8* kivi, int64_t pool_rows, const float* rope_cos,
+                        const kvf_kivi* kivi, int64_t pool_rows, const float* rope_cos,
                         const float* rope_sin, int32_t rope_n_pos, void* fused_k, void* fused_v,
                         int64_t fused_rows, void* stream) {
   KVF_GUARD_BEGIN
@@ -146,12 +146,14 @@ kvf_status kvf_rerotate(const kvf_layer_desc* layer, const kvf_chunk* chunks, in
   KVF_CHECK(chunks && rope_cos && rope_sin && fused_k && fused_v, KVF_ERR_INVALID_ARG,
             "required pointer is NULL");
   if (kivi) {
-    KVF_CHECK(layer->dtype == KVF_BF16, KVF_ERR_UNSUPPORTED, "int8 caches decode to bf16 only");
+    KVF_CHECK(layer->dtype == KVF_BF16, KVF_ERR_UNSUPPORTED, "KIVI caches decode to bf16 only");
+    KVF_CHECK(kivi->bits == 8 || kivi->bits == 4, KVF_ERR_UNSUPPORTED,
+              "KIVI codes are 8 or 4 bits, not %d", kivi->bits);
     KVF_CHECK(pool_k == nullptr && pool_v == nullptr, KVF_ERR_INVALID_ARG,
               "pass either dense pool pointers or kivi, not both");
     KVF_CHECK(kivi->k_codes && kivi->v_codes && kivi->k_min && kivi->k_scale && kivi->v_min &&
                   kivi->v_scale && kivi->n_pool_chunks > 0, KVF_ERR_INVALID_ARG,
-              "incomplete kvf_kivi8");
+              "incomplete kvf_kivi");
   } else {
     KVF_CHECK(pool_k && pool_v, KVF_ERR_INVALID_ARG, "pool pointers are NULL");
   }
@@ -163,24 +165,26 @@ kvf_status kvf_rerotate(const kvf_layer_desc* layer, const kvf_chunk* chunks, in
   KVF_GUARD_END
 }
 
-kvf_status kvf_kivi8_encode(const kvf_layer_desc* layer, const void* pool_k, const void* pool_v,
-                            const int32_t* pool_cu, int32_t n_pool_chunks, int64_t pool_rows,
-                            int32_t max_chunk_len, const kvf_kivi8* out, void* stream) {
+kvf_status kvf_kivi_encode(const kvf_layer_desc* layer, const void* pool_k, const void* pool_v,
+                           const int32_t* pool_cu, int32_t n_pool_chunks, int64_t pool_rows,
+                           int32_t max_chunk_len, const kvf_kivi* out, void* stream) {
   KVF_GUARD_BEGIN
   kvf_status st = check_layer(layer);
   if (st != KVF_OK) return st;
-  KVF_CHECK(layer->dtype == KVF_BF16, KVF_ERR_UNSUPPORTED, "the int8 encoder reads bf16 caches");
+  KVF_CHECK(layer->dtype == KVF_BF16, KVF_ERR_UNSUPPORTED, "the KIVI encoder reads bf16 caches");
   KVF_CHECK(n_pool_chunks >= 0 && pool_rows >= 0 && max_chunk_len >= 0, KVF_ERR_INVALID_ARG,
             "negative size");
   if (n_pool_chunks == 0 || pool_rows == 0) return KVF_OK;
   KVF_CHECK(pool_k && pool_v && pool_cu && out, KVF_ERR_INVALID_ARG, "required pointer is NULL");
   KVF_CHECK(out->k_codes && out->v_codes && out->k_min && out->k_scale && out->v_min &&
-                out->v_scale, KVF_ERR_INVALID_ARG, "incomplete output kvf_kivi8");
+                out->v_scale, KVF_ERR_INVALID_ARG, "incomplete output kvf_kivi");
+  KVF_CHECK(out->bits == 8 || out->bits == 4, KVF_ERR_UNSUPPORTED,
+            "KIVI codes are 8 or 4 bits, not %d", out->bits);
   KVF_CHECK(out->n_pool_chunks >= n_pool_chunks, KVF_ERR_INVALID_ARG,
             "output statistics hold %d chunks, need %d", out->n_pool_chunks, n_pool_chunks);
-  return from_hip(kvf::launch_kivi8_encode(*layer, pool_k, pool_v, pool_cu, n_pool_chunks,
-                                           pool_rows, max_chunk_len, *out, as_stream(stream)),
-                  "kvf_kivi8_encode");
+  return from_hip(kvf::launch_kivi_encode(*layer, pool_k, pool_v, pool_cu, n_pool_chunks,
+                                          pool_rows, max_chunk_len, *out, as_stream(stream)),
+                  "kvf_kivi_encode");
   KVF_GUARD_END
 }
 

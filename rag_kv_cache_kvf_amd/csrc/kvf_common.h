@@ -152,12 +152,12 @@ __device__ __forceinline__ void store_score(const ScoreOut& o, int64_t j, float 
 namespace kvf {
 hipError_t launch_rope_table(double base, int d, int n_pos, float* c, float* s, hipStream_t st);
 hipError_t launch_rerotate(const kvf_layer_desc& L, const kvf_chunk* chunks, int n_chunks,
-                           int max_len, const void* pk, const void* pv, const kvf_kivi8* q,
+                           int max_len, const void* pk, const void* pv, const kvf_kivi* q,
                            int64_t pool_rows, const float* rc, const float* rs, int rope_n,
                            void* fk, void* fv, int64_t fused_rows, hipStream_t st);
-hipError_t launch_kivi8_encode(const kvf_layer_desc& L, const void* pk, const void* pv,
-                               const int32_t* pool_cu, int n_pool, int64_t pool_rows,
-                               int max_len, const kvf_kivi8& out, hipStream_t st);
+hipError_t launch_kivi_encode(const kvf_layer_desc& L, const void* pk, const void* pv,
+                              const int32_t* pool_cu, int n_pool, int64_t pool_rows,
+                              int max_len, const kvf_kivi& out, hipStream_t st);
 hipError_t launch_deviation(const kvf_layer_desc& L, const BatchArgs& B, const void* fk,
                             const void* kf, const ScoreOut& out, hipStream_t st);
 hipError_t launch_attn_mass(const kvf_layer_desc& L, const BatchArgs& B, const void* fk,

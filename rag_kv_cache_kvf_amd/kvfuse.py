@@ -54,11 +54,11 @@ class BatchDesc(ctypes.Structure):
                 ("n_ctx", ctypes.POINTER(ctypes.c_int32))]
 
 
-class Kivi8Desc(ctypes.Structure):
+class KiviDesc(ctypes.Structure):
     _fields_ = [("k_codes", ctypes.c_void_p), ("v_codes", ctypes.c_void_p),
                 ("k_min", ctypes.c_void_p), ("k_scale", ctypes.c_void_p),
                 ("v_min", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
-                ("n_pool_chunks", ctypes.c_int32)]
+                ("n_pool_chunks", ctypes.c_int32), ("bits", ctypes.c_int32)]
 
 
 class StaticRules(ctypes.Structure):
@@ -75,7 +75,7 @@ _IP = ctypes.POINTER(ctypes.c_int32)
 
 _SIGS = {
     "kvf_rope_table": (_I32, [ctypes.c_double, _I32, _I32, _P, _P, _P]),
-    "kvf_rerotate": (_I32, [_LP, _P, _I32, _I32, _P, _P, ctypes.POINTER(Kivi8Desc), _I64, _P, _P,
+    "kvf_rerotate": (_I32, [_LP, _P, _I32, _I32, _P, _P, ctypes.POINTER(KiviDesc), _I64, _P, _P,
                             _I32, _P, _P, _I64, _P]),
     "kvf_score": (_I32, [_I32, _LP, _BP, _P, _P, _P, _I32, _P, _P, _P, _SZ, _P]),
     "kvf_score_workspace_size": (_SZ, [_I32, _LP, _BP, _I32]),
@@ -91,7 +91,7 @@ _SIGS = {
     "kvf_sparse_q_attention": (_I32, [_LP, _BP, _P, _P, _IP, _P, _P, ctypes.c_float, _P, _P, _P,
                                       _SZ, _P]),
     "kvf_attention_workspace_size": (_SZ, [_LP, _BP, _IP]),
-    "kvf_kivi8_encode": (_I32, [_LP, _P, _P, _P, _I32, _I64, _I32, ctypes.POINTER(Kivi8Desc), _P]),
+    "kvf_kivi_encode": (_I32, [_LP, _P, _P, _P, _I32, _I64, _I32, ctypes.POINTER(KiviDesc), _P]),
     "kvf_recompute_budget": (_I32, [_I32, _I32]),
     "kvf_anchor_budget": (_I32, [_I32, _I32, _I32]),
     "kvf_status_string": (ctypes.c_char_p, [_I32]),
@@ -204,14 +204,14 @@ def rerotate(layer: Layer, chunks: torch.Tensor, max_chunk_len: int,
              pool_k: Optional[torch.Tensor], pool_v: Optional[torch.Tensor],
              rope_cos: torch.Tensor, rope_sin: torch.Tensor, fused_k: torch.Tensor,
              fused_v: torch.Tensor, kivi: Optional[dict] = None, stream=None):
-    """chunks: int32 [n_chunks, 8] device tensor (kvf_chunk rows)."""
+    """chunks: int32 [n_chunks, 8] device tensor (kvf_chunk rows).
+    kivi: dict of k_codes, v_codes ([rows, Hkv, d * bits / 8] uint8), k_min,
+    k_scale ([n_pool, Hkv, d]), v_min, v_scale ([rows, Hkv]); the code width
+    follows from the shapes."""
     kd = None
     pool_rows = _rows(pool_k)
     if kivi is not None:
-        kd = ctypes.byref(Kivi8Desc(_ptr(kivi["k_codes"]), _ptr(kivi["v_codes"]),
-                                    _ptr(kivi["k_min"]), _ptr(kivi["k_scale"]),
-                                    _ptr(kivi["v_min"]), _ptr(kivi["v_scale"]),
-                                    int(kivi["k_min"].shape[0])))
+        kd = ctypes.byref(_kivi_desc(kivi))
         pool_rows = int(kivi["k_codes"].shape[0])
     d = layer.desc()
     _check(_lib.kvf_rerotate(ctypes.byref(d), _ptr(chunks), int(chunks.shape[0]), max_chunk_len,
@@ -353,13 +353,19 @@ def sparse_q_attention(layer: Layer, batch: Batch, q: torch.Tensor, q_pos: torch
            "kvf_sparse_q_attention")
 
 
-def kivi8_encode(layer: Layer, pool_k: torch.Tensor, pool_v: torch.Tensor, pool_cu: torch.Tensor,
-                 max_chunk_len: int, out: dict, stream=None):
+def _kivi_desc(k: dict) -> KiviDesc:
+    bits = 8 * int(k["k_codes"].shape[-1]) // int(k["k_min"].shape[-1])
+    return KiviDesc(_ptr(k["k_codes"]), _ptr(k["v_codes"]), _ptr(k["k_min"]), _ptr(k["k_scale"]),
+                    _ptr(k["v_min"]), _ptr(k["v_scale"]), int(k["k_min"].shape[0]), bits)
+
+
+def kivi_encode(layer: Layer, pool_k: torch.Tensor, pool_v: torch.Tensor, pool_cu: torch.Tensor,
+                max_chunk_len: int, out: dict, stream=None):
+    """out: the kivi dict of rerotate, allocated by the caller; the code
+    width follows from the shapes of k_codes and k_min."""
     d = layer.desc()
     n_pool = int(pool_cu.shape[0]) - 1
-    od = Kivi8Desc(_ptr(out["k_codes"]), _ptr(out["v_codes"]), _ptr(out["k_min"]),
-                   _ptr(out["k_scale"]), _ptr(out["v_min"]), _ptr(out["v_scale"]),
-                   int(out["k_min"].shape[0]))
-    _check(_lib.kvf_kivi8_encode(ctypes.byref(d), _ptr(pool_k), _ptr(pool_v), _ptr(pool_cu),
-                                 n_pool, _rows(pool_k), max_chunk_len, ctypes.byref(od),
-                                 _stream(stream)), "kvf_kivi8_encode")
+    od = _kivi_desc(out)
+    _check(_lib.kvf_kivi_encode(ctypes.byref(d), _ptr(pool_k), _ptr(pool_v), _ptr(pool_cu),
+                                n_pool, _rows(pool_k), max_chunk_len, ctypes.byref(od),
+                                _stream(stream)), "kvf_kivi_encode")

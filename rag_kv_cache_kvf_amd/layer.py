@@ -27,7 +27,7 @@ itself.  Order (all on one stream, no host synchronisation):
 
 The per-chunk caches are built ahead of serving (QCFuse page, section 2.1.2,
 Eq. 3) either by the caller (`pic=`) or on the GPU by this library's own
-projection at chunk-local positions (and its int8 encoder for int8 caches).
+projection at chunk-local positions (and its KIVI encoder for 8- or 4-bit caches).
 """
 from __future__ import annotations
 
@@ -105,17 +105,18 @@ class FusedLayerGPU:
             pv = torch.empty_like(pk)
             kvf.recompute_qkv(L, pool_hidden, None, pool_pos, self.w, kvf.KVF_OUT_K | kvf.KVF_OUT_V,
                               self.rope_cos, self.rope_sin, k_out=pk, v_out=pv)
-            if wl.kivi8:
+            if wl.kivi_bits:
                 n_pool = len(batch.pool_cu) - 1
+                cb = d * wl.kivi_bits // 8               # code bytes per head row
                 self.kivi = {
-                    "k_codes": torch.empty((pool_rows, hkv, d), dtype=torch.uint8, device=dev),
-                    "v_codes": torch.empty((pool_rows, hkv, d), dtype=torch.uint8, device=dev),
+                    "k_codes": torch.empty((pool_rows, hkv, cb), dtype=torch.uint8, device=dev),
+                    "v_codes": torch.empty((pool_rows, hkv, cb), dtype=torch.uint8, device=dev),
                     "k_min": torch.empty((n_pool, hkv, d), dtype=torch.float32, device=dev),
                     "k_scale": torch.empty((n_pool, hkv, d), dtype=torch.float32, device=dev),
                     "v_min": torch.empty((pool_rows, hkv), dtype=torch.float32, device=dev),
                     "v_scale": torch.empty((pool_rows, hkv), dtype=torch.float32, device=dev),
                 }
-                kvf.kivi8_encode(L, pk, pv, _i32(batch.pool_cu, dev), self.max_chunk_len, self.kivi)
+                kvf.kivi_encode(L, pk, pv, _i32(batch.pool_cu, dev), self.max_chunk_len, self.kivi)
                 del pk, pv
             else:
                 self.pool_k, self.pool_v = pk, pv

@@ -47,7 +47,7 @@ class Workload:
     ratio_pct: tuple           # recompute ratios in percent
     sigma: float               # cached-hidden perturbation of non-first chunks
     pool_chunks: int = 0       # >0: chunks drawn from a shared pool of this size
-    kivi8: bool = False        # cached K/V stored as int8 codes
+    kivi_bits: int = 0         # cached K/V stored as KIVI codes of 8 or 4 bits (0: dense)
     seed: int = 0
     description: str = ""
     # selector feeding the recompute path: "score" (top-k of `score`, with
@@ -163,8 +163,16 @@ WORKLOADS = {
         name="qwen25_3b_kivi8", dtype="bf16", n_req=16, chunk_lens=(128,) * 24,
         n_query=(64,), hidden=2048, n_q_heads=16, n_kv_heads=2, head_dim=128,
         rope_base=1e6, score="deviation", ratio_pct=(15,), sigma=0.1,
-        kivi8=True,
+        kivi_bits=8,
         description="Qwen2.5-3B-shaped layer, bf16 + int8 KIVI cache, 16 requests "
+                    "of 24x128 + 64 query"),
+    # The same with 4-bit KIVI codes (KVBoost's int4 setting).
+    "qwen25_3b_kivi4": _wl(
+        name="qwen25_3b_kivi4", dtype="bf16", n_req=16, chunk_lens=(128,) * 24,
+        n_query=(64,), hidden=2048, n_q_heads=16, n_kv_heads=2, head_dim=128,
+        rope_base=1e6, score="deviation", ratio_pct=(15,), sigma=0.1,
+        kivi_bits=4,
+        description="Qwen2.5-3B-shaped layer, bf16 + int4 KIVI cache, 16 requests "
                     "of 24x128 + 64 query"),
 }
 
@@ -183,7 +191,11 @@ MINI_WORKLOADS = {
     "mini_bf16_kivi8": _wl(
         name="mini_bf16_kivi8", dtype="bf16", n_req=2, chunk_lens=(128, 45, 128),
         n_query=(33, 7), hidden=256, n_q_heads=8, n_kv_heads=1, head_dim=128,
-        rope_base=1e6, score="deviation", ratio_pct=(15,), sigma=0.1, kivi8=True),
+        rope_base=1e6, score="deviation", ratio_pct=(15,), sigma=0.1, kivi_bits=8),
+    "mini_bf16_kivi4": _wl(
+        name="mini_bf16_kivi4", dtype="bf16", n_req=2, chunk_lens=(128, 45, 128),
+        n_query=(33, 7), hidden=256, n_q_heads=8, n_kv_heads=1, head_dim=128,
+        rope_base=1e6, score="deviation", ratio_pct=(15,), sigma=0.1, kivi_bits=4),
     "mini_bf16_d64_mass": _wl(
         name="mini_bf16_d64_mass", dtype="bf16", n_req=1, chunk_lens=(50, 77, 61),
         n_query=(45,), hidden=256, n_q_heads=4, n_kv_heads=2, head_dim=64,

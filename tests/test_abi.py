@@ -48,7 +48,7 @@ def test_status_strings_and_version(lib):
     lib.kvf_status_string.restype = ctypes.c_char_p
     assert lib.kvf_status_string(0) == b"KVF_OK"
     assert lib.kvf_status_string(2) == b"KVF_ERR_UNSUPPORTED"
-    assert lib.kvf_abi_version() == 6
+    assert lib.kvf_abi_version() == 7
 
 
 def test_budget_matches_oracle(lib):
@@ -191,10 +191,18 @@ def test_validation_errors(lib):
     # rerotate: int8 caches need bf16 output
     class Kivi(ctypes.Structure):
         _fields_ = [(n, ctypes.c_void_p) for n in ("kc", "vc", "km", "ks", "vm", "vs")] + [
-            ("n", ctypes.c_int32)]
-    kv = Kivi(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1)
+            ("n", ctypes.c_int32), ("bits", ctypes.c_int32)]
+    kv = Kivi(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8)
     assert lib.kvf_rerotate(ctypes.byref(ok), FAKE, 1, 4, None, None, ctypes.byref(kv), 4, FAKE,
                             FAKE, 4, FAKE, FAKE, 4, None) == 2
+    # KIVI codes are 8 or 4 bits
+    bfl = Layer(256, 4, 4, 64, 1)
+    for bits, want in ((3, 2), (16, 2), (0, 2)):
+        kv = Kivi(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, bits)
+        assert lib.kvf_rerotate(ctypes.byref(bfl), FAKE, 1, 4, None, None, ctypes.byref(kv), 4,
+                                FAKE, FAKE, 4, FAKE, FAKE, 4, None) == want
+        assert lib.kvf_kivi_encode(ctypes.byref(bfl), FAKE, FAKE, FAKE, 1, 4, 4,
+                                   ctypes.byref(kv), None) == want
 
 
 def test_empty_calls_are_noops(lib):

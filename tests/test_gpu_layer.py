@@ -19,7 +19,7 @@ from tests.gpu_util import TOL, assert_close, assert_close_vectors, decode, enco
 
 pytestmark = pytest.mark.gpu
 
-E2E = ["tiny_fp32_dev", "mini_bf16_mass", "mini_bf16_dev_pool", "mini_bf16_kivi8",
+E2E = ["tiny_fp32_dev", "mini_bf16_mass", "mini_bf16_dev_pool", "mini_bf16_kivi8", "mini_bf16_kivi4",
        "mini_bf16_d64_mass", "mini_f32_mass"]
 
 
@@ -38,13 +38,15 @@ def _oracle_inputs(name, pct=None):
     x = decode(b.x, wl.dtype)
     w = decode(b.w_qkv, wl.dtype)
     pk, pv = fusion.pic_encode(decode(b.pool_hidden, wl.dtype), b.pool_pos, w, lo)
-    if wl.kivi8:
+    if wl.kivi_bits:
+        bits = wl.kivi_bits
         pk32 = decode(encode(pk, "bf16"), "bf16").astype(np.float32)
         pv32 = decode(encode(pv, "bf16"), "bf16").astype(np.float32)
-        kc, kmin, ksc = kivi.encode_keys(pk32, b.pool_cu)
-        vc, vmin, vsc = kivi.encode_values(pv32)
-        pic = {"k_codes": kc, "v_codes": vc, "k_min": kmin, "k_scale": ksc, "v_min": vmin,
-               "v_scale": vsc}
+        kc, kmin, ksc = kivi.encode_keys(pk32, b.pool_cu, bits=bits)
+        vc, vmin, vsc = kivi.encode_values(pv32, bits=bits)
+        store = kivi.pack4 if bits == 4 else (lambda c: c)
+        pic = {"k_codes": store(kc), "v_codes": store(vc), "k_min": kmin, "k_scale": ksc,
+               "v_min": vmin, "v_scale": vsc}
         opk = kivi.decode_keys(kc, kmin, ksc, b.pool_cu)
         opv = kivi.decode_values(vc, vmin, vsc)
     else:

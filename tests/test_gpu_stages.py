@@ -92,13 +92,16 @@ def test_rerotate_dense(kvf, name):
     assert not from_gpu(fk)[b.query_rows()].any()
 
 
-@pytest.mark.parametrize("name", ["mini_bf16_kivi8", "qwen25_3b_kivi8"])
-def test_rerotate_kivi8(kvf, name):
+@pytest.mark.parametrize("name", ["mini_bf16_kivi8", "qwen25_3b_kivi8", "mini_bf16_kivi4",
+                                  "qwen25_3b_kivi4"])
+def test_rerotate_kivi(kvf, name):
     import torch
     b = synth.make_batch(name)
     wl = b.wl
+    bits = wl.kivi_bits
     lo = _olayer(wl)
-    if name == "qwen25_3b_kivi8":
+    full = name.startswith("qwen25")
+    if full:
         # full size: random cached K/V instead of projected ones (cheap to build)
         pk = _randn((b.pool_rows, wl.n_kv_heads, wl.head_dim), 3, "pool_k")
         pv = _randn((b.pool_rows, wl.n_kv_heads, wl.head_dim), 3, "pool_v")
@@ -106,9 +109,10 @@ def test_rerotate_kivi8(kvf, name):
         pk, pv = _pic(b, lo)
     pk32 = decode(encode(pk, "bf16"), "bf16").astype(np.float32)
     pv32 = decode(encode(pv, "bf16"), "bf16").astype(np.float32)
-    kc, kmin, ksc = kivi.encode_keys(pk32, b.pool_cu)
-    vc, vmin, vsc = kivi.encode_values(pv32)
-    q = {"k_codes": to_gpu(kc), "v_codes": to_gpu(vc), "k_min": to_gpu(kmin),
+    kc, kmin, ksc = kivi.encode_keys(pk32, b.pool_cu, bits=bits)
+    vc, vmin, vsc = kivi.encode_values(pv32, bits=bits)
+    store = kivi.pack4 if bits == 4 else (lambda c: c)
+    q = {"k_codes": to_gpu(store(kc)), "v_codes": to_gpu(store(vc)), "k_min": to_gpu(kmin),
          "k_scale": to_gpu(ksc), "v_min": to_gpu(vmin), "v_scale": to_gpu(vsc)}
     L = _layer(kvf, wl.hidden, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, "bf16")
     c, s = _rope_tables(kvf, wl.rope_base, wl.head_dim, int(np.diff(b.cu_T).max()))
@@ -121,35 +125,41 @@ def test_rerotate_kivi8(kvf, name):
     ok, ov = fusion.rerotate_stitch(dk, dv, b.chunk_table, b.total_rows, lo)
     ctx = b.context_rows()
     gk, gv = from_gpu(fk), from_gpu(fv)
-    if name == "qwen25_3b_kivi8":
+    if full:
         rows = ctx[synth.random_rows(len(ctx), 512, 7)]
     else:
         rows = ctx
-    assert_close(gk[rows], ok[rows], "bf16", f"{name} fused K (int8 decode)")
-    assert_close(gv[rows], ov[rows], "bf16", f"{name} fused V (int8 decode)")
+    assert_close(gk[rows], ok[rows], "bf16", f"{name} fused K ({bits}-bit decode)")
+    assert_close(gv[rows], ov[rows], "bf16", f"{name} fused V ({bits}-bit decode)")
     # the decode is exact up to one bf16 rounding of an fp32 value
     assert np.max(np.abs(gv[rows] - ov[rows]) / np.maximum(np.abs(ov[rows]), 1e-30)) <= 2 ** -8 + 1e-6
 
 
-def test_kivi8_encoder_bit_exact(kvf):
+@pytest.mark.parametrize("name", ["mini_bf16_kivi8", "mini_bf16_kivi4"])
+def test_kivi_encoder_bit_exact(kvf, name):
     import torch
-    b = synth.make_batch("mini_bf16_kivi8")
+    b = synth.make_batch(name)
     wl = b.wl
+    bits = wl.kivi_bits
     pk, pv = _pic(b, _olayer(wl))
     pk_s, pv_s = encode(pk, "bf16"), encode(pv, "bf16")
     L = _layer(kvf, wl.hidden, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, "bf16")
     n_pool = len(b.pool_cu) - 1
     sh = (b.pool_rows, wl.n_kv_heads, wl.head_dim)
-    out = {"k_codes": torch.empty(sh, dtype=torch.uint8, device="cuda"),
-           "v_codes": torch.empty(sh, dtype=torch.uint8, device="cuda"),
+    csh = sh[:2] + (wl.head_dim * bits // 8,)
+    out = {"k_codes": torch.empty(csh, dtype=torch.uint8, device="cuda"),
+           "v_codes": torch.empty(csh, dtype=torch.uint8, device="cuda"),
            "k_min": torch.empty((n_pool,) + sh[1:], dtype=torch.float32, device="cuda"),
            "k_scale": torch.empty((n_pool,) + sh[1:], dtype=torch.float32, device="cuda"),
            "v_min": torch.empty(sh[:2], dtype=torch.float32, device="cuda"),
            "v_scale": torch.empty(sh[:2], dtype=torch.float32, device="cuda")}
-    kvf.kivi8_encode(L, to_gpu(pk_s, "bf16"), to_gpu(pv_s, "bf16"), to_gpu(b.pool_cu),
-                     int(b.chunk_table[:, 3].max()), out)
-    kc, kmin, ksc = kivi.encode_keys(decode(pk_s, "bf16").astype(np.float32), b.pool_cu)
-    vc, vmin, vsc = kivi.encode_values(decode(pv_s, "bf16").astype(np.float32))
+    kvf.kivi_encode(L, to_gpu(pk_s, "bf16"), to_gpu(pv_s, "bf16"), to_gpu(b.pool_cu),
+                    int(b.chunk_table[:, 3].max()), out)
+    kc, kmin, ksc = kivi.encode_keys(decode(pk_s, "bf16").astype(np.float32), b.pool_cu,
+                                     bits=bits)
+    vc, vmin, vsc = kivi.encode_values(decode(pv_s, "bf16").astype(np.float32), bits=bits)
+    if bits == 4:
+        kc, vc = kivi.pack4(kc), kivi.pack4(vc)
     for key, ref in (("k_codes", kc), ("k_min", kmin), ("k_scale", ksc), ("v_codes", vc),
                      ("v_min", vmin), ("v_scale", vsc)):
         got = raw(out[key])
