@@ -646,8 +646,11 @@ struct Bf16Plan {
 // is a multiple of it; row-tile height the candidate whose tiles fill 256 CUs
 // with the least per-CU work (rounds x tile area, ties to the larger tile).
 // A call with too few tiles for half the chip (few rows) splits K instead:
-// 64 or 128-row tiles, K cut into 2^j slices of >= 256 until about two tiles
-// per CU, the slices added by gemm_split_finish_kernel.
+// 64 or 128-row tiles, K cut into 2^j slices of >= 256, the count that
+// brings the workgroups closest to one per CU (more slices shorten each
+// workgroup's K loop but add partial sums the finish kernel must read: at
+// 64 rows, 192 workgroups beat 384; at 256 rows, 320 beat 160), the slices
+// added by gemm_split_finish_kernel.
 Bf16Plan plan_bf16(const kvf_layer_desc& L, int M, uint32_t mask) {
   const int heads[3] = {L.n_q_heads, L.n_kv_heads, L.n_kv_heads};
   const uint32_t bits[3] = {KVF_OUT_Q, KVF_OUT_K, KVF_OUT_V};
@@ -678,9 +681,15 @@ Bf16Plan plan_bf16(const kvf_layer_desc& L, int M, uint32_t mask) {
   if (static_cast<int64_t>(ceil_div(M, p.bm)) * total >= 128) return p;
   Bf16Plan q{M <= 64 ? 64 : 128, 128, 1, 1, {0, 0, 0}};
   const int64_t base = static_cast<int64_t>(ceil_div(M, q.bm)) * tiles(128, q.n_tiles);
-  while (base * q.splits * 2 <= 512 && L.hidden % (q.splits * 2 * kBK) == 0 &&
-         L.hidden / (q.splits * 2) >= 256)
-    q.splits *= 2;
+  int64_t best_gap = base > kCUs ? base - kCUs : kCUs - base;
+  for (int sp = 2; L.hidden % (sp * kBK) == 0 && L.hidden / sp >= 256; sp *= 2) {
+    const int64_t n = base * sp;
+    const int64_t gap = n > kCUs ? n - kCUs : kCUs - n;
+    if (gap < best_gap) {
+      best_gap = gap;
+      q.splits = sp;
+    }
+  }
   return q.splits > 1 ? q : p;
 }
 

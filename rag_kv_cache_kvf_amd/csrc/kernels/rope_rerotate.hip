@@ -46,7 +46,7 @@ hipError_t launch_rope_table(double base, int d, int n_pos, float* c, float* s, 
 // ---------------------------------------------------------------------------
 // S1: re-position and stitch
 // ---------------------------------------------------------------------------
-constexpr int kRotRows = 16;      // tokens per workgroup tile
+constexpr int kRotRows = 8;       // tokens per workgroup tile
 
 struct RotArgs {
   const kvf_chunk* chunks;

@@ -87,6 +87,12 @@ struct SelectLds {
   uint32_t keys[CACHE];     // the selection's keys, read from HBM once when they fit
 };
 
+// LDS slot of key i: one pad word after every 32 keys.  The compaction reads
+// contiguous per-thread segments (thread t reads key t * seg + j at step j);
+// with seg = 32 (32768 keys, 1024 threads) every lane of a wave would hit
+// the same bank without the pad, with it the stride is 33 words.
+__device__ __forceinline__ int key_slot(int i) { return i + (i >> 5); }
+
 // The k largest keys of positions [0, N) with ties to the lower position;
 // emit(o, i) is called for the o-th chosen position i, o ascending with i.
 // sc == nullptr ranks every unforced position equal (lowest positions win).
@@ -101,11 +107,11 @@ __device__ __forceinline__ void select_block(const float* __restrict__ sc,
     if (forced && forced[i]) return kForcedKey;
     return sc ? order_key(sc[i]) : 0u;
   };
-  const bool cached = N <= CACHE;
+  const bool cached = key_slot(N) <= CACHE;
   if (cached && k > 0 && k < N)
-    for (int i = tid; i < N; i += NT) s.keys[i] = key_of(i);
+    for (int i = tid; i < N; i += NT) s.keys[key_slot(i)] = key_of(i);
   auto key_at = [&](int i) __attribute__((always_inline)) {
-    return cached ? s.keys[i] : key_of(i);
+    return cached ? s.keys[key_slot(i)] : key_of(i);
   };
 
   uint32_t tau = 0u;        // keys > tau are taken; `need` keys == tau in index order
@@ -196,22 +202,38 @@ __device__ __forceinline__ void select_block(const float* __restrict__ sc,
   const int eq_base = block_exclusive_scan<NT>(n_eq, s.wave, &tot);
   const int take = max(0, min(n_eq, need - eq_base));
   const int out_base = block_exclusive_scan<NT>(n_gt + take, s.wave, &tot);
-  if (k > 0 || mask) {
+  auto decide = [&](int i, int& eq_seen) __attribute__((always_inline)) {
+    if (k == 0) return false;
+    if (k == N) return true;
+    const uint32_t key = key_at(i);
+    if (key != tau) return key > tau;
+    return eq_seen++ < take;
+  };
+  if (cached && seg <= 32) {
+    // Decisions as a bit mask over the thread's segment, then the picks are
+    // laid out in LDS (over the key cache, no longer read) and written out
+    // in index order by consecutive threads: coalesced stores instead of
+    // each lane writing its own run of up to 32 scattered words.
+    uint32_t bits = 0u;
+    int eq_seen = 0;
+    for (int i = s0; i < s1; ++i)
+      if (decide(i, eq_seen)) bits |= 1u << (i - s0);
+    __syncthreads();                              // every key read is done
+    uint32_t* picks = s.keys;                     // k <= N entries fit
+    int o = out_base;
+    for (uint32_t b = bits; b; b &= b - 1) picks[o++] = static_cast<uint32_t>(s0 + __builtin_ctz(b));
+    if (mask) s.hist[tid] = bits;                 // the histogram is no longer read
+    __syncthreads();
+    for (int o2 = tid; o2 < k; o2 += NT) emit(o2, static_cast<int>(picks[o2]));
+    if (mask)
+      for (int i = tid; i < N; i += NT) {
+        const int t = i / seg;
+        mask[i] = static_cast<uint8_t>((s.hist[t] >> (i - t * seg)) & 1u);
+      }
+  } else if (k > 0 || mask) {
     int o = out_base, eq_seen = 0;
     for (int i = s0; i < s1; ++i) {
-      bool sel;
-      if (k == 0) {
-        sel = false;
-      } else if (k == N) {
-        sel = true;
-      } else {
-        const uint32_t key = key_at(i);
-        sel = key > tau;
-        if (key == tau) {
-          sel = eq_seen < take;
-          ++eq_seen;
-        }
-      }
+      const bool sel = decide(i, eq_seen);
       if (mask) mask[i] = sel ? 1 : 0;
       if (sel) emit(o++, i);
     }

@@ -109,7 +109,8 @@ def test_validation_errors(lib):
     # bf16 projection of few rows splits K and needs its workspace
     bf = Layer(4096, 32, 8, 128, 1)
     need = lib.kvf_recompute_workspace_size(ctypes.byref(bf), 64, 7)
-    assert need == 8 * 64 * (32 + 16) * 128 * 4
+    # 48 column tiles of 128 x 4 slices = 192 workgroups, the closest to one per CU
+    assert need == 4 * 64 * (32 + 16) * 128 * 4
     assert lib.kvf_recompute_qkv(ctypes.byref(bf), FAKE, 64, None, FAKE, 64, FAKE, 7, FAKE, FAKE, 4,
                                  FAKE, FAKE, FAKE, None, 0, None, 0, None) == 3
     assert lib.kvf_recompute_qkv(ctypes.byref(bf), FAKE, 64, None, FAKE, 64, FAKE, 7, FAKE, FAKE, 4,
