@@ -8,6 +8,7 @@ or importing this module fails.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import dataclasses
 import os
@@ -130,6 +131,46 @@ def _check(status: int, func: str):
 
 
 # ----------------------------------------------------------------------------
+# prepared calls: the arguments of a call marshalled once
+# ----------------------------------------------------------------------------
+class Prepared:
+    """One library call with its arguments converted once (device pointers,
+    ctypes structs and arrays); calling it runs the C entry point on the
+    current HIP stream, or on `stream`.  The tensors behind the pointers
+    must stay alive and keep their storage while it is used; `keep` holds
+    the ones the binding created itself."""
+    __slots__ = ("fn", "args", "name", "keep")
+
+    def __init__(self, fn, args, name, keep=()):
+        self.fn, self.args, self.name, self.keep = fn, args, name, keep
+
+    def __call__(self, stream=None):
+        _check(self.fn(*self.args, _stream(stream)), self.name)
+
+
+_preparing = False
+
+
+@contextlib.contextmanager
+def preparing():
+    """Inside this context the entry points below return a Prepared call
+    instead of running it."""
+    global _preparing
+    old, _preparing = _preparing, True
+    try:
+        yield
+    finally:
+        _preparing = old
+
+
+def _run(fn, args: tuple, name: str, stream, keep=()):
+    if _preparing:
+        return Prepared(fn, args, name, keep)
+    _check(fn(*args, _stream(stream)), name)
+    return None
+
+
+# ----------------------------------------------------------------------------
 # marshalling helpers
 # ----------------------------------------------------------------------------
 @dataclasses.dataclass(frozen=True)
@@ -196,8 +237,8 @@ def _rows(t: Optional[torch.Tensor]) -> int:
 # ----------------------------------------------------------------------------
 def rope_table(base: float, head_dim: int, n_pos: int, cos_out: torch.Tensor,
                sin_out: torch.Tensor, stream=None):
-    _check(_lib.kvf_rope_table(float(base), head_dim, n_pos, _ptr(cos_out), _ptr(sin_out),
-                               _stream(stream)), "kvf_rope_table")
+    return _run(_lib.kvf_rope_table, (float(base), head_dim, n_pos, _ptr(cos_out), _ptr(sin_out)),
+                "kvf_rope_table", stream)
 
 
 def rerotate(layer: Layer, chunks: torch.Tensor, max_chunk_len: int,
@@ -214,10 +255,10 @@ def rerotate(layer: Layer, chunks: torch.Tensor, max_chunk_len: int,
         kd = ctypes.byref(_kivi_desc(kivi))
         pool_rows = int(kivi["k_codes"].shape[0])
     d = layer.desc()
-    _check(_lib.kvf_rerotate(ctypes.byref(d), _ptr(chunks), int(chunks.shape[0]), max_chunk_len,
+    return _run(_lib.kvf_rerotate, (ctypes.byref(d), _ptr(chunks), int(chunks.shape[0]), max_chunk_len,
                              _ptr(pool_k), _ptr(pool_v), kd, pool_rows, _ptr(rope_cos),
                              _ptr(rope_sin), int(rope_cos.shape[0]), _ptr(fused_k), _ptr(fused_v),
-                             _rows(fused_k), _stream(stream)), "kvf_rerotate")
+                             _rows(fused_k),), "kvf_rerotate", stream)
 
 
 def score_workspace_size(mode: int, layer: Layer, batch: Batch, n_last_q: int = 0) -> int:
@@ -233,9 +274,9 @@ def score(mode: int, layer: Layer, batch: Batch, fused_k: torch.Tensor,
     d = layer.desc()
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     flags = mode | (KVF_SCORE_ACCUMULATE if accumulate else 0)
-    _check(_lib.kvf_score(flags, ctypes.byref(d), ctypes.byref(batch.desc), _ptr(fused_k),
+    return _run(_lib.kvf_score, (flags, ctypes.byref(d), ctypes.byref(batch.desc), _ptr(fused_k),
                           _ptr(k_fresh), _ptr(q_u), n_last_q, _ptr(eligible), _ptr(scores),
-                          _ptr(workspace), ws_bytes, _stream(stream)), "kvf_score")
+                          _ptr(workspace), ws_bytes,), "kvf_score", stream)
 
 
 def select_topk(scores: Optional[torch.Tensor], batch: Batch, k_per_req: Sequence[int],
@@ -245,10 +286,9 @@ def select_topk(scores: Optional[torch.Tensor], batch: Batch, k_per_req: Sequenc
     """forced: uint8 [sum N] mask of positions ranked above every score;
     out_mask: uint8 [sum N], 1 at the picks."""
     ka = _int_array(k_per_req)
-    _check(_lib.kvf_select_topk(_ptr(scores), _ptr(forced), ctypes.byref(batch.desc), ka,
+    return _run(_lib.kvf_select_topk, (_ptr(scores), _ptr(forced), ctypes.byref(batch.desc), ka,
                                 _ptr(out_idx), _ptr(out_rows), _ptr(out_pos), _ptr(out_mask),
-                                None, 0, _stream(stream)),
-           "kvf_select_topk")
+                                None, 0,), "kvf_select_topk", stream)
 
 
 def select_topk_segmented(scores: Optional[torch.Tensor], batch: Batch, segs: torch.Tensor,
@@ -258,19 +298,17 @@ def select_topk_segmented(scores: Optional[torch.Tensor], batch: Batch, segs: to
                           forced: Optional[torch.Tensor] = None, stream=None):
     """segs: int32 [n_segs, 8] device tensor (kvf_segment rows)."""
     ka = _int_array(k_per_req)
-    _check(_lib.kvf_select_topk_segmented(_ptr(scores), _ptr(forced), ctypes.byref(batch.desc),
+    return _run(_lib.kvf_select_topk_segmented, (_ptr(scores), _ptr(forced), ctypes.byref(batch.desc),
                                           _ptr(segs), int(segs.shape[0]), ka, _ptr(out_idx),
-                                          _ptr(out_rows), _ptr(out_pos), _stream(stream)),
-           "kvf_select_topk_segmented")
+                                          _ptr(out_rows), _ptr(out_pos),), "kvf_select_topk_segmented", stream)
 
 
 def select_static(batch: Batch, chunks: torch.Tensor, rules: Sequence[int], mask: torch.Tensor,
                   stream=None):
     """rules: (sink, boundary, seam); chunks: int32 [n_chunks, 8] device tensor."""
     r = StaticRules(*[int(v) for v in rules])
-    _check(_lib.kvf_select_static(ctypes.byref(batch.desc), _ptr(chunks), int(chunks.shape[0]),
-                                  ctypes.byref(r), _ptr(mask), _stream(stream)),
-           "kvf_select_static")
+    return _run(_lib.kvf_select_static, (ctypes.byref(batch.desc), _ptr(chunks), int(chunks.shape[0]),
+                                  ctypes.byref(r), _ptr(mask),), "kvf_select_static", stream)
 
 
 def static_counts(batch: Batch, chunks_host, rules: Sequence[int]) -> list:
@@ -307,11 +345,11 @@ def recompute_qkv(layer: Layer, x: torch.Tensor, row_src: Optional[torch.Tensor]
     kv_rows = 0
     if kv_out_row is not None:
         kv_rows = min(_rows(t) for t in (k_out, v_out) if t is not None)
-    _check(_lib.kvf_recompute_qkv(ctypes.byref(d), _ptr(x), _rows(x), _ptr(row_src), _ptr(row_pos),
-                                  M, _ptr(w_qkv), out_mask, _ptr(rope_cos), _ptr(rope_sin),
-                                  _rows(rope_cos), _ptr(q_out), _ptr(k_out), _ptr(v_out),
-                                  _ptr(kv_out_row), kv_rows, _ptr(workspace), ws_bytes,
-                                  _stream(stream)), "kvf_recompute_qkv")
+    return _run(_lib.kvf_recompute_qkv,
+                (ctypes.byref(d), _ptr(x), _rows(x), _ptr(row_src), _ptr(row_pos), M, _ptr(w_qkv),
+                 out_mask, _ptr(rope_cos), _ptr(rope_sin), _rows(rope_cos), _ptr(q_out),
+                 _ptr(k_out), _ptr(v_out), _ptr(kv_out_row), kv_rows, _ptr(workspace), ws_bytes),
+                "kvf_recompute_qkv", stream, keep=(workspace,))
 
 
 def recompute_workspace_size(layer: Layer, M: int, out_mask: int) -> int:
@@ -325,10 +363,9 @@ def scatter_kv(layer: Layer, k_src: Optional[torch.Tensor], k_src_row: Optional[
                M: Optional[int] = None, stream=None):
     d = layer.desc()
     M = int(dst_row.shape[0]) if M is None else M
-    _check(_lib.kvf_scatter_kv(ctypes.byref(d), _ptr(k_src), _ptr(k_src_row), _rows(k_src),
+    return _run(_lib.kvf_scatter_kv, (ctypes.byref(d), _ptr(k_src), _ptr(k_src_row), _rows(k_src),
                                _ptr(v_src), _ptr(v_src_row), _rows(v_src), _ptr(dst_row), M,
-                               _ptr(fused_k), _ptr(fused_v), _rows(fused_k), _stream(stream)),
-           "kvf_scatter_kv")
+                               _ptr(fused_k), _ptr(fused_v), _rows(fused_k),), "kvf_scatter_kv", stream)
 
 
 def attention_workspace_size(layer: Layer, batch: Batch, cu_q: Sequence[int]) -> int:
@@ -346,11 +383,10 @@ def sparse_q_attention(layer: Layer, batch: Batch, q: torch.Tensor, q_pos: torch
     d = layer.desc()
     cq = _int_array(cu_q)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(_lib.kvf_sparse_q_attention(ctypes.byref(d), ctypes.byref(batch.desc), _ptr(q),
+    return _run(_lib.kvf_sparse_q_attention, (ctypes.byref(d), ctypes.byref(batch.desc), _ptr(q),
                                        _ptr(q_pos), cq, _ptr(fused_k), _ptr(fused_v),
                                        float(sm_scale), _ptr(out), _ptr(lse), _ptr(workspace),
-                                       ws_bytes, _stream(stream)),
-           "kvf_sparse_q_attention")
+                                       ws_bytes,), "kvf_sparse_q_attention", stream)
 
 
 def _kivi_desc(k: dict) -> KiviDesc:
@@ -366,6 +402,5 @@ def kivi_encode(layer: Layer, pool_k: torch.Tensor, pool_v: torch.Tensor, pool_c
     d = layer.desc()
     n_pool = int(pool_cu.shape[0]) - 1
     od = _kivi_desc(out)
-    _check(_lib.kvf_kivi_encode(ctypes.byref(d), _ptr(pool_k), _ptr(pool_v), _ptr(pool_cu),
-                                n_pool, _rows(pool_k), max_chunk_len, ctypes.byref(od),
-                                _stream(stream)), "kvf_kivi_encode")
+    return _run(_lib.kvf_kivi_encode, (ctypes.byref(d), _ptr(pool_k), _ptr(pool_v), _ptr(pool_cu),
+                                n_pool, _rows(pool_k), max_chunk_len, ctypes.byref(od),), "kvf_kivi_encode", stream)

@@ -52,6 +52,10 @@ def _i32(a, device) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(np.asarray(a, dtype=np.int32))).to(device)
 
 
+def _noop(stream=None):
+    return None
+
+
 class FusedLayerGPU:
     def __init__(self, batch: SynthBatch, ratio_pct: int, device="cuda",
                  pic: Optional[dict] = None, n_last_q: int = 0, mode: Optional[str] = None):
@@ -184,93 +188,117 @@ class FusedLayerGPU:
         attn_need = kvf.attention_workspace_size(self.layer, self.kb, self.cu_q)
         self.attn_ws = (torch.zeros(attn_need, dtype=torch.uint8, device=dev)
                         if attn_need > 0 else None)
+        self.use_prepared = True
+        self._prep = {}
 
     # ------------------------------------------------------------------ calls
     def _rerotate(self):
-        kvf.rerotate(self.layer, self.chunks, self.max_chunk_len, self.pool_k, self.pool_v,
-                     self.rope_cos, self.rope_sin, self.fused_k, self.fused_v, kivi=self.kivi)
+        return kvf.rerotate(self.layer, self.chunks, self.max_chunk_len, self.pool_k, self.pool_v,
+                            self.rope_cos, self.rope_sin, self.fused_k, self.fused_v, kivi=self.kivi)
 
     def _k_probe(self):
-        kvf.recompute_qkv(self.layer, self.x, None, self.all_pos, self.w, kvf.KVF_OUT_K,
-                          self.rope_cos, self.rope_sin, k_out=self.k_probe, workspace=self.gemm_ws)
+        return kvf.recompute_qkv(self.layer, self.x, None, self.all_pos, self.w, kvf.KVF_OUT_K,
+                                 self.rope_cos, self.rope_sin, k_out=self.k_probe, workspace=self.gemm_ws)
 
     def _u_probe(self):
-        kvf.recompute_qkv(self.layer, self.x, self.u_rows, self.u_pos, self.w,
-                          kvf.KVF_OUT_Q | kvf.KVF_OUT_K | kvf.KVF_OUT_V, self.rope_cos,
-                          self.rope_sin, q_out=self.q_u, k_out=self.fused_k, v_out=self.fused_v,
-                          kv_out_row=self.u_rows, workspace=self.gemm_ws)
+        return kvf.recompute_qkv(self.layer, self.x, self.u_rows, self.u_pos, self.w,
+                                 kvf.KVF_OUT_Q | kvf.KVF_OUT_K | kvf.KVF_OUT_V, self.rope_cos,
+                                 self.rope_sin, q_out=self.q_u, k_out=self.fused_k, v_out=self.fused_v,
+                                 kv_out_row=self.u_rows, workspace=self.gemm_ws)
 
     def _static_mask(self):
-        kvf.select_static(self.kb, self.chunks, self.rules, self.static_mask)
+        return kvf.select_static(self.kb, self.chunks, self.rules, self.static_mask)
 
     def _score(self):
         if self.selector == "anchor":
-            kvf.score(kvf.KVF_SCORE_KEY_NORM, self.layer, self.kb, self.fused_k, None, None,
-                      self.scores)
+            return kvf.score(kvf.KVF_SCORE_KEY_NORM, self.layer, self.kb, self.fused_k, None, None,
+                             self.scores)
         elif self.mode == "deviation":
-            kvf.score(kvf.KVF_SCORE_DEVIATION, self.layer, self.kb, self.fused_k, self.k_probe,
-                      None, self.scores)
+            return kvf.score(kvf.KVF_SCORE_DEVIATION, self.layer, self.kb, self.fused_k, self.k_probe,
+                             None, self.scores)
         else:
-            kvf.score(kvf.KVF_SCORE_ATTN_MASS, self.layer, self.kb, self.fused_k, None, self.q_u,
-                      self.scores, self.ws, n_last_q=self.n_last_q)
+            return kvf.score(kvf.KVF_SCORE_ATTN_MASS, self.layer, self.kb, self.fused_k, None, self.q_u,
+                             self.scores, self.ws, n_last_q=self.n_last_q)
 
     def _select(self):
         if self.selector == "anchor":
-            kvf.select_topk_segmented(self.scores, self.kb, self.segs, self.k_per_req, self.sel,
-                                      self.rows, self.pos)
+            return kvf.select_topk_segmented(self.scores, self.kb, self.segs, self.k_per_req, self.sel,
+                                             self.rows, self.pos)
         else:
-            kvf.select_topk(None if self.selector == "static" else self.scores, self.kb,
-                            self.k_per_req, self.sel, self.rows, self.pos,
-                            forced=self.static_mask)
+            return kvf.select_topk(None if self.selector == "static" else self.scores, self.kb,
+                                   self.k_per_req, self.sel, self.rows, self.pos,
+                                   forced=self.static_mask)
 
     def _recompute(self):
         if self.M == 0:
-            return
+            return None
         if self.probe:
             # K of these rows is already in the probe
-            kvf.recompute_qkv(self.layer, self.x, self.rows, self.pos, self.w,
-                              kvf.KVF_OUT_Q | kvf.KVF_OUT_V, self.rope_cos, self.rope_sin,
-                              q_out=self.q, v_out=self.fused_v, kv_out_row=self.rows, M=self.M,
-                              workspace=self.gemm_ws)
+            return kvf.recompute_qkv(self.layer, self.x, self.rows, self.pos, self.w,
+                                     kvf.KVF_OUT_Q | kvf.KVF_OUT_V, self.rope_cos, self.rope_sin,
+                                     q_out=self.q, v_out=self.fused_v, kv_out_row=self.rows, M=self.M,
+                                     workspace=self.gemm_ws)
         else:
-            kvf.recompute_qkv(self.layer, self.x, self.rows, self.pos, self.w,
-                              kvf.KVF_OUT_Q | kvf.KVF_OUT_K | kvf.KVF_OUT_V, self.rope_cos,
-                              self.rope_sin, q_out=self.q, k_out=self.fused_k, v_out=self.fused_v,
-                              kv_out_row=self.rows,
-                              M=self.M, workspace=self.gemm_ws)
+            return kvf.recompute_qkv(self.layer, self.x, self.rows, self.pos, self.w,
+                                     kvf.KVF_OUT_Q | kvf.KVF_OUT_K | kvf.KVF_OUT_V, self.rope_cos,
+                                     self.rope_sin, q_out=self.q, k_out=self.fused_k, v_out=self.fused_v,
+                                     kv_out_row=self.rows,
+                                     M=self.M, workspace=self.gemm_ws)
 
     def _scatter(self):
         # deviation mode: K of the recomputed rows is the probe's
         if self.M == 0:
-            return
-        kvf.scatter_kv(self.layer, self.k_probe, self.rows, None, None, self.rows, self.fused_k,
-                       self.fused_v, M=self.M)
+            return None
+        return kvf.scatter_kv(self.layer, self.k_probe, self.rows, None, None, self.rows, self.fused_k,
+                              self.fused_v, M=self.M)
 
     def _attention(self):
         if self.M == 0:
-            return
-        kvf.sparse_q_attention(self.layer, self.kb, self.q, self.pos, self.cu_q, self.fused_k,
-                               self.fused_v, self.sm_scale, self.out, self.lse,
-                               workspace=self.attn_ws)
+            return None
+        return kvf.sparse_q_attention(self.layer, self.kb, self.q, self.pos, self.cu_q, self.fused_k,
+                                      self.fused_v, self.sm_scale, self.out, self.lse,
+                                      workspace=self.attn_ws)
+
+    def fn(self, name):
+        """The library call `name` (rerotate, k_probe, u_probe, static_mask,
+        score, select, recompute, scatter, attention) as a callable.  With
+        use_prepared, its arguments are marshalled on first use and reused
+        (device pointers, ctypes structs), so a pass costs the host little
+        more than the launches; call invalidate_prepared() after replacing a
+        buffer the calls read."""
+        if not self.use_prepared:
+            return getattr(self, "_" + name)
+        p = self._prep.get(name)
+        if p is None:
+            with kvf.preparing():
+                p = getattr(self, "_" + name)()
+            if p is None:                        # nothing to run (no recomputed rows)
+                p = _noop
+            self._prep[name] = p
+        return p
+
+    def invalidate_prepared(self):
+        self._prep = {}
 
     def calls(self):
         """The library calls of one pass, in order, as (name, stage, fn):
         stage is one of rerotate / score / select / recompute_fuse / attention."""
-        fuse = [("recompute", "recompute_fuse", self._recompute)]
+        f = self.fn
+        fuse = [("recompute", "recompute_fuse", f("recompute"))]
         if self.probe:
-            score = [("k_probe", "score", self._k_probe), ("score", "score", self._score)]
-            fuse.append(("scatter", "recompute_fuse", self._scatter))
+            score = [("k_probe", "score", f("k_probe")), ("score", "score", f("score"))]
+            fuse.append(("scatter", "recompute_fuse", f("scatter")))
         elif self.mass:
-            score = [("u_probe", "score", self._u_probe), ("score", "score", self._score)]
+            score = [("u_probe", "score", f("u_probe")), ("score", "score", f("score"))]
         elif self.selector == "anchor":
-            score = [("score", "score", self._score)]
+            score = [("score", "score", f("score"))]
         else:
             score = []
-        select = [("select", "select", self._select)]
+        select = [("select", "select", f("select"))]
         if self.static_mask is not None:
-            select.insert(0, ("static_mask", "select", self._static_mask))
-        return ([("rerotate", "rerotate", self._rerotate)] + score + select + fuse +
-                [("attention", "attention", self._attention)])
+            select.insert(0, ("static_mask", "select", f("static_mask")))
+        return ([("rerotate", "rerotate", f("rerotate"))] + score + select + fuse +
+                [("attention", "attention", f("attention"))])
 
     def _stage(self, stage):
         for _, st, fn in self.calls():

@@ -61,6 +61,7 @@ class MultiLayerGPU:
             for l, (b, p) in enumerate(zip(batches, pcts))]
         l0 = self.layers[0]
         self.kb = l0.kb
+        self._prep = {}          # prepared calls of this driver's own closures
 
         if self.signal == "sum":
             if wl.score != "attn_mass":
@@ -134,23 +135,23 @@ class MultiLayerGPU:
             for j, l in enumerate(self.score_layers):
                 ly = L[l]
                 out.append(("rerotate", l, self._rerotate_fn(l)))
-                out.append(("u_probe", l, ly._u_probe))
+                out.append(("u_probe", l, ly.fn("u_probe")))
                 out.append(("score", l, self._sum_score_fn(l, accumulate=j > 0)))
-            out.append(("select", 0, l0._select))
+            out.append(("select", 0, l0.fn("select")))
             for l in range(self.n_layers):
                 if l not in self.score_layers:
                     out.append(("rerotate", l, self._rerotate_fn(l)))
-                out.append(("recompute", l, L[l]._recompute))
-                out.append(("attention", l, L[l]._attention))
+                out.append(("recompute", l, L[l].fn("recompute")))
+                out.append(("attention", l, L[l].fn("attention")))
         elif self.signal == "progressive":
             for l, ly in enumerate(L):
                 out.append(("rerotate", l, self._rerotate_fn(l)))
                 out.append(("k_probe", l, self._probe_fn(l)))
                 out.append(("score", l, self._prog_score_fn(l)))
                 out.append(("select", l, self._prog_select_fn(l)))
-                out.append(("recompute", l, ly._recompute))
-                out.append(("scatter", l, ly._scatter))
-                out.append(("attention", l, ly._attention))
+                out.append(("recompute", l, ly.fn("recompute")))
+                out.append(("scatter", l, ly.fn("scatter")))
+                out.append(("attention", l, ly.fn("attention")))
         else:
             for l, ly in enumerate(L):
                 for name, _, fn in ly.calls():
@@ -158,19 +159,34 @@ class MultiLayerGPU:
         return out
 
     # ------------------------------------------------------------------ calls
+    def _prepared(self, key, make):
+        """A prepared library call of this driver, made once by make()."""
+        p = self._prep.get(key)
+        if p is None:
+            with kvf.preparing():
+                p = make()
+            self._prep[key] = p
+        return p
+
     def _rerotate_fn(self, l):
         ly = self.layers[l]
         if not self.stream_pools:
-            return ly._rerotate
+            return ly.fn("rerotate")
+
+        def rot_from(s):
+            def make():
+                ly.pool_k, ly.pool_v = self.slots[s][0], self.slots[s][1]
+                try:
+                    return ly._rerotate()
+                finally:
+                    ly.pool_k = ly.pool_v = None
+            return self._prepared(("rerotate", l, s), make)
 
         def run():
             j = self._order_index[l]
             cur = torch.cuda.current_stream(self.device)
             cur.wait_event(self._copied[j])
-            slot = self.slots[j % 2]
-            ly.pool_k, ly.pool_v = slot[0], slot[1]
-            ly._rerotate()
-            ly.pool_k = ly.pool_v = None
+            rot_from(j % 2)()
             done = self._ev_read[j % 2]
             done.record(cur)
             self._slot_reader[j % 2] = done
@@ -206,41 +222,31 @@ class MultiLayerGPU:
 
     def _sum_score_fn(self, l, accumulate):
         ly, l0 = self.layers[l], self.layers[0]
-
-        def run():
-            kvf.score(kvf.KVF_SCORE_ATTN_MASS, ly.layer, ly.kb, ly.fused_k, None, ly.q_u,
-                      l0.scores, ly.ws, n_last_q=ly.n_last_q, accumulate=accumulate)
-        return run
+        return self._prepared(("score", l), lambda: kvf.score(
+            kvf.KVF_SCORE_ATTN_MASS, ly.layer, ly.kb, ly.fused_k, None, ly.q_u, l0.scores, ly.ws,
+            n_last_q=ly.n_last_q, accumulate=accumulate))
 
     def _probe_fn(self, l):
         ly = self.layers[l]
         if l == 0:
-            return ly._k_probe
+            return ly.fn("k_probe")
         prev = self.layers[l - 1]
-
-        def run():
-            # the probe keys of the previous layer's picks (and query rows) only
-            kvf.recompute_qkv(ly.layer, ly.x, prev.rows, prev.pos, ly.w, kvf.KVF_OUT_K,
-                              ly.rope_cos, ly.rope_sin, k_out=ly.k_probe, kv_out_row=prev.rows,
-                              M=prev.M, workspace=ly.gemm_ws)
-        return run
+        # the probe keys of the previous layer's picks (and query rows) only
+        return self._prepared(("k_probe", l), lambda: kvf.recompute_qkv(
+            ly.layer, ly.x, prev.rows, prev.pos, ly.w, kvf.KVF_OUT_K, ly.rope_cos, ly.rope_sin,
+            k_out=ly.k_probe, kv_out_row=prev.rows, M=prev.M, workspace=ly.gemm_ws))
 
     def _prog_score_fn(self, l):
         ly = self.layers[l]
         elig = None if l == 0 else self.layers[l - 1].sel_mask
-
-        def run():
-            kvf.score(kvf.KVF_SCORE_DEVIATION, ly.layer, ly.kb, ly.fused_k, ly.k_probe, None,
-                      ly.scores, eligible=elig)
-        return run
+        return self._prepared(("score", l), lambda: kvf.score(
+            kvf.KVF_SCORE_DEVIATION, ly.layer, ly.kb, ly.fused_k, ly.k_probe, None, ly.scores,
+            eligible=elig))
 
     def _prog_select_fn(self, l):
         ly = self.layers[l]
-
-        def run():
-            kvf.select_topk(ly.scores, ly.kb, ly.k_per_req, ly.sel, ly.rows, ly.pos,
-                            out_mask=ly.sel_mask)
-        return run
+        return self._prepared(("select", l), lambda: kvf.select_topk(
+            ly.scores, ly.kb, ly.k_per_req, ly.sel, ly.rows, ly.pos, out_mask=ly.sel_mask))
 
     # ------------------------------------------------------------------ passes
     def run(self, forced_sel: Optional[Sequence] = None):
@@ -291,6 +297,9 @@ class MultiLayerGPU:
         torch.cuda.synchronize()
         self.stream_pools = on
         self._slot_reader = [None, None]
+        self._prep = {}
+        for ly in self.layers:
+            ly.invalidate_prepared()
 
     def cache_bytes(self) -> int:
         """Bytes of per-chunk cache a streamed pass copies in."""
