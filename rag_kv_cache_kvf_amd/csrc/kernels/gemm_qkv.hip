@@ -645,8 +645,8 @@ struct Bf16Plan {
 // Tile shape of a bf16 call.  Column tile 256 when every requested segment
 // is a multiple of it; row-tile height the candidate whose tiles fill 256 CUs
 // with the least per-CU work (rounds x tile area, ties to the larger tile).
-// A call with too few tiles for half the chip (few rows) splits K instead:
-// 64 or 128-row tiles, K cut into 2^j slices of >= 256, the count that
+// A call with too few tiles for half the chip (few rows) takes 64 or
+// 128 x 128 tiles instead and may split K: 2^j slices of >= 256, the count that
 // brings the workgroups closest to one per CU (more slices shorten each
 // workgroup's K loop but add partial sums the finish kernel must read: at
 // 64 rows, 192 workgroups beat 384; at 256 rows, 320 beat 160), the slices
@@ -690,7 +690,7 @@ Bf16Plan plan_bf16(const kvf_layer_desc& L, int M, uint32_t mask) {
       q.splits = sp;
     }
   }
-  return q.splits > 1 ? q : p;
+  return q;                                // smaller tiles, split or not: more workgroups than p
 }
 
 }  // namespace
