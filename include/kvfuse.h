@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define KVF_ABI_VERSION 7
+#define KVF_ABI_VERSION 8
 #define KVF_MAX_REQ 64      /* requests per call (batch metadata is passed by value) */
 
 typedef enum {
@@ -323,8 +323,12 @@ kvf_status kvf_static_counts(const kvf_batch* batch, const kvf_chunk* chunks_hos
  * ([QCF] 2.1.3 Eq. 7) into this call.  Entries outside [0, kv_out_rows) are
  * skipped; destination rows must be unique.  Q is always written densely.
  * workspace: kvf_recompute_workspace_size(layer, M, out_mask) bytes of
- * device memory (may be NULL when that is 0); calls with few rows use it for
- * per-slice partial sums, so two calls sharing one workspace must be ordered.
+ * device memory (may be NULL when that is 0).  Calls with few rows split the
+ * hidden dimension: the workspace then holds 4096 bytes of per-tile arrival
+ * counters, which must be zero before its first use and which every call
+ * leaves zero, followed by the slices' partial sums.  Calls of any shape may
+ * share one workspace (the counters sit at a fixed offset) but must not
+ * overlap in time.
  */
 size_t kvf_recompute_workspace_size(const kvf_layer_desc* layer, int32_t M,
                                     uint32_t out_mask);

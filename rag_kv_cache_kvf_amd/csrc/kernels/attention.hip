@@ -49,7 +49,7 @@ struct AttnArgs {
   int fold_from;                 // dispatch slots at or past this run smallest-first
   int parts;                     // > 1: long row tiles split their keys over up to this many workgroups
   int split_min;                 // key tiles from which a row tile is split
-  float* ws_part;                // [tiles * Hkv, 2 parts, partial values, threads]
+  float* ws_part;                // [tiles * Hkv, parts, 16-byte chunks, threads]
   int* ws_cnt;                   // [tiles * Hkv] arrivals; zero between calls
   int rows_per_tile;             // R
   const void* q;
@@ -97,11 +97,36 @@ constexpr int kAThreads = 64 * kAWaves;
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
-typedef __attribute__((address_space(3))) void lds_void_t;
 // Word 3 of a gfx9-family buffer descriptor for raw byte addressing
 // (stride 0): 32-bit data format, no swizzle; accesses at or past the
 // descriptor's byte range read as zero.
 constexpr int kBufferRsrcWord3 = 0x00020000;
+
+// Buffer descriptor over `bytes` bytes at `base` (wave-uniform values).
+__device__ __forceinline__ u32x4_t buffer_rsrc(const void* base, int bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  u32x4_t r;
+  r[0] = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(p));
+  r[1] = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(p >> 32) & 0xffffu);   // stride 0
+  r[2] = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(bytes));
+  r[3] = kBufferRsrcWord3;
+  return r;
+}
+
+// One 16-byte-per-lane buffer -> LDS copy (lane l writes lds_base + 16 l;
+// lds_base wave-uniform; bytes past the descriptor's range land as zeros).
+// Issued from inline assembly so that the compiler's wait-count tracking
+// does not see it: it cannot tell which LDS buffer a copy writes, and would
+// otherwise wait for every copy in flight before the next LDS read, that is
+// half a tile after the copy was issued.  Completion is awaited explicitly
+// by copies_landed_barrier.  The s_nop keeps one wait state between the M0
+// write and the copy that reads it.
+__device__ __forceinline__ void buffer_copy16(const u32x4_t& rsrc, int voff, const void* lds_base) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds_base)));
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               ::"s"(m0), "v"(voff), "s"(rsrc) : "memory");
+}
 
 // XOR applied to the 16-byte chunk index of tile row `row`.  LDS serves a
 // wide read over 64 banks (256 B) per cycle: 16 lanes of a 16-byte read or
@@ -252,10 +277,8 @@ attn_bf16_kernel(AttnArgs a) {
   // per-row clamp is needed.  A lane's byte offset within a tile is fixed
   // per copy instruction; the tile adds kb0 rows.
   const int rs2 = static_cast<int>(row_stride) * 2;        // bytes per key row
-  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<bf16_t*>(Kreq), 0, klim > 0 ? klim * rs2 : 0, kBufferRsrcWord3);
-  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<bf16_t*>(Vreq), 0, klim > 0 ? klim * rs2 : 0, kBufferRsrcWord3);
+  const u32x4_t krs = buffer_rsrc(Kreq, klim > 0 ? klim * rs2 : 0);
+  const u32x4_t vrs = buffer_rsrc(Vreq, klim > 0 ? klim * rs2 : 0);
   int dvo[NDMA];
   {
     const int dma_rr = lane / CPR, dma_p = lane % CPR;
@@ -265,12 +288,10 @@ attn_bf16_kernel(AttnArgs a) {
       dvo[j] = row * rs2 + ((dma_p ^ chunk_xor<D>(row)) << 4);   // slot holds logical chunk p ^ x
     }
   }
-  auto dma_tile = [&](__amdgpu_buffer_rsrc_t rs, bf16_t* dst, int kb0) __attribute__((always_inline)) {
+  auto dma_tile = [&](const u32x4_t& rs, bf16_t* dst, int kb0) __attribute__((always_inline)) {
     const int toff = kb0 * rs2;
 #pragma unroll
-    for (int j = 0; j < NDMA; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(dst + (w * NDMA + j) * RPI * D), 16u,
-                                               static_cast<unsigned>(dvo[j] + toff), 0u, 0u, 0u);
+    for (int j = 0; j < NDMA; ++j) buffer_copy16(rs, dvo[j] + toff, dst + (w * NDMA + j) * RPI * D);
   };
 
   // Softmax state in the log2 domain: scores enter as s * c with
@@ -447,6 +468,10 @@ attn_bf16_kernel(AttnArgs a) {
     if (t0 >= n_plain) apply_mask(s_a, t0 * kAT);
     raise_max(s_a);                                 // the first block sets the max exactly
   }
+  // Every global load the compiler tracks (Q) has completed here on all
+  // paths; saying so keeps it from waiting for them, and so for the tile
+  // copies behind them, inside the loop (vmcnt(0), expcnt and lgkmcnt free).
+  __builtin_amdgcn_s_waitcnt(0x0F70);
   // two tiles per trip so every buffer is a distinct static array
   int tl = t0;                                      // last tile processed
   for (int t = t0; t < t1; t += 2) {
@@ -463,29 +488,34 @@ attn_bf16_kernel(AttnArgs a) {
   }
 
   if (split) {
-    // Partial state of this part, value-major so a store is one coalesced
-    // row per value: O (unnormalised), then m and the lane's half of l.
-    // Every partial value is stored and loaded as a relaxed device-scope
-    // atomic, which is coherent across the XCDs' L2 caches, and the arrival
-    // counter is bumped only after the barrier has waited for all of the
-    // workgroup's stores to complete.  Device-scope fences would do the same
-    // by writing back and invalidating the whole L2, evicting the K/V tiles
-    // the other workgroups on this XCD are streaming.
-    constexpr int NV = kQB * (DB * 16 + 2);
+    // Partial state of this part in 16-byte chunks, chunk-major so that a
+    // wave's store of one chunk is 1 KB contiguous: per query block the
+    // unnormalised O (DB x 4 chunks), then (m, the lane's half of l, 0, 0).
+    // The chunks are stored and loaded with device-scope coherence, which
+    // reaches across the XCDs' L2 caches, and the arrival counter is bumped
+    // only after the barrier has waited for all of the workgroup's stores.
+    // Device-scope fences would do the same by writing back and invalidating
+    // the whole L2, evicting the K/V tiles the other workgroups on this XCD
+    // are streaming.
+    constexpr int NC = kQB * (DB * 4 + 1);
     const int64_t item = static_cast<int64_t>(tile) * hkv + g;
-    float* mine = a.ws_part + ((item * a.parts + part) * NV) * kAThreads + tid;
-    auto put = [&](int e, float x) __attribute__((always_inline)) {
-      __hip_atomic_store(mine + e * kAThreads, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const __amdgpu_buffer_rsrc_t pr = handoff_rsrc(
+        a.ws_part, static_cast<int64_t>(a.total_tiles) * hkv * a.parts * NC * kAThreads * 16);
+    auto chunk_off = [&](int pt, int c) __attribute__((always_inline)) {
+      return static_cast<uint32_t>((((item * a.parts + pt) * NC + c) * kAThreads + tid) * 16);
     };
-    int e = 0;
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb) {
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) put(e++, o[qb][db][i]);
-      put(e++, m_run[qb]);
-      put(e++, l_lane[qb]);
+        for (int c4 = 0; c4 < 4; ++c4) {
+          const f32x4_t v = {o[qb][db][4 * c4], o[qb][db][4 * c4 + 1], o[qb][db][4 * c4 + 2],
+                             o[qb][db][4 * c4 + 3]};
+          put_dev4(pr, chunk_off(part, qb * (DB * 4 + 1) + db * 4 + c4), v);
+        }
+      const f32x4_t ml = {m_run[qb], l_lane[qb], 0.f, 0.f};
+      put_dev4(pr, chunk_off(part, qb * (DB * 4 + 1) + DB * 4), ml);
     }
     __syncthreads();                              // waits for this workgroup's stores
     if (tid == 0)
@@ -494,23 +524,21 @@ attn_bf16_kernel(AttnArgs a) {
     if (s_pos[0] != np - 1) return;               // not the last to finish: it merges
     for (int op = 0; op < np; ++op) {
       if (op == part) continue;
-      const float* other = a.ws_part + ((item * a.parts + op) * NV) * kAThreads + tid;
-      auto get = [&](int e) __attribute__((always_inline)) {
-        return __hip_atomic_load(other + e * kAThreads, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      };
-      e = 0;
 #pragma unroll
       for (int qb = 0; qb < kQB; ++qb) {
-        const float m2 = get(e + DB * 16);
-        const float l2 = get(e + DB * 16 + 1);
+        const f32x4_t ml = get_dev4(pr, chunk_off(op, qb * (DB * 4 + 1) + DB * 4));
+        const float m2 = ml[0], l2 = ml[1];
         const float mm = fmaxf(m_run[qb], m2);
         const float mu = mm == -INFINITY ? 0.f : mm;
         const float a1 = __builtin_amdgcn_exp2f(m_run[qb] - mu), a2 = __builtin_amdgcn_exp2f(m2 - mu);
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) o[qb][db][i] = o[qb][db][i] * a1 + get(e++) * a2;
-        e += 2;
+          for (int c4 = 0; c4 < 4; ++c4) {
+            const f32x4_t v = get_dev4(pr, chunk_off(op, qb * (DB * 4 + 1) + db * 4 + c4));
+#pragma unroll
+            for (int e4 = 0; e4 < 4; ++e4) o[qb][db][4 * c4 + e4] = o[qb][db][4 * c4 + e4] * a1 + v[e4] * a2;
+          }
         l_lane[qb] = l_lane[qb] * a1 + l2 * a2;
         m_run[qb] = mm;
       }
@@ -658,11 +686,11 @@ static AttnSplitLayout attn_split_layout(const kvf_layer_desc& L, const BatchArg
   for (int r = 0; r < B.n_req; ++r) tiles += ceil_div(cu_q[r + 1] - cu_q[r], R);
   const int64_t items = tiles * L.n_kv_heads;
   if (items == 0 || items > kSplitMaxItems) return s;
-  const int64_t nv = kQB * (L.head_dim / 32 * 16 + 2);
+  const int64_t chunks = kQB * (L.head_dim / 32 * 4 + 1);   // 16-byte chunks per thread and part
   s.items = items;
   s.parts = static_cast<int>(std::min<int64_t>(
       kSplitMaxParts, std::max<int64_t>(2, (kSplitMaxItems + items - 1) / items)));
-  s.off_cnt = static_cast<size_t>(items * s.parts * nv * kAThreads) * sizeof(float);
+  s.off_cnt = static_cast<size_t>(items * s.parts * chunks * kAThreads) * 16;
   s.bytes = s.off_cnt + static_cast<size_t>(items) * sizeof(int);
   return s;
 }
@@ -788,30 +816,6 @@ struct MassArgs {
   int* cnt_cols;                 // [total_ktiles]
   ScoreOut out;                  // scores [sum N]
 };
-
-// Relaxed device-scope atomics: coherent across the XCDs' L2 caches without
-// the whole-cache write-back/invalidate of a device-scope fence.  A
-// workgroup stores its partial results this way, the barrier waits for the
-// stores, then one arrival counter is bumped; the last arrival reads the
-// others' results the same way.
-__device__ __forceinline__ void put_dev(float* p, float x) {
-  __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float get_dev(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// all threads: returns true in the workgroup that arrived last of n
-__device__ __forceinline__ bool arrive_last(int* cnt, int n, int* s_flag) {
-  __syncthreads();                                // this workgroup's stores have completed
-  if (threadIdx.x == 0) {
-    const int old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const bool last = old == n - 1;
-    if (last) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);   // next call
-    *s_flag = last;
-  }
-  __syncthreads();
-  return *s_flag != 0;
-}
 
 constexpr int kMK = 128;         // keys per workgroup (4 waves x 32)
 constexpr int kMQS = 256;        // query vectors staged per round (LDS)

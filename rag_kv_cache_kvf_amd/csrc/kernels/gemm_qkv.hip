@@ -19,8 +19,6 @@
 
 namespace kvf {
 
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) const void global_cvoid_t;
 
 struct GemmArgs {
   const void* x;
@@ -38,13 +36,13 @@ struct GemmArgs {
   int seg_heads[3];         // heads of each segment
   int seg_w_row0[3];        // first weight row of each segment
   void* out[3];
-  // split-K: blockIdx.z covers K range [z k_len, (z+1) k_len) and writes raw
-  // fp32 sums to partial[z][m][c] (c = weight row, c_total columns); a
-  // second kernel adds the slices, rotates and stores.  partial == nullptr:
-  // one slice, the kernel finishes the rows itself.
+  // split-K: blockIdx.z covers K range [z k_len, (z+1) k_len) and stores its
+  // raw fp32 sums in partial (one tile-sized block per slice and output
+  // tile); the last slice of an output tile to finish (tile_cnt counts
+  // arrivals) adds the slices in order and finishes the rows.
   float* partial;
+  int* tile_cnt;            // [row tiles x column tiles], zero between calls
   int k_len;
-  int c_total;
   // K/V destination rows: row m of K and V goes to row kv_row[m] of its
   // output (kv_rows rows; entries outside are skipped); nullptr: row m
   const int32_t* kv_row;
@@ -106,6 +104,8 @@ __device__ __forceinline__ int segment_of(const int (&n_tiles)[3], int& t) {
 // Epilogue: 32 rows at a time go through LDS as fp32, where each thread
 // takes 8 channels j.. of a head together with their RoPE partners j+d/2..,
 // rotates them at the row's position and writes both as 16-byte bf16 stores.
+// With K split, every slice stores its raw sums; the last slice of the tile
+// to arrive reads all of them back in slice order and runs the epilogue.
 constexpr int kBK = 64, kGThreads = 256;
 
 template <int BM, int BN>
@@ -139,11 +139,12 @@ __device__ __forceinline__ int gswz(int row, int chunk) {   // element offset of
 // assembly so the copies are invisible to the compiler's wait-count tracking:
 // their completion is awaited explicitly by dma_wait_barrier, which lets
 // stages k+1.. stay in flight while stage k is read.  lds_base must be
-// wave-uniform; lane l writes lds_base + 16 l.
+// wave-uniform; lane l writes lds_base + 16 l.  The s_nop keeps one wait
+// state between the M0 write and the copy that reads it.
 __device__ __forceinline__ void dma16(const void* src, const void* lds_base) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane(
       static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds_base)));
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(src)
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(src)
                : "memory");
 }
 
@@ -163,7 +164,7 @@ __device__ __forceinline__ void lds_dma_wait_barrier() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"i"(N) : "memory");
 }
 
-template <int BM, int BN, int WM>
+template <int BM, int BN, int WM, bool SPLIT>
 __global__ void __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 gemm_qkv_bf16_kernel(GemmArgs a) {
   constexpr int WN = 4 / WM;                // wave grid WM x WN
@@ -202,6 +203,7 @@ gemm_qkv_bf16_kernel(GemmArgs a) {
 
   int tx, t, kz;
   xcd_tile(tx, t, kz);
+  const int tile_id = tx + static_cast<int>(gridDim.x) * t;   // output tile (row tile fastest)
   const int seg = segment_of(a.n_tiles, t);
   const int n0 = t * BN;                    // first column inside the segment
   const int m0 = tx * BM;
@@ -258,25 +260,23 @@ gemm_qkv_bf16_kernel(GemmArgs a) {
   constexpr int ROUNDS = (BM + ER - 1) / ER;
   int epos[ROUNDS][UPT];
   int64_t erow[ROUNDS][UPT];
-  if (!a.partial) {
 #pragma unroll
-    for (int rd = 0; rd < ROUNDS; ++rd)
+  for (int rd = 0; rd < ROUNDS; ++rd)
 #pragma unroll
-      for (int i = 0; i < UPT; ++i) {
-        const int m = m0 + rd * ER + (tid + kGThreads * i) / UPR;
-        int pos = -1;                                   // -1: row not stored
-        int64_t orow = -1;
-        if (rd * ER + (tid + kGThreads * i) / UPR < BM && m < a.M && row_ok(a, m)) {
-          pos = a.row_pos[m];
-          if (seg < 2 && (pos < 0 || pos >= a.rope_n)) pos = -1;
-          if (seg == 2) pos = 0;
-          orow = out_row(a, seg, m);
-          if (orow < 0) pos = -1;
-        }
-        epos[rd][i] = pos;
-        erow[rd][i] = orow;
+    for (int i = 0; i < UPT; ++i) {
+      const int m = m0 + rd * ER + (tid + kGThreads * i) / UPR;
+      int pos = -1;                                     // -1: row not stored
+      int64_t orow = -1;
+      if (rd * ER + (tid + kGThreads * i) / UPR < BM && m < a.M && row_ok(a, m)) {
+        pos = a.row_pos[m];
+        if (seg < 2 && (pos < 0 || pos >= a.rope_n)) pos = -1;
+        if (seg == 2) pos = 0;
+        orow = out_row(a, seg, m);
+        if (orow < 0) pos = -1;
       }
-  }
+      epos[rd][i] = pos;
+      erow[rd][i] = orow;
+    }
 
   // operand read offsets (the swizzle depends on row mod 8 = lane mod 8)
   const int lr = lane & 31, hf = lane >> 5;
@@ -394,21 +394,50 @@ gemm_qkv_bf16_kernel(GemmArgs a) {
     }
   }
 
-  if (a.partial) {
-    // raw slice sums; each 32-lane run stores 128 contiguous bytes of a row
-    float* part = a.partial + static_cast<int64_t>(kz) * a.M * a.c_total;
-    const int c0 = a.seg_w_row0[seg] + n0 + WC * wc + lr;
+  if constexpr (SPLIT) {
+    // Raw slice sums in the thread's own order: slice z, output tile, then
+    // per (32-row block, 32-column block, 4-row group) one 16-byte chunk per
+    // thread, so every wave store or load is 1 KB contiguous.  Stored and
+    // read with device-scope coherence (the slices run on different XCDs).
+    constexpr int CH = MB * NI * 4;                  // chunks per thread
+    const int64_t tiles = static_cast<int64_t>(gridDim.x) * gridDim.y;
+    const __amdgpu_buffer_rsrc_t pr =
+        handoff_rsrc(a.partial, static_cast<int64_t>(gridDim.z) * tiles * CH * kGThreads * 16);
+    auto chunk_off = [&](int z, int c) -> uint32_t {
+      return static_cast<uint32_t>((((z * tiles + tile_id) * CH + c) * kGThreads + tid) * 16);
+    };
 #pragma unroll
     for (int mi = 0; mi < MB; ++mi)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = m0 + WR * wr + mi * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-        if (m >= a.M) continue;
+      for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          const f32x4_t v = {acc[mi][ni][4 * rq], acc[mi][ni][4 * rq + 1], acc[mi][ni][4 * rq + 2],
+                             acc[mi][ni][4 * rq + 3]};
+          put_dev4(pr, chunk_off(kz, (mi * NI + ni) * 4 + rq), v);
+        }
+    // (the stage buffers are idle: every copy has landed and been read)
+    if (!arrive_last(a.tile_cnt + tile_id, static_cast<int>(gridDim.z), reinterpret_cast<int*>(smem)))
+      return;
+    // the last slice to arrive: the tile's sums over slices 0, 1, .. in order
+#pragma unroll
+    for (int mi = 0; mi < MB; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
+    for (int z = 0; z < static_cast<int>(gridDim.z); ++z) {
+#pragma unroll
+      for (int mi = 0; mi < MB; ++mi)
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni)
-          part[static_cast<int64_t>(m) * a.c_total + c0 + 32 * ni] = acc[mi][ni][r];
-      }
-    return;
+#pragma unroll
+          for (int rq = 0; rq < 4; ++rq) {
+            const f32x4_t v = get_dev4(pr, chunk_off(z, (mi * NI + ni) * 4 + rq));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[mi][ni][4 * rq + e] += v[e];
+          }
+    }
   }
   __syncthreads();
 
@@ -480,64 +509,6 @@ gemm_qkv_bf16_kernel(GemmArgs a) {
     }
     if (rd + 1 < ROUNDS) __syncthreads();
   }
-}
-
-// ---------------------------------------------------------------------------
-// split-K finish: one thread per (row, 8 low channels of a head): add the
-// K slices of those channels and of their RoPE partners, rotate, store bf16.
-// units_q / units_k / units_v: such units per row in each requested segment.
-// ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(256) gemm_split_finish_kernel(GemmArgs a, int splits,
-                                                                int units_q, int units_k,
-                                                                int units_v) {
-  const int upr = units_q + units_k + units_v;
-  const int64_t u = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (u >= static_cast<int64_t>(a.M) * upr) return;
-  const int m = static_cast<int>(u / upr);
-  int r = static_cast<int>(u % upr);
-  int seg = 0;
-  if (r >= units_q) {
-    r -= units_q;
-    seg = 1;
-    if (r >= units_k) {
-      r -= units_k;
-      seg = 2;
-    }
-  }
-  if (!row_ok(a, m)) return;
-  const int d = a.d, half = d >> 1;
-  const int head = r / (half / 8), j0 = (r % (half / 8)) * 8;
-  const int cl = head * d + j0, ch = cl + half;
-  float lo[8] = {0, 0, 0, 0, 0, 0, 0, 0}, hi[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  const int64_t slice = static_cast<int64_t>(a.M) * a.c_total;
-  const float* p = a.partial + static_cast<int64_t>(m) * a.c_total + a.seg_w_row0[seg];
-  for (int z = 0; z < splits; ++z, p += slice) {
-    float t[8];
-    Elem<float>::load8(p + cl, t);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) lo[e] += t[e];
-    Elem<float>::load8(p + ch, t);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) hi[e] += t[e];
-  }
-  if (seg < 2) {
-    const int pos = a.row_pos[m];
-    if (pos < 0 || pos >= a.rope_n) return;
-    float cs[8], sn[8];
-    Elem<float>::load8(a.rope_cos + static_cast<int64_t>(pos) * half + j0, cs);
-    Elem<float>::load8(a.rope_sin + static_cast<int64_t>(pos) * half + j0, sn);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float x = lo[e], y = hi[e];
-      lo[e] = x * cs[e] - y * sn[e];
-      hi[e] = y * cs[e] + x * sn[e];
-    }
-  }
-  const int64_t dst = out_row(a, seg, m);
-  if (dst < 0) return;
-  bf16_t* orow = static_cast<bf16_t*>(a.out[seg]) + dst * a.seg_heads[seg] * d;
-  Elem<bf16_t>::store8(orow + cl, lo);
-  Elem<bf16_t>::store8(orow + ch, hi);
 }
 
 // ---------------------------------------------------------------------------
@@ -648,9 +619,8 @@ struct Bf16Plan {
 // A call with too few tiles for half the chip (few rows) takes 64 or
 // 128 x 128 tiles instead and may split K: 2^j slices of >= 256, the count that
 // brings the workgroups closest to one per CU (more slices shorten each
-// workgroup's K loop but add partial sums the finish kernel must read: at
-// 64 rows, 192 workgroups beat 384; at 256 rows, 320 beat 160), the slices
-// added by gemm_split_finish_kernel.
+// workgroup's K loop but add partial sums to store and read back), the
+// slices added by the last slice of each output tile to finish.
 Bf16Plan plan_bf16(const kvf_layer_desc& L, int M, uint32_t mask) {
   const int heads[3] = {L.n_q_heads, L.n_kv_heads, L.n_kv_heads};
   const uint32_t bits[3] = {KVF_OUT_Q, KVF_OUT_K, KVF_OUT_V};
@@ -695,12 +665,18 @@ Bf16Plan plan_bf16(const kvf_layer_desc& L, int M, uint32_t mask) {
 
 }  // namespace
 
+// Split-K workspace: kSplitCounterBytes of arrival counters (one int per
+// output tile, zero between calls), then the slices' partial sums.  The
+// counters sit at a fixed offset so that calls of any shape can share one
+// workspace without their partial sums landing on another call's counters.
+constexpr int kSplitCounterBytes = 4096;
+
 size_t recompute_workspace(const kvf_layer_desc& L, int M, uint32_t mask) {
   if (L.dtype != KVF_BF16 || M <= 0 || mask == 0) return 0;
   const Bf16Plan p = plan_bf16(L, M, mask);
   if (p.splits == 1) return 0;
-  const int64_t c_total = static_cast<int64_t>(L.n_q_heads + 2 * L.n_kv_heads) * L.head_dim;
-  return static_cast<size_t>(p.splits) * M * c_total * sizeof(float);
+  const int64_t tiles = static_cast<int64_t>(ceil_div(M, p.bm)) * (p.n_tiles[0] + p.n_tiles[1] + p.n_tiles[2]);
+  return kSplitCounterBytes + static_cast<size_t>(p.splits) * tiles * p.bm * p.bn * sizeof(float);
 }
 
 hipError_t launch_recompute(const kvf_layer_desc& L, const void* x, int64_t x_rows,
@@ -733,7 +709,6 @@ hipError_t launch_recompute(const kvf_layer_desc& L, const void* x, int64_t x_ro
     a.out[s] = outs[s];
     row0 += heads[s] * L.head_dim;
   }
-  a.c_total = row0;
   if (L.dtype == KVF_BF16) {
     for (int s = 0; s < 3; ++s)
       if ((heads[s] * L.head_dim) % 128 != 0) return hipErrorInvalidValue;  // rejected earlier
@@ -747,35 +722,33 @@ hipError_t launch_recompute(const kvf_layer_desc& L, const void* x, int64_t x_ro
     if (total == 0 || total > 65535) return hipErrorInvalidValue;
     if (p.splits > 1) {
       if (ws == nullptr || ws_bytes < recompute_workspace(L, M, mask)) return hipErrorInvalidValue;
-      a.partial = static_cast<float*>(ws);
+      if (static_cast<int64_t>(ceil_div(M, p.bm)) * total * static_cast<int64_t>(sizeof(int)) >
+          kSplitCounterBytes)
+        return hipErrorInvalidValue;                // the plan splits small calls only
+      a.tile_cnt = static_cast<int*>(ws);
+      a.partial = reinterpret_cast<float*>(static_cast<char*>(ws) + kSplitCounterBytes);
       a.k_len = L.hidden / p.splits;
     }
     const dim3 grid(ceil_div(M, p.bm), total, p.splits);
     bool launched = false;
-#define KVF_GEMM_CASE(BM_, BN_, WM_)                                                       \
-  if (!launched && p.bm == BM_ && p.bn == BN_ && p.wm == WM_) {                            \
-    hipLaunchKernelGGL((gemm_qkv_bf16_kernel<BM_, BN_, WM_>), grid, dim3(kGThreads), 0, st, \
-                       a);                                                                 \
-    launched = true;                                                                       \
+    const bool split = p.splits > 1;
+#define KVF_GEMM_CASE(BM_, BN_, WM_, SPLIT_)                                                  \
+  if (!launched && p.bm == BM_ && p.bn == BN_ && p.wm == WM_ && split == SPLIT_) {            \
+    hipLaunchKernelGGL((gemm_qkv_bf16_kernel<BM_, BN_, WM_, SPLIT_>), grid, dim3(kGThreads), 0, \
+                       st, a);                                                                \
+    launched = true;                                                                          \
   }
-    KVF_GEMM_CASE(256, 128, 1)
-    KVF_GEMM_CASE(192, 128, 1)
-    KVF_GEMM_CASE(160, 128, 1)
-    KVF_GEMM_CASE(128, 128, 1)
-    KVF_GEMM_CASE(64, 128, 1)
-    KVF_GEMM_CASE(160, 256, 1)
-    KVF_GEMM_CASE(128, 256, 1)
+    KVF_GEMM_CASE(256, 128, 1, false)
+    KVF_GEMM_CASE(192, 128, 1, false)
+    KVF_GEMM_CASE(160, 128, 1, false)
+    KVF_GEMM_CASE(128, 128, 1, false)
+    KVF_GEMM_CASE(64, 128, 1, false)
+    KVF_GEMM_CASE(160, 256, 1, false)
+    KVF_GEMM_CASE(128, 256, 1, false)
+    KVF_GEMM_CASE(128, 128, 1, true)     // the few-row plans that split K
+    KVF_GEMM_CASE(64, 128, 1, true)
 #undef KVF_GEMM_CASE
     if (!launched) return hipErrorInvalidValue;
-    if (p.splits > 1) {
-      const int per_head = L.head_dim / 16;
-      const int uq = (mask & KVF_OUT_Q) ? L.n_q_heads * per_head : 0;
-      const int uk = (mask & KVF_OUT_K) ? L.n_kv_heads * per_head : 0;
-      const int uv = (mask & KVF_OUT_V) ? L.n_kv_heads * per_head : 0;
-      const int64_t units = static_cast<int64_t>(M) * (uq + uk + uv);
-      hipLaunchKernelGGL(gemm_split_finish_kernel, dim3(static_cast<unsigned>((units + 255) / 256)),
-                         dim3(256), 0, st, a, p.splits, uq, uk, uv);
-    }
   } else {
     int pt[3], total = 0;
     for (int s = 0; s < 3; ++s) {

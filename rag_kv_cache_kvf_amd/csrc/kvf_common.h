@@ -105,6 +105,48 @@ __device__ __forceinline__ float group_sum(float v, int width) {
 // ---------------------------------------------------------------------------
 // batch metadata passed by value in kernel arguments
 // ---------------------------------------------------------------------------
+// hand-off between workgroups
+// ---------------------------------------------------------------------------
+// Relaxed device-scope atomics: coherent across the XCDs' L2 caches without
+// the whole-cache write-back/invalidate of a device-scope fence.  A
+// workgroup stores its partial results this way, the barrier waits for the
+// stores, then one arrival counter is bumped; the last arrival reads the
+// others' results the same way.
+__device__ __forceinline__ void put_dev(float* p, float x) {
+  __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float get_dev(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// The same coherence for 16-byte accesses: buffer loads/stores with the
+// device-scope cache policy (sc1), through a descriptor over the hand-off
+// buffer (byte offsets below 4 GiB).
+constexpr int kDeviceScope = 16;                  // cache-policy bits: sc1
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t handoff_rsrc(void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(base, 0, static_cast<int>(bytes < 0x7fffffff ? bytes : 0x7fffffff),
+                                           0x00020000);
+}
+__device__ __forceinline__ void put_dev4(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4_t v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, off, 0, kDeviceScope);
+}
+__device__ __forceinline__ f32x4_t get_dev4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kDeviceScope));
+}
+// All threads: true in the workgroup that arrived last of n at *cnt, which
+// that workgroup sets back to zero for the next call.
+__device__ __forceinline__ bool arrive_last(int* cnt, int n, int* s_flag) {
+  __syncthreads();                                // this workgroup's stores have completed
+  if (threadIdx.x == 0) {
+    const int old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = old == n - 1;
+    if (last) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *s_flag = last;
+  }
+  __syncthreads();
+  return *s_flag != 0;
+}
+
+// ---------------------------------------------------------------------------
 struct BatchArgs {
   int n_req;
   int cu_T[KVF_MAX_REQ + 1];   // row offsets of each request (x, fused cache)

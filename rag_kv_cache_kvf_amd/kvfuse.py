@@ -332,15 +332,16 @@ def recompute_qkv(layer: Layer, x: torch.Tensor, row_src: Optional[torch.Tensor]
                   v_out: Optional[torch.Tensor] = None, M: Optional[int] = None,
                   workspace: Optional[torch.Tensor] = None, kv_out_row: Optional[torch.Tensor] = None,
                   stream=None):
-    """workspace: kvf_recompute_workspace_size bytes; allocated here when
-    omitted and needed (pass one to keep the call allocation-free).
+    """workspace: kvf_recompute_workspace_size bytes, zeroed before its first
+    use; allocated here when omitted and needed (pass one to keep the call
+    allocation-free).
     kv_out_row: destination rows of K/V in k_out / v_out (e.g. the fused cache)."""
     d = layer.desc()
     M = int(row_pos.shape[0]) if M is None else M
     if workspace is None:
         need = recompute_workspace_size(layer, M, out_mask)
         if need:
-            workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+            workspace = torch.zeros(need, dtype=torch.uint8, device=x.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     kv_rows = 0
     if kv_out_row is not None:

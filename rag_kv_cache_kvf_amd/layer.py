@@ -182,7 +182,8 @@ class FusedLayerGPU:
             need.append(kvf.recompute_workspace_size(L, T_total, kvf.KVF_OUT_K))
         elif self.mass:
             need.append(kvf.recompute_workspace_size(L, nU, QKV))
-        self.gemm_ws = torch.empty(max(max(need), 1), dtype=torch.uint8, device=dev)
+        # zeroed: split projections keep arrival counters at its start
+        self.gemm_ws = torch.zeros(max(max(need), 1), dtype=torch.uint8, device=dev)
         # key-split workspace of the attention call: zero-filled once, every
         # call leaves it zeroed
         attn_need = kvf.attention_workspace_size(self.layer, self.kb, self.cu_q)

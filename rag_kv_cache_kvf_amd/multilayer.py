@@ -79,7 +79,7 @@ class MultiLayerGPU:
                     need = kvf.recompute_workspace_size(ly.layer, self.layers[l - 1].M,
                                                         kvf.KVF_OUT_K)
                     if need > ly.gemm_ws.numel():
-                        ly.gemm_ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+                        ly.gemm_ws = torch.zeros(need, dtype=torch.uint8, device=self.device)
 
         # layer-wise pipeline: per-chunk caches in pinned host memory
         self.stream_pools = wl.stream_pools if stream_pools is None else stream_pools

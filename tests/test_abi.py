@@ -48,7 +48,7 @@ def test_status_strings_and_version(lib):
     lib.kvf_status_string.restype = ctypes.c_char_p
     assert lib.kvf_status_string(0) == b"KVF_OK"
     assert lib.kvf_status_string(2) == b"KVF_ERR_UNSUPPORTED"
-    assert lib.kvf_abi_version() == 7
+    assert lib.kvf_abi_version() == 8
 
 
 def test_budget_matches_oracle(lib):
@@ -109,8 +109,9 @@ def test_validation_errors(lib):
     # bf16 projection of few rows splits K and needs its workspace
     bf = Layer(4096, 32, 8, 128, 1)
     need = lib.kvf_recompute_workspace_size(ctypes.byref(bf), 64, 7)
-    # 48 column tiles of 128 x 4 slices = 192 workgroups, the closest to one per CU
-    assert need == 4 * 64 * (32 + 16) * 128 * 4
+    # 48 column tiles of 128 x 4 slices = 192 workgroups, the closest to one per
+    # CU: 4096 bytes of arrival counters, then the slices' partial sums
+    assert need == 4096 + 4 * 64 * (32 + 16) * 128 * 4
     assert lib.kvf_recompute_qkv(ctypes.byref(bf), FAKE, 64, None, FAKE, 64, FAKE, 7, FAKE, FAKE, 4,
                                  FAKE, FAKE, FAKE, None, 0, None, 0, None) == 3
     assert lib.kvf_recompute_qkv(ctypes.byref(bf), FAKE, 64, None, FAKE, 64, FAKE, 7, FAKE, FAKE, 4,
@@ -152,7 +153,9 @@ def test_validation_errors(lib):
     ba, keep_a = _batch([0, 5184], [5120])
     cq = (ctypes.c_int32 * 2)(0, 1600)
     need = lib.kvf_attention_workspace_size(ctypes.byref(bq), ctypes.byref(ba), cq)
-    assert need == 50 * 8 * (2 * (4 * 16 + 2) * 256 * 4 + 4)
+    # 400 (row tile, kv head) items x 2 parts x (16 + 1) 16-byte chunks per
+    # thread of 256, then one int32 arrival counter per item
+    assert need == 50 * 8 * (2 * (4 * 4 + 1) * 256 * 16 + 4)
     assert lib.kvf_sparse_q_attention(ctypes.byref(bq), ctypes.byref(ba), FAKE, FAKE, cq, FAKE, FAKE,
                                       0.088, FAKE, None, FAKE, need - 1, None) == 3
     big = (ctypes.c_int32 * 2)(0, 5184)

@@ -354,6 +354,43 @@ def test_recompute(kvf, case):
             assert not from_gpu(t).any()
 
 
+def test_recompute_split_shared_workspace(kvf):
+    """Few-row projections split the hidden dimension and hand the slices'
+    sums to the last slice of each output tile through arrival counters at
+    the start of the workspace.  Three calls of different shapes share one
+    workspace: each must match the oracle, and the counters must be zero
+    after every call."""
+    import torch
+    hidden, hq, hkv, d, xr = 2048, 8, 2, 128, 400
+    L = _layer(kvf, hidden, hq, hkv, d, "bf16")
+    c, s = _rope_tables(kvf, 1e6, d, 20000)
+    x = _randn((xr, hidden), 40, "x")
+    w = _randn(((hq + 2 * hkv) * d, hidden), 41, "w", std=1 / math.sqrt(hidden))
+    x_s, w_s = encode(x, "bf16"), encode(w, "bf16")
+    lo = fusion.Layer(hidden, hq, hkv, d, 1e6)
+    shapes = [(120, 7), (33, 7), (64, 3)]
+    needs = [kvf.recompute_workspace_size(L, M, mask) for M, mask in shapes]
+    assert all(n > 4096 for n in needs), needs          # every call splits
+    ws = torch.zeros(max(needs), dtype=torch.uint8, device="cuda")
+    for i, (M, mask) in enumerate(shapes):
+        rows = synth.random_rows(xr, M, 42 + i)
+        pos = synth.random_rows(20000, M, 45 + i)
+        q = torch.zeros((M, hq, d), dtype=torch.bfloat16, device="cuda")
+        k = torch.zeros((M, hkv, d), dtype=torch.bfloat16, device="cuda")
+        v = torch.zeros((M, hkv, d), dtype=torch.bfloat16, device="cuda")
+        kvf.recompute_qkv(L, to_gpu(x_s, "bf16"), to_gpu(rows), to_gpu(pos), to_gpu(w_s, "bf16"), mask,
+                          c, s, q_out=q if mask & 1 else None, k_out=k if mask & 2 else None,
+                          v_out=v if mask & 4 else None, workspace=ws)
+        torch.cuda.synchronize()
+        assert not bool(ws[:4096].any()), f"arrival counters not reset after call {i}"
+        ref = fusion.recompute(decode(x_s, "bf16")[rows], pos, decode(w_s, "bf16"), lo)
+        for bit, name, t in ((1, "q", q), (2, "k", k), (4, "v", v)):
+            if mask & bit:
+                assert_close(from_gpu(t), ref[name], "bf16", f"split recompute {name} call {i} M={M}")
+            else:
+                assert not from_gpu(t).any()
+
+
 @pytest.mark.parametrize("dtype,hidden,M", [("bf16", 1024, 40), ("bf16", 256, 300), ("f32", 128, 50)])
 def test_recompute_skips_rows_outside_tables(kvf, dtype, hidden, M):
     """A row map entry outside x or a position outside the rope table leaves
