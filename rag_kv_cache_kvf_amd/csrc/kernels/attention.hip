@@ -113,19 +113,18 @@ __device__ __forceinline__ u32x4_t buffer_rsrc(const void* base, int bytes) {
   return r;
 }
 
-// One 16-byte-per-lane buffer -> LDS copy (lane l writes lds_base + 16 l;
-// lds_base wave-uniform; bytes past the descriptor's range land as zeros).
+// One 16-byte-per-lane buffer -> LDS copy (lane l writes LDS byte address
+// lds + 16 l; lds wave-uniform; bytes past the descriptor's range land as
+// zeros).
 // Issued from inline assembly so that the compiler's wait-count tracking
 // does not see it: it cannot tell which LDS buffer a copy writes, and would
 // otherwise wait for every copy in flight before the next LDS read, that is
 // half a tile after the copy was issued.  Completion is awaited explicitly
 // by copies_landed_barrier.  The s_nop keeps one wait state between the M0
 // write and the copy that reads it.
-__device__ __forceinline__ void buffer_copy16(const u32x4_t& rsrc, int voff, const void* lds_base) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
-      static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds_base)));
+__device__ __forceinline__ void buffer_copy16(const u32x4_t& rsrc, int voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               ::"s"(m0), "v"(voff), "s"(rsrc) : "memory");
+               ::"s"(lds), "v"(voff), "s"(rsrc) : "memory");
 }
 
 // XOR applied to the 16-byte chunk index of tile row `row`.  LDS serves a
@@ -167,10 +166,13 @@ attn_bf16_kernel(AttnArgs a) {
   constexpr int NDMA = kAT / RPI / kAWaves;   // DMA instructions per wave per tile and tensor
   constexpr int TILE = kAT * D;
   static_assert(NDMA >= 1 && NDMA * RPI * kAWaves == kAT, "tile copy split");
-  __shared__ __attribute__((aligned(16))) bf16_t k0s[TILE];
-  __shared__ __attribute__((aligned(16))) bf16_t k1s[TILE];
-  __shared__ __attribute__((aligned(16))) bf16_t v0s[TILE];
-  __shared__ __attribute__((aligned(16))) bf16_t v1s[TILE];
+  // the two K and two V tile buffers, one array so that every copy's LDS
+  // address is one scalar base plus a constant
+  __shared__ __attribute__((aligned(16))) bf16_t kvs[4 * TILE];
+  bf16_t* const k0s = kvs;
+  bf16_t* const k1s = kvs + TILE;
+  bf16_t* const v0s = kvs + 2 * TILE;
+  bf16_t* const v1s = kvs + 3 * TILE;
   __shared__ int s_pos[2];
 
   const int hkv = a.hkv;
@@ -288,10 +290,13 @@ attn_bf16_kernel(AttnArgs a) {
       dvo[j] = row * rs2 + ((dma_p ^ chunk_xor<D>(row)) << 4);   // slot holds logical chunk p ^ x
     }
   }
+  const uint32_t lds_w = __builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>(kvs)) + w * NDMA * RPI * D * 2);
   auto dma_tile = [&](const u32x4_t& rs, bf16_t* dst, int kb0) __attribute__((always_inline)) {
     const int toff = kb0 * rs2;
+    const uint32_t buf = static_cast<uint32_t>(dst - kvs) * 2;    // a constant at every call
 #pragma unroll
-    for (int j = 0; j < NDMA; ++j) buffer_copy16(rs, dvo[j] + toff, dst + (w * NDMA + j) * RPI * D);
+    for (int j = 0; j < NDMA; ++j) buffer_copy16(rs, dvo[j] + toff, lds_w + buf + j * RPI * D * 2);
   };
 
   // Softmax state in the log2 domain: scores enter as s * c with
@@ -501,8 +506,11 @@ attn_bf16_kernel(AttnArgs a) {
     const int64_t item = static_cast<int64_t>(tile) * hkv + g;
     const __amdgpu_buffer_rsrc_t pr = handoff_rsrc(
         a.ws_part, static_cast<int64_t>(a.total_tiles) * hkv * a.parts * NC * kAThreads * 16);
+    // lane part of a chunk's offset, and its uniform part (a scalar offset)
+    const uint32_t lane_off = static_cast<uint32_t>(tid) * 16;
     auto chunk_off = [&](int pt, int c) __attribute__((always_inline)) {
-      return static_cast<uint32_t>((((item * a.parts + pt) * NC + c) * kAThreads + tid) * 16);
+      return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(
+          static_cast<int>(((item * a.parts + pt) * NC + c) * kAThreads * 16)));
     };
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb) {
@@ -512,10 +520,10 @@ attn_bf16_kernel(AttnArgs a) {
         for (int c4 = 0; c4 < 4; ++c4) {
           const f32x4_t v = {o[qb][db][4 * c4], o[qb][db][4 * c4 + 1], o[qb][db][4 * c4 + 2],
                              o[qb][db][4 * c4 + 3]};
-          put_dev4(pr, chunk_off(part, qb * (DB * 4 + 1) + db * 4 + c4), v);
+          put_dev4(pr, lane_off, chunk_off(part, qb * (DB * 4 + 1) + db * 4 + c4), v);
         }
       const f32x4_t ml = {m_run[qb], l_lane[qb], 0.f, 0.f};
-      put_dev4(pr, chunk_off(part, qb * (DB * 4 + 1) + DB * 4), ml);
+      put_dev4(pr, lane_off, chunk_off(part, qb * (DB * 4 + 1) + DB * 4), ml);
     }
     __syncthreads();                              // waits for this workgroup's stores
     if (tid == 0)
@@ -526,7 +534,7 @@ attn_bf16_kernel(AttnArgs a) {
       if (op == part) continue;
 #pragma unroll
       for (int qb = 0; qb < kQB; ++qb) {
-        const f32x4_t ml = get_dev4(pr, chunk_off(op, qb * (DB * 4 + 1) + DB * 4));
+        const f32x4_t ml = get_dev4(pr, lane_off, chunk_off(op, qb * (DB * 4 + 1) + DB * 4));
         const float m2 = ml[0], l2 = ml[1];
         const float mm = fmaxf(m_run[qb], m2);
         const float mu = mm == -INFINITY ? 0.f : mm;
@@ -535,7 +543,7 @@ attn_bf16_kernel(AttnArgs a) {
         for (int db = 0; db < DB; ++db)
 #pragma unroll
           for (int c4 = 0; c4 < 4; ++c4) {
-            const f32x4_t v = get_dev4(pr, chunk_off(op, qb * (DB * 4 + 1) + db * 4 + c4));
+            const f32x4_t v = get_dev4(pr, lane_off, chunk_off(op, qb * (DB * 4 + 1) + db * 4 + c4));
 #pragma unroll
             for (int e4 = 0; e4 < 4; ++e4) o[qb][db][4 * c4 + e4] = o[qb][db][4 * c4 + e4] * a1 + v[e4] * a2;
           }

@@ -403,8 +403,9 @@ gemm_qkv_bf16_kernel(GemmArgs a) {
     const int64_t tiles = static_cast<int64_t>(gridDim.x) * gridDim.y;
     const __amdgpu_buffer_rsrc_t pr =
         handoff_rsrc(a.partial, static_cast<int64_t>(gridDim.z) * tiles * CH * kGThreads * 16);
-    auto chunk_off = [&](int z, int c) -> uint32_t {
-      return static_cast<uint32_t>((((z * tiles + tile_id) * CH + c) * kGThreads + tid) * 16);
+    const uint32_t lane_off = static_cast<uint32_t>(tid) * 16;
+    auto chunk_off = [&](int z, int c) -> uint32_t {    // uniform part: a scalar offset
+      return static_cast<uint32_t>(((z * tiles + tile_id) * CH + c) * kGThreads * 16);
     };
 #pragma unroll
     for (int mi = 0; mi < MB; ++mi)
@@ -414,7 +415,7 @@ gemm_qkv_bf16_kernel(GemmArgs a) {
         for (int rq = 0; rq < 4; ++rq) {
           const f32x4_t v = {acc[mi][ni][4 * rq], acc[mi][ni][4 * rq + 1], acc[mi][ni][4 * rq + 2],
                              acc[mi][ni][4 * rq + 3]};
-          put_dev4(pr, chunk_off(kz, (mi * NI + ni) * 4 + rq), v);
+          put_dev4(pr, lane_off, chunk_off(kz, (mi * NI + ni) * 4 + rq), v);
         }
     // (the stage buffers are idle: every copy has landed and been read)
     if (!arrive_last(a.tile_cnt + tile_id, static_cast<int>(gridDim.z), reinterpret_cast<int*>(smem)))
@@ -433,7 +434,7 @@ gemm_qkv_bf16_kernel(GemmArgs a) {
         for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
           for (int rq = 0; rq < 4; ++rq) {
-            const f32x4_t v = get_dev4(pr, chunk_off(z, (mi * NI + ni) * 4 + rq));
+            const f32x4_t v = get_dev4(pr, lane_off, chunk_off(z, (mi * NI + ni) * 4 + rq));
 #pragma unroll
             for (int e = 0; e < 4; ++e) acc[mi][ni][4 * rq + e] += v[e];
           }

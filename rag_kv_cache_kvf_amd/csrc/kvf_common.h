@@ -126,11 +126,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t handoff_rsrc(void* base, int64
   return __builtin_amdgcn_make_buffer_rsrc(base, 0, static_cast<int>(bytes < 0x7fffffff ? bytes : 0x7fffffff),
                                            0x00020000);
 }
-__device__ __forceinline__ void put_dev4(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4_t v) {
-  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, off, 0, kDeviceScope);
+// Byte offset = voff (per lane) + soff (wave-uniform, a scalar register).
+__device__ __forceinline__ void put_dev4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, f32x4_t v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, voff, soff, kDeviceScope);
 }
-__device__ __forceinline__ f32x4_t get_dev4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kDeviceScope));
+__device__ __forceinline__ f32x4_t get_dev4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kDeviceScope));
 }
 // All threads: true in the workgroup that arrived last of n at *cnt, which
 // that workgroup sets back to zero for the next call.
