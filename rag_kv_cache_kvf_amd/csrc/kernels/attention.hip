@@ -778,12 +778,60 @@ hipError_t launch_attention(const kvf_layer_desc& L, const BatchArgs& B, const v
 // fp32: statistics by the fp32 attention kernel, column sums by one wave per
 // (key, kv head).
 
-// combine split statistics into log2-domain LSE per (row, head): one wave per
-// entry, lanes over splits
+// Combine split statistics into log2-domain LSE per (row, head).
+// Large planes: a block takes E = 64 consecutive entries and 256 / E groups of
+// splits (group k takes every (256 / E)-th split from k); lane = entry, so
+// each load reads 256 contiguous bytes of one statistics plane.  The groups'
+// (max, sum) pairs are combined in a fixed order.
+template <int E>
 __global__ void __launch_bounds__(256) lse_combine_kernel(const float* __restrict__ pm,
                                                           const float* __restrict__ pl, int n_splits,
                                                           int64_t plane, int64_t n,
                                                           float* __restrict__ lse2) {
+  constexpr int NG = 256 / E;
+  __shared__ float s_m[NG][E], s_l[NG][E];
+  const int e = threadIdx.x % E, grp = threadIdx.x / E;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * E + e;
+  float m = -INFINITY, l = 0.f;
+  auto add = [&](float ms, float ls) {
+    if (ms > m) {
+      l = l * (m == -INFINITY ? 0.f : exp2f(m - ms)) + ls;
+      m = ms;
+    } else if (ms > -INFINITY) {
+      l += ls * exp2f(ms - m);
+    }
+  };
+  if (i < n) {
+    for (int sp = grp; sp < n_splits; sp += 4 * NG) {   // four loads of each plane in flight
+      float ms[4], ls[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const bool ok = sp + NG * u < n_splits;
+        ms[u] = ok ? pm[(sp + NG * u) * plane + i] : -INFINITY;
+        ls[u] = ok ? pl[(sp + NG * u) * plane + i] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) add(ms[u], ls[u]);
+    }
+  }
+  s_m[grp][e] = m;
+  s_l[grp][e] = l;
+  __syncthreads();
+  if (grp == 0 && i < n) {
+    m = -INFINITY;
+    l = 0.f;
+#pragma unroll
+    for (int k = 0; k < NG; ++k) add(s_m[k][e], s_l[k][e]);
+    lse2[i] = l > 0.f ? m + log2f(l) : INFINITY;   // INFINITY: contributes nothing
+  }
+}
+
+// Small planes (too few entries to fill the chip 64 at a time): one wave per
+// entry, lanes over splits.
+__global__ void __launch_bounds__(256) lse_combine_wave_kernel(const float* __restrict__ pm,
+                                                               const float* __restrict__ pl, int n_splits,
+                                                               int64_t plane, int64_t n,
+                                                               float* __restrict__ lse2) {
   const int64_t i = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) / kWave;
   const int lane = threadIdx.x & (kWave - 1);
   if (i >= n) return;
@@ -1246,8 +1294,12 @@ hipError_t launch_attn_mass(const kvf_layer_desc& L, const BatchArgs& B, const v
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(lse_combine_kernel, dim3(ceil_div(static_cast<int>(plane), 256 / kWave)),
-                     dim3(256), 0, st, pm, pl, lay.n_splits, plane, plane, lse2);
+  if (plane >= 64 * kCUs)
+    hipLaunchKernelGGL(lse_combine_kernel<64>, dim3(ceil_div(static_cast<int>(plane), 64)), dim3(256), 0, st,
+                       pm, pl, lay.n_splits, plane, plane, lse2);
+  else
+    hipLaunchKernelGGL(lse_combine_wave_kernel, dim3(ceil_div(static_cast<int>(plane), 256 / kWave)),
+                       dim3(256), 0, st, pm, pl, lay.n_splits, plane, plane, lse2);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
 

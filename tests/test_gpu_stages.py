@@ -205,6 +205,9 @@ MASS_CASES = [
     ("bf16", 32, 8, 128, [0, 5184], [5120], 0),
     # long context with many query vectors (71 key chunks, 2048 vectors)
     ("bf16", 16, 2, 128, [0, 9000], [8744], 0),
+    # 256 query rows x 64 heads: statistics planes of 16384 entries, which
+    # take the 64-entries-per-block combine
+    ("bf16", 64, 8, 128, [0, 2304], [2048], 0),
     ("f32", 4, 2, 64, [0, 150, 290], [127, 100], 0),
 ]
 
