@@ -103,15 +103,22 @@ __device__ __forceinline__ float group_sum(float v, int width) {
 }
 
 // ---------------------------------------------------------------------------
-// batch metadata passed by value in kernel arguments
-// ---------------------------------------------------------------------------
 // hand-off between workgroups
 // ---------------------------------------------------------------------------
-// Relaxed device-scope atomics: coherent across the XCDs' L2 caches without
-// the whole-cache write-back/invalidate of a device-scope fence.  A
-// workgroup stores its partial results this way, the barrier waits for the
-// stores, then one arrival counter is bumped; the last arrival reads the
-// others' results the same way.
+// "The last workgroup to arrive combines": every workgroup stores its partial
+// results with device-scope coherence (the sc1 cache policy: the store is
+// written through to the level shared by all XCDs instead of staying in its
+// own XCD's L2), then waits for its own stores to be acknowledged
+// (s_waitcnt vmcnt(0): on gfx9-family parts vmcnt counts outstanding vector
+// stores as well as loads, and a store is acknowledged once it has reached
+// the coherence level its cache policy names), then the workgroup barrier
+// orders that wait before one thread's counter bump.  The last arrival sees
+// the count of every other workgroup, so every other workgroup's stores had
+// completed before it bumped; it reads them with device-scope loads (which
+// do not hit a stale line in its own L2).  This needs neither a release
+// fence (an L2 write-back of the whole cache on this part) nor an acquire
+// fence (an L2 invalidate), which evict the K/V tiles that other workgroups
+// on the same XCD are streaming.
 __device__ __forceinline__ void put_dev(float* p, float x) {
   __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -133,10 +140,19 @@ __device__ __forceinline__ void put_dev4(__amdgpu_buffer_rsrc_t r, uint32_t voff
 __device__ __forceinline__ f32x4_t get_dev4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kDeviceScope));
 }
+// Every wave: wait until this wave's vector stores have been acknowledged,
+// then the workgroup barrier.  (A plain __syncthreads() waits only for LDS
+// traffic on this part, not for global stores.)  The memory clobber keeps
+// the compiler from moving any store past the wait.
+__device__ __forceinline__ void stores_done_barrier() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+}
 // All threads: true in the workgroup that arrived last of n at *cnt, which
-// that workgroup sets back to zero for the next call.
+// that workgroup sets back to zero for the next call.  Call it after the
+// workgroup's device-scope partial stores.
 __device__ __forceinline__ bool arrive_last(int* cnt, int n, int* s_flag) {
-  __syncthreads();                                // this workgroup's stores have completed
+  stores_done_barrier();                          // every wave's stores have completed
   if (threadIdx.x == 0) {
     const int old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const bool last = old == n - 1;
@@ -147,6 +163,8 @@ __device__ __forceinline__ bool arrive_last(int* cnt, int n, int* s_flag) {
   return *s_flag != 0;
 }
 
+// ---------------------------------------------------------------------------
+// batch metadata passed by value in kernel arguments
 // ---------------------------------------------------------------------------
 struct BatchArgs {
   int n_req;
@@ -197,7 +215,7 @@ hipError_t launch_rope_table(double base, int d, int n_pos, float* c, float* s, 
 hipError_t launch_rerotate(const kvf_layer_desc& L, const kvf_chunk* chunks, int n_chunks,
                            int max_len, const void* pk, const void* pv, const kvf_kivi* q,
                            int64_t pool_rows, const float* rc, const float* rs, int rope_n,
-                           void* fk, void* fv, int64_t fused_rows, hipStream_t st);
+                           void* fk, void* fv, int64_t fused_rows, int k_only, hipStream_t st);
 hipError_t launch_kivi_encode(const kvf_layer_desc& L, const void* pk, const void* pv,
                               const int32_t* pool_cu, int n_pool, int64_t pool_rows,
                               int max_len, const kvf_kivi& out, hipStream_t st);
@@ -207,6 +225,8 @@ hipError_t launch_attn_mass(const kvf_layer_desc& L, const BatchArgs& B, const v
                             const void* q_u, int n_last_q, const ScoreOut& out, void* ws,
                             size_t ws_bytes, hipStream_t st);
 size_t attn_mass_workspace(const kvf_layer_desc& L, const BatchArgs& B, int n_last_q);
+// 128-key context tiles of a batch; the attention-mass call takes at most 16384
+int64_t attn_mass_key_tiles(const BatchArgs& B);
 hipError_t launch_key_norm(const kvf_layer_desc& L, const BatchArgs& B, const void* fk,
                            const ScoreOut& out, hipStream_t st);
 hipError_t launch_topk(const float* scores, const uint8_t* forced, const BatchArgs& B,
