@@ -50,7 +50,7 @@ struct AttnArgs {
   int parts;                     // > 1: long row tiles split their keys over up to this many workgroups
   int split_min;                 // key tiles from which a row tile is split
   float* ws_part;                // [tiles * Hkv, parts, 16-byte chunks, threads]
-  int* ws_cnt;                   // [tiles * Hkv] arrivals; zero between calls
+  int* ws_cnt;                   // [tiles * Hkv] arrivals (workspace offset 0); zero between calls
   int rows_per_tile;             // R
   const void* q;
   const int32_t* q_pos;
@@ -300,12 +300,12 @@ attn_bf16_kernel(AttnArgs a) {
   };
 
   // Softmax state in the log2 domain: scores enter as s * c with
-  // c = sm_scale * log2(e).  Probabilities are taken against a running max
-  // m_run that is raised only when a block's probabilities would exceed
-  // 2^8 (then O and l are rescaled); fp32 sums and bf16 operands carry such
-  // values exactly as well, so the result is the same softmax with far
-  // fewer rescales.
-  constexpr float kSlackSum = 256.f;                // 2^8
+  // c = sm_scale * log2(e).  The running max m_run follows the block maxima:
+  // it is raised to a block's exact max whenever that exceeds it by more than
+  // kRaise, so every probability is at most 2^kRaise and the key that set the
+  // max has probability exactly 1 (the bf16 rounding of P then costs no more
+  // than it does against the row's true max).
+  constexpr float kRaise = 0.5f;
   const float c_scale = a.scale_log2;
   const f32x16_t zero16 = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   const bf16x2_t ones2 = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
@@ -367,22 +367,43 @@ attn_bf16_kernel(AttnArgs a) {
       }
     }
   };
-  // Raise the running max to the exact max of block s, rescaling O and l.
-  auto raise_max = [&](const f32x16_t (&s)[kQB]) __attribute__((always_inline)) {
+  // Max of one block's scores in the log2 domain, over both lane halves
+  // (v_permlane32_swap exchanges the halves without going through LDS).
+  auto block_max = [&](const f32x16_t (&s)[kQB], float (&bm)[kQB]) __attribute__((always_inline)) {
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb) {
       float m = fmaxf(s[qb][0], s[qb][1]);
 #pragma unroll
       for (int i = 2; i < 16; ++i) m = fmaxf(m, s[qb][i]);
-      const float mx = fmaxf(m, __shfl_xor(m, 32, kWave)) * c_scale;
-      const float m_new = fmaxf(m_run[qb], mx);
-      const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run[qb] - m_new);
-      l_lane[qb] *= alpha;
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+      bm[qb] = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * c_scale;
+    }
+  };
+  // Set the running max from block s, given as the first block (exact).
+  auto init_max = [&](const f32x16_t (&s)[kQB]) __attribute__((always_inline)) {
+    float bm[kQB];
+    block_max(s, bm);
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+    for (int qb = 0; qb < kQB; ++qb) m_run[qb] = bm[qb];
+  };
+  // O is kept against the max its latest V product used; alpha_pend takes it
+  // to the max of the block whose V product comes next.
+  float alpha_pend[kQB];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) o[qb][db][i] *= alpha;
-      m_run[qb] = m_new;
+  for (int qb = 0; qb < kQB; ++qb) alpha_pend[qb] = 1.f;
+  auto catch_up = [&]() __attribute__((always_inline)) {
+    bool any = false;
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) any = any || alpha_pend[qb] != 1.f;
+    if (__any(any)) {
+#pragma unroll
+      for (int qb = 0; qb < kQB; ++qb) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) o[qb][db][i] *= alpha_pend[qb];
+        alpha_pend[qb] = 1.f;
+      }
     }
   };
   // O^T += V^T P^T for one 32-key block of tile vt
@@ -424,26 +445,26 @@ attn_bf16_kernel(AttnArgs a) {
     for (int i = 0; i < 8; ++i) pk_b[qb][i] = 0u;  // "block -1": contributes nothing
   // sc: scores of block b (first key kb0); kt/kbs: K tile and block of b+1
   // into sn; vt/kbp/pkp: V tile, block and probabilities of b-1; pkc gets b's.
-  // Lazy rescaling without a per-element max: a block whose lane-local
-  // probability sums stay within 2^8 has no probability above 2^8, so it is
-  // used as computed; otherwise the exact block max is taken, O and l are
-  // rescaled to it and the block's probabilities are recomputed.
+  // The rescale of O for block b's max is applied before the V product of
+  // block b (in the next half step), after that of block b-1.
   auto half_step = [&](f32x16_t (&sc)[kQB], int kb0, bool masked, const bf16_t* kt, int kbs,
                        f32x16_t (&sn)[kQB], const bf16_t* vt, int kbp, const uint32_t (&pkp)[kQB][8],
                        uint32_t (&pkc)[kQB][8]) __attribute__((always_inline)) {
     if (masked) apply_mask(sc, kb0);
-    float lb[kQB];
     scores(kt, kbs, sn);
-    probs(sc, pkc, lb);
+    catch_up();
     pv(vt, kbp, pkp);
-    bool big = false;
+    float bm[kQB], lb[kQB];
+    block_max(sc, bm);
 #pragma unroll
-    for (int qb = 0; qb < kQB; ++qb) big = big || lb[qb] > kSlackSum;
-    if (__builtin_expect(__any(big), 0)) {
-      asm volatile("; rescale");                  // keeps this rare path a branch
-      raise_max(sc);
-      probs(sc, pkc, lb);
+    for (int qb = 0; qb < kQB; ++qb) {
+      if (bm[qb] > m_run[qb] + kRaise) {
+        alpha_pend[qb] = __builtin_amdgcn_exp2f(m_run[qb] - bm[qb]);   // m_run = -inf: 0 (O, l are 0)
+        l_lane[qb] *= alpha_pend[qb];
+        m_run[qb] = bm[qb];
+      }
     }
+    probs(sc, pkc, lb);
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb) l_lane[qb] += lb[qb];
   };
@@ -471,7 +492,7 @@ attn_bf16_kernel(AttnArgs a) {
     copies_landed_barrier<0>();
     scores(k0s, 0, s_a);
     if (t0 >= n_plain) apply_mask(s_a, t0 * kAT);
-    raise_max(s_a);                                 // the first block sets the max exactly
+    init_max(s_a);                                  // the first block sets the max exactly
   }
   // Every global load the compiler tracks (Q) has completed here on all
   // paths; saying so keeps it from waiting for them, and so for the tile
@@ -488,6 +509,7 @@ attn_bf16_kernel(AttnArgs a) {
   }
   // P(last block) V_{last tile}
   if (t1 > t0) {
+    catch_up();
     if (((tl - t0) & 1) == 0) pv(v0s, 1, pk_b);
     else pv(v1s, 1, pk_b);
   }
@@ -497,11 +519,9 @@ attn_bf16_kernel(AttnArgs a) {
     // wave's store of one chunk is 1 KB contiguous: per query block the
     // unnormalised O (DB x 4 chunks), then (m, the lane's half of l, 0, 0).
     // The chunks are stored and loaded with device-scope coherence, which
-    // reaches across the XCDs' L2 caches, and the arrival counter is bumped
-    // only after the barrier has waited for all of the workgroup's stores.
-    // Device-scope fences would do the same by writing back and invalidating
-    // the whole L2, evicting the K/V tiles the other workgroups on this XCD
-    // are streaming.
+    // reaches across the XCDs' L2 caches; every wave waits for its stores to
+    // be acknowledged before the barrier that precedes the counter bump
+    // (stores_done_barrier), so the last arrival reads complete partials.
     constexpr int NC = kQB * (DB * 4 + 1);
     const int64_t item = static_cast<int64_t>(tile) * hkv + g;
     const __amdgpu_buffer_rsrc_t pr = handoff_rsrc(
@@ -525,7 +545,7 @@ attn_bf16_kernel(AttnArgs a) {
       const f32x4_t ml = {m_run[qb], l_lane[qb], 0.f, 0.f};
       put_dev4(pr, lane_off, chunk_off(part, qb * (DB * 4 + 1) + DB * 4), ml);
     }
-    __syncthreads();                              // waits for this workgroup's stores
+    stores_done_barrier();                        // every wave's stores have completed
     if (tid == 0)
       s_pos[0] = __hip_atomic_fetch_add(&a.ws_cnt[item], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
@@ -679,10 +699,16 @@ constexpr int kSplitMinTiles = 12;
 constexpr int kSplitMinTilesSmall = 6;
 constexpr int kSplitMaxParts = 8;
 
+// Workspace: arrival counters first, at a fixed offset and size, so that
+// calls of any shape can share one zero-filled workspace (every completed
+// call leaves the counters zero); the parts' partial results after them.
+constexpr size_t kAttnCntBytes = 4096;
+static_assert(kSplitMaxItems * sizeof(int) <= kAttnCntBytes, "counter region");
+
 struct AttnSplitLayout {
   int64_t items = 0;             // row tiles x kv heads
   int parts = 1;
-  size_t off_cnt = 0, bytes = 0;
+  size_t off_part = 0, bytes = 0;
 };
 
 static AttnSplitLayout attn_split_layout(const kvf_layer_desc& L, const BatchArgs& B,
@@ -698,8 +724,8 @@ static AttnSplitLayout attn_split_layout(const kvf_layer_desc& L, const BatchArg
   s.items = items;
   s.parts = static_cast<int>(std::min<int64_t>(
       kSplitMaxParts, std::max<int64_t>(2, (kSplitMaxItems + items - 1) / items)));
-  s.off_cnt = static_cast<size_t>(items * s.parts * chunks * kAThreads) * 16;
-  s.bytes = s.off_cnt + static_cast<size_t>(items) * sizeof(int);
+  s.off_part = kAttnCntBytes;
+  s.bytes = s.off_part + static_cast<size_t>(items * s.parts * chunks * kAThreads) * 16;
   return s;
 }
 
@@ -739,8 +765,8 @@ hipError_t launch_attention(const kvf_layer_desc& L, const BatchArgs& B, const v
     if (sl.bytes > 0 && ws != nullptr && ws_bytes >= sl.bytes) {
       a.parts = sl.parts;
       a.split_min = sl.parts > 2 ? kSplitMinTilesSmall : kSplitMinTiles;
-      a.ws_part = static_cast<float*>(ws);
-      a.ws_cnt = reinterpret_cast<int*>(static_cast<char*>(ws) + sl.off_cnt);
+      a.ws_cnt = static_cast<int*>(ws);
+      a.ws_part = reinterpret_cast<float*>(static_cast<char*>(ws) + sl.off_part);
     }
     const int64_t blocks = tiles * a.parts;
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
@@ -1157,6 +1183,17 @@ __global__ void __launch_bounds__(256) head_sum_kernel(const float* __restrict__
   store_score(out, i, s);
 }
 
+// Arrival counters of the attention-mass workspace: one per 128-key tile of
+// context, at workspace offset 0 in a region of fixed size.
+constexpr size_t kMassCntBytes = 65536;
+constexpr int64_t kMassMaxKeyTiles = kMassCntBytes / sizeof(int);
+
+int64_t attn_mass_key_tiles(const BatchArgs& B) {
+  int64_t ktiles = 0;
+  for (int r = 0; r < B.n_req; ++r) ktiles += ceil_div(B.n_ctx[r], kMK);
+  return ktiles;
+}
+
 namespace {
 struct MassLayout {
   int64_t rows;          // query rows used (sum over requests)
@@ -1190,15 +1227,17 @@ MassLayout mass_layout(const kvf_layer_desc& L, const BatchArgs& B, int n_last_q
   }
   const int64_t plane = m.rows * L.n_q_heads;
   auto align = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
-  m.off_pm = 0;
-  m.off_pl = align(m.off_pm + sizeof(float) * plane * m.n_splits);
-  m.off_lse = align(m.off_pl + sizeof(float) * plane * m.n_splits);
-  m.off_part = align(m.off_lse + sizeof(float) * plane);
-  m.off_cnt = align(m.off_part + sizeof(float) * static_cast<size_t>(L.n_kv_heads) * B.cu_N[B.n_req]);
   int64_t ktiles = 0;
   for (int r = 0; r < B.n_req; ++r) ktiles += ceil_div(B.n_ctx[r], kMK);
   m.n_cnt = ktiles;
-  m.total = align(m.off_cnt + sizeof(int) * m.n_cnt);
+  // arrival counters first, at a fixed offset and size: calls of any shape
+  // can share one zero-filled workspace
+  m.off_cnt = 0;
+  m.off_pm = kMassCntBytes;
+  m.off_pl = align(m.off_pm + sizeof(float) * plane * m.n_splits);
+  m.off_lse = align(m.off_pl + sizeof(float) * plane * m.n_splits);
+  m.off_part = align(m.off_lse + sizeof(float) * plane);
+  m.total = align(m.off_part + sizeof(float) * static_cast<size_t>(L.n_kv_heads) * B.cu_N[B.n_req]);
   return m;
 }
 }  // namespace
@@ -1211,7 +1250,7 @@ hipError_t launch_attn_mass(const kvf_layer_desc& L, const BatchArgs& B, const v
                             const void* q_u, int n_last_q, const ScoreOut& out, void* ws,
                             size_t ws_bytes, hipStream_t st) {
   const MassLayout lay = mass_layout(L, B, n_last_q);
-  if (ws_bytes < lay.total) return hipErrorInvalidValue;
+  if (ws_bytes < lay.total || lay.n_cnt > kMassMaxKeyTiles) return hipErrorInvalidValue;
   char* base = static_cast<char*>(ws);
   float* pm = reinterpret_cast<float*>(base + lay.off_pm);
   float* pl = reinterpret_cast<float*>(base + lay.off_pl);

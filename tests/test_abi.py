@@ -48,7 +48,7 @@ def test_status_strings_and_version(lib):
     lib.kvf_status_string.restype = ctypes.c_char_p
     assert lib.kvf_status_string(0) == b"KVF_OK"
     assert lib.kvf_status_string(2) == b"KVF_ERR_UNSUPPORTED"
-    assert lib.kvf_abi_version() == 8
+    assert lib.kvf_abi_version() == 9
 
 
 def test_budget_matches_oracle(lib):
@@ -153,9 +153,9 @@ def test_validation_errors(lib):
     ba, keep_a = _batch([0, 5184], [5120])
     cq = (ctypes.c_int32 * 2)(0, 1600)
     need = lib.kvf_attention_workspace_size(ctypes.byref(bq), ctypes.byref(ba), cq)
-    # 400 (row tile, kv head) items x 2 parts x (16 + 1) 16-byte chunks per
-    # thread of 256, then one int32 arrival counter per item
-    assert need == 50 * 8 * (2 * (4 * 4 + 1) * 256 * 16 + 4)
+    # 4096 bytes of arrival counters, then 400 (row tile, kv head) items x 2
+    # parts x (16 + 1) 16-byte chunks per thread of 256
+    assert need == 4096 + 50 * 8 * 2 * (4 * 4 + 1) * 256 * 16
     assert lib.kvf_sparse_q_attention(ctypes.byref(bq), ctypes.byref(ba), FAKE, FAKE, cq, FAKE, FAKE,
                                       0.088, FAKE, None, FAKE, need - 1, None) == 3
     big = (ctypes.c_int32 * 2)(0, 5184)
@@ -198,15 +198,26 @@ def test_validation_errors(lib):
             ("n", ctypes.c_int32), ("bits", ctypes.c_int32)]
     kv = Kivi(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8)
     assert lib.kvf_rerotate(ctypes.byref(ok), FAKE, 1, 4, None, None, ctypes.byref(kv), 4, FAKE,
-                            FAKE, 4, FAKE, FAKE, 4, None) == 2
+                            FAKE, 4, FAKE, FAKE, 4, 0, None) == 2
     # KIVI codes are 8 or 4 bits
     bfl = Layer(256, 4, 4, 64, 1)
     for bits, want in ((3, 2), (16, 2), (0, 2)):
         kv = Kivi(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, bits)
         assert lib.kvf_rerotate(ctypes.byref(bfl), FAKE, 1, 4, None, None, ctypes.byref(kv), 4,
-                                FAKE, FAKE, 4, FAKE, FAKE, 4, None) == want
+                                FAKE, FAKE, 4, FAKE, FAKE, 4, 0, None) == want
         assert lib.kvf_kivi_encode(ctypes.byref(bfl), FAKE, FAKE, FAKE, 1, 4, 4,
                                    ctypes.byref(kv), None) == want
+    # keys-only re-positioning: dense caches only, a pool_k, k_only 0 or 1
+    kv = Kivi(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8)
+    assert lib.kvf_rerotate(ctypes.byref(bfl), FAKE, 1, 4, None, None, ctypes.byref(kv), 4,
+                            FAKE, FAKE, 4, FAKE, None, 4, 1, None) == 2
+    assert lib.kvf_rerotate(ctypes.byref(bfl), FAKE, 1, 4, None, None, None, 4,
+                            FAKE, FAKE, 4, FAKE, None, 4, 1, None) == 1
+    assert lib.kvf_rerotate(ctypes.byref(bfl), FAKE, 1, 4, FAKE, FAKE, None, 4,
+                            FAKE, FAKE, 4, FAKE, FAKE, 4, 2, None) == 1
+    # gather mode needs fused_v
+    assert lib.kvf_rerotate(ctypes.byref(bfl), FAKE, 1, 4, FAKE, FAKE, None, 4,
+                            FAKE, FAKE, 4, FAKE, None, 4, 0, None) == 1
 
 
 def test_empty_calls_are_noops(lib):
