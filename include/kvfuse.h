@@ -53,6 +53,11 @@
  *    instead of reading or writing outside the buffers.
  *  - Thread safety: calls may be made from several host threads; calls that
  *    write the same buffers must be ordered by the caller.
+ *  - Debugging: with KVF_SYNC_CHECK=1 in the environment (read once per
+ *    process), every call synchronises its stream after enqueueing and
+ *    returns KVF_ERR_HIP if one of its kernels failed to launch or run, so a
+ *    fault is reported by the call that caused it.  Streams being captured
+ *    into a graph are not synchronised.
  */
 #ifndef KVFUSE_H
 #define KVFUSE_H
@@ -64,7 +69,7 @@
 extern "C" {
 #endif
 
-#define KVF_ABI_VERSION 8
+#define KVF_ABI_VERSION 9
 #define KVF_MAX_REQ 64      /* requests per call (batch metadata is passed by value) */
 
 typedef enum {
@@ -186,6 +191,14 @@ kvf_status kvf_rope_table(double base, int32_t head_dim, int32_t n_pos,
  * KIVI caches (8 or 4 bits): pool_k = pool_v = NULL and kivi != NULL; codes
  * are decoded (min + code * scale, fp32) before the rotation
  * (dequant-on-load).  Output dtype must be bf16 for KIVI caches.
+ * k_only = 1 (dense caches only): keys only - the loader has already
+ *   stitched the values into fused_v ([QCF] 2.1.2: values keep their token
+ *   order; only keys carry the rotation, [KVB] 3.2 Eq. 3), so pool_v and
+ *   fused_v are not read or written (either may be NULL).  pool_k may be
+ *   fused_k itself (in place) when every chunk has src_row == dst_row; a
+ *   thread reads both channels of each rotation pair before writing them.
+ *   Chunks whose rows overlap between source and destination otherwise are
+ *   undefined.  k_only = 0 gathers keys and values as above.
  * chunks: device [n_chunks]; max_chunk_len (host) bounds every len.
  * rope tables cover positions [0, rope_n_pos); pos0 >= rope_n_pos skips the
  * chunk.  Fused rows no chunk covers are not written.
@@ -196,7 +209,7 @@ kvf_status kvf_rerotate(const kvf_layer_desc* layer, const kvf_chunk* chunks,
                         const kvf_kivi* kivi, int64_t pool_rows,
                         const float* rope_cos, const float* rope_sin,
                         int32_t rope_n_pos, void* fused_k, void* fused_v,
-                        int64_t fused_rows, void* stream);
+                        int64_t fused_rows, int32_t k_only, void* stream);
 
 /* ---------------------------------------------------------------------------
  * kvf_score - S2: one fp32 score per context token; scores [sum_r n_ctx[r]]
@@ -218,11 +231,13 @@ kvf_status kvf_rerotate(const kvf_layer_desc* layer, const kvf_chunk* chunks,
  *   keys 0..N+i; each (i, head) softmax is over that whole row, and
  *   score_t = sum over the last n_last_q query tokens (all when <= 0) and all
  *   query heads of the probability at context position t.  Softmax scale is
- *   1/sqrt(d).  Needs a workspace of kvf_score_workspace_size() bytes; it
- *   ends in arrival counters that must be zero before its first use
- *   (zero-fill it once when allocating it); every completed call leaves them
- *   zero.  Calls that share a workspace must not overlap.  The scores are
- *   deterministic (fixed summation order).
+ *   1/sqrt(d).  Needs a workspace of kvf_score_workspace_size() bytes; its
+ *   first 65536 bytes are arrival counters (one per 128-key context tile, so
+ *   at most 16384 tiles per call, else KVF_ERR_UNSUPPORTED) that must be
+ *   zero before its first use (zero-fill it once when allocating it); every
+ *   completed call leaves them zero, so calls of any shape may share one
+ *   workspace.  Calls that share a workspace must not overlap.  The scores
+ *   are deterministic (fixed summation order).
  * KVF_SCORE_KEY_NORM ([QCF] 3.3.1, the Knorm ranking rule):
  *   score_t = sqrt(sum over heads h and channels j of fused_k[t, h, j]^2),
  *   fp32 accumulation.  The norm is rotation invariant, so the re-positioned
@@ -382,9 +397,10 @@ kvf_status kvf_sparse_q_attention(const kvf_layer_desc* layer,
  * rows split their keys over several workgroups (2 to 8, more when the grid
  * has fewer row tiles) and merge (same result up to fp32 rounding order);
  * with workspace NULL the call runs unsplit.  The
- * workspace ends in per-tile arrival counters that must be zero before its
- * first use (zero-fill it once when allocating it); every completed call
- * leaves them zero again.  Calls that share a workspace must not overlap.
+ * workspace's first 4096 bytes are per-tile arrival counters that must be
+ * zero before its first use (zero-fill it once when allocating it); every
+ * completed call leaves them zero again, so calls of any shape may share one
+ * workspace.  Calls that share a workspace must not overlap.
  * A non-NULL workspace smaller than this size gives KVF_ERR_WORKSPACE. */
 size_t kvf_attention_workspace_size(const kvf_layer_desc* layer,
                                     const kvf_batch* batch,

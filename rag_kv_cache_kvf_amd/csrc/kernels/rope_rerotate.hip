@@ -11,7 +11,9 @@
 //
 // All kernels here are HBM-bound streams: 16-byte vector loads/stores, one
 // chunk tile per workgroup so the chunk descriptor and its rotation row are
-// fetched once per tile.
+// fetched once per tile.  In keys-only mode the values were stitched by the
+// loader and are not touched; the keys may be rotated in place (a thread
+// reads the 16 channels of a rotation pair set before it writes them).
 #include "../kvf_common.h"
 
 namespace kvf {
@@ -68,6 +70,7 @@ struct RotArgs {
   int64_t fused_rows;
   int hkv;
   int d;
+  int k_only;                     // keys only: values are already in place
 };
 
 // the 8 codes of channels e..e+7 (e a multiple of 8), `codes` pointing at
@@ -155,6 +158,7 @@ __global__ void __launch_bounds__(256) rerotate_kernel(RotArgs a) {
   }
 
   // values: stitched unchanged (decoded for int8 caches)
+  if (!KIVI && a.k_only) return;
   const int vu = row_elems >> 3;
   for (int u = threadIdx.x; u < nrows * vu; u += blockDim.x) {
     const int t = u / vu, e0 = (u - t * vu) << 3;
@@ -180,7 +184,7 @@ __global__ void __launch_bounds__(256) rerotate_kernel(RotArgs a) {
 hipError_t launch_rerotate(const kvf_layer_desc& L, const kvf_chunk* chunks, int n_chunks,
                            int max_len, const void* pk, const void* pv, const kvf_kivi* q,
                            int64_t pool_rows, const float* rc, const float* rs, int rope_n,
-                           void* fk, void* fv, int64_t fused_rows, hipStream_t st) {
+                           void* fk, void* fv, int64_t fused_rows, int k_only, hipStream_t st) {
   RotArgs a{};
   a.chunks = chunks;
   a.pool_k = pk;
@@ -203,6 +207,7 @@ hipError_t launch_rerotate(const kvf_layer_desc& L, const kvf_chunk* chunks, int
   a.fused_rows = fused_rows;
   a.hkv = L.n_kv_heads;
   a.d = L.head_dim;
+  a.k_only = k_only;
   const dim3 grid(n_chunks, ceil_div(max_len, kRotRows));
   if (grid.y > 65535) return hipErrorInvalidValue;
   if (q && q->bits == 4)

@@ -5,6 +5,7 @@
 // C++ exception cross the interface.
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <exception>
 
@@ -28,6 +29,31 @@ kvf_status from_hip(hipError_t e, const char* what) {
     return KVF_OK;
   }
   return fail(KVF_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// KVF_SYNC_CHECK=1 in the environment (read once): after a call has
+// enqueued its kernels, synchronise its stream and report any launch or
+// execution error of those kernels as that call's KVF_ERR_HIP.  A debugging
+// aid: it serialises the host with the GPU, and is skipped on a stream that
+// is being captured into a graph (synchronising one is illegal).
+bool sync_check_enabled() {
+  static const bool on = [] {
+    const char* v = std::getenv("KVF_SYNC_CHECK");
+    return v != nullptr && v[0] != '\0' && std::strcmp(v, "0") != 0;
+  }();
+  return on;
+}
+
+kvf_status finish(hipError_t e, hipStream_t st, const char* what) {
+  if (e == hipSuccess && sync_check_enabled()) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    e = hipStreamIsCapturing(st, &cs);
+    if (e == hipSuccess && cs == hipStreamCaptureStatusNone) {
+      e = hipStreamSynchronize(st);
+      if (e == hipSuccess) e = hipGetLastError();
+    }
+  }
+  return from_hip(e, what);
 }
 
 #define KVF_CHECK(cond, st, ...)            \
@@ -127,8 +153,9 @@ kvf_status kvf_rope_table(double base, int32_t head_dim, int32_t n_pos, float* c
   KVF_CHECK(n_pos >= 0, KVF_ERR_INVALID_ARG, "n_pos negative");
   if (n_pos == 0) return KVF_OK;
   KVF_CHECK(cos_tab && sin_tab, KVF_ERR_INVALID_ARG, "table pointers are NULL");
-  return from_hip(kvf::launch_rope_table(base, head_dim, n_pos, cos_tab, sin_tab,
-                                         as_stream(stream)), "kvf_rope_table");
+  return finish(kvf::launch_rope_table(base, head_dim, n_pos, cos_tab, sin_tab,
+                                         as_stream(stream)),
+                as_stream(stream), "kvf_rope_table");
   KVF_GUARD_END
 }
 
@@ -136,16 +163,21 @@ kvf_status kvf_rerotate(const kvf_layer_desc* layer, const kvf_chunk* chunks, in
                         int32_t max_chunk_len, const void* pool_k, const void* pool_v,
                         const kvf_kivi* kivi, int64_t pool_rows, const float* rope_cos,
                         const float* rope_sin, int32_t rope_n_pos, void* fused_k, void* fused_v,
-                        int64_t fused_rows, void* stream) {
+                        int64_t fused_rows, int32_t k_only, void* stream) {
   KVF_GUARD_BEGIN
   kvf_status st = check_layer(layer);
   if (st != KVF_OK) return st;
   KVF_CHECK(n_chunks >= 0 && max_chunk_len >= 0 && pool_rows >= 0 && fused_rows >= 0 &&
                 rope_n_pos >= 0, KVF_ERR_INVALID_ARG, "negative size");
+  KVF_CHECK(k_only == 0 || k_only == 1, KVF_ERR_INVALID_ARG, "k_only must be 0 or 1");
   if (n_chunks == 0 || max_chunk_len == 0) return KVF_OK;
-  KVF_CHECK(chunks && rope_cos && rope_sin && fused_k && fused_v, KVF_ERR_INVALID_ARG,
+  KVF_CHECK(chunks && rope_cos && rope_sin && fused_k && (k_only || fused_v), KVF_ERR_INVALID_ARG,
             "required pointer is NULL");
-  if (kivi) {
+  if (k_only) {
+    KVF_CHECK(kivi == nullptr, KVF_ERR_UNSUPPORTED,
+              "keys-only re-positioning reads a dense cache (KIVI codes decode to new buffers)");
+    KVF_CHECK(pool_k != nullptr, KVF_ERR_INVALID_ARG, "pool_k is NULL");
+  } else if (kivi) {
     KVF_CHECK(layer->dtype == KVF_BF16, KVF_ERR_UNSUPPORTED, "KIVI caches decode to bf16 only");
     KVF_CHECK(kivi->bits == 8 || kivi->bits == 4, KVF_ERR_UNSUPPORTED,
               "KIVI codes are 8 or 4 bits, not %d", kivi->bits);
@@ -158,10 +190,10 @@ kvf_status kvf_rerotate(const kvf_layer_desc* layer, const kvf_chunk* chunks, in
     KVF_CHECK(pool_k && pool_v, KVF_ERR_INVALID_ARG, "pool pointers are NULL");
   }
   KVF_CHECK(max_chunk_len <= (1 << 24), KVF_ERR_UNSUPPORTED, "max_chunk_len too large");
-  return from_hip(kvf::launch_rerotate(*layer, chunks, n_chunks, max_chunk_len, pool_k, pool_v,
+  return finish(kvf::launch_rerotate(*layer, chunks, n_chunks, max_chunk_len, pool_k, pool_v,
                                        kivi, pool_rows, rope_cos, rope_sin, rope_n_pos, fused_k,
-                                       fused_v, fused_rows, as_stream(stream)),
-                  "kvf_rerotate");
+                                       fused_v, fused_rows, k_only, as_stream(stream)),
+                as_stream(stream), "kvf_rerotate");
   KVF_GUARD_END
 }
 
@@ -182,9 +214,9 @@ kvf_status kvf_kivi_encode(const kvf_layer_desc* layer, const void* pool_k, cons
             "KIVI codes are 8 or 4 bits, not %d", out->bits);
   KVF_CHECK(out->n_pool_chunks >= n_pool_chunks, KVF_ERR_INVALID_ARG,
             "output statistics hold %d chunks, need %d", out->n_pool_chunks, n_pool_chunks);
-  return from_hip(kvf::launch_kivi_encode(*layer, pool_k, pool_v, pool_cu, n_pool_chunks,
+  return finish(kvf::launch_kivi_encode(*layer, pool_k, pool_v, pool_cu, n_pool_chunks,
                                           pool_rows, max_chunk_len, *out, as_stream(stream)),
-                  "kvf_kivi_encode");
+                as_stream(stream), "kvf_kivi_encode");
   KVF_GUARD_END
 }
 
@@ -221,18 +253,22 @@ kvf_status kvf_score(kvf_score_mode mode_flags, const kvf_layer_desc* layer,
   const kvf::ScoreOut out{scores, eligible, (flags & KVF_SCORE_ACCUMULATE) ? 1 : 0};
   if (mode == KVF_SCORE_DEVIATION) {
     KVF_CHECK(k_fresh != nullptr, KVF_ERR_INVALID_ARG, "k_fresh is NULL");
-    return from_hip(kvf::launch_deviation(*layer, B, fused_k, k_fresh, out, as_stream(stream)),
-                    "kvf_score(deviation)");
+    return finish(kvf::launch_deviation(*layer, B, fused_k, k_fresh, out, as_stream(stream)),
+                as_stream(stream), "kvf_score(deviation)");
   }
   if (mode == KVF_SCORE_KEY_NORM)
-    return from_hip(kvf::launch_key_norm(*layer, B, fused_k, out, as_stream(stream)),
-                    "kvf_score(key_norm)");
+    return finish(kvf::launch_key_norm(*layer, B, fused_k, out, as_stream(stream)),
+                as_stream(stream), "kvf_score(key_norm)");
   KVF_CHECK(q_u != nullptr, KVF_ERR_INVALID_ARG, "q_u is NULL");
+  KVF_CHECK(kvf::attn_mass_key_tiles(B) <= 16384, KVF_ERR_UNSUPPORTED,
+            "attention mass over %lld 128-key context tiles (at most 16384 per call)",
+            static_cast<long long>(kvf::attn_mass_key_tiles(B)));
   const size_t need = kvf::attn_mass_workspace(*layer, B, n_last_q);
   KVF_CHECK(ws_bytes >= need, KVF_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);
   KVF_CHECK(need == 0 || workspace != nullptr, KVF_ERR_WORKSPACE, "workspace is NULL");
-  return from_hip(kvf::launch_attn_mass(*layer, B, fused_k, q_u, n_last_q, out, workspace,
-                                        ws_bytes, as_stream(stream)), "kvf_score(attn_mass)");
+  return finish(kvf::launch_attn_mass(*layer, B, fused_k, q_u, n_last_q, out, workspace,
+                                        ws_bytes, as_stream(stream)),
+                as_stream(stream), "kvf_score(attn_mass)");
   KVF_GUARD_END
 }
 
@@ -263,8 +299,9 @@ kvf_status kvf_select_topk(const float* scores, const uint8_t* forced, const kvf
   KVF_CHECK(total_k == 0 || out_idx, KVF_ERR_INVALID_ARG, "out_idx is NULL");
   KVF_CHECK((out_rows == nullptr) == (out_pos == nullptr), KVF_ERR_INVALID_ARG,
             "out_rows and out_pos must both be given or both be NULL");
-  return from_hip(kvf::launch_topk(scores, forced, B, k_per_req, out_idx, out_rows, out_pos,
-                                   out_mask, as_stream(stream)), "kvf_select_topk");
+  return finish(kvf::launch_topk(scores, forced, B, k_per_req, out_idx, out_rows, out_pos,
+                                   out_mask, as_stream(stream)),
+                as_stream(stream), "kvf_select_topk");
   KVF_GUARD_END
 }
 
@@ -292,9 +329,9 @@ kvf_status kvf_select_topk_segmented(const float* scores, const uint8_t* forced,
   if (total_m == 0) return KVF_OK;
   KVF_CHECK(total_k == 0 || out_idx, KVF_ERR_INVALID_ARG, "out_idx is NULL");
   KVF_CHECK(n_segs == 0 || segs, KVF_ERR_INVALID_ARG, "segs is NULL");
-  return from_hip(kvf::launch_topk_segmented(scores, forced, B, segs, n_segs, k_per_req, out_idx,
+  return finish(kvf::launch_topk_segmented(scores, forced, B, segs, n_segs, k_per_req, out_idx,
                                              out_rows, out_pos, as_stream(stream)),
-                  "kvf_select_topk_segmented");
+                as_stream(stream), "kvf_select_topk_segmented");
   KVF_GUARD_END
 }
 
@@ -317,8 +354,8 @@ kvf_status kvf_select_static(const kvf_batch* batch, const kvf_chunk* chunks, in
   if (B.cu_N[B.n_req] == 0) return KVF_OK;
   KVF_CHECK(mask != nullptr, KVF_ERR_INVALID_ARG, "mask is NULL");
   KVF_CHECK(n_chunks == 0 || chunks, KVF_ERR_INVALID_ARG, "chunks is NULL");
-  return from_hip(kvf::launch_static_mask(B, chunks, n_chunks, *rules, mask, as_stream(stream)),
-                  "kvf_select_static");
+  return finish(kvf::launch_static_mask(B, chunks, n_chunks, *rules, mask, as_stream(stream)),
+                as_stream(stream), "kvf_select_static");
   KVF_GUARD_END
 }
 
@@ -379,11 +416,11 @@ kvf_status kvf_recompute_qkv(const kvf_layer_desc* layer, const void* x, int64_t
   const size_t need = kvf::recompute_workspace(*layer, M, out_mask);
   KVF_CHECK(ws_bytes >= need && (need == 0 || workspace != nullptr), KVF_ERR_WORKSPACE,
             "workspace of %zu bytes given, %zu needed", ws_bytes, need);
-  return from_hip(kvf::launch_recompute(*layer, x, x_rows, row_src, row_pos, M, w_qkv, out_mask,
+  return finish(kvf::launch_recompute(*layer, x, x_rows, row_src, row_pos, M, w_qkv, out_mask,
                                         rope_cos, rope_sin, rope_n_pos, q_out, k_out, v_out,
                                         kv_out_row, kv_out_rows, workspace, ws_bytes,
                                         as_stream(stream)),
-                  "kvf_recompute_qkv");
+                as_stream(stream), "kvf_recompute_qkv");
   KVF_GUARD_END
 }
 
@@ -405,9 +442,10 @@ kvf_status kvf_scatter_kv(const kvf_layer_desc* layer, const void* k_src,
             "identity k source map needs M <= k_src_rows");
   KVF_CHECK(!v_src || v_src_row || M <= v_src_rows, KVF_ERR_INVALID_ARG,
             "identity v source map needs M <= v_src_rows");
-  return from_hip(kvf::launch_scatter(*layer, k_src, k_src_row, k_src_rows, v_src, v_src_row,
+  return finish(kvf::launch_scatter(*layer, k_src, k_src_row, k_src_rows, v_src, v_src_row,
                                       v_src_rows, dst_row, M, fused_k, fused_v, fused_rows,
-                                      as_stream(stream)), "kvf_scatter_kv");
+                                      as_stream(stream)),
+                as_stream(stream), "kvf_scatter_kv");
   KVF_GUARD_END
 }
 
@@ -453,9 +491,9 @@ kvf_status kvf_sparse_q_attention(const kvf_layer_desc* layer, const kvf_batch* 
     KVF_CHECK(workspace_bytes >= need, KVF_ERR_WORKSPACE,
               "attention workspace %zu bytes, needs %zu", workspace_bytes, need);
   }
-  return from_hip(kvf::launch_attention(*layer, B, q, q_pos, cu_q, fused_k, fused_v, sm_scale,
+  return finish(kvf::launch_attention(*layer, B, q, q_pos, cu_q, fused_k, fused_v, sm_scale,
                                         out, lse, workspace, workspace_bytes, as_stream(stream)),
-                  "kvf_sparse_q_attention");
+                as_stream(stream), "kvf_sparse_q_attention");
   KVF_GUARD_END
 }
 

@@ -77,7 +77,7 @@ _IP = ctypes.POINTER(ctypes.c_int32)
 _SIGS = {
     "kvf_rope_table": (_I32, [ctypes.c_double, _I32, _I32, _P, _P, _P]),
     "kvf_rerotate": (_I32, [_LP, _P, _I32, _I32, _P, _P, ctypes.POINTER(KiviDesc), _I64, _P, _P,
-                            _I32, _P, _P, _I64, _P]),
+                            _I32, _P, _P, _I64, _I32, _P]),
     "kvf_score": (_I32, [_I32, _LP, _BP, _P, _P, _P, _I32, _P, _P, _P, _SZ, _P]),
     "kvf_score_workspace_size": (_SZ, [_I32, _LP, _BP, _I32]),
     "kvf_select_topk": (_I32, [_P, _P, _BP, _IP, _P, _P, _P, _P, _P, _SZ, _P]),
@@ -244,11 +244,13 @@ def rope_table(base: float, head_dim: int, n_pos: int, cos_out: torch.Tensor,
 def rerotate(layer: Layer, chunks: torch.Tensor, max_chunk_len: int,
              pool_k: Optional[torch.Tensor], pool_v: Optional[torch.Tensor],
              rope_cos: torch.Tensor, rope_sin: torch.Tensor, fused_k: torch.Tensor,
-             fused_v: torch.Tensor, kivi: Optional[dict] = None, stream=None):
+             fused_v: Optional[torch.Tensor], kivi: Optional[dict] = None, k_only: bool = False,
+             stream=None):
     """chunks: int32 [n_chunks, 8] device tensor (kvf_chunk rows).
     kivi: dict of k_codes, v_codes ([rows, Hkv, d * bits / 8] uint8), k_min,
     k_scale ([n_pool, Hkv, d]), v_min, v_scale ([rows, Hkv]); the code width
-    follows from the shapes."""
+    follows from the shapes.  k_only: keys only (values already in place;
+    pool_v / fused_v unused; pool_k may be fused_k)."""
     kd = None
     pool_rows = _rows(pool_k)
     if kivi is not None:
@@ -258,7 +260,7 @@ def rerotate(layer: Layer, chunks: torch.Tensor, max_chunk_len: int,
     return _run(_lib.kvf_rerotate, (ctypes.byref(d), _ptr(chunks), int(chunks.shape[0]), max_chunk_len,
                              _ptr(pool_k), _ptr(pool_v), kd, pool_rows, _ptr(rope_cos),
                              _ptr(rope_sin), int(rope_cos.shape[0]), _ptr(fused_k), _ptr(fused_v),
-                             _rows(fused_k),), "kvf_rerotate", stream)
+                             _rows(fused_k), 1 if k_only else 0), "kvf_rerotate", stream)
 
 
 def score_workspace_size(mode: int, layer: Layer, batch: Batch, n_last_q: int = 0) -> int:

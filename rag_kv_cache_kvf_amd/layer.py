@@ -57,8 +57,16 @@ def _noop(stream=None):
 
 
 class FusedLayerGPU:
+    """k_only (default: dense per-request caches): the per-chunk values are
+    stitched into the fused cache by the loader (`load()`, ahead of the pass),
+    and the pass re-positions the keys only (QCFuse page, section 2.1.2: the
+    values keep their token order; only the keys carry the rotation).  With
+    k_only False, or for a shared chunk pool or KIVI codes, the pass gathers
+    keys and values from the per-chunk caches itself."""
+
     def __init__(self, batch: SynthBatch, ratio_pct: int, device="cuda",
-                 pic: Optional[dict] = None, n_last_q: int = 0, mode: Optional[str] = None):
+                 pic: Optional[dict] = None, n_last_q: int = 0, mode: Optional[str] = None,
+                 k_only: Optional[bool] = None):
         wl = batch.wl
         self.wl = wl
         self.batch = batch
@@ -125,6 +133,19 @@ class FusedLayerGPU:
             else:
                 self.pool_k, self.pool_v = pk, pv
             del pool_hidden
+
+        # keys-only re-positioning: the values are stitched by load()
+        dense = self.kivi is None
+        self.k_only = (dense and not wl.pool_chunks) if k_only is None else bool(k_only)
+        if self.k_only and not dense:
+            raise ValueError("keys-only re-positioning needs a dense per-chunk cache")
+        if self.k_only:
+            src, dst = [], []
+            for s0, d0, _, ln in batch.chunk_table[:, :4]:
+                src.append(np.arange(s0, s0 + ln, dtype=np.int32))
+                dst.append(np.arange(d0, d0 + ln, dtype=np.int32))
+            self.stitch_src = _i32(np.concatenate(src), dev)
+            self.stitch_dst = _i32(np.concatenate(dst), dev)
 
         # budgets and buffers
         self.static_mask = None
@@ -194,8 +215,20 @@ class FusedLayerGPU:
 
     # ------------------------------------------------------------------ calls
     def _rerotate(self):
+        if self.k_only:
+            return kvf.rerotate(self.layer, self.chunks, self.max_chunk_len, self.pool_k, None,
+                                self.rope_cos, self.rope_sin, self.fused_k, None, k_only=True)
         return kvf.rerotate(self.layer, self.chunks, self.max_chunk_len, self.pool_k, self.pool_v,
                             self.rope_cos, self.rope_sin, self.fused_k, self.fused_v, kivi=self.kivi)
+
+    def load(self):
+        """The loader's part ahead of a pass in keys-only mode: the per-chunk
+        values stitched into the fused value cache in token order (a row copy
+        through kvf_scatter_kv).  A no-op when the pass gathers the values."""
+        if not self.k_only:
+            return
+        kvf.scatter_kv(self.layer, None, None, self.pool_v, self.stitch_src, self.stitch_dst,
+                       self.fused_k, self.fused_v, M=int(self.stitch_dst.shape[0]))
 
     def _k_probe(self):
         return kvf.recompute_qkv(self.layer, self.x, None, self.all_pos, self.w, kvf.KVF_OUT_K,
@@ -337,11 +370,20 @@ class FusedLayerGPU:
     def stage_attention(self):
         self._stage("attention")
 
+    def step(self):
+        """Enqueue one pass of the hot path (the calls() list) on the current
+        stream; in keys-only mode the values must already be stitched
+        (load()), and a pass leaves them stitched except at the rows it
+        recomputes, which the next pass with the same selection rewrites."""
+        for _, _, fn in self.calls():
+            fn()
+
     def run(self, forced_sel: Optional[Sequence[np.ndarray]] = None):
-        """Enqueue one pass of the whole path on the current stream."""
+        """Enqueue load() and one pass of the whole path on the current
+        stream (optionally with a given selection instead of top-k)."""
+        self.load()
         if forced_sel is None:
-            for _, _, fn in self.calls():
-                fn()
+            self.step()
             return
         forced = False
         for _, st, fn in self.calls():

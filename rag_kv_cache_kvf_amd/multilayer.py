@@ -57,7 +57,7 @@ class MultiLayerGPU:
         self.pcts = pcts
         self.device = torch.device(device)
         self.layers: List[FusedLayerGPU] = [
-            FusedLayerGPU(b, p, device=device, pic=None if pics is None else pics[l])
+            FusedLayerGPU(b, p, device=device, pic=None if pics is None else pics[l], k_only=False)
             for l, (b, p) in enumerate(zip(batches, pcts))]
         l0 = self.layers[0]
         self.kb = l0.kb
