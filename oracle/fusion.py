@@ -255,7 +255,8 @@ def fused_layer(x: np.ndarray, w_qkv: np.ndarray, pool_k: np.ndarray, pool_v: np
                 layer: Layer, mode: str, k_per_req: Sequence[int],
                 n_last_q: Optional[int] = None,
                 forced_sel: Optional[Sequence[np.ndarray]] = None,
-                store: Optional[str] = None) -> dict:
+                store: Optional[str] = None,
+                attend: Optional[Sequence[np.ndarray]] = None) -> dict:
     """Run the fused layer for a batch of independent requests.
 
     mode "deviation" ([KVB] Algorithm 2 at one layer): probe K~ for every row,
@@ -282,6 +283,12 @@ def fused_layer(x: np.ndarray, w_qkv: np.ndarray, pool_k: np.ndarray, pool_v: np
     and LSE are not rounded.  The QCFuse page runs every strategy in a BF16
     serving stack (section 4.1.1); store="bf16" is that reading.  With
     store=None nothing is rounded.
+
+    `attend` (per request, indices into that request's recomputed rows, i.e.
+    its P followed by its U rows) restricts the attention step to those rows:
+    "q", "out" and "lse" then hold only them, in that order (their queries
+    are the only ones projected), and "attend_flat" gives their indices
+    among all recomputed rows.  Every other output is unchanged.
     Returns every intermediate, float64, in flat request-major layouts.
     """
     def S(a):
@@ -336,23 +343,32 @@ def fused_layer(x: np.ndarray, w_qkv: np.ndarray, pool_k: np.ndarray, pool_v: np
 
     rows = np.concatenate(rows_all)
     pos = np.concatenate(pos_all)
-    if mode == "deviation":
-        new = {k: S(v) for k, v in recompute(x[rows], pos, w_qkv, layer, want=("q", "v")).items()}
-        new["k"] = k_probe[rows]
+    sizes = [len(p) for p in pos_all]
+    starts = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64)
+    if attend is None:
+        flat = np.arange(len(rows), dtype=np.int64)
     else:
-        new = {k: S(v) for k, v in recompute(x[rows], pos, w_qkv, layer).items()}
+        flat = np.concatenate([starts[r] + np.asarray(attend[r], dtype=np.int64)
+                               for r in range(n_req)])
+    want_kv = ("v",) if mode == "deviation" else ("k", "v")
+    new = {k: S(v) for k, v in recompute(x[rows], pos, w_qkv, layer, want=want_kv).items()}
+    if mode == "deviation":
+        new["k"] = k_probe[rows]
+    new["q"] = S(recompute(x[rows[flat]], pos[flat], w_qkv, layer, want=("q",))["q"])
     fk, fv = fuse(fk, fv, rows, new["k"], new["v"])
 
     outs, lses = [], []
-    off = 0
+    qoff = 0
     for r in range(n_req):
         a, b = cu_T[r], cu_T[r + 1]
-        m = len(rows_all[r])
-        o, l = causal_attention(new["q"][off:off + m], pos_all[r], fk[a:b], fv[a:b], layer)
+        idx = np.arange(sizes[r]) if attend is None else np.asarray(attend[r], dtype=np.int64)
+        o, l = causal_attention(new["q"][qoff:qoff + len(idx)], pos_all[r][idx], fk[a:b], fv[a:b],
+                                layer)
         outs.append(o)
         lses.append(l)
-        off += m
-    res.update(scores=scores, sel=sels, rows=rows, pos=pos, cu_q=np.concatenate([[0], np.cumsum([len(p) for p in pos_all])]),
+        qoff += len(idx)
+    res["attend_flat"] = flat
+    res.update(scores=scores, sel=sels, rows=rows, pos=pos, cu_q=starts,
                q=new["q"], k_new=new["k"], v_new=new["v"], fused_k=fk, fused_v=fv,
                out=np.concatenate(outs), lse=np.concatenate(lses))
     return res

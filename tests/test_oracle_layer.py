@@ -161,3 +161,24 @@ def test_given_selection_mode(name):
     np.testing.assert_allclose(allr["fused_k"], full["k"], rtol=1e-9, atol=1e-9)
     with pytest.raises(ValueError):
         fusion.fused_layer(x, w, pk, pv, b.chunk_table, b.cu_T, b.n_ctx, layer, "none", ks)
+
+
+@pytest.mark.parametrize("name", ["mini_bf16_mass", "mini_bf16_dev_pool"])
+def test_attend_subset(name):
+    """attend= computes the queries, outputs and LSE of the chosen recomputed
+    rows only; they equal the same rows of the full computation, and every
+    cache output is unchanged."""
+    wl, b, layer, x, w, pk, pv = _setup(name)
+    k = [fusion.budget(int(n), 30) for n in b.n_ctx]
+    args = (x, w, pk, pv, b.chunk_table, b.cu_T, b.n_ctx, layer, wl.score, k)
+    full = fusion.fused_layer(*args, store="bf16")
+    g = np.random.default_rng(3)
+    sizes = np.diff(full["cu_q"])
+    att = [np.sort(g.choice(int(m), size=max(1, int(m) // 3), replace=False)) for m in sizes]
+    sub = fusion.fused_layer(*args, store="bf16", attend=att)
+    flat = sub["attend_flat"]
+    assert len(flat) == sum(len(a) for a in att)
+    for key in ("out", "lse", "q"):
+        np.testing.assert_array_equal(sub[key], full[key][flat], err_msg=key)
+    for key in ("fused_k", "fused_v", "rows", "pos", "k_new", "v_new"):
+        np.testing.assert_array_equal(sub[key], full[key], err_msg=key)
