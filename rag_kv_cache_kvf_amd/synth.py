@@ -249,11 +249,24 @@ def get_workload(name: str) -> Workload:
 # storage encodings
 # ----------------------------------------------------------------------------
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
-    """float32 -> bf16 bit patterns (uint16), round to nearest even."""
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
-    lsb = (u >> 16) & np.uint32(1)
-    r = (u + np.uint32(0x7FFF) + lsb) >> 16
-    return r.astype(np.uint16)
+    """float32 -> bf16 bit patterns (uint16), round to nearest even: add
+    0x7FFF plus the lowest kept bit, then drop the low 16 bits.  Works in
+    blocks of 2^20 values so large tensors stay cache-sized."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.reshape(-1).view(np.uint32)
+    out = np.empty(u.shape, dtype=np.uint16)
+    step = 1 << 20
+    t = np.empty(min(step, max(u.size, 1)), dtype=np.uint32)
+    for i in range(0, u.size, step):
+        uc = u[i:i + step]
+        tc = t[:uc.size]
+        np.right_shift(uc, 16, out=tc)
+        np.bitwise_and(tc, 1, out=tc)
+        np.add(tc, uc, out=tc)
+        np.add(tc, np.uint32(0x7FFF), out=tc)
+        np.right_shift(tc, 16, out=tc)
+        out[i:i + step] = tc
+    return out.reshape(x.shape)
 
 
 def encode(x: np.ndarray, dtype: str) -> np.ndarray:
@@ -264,12 +277,39 @@ def encode(x: np.ndarray, dtype: str) -> np.ndarray:
     raise ValueError(dtype)
 
 
+def _encode_rows(x: np.ndarray, dtype: str) -> np.ndarray:
+    """encode() of a 2-D array, row blocks in parallel."""
+    if dtype != "bf16" or x.ndim != 2 or x.shape[0] < 64:
+        return encode(x, dtype)
+    out = np.empty(x.shape, dtype=np.uint16)
+    step = max(1, x.shape[0] // 32)
+
+    def one(i):
+        out[i:i + step] = f32_to_bf16_bits(x[i:i + step])
+    list(_pool().map(one, range(0, x.shape[0], step)))
+    return out
+
+
 # ----------------------------------------------------------------------------
 # random streams
 # ----------------------------------------------------------------------------
 def _rng(seed: int, name: str, *keys: int) -> np.random.Generator:
     tag = zlib.crc32(name.encode())
     return np.random.default_rng(np.random.SeedSequence([seed, tag, *keys]))
+
+
+def _pool():
+    """Thread pool for independent seeded draws (one per process)."""
+    global _POOL
+    if _POOL is None:
+        import concurrent.futures
+        import os
+        n = min(16, len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else 8)
+        _POOL = concurrent.futures.ThreadPoolExecutor(max_workers=max(1, n))
+    return _POOL
+
+
+_POOL = None
 
 
 def _normal(seed: int, name: str, shape, *keys: int, std: float = 1.0) -> np.ndarray:
@@ -409,33 +449,47 @@ def make_batch(wl: Workload | str, seed: Optional[int] = None) -> Batch:
     H = wl.hidden
     x = np.empty((total, H), dtype=np.float32)
     pool_hidden = np.empty((int(pool_cu[-1]), H), dtype=np.float32)
+    # Every draw has its own key, so the draws run on a thread pool (the
+    # generator releases the GIL) without changing any value.
+    pool = _pool()
 
     if wl.pool_chunks:
-        for c in range(n_pool):
+        def fill_pool(c):
             pool_hidden[pool_cu[c]:pool_cu[c + 1]] = _normal(sd, "pool_hidden", (pool_len[c], H), c)
+        list(pool.map(fill_pool, range(n_pool)))
 
     table = []
+    jobs = []
     for r in range(wl.n_req):
         ids = _chunk_ids(wl, r)
         for s in range(m):
             c = ids[s]
             rows = slice(int(cu_T[r] + starts[s]), int(cu_T[r] + starts[s + 1]))
-            if wl.pool_chunks:
-                base = pool_hidden[pool_cu[c]:pool_cu[c + 1]]
-                if s == 0:
-                    x[rows] = base
-                else:
-                    x[rows] = base + np.float32(wl.sigma) * _normal(sd, "fresh_noise", base.shape, r, s)
-            else:
-                fresh = _normal(sd, "fresh_hidden", (lens[s], H), r, s)
-                x[rows] = fresh
-                if s == 0:
-                    pool_hidden[pool_cu[c]:pool_cu[c + 1]] = fresh
-                else:
-                    pool_hidden[pool_cu[c]:pool_cu[c + 1]] = fresh + np.float32(wl.sigma) * _normal(
-                        sd, "cached_noise", fresh.shape, r, s)
+            jobs.append((r, s, c, rows))
             table.append([int(pool_cu[c]), rows.start, int(starts[s]), lens[s], c, 0, 0, 0])
+
+    def fill_slot(job):
+        r, s, c, rows = job
+        if wl.pool_chunks:
+            base = pool_hidden[pool_cu[c]:pool_cu[c + 1]]
+            if s == 0:
+                x[rows] = base
+            else:
+                x[rows] = base + np.float32(wl.sigma) * _normal(sd, "fresh_noise", base.shape, r, s)
+        else:
+            fresh = _normal(sd, "fresh_hidden", (lens[s], H), r, s)
+            x[rows] = fresh
+            if s == 0:
+                pool_hidden[pool_cu[c]:pool_cu[c + 1]] = fresh
+            else:
+                pool_hidden[pool_cu[c]:pool_cu[c + 1]] = fresh + np.float32(wl.sigma) * _normal(
+                    sd, "cached_noise", fresh.shape, r, s)
+
+    def fill_query(r):
         x[cu_T[r] + n_ctx:cu_T[r + 1]] = _normal(sd, "query_hidden", (tq[r], H), r)
+
+    list(pool.map(fill_slot, jobs))
+    list(pool.map(fill_query, range(wl.n_req)))
 
     n_out = (wl.n_q_heads + 2 * wl.n_kv_heads) * wl.head_dim
     w = _normal(sd, "w_qkv", (n_out, H), std=1.0 / np.sqrt(H))
@@ -447,9 +501,9 @@ def make_batch(wl: Workload | str, seed: Optional[int] = None) -> Batch:
         chunk_table=np.asarray(table, dtype=np.int32).reshape(-1, 8),
         pool_cu=pool_cu,
         pool_pos=pool_pos,
-        pool_hidden=encode(pool_hidden, wl.dtype),
-        x=encode(x, wl.dtype),
-        w_qkv=encode(w, wl.dtype),
+        pool_hidden=_encode_rows(pool_hidden, wl.dtype),
+        x=_encode_rows(x, wl.dtype),
+        w_qkv=_encode_rows(w, wl.dtype),
     )
 
 
