@@ -3,7 +3,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from oracle import storage
+from oracle import fusion, storage
 
 TOL = {"bf16": 2e-2, "f32": 1e-4}     # max |gpu - oracle| / rms(oracle)
 
@@ -87,3 +87,24 @@ def encode(x: np.ndarray, dtype: str) -> np.ndarray:
 
 def decode(a: np.ndarray, dtype: str) -> np.ndarray:
     return storage.decode(a, dtype)
+
+
+def check_selection(name, sel_gpu, gs, rs, ks, n_ctx):
+    """GPU picks = TopK of the GPU's own scores, bit for bit; differences from
+    the oracle's picks only where the scores' error can reorder them."""
+    delta = float(np.max(np.abs(gs - rs)))
+    off = 0
+    for r, k in enumerate(ks):
+        n = int(n_ctx[r])
+        g_r, o_r = gs[off:off + n], rs[off:off + n]
+        want = fusion.select_topk(g_r.astype(np.float32), k)
+        assert np.array_equal(sel_gpu[r], want), f"{name} req {r}: not the TopK of its own scores"
+        ref_sel = fusion.select_topk(o_r.astype(np.float32), k)
+        diff = np.setxor1d(sel_gpu[r], ref_sel)
+        if k and len(diff):
+            kth = np.sort(o_r)[::-1][k - 1]
+            far = np.abs(o_r[diff] - kth).max()
+            assert far <= 2 * delta, f"{name} req {r}: a pick {far:.3g} from the k-th score (2 max|d| = {2 * delta:.3g})"
+        print(f"[info] {name} req {r}: {len(diff) // 2} of {k} picks differ from the oracle's "
+              f"(scores max|d| {delta:.3g})", flush=True)
+        off += n
