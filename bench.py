@@ -622,7 +622,7 @@ def measure(wl, ratio, steps, warmup, flush, graph=False):
             ach, peak, unit = amount / (ms * 1e-3) / 1e12, peak_mfma, "TFLOP/s"
         calls[name] = {"ms": round(ms, 5), "bound": kind, "achieved": round(ach, 2),
                        "unit": unit, "frac": round(ach / peak, 4),
-                       "algorithmic": amount}
+                       "algorithmic": float(amount)}
     dom = max(per_call, key=per_call.get)
     kname, ksrc = CALL_KERNEL[dom]
     if dom == "score" and g.selector == "anchor":
@@ -635,7 +635,7 @@ def measure(wl, ratio, steps, warmup, flush, graph=False):
     c = calls[dom]
     roofline = {"kernel": kname, "call": dom, "bound": kind, "achieved": c["achieved"],
                 "peak": PEAK["hbm"] if kind == "hbm" else peak_mfma, "unit": c["unit"],
-                "frac": c["frac"], "avg_ms": c["ms"], "algorithmic_per_launch": amount,
+                "frac": c["frac"], "avg_ms": c["ms"], "algorithmic_per_launch": float(amount),
                 "traffic": _traffic(kname, ksrc, wl.name)}
     timing = {"protocol": f"{steps} steps timed one by one with HIP events on the launch stream, "
                           f"each after an untimed read-modify-write of {FLUSH_BYTES >> 30} GiB "

@@ -67,10 +67,10 @@ def sources():
     return sorted(glob.glob(os.path.join(HERE, "*.hip")) + glob.glob(os.path.join(HERE, "kernels", "*.hip")))
 
 
-def _compile(src: str) -> str:
+def _compile(src: str, out_dir: str = BUILD_DIR, extra: tuple = ()) -> str:
     rel = os.path.relpath(src, HERE).replace(os.sep, "_")
-    obj = os.path.join(BUILD_DIR, rel[:-4] + ".o")
-    cmd = [HIPCC, *CFLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
+    obj = os.path.join(out_dir, rel[:-4] + ".o")
+    cmd = [HIPCC, *CFLAGS, *FILE_FLAGS.get(os.path.basename(src), []), *extra, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
@@ -126,6 +126,42 @@ def build(jobs: int | None = None, verbose: bool = True) -> str:
     if verbose:
         print(f"built {OUT_LIB} from {len(srcs)} sources")
     return OUT_LIB
+
+
+# AddressSanitizer on the host code only: each -fsanitize= right after
+# -Xarch_host, so the device code is built exactly as in the library.
+ASAN_HOST = ("-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer",
+             "-Xarch_host", "-g")
+ASAN_DIR = os.path.join(BUILD_DIR, "asan")
+CLANG = os.environ.get("KVF_CLANG", "/opt/rocm/llvm/bin/clang")
+
+
+def build_asan(driver_src: str, jobs: int | None = None) -> str:
+    """A host-AddressSanitizer build of the library (_build/asan/libkvfuse_asan.so)
+    and of a C test driver linked against it; returns the driver's path.
+    For checking the host-side validation and bookkeeping on a machine
+    without a GPU."""
+    os.makedirs(ASAN_DIR, exist_ok=True)
+    srcs = sources()
+    jobs = jobs or min(len(srcs), max(1, (os.cpu_count() or 4)))
+    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(lambda f: _compile(f, ASAN_DIR, ASAN_HOST), srcs))
+    lib = os.path.join(ASAN_DIR, "libkvfuse_asan.so")
+    # the sanitizer runtime comes from the driver executable (statically
+    # linked there), which resolves the library's instrumentation calls
+    r = subprocess.run([HIPCC, "-shared", f"--offload-arch={ARCH}", "-fPIC", "-Xarch_host",
+                        "-fsanitize=address", "-o", lib, *objs],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"asan link failed:\n{r.stdout}\n{r.stderr}")
+    exe = os.path.join(ASAN_DIR, os.path.splitext(os.path.basename(driver_src))[0])
+    r = subprocess.run([CLANG, "-fsanitize=address", "-fno-omit-frame-pointer",
+                        "-g", "-O1", "-I", INCLUDE, driver_src, "-o", exe, "-L", ASAN_DIR,
+                        "-lkvfuse_asan", f"-Wl,-rpath,{ASAN_DIR}"],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"asan driver build failed:\n{r.stdout}\n{r.stderr}")
+    return exe
 
 
 if __name__ == "__main__":
