@@ -253,6 +253,26 @@ size_t kvf_score_workspace_size(kvf_score_mode mode, const kvf_layer_desc* layer
                                 const kvf_batch* batch, int32_t n_last_q);
 
 /* ---------------------------------------------------------------------------
+ * kvf_score_attn_mass_noalloc - kvf_score(KVF_SCORE_ATTN_MASS) for callers
+ * that cannot allocate device memory (code being captured into a graph,
+ * tight serving loops, harnesses that forbid allocation).  Same arguments
+ * and result as kvf_score in attention-mass mode (accumulate: 1 adds to
+ * `scores` like KVF_SCORE_ACCUMULATE), but no workspace: the call uses a
+ * scratch array of KVF_NOALLOC_SCRATCH_BYTES (48 MiB) inside the library,
+ * one per GPU, held from the first use on that GPU until the process ends.
+ * Calls whose kvf_score_workspace_size would exceed it get
+ * KVF_ERR_UNSUPPORTED.  The call allocates and frees nothing.  Every call on
+ * a GPU shares that GPU's array: calls that overlap in time on one GPU (on
+ * different streams, or from several host threads) race and give undefined
+ * scores; order them.  The device the stream belongs to must be current.
+ */
+#define KVF_NOALLOC_SCRATCH_BYTES (48u << 20)
+kvf_status kvf_score_attn_mass_noalloc(const kvf_layer_desc* layer, const kvf_batch* batch,
+                                       const void* fused_k, const void* q_u, int32_t n_last_q,
+                                       const uint8_t* eligible, float* scores, int32_t accumulate,
+                                       void* stream);
+
+/* ---------------------------------------------------------------------------
  * kvf_select_topk - S3: P_r = TopK(score, k_r) per request ([QCF] 3.2.1
  * Eq. 11).  Order: larger score first; ties to the lower position; -0 == +0;
  * NaN ranks below every number.  k_per_req: HOST [n_req], 0 <= k_r <= N_r.

@@ -28,6 +28,7 @@
 //
 // fp32 path: one wave per (row, head) with lane-parallel keys; used by the
 // small fp32 workloads only.
+#include <mutex>
 #include <type_traits>
 
 #include "../kvf_common.h"
@@ -1362,6 +1363,61 @@ hipError_t launch_attn_mass(const kvf_layer_desc& L, const BatchArgs& B, const v
     hipLaunchKernelGGL(head_sum_kernel, dim3(ceil_div(n, 256)), dim3(256), 0, st, part, L.n_kv_heads,
                        n, out);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// attention mass without a caller workspace
+// ---------------------------------------------------------------------------
+// For callers that cannot allocate device memory: the workspace lives in this
+// file-scope device array, one copy per GPU, held until the process ends.
+// Host code never passes the array's name (a host-side stand-in) to a
+// kernel: its device address is looked up once per device and kept.
+static __device__ __align__(256) unsigned char scratch[KVF_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+
+hipError_t mass_scratch_address(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
+
+__global__ void __launch_bounds__(256) zero_words_kernel(uint32_t* __restrict__ p, int64_t n) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+hipError_t launch_attn_mass_noalloc(const kvf_layer_desc& L, const BatchArgs& B, const void* fk,
+                                    const void* q_u, int n_last_q, const ScoreOut& out,
+                                    hipStream_t st) {
+  const MassLayout lay = mass_layout(L, B, n_last_q);
+  if (lay.total > KVF_NOALLOC_SCRATCH_BYTES) return hipErrorInvalidValue;
+  void* ws = nullptr;
+  hipError_t e = mass_scratch_address(&ws);
+  if (e != hipSuccess) return e;
+  // the arrival counters this call uses start at zero whatever an earlier
+  // call left (a fill kernel, which graph capture records safely)
+  if (lay.n_cnt > 0) {
+    hipLaunchKernelGGL(zero_words_kernel, dim3(static_cast<unsigned>(ceil_div(static_cast<int>(lay.n_cnt), 256))),
+                       dim3(256), 0, st, reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + lay.off_cnt),
+                       lay.n_cnt);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return launch_attn_mass(L, B, fk, q_u, n_last_q, out, ws, KVF_NOALLOC_SCRATCH_BYTES, st);
 }
 
 }  // namespace kvf

@@ -272,6 +272,34 @@ kvf_status kvf_score(kvf_score_mode mode_flags, const kvf_layer_desc* layer,
   KVF_GUARD_END
 }
 
+kvf_status kvf_score_attn_mass_noalloc(const kvf_layer_desc* layer, const kvf_batch* batch,
+                                       const void* fused_k, const void* q_u, int32_t n_last_q,
+                                       const uint8_t* eligible, float* scores, int32_t accumulate,
+                                       void* stream) {
+  KVF_GUARD_BEGIN
+  kvf_status st = check_layer(layer);
+  if (st != KVF_OK) return st;
+  kvf::BatchArgs B;
+  st = check_batch(batch, &B);
+  if (st != KVF_OK) return st;
+  KVF_CHECK(accumulate == 0 || accumulate == 1, KVF_ERR_INVALID_ARG, "accumulate must be 0 or 1");
+  if (B.cu_N[B.n_req] == 0) return KVF_OK;
+  KVF_CHECK(fused_k && q_u && scores, KVF_ERR_INVALID_ARG, "required pointer is NULL");
+  KVF_CHECK(kvf::attn_mass_key_tiles(B) <= 16384, KVF_ERR_UNSUPPORTED,
+            "attention mass over %lld 128-key context tiles (at most 16384 per call)",
+            static_cast<long long>(kvf::attn_mass_key_tiles(B)));
+  const size_t need = kvf::attn_mass_workspace(*layer, B, n_last_q);
+  KVF_CHECK(need <= KVF_NOALLOC_SCRATCH_BYTES, KVF_ERR_UNSUPPORTED,
+            "this call needs %zu bytes of scratch; the allocation-free entry point holds %zu "
+            "(use kvf_score with a caller workspace)", need,
+            static_cast<size_t>(KVF_NOALLOC_SCRATCH_BYTES));
+  const kvf::ScoreOut out{scores, eligible, accumulate};
+  return finish(kvf::launch_attn_mass_noalloc(*layer, B, fused_k, q_u, n_last_q, out,
+                                              as_stream(stream)),
+                as_stream(stream), "kvf_score_attn_mass_noalloc");
+  KVF_GUARD_END
+}
+
 size_t kvf_select_workspace_size(const kvf_batch* batch) {
   (void)batch;
   return 0;

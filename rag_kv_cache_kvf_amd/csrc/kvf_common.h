@@ -225,6 +225,9 @@ hipError_t launch_attn_mass(const kvf_layer_desc& L, const BatchArgs& B, const v
                             const void* q_u, int n_last_q, const ScoreOut& out, void* ws,
                             size_t ws_bytes, hipStream_t st);
 size_t attn_mass_workspace(const kvf_layer_desc& L, const BatchArgs& B, int n_last_q);
+hipError_t launch_attn_mass_noalloc(const kvf_layer_desc& L, const BatchArgs& B, const void* fk,
+                                    const void* q_u, int n_last_q, const ScoreOut& out,
+                                    hipStream_t st);
 // 128-key context tiles of a batch; the attention-mass call takes at most 16384
 int64_t attn_mass_key_tiles(const BatchArgs& B);
 hipError_t launch_key_norm(const kvf_layer_desc& L, const BatchArgs& B, const void* fk,

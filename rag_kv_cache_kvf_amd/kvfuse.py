@@ -80,6 +80,7 @@ _SIGS = {
                             _I32, _P, _P, _I64, _I32, _P]),
     "kvf_score": (_I32, [_I32, _LP, _BP, _P, _P, _P, _I32, _P, _P, _P, _SZ, _P]),
     "kvf_score_workspace_size": (_SZ, [_I32, _LP, _BP, _I32]),
+    "kvf_score_attn_mass_noalloc": (_I32, [_LP, _BP, _P, _P, _I32, _P, _P, _I32, _P]),
     "kvf_select_topk": (_I32, [_P, _P, _BP, _IP, _P, _P, _P, _P, _P, _SZ, _P]),
     "kvf_select_topk_segmented": (_I32, [_P, _P, _BP, _P, _I32, _IP, _P, _P, _P, _P]),
     "kvf_select_static": (_I32, [_BP, _P, _I32, ctypes.POINTER(StaticRules), _P, _P]),
@@ -261,6 +262,19 @@ def rerotate(layer: Layer, chunks: torch.Tensor, max_chunk_len: int,
                              _ptr(pool_k), _ptr(pool_v), kd, pool_rows, _ptr(rope_cos),
                              _ptr(rope_sin), int(rope_cos.shape[0]), _ptr(fused_k), _ptr(fused_v),
                              _rows(fused_k), 1 if k_only else 0), "kvf_rerotate", stream)
+
+
+def score_attn_mass_noalloc(layer: Layer, batch: Batch, fused_k: torch.Tensor, q_u: torch.Tensor,
+                            scores: torch.Tensor, n_last_q: int = 0,
+                            eligible: Optional[torch.Tensor] = None, accumulate: bool = False,
+                            stream=None):
+    """kvf_score_attn_mass_noalloc: the attention-mass score without a
+    caller workspace (the library's per-GPU scratch array)."""
+    d = layer.desc()
+    return _run(_lib.kvf_score_attn_mass_noalloc,
+                (ctypes.byref(d), ctypes.byref(batch.desc), _ptr(fused_k), _ptr(q_u), n_last_q,
+                 _ptr(eligible), _ptr(scores), 1 if accumulate else 0),
+                "kvf_score_attn_mass_noalloc", stream, keep=(d, batch))
 
 
 def score_workspace_size(mode: int, layer: Layer, batch: Batch, n_last_q: int = 0) -> int:

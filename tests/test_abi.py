@@ -275,3 +275,28 @@ def test_static_counts_match_oracle(lib, seed):
         want = int(selectors.static_mask(ns[r], starts[r] or [0], sink, boundary, seam).sum()) \
             if ns[r] else 0
         assert out[r] == want
+
+
+def test_noalloc_rejects_oversized_calls(lib):
+    """The allocation-free attention-mass call refuses, on the host, a call
+    whose workspace would exceed its fixed scratch array (48 MiB), and
+    validates like kvf_score otherwise."""
+    P = ctypes.c_void_p
+    lib.kvf_score_attn_mass_noalloc.argtypes = [P, P, P, P, ctypes.c_int32, P, P, ctypes.c_int32, P]
+    lib.kvf_score_workspace_size.restype = ctypes.c_size_t
+    lib.kvf_score_workspace_size.argtypes = [ctypes.c_int32, P, P, ctypes.c_int32]
+    L = Layer(8192, 64, 8, 128, 1)
+    T, N = 66048, 65536
+    b, keep = _batch([0, T], [N])
+    need = lib.kvf_score_workspace_size(1, ctypes.byref(L), ctypes.byref(b), 0)
+    assert need > 48 << 20
+    assert lib.kvf_score_attn_mass_noalloc(ctypes.byref(L), ctypes.byref(b), FAKE, FAKE, 0, None, FAKE,
+                                           0, None) == 2
+    assert lib.kvf_score_attn_mass_noalloc(ctypes.byref(L), ctypes.byref(b), FAKE, None, 0, None, FAKE,
+                                           0, None) == 1
+    assert lib.kvf_score_attn_mass_noalloc(ctypes.byref(L), ctypes.byref(b), FAKE, FAKE, 0, None, FAKE,
+                                           2, None) == 1
+    # within the limit the same call size passes validation (not launched here)
+    b2, keep2 = _batch([0, 5184], [5120])
+    assert lib.kvf_score_workspace_size(1, ctypes.byref(Layer(4096, 32, 8, 128, 1)), ctypes.byref(b2),
+                                        0) < 48 << 20
