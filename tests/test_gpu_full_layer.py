@@ -9,8 +9,8 @@ Per workload:
     lies within 2 max|d| of the oracle's k-th score (the most a top-k can
     move when no score moves by more than max|d|);
   * with the oracle's selection forced into the GPU path: the recomputed row
-    list bit-exact, the fused cache, the queries and the attention output and
-    LSE of the recomputed rows - every row for the 8B-shaped mass workload and
+    list bit-exact, the fused cache and the queries (against the exact
+    float64 layer), and the attention output and LSE of the recomputed rows - every row for the 8B-shaped mass workload and
     the int8 workload, sampled rows (the oracle computes their queries and
     attention one by one) for the 8-request pool workload and the 70B-shaped
     layer.
@@ -88,13 +88,17 @@ def test_full_size_layer(layer_mod, name, pct, rows):
     else:
         # every recomputed row plus a sample of the re-positioned ones
         crow = np.unique(np.concatenate([ref["rows"], synth.random_rows(b.total_rows, 8192, 41)]))
+    # cache entries and queries: the exact float64 layer on the same
+    # selection (the GPU's are one bf16 rounding of an fp32 sum from it)
+    exact = fusion.fused_layer(x, w, opk, opv, b.chunk_table, b.cu_T, b.n_ctx, lo, wl.score, ks,
+                               forced_sel=ref["sel"], attend=attend)
     gk = from_gpu(g.fused_k[torch.from_numpy(crow).cuda()])
     gv = from_gpu(g.fused_v[torch.from_numpy(crow).cuda()])
-    assert_close(gk, ref["fused_k"][crow], wl.dtype, f"{name}@{pct} fused K ({len(crow)} rows)")
-    assert_close(gv, ref["fused_v"][crow], wl.dtype, f"{name}@{pct} fused V ({len(crow)} rows)")
+    assert_close(gk, exact["fused_k"][crow], wl.dtype, f"{name}@{pct} fused K ({len(crow)} rows)")
+    assert_close(gv, exact["fused_v"][crow], wl.dtype, f"{name}@{pct} fused V ({len(crow)} rows)")
     flat = ref["attend_flat"]
     sel_t = torch.from_numpy(flat).cuda()
-    assert_close(from_gpu(g.q[sel_t]), ref["q"], wl.dtype, f"{name}@{pct} recomputed Q ({len(flat)} rows)")
+    assert_close(from_gpu(g.q[sel_t]), exact["q"], wl.dtype, f"{name}@{pct} recomputed Q ({len(flat)} rows)")
     assert_close_vectors(from_gpu(g.out[sel_t]), ref["out"], wl.dtype,
                          f"{name}@{pct} attention output ({len(flat)} rows)")
     assert_close(from_gpu(g.lse[sel_t]), ref["lse"], wl.dtype, f"{name}@{pct} lse", tol=1e-3)
