@@ -140,6 +140,24 @@ __device__ __forceinline__ void put_dev4(__amdgpu_buffer_rsrc_t r, uint32_t voff
 __device__ __forceinline__ f32x4_t get_dev4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kDeviceScope));
 }
+// 8- and 4-byte forms (plain loads and stores to the compiler, so a batch of
+// them is issued back to back; relaxed atomics would be issued one at a
+// time).
+__device__ __forceinline__ void put_dev2(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, float x,
+                                         float y) {
+  const u32x2_t v = {__float_as_uint(x), __float_as_uint(y)};
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, voff, soff, kDeviceScope);
+}
+__device__ __forceinline__ float2 get_dev2(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, kDeviceScope);
+  return make_float2(__uint_as_float(v[0]), __uint_as_float(v[1]));
+}
+__device__ __forceinline__ void put_dev1(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, float x) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, voff, soff, kDeviceScope);
+}
+__device__ __forceinline__ float get_dev1(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, kDeviceScope));
+}
 // Every wave: wait until this wave's vector stores have been acknowledged,
 // then the workgroup barrier.  (A plain __syncthreads() waits only for LDS
 // traffic on this part, not for global stores.)  The memory clobber keeps

@@ -16,7 +16,10 @@ from typing import Optional, Sequence
 
 import torch
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvfuse.so")
+# KVF_LIBRARY selects another build of the same library (an instrumented
+# one, say); by default the one built in this directory.
+_LIB_PATH = os.environ.get("KVF_LIBRARY") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libkvfuse.so")
 
 KVF_OK, KVF_ERR_INVALID_ARG, KVF_ERR_UNSUPPORTED, KVF_ERR_WORKSPACE, KVF_ERR_HIP = range(5)
 KVF_F32, KVF_BF16 = 0, 1
