@@ -232,15 +232,12 @@ kvf_status kvf_rerotate(const kvf_layer_desc* layer, const kvf_chunk* chunks,
  *   score_t = sum over the last n_last_q query tokens (all when <= 0) and all
  *   query heads of the probability at context position t.  Softmax scale is
  *   1/sqrt(d).  Needs a workspace of kvf_score_workspace_size() bytes; its
- *   first 131072 bytes are arrival counters (one per 128-key context tile,
- *   so at most 16384 tiles per call, else KVF_ERR_UNSUPPORTED) that must be
+ *   first 65536 bytes are arrival counters (one per 128-key context tile, so
+ *   at most 16384 tiles per call, else KVF_ERR_UNSUPPORTED) that must be
  *   zero before its first use (zero-fill it once when allocating it); every
  *   completed call leaves them zero, so calls of any shape may share one
  *   workspace.  Calls that share a workspace must not overlap.  The scores
- *   are deterministic (fixed summation order).  With at most 256 query
- *   vectors (query rows x Hq/Hkv) per request and kv head, the call is one
- *   cooperative launch whose workgroups wait for each other (the GPU holds
- *   them all at once); otherwise it takes three launches.
+ *   are deterministic (fixed summation order).
  * KVF_SCORE_KEY_NORM ([QCF] 3.3.1, the Knorm ranking rule):
  *   score_t = sqrt(sum over heads h and channels j of fused_k[t, h, j]^2),
  *   fp32 accumulation.  The norm is rotation invariant, so the re-positioned

@@ -883,10 +883,8 @@ struct MassArgs {
   int nq[KVF_MAX_REQ];           // query rows used
   int pos0[KVF_MAX_REQ];         // position of the first used query row
   int orow0[KVF_MAX_REQ];        // their rows in lse2 / the statistics planes
-  int cu_ktiles[KVF_MAX_REQ + 1];  // 128-key tiles of each request's context
+  int cu_ktiles[KVF_MAX_REQ + 1];
   int total_ktiles;
-  int cu_ttiles[KVF_MAX_REQ + 1];  // one launch: 256-key tiles of all of each request's keys
-  int cu_ftiles[KVF_MAX_REQ + 1];  // one launch: 256-key tiles of each request's context
   const void* q;
   const void* k;
   const float* lse2;             // [rows, Hq]
@@ -903,8 +901,6 @@ struct MassArgs {
 };
 
 constexpr int kMK = 128;         // keys per workgroup (4 waves x 32)
-// counter slots of the one-launch path (see the workspace layout below)
-constexpr int kMassCntArrive = 16384, kMassCntDepart = 24576, kMassMaxPairs = 8192;
 constexpr int kMQS = 256;        // query vectors staged per round (LDS)
 
 template <int D>
@@ -1135,6 +1131,9 @@ __global__ void __launch_bounds__(256) mass_colsum_bf16_kernel(MassArgs a) {
   }
   colsum += __shfl_xor(colsum, 32, kWave);
   const int n_all = a.b.cu_N[a.b.n_req];
+  // per-head column sums [kv head][sum N], moved as plain buffer accesses
+  // with the device-scope cache policy so a batch of them is in flight at
+  // once (relaxed atomics would go one at a time)
   const __amdgpu_buffer_rsrc_t pr = handoff_rsrc(a.part, static_cast<int64_t>(a.hkv) * n_all * 4);
   if (hf == 0 && kvalid)
     put_dev1(pr, static_cast<uint32_t>(a.b.cu_N[r] + key) * 4, static_cast<uint32_t>(g) * n_all * 4, colsum);
@@ -1148,272 +1147,10 @@ __global__ void __launch_bounds__(256) mass_colsum_bf16_kernel(MassArgs a) {
       float pv8[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u)
-        pv8[u] = g0 + u < a.hkv ? get_dev1(pr, key_off, static_cast<uint32_t>(g0 + u) * n_all * 4) : 0.f;
+        pv8[u] = get_dev1(pr, key_off, static_cast<uint32_t>(min(g0 + u, a.hkv - 1)) * n_all * 4);
 #pragma unroll
       for (int u = 0; u < 8; ++u)
         if (g0 + u < a.hkv) sum += pv8[u];
-    }
-    store_score(a.out, a.b.cu_N[r] + key0 + tid, sum);
-  }
-}
-
-// ---------------------------------------------------------------------------
-// bf16, at most 256 query vectors per kv head: one launch.  A workgroup owns
-// 256 keys (context or query; 32 per wave) of one kv head and computes S^T = K Q^T for
-// every query vector of that head once, keeping the scores in registers:
-//  1. per query vector, the (max, sum) of its exp2 scores over the
-//     workgroup's keys, published to the workspace;
-//  2. the workgroups of one (request, kv head) wait for each other (a
-//     counter and a bounded spin - the launch is cooperative, so every
-//     workgroup is resident), then each merges every tile's statistics into
-//     the log-sum-exp of each query vector;
-//  3. the column sums exp2(s - lse) over the query vectors of its context
-//     keys, from the scores still in registers; the last kv head of the key
-//     tile to finish adds the heads in a fixed order, as in the two-pass
-//     path.
-// The barrier's arrival counter is reset by the last workgroup to leave it,
-// when every workgroup of the group has passed its wait.
-constexpr int kMFV = 256;              // query vectors per kv head
-constexpr int kMFK = 256;              // keys per workgroup (8 waves x 32)
-constexpr int kMFT = 512;              // threads per workgroup
-constexpr int kMassSpin = 1 << 22;     // polls before a wait gives up (~0.1 s)
-
-template <int D>
-__global__ void __launch_bounds__(kMFT) mass_fused_bf16_kernel(MassArgs a) {
-  constexpr int KS = D / 16;
-  constexpr int LDQ = D + 8;
-  constexpr int VPR = D / 8;
-  constexpr int NB = kMFV / 32;
-  // query vectors during the scores; afterwards the cross-lane column sums
-  __shared__ __attribute__((aligned(16))) bf16_t Qs[kMFV][LDQ];
-  __shared__ float2 st[kMFT / 64][kMFV];
-  __shared__ float Ls[kMFV];
-  __shared__ int s_flag;
-  const int hkv = a.hkv;
-  const int g = blockIdx.x % hkv;
-  const int ktf = static_cast<int>(blockIdx.x / hkv);            // key tile over all requests
-  const int r = find_segment(a.cu_ttiles, a.b.n_req, ktf);
-  const int kt = ktf - a.cu_ttiles[r];
-  const int ntile = a.cu_ttiles[r + 1] - a.cu_ttiles[r];
-  const int T = a.b.cu_T[r + 1] - a.b.cu_T[r];
-  const int N = a.b.n_ctx[r];
-  const int64_t krow0 = a.b.cu_T[r];
-  const int key0 = kt * kMFK;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int c = lane & 31, hf = lane >> 5;
-  const int nqv = a.nq[r] * a.G;
-  const int nb = ceil_div(nqv, 32);
-  const int pair = r * hkv + g;
-
-  // this wave's 32 keys as the A operand: row = key, k = 8 hf + e
-  const bf16_t* Kg = static_cast<const bf16_t*>(a.k);
-  const int key_a = key0 + 32 * w + c;
-  bf16x8_t kf[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    if (key_a < T) {
-      kf[ks] = *reinterpret_cast<const bf16x8_t*>(Kg + ((krow0 + key_a) * hkv + g) * D + ks * 16 + hf * 8);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) kf[ks][e] = static_cast<__bf16>(0.f);
-    }
-  }
-  // the head's query vectors (vector v = row v / G, head g G + v % G), zero
-  // past nqv
-  const bf16_t* Qg = static_cast<const bf16_t*>(a.q);
-  {
-    constexpr int NV = kMFV * VPR / kMFT;
-    u32x4_t v4[NV];
-#pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      const int idx = tid + kMFT * j;
-      const int qq = idx / VPR, vc = idx - qq * VPR;
-      v4[j] = u32x4_t{0u, 0u, 0u, 0u};
-      if (qq < nqv) {
-        const int row = qq / a.G, hl = qq - row * a.G;
-        v4[j] = *reinterpret_cast<const u32x4_t*>(
-            Qg + ((static_cast<int64_t>(a.qrow0[r]) + row) * a.hq + g * a.G + hl) * D + vc * 8);
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      const int idx = tid + kMFT * j;
-      const int qq = idx / VPR, vc = idx - qq * VPR;
-      *reinterpret_cast<u32x4_t*>(&Qs[qq][vc * 8]) = v4[j];
-    }
-  }
-  __syncthreads();
-
-  // scores of every 32-vector block: lane (c, hf) value i is key
-  // key0 + 32 w + 8 (i/4) + 4 hf + (i%4) of query vector 32 j + c
-  const float cs = a.scale_log2;
-  f32x16_t s[NB];
-#pragma unroll
-  for (int j = 0; j < NB; ++j)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) s[j][i] = 0.f;
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      if (j < nb) {
-        const bf16x8_t qfrag = *reinterpret_cast<const bf16x8_t*>(&Qs[32 * j + c][ks * 16 + hf * 8]);
-        s[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qfrag, s[j], 0, 0, 0);
-      }
-    }
-  // Keys past a vector's position (or past the request) are masked; a tile
-  // whose keys every query row sees whole (keys below the first query
-  // position, within the request) needs no mask.
-  const bool masked = key0 + kMFK - 1 > min(a.pos0[r], T - 1);
-  // Per (wave, vector): M = max over the wave's 32 keys (log2 domain), then
-  // the scores are replaced by e = exp2(s c - M) and l = sum of e.  The
-  // column sums later reuse e: exp2(s c - lse) = e exp2(M - lse).
-  float Mw[NB];
-#pragma unroll
-  for (int j = 0; j < NB; ++j) {
-    const int qv = 32 * j + c;
-    if (masked) {
-      const int pos = qv < nqv ? a.pos0[r] + qv / a.G : -1;
-      const int lim = min(pos, T - 1) - (key0 + 32 * w + 4 * hf);
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-        if (8 * (i >> 2) + (i & 3) > lim) s[j][i] = -INFINITY;
-    }
-    float m = fmaxf(s[j][0], s[j][1]);
-#pragma unroll
-    for (int i = 2; i < 16; ++i) m = fmaxf(m, s[j][i]);
-    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
-    m = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-    const float M = m == -INFINITY ? -INFINITY : m * cs;
-    const float negM = m == -INFINITY ? 0.f : -M;
-    float l = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      s[j][i] = __builtin_amdgcn_exp2f(fmaf(s[j][i], cs, negM));
-      l += s[j][i];
-    }
-    const auto sl = __builtin_amdgcn_permlane32_swap(__float_as_uint(l), __float_as_uint(l), false, false);
-    l = __uint_as_float(sl[0]) + __uint_as_float(sl[1]);
-    Mw[j] = M;
-    if (hf == 0 && j < nb) st[w][qv] = make_float2(M, l);
-  }
-  __syncthreads();
-  // this tile's statistics of every query vector, published device-wide:
-  // (max, sum) of vector v of (key tile t, kv head g) at pair slot
-  // (t hkv + g) kMFV + v of the request's statistics block
-  const int64_t stat_pairs = static_cast<int64_t>(ntile) * hkv * kMFV;
-  const __amdgpu_buffer_rsrc_t sr = handoff_rsrc(
-      a.part_m + static_cast<int64_t>(a.cu_ttiles[r]) * hkv * (2 * kMFV), stat_pairs * 8);
-  if (tid < nqv) {
-    float m = -INFINITY, l = 0.f;
-#pragma unroll
-    for (int ww = 0; ww < kMFT / 64; ++ww) {
-      const float2 x = st[ww][tid];
-      if (x.x > m) {
-        l = l * (m == -INFINITY ? 0.f : exp2f(m - x.x)) + x.y;
-        m = x.x;
-      } else if (x.x > -INFINITY) {
-        l += x.y * exp2f(x.x - m);
-      }
-    }
-    put_dev2(sr, static_cast<uint32_t>(tid) * 8,
-             static_cast<uint32_t>(((kt * hkv + g) * kMFV) * 8), m, l);
-  }
-  stores_done_barrier();
-  int* arr = a.cnt_cols + kMassCntArrive + pair;
-  int* dep = a.cnt_cols + kMassCntDepart + pair;
-  if (tid == 0) {
-    __hip_atomic_fetch_add(arr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    int it = 0;
-    while (__hip_atomic_load(arr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < ntile && it < kMassSpin) {
-      __builtin_amdgcn_s_sleep(2);
-      ++it;
-    }
-  }
-  __syncthreads();
-  // every workgroup of this (request, kv head) has published its statistics
-  if (tid < nqv) {
-    float m = -INFINITY, l = 0.f;
-    // the tiles in order, up to kBatch loads in flight at a time
-    constexpr int kBatch = 48;
-    for (int t0 = 0; t0 < ntile; t0 += kBatch) {
-      float2 x[kBatch];
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u)
-        x[u] = t0 + u < ntile ? get_dev2(sr, static_cast<uint32_t>(tid) * 8,
-                                         static_cast<uint32_t>((((t0 + u) * hkv + g) * kMFV) * 8))
-                              : make_float2(-INFINITY, 0.f);
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const float ms = x[u].x, ls = x[u].y;
-        if (ms > m) {
-          l = l * (m == -INFINITY ? 0.f : exp2f(m - ms)) + ls;
-          m = ms;
-        } else if (ms > -INFINITY) {
-          l += ls * exp2f(ms - m);
-        }
-      }
-    }
-    Ls[tid] = l > 0.f ? m + log2f(l) : INFINITY;
-  } else if (tid < kMFV) {
-    Ls[tid] = INFINITY;                                    // padding: contributes nothing
-  }
-  // leave the barrier: the last workgroup out resets its counters
-  if (tid == 0) {
-    const int old = __hip_atomic_fetch_add(dep, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (old == ntile - 1) {
-      __hip_atomic_store(arr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(dep, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
-  __syncthreads();
-  if (key0 >= N) return;                                   // query keys only: no scores (uniform)
-
-  // column sums of this wave's 32 keys over the query vectors:
-  // sum over vectors of e exp2(M - lse)
-  float cols[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) cols[i] = 0.f;
-#pragma unroll
-  for (int j = 0; j < NB; ++j) {
-    if (j < nb) {
-      const float f = Mw[j] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(Mw[j] - Ls[32 * j + c]);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) cols[i] = fmaf(s[j][i], f, cols[i]);
-    }
-  }
-  // across the 32 lanes of each half: through LDS (the query tile is no
-  // longer read), then one thread per key adds its 32 entries in order
-  float* red = reinterpret_cast<float*>(&Qs[0][0]) + w * (32 * 33);
-#pragma unroll
-  for (int i = 0; i < 16; ++i) red[(8 * (i >> 2) + 4 * hf + (i & 3)) * 33 + c] = cols[i];
-  __syncthreads();
-  const int n_all = a.b.cu_N[a.b.n_req];
-  // per-head column sums: [kv head][sum N] floats
-  const __amdgpu_buffer_rsrc_t pr = handoff_rsrc(a.part, static_cast<int64_t>(hkv) * n_all * 4);
-  const uint32_t key_off = static_cast<uint32_t>(a.b.cu_N[r] + key0 + tid) * 4;
-  if (tid < kMFK) {
-    const int ww = tid >> 5, kl = tid & 31;
-    const float* rr = reinterpret_cast<const float*>(&Qs[0][0]) + ww * (32 * 33) + kl * 33;
-    float sum = 0.f;
-#pragma unroll
-    for (int e = 0; e < 32; ++e) sum += rr[e];
-    if (key0 + tid < N) put_dev1(pr, key_off, static_cast<uint32_t>(g) * n_all * 4, sum);
-  }
-  // the last kv head of this key tile adds the heads in a fixed order
-  const int ctile = a.cu_ftiles[r] + kt;                    // context key tile over all requests
-  if (!arrive_last(a.cnt_cols + ctile, hkv, &s_flag)) return;
-  if (tid < kMFK && key0 + tid < N) {
-    float sum = 0.f;
-    for (int g0 = 0; g0 < hkv; g0 += 8) {
-      float pv8[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-        pv8[u] = g0 + u < hkv ? get_dev1(pr, key_off, static_cast<uint32_t>(g0 + u) * n_all * 4) : 0.f;
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (g0 + u < hkv) sum += pv8[u];
     }
     store_score(a.out, a.b.cu_N[r] + key0 + tid, sum);
   }
@@ -1453,12 +1190,10 @@ __global__ void __launch_bounds__(256) head_sum_kernel(const float* __restrict__
   store_score(out, i, s);
 }
 
-// Arrival counters of the attention-mass workspace, at offset 0 in a region
-// of fixed size: one per 128-key tile of context (the head sums), then the
-// arrive and depart counters of the one-launch path's barrier, one per
-// (request, kv head).
-constexpr size_t kMassCntBytes = 131072;
-constexpr int64_t kMassMaxKeyTiles = 16384;
+// Arrival counters of the attention-mass workspace: one per 128-key tile of
+// context, at workspace offset 0 in a region of fixed size.
+constexpr size_t kMassCntBytes = 65536;
+constexpr int64_t kMassMaxKeyTiles = kMassCntBytes / sizeof(int);
 
 int64_t attn_mass_key_tiles(const BatchArgs& B) {
   int64_t ktiles = 0;
@@ -1473,8 +1208,6 @@ struct MassLayout {
   int split_keys;
   size_t off_pm, off_pl, off_lse, off_part, off_cnt, total;
   int64_t n_cnt;         // arrival counters: one per key tile
-  bool one_launch;       // every request has at most 256 query vectors per kv head
-  int64_t ttiles;        // 128-key tiles over all keys (one-launch path)
 };
 
 MassLayout mass_layout(const kvf_layer_desc& L, const BatchArgs& B, int n_last_q) {
@@ -1502,29 +1235,14 @@ MassLayout mass_layout(const kvf_layer_desc& L, const BatchArgs& B, int n_last_q
   const int64_t plane = m.rows * L.n_q_heads;
   auto align = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
   int64_t ktiles = 0;
-  for (int r = 0; r < B.n_req; ++r) {
-    ktiles += ceil_div(B.n_ctx[r], kMK);
-    m.ttiles += ceil_div(B.cu_T[r + 1] - B.cu_T[r], kMFK);
-  }
+  for (int r = 0; r < B.n_req; ++r) ktiles += ceil_div(B.n_ctx[r], kMK);
   m.n_cnt = ktiles;
-  const int G = L.n_q_heads / L.n_kv_heads;
-  m.one_launch = L.dtype == KVF_BF16 && m.rows > 0 &&
-                 static_cast<int64_t>(B.n_req) * L.n_kv_heads <= kMassMaxPairs;
-  for (int r = 0; r < B.n_req && m.one_launch; ++r) {
-    const int U = B.cu_T[r + 1] - B.cu_T[r] - B.n_ctx[r];
-    const int nq = n_last_q > 0 ? std::min(n_last_q, U) : U;
-    if (static_cast<int64_t>(nq) * G > kMFV) m.one_launch = false;
-  }
   // arrival counters first, at a fixed offset and size: calls of any shape
-  // can share one zero-filled workspace.  The statistics region serves both
-  // paths: per (chunk, row, head) planes for the two-pass path, per (key
-  // tile, kv head, query vector) (max, sum) pairs for the one-launch path.
-  const size_t stats = std::max(sizeof(float) * plane * m.n_splits * 2,
-                                m.one_launch ? sizeof(float) * 2 * kMFV * m.ttiles * L.n_kv_heads : 0);
+  // can share one zero-filled workspace
   m.off_cnt = 0;
   m.off_pm = kMassCntBytes;
   m.off_pl = align(m.off_pm + sizeof(float) * plane * m.n_splits);
-  m.off_lse = align(m.off_pm + stats);
+  m.off_lse = align(m.off_pl + sizeof(float) * plane * m.n_splits);
   m.off_part = align(m.off_lse + sizeof(float) * plane);
   m.total = align(m.off_part + sizeof(float) * static_cast<size_t>(L.n_kv_heads) * B.cu_N[B.n_req]);
   return m;
@@ -1533,25 +1251,6 @@ MassLayout mass_layout(const kvf_layer_desc& L, const BatchArgs& B, int n_last_q
 
 size_t attn_mass_workspace(const kvf_layer_desc& L, const BatchArgs& B, int n_last_q) {
   return mass_layout(L, B, n_last_q).total;
-}
-
-// Workgroups of the one-launch kernel the current device holds at once.
-static int64_t mass_fused_capacity(const void* fn, int d) {
-  static std::mutex mu;
-  static int64_t cap[2][64] = {};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  std::lock_guard<std::mutex> lock(mu);
-  int64_t& c = cap[d == 128 ? 1 : 0][dev];
-  if (c == 0) {
-    int per_cu = 0, cus = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kMFT, 0) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-      return 0;
-    c = static_cast<int64_t>(per_cu) * cus;
-    if (c == 0) c = -1;
-  }
-  return c;
 }
 
 hipError_t launch_attn_mass(const kvf_layer_desc& L, const BatchArgs& B, const void* fk,
@@ -1584,10 +1283,6 @@ hipError_t launch_attn_mass(const kvf_layer_desc& L, const BatchArgs& B, const v
     m.cu_ktiles[r + 1] = m.cu_ktiles[r] + ceil_div(B.n_ctx[r], kMK);
   }
   m.total_ktiles = m.cu_ktiles[B.n_req];
-  for (int r = 0; r < B.n_req; ++r) {
-    m.cu_ttiles[r + 1] = m.cu_ttiles[r] + ceil_div(B.cu_T[r + 1] - B.cu_T[r], kMFK);
-    m.cu_ftiles[r + 1] = m.cu_ftiles[r] + ceil_div(B.n_ctx[r], kMFK);
-  }
   m.q = q_u;
   m.k = fk;
   m.lse2 = lse2;
@@ -1609,21 +1304,6 @@ hipError_t launch_attn_mass(const kvf_layer_desc& L, const BatchArgs& B, const v
                          out);
     }
     return hipGetLastError();
-  }
-
-  // one launch when the grid can be resident at once (a cooperative launch,
-  // which graph capture records as such)
-  if (lay.one_launch && B.cu_N[B.n_req] > 0) {
-    const int64_t blocks = lay.ttiles * m.hkv;
-    const void* fn = L.head_dim == 128 ? reinterpret_cast<const void*>(&mass_fused_bf16_kernel<128>)
-                                       : reinterpret_cast<const void*>(&mass_fused_bf16_kernel<64>);
-    if (blocks <= mass_fused_capacity(fn, L.head_dim)) {
-      void* params[] = {&m};
-      const hipError_t le = hipLaunchCooperativeKernel(fn, dim3(static_cast<unsigned>(blocks)), dim3(kMFT),
-                                                       params, 0, st);
-      if (le != hipErrorCooperativeLaunchTooLarge) return le;
-      (void)hipGetLastError();                    // too large after all: the two-pass path
-    }
   }
 
   // pass 1: softmax statistics of the used query rows
@@ -1734,13 +1414,15 @@ hipError_t launch_attn_mass_noalloc(const kvf_layer_desc& L, const BatchArgs& B,
   void* ws = nullptr;
   hipError_t e = mass_scratch_address(&ws);
   if (e != hipSuccess) return e;
-  // the arrival counters start at zero whatever an earlier call left (a
-  // fill kernel, which graph capture records safely)
-  constexpr int64_t words = kMassCntBytes / sizeof(uint32_t);
-  hipLaunchKernelGGL(zero_words_kernel, dim3(static_cast<unsigned>(words / 256)), dim3(256), 0, st,
-                     reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + lay.off_cnt), words);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  // the arrival counters this call uses start at zero whatever an earlier
+  // call left (a fill kernel, which graph capture records safely)
+  if (lay.n_cnt > 0) {
+    hipLaunchKernelGGL(zero_words_kernel, dim3(static_cast<unsigned>(ceil_div(static_cast<int>(lay.n_cnt), 256))),
+                       dim3(256), 0, st, reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + lay.off_cnt),
+                       lay.n_cnt);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   return launch_attn_mass(L, B, fk, q_u, n_last_q, out, ws, KVF_NOALLOC_SCRATCH_BYTES, st);
 }
 

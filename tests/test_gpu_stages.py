@@ -277,7 +277,7 @@ def test_attention_mass(kvf, case):
                   ws, n_last_q=nlq)
         runs.append(from_gpu(sc))
     assert np.array_equal(runs[0], runs[1]), "attention mass differs between two calls"
-    assert not bool(ws[:131072].any()), "arrival counters not reset"
+    assert not bool(ws[:65536].any()), "arrival counters not reset"
     dk, dq = decode(k_s, dtype), decode(q_s, dtype)
     lo = fusion.Layer(256, hq, hkv, d, 1e4)
     ref, uoff = [], 0
@@ -697,7 +697,7 @@ def test_attention_mass_workspace_shared_across_shapes(kvf):
                       sc, ws, n_last_q=nlq)
             outs.append(raw(sc).copy())
         assert np.array_equal(outs[0], outs[1]), f"shape {order}: shared workspace changes the scores"
-        assert not bool(shared[:131072].any())
+        assert not bool(shared[:65536].any())
 
 
 @pytest.mark.parametrize("wl_name", ["qwen3_8b_mass", "llama3_70b_mass", "qwen3_8b_dev_pool"])
