@@ -22,7 +22,7 @@ Timing, after W warm-up steps:
   2. K steps back to back (warm caches), for comparison;
   3. K flushed steps with every library call bracketed by HIP events: each
      call's average duration and its roofline fraction (algorithmic bytes or
-     flops / duration).
+     flops / duration); `ms_warm` is the same without the flushes.
 The roofline object describes the call that takes longest; its `traffic` is
 the HBM bytes per launch from the committed counter summary of that kernel
 and workload under profiles/, or null when the kernel source has changed
@@ -608,6 +608,7 @@ def measure(wl, ratio, steps, warmup, flush, graph=False):
     times, wall = _timed_steps(step, steps, flush)
     warm = _timed_back_to_back(step, steps)
     per_call = _timed_per_call(g, steps, flush)
+    per_call_warm = _timed_per_call(g, steps, None)
     work = call_work(g)
     n_ctx = int(np.sum(batch.n_ctx))
     med = _pct(times, 50)
@@ -622,7 +623,7 @@ def measure(wl, ratio, steps, warmup, flush, graph=False):
             ach, peak, unit = amount / (ms * 1e-3) / 1e12, peak_mfma, "TFLOP/s"
         calls[name] = {"ms": round(ms, 5), "bound": kind, "achieved": round(ach, 2),
                        "unit": unit, "frac": round(ach / peak, 4),
-                       "algorithmic": float(amount)}
+                       "algorithmic": float(amount), "ms_warm": round(per_call_warm[name], 5)}
     dom = max(per_call, key=per_call.get)
     kname, ksrc = CALL_KERNEL[dom]
     if dom == "score" and g.selector == "anchor":
