@@ -14,7 +14,7 @@ Sources (cited by page title and section / equation):
   [KVB] "KVBoost: Chunk-Level Key-Value Cache Reuse with Deviation-Guided
         Recomputation for Efficient Large Language Model Inference" -
         section 3.1 (Eq. 1-2), 3.2 (Eq. 3), 4.1, 4.5 (Eq. 7), 4.6.1
-        (Algorithm 1), 4.6.2 (Algorithm 2).
+        (Algorithm 1), 4.6.2 (Algorithm 2), 7.3 (memory budget).
 
 Pins: every function here is checked by `tests/test_oracle_*.py` against
 closed forms, invariants, brute force on tiny inputs or special cases
@@ -22,4 +22,4 @@ closed forms, invariants, brute force on tiny inputs or special cases
 package is "parity unpinned"; the quality of the selected set on real text
 (which needs trained weights and datasets) is not claimed anywhere.
 """
-from . import storage, rope, kivi, fusion, selectors, multilayer  # noqa: F401
+from . import storage, rope, kivi, fusion, selectors, multilayer, q8cache  # noqa: F401
