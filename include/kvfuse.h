@@ -14,7 +14,8 @@
  *         3.1 (Eq. 1-2, projections, attention, cache layout), 3.2 (Eq. 3,
  *         RoPE and the rotation correction), 4.1 (attention-sink tokens),
  *         4.5 (Eq. 7, KIVI int8/int4), 4.6.1 (Algorithm 1, seam windows),
- *         4.6.2 (Algorithm 2, key-deviation scoring).
+ *         4.6.2 (Algorithm 2, key-deviation scoring), 7.3 (memory budget:
+ *         an 8-bit cache halves a 16-bit one).
  *
  * One layer, per request:  N context tokens (stitched chunks) then U query
  * tokens, T = N + U.  The path is
@@ -25,7 +26,10 @@
  * same recompute path: kvf_select_static builds a mask of static positions
  * (attention sinks, chunk boundary tokens, seam windows) that kvf_select_topk
  * takes as a forced set, and kvf_select_topk_segmented selects per chunk
- * (e.g. over kvf_score's KVF_SCORE_KEY_NORM scores).
+ * (e.g. over kvf_score's KVF_SCORE_KEY_NORM scores).  With an int8-resident
+ * fused cache (kvf_q8_cache) the calls that touch the cache have _q8 forms:
+ *   kvf_rerotate_q8 -> kvf_score_q8 -> kvf_select_topk -> kvf_recompute_qkv
+ *   -> kvf_scatter_kv_q8 -> kvf_sparse_q_attention_q8
  *
  * Conventions for every call:
  *  - Pointers are DEVICE pointers unless the comment says "host".
@@ -69,7 +73,7 @@
 extern "C" {
 #endif
 
-#define KVF_ABI_VERSION 9
+#define KVF_ABI_VERSION 10
 #define KVF_MAX_REQ 64      /* requests per call (batch metadata is passed by value) */
 
 typedef enum {
@@ -143,6 +147,26 @@ typedef struct {
   int32_t bits;              /* 8 or 4 */
 } kvf_kivi;
 
+/* Int8-resident fused cache ([KVB] 4.5 Eq. 7 with b = 8, kept by the fused
+ * cache itself instead of expanding it to bf16 - [KVB] 7.3: an 8-bit cache
+ * takes half the bytes).  Device arrays.  Every (row, kv head) of K and of V
+ * is d one-byte codes plus one float pair (min, scale); value = min + code *
+ * scale.  A (row, head) group's statistics come from that row's own d values
+ * - one group per token for keys as for values, because fused rows are
+ * written one at a time (by re-positioning and by fusion).  Encoding, fp32
+ * in this order: range = max - min; scale = range / 255; inv = 255 / range;
+ * code = (x - min) * inv rounded half to even, clamped to [0, 255]; a group
+ * with range 0 gets scale 0 and codes 0.  Written by kvf_rerotate_q8 and
+ * kvf_scatter_kv_q8, read (decoded on load) by kvf_score_q8 and
+ * kvf_sparse_q_attention_q8. */
+typedef struct {
+  uint8_t* k_codes;          /* [rows, Hkv, d] */
+  uint8_t* v_codes;          /* [rows, Hkv, d] */
+  float* k_stats;            /* [rows, Hkv, 2]: (min, scale) */
+  float* v_stats;            /* [rows, Hkv, 2] */
+  int64_t rows;
+} kvf_q8_cache;
+
 /* Static recompute rules (host struct); every field >= 0, 0 turns a rule off.
  *   sink:     request positions 0 .. sink-1 ([KVB] 4.1, attention-sink
  *             tokens always kept live);
@@ -212,6 +236,28 @@ kvf_status kvf_rerotate(const kvf_layer_desc* layer, const kvf_chunk* chunks,
                         int64_t fused_rows, int32_t k_only, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * kvf_rerotate_q8 - S1 into an int8-resident fused cache (kvf_q8_cache):
+ * the chunks of kvf_rerotate (k_only = 0), with fused row dst_row + t of
+ * every chunk written as
+ *   K: R(pos0) * K_pool[src_row + t] - the per-chunk key decoded and
+ *      rotated in fp32, then encoded (one group per row and kv head);
+ *   V: from an 8-bit KIVI per-chunk cache, the row's codes and (min, scale)
+ *      copied unchanged (KIVI values are per-token 8-bit groups already);
+ *      from a dense bf16 cache, the value encoded.
+ * Per-chunk cache: dense bf16 (pool_k, pool_v; kivi = NULL) or KIVI with
+ * bits = 8 (pool_k = pool_v = NULL); a 4-bit KIVI cache gives
+ * KVF_ERR_UNSUPPORTED.  layer->dtype must be KVF_BF16.  Fused rows no chunk
+ * covers are not written; chunk descriptors are checked as in kvf_rerotate.
+ */
+kvf_status kvf_rerotate_q8(const kvf_layer_desc* layer, const kvf_chunk* chunks,
+                           int32_t n_chunks, int32_t max_chunk_len,
+                           const void* pool_k, const void* pool_v,
+                           const kvf_kivi* kivi, int64_t pool_rows,
+                           const float* rope_cos, const float* rope_sin,
+                           int32_t rope_n_pos, const kvf_q8_cache* fused,
+                           void* stream);
+
+/* ---------------------------------------------------------------------------
  * kvf_score - S2: one fp32 score per context token; scores [sum_r n_ctx[r]]
  * request-major.  mode: one of the modes below, optionally OR KVF_SCORE_ACCUMULATE
  * (scores[t] += this layer's score; a NaN already there stays NaN).
@@ -251,6 +297,17 @@ kvf_status kvf_score(kvf_score_mode mode, const kvf_layer_desc* layer,
                      size_t ws_bytes, void* stream);
 size_t kvf_score_workspace_size(kvf_score_mode mode, const kvf_layer_desc* layer,
                                 const kvf_batch* batch, int32_t n_last_q);
+
+/* kvf_score_q8 - kvf_score over an int8-resident fused cache: modes
+ * KVF_SCORE_DEVIATION and KVF_SCORE_KEY_NORM (optionally OR
+ * KVF_SCORE_ACCUMULATE), with the same definitions, batch, eligibility and
+ * output; every fused key is decoded in fp32 (min + code * scale, one fused
+ * multiply-add) before use.  k_fresh (deviation) is bf16 [sum T, Hkv, d].
+ * KVF_SCORE_ATTN_MASS gives KVF_ERR_UNSUPPORTED.  No workspace. */
+kvf_status kvf_score_q8(kvf_score_mode mode, const kvf_layer_desc* layer,
+                        const kvf_batch* batch, const kvf_q8_cache* fused,
+                        const void* k_fresh, const uint8_t* eligible, float* scores,
+                        void* stream);
 
 /* ---------------------------------------------------------------------------
  * kvf_score_attn_mass_noalloc - kvf_score(KVF_SCORE_ATTN_MASS) for callers
@@ -393,6 +450,17 @@ kvf_status kvf_scatter_kv(const kvf_layer_desc* layer, const void* k_src,
                           void* fused_k, void* fused_v, int64_t fused_rows,
                           void* stream);
 
+/* kvf_scatter_kv_q8 - S5 into an int8-resident fused cache: the rows of
+ * kvf_scatter_kv (k_src, v_src bf16 [rows, Hkv, d], either may be NULL),
+ * each destination (row, kv head) encoded from its source values.
+ * Destination rows must be unique (duplicates race); entries outside
+ * [0, fused->rows), and sources outside their row range, are skipped. */
+kvf_status kvf_scatter_kv_q8(const kvf_layer_desc* layer, const void* k_src,
+                             const int32_t* k_src_row, int64_t k_src_rows,
+                             const void* v_src, const int32_t* v_src_row,
+                             int64_t v_src_rows, const int32_t* dst_row, int32_t M,
+                             const kvf_q8_cache* fused, void* stream);
+
 /* ---------------------------------------------------------------------------
  * kvf_sparse_q_attention - S6: causal attention of the recomputed rows over
  * the fused cache ([QCF] 2.1.3: a recomputed token reads prefix positions
@@ -410,6 +478,22 @@ kvf_status kvf_sparse_q_attention(const kvf_layer_desc* layer,
                                   float sm_scale, void* out, float* lse,
                                   void* workspace, size_t workspace_bytes,
                                   void* stream);
+
+/* kvf_sparse_q_attention_q8 - kvf_sparse_q_attention over an int8-resident
+ * fused cache (same arguments otherwise, layer->dtype KVF_BF16, q bf16).
+ * Each K/V tile is decoded once per workgroup (fp32 min + code * scale,
+ * rounded to fp16) on its way into on-chip memory, and the products run in
+ * fp16 with fp32 accumulation: queries and probabilities are rounded to fp16
+ * as well.  Every decoded value and query element must lie within the fp16
+ * range (|x| <= 65504); outputs of rows that read one beyond it are
+ * undefined.  The workspace is that of kvf_attention_workspace_size (the same
+ * layer, batch and cu_q) and follows the same rules. */
+kvf_status kvf_sparse_q_attention_q8(const kvf_layer_desc* layer,
+                                     const kvf_batch* batch, const void* q,
+                                     const int32_t* q_pos, const int32_t* cu_q,
+                                     const kvf_q8_cache* fused, float sm_scale,
+                                     void* out, float* lse, void* workspace,
+                                     size_t workspace_bytes, void* stream);
 
 /* Workspace bytes kvf_sparse_q_attention can use for the same layer, batch
  * and cu_q (HOST).  0 when the call would not use one (fp32, or a grid large

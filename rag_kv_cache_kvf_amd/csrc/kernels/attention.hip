@@ -26,6 +26,20 @@
 // probabilities per key in a second MFMA pass and adds the kv heads in a
 // fixed order, so the result is deterministic.
 //
+// Int8-resident fused cache (KVBoost page, section 4.5, Eq. 7 held by the
+// fused cache; section 7.3: half the bytes of a 16-bit cache): the same
+// kernel reads the 8-bit codes and each row's (min, scale), once per
+// workgroup per tile on the way into LDS, and runs the fp16 MFMA
+// (v_mfma_f32_32x32x16_f16) with queries and probabilities in fp16.
+//  * Keys stay exact: the tile holds 1024 + code (an fp16 integer, built by
+//    byte permutes), so the MFMA gives q . (1024 + c) exactly up to fp32
+//    summation, and each key's affine map - scale and min - 1024 scale times
+//    the query's channel sum - is applied to the fp32 scores.  (Rounding the
+//    decoded keys to fp16 instead costs up to 2.2e-2 of an output vector on
+//    peaked rows, the whole error budget.)
+//  * Values are decoded to fp16 (min + code * scale, one rounding), whose
+//    error averages out over the keys a row attends to.
+//
 // fp32 path: one wave per (row, head) with lane-parallel keys; used by the
 // small fp32 workloads only.
 #include <mutex>
@@ -55,8 +69,10 @@ struct AttnArgs {
   int rows_per_tile;             // R
   const void* q;
   const int32_t* q_pos;
-  const void* k;
+  const void* k;                 // bf16 [rows, Hkv, d], or 8-bit codes (int8-resident)
   const void* v;
+  const float* k_stats;          // int8-resident: [rows, Hkv, 2] (min, scale)
+  const float* v_stats;
   void* out;                     // [out rows, Hq, d]
   float* lse;                    // [out rows, Hq] natural log (attention mode)
   float* part_m;                 // [splits, out rows, Hq] log2 domain (statistics mode)
@@ -97,6 +113,13 @@ constexpr int kAWaves = 4 / kQB; // 128 query vectors per workgroup
 constexpr int kAThreads = 64 * kAWaves;
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  const f16x2_t v = {static_cast<_Float16>(lo), static_cast<_Float16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
+}
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 // Word 3 of a gfx9-family buffer descriptor for raw byte addressing
 // (stride 0): 32-bit data format, no swizzle; accesses at or past the
@@ -157,9 +180,16 @@ __device__ __forceinline__ void copies_landed_barrier() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
-template <int D>
+// Q8: K/V are 8-bit codes with per-row statistics (int8-resident cache).
+// Their tiles are not copied by DMA but loaded into registers a tile ahead
+// (thread t: key row t / 4 of the tile, the 8-code pieces (t % 4) + 4 i),
+// dequantised after the barrier that frees their LDS buffer and written as
+// fp16; the piece order makes each 16-lane group of a write cover all 64
+// banks.
+template <int D, bool Q8>
 __global__ void __launch_bounds__(kAThreads) __attribute__((amdgpu_waves_per_eu(2 / kQB, 2 / kQB)))
-attn_bf16_kernel(AttnArgs a) {
+attn_mfma_kernel(AttnArgs a) {
+  using OpT = std::conditional_t<Q8, f16x8_t, bf16x8_t>;   // MFMA operand (8 values)
   constexpr int KS = D / 16;       // MFMA k-steps over the head dimension
   constexpr int DB = D / 32;       // 32-channel output blocks
   constexpr int CPR = D / 8;       // 16-byte chunks per row
@@ -175,6 +205,9 @@ attn_bf16_kernel(AttnArgs a) {
   bf16_t* const v0s = kvs + 2 * TILE;
   bf16_t* const v1s = kvs + 3 * TILE;
   __shared__ int s_pos[2];
+  // Q8: per key of the last four K tiles, (scale, min - 1024 scale) times
+  // the score scale; slot = tile & 3
+  __shared__ __attribute__((aligned(16))) float kab[Q8 ? 4 * 2 * kAT : 4];
 
   const int hkv = a.hkv;
   const int g = blockIdx.x % hkv;
@@ -245,16 +278,22 @@ attn_bf16_kernel(AttnArgs a) {
   const int t1 = (part + 1) * n / np;
 
   const bf16_t* Q = static_cast<const bf16_t*>(a.q);
-  bf16x8_t qf[kQB][KS];
+  OpT qf[kQB][KS];
 #pragma unroll
   for (int qb = 0; qb < kQB; ++qb)
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       if (pos[qb] >= 0) {
-        qf[qb][ks] = *reinterpret_cast<const bf16x8_t*>(Q + (qrow[qb] * a.hq + h[qb]) * D + ks * 16 + hf * 8);
+        const bf16x8_t qv = *reinterpret_cast<const bf16x8_t*>(Q + (qrow[qb] * a.hq + h[qb]) * D + ks * 16 + hf * 8);
+        if constexpr (Q8) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) qf[qb][ks][e] = static_cast<_Float16>(static_cast<float>(qv[e]));
+        } else {
+          qf[qb][ks] = qv;
+        }
       } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) qf[qb][ks][e] = static_cast<__bf16>(0.f);
+        for (int e = 0; e < 8; ++e) qf[qb][ks][e] = 0;
       }
     }
 
@@ -279,7 +318,7 @@ attn_bf16_kernel(AttnArgs a) {
   // rows past it read as zeros (those keys are masked for every row), so no
   // per-row clamp is needed.  A lane's byte offset within a tile is fixed
   // per copy instruction; the tile adds kb0 rows.
-  const int rs2 = static_cast<int>(row_stride) * 2;        // bytes per key row
+  const int rs2 = static_cast<int>(row_stride) * (Q8 ? 1 : 2);   // bytes per key row
   const u32x4_t krs = buffer_rsrc(Kreq, klim > 0 ? klim * rs2 : 0);
   const u32x4_t vrs = buffer_rsrc(Vreq, klim > 0 ? klim * rs2 : 0);
   int dvo[NDMA];
@@ -300,6 +339,74 @@ attn_bf16_kernel(AttnArgs a) {
     for (int j = 0; j < NDMA; ++j) buffer_copy16(rs, dvo[j] + toff, lds_w + buf + j * RPI * D * 2);
   };
 
+  // int8-resident staging: this thread's key row of a tile and its pieces
+  constexpr int NPC = D / 32;                      // 8-code pieces per thread and tensor
+  const int st_row = tid >> 2;
+  const int code_bytes = klim > 0 ? klim * rs2 : 0;
+  const __amdgpu_buffer_rsrc_t kcr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(static_cast<const uint8_t*>(a.k) + krow0 * row_stride + g * D), 0, code_bytes,
+      kBufferRsrcWord3);
+  const __amdgpu_buffer_rsrc_t vcr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(static_cast<const uint8_t*>(a.v) + krow0 * row_stride + g * D), 0, code_bytes,
+      kBufferRsrcWord3);
+  const int64_t st0 = (krow0 * hkv + g) * 2;        // first stats float of this request and head
+  const int st_bytes = klim > 0 ? klim * hkv * 8 : 0;
+  const __amdgpu_buffer_rsrc_t ksr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(Q8 ? a.k_stats + st0 : nullptr), 0, st_bytes, kBufferRsrcWord3);
+  const __amdgpu_buffer_rsrc_t vsr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(Q8 ? a.v_stats + st0 : nullptr), 0, st_bytes, kBufferRsrcWord3);
+  u32x2_t kreg[NPC], vreg[NPC];
+  u32x2_t kst = {0u, 0u}, vst = {0u, 0u};
+  // codes and statistics of key row kb0 + st_row (past klim: zeros)
+  auto stage_load = [&](const __amdgpu_buffer_rsrc_t& cr, const __amdgpu_buffer_rsrc_t& sr, int kb0,
+                        u32x2_t (&c)[NPC], u32x2_t& stv) __attribute__((always_inline)) {
+    const int key = kb0 + st_row;
+    const int base = key * rs2 + 8 * (tid & 3);
+#pragma unroll
+    for (int i = 0; i < NPC; ++i) c[i] = __builtin_amdgcn_raw_buffer_load_b64(cr, base + 32 * i, 0, 0);
+    stv = __builtin_amdgcn_raw_buffer_load_b64(sr, key * hkv * 8, 0, 0);
+  };
+  // keys: 1024 + code as fp16 into the swizzled tile row, and the row's
+  // affine map into the statistics slot of `tile`
+  auto stage_commit_k = [&](const u32x2_t (&c)[NPC], const u32x2_t& stv, bf16_t* dst, int tile)
+      __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NPC; ++i) {
+      u32x4_t w;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        // bytes c0..c3 -> halves 0x64 c0, 0x64 c1 and 0x64 c2, 0x64 c3
+        w[2 * e] = __builtin_amdgcn_perm(0x64646464u, c[i][e], 0x04010400u);
+        w[2 * e + 1] = __builtin_amdgcn_perm(0x64646464u, c[i][e], 0x04030402u);
+      }
+      const int piece = (tid & 3) + 4 * i;
+      *reinterpret_cast<u32x4_t*>(dst + st_row * D + ((piece ^ chunk_xor<D>(st_row)) << 3)) = w;
+    }
+    if ((tid & 3) == 0) {
+      const float mn = __uint_as_float(stv[0]), sc = __uint_as_float(stv[1]);
+      float* slot = kab + (tile & 3) * (2 * kAT);
+      slot[st_row] = sc * a.scale_log2;
+      slot[kAT + st_row] = fmaf(-1024.f, sc, mn) * a.scale_log2;
+    }
+  };
+  // values: min + code * scale as fp16 into the swizzled tile row
+  auto stage_commit = [&](const u32x2_t (&c)[NPC], const u32x2_t& stv, bf16_t* dst)
+      __attribute__((always_inline)) {
+    const float mn = __uint_as_float(stv[0]), sc = __uint_as_float(stv[1]);
+#pragma unroll
+    for (int i = 0; i < NPC; ++i) {
+      u32x4_t w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t word = c[i][e >> 1] >> (16 * (e & 1));
+        w[e] = pack_f16x2(fmaf(static_cast<float>(word & 0xffu), sc, mn),
+                          fmaf(static_cast<float>((word >> 8) & 0xffu), sc, mn));
+      }
+      const int piece = (tid & 3) + 4 * i;
+      *reinterpret_cast<u32x4_t*>(dst + st_row * D + ((piece ^ chunk_xor<D>(st_row)) << 3)) = w;
+    }
+  };
+
   // Softmax state in the log2 domain: scores enter as s * c with
   // c = sm_scale * log2(e).  The running max m_run follows the block maxima:
   // it is raised to a block's exact max whenever that exceeds it by more than
@@ -307,9 +414,11 @@ attn_bf16_kernel(AttnArgs a) {
   // max has probability exactly 1 (the bf16 rounding of P then costs no more
   // than it does against the row's true max).
   constexpr float kRaise = 0.5f;
-  const float c_scale = a.scale_log2;
+  // (Q8 scores leave key_affine already scaled)
+  const float c_scale = Q8 ? 1.f : a.scale_log2;
   const f32x16_t zero16 = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   const bf16x2_t ones2 = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
+  const f16x2_t ones2h = {static_cast<_Float16>(1.f), static_cast<_Float16>(1.f)};
   // LDS element offsets of this lane's operand reads with the swizzle
   // resolved once (it depends on row mod 16 only).
   // K: row c of a 32-key block, channel chunk 2 ks + hf
@@ -335,10 +444,42 @@ attn_bf16_kernel(AttnArgs a) {
     const bf16_t* kr = kt + kb * 32 * D;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(kr + koff[ks]);
+      const OpT kf = *reinterpret_cast<const OpT*>(kr + koff[ks]);
+#pragma unroll
+      for (int qb = 0; qb < kQB; ++qb) {
+        if constexpr (Q8)
+          s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[qb][ks], ks == 0 ? zero16 : s[qb], 0, 0, 0);
+        else
+          s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][ks], ks == 0 ? zero16 : s[qb], 0, 0, 0);
+      }
+    }
+  };
+  // Q8: channel sum of each query vector (both lane halves)
+  float sumq[kQB];
+#pragma unroll
+  for (int qb = 0; qb < kQB; ++qb) {
+    float sq = 0.f;
+    if constexpr (Q8) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sq += static_cast<float>(qf[qb][ks][e]);
+      sq += __shfl_xor(sq, 32, kWave);
+    }
+    sumq[qb] = sq;
+  }
+  // Q8: scores of block kb0 from q . (1024 + c) to log2-domain logits,
+  // s * A_key + B_key * sum(q); before the mask (a constant key row has A = 0)
+  auto key_affine = [&](f32x16_t (&s)[kQB], int kb0) __attribute__((always_inline)) {
+    const float* ab = kab + ((kb0 >> 6) & 3) * (2 * kAT) + (kb0 & 32) + 4 * hf;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x4_t A = *reinterpret_cast<const f32x4_t*>(ab + 8 * j);
+      const f32x4_t B = *reinterpret_cast<const f32x4_t*>(ab + kAT + 8 * j);
 #pragma unroll
       for (int qb = 0; qb < kQB; ++qb)
-        s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][ks], ks == 0 ? zero16 : s[qb], 0, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s[qb][4 * j + e] = fmaf(A[e], s[qb][4 * j + e], B[e] * sumq[qb]);
     }
   };
   // masked keys -> -inf (keys past a row's position; kb0 = block's first key)
@@ -363,8 +504,13 @@ attn_bf16_kernel(AttnArgs a) {
       for (int i = 0; i < 8; ++i) {
         const float p0 = __builtin_amdgcn_exp2f(fmaf(s[qb][2 * i], c_scale, neg_m));
         const float p1 = __builtin_amdgcn_exp2f(fmaf(s[qb][2 * i + 1], c_scale, neg_m));
-        pk[qb][i] = pack_bf16x2(p0, p1);
-        lb[qb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[qb][i]), ones2, lb[qb], false);
+        if constexpr (Q8) {
+          pk[qb][i] = pack_f16x2(p0, p1);
+          lb[qb] = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, pk[qb][i]), ones2h, lb[qb], false);
+        } else {
+          pk[qb][i] = pack_bf16x2(p0, p1);
+          lb[qb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[qb][i]), ones2, lb[qb], false);
+        }
       }
     }
   };
@@ -411,11 +557,11 @@ attn_bf16_kernel(AttnArgs a) {
   auto pv = [&](const bf16_t* vt, int kb, const uint32_t (&pk)[kQB][8]) __attribute__((always_inline)) {
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
-      bf16x8_t pb[kQB];
+      OpT pb[kQB];
 #pragma unroll
       for (int qb = 0; qb < kQB; ++qb) {
         const u32x4_t pw = {pk[qb][4 * st], pk[qb][4 * st + 1], pk[qb][4 * st + 2], pk[qb][4 * st + 3]};
-        pb[qb] = __builtin_bit_cast(bf16x8_t, pw);
+        pb[qb] = __builtin_bit_cast(OpT, pw);
       }
       const bf16_t* vblk = vt + (kb * 32 + 16 * st) * D;
 #pragma unroll
@@ -423,10 +569,14 @@ attn_bf16_kernel(AttnArgs a) {
         const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vblk + voff[0][db]));
         const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vblk + voff[1][db]));
         const s16x4_t vv[2] = {lo, hi};
-        const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, vv);
+        const OpT vf = __builtin_bit_cast(OpT, vv);
 #pragma unroll
-        for (int qb = 0; qb < kQB; ++qb)
-          o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[qb], o[qb][db], 0, 0, 0);
+        for (int qb = 0; qb < kQB; ++qb) {
+          if constexpr (Q8)
+            o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pb[qb], o[qb][db], 0, 0, 0);
+          else
+            o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[qb], o[qb][db], 0, 0, 0);
+        }
       }
     }
   };
@@ -451,6 +601,7 @@ attn_bf16_kernel(AttnArgs a) {
   auto half_step = [&](f32x16_t (&sc)[kQB], int kb0, bool masked, const bf16_t* kt, int kbs,
                        f32x16_t (&sn)[kQB], const bf16_t* vt, int kbp, const uint32_t (&pkp)[kQB][8],
                        uint32_t (&pkc)[kQB][8]) __attribute__((always_inline)) {
+    if constexpr (Q8) key_affine(sc, kb0);
     if (masked) apply_mask(sc, kb0);
     scores(kt, kbs, sn);
     catch_up();
@@ -476,29 +627,66 @@ attn_bf16_kernel(AttnArgs a) {
     // S(2t+1) from K_t, softmax(2t), P(2t-1) V_{t-1}
     half_step(s_a, t * kAT, masked, kc, 1, s_b, vp, 1, pk_b, pk_a);
     // B: K_{t+1} and V_t landed everywhere; K_t and V_{t-1} free
-    copies_landed_barrier<0>();
-    if (t + 2 < t1) dma_tile(krs, kc, (t + 2) * kAT);
-    if (t + 1 < t1) dma_tile(vrs, vp, (t + 1) * kAT);
+    if constexpr (Q8) {
+      // this wave's tile writes done (its register loads are awaited by the
+      // compiler where the commits below use them)
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      if (t + 2 < t1) stage_commit_k(kreg, kst, kc, t + 2);
+      if (t + 1 < t1) stage_commit(vreg, vst, vp);
+      if (t + 3 < t1) stage_load(kcr, ksr, (t + 3) * kAT, kreg, kst);
+      if (t + 2 < t1) stage_load(vcr, vsr, (t + 2) * kAT, vreg, vst);
+    } else {
+      copies_landed_barrier<0>();
+      if (t + 2 < t1) dma_tile(krs, kc, (t + 2) * kAT);
+      if (t + 1 < t1) dma_tile(vrs, vp, (t + 1) * kAT);
+    }
     // S(2t+2) from K_{t+1} (unused after the last tile), softmax(2t+1), P(2t) V_t
     half_step(s_b, t * kAT + 32, masked, kn, 0, s_a, vc, 0, pk_a, pk_b);
   };
 
   if (t1 > t0) {
-    dma_tile(krs, k0s, t0 * kAT);
-    dma_tile(vrs, v0s, t0 * kAT);
-    if (t0 + 1 < t1) dma_tile(krs, k1s, (t0 + 1) * kAT);
+    if constexpr (Q8) {
+      stage_load(kcr, ksr, t0 * kAT, kreg, kst);
+      stage_load(vcr, vsr, t0 * kAT, vreg, vst);
+      stage_commit_k(kreg, kst, k0s, t0);
+      stage_commit(vreg, vst, v0s);
+      if (t0 + 1 < t1) {
+        stage_load(kcr, ksr, (t0 + 1) * kAT, kreg, kst);
+        stage_commit_k(kreg, kst, k1s, t0 + 1);
+      }
+      // the first tile step commits K_{t0+2} and V_{t0+1}
+      if (t0 + 2 < t1) stage_load(kcr, ksr, (t0 + 2) * kAT, kreg, kst);
+      if (t0 + 1 < t1) stage_load(vcr, vsr, (t0 + 1) * kAT, vreg, vst);
+    } else {
+      dma_tile(krs, k0s, t0 * kAT);
+      dma_tile(vrs, v0s, t0 * kAT);
+      if (t0 + 1 < t1) dma_tile(krs, k1s, (t0 + 1) * kAT);
+    }
     // the first half step multiplies zero probabilities with "V_{t0-1}"
     for (int i = tid; i < TILE / 8; i += kAThreads)
       *reinterpret_cast<u32x4_t*>(v1s + 8 * i) = u32x4_t{0u, 0u, 0u, 0u};
-    copies_landed_barrier<0>();
+    if constexpr (Q8)
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else
+      copies_landed_barrier<0>();
     scores(k0s, 0, s_a);
-    if (t0 >= n_plain) apply_mask(s_a, t0 * kAT);
-    init_max(s_a);                                  // the first block sets the max exactly
+    if constexpr (Q8) {
+      // the first half step maps s_a itself; the max is taken from a copy
+      f32x16_t s0[kQB];
+#pragma unroll
+      for (int qb = 0; qb < kQB; ++qb) s0[qb] = s_a[qb];
+      key_affine(s0, t0 * kAT);
+      if (t0 >= n_plain) apply_mask(s0, t0 * kAT);
+      init_max(s0);                                 // the first block sets the max exactly
+    } else {
+      if (t0 >= n_plain) apply_mask(s_a, t0 * kAT);
+      init_max(s_a);                                // the first block sets the max exactly
+    }
   }
   // Every global load the compiler tracks (Q) has completed here on all
   // paths; saying so keeps it from waiting for them, and so for the tile
   // copies behind them, inside the loop (vmcnt(0), expcnt and lgkmcnt free).
-  __builtin_amdgcn_s_waitcnt(0x0F70);
+  if constexpr (!Q8) __builtin_amdgcn_s_waitcnt(0x0F70);
   // two tiles per trip so every buffer is a distinct static array
   int tl = t0;                                      // last tile processed
   for (int t = t0; t < t1; t += 2) {
@@ -597,9 +785,9 @@ attn_bf16_kernel(AttnArgs a) {
   }
 }
 
-template <int D>
-static hipError_t launch_attn_bf16(const AttnArgs& a, dim3 grid, hipStream_t st) {
-  hipLaunchKernelGGL((attn_bf16_kernel<D>), grid, dim3(kAThreads), 0, st, a);
+template <int D, bool Q8>
+static hipError_t launch_attn_mfma(const AttnArgs& a, dim3 grid, hipStream_t st) {
+  hipLaunchKernelGGL((attn_mfma_kernel<D, Q8>), grid, dim3(kAThreads), 0, st, a);
   return hipGetLastError();
 }
 
@@ -734,10 +922,12 @@ size_t attention_workspace(const kvf_layer_desc& L, const BatchArgs& B, const in
   return attn_split_layout(L, B, cu_q).bytes;
 }
 
-hipError_t launch_attention(const kvf_layer_desc& L, const BatchArgs& B, const void* q,
-                            const int32_t* q_pos, const int32_t* cu_q, const void* fk,
-                            const void* fv, float sm_scale, void* out, float* lse, void* ws,
-                            size_t ws_bytes, hipStream_t st) {
+// kst/vst non-null: fk/fv are the 8-bit codes of an int8-resident cache
+static hipError_t attention_impl(const kvf_layer_desc& L, const BatchArgs& B, const void* q,
+                                 const int32_t* q_pos, const int32_t* cu_q, const void* fk,
+                                 const void* fv, const float* kst, const float* vst, float sm_scale,
+                                 void* out, float* lse, void* ws, size_t ws_bytes, hipStream_t st) {
+  const bool q8 = kst != nullptr;
   AttnArgs a{};
   a.b = B;
   for (int r = 0; r < B.n_req; ++r) {
@@ -750,6 +940,8 @@ hipError_t launch_attention(const kvf_layer_desc& L, const BatchArgs& B, const v
   a.q_pos = q_pos;
   a.k = fk;
   a.v = fv;
+  a.k_stats = kst;
+  a.v_stats = vst;
   a.out = out;
   a.lse = lse;
   a.hq = L.n_q_heads;
@@ -774,16 +966,38 @@ hipError_t launch_attention(const kvf_layer_desc& L, const BatchArgs& B, const v
     // without splitting, a grid that one dispatch round holds runs its second
     // round smallest-first, pairing long and short tiles on a CU
     a.fold_from = a.parts == 1 && blocks <= 2 * kCUs ? std::max(1, kCUs / a.hkv) : a.total_tiles;
-    const hipError_t e = L.head_dim == 128 ? launch_attn_bf16<128>(a, dim3(blocks), st)
-                                           : launch_attn_bf16<64>(a, dim3(blocks), st);
+    hipError_t e;
+    if (q8)
+      e = L.head_dim == 128 ? launch_attn_mfma<128, true>(a, dim3(blocks), st)
+                            : launch_attn_mfma<64, true>(a, dim3(blocks), st);
+    else
+      e = L.head_dim == 128 ? launch_attn_mfma<128, false>(a, dim3(blocks), st)
+                            : launch_attn_mfma<64, false>(a, dim3(blocks), st);
     if (e != hipSuccess) return e;
   } else {
+    if (q8) return hipErrorInvalidValue;
     const int total_rows = cu_q[B.n_req];
     const int64_t waves = static_cast<int64_t>(total_rows) * a.hq;
     hipLaunchKernelGGL((attn_f32_kernel<false>), dim3(ceil_div(static_cast<int>(waves), 4)),
                        dim3(256), 0, st, a, L.head_dim, total_rows);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_attention(const kvf_layer_desc& L, const BatchArgs& B, const void* q,
+                            const int32_t* q_pos, const int32_t* cu_q, const void* fk,
+                            const void* fv, float sm_scale, void* out, float* lse, void* ws,
+                            size_t ws_bytes, hipStream_t st) {
+  return attention_impl(L, B, q, q_pos, cu_q, fk, fv, nullptr, nullptr, sm_scale, out, lse, ws,
+                        ws_bytes, st);
+}
+
+hipError_t launch_attention_q8(const kvf_layer_desc& L, const BatchArgs& B, const void* q,
+                               const int32_t* q_pos, const int32_t* cu_q, const kvf_q8_cache& c,
+                               float sm_scale, void* out, float* lse, void* ws, size_t ws_bytes,
+                               hipStream_t st) {
+  return attention_impl(L, B, q, q_pos, cu_q, c.k_codes, c.v_codes, c.k_stats, c.v_stats,
+                        sm_scale, out, lse, ws, ws_bytes, st);
 }
 
 // ---------------------------------------------------------------------------

@@ -1,5 +1,6 @@
 // RoPE tables, S1 re-position + stitch of per-chunk caches (dense, and KIVI
-// int8 / int4 dequant-on-load), and the offline KIVI encoder.
+// int8 / int4 dequant-on-load) into a bf16 or an int8-resident fused cache,
+// and the offline KIVI encoder.
 //
 // QCFuse page, section 2.1.2 (Eq. 3-4): chunk caches are built in isolation
 // with keys at chunk-local positions from zero; serving remaps keys to request
@@ -222,23 +223,152 @@ hipError_t launch_rerotate(const kvf_layer_desc& L, const kvf_chunk* chunks, int
 }
 
 // ---------------------------------------------------------------------------
+// S1 into an int8-resident fused cache
+// ---------------------------------------------------------------------------
+// One wave per fused row of a chunk tile; a group of d/2 lanes takes one kv
+// head, lane j its rotation pair (j, j + d/2), so the row's 8-bit group is
+// encoded after one min/max reduction over the group and no value leaves
+// registers.  Code bytes j and j + d/2 of consecutive lanes are contiguous,
+// so every byte load and store of the wave covers whole 64- or 32-byte runs.
+constexpr int kQ8RotRows = 4;     // rows per workgroup (one per wave)
+
+struct RotQ8Args {
+  const kvf_chunk* chunks;
+  const bf16_t* pool_k;           // dense per-chunk cache
+  const bf16_t* pool_v;
+  const uint8_t* k_codes;         // 8-bit KIVI per-chunk cache
+  const uint8_t* v_codes;
+  const float* k_min;
+  const float* k_scale;
+  const float* v_min;
+  const float* v_scale;
+  int n_pool_chunks;
+  int64_t pool_rows;
+  const float* rope_cos;
+  const float* rope_sin;
+  int rope_n;
+  kvf_q8_cache out;
+  int hkv;
+  int d;
+};
+
+// encode the pair (lo, hi) of every lane of a group of `half` lanes;
+// returns the codes, the group's (min, scale) in mn/sc
+__device__ __forceinline__ void encode_pair(float lo, float hi, int half, bool valid,
+                                            uint32_t& c_lo, uint32_t& c_hi, float& mn, float& sc) {
+  mn = valid ? fminf(lo, hi) : INFINITY;
+  float mx = valid ? fmaxf(lo, hi) : -INFINITY;
+  group_minmax(mn, mx, half);
+  float inv;
+  kivi_stats<8>(mn, mx, sc, inv);
+  c_lo = kivi_code<8>(lo, mn, inv);
+  c_hi = kivi_code<8>(hi, mn, inv);
+}
+
+// KB: 0 for a dense bf16 per-chunk cache, 8 for an 8-bit KIVI one
+template <int KB>
+__global__ void __launch_bounds__(256) rerotate_q8_kernel(RotQ8Args a) {
+  const kvf_chunk ch = a.chunks[blockIdx.x];
+  const int t = blockIdx.y * kQ8RotRows + static_cast<int>(threadIdx.x >> 6);
+  if (ch.len <= 0 || t >= ch.len) return;
+  if (ch.src_row < 0 || static_cast<int64_t>(ch.src_row) + ch.len > a.pool_rows) return;
+  if (ch.dst_row < 0 || static_cast<int64_t>(ch.dst_row) + ch.len > a.out.rows) return;
+  if (ch.pos0 < 0 || ch.pos0 >= a.rope_n) return;
+  if (KB && (ch.pool_chunk < 0 || ch.pool_chunk >= a.n_pool_chunks)) return;
+
+  const int d = a.d, half = d >> 1, hkv = a.hkv;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int j = lane & (half - 1);
+  const int hpp = kWave / half;                    // heads per pass
+  const int64_t srow = static_cast<int64_t>(ch.src_row) + t;
+  const int64_t drow = static_cast<int64_t>(ch.dst_row) + t;
+  const float c = a.rope_cos[static_cast<int64_t>(ch.pos0) * half + j];
+  const float sn = a.rope_sin[static_cast<int64_t>(ch.pos0) * half + j];
+  for (int h0 = 0; h0 < hkv; h0 += hpp) {
+    const int h = h0 + lane / half;
+    const bool valid = h < hkv;
+    const int64_t src = (srow * hkv + h) * d + j;  // element offsets of channel j
+    const int64_t dst = (drow * hkv + h) * d + j;
+    // keys: decode, rotate by R(pos0), encode
+    float lo = 0.f, hi = 0.f;
+    if (valid) {
+      if constexpr (KB == 8) {
+        const int64_t st = (static_cast<int64_t>(ch.pool_chunk) * hkv + h) * d + j;
+        lo = fmaf(static_cast<float>(a.k_codes[src]), a.k_scale[st], a.k_min[st]);
+        hi = fmaf(static_cast<float>(a.k_codes[src + half]), a.k_scale[st + half], a.k_min[st + half]);
+      } else {
+        lo = bf16_to_f32(a.pool_k[src]);
+        hi = bf16_to_f32(a.pool_k[src + half]);
+      }
+    }
+    const float rlo = lo * c - hi * sn;
+    const float rhi = hi * c + lo * sn;
+    uint32_t clo, chi;
+    float mn, sc;
+    encode_pair(rlo, rhi, half, valid, clo, chi, mn, sc);
+    if (valid) {
+      a.out.k_codes[dst] = static_cast<uint8_t>(clo);
+      a.out.k_codes[dst + half] = static_cast<uint8_t>(chi);
+      if (j == 0) *reinterpret_cast<float2*>(a.out.k_stats + (drow * hkv + h) * 2) = make_float2(mn, sc);
+    }
+    // values: 8-bit KIVI rows are copied, dense ones encoded
+    if constexpr (KB == 8) {
+      if (valid) {
+        a.out.v_codes[dst] = a.v_codes[src];
+        a.out.v_codes[dst + half] = a.v_codes[src + half];
+        if (j == 0)
+          *reinterpret_cast<float2*>(a.out.v_stats + (drow * hkv + h) * 2) =
+              make_float2(a.v_min[srow * hkv + h], a.v_scale[srow * hkv + h]);
+      }
+    } else {
+      const float vlo = valid ? bf16_to_f32(a.pool_v[src]) : 0.f;
+      const float vhi = valid ? bf16_to_f32(a.pool_v[src + half]) : 0.f;
+      encode_pair(vlo, vhi, half, valid, clo, chi, mn, sc);
+      if (valid) {
+        a.out.v_codes[dst] = static_cast<uint8_t>(clo);
+        a.out.v_codes[dst + half] = static_cast<uint8_t>(chi);
+        if (j == 0) *reinterpret_cast<float2*>(a.out.v_stats + (drow * hkv + h) * 2) = make_float2(mn, sc);
+      }
+    }
+  }
+}
+
+hipError_t launch_rerotate_q8(const kvf_layer_desc& L, const kvf_chunk* chunks, int n_chunks,
+                              int max_len, const void* pk, const void* pv, const kvf_kivi* q,
+                              int64_t pool_rows, const float* rc, const float* rs, int rope_n,
+                              const kvf_q8_cache& fused, hipStream_t st) {
+  RotQ8Args a{};
+  a.chunks = chunks;
+  a.pool_k = static_cast<const bf16_t*>(pk);
+  a.pool_v = static_cast<const bf16_t*>(pv);
+  if (q) {
+    a.k_codes = q->k_codes;
+    a.v_codes = q->v_codes;
+    a.k_min = q->k_min;
+    a.k_scale = q->k_scale;
+    a.v_min = q->v_min;
+    a.v_scale = q->v_scale;
+    a.n_pool_chunks = q->n_pool_chunks;
+  }
+  a.pool_rows = pool_rows;
+  a.rope_cos = rc;
+  a.rope_sin = rs;
+  a.rope_n = rope_n;
+  a.out = fused;
+  a.hkv = L.n_kv_heads;
+  a.d = L.head_dim;
+  const dim3 grid(n_chunks, ceil_div(max_len, kQ8RotRows));
+  if (grid.y > 65535) return hipErrorInvalidValue;
+  if (q)
+    hipLaunchKernelGGL((rerotate_q8_kernel<8>), grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((rerotate_q8_kernel<0>), grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // offline KIVI encoder (not on the fused-layer path)
 // ---------------------------------------------------------------------------
-template <int BITS>
-__device__ __forceinline__ uint32_t kivi_code(float x, float mn, float inv) {
-  constexpr float kTop = static_cast<float>((1 << BITS) - 1);
-  const float t = (x - mn) * inv;
-  return static_cast<uint32_t>(fminf(fmaxf(rintf(t), 0.f), kTop));
-}
-
-template <int BITS>
-__device__ __forceinline__ void kivi_stats(float mn, float mx, float& sc, float& inv) {
-  constexpr float kTop = static_cast<float>((1 << BITS) - 1);
-  const float rng = mx - mn;
-  sc = rng > 0.f ? rng / kTop : 0.f;
-  inv = rng > 0.f ? kTop / rng : 0.f;
-}
-
 // keys: one thread per (pool chunk, head, code byte) - one channel for
 // b = 8, the channel pair (2i, 2i+1) for b = 4; two passes over the chunk
 template <int BITS>

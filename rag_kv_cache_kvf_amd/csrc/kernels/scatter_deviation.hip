@@ -1,5 +1,5 @@
-// S5 in-place K/V scatter into the fused cache, S2 key-deviation score and
-// the key-norm ranking score.
+// S5 in-place K/V scatter into the fused cache (bf16 or int8-resident), S2
+// key-deviation score and the key-norm ranking score (reading either cache).
 //
 // Scatter: QCFuse page, section 2.1.3, Eq. 7 - the fused cache takes the
 // recomputed entry at every selected position and keeps the reused one
@@ -87,11 +87,113 @@ hipError_t launch_scatter(const kvf_layer_desc& L, const void* ks, const int32_t
   return hipGetLastError();
 }
 
+// S5 into an int8-resident fused cache: one wave per recomputed row; a group
+// of d/2 lanes encodes one kv head's row from channels (j, j + d/2) of lane j
+// (the layout of the int8-resident re-positioning kernel).
+struct ScatterQ8Args {
+  const bf16_t* k_src;
+  const int32_t* k_src_row;
+  int64_t k_src_rows;
+  const bf16_t* v_src;
+  const int32_t* v_src_row;
+  int64_t v_src_rows;
+  const int32_t* dst_row;
+  int M;
+  kvf_q8_cache out;
+  int hkv;
+  int d;
+};
+
+// one row of one tensor: src row s -> codes/stats at dst (lanes of invalid
+// heads take part in the reductions only)
+__device__ __forceinline__ void encode_row_q8(const bf16_t* src, int64_t s, int64_t dst, int hkv,
+                                              int d, uint8_t* codes, float* stats) {
+  const int half = d >> 1;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int j = lane & (half - 1);
+  for (int h0 = 0; h0 < hkv; h0 += kWave / half) {
+    const int h = h0 + lane / half;
+    const bool valid = h < hkv;
+    const int64_t so = (s * hkv + h) * d + j;
+    const float lo = valid ? bf16_to_f32(src[so]) : 0.f;
+    const float hi = valid ? bf16_to_f32(src[so + half]) : 0.f;
+    float mn = valid ? fminf(lo, hi) : INFINITY;
+    float mx = valid ? fmaxf(lo, hi) : -INFINITY;
+    group_minmax(mn, mx, half);
+    float sc, inv;
+    kivi_stats<8>(mn, mx, sc, inv);
+    if (valid) {
+      const int64_t dof = (dst * hkv + h) * d + j;
+      codes[dof] = static_cast<uint8_t>(kivi_code<8>(lo, mn, inv));
+      codes[dof + half] = static_cast<uint8_t>(kivi_code<8>(hi, mn, inv));
+      if (j == 0) *reinterpret_cast<float2*>(stats + (dst * hkv + h) * 2) = make_float2(mn, sc);
+    }
+  }
+}
+
+__global__ void __launch_bounds__(256) scatter_q8_kernel(ScatterQ8Args a) {
+  const int m = static_cast<int>((static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) / kWave);
+  if (m >= a.M) return;
+  const int64_t dst = a.dst_row[m];
+  if (dst < 0 || dst >= a.out.rows) return;
+  if (a.k_src) {
+    const int64_t s = a.k_src_row ? a.k_src_row[m] : m;
+    if (s >= 0 && s < a.k_src_rows) encode_row_q8(a.k_src, s, dst, a.hkv, a.d, a.out.k_codes, a.out.k_stats);
+  }
+  if (a.v_src) {
+    const int64_t s = a.v_src_row ? a.v_src_row[m] : m;
+    if (s >= 0 && s < a.v_src_rows) encode_row_q8(a.v_src, s, dst, a.hkv, a.d, a.out.v_codes, a.out.v_stats);
+  }
+}
+
+hipError_t launch_scatter_q8(const kvf_layer_desc& L, const void* ks, const int32_t* ksr,
+                             int64_t ks_rows, const void* vs, const int32_t* vsr, int64_t vs_rows,
+                             const int32_t* dst, int M, const kvf_q8_cache& fused, hipStream_t st) {
+  ScatterQ8Args a{};
+  a.k_src = static_cast<const bf16_t*>(ks);
+  a.k_src_row = ksr;
+  a.k_src_rows = ks_rows;
+  a.v_src = static_cast<const bf16_t*>(vs);
+  a.v_src_row = vsr;
+  a.v_src_rows = vs_rows;
+  a.dst_row = dst;
+  a.M = M;
+  a.out = fused;
+  a.hkv = L.n_kv_heads;
+  a.d = L.head_dim;
+  hipLaunchKernelGGL(scatter_q8_kernel, dim3(ceil_div(M, 256 / kWave)), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+// Eight consecutive key elements e0..e0+7 (one head) of fused row `row`,
+// in fp32: bf16/fp32 caches as stored, int8-resident ones decoded.
+template <typename T>
+struct KeyRow {
+  const T* k;
+  __device__ __forceinline__ void load8(int64_t row, int row_elems, int e0, float (&x)[8]) const {
+    Elem<T>::load8(k + row * row_elems + e0, x);
+  }
+};
+template <>
+struct KeyRow<uint8_t> {
+  const uint8_t* k;
+  const float* st;
+  int d;
+  __device__ __forceinline__ void load8(int64_t row, int row_elems, int e0, float (&x)[8]) const {
+    const u32x2_t c = *reinterpret_cast<const u32x2_t*>(k + row * row_elems + e0);
+    const int64_t g = row * (row_elems / d) + e0 / d;
+    const float2 ms = *reinterpret_cast<const float2*>(st + 2 * g);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      x[i] = fmaf(static_cast<float>((c[i >> 2] >> (8 * (i & 3))) & 0xffu), ms.y, ms.x);
+  }
+};
+
 // ---------------------------------------------------------------------------
 // S2: key deviation
 // ---------------------------------------------------------------------------
-template <typename T>
-__global__ void __launch_bounds__(256) deviation_kernel(BatchArgs B, const T* __restrict__ fk,
+template <typename T, typename KR>
+__global__ void __launch_bounds__(256) deviation_kernel(BatchArgs B, KR fk,
                                                         const T* __restrict__ kf, int hkv, int d,
                                                         ScoreOut out) {
   const int wave = (blockIdx.x * blockDim.x + threadIdx.x) / kWave;
@@ -106,12 +208,11 @@ __global__ void __launch_bounds__(256) deviation_kernel(BatchArgs B, const T* __
   const int64_t row = B.cu_T[r] + (wave - B.cu_N[r]);
   const int row_elems = hkv * d;
   const int lanes_per_head = d >> 3;           // 8 elements per lane
-  const T* a = fk + row * row_elems;
   const T* b = kf + row * row_elems;
   float cos_acc = 0.f;
   for (int e0 = lane * 8; e0 < row_elems; e0 += kWave * 8) {
     float x[8], y[8];
-    Elem<T>::load8(a + e0, x);
+    fk.load8(row, row_elems, e0, x);
     Elem<T>::load8(b + e0, y);
     float dot = 0.f, nx = 0.f, ny = 0.f;
 #pragma unroll
@@ -136,22 +237,32 @@ hipError_t launch_deviation(const kvf_layer_desc& L, const BatchArgs& B, const v
   const int total = B.cu_N[B.n_req];
   const int blocks = ceil_div(total, 256 / kWave);
   if (L.dtype == KVF_BF16)
-    hipLaunchKernelGGL(deviation_kernel<bf16_t>, dim3(blocks), dim3(256), 0, st, B,
-                       static_cast<const bf16_t*>(fk), static_cast<const bf16_t*>(kf),
+    hipLaunchKernelGGL((deviation_kernel<bf16_t, KeyRow<bf16_t>>), dim3(blocks), dim3(256), 0, st, B,
+                       KeyRow<bf16_t>{static_cast<const bf16_t*>(fk)}, static_cast<const bf16_t*>(kf),
                        L.n_kv_heads, L.head_dim, out);
   else
-    hipLaunchKernelGGL(deviation_kernel<float>, dim3(blocks), dim3(256), 0, st, B,
-                       static_cast<const float*>(fk), static_cast<const float*>(kf),
+    hipLaunchKernelGGL((deviation_kernel<float, KeyRow<float>>), dim3(blocks), dim3(256), 0, st, B,
+                       KeyRow<float>{static_cast<const float*>(fk)}, static_cast<const float*>(kf),
                        L.n_kv_heads, L.head_dim, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_deviation_q8(const kvf_layer_desc& L, const BatchArgs& B, const kvf_q8_cache& c,
+                               const void* kf, const ScoreOut& out, hipStream_t st) {
+  const int total = B.cu_N[B.n_req];
+  const int blocks = ceil_div(total, 256 / kWave);
+  hipLaunchKernelGGL((deviation_kernel<bf16_t, KeyRow<uint8_t>>), dim3(blocks), dim3(256), 0, st, B,
+                     KeyRow<uint8_t>{c.k_codes, c.k_stats, L.head_dim}, static_cast<const bf16_t*>(kf),
+                     L.n_kv_heads, L.head_dim, out);
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
 // key norm
 // ---------------------------------------------------------------------------
-template <typename T>
-__global__ void __launch_bounds__(256) key_norm_kernel(BatchArgs B, const T* __restrict__ fk,
-                                                       int row_elems, ScoreOut out) {
+template <typename KR>
+__global__ void __launch_bounds__(256) key_norm_kernel(BatchArgs B, KR fk, int row_elems,
+                                                       ScoreOut out) {
   const int wave = (blockIdx.x * blockDim.x + threadIdx.x) / kWave;
   const int lane = threadIdx.x & (kWave - 1);
   const int total = B.cu_N[B.n_req];
@@ -162,11 +273,10 @@ __global__ void __launch_bounds__(256) key_norm_kernel(BatchArgs B, const T* __r
   }
   const int r = find_segment(B.cu_N, B.n_req, wave);
   const int64_t row = B.cu_T[r] + (wave - B.cu_N[r]);
-  const T* a = fk + row * row_elems;
   float ss = 0.f;
   for (int e0 = lane * 8; e0 < row_elems; e0 += kWave * 8) {
     float x[8];
-    Elem<T>::load8(a + e0, x);
+    fk.load8(row, row_elems, e0, x);
 #pragma unroll
     for (int i = 0; i < 8; ++i) ss = fmaf(x[i], x[i], ss);
   }
@@ -180,11 +290,21 @@ hipError_t launch_key_norm(const kvf_layer_desc& L, const BatchArgs& B, const vo
   const int blocks = ceil_div(total, 256 / kWave);
   const int row_elems = L.n_kv_heads * L.head_dim;
   if (L.dtype == KVF_BF16)
-    hipLaunchKernelGGL(key_norm_kernel<bf16_t>, dim3(blocks), dim3(256), 0, st, B,
-                       static_cast<const bf16_t*>(fk), row_elems, out);
+    hipLaunchKernelGGL(key_norm_kernel<KeyRow<bf16_t>>, dim3(blocks), dim3(256), 0, st, B,
+                       KeyRow<bf16_t>{static_cast<const bf16_t*>(fk)}, row_elems, out);
   else
-    hipLaunchKernelGGL(key_norm_kernel<float>, dim3(blocks), dim3(256), 0, st, B,
-                       static_cast<const float*>(fk), row_elems, out);
+    hipLaunchKernelGGL(key_norm_kernel<KeyRow<float>>, dim3(blocks), dim3(256), 0, st, B,
+                       KeyRow<float>{static_cast<const float*>(fk)}, row_elems, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_key_norm_q8(const kvf_layer_desc& L, const BatchArgs& B, const kvf_q8_cache& c,
+                              const ScoreOut& out, hipStream_t st) {
+  const int total = B.cu_N[B.n_req];
+  const int blocks = ceil_div(total, 256 / kWave);
+  const int row_elems = L.n_kv_heads * L.head_dim;
+  hipLaunchKernelGGL(key_norm_kernel<KeyRow<uint8_t>>, dim3(blocks), dim3(256), 0, st, B,
+                     KeyRow<uint8_t>{c.k_codes, c.k_stats, L.head_dim}, row_elems, out);
   return hipGetLastError();
 }
 

@@ -104,6 +104,16 @@ kvf_status check_batch(const kvf_batch* b, kvf::BatchArgs* out) {
 
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
+// an int8-resident fused cache of at least `min_rows` rows
+kvf_status check_q8(const kvf_q8_cache* c, int64_t min_rows) {
+  KVF_CHECK(c != nullptr, KVF_ERR_INVALID_ARG, "kvf_q8_cache is NULL");
+  KVF_CHECK(c->k_codes && c->v_codes && c->k_stats && c->v_stats, KVF_ERR_INVALID_ARG,
+            "incomplete kvf_q8_cache");
+  KVF_CHECK(c->rows >= min_rows, KVF_ERR_INVALID_ARG, "kvf_q8_cache holds %lld rows, need %lld",
+            static_cast<long long>(c->rows), static_cast<long long>(min_rows));
+  return KVF_OK;
+}
+
 }  // namespace
 
 #define KVF_GUARD_BEGIN try {
@@ -197,6 +207,40 @@ kvf_status kvf_rerotate(const kvf_layer_desc* layer, const kvf_chunk* chunks, in
   KVF_GUARD_END
 }
 
+kvf_status kvf_rerotate_q8(const kvf_layer_desc* layer, const kvf_chunk* chunks, int32_t n_chunks,
+                           int32_t max_chunk_len, const void* pool_k, const void* pool_v,
+                           const kvf_kivi* kivi, int64_t pool_rows, const float* rope_cos,
+                           const float* rope_sin, int32_t rope_n_pos, const kvf_q8_cache* fused,
+                           void* stream) {
+  KVF_GUARD_BEGIN
+  kvf_status st = check_layer(layer);
+  if (st != KVF_OK) return st;
+  KVF_CHECK(layer->dtype == KVF_BF16, KVF_ERR_UNSUPPORTED, "int8-resident caches need a bf16 layer");
+  KVF_CHECK(n_chunks >= 0 && max_chunk_len >= 0 && pool_rows >= 0 && rope_n_pos >= 0,
+            KVF_ERR_INVALID_ARG, "negative size");
+  st = check_q8(fused, 0);
+  if (st != KVF_OK) return st;
+  if (n_chunks == 0 || max_chunk_len == 0) return KVF_OK;
+  KVF_CHECK(chunks && rope_cos && rope_sin, KVF_ERR_INVALID_ARG, "required pointer is NULL");
+  if (kivi) {
+    KVF_CHECK(kivi->bits == 8, KVF_ERR_UNSUPPORTED,
+              "int8-resident re-positioning reads 8-bit KIVI caches, not %d-bit", kivi->bits);
+    KVF_CHECK(pool_k == nullptr && pool_v == nullptr, KVF_ERR_INVALID_ARG,
+              "pass either dense pool pointers or kivi, not both");
+    KVF_CHECK(kivi->k_codes && kivi->v_codes && kivi->k_min && kivi->k_scale && kivi->v_min &&
+                  kivi->v_scale && kivi->n_pool_chunks > 0, KVF_ERR_INVALID_ARG,
+              "incomplete kvf_kivi");
+  } else {
+    KVF_CHECK(pool_k && pool_v, KVF_ERR_INVALID_ARG, "pool pointers are NULL");
+  }
+  KVF_CHECK(max_chunk_len <= (1 << 24), KVF_ERR_UNSUPPORTED, "max_chunk_len too large");
+  return finish(kvf::launch_rerotate_q8(*layer, chunks, n_chunks, max_chunk_len, pool_k, pool_v,
+                                          kivi, pool_rows, rope_cos, rope_sin, rope_n_pos, *fused,
+                                          as_stream(stream)),
+                as_stream(stream), "kvf_rerotate_q8");
+  KVF_GUARD_END
+}
+
 kvf_status kvf_kivi_encode(const kvf_layer_desc* layer, const void* pool_k, const void* pool_v,
                            const int32_t* pool_cu, int32_t n_pool_chunks, int64_t pool_rows,
                            int32_t max_chunk_len, const kvf_kivi* out, void* stream) {
@@ -269,6 +313,39 @@ kvf_status kvf_score(kvf_score_mode mode_flags, const kvf_layer_desc* layer,
   return finish(kvf::launch_attn_mass(*layer, B, fused_k, q_u, n_last_q, out, workspace,
                                         ws_bytes, as_stream(stream)),
                 as_stream(stream), "kvf_score(attn_mass)");
+  KVF_GUARD_END
+}
+
+kvf_status kvf_score_q8(kvf_score_mode mode_flags, const kvf_layer_desc* layer,
+                        const kvf_batch* batch, const kvf_q8_cache* fused, const void* k_fresh,
+                        const uint8_t* eligible, float* scores, void* stream) {
+  KVF_GUARD_BEGIN
+  kvf_status st = check_layer(layer);
+  if (st != KVF_OK) return st;
+  KVF_CHECK(layer->dtype == KVF_BF16, KVF_ERR_UNSUPPORTED, "int8-resident caches need a bf16 layer");
+  kvf::BatchArgs B;
+  st = check_batch(batch, &B);
+  if (st != KVF_OK) return st;
+  const int flags = static_cast<int>(mode_flags);
+  KVF_CHECK((flags & ~(0xff | KVF_SCORE_ACCUMULATE)) == 0, KVF_ERR_INVALID_ARG,
+            "unknown score flags 0x%x", flags);
+  const int mode = flags & 0xff;
+  KVF_CHECK(mode == KVF_SCORE_DEVIATION || mode == KVF_SCORE_ATTN_MASS ||
+                mode == KVF_SCORE_KEY_NORM, KVF_ERR_INVALID_ARG, "unknown score mode %d", mode);
+  KVF_CHECK(mode != KVF_SCORE_ATTN_MASS, KVF_ERR_UNSUPPORTED,
+            "attention-mass scoring reads a bf16 fused cache");
+  st = check_q8(fused, B.cu_T[B.n_req]);
+  if (st != KVF_OK) return st;
+  if (B.cu_N[B.n_req] == 0) return KVF_OK;
+  KVF_CHECK(scores != nullptr, KVF_ERR_INVALID_ARG, "scores is NULL");
+  const kvf::ScoreOut out{scores, eligible, (flags & KVF_SCORE_ACCUMULATE) ? 1 : 0};
+  if (mode == KVF_SCORE_DEVIATION) {
+    KVF_CHECK(k_fresh != nullptr, KVF_ERR_INVALID_ARG, "k_fresh is NULL");
+    return finish(kvf::launch_deviation_q8(*layer, B, *fused, k_fresh, out, as_stream(stream)),
+                  as_stream(stream), "kvf_score_q8(deviation)");
+  }
+  return finish(kvf::launch_key_norm_q8(*layer, B, *fused, out, as_stream(stream)),
+                as_stream(stream), "kvf_score_q8(key_norm)");
   KVF_GUARD_END
 }
 
@@ -477,6 +554,30 @@ kvf_status kvf_scatter_kv(const kvf_layer_desc* layer, const void* k_src,
   KVF_GUARD_END
 }
 
+kvf_status kvf_scatter_kv_q8(const kvf_layer_desc* layer, const void* k_src,
+                             const int32_t* k_src_row, int64_t k_src_rows, const void* v_src,
+                             const int32_t* v_src_row, int64_t v_src_rows, const int32_t* dst_row,
+                             int32_t M, const kvf_q8_cache* fused, void* stream) {
+  KVF_GUARD_BEGIN
+  kvf_status st = check_layer(layer);
+  if (st != KVF_OK) return st;
+  KVF_CHECK(layer->dtype == KVF_BF16, KVF_ERR_UNSUPPORTED, "int8-resident caches need a bf16 layer");
+  KVF_CHECK(M >= 0 && k_src_rows >= 0 && v_src_rows >= 0, KVF_ERR_INVALID_ARG, "negative size");
+  st = check_q8(fused, 0);
+  if (st != KVF_OK) return st;
+  if (M == 0 || (k_src == nullptr && v_src == nullptr)) return KVF_OK;
+  KVF_CHECK(dst_row != nullptr, KVF_ERR_INVALID_ARG, "dst_row is NULL");
+  KVF_CHECK(!k_src || k_src_row || M <= k_src_rows, KVF_ERR_INVALID_ARG,
+            "identity k source map needs M <= k_src_rows");
+  KVF_CHECK(!v_src || v_src_row || M <= v_src_rows, KVF_ERR_INVALID_ARG,
+            "identity v source map needs M <= v_src_rows");
+  KVF_CHECK(M <= (1 << 28), KVF_ERR_UNSUPPORTED, "M too large");
+  return finish(kvf::launch_scatter_q8(*layer, k_src, k_src_row, k_src_rows, v_src, v_src_row,
+                                         v_src_rows, dst_row, M, *fused, as_stream(stream)),
+                as_stream(stream), "kvf_scatter_kv_q8");
+  KVF_GUARD_END
+}
+
 static kvf_status check_cu_q(const kvf::BatchArgs& B, const int32_t* cu_q) {
   KVF_CHECK(cu_q != nullptr, KVF_ERR_INVALID_ARG, "cu_q is NULL");
   KVF_CHECK(cu_q[0] == 0, KVF_ERR_INVALID_ARG, "cu_q[0] must be 0");
@@ -522,6 +623,36 @@ kvf_status kvf_sparse_q_attention(const kvf_layer_desc* layer, const kvf_batch* 
   return finish(kvf::launch_attention(*layer, B, q, q_pos, cu_q, fused_k, fused_v, sm_scale,
                                         out, lse, workspace, workspace_bytes, as_stream(stream)),
                 as_stream(stream), "kvf_sparse_q_attention");
+  KVF_GUARD_END
+}
+
+kvf_status kvf_sparse_q_attention_q8(const kvf_layer_desc* layer, const kvf_batch* batch,
+                                     const void* q, const int32_t* q_pos, const int32_t* cu_q,
+                                     const kvf_q8_cache* fused, float sm_scale, void* out,
+                                     float* lse, void* workspace, size_t workspace_bytes,
+                                     void* stream) {
+  KVF_GUARD_BEGIN
+  kvf_status st = check_layer(layer);
+  if (st != KVF_OK) return st;
+  KVF_CHECK(layer->dtype == KVF_BF16, KVF_ERR_UNSUPPORTED, "int8-resident caches need a bf16 layer");
+  kvf::BatchArgs B;
+  st = check_batch(batch, &B);
+  if (st != KVF_OK) return st;
+  st = check_cu_q(B, cu_q);
+  if (st != KVF_OK) return st;
+  KVF_CHECK(sm_scale > 0.f && sm_scale < 1e30f, KVF_ERR_INVALID_ARG, "bad sm_scale");
+  st = check_q8(fused, B.cu_T[B.n_req]);
+  if (st != KVF_OK) return st;
+  if (cu_q[B.n_req] == 0) return KVF_OK;
+  KVF_CHECK(q && q_pos && out, KVF_ERR_INVALID_ARG, "required pointer is NULL");
+  if (workspace != nullptr) {
+    const size_t need = kvf::attention_workspace(*layer, B, cu_q);
+    KVF_CHECK(workspace_bytes >= need, KVF_ERR_WORKSPACE,
+              "attention workspace %zu bytes, needs %zu", workspace_bytes, need);
+  }
+  return finish(kvf::launch_attention_q8(*layer, B, q, q_pos, cu_q, *fused, sm_scale, out, lse,
+                                           workspace, workspace_bytes, as_stream(stream)),
+                as_stream(stream), "kvf_sparse_q_attention_q8");
   KVF_GUARD_END
 }
 

@@ -102,6 +102,35 @@ __device__ __forceinline__ float group_sum(float v, int width) {
   return v;
 }
 
+// min and max over aligned groups of `width` lanes (width a power of two <= 64)
+__device__ __forceinline__ void group_minmax(float& mn, float& mx, int width) {
+  for (int o = width >> 1; o > 0; o >>= 1) {
+    mn = fminf(mn, __shfl_xor(mn, o, kWave));
+    mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
+  }
+}
+
+// ---------------------------------------------------------------------------
+// KIVI-style affine codes (KVBoost page, section 4.5, Eq. 7): fp32, in this
+// order: range = max - min, scale = range / levels, inv = levels / range,
+// code = (x - min) * inv rounded half to even and clamped to [0, levels];
+// range 0 gives scale 0 and codes 0.  levels = 2^BITS - 1.
+// ---------------------------------------------------------------------------
+template <int BITS>
+__device__ __forceinline__ uint32_t kivi_code(float x, float mn, float inv) {
+  constexpr float kTop = static_cast<float>((1 << BITS) - 1);
+  const float t = (x - mn) * inv;
+  return static_cast<uint32_t>(fminf(fmaxf(rintf(t), 0.f), kTop));
+}
+
+template <int BITS>
+__device__ __forceinline__ void kivi_stats(float mn, float mx, float& sc, float& inv) {
+  constexpr float kTop = static_cast<float>((1 << BITS) - 1);
+  const float rng = mx - mn;
+  sc = rng > 0.f ? rng / kTop : 0.f;
+  inv = rng > 0.f ? kTop / rng : 0.f;
+}
+
 // ---------------------------------------------------------------------------
 // hand-off between workgroups
 // ---------------------------------------------------------------------------
@@ -234,6 +263,22 @@ hipError_t launch_rerotate(const kvf_layer_desc& L, const kvf_chunk* chunks, int
                            int max_len, const void* pk, const void* pv, const kvf_kivi* q,
                            int64_t pool_rows, const float* rc, const float* rs, int rope_n,
                            void* fk, void* fv, int64_t fused_rows, int k_only, hipStream_t st);
+// int8-resident fused cache (kvf_q8_cache)
+hipError_t launch_rerotate_q8(const kvf_layer_desc& L, const kvf_chunk* chunks, int n_chunks,
+                              int max_len, const void* pk, const void* pv, const kvf_kivi* q,
+                              int64_t pool_rows, const float* rc, const float* rs, int rope_n,
+                              const kvf_q8_cache& fused, hipStream_t st);
+hipError_t launch_scatter_q8(const kvf_layer_desc& L, const void* ks, const int32_t* ksr,
+                             int64_t ks_rows, const void* vs, const int32_t* vsr, int64_t vs_rows,
+                             const int32_t* dst, int M, const kvf_q8_cache& fused, hipStream_t st);
+hipError_t launch_deviation_q8(const kvf_layer_desc& L, const BatchArgs& B, const kvf_q8_cache& c,
+                               const void* kf, const ScoreOut& out, hipStream_t st);
+hipError_t launch_key_norm_q8(const kvf_layer_desc& L, const BatchArgs& B, const kvf_q8_cache& c,
+                              const ScoreOut& out, hipStream_t st);
+hipError_t launch_attention_q8(const kvf_layer_desc& L, const BatchArgs& B, const void* q,
+                               const int32_t* q_pos, const int32_t* cu_q, const kvf_q8_cache& c,
+                               float sm_scale, void* out, float* lse, void* ws, size_t ws_bytes,
+                               hipStream_t st);
 hipError_t launch_kivi_encode(const kvf_layer_desc& L, const void* pk, const void* pv,
                               const int32_t* pool_cu, int n_pool, int64_t pool_rows,
                               int max_len, const kvf_kivi& out, hipStream_t st);

@@ -65,6 +65,12 @@ class KiviDesc(ctypes.Structure):
                 ("n_pool_chunks", ctypes.c_int32), ("bits", ctypes.c_int32)]
 
 
+class Q8CacheDesc(ctypes.Structure):
+    _fields_ = [("k_codes", ctypes.c_void_p), ("v_codes", ctypes.c_void_p),
+                ("k_stats", ctypes.c_void_p), ("v_stats", ctypes.c_void_p),
+                ("rows", ctypes.c_int64)]
+
+
 class StaticRules(ctypes.Structure):
     _fields_ = [("sink", ctypes.c_int32), ("boundary", ctypes.c_int32), ("seam", ctypes.c_int32)]
 
@@ -96,6 +102,13 @@ _SIGS = {
     "kvf_sparse_q_attention": (_I32, [_LP, _BP, _P, _P, _IP, _P, _P, ctypes.c_float, _P, _P, _P,
                                       _SZ, _P]),
     "kvf_attention_workspace_size": (_SZ, [_LP, _BP, _IP]),
+    "kvf_rerotate_q8": (_I32, [_LP, _P, _I32, _I32, _P, _P, ctypes.POINTER(KiviDesc), _I64, _P, _P,
+                               _I32, ctypes.POINTER(Q8CacheDesc), _P]),
+    "kvf_score_q8": (_I32, [_I32, _LP, _BP, ctypes.POINTER(Q8CacheDesc), _P, _P, _P, _P]),
+    "kvf_scatter_kv_q8": (_I32, [_LP, _P, _P, _I64, _P, _P, _I64, _P, _I32,
+                                 ctypes.POINTER(Q8CacheDesc), _P]),
+    "kvf_sparse_q_attention_q8": (_I32, [_LP, _BP, _P, _P, _IP, ctypes.POINTER(Q8CacheDesc),
+                                         ctypes.c_float, _P, _P, _P, _SZ, _P]),
     "kvf_kivi_encode": (_I32, [_LP, _P, _P, _P, _I32, _I64, _I32, ctypes.POINTER(KiviDesc), _P]),
     "kvf_recompute_budget": (_I32, [_I32, _I32]),
     "kvf_anchor_budget": (_I32, [_I32, _I32, _I32]),
@@ -424,3 +437,81 @@ def kivi_encode(layer: Layer, pool_k: torch.Tensor, pool_v: torch.Tensor, pool_c
     od = _kivi_desc(out)
     return _run(_lib.kvf_kivi_encode, (ctypes.byref(d), _ptr(pool_k), _ptr(pool_v), _ptr(pool_cu),
                                 n_pool, _rows(pool_k), max_chunk_len, ctypes.byref(od),), "kvf_kivi_encode", stream)
+
+
+# ----------------------------------------------------------------------------
+# int8-resident fused cache
+# ----------------------------------------------------------------------------
+def q8_cache(rows: int, n_kv_heads: int, head_dim: int, device="cuda") -> dict:
+    """A zeroed int8-resident fused cache (kvf_q8_cache): k_codes, v_codes
+    uint8 [rows, Hkv, d]; k_stats, v_stats float32 [rows, Hkv, 2] (min, scale)."""
+    codes = (rows, n_kv_heads, head_dim)
+    stats = (rows, n_kv_heads, 2)
+    return {"k_codes": torch.zeros(codes, dtype=torch.uint8, device=device),
+            "v_codes": torch.zeros(codes, dtype=torch.uint8, device=device),
+            "k_stats": torch.zeros(stats, dtype=torch.float32, device=device),
+            "v_stats": torch.zeros(stats, dtype=torch.float32, device=device)}
+
+
+def _q8_desc(c: dict) -> Q8CacheDesc:
+    return Q8CacheDesc(_ptr(c["k_codes"]), _ptr(c["v_codes"]), _ptr(c["k_stats"]),
+                       _ptr(c["v_stats"]), int(c["k_codes"].shape[0]))
+
+
+def rerotate_q8(layer: Layer, chunks: torch.Tensor, max_chunk_len: int,
+                pool_k: Optional[torch.Tensor], pool_v: Optional[torch.Tensor],
+                rope_cos: torch.Tensor, rope_sin: torch.Tensor, fused: dict,
+                kivi: Optional[dict] = None, stream=None):
+    """kvf_rerotate_q8: S1 into the int8-resident cache `fused` (q8_cache)
+    from a dense bf16 per-chunk cache or an 8-bit KIVI one (`kivi`)."""
+    kd = None
+    pool_rows = _rows(pool_k)
+    if kivi is not None:
+        kd = ctypes.byref(_kivi_desc(kivi))
+        pool_rows = int(kivi["k_codes"].shape[0])
+    d = layer.desc()
+    fd = _q8_desc(fused)
+    return _run(_lib.kvf_rerotate_q8, (ctypes.byref(d), _ptr(chunks), int(chunks.shape[0]),
+                                       max_chunk_len, _ptr(pool_k), _ptr(pool_v), kd, pool_rows,
+                                       _ptr(rope_cos), _ptr(rope_sin), int(rope_cos.shape[0]),
+                                       ctypes.byref(fd)), "kvf_rerotate_q8", stream, keep=(d, fd))
+
+
+def score_q8(mode: int, layer: Layer, batch: Batch, fused: dict, k_fresh: Optional[torch.Tensor],
+             scores: torch.Tensor, eligible: Optional[torch.Tensor] = None,
+             accumulate: bool = False, stream=None):
+    """kvf_score_q8: deviation or key-norm score over the int8-resident cache."""
+    d = layer.desc()
+    fd = _q8_desc(fused)
+    flags = mode | (KVF_SCORE_ACCUMULATE if accumulate else 0)
+    return _run(_lib.kvf_score_q8, (flags, ctypes.byref(d), ctypes.byref(batch.desc), ctypes.byref(fd),
+                                    _ptr(k_fresh), _ptr(eligible), _ptr(scores)), "kvf_score_q8",
+                stream, keep=(d, fd, batch))
+
+
+def scatter_kv_q8(layer: Layer, k_src: Optional[torch.Tensor], k_src_row: Optional[torch.Tensor],
+                  v_src: Optional[torch.Tensor], v_src_row: Optional[torch.Tensor],
+                  dst_row: torch.Tensor, fused: dict, M: Optional[int] = None, stream=None):
+    """kvf_scatter_kv_q8: bf16 rows encoded into the int8-resident cache."""
+    d = layer.desc()
+    fd = _q8_desc(fused)
+    M = int(dst_row.shape[0]) if M is None else M
+    return _run(_lib.kvf_scatter_kv_q8, (ctypes.byref(d), _ptr(k_src), _ptr(k_src_row), _rows(k_src),
+                                         _ptr(v_src), _ptr(v_src_row), _rows(v_src), _ptr(dst_row), M,
+                                         ctypes.byref(fd)), "kvf_scatter_kv_q8", stream, keep=(d, fd))
+
+
+def sparse_q_attention_q8(layer: Layer, batch: Batch, q: torch.Tensor, q_pos: torch.Tensor,
+                          cu_q: Sequence[int], fused: dict, sm_scale: float, out: torch.Tensor,
+                          lse: Optional[torch.Tensor] = None,
+                          workspace: Optional[torch.Tensor] = None, stream=None):
+    """kvf_sparse_q_attention_q8: the attention call over the int8-resident
+    cache (workspace as for sparse_q_attention)."""
+    d = layer.desc()
+    fd = _q8_desc(fused)
+    cq = _int_array(cu_q)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return _run(_lib.kvf_sparse_q_attention_q8, (ctypes.byref(d), ctypes.byref(batch.desc), _ptr(q),
+                                                 _ptr(q_pos), cq, ctypes.byref(fd), float(sm_scale),
+                                                 _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes),
+                "kvf_sparse_q_attention_q8", stream, keep=(d, fd, batch, cq))

@@ -24,6 +24,10 @@ itself.  Order (all on one stream, no host synchronisation):
     kvf_recompute_qkv(P+U, Q|K|V into the fused cache) -> kvf_sparse_q_attention
   A score selector with static rules takes their positions as a forced set
   (kvf_select_static before kvf_select_topk).
+  int8-resident fused cache (KVBoost page, section 4.5, Eq. 7 kept by the
+  fused cache; section 7.3): the same order with kvf_rerotate_q8,
+  kvf_score_q8 and kvf_sparse_q_attention_q8, and the recomputed K/V written
+  to compact bf16 rows that kvf_scatter_kv_q8 encodes into the cache.
 
 The per-chunk caches are built ahead of serving (QCFuse page, section 2.1.2,
 Eq. 3) either by the caller (`pic=`) or on the GPU by this library's own
@@ -66,8 +70,9 @@ class FusedLayerGPU:
 
     def __init__(self, batch: SynthBatch, ratio_pct: int, device="cuda",
                  pic: Optional[dict] = None, n_last_q: int = 0, mode: Optional[str] = None,
-                 k_only: Optional[bool] = None):
+                 k_only: Optional[bool] = None, resident: Optional[str] = None):
         wl = batch.wl
+        self.q8 = (wl.resident if resident is None else resident) == "q8"
         self.wl = wl
         self.batch = batch
         self.mode = mode or wl.score
@@ -136,7 +141,10 @@ class FusedLayerGPU:
 
         # keys-only re-positioning: the values are stitched by load()
         dense = self.kivi is None
-        self.k_only = (dense and not wl.pool_chunks) if k_only is None else bool(k_only)
+        self.k_only = (dense and not wl.pool_chunks and not self.q8) if k_only is None else bool(k_only)
+        if self.q8 and (self.k_only or self.mass or wl.dtype != "bf16"):
+            raise ValueError("the int8-resident cache takes a bf16 layer, a gathering "
+                             "re-positioning and a score other than attention mass")
         if self.k_only and not dense:
             raise ValueError("keys-only re-positioning needs a dense per-chunk cache")
         if self.k_only:
@@ -174,8 +182,19 @@ class FusedLayerGPU:
         M = self.cu_q[-1]
         self.M = M
         n_scores = int(np.sum(batch.n_ctx))
-        self.fused_k = torch.zeros((T_total, hkv, d), dtype=td, device=dev)
-        self.fused_v = torch.zeros_like(self.fused_k)
+        if self.q8:
+            self.fused = kvf.q8_cache(T_total, hkv, d, device=dev)
+            self.fused_k = self.fused_v = None
+            # the recomputed rows' K (without a probe) and V, compact, before
+            # kvf_scatter_kv_q8 encodes them into the cache
+            self.k_new = torch.zeros((max(M, 1), hkv, d), dtype=td,
+                                     device=dev) if not self.probe else None
+            self.v_new = torch.zeros((max(M, 1), hkv, d), dtype=td,
+                                     device=dev)
+        else:
+            self.fused = None
+            self.fused_k = torch.zeros((T_total, hkv, d), dtype=td, device=dev)
+            self.fused_v = torch.zeros_like(self.fused_k)
         self.scores = torch.zeros(max(n_scores, 1), dtype=torch.float32, device=dev)
         self.sel = torch.zeros(max(sum(self.k_per_req), 1), dtype=torch.int32, device=dev)
         self.rows = torch.zeros(max(M, 1), dtype=torch.int32, device=dev)
@@ -215,6 +234,9 @@ class FusedLayerGPU:
 
     # ------------------------------------------------------------------ calls
     def _rerotate(self):
+        if self.q8:
+            return kvf.rerotate_q8(self.layer, self.chunks, self.max_chunk_len, self.pool_k, self.pool_v,
+                                   self.rope_cos, self.rope_sin, self.fused, kivi=self.kivi)
         if self.k_only:
             return kvf.rerotate(self.layer, self.chunks, self.max_chunk_len, self.pool_k, None,
                                 self.rope_cos, self.rope_sin, self.fused_k, None, k_only=True)
@@ -244,6 +266,12 @@ class FusedLayerGPU:
         return kvf.select_static(self.kb, self.chunks, self.rules, self.static_mask)
 
     def _score(self):
+        if self.q8:
+            if self.selector == "anchor":
+                return kvf.score_q8(kvf.KVF_SCORE_KEY_NORM, self.layer, self.kb, self.fused, None,
+                                    self.scores)
+            return kvf.score_q8(kvf.KVF_SCORE_DEVIATION, self.layer, self.kb, self.fused, self.k_probe,
+                                self.scores)
         if self.selector == "anchor":
             return kvf.score(kvf.KVF_SCORE_KEY_NORM, self.layer, self.kb, self.fused_k, None, None,
                              self.scores)
@@ -266,6 +294,12 @@ class FusedLayerGPU:
     def _recompute(self):
         if self.M == 0:
             return None
+        if self.q8:
+            # compact K (unless the probe has it) and V rows for kvf_scatter_kv_q8
+            mask = kvf.KVF_OUT_Q | kvf.KVF_OUT_V | (0 if self.probe else kvf.KVF_OUT_K)
+            return kvf.recompute_qkv(self.layer, self.x, self.rows, self.pos, self.w, mask,
+                                     self.rope_cos, self.rope_sin, q_out=self.q, k_out=self.k_new,
+                                     v_out=self.v_new, M=self.M, workspace=self.gemm_ws)
         if self.probe:
             # K of these rows is already in the probe
             return kvf.recompute_qkv(self.layer, self.x, self.rows, self.pos, self.w,
@@ -283,12 +317,19 @@ class FusedLayerGPU:
         # deviation mode: K of the recomputed rows is the probe's
         if self.M == 0:
             return None
+        if self.q8:
+            k_src, k_row = (self.k_probe, self.rows) if self.probe else (self.k_new, None)
+            return kvf.scatter_kv_q8(self.layer, k_src, k_row, self.v_new, None, self.rows, self.fused,
+                                     M=self.M)
         return kvf.scatter_kv(self.layer, self.k_probe, self.rows, None, None, self.rows, self.fused_k,
                               self.fused_v, M=self.M)
 
     def _attention(self):
         if self.M == 0:
             return None
+        if self.q8:
+            return kvf.sparse_q_attention_q8(self.layer, self.kb, self.q, self.pos, self.cu_q, self.fused,
+                                             self.sm_scale, self.out, self.lse, workspace=self.attn_ws)
         return kvf.sparse_q_attention(self.layer, self.kb, self.q, self.pos, self.cu_q, self.fused_k,
                                       self.fused_v, self.sm_scale, self.out, self.lse,
                                       workspace=self.attn_ws)
@@ -319,9 +360,10 @@ class FusedLayerGPU:
         stage is one of rerotate / score / select / recompute_fuse / attention."""
         f = self.fn
         fuse = [("recompute", "recompute_fuse", f("recompute"))]
+        if self.probe or self.q8:
+            fuse.append(("scatter", "recompute_fuse", f("scatter")))
         if self.probe:
             score = [("k_probe", "score", f("k_probe")), ("score", "score", f("score"))]
-            fuse.append(("scatter", "recompute_fuse", f("scatter")))
         elif self.mass:
             score = [("u_probe", "score", f("u_probe")), ("score", "score", f("score"))]
         elif self.selector == "anchor":

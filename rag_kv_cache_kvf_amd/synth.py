@@ -48,6 +48,7 @@ class Workload:
     sigma: float               # cached-hidden perturbation of non-first chunks
     pool_chunks: int = 0       # >0: chunks drawn from a shared pool of this size
     kivi_bits: int = 0         # cached K/V stored as KIVI codes of 8 or 4 bits (0: dense)
+    resident: str = ""         # fused cache format: "" bf16/f32 as dtype, "q8" int8-resident
     seed: int = 0
     description: str = ""
     # selector feeding the recompute path: "score" (top-k of `score`, with
@@ -166,6 +167,15 @@ WORKLOADS = {
         kivi_bits=8,
         description="Qwen2.5-3B-shaped layer, bf16 + int8 KIVI cache, 16 requests "
                     "of 24x128 + 64 query"),
+    # The same layer and data with the fused cache itself held as 8-bit codes
+    # (int8-resident: the scores and the attention decode on load).
+    "qwen25_3b_kivi8_resident": _wl(
+        name="qwen25_3b_kivi8_resident", dtype="bf16", n_req=16, chunk_lens=(128,) * 24,
+        n_query=(64,), hidden=2048, n_q_heads=16, n_kv_heads=2, head_dim=128,
+        rope_base=1e6, score="deviation", ratio_pct=(15,), sigma=0.1,
+        kivi_bits=8, resident="q8",
+        description="Qwen2.5-3B-shaped layer, bf16 + int8 KIVI cache, int8-resident fused "
+                    "cache, 16 requests of 24x128 + 64 query"),
     # The same with 4-bit KIVI codes (KVBoost's int4 setting).
     "qwen25_3b_kivi4": _wl(
         name="qwen25_3b_kivi4", dtype="bf16", n_req=16, chunk_lens=(128,) * 24,
@@ -192,6 +202,15 @@ MINI_WORKLOADS = {
         name="mini_bf16_kivi8", dtype="bf16", n_req=2, chunk_lens=(128, 45, 128),
         n_query=(33, 7), hidden=256, n_q_heads=8, n_kv_heads=1, head_dim=128,
         rope_base=1e6, score="deviation", ratio_pct=(15,), sigma=0.1, kivi_bits=8),
+    "mini_bf16_kivi8_resident": _wl(
+        name="mini_bf16_kivi8_resident", dtype="bf16", n_req=2, chunk_lens=(128, 45, 128),
+        n_query=(33, 7), hidden=256, n_q_heads=8, n_kv_heads=1, head_dim=128,
+        rope_base=1e6, score="deviation", ratio_pct=(15,), sigma=0.1, kivi_bits=8,
+        resident="q8"),
+    "mini_bf16_dense_resident": _wl(
+        name="mini_bf16_dense_resident", dtype="bf16", n_req=3, chunk_lens=(70, 70, 70, 70),
+        n_query=(21,), hidden=384, n_q_heads=4, n_kv_heads=2, head_dim=64,
+        rope_base=1e6, score="deviation", ratio_pct=(30,), sigma=0.1, resident="q8"),
     "mini_bf16_kivi4": _wl(
         name="mini_bf16_kivi4", dtype="bf16", n_req=2, chunk_lens=(128, 45, 128),
         n_query=(33, 7), hidden=256, n_q_heads=8, n_kv_heads=1, head_dim=128,

@@ -48,7 +48,7 @@ def test_status_strings_and_version(lib):
     lib.kvf_status_string.restype = ctypes.c_char_p
     assert lib.kvf_status_string(0) == b"KVF_OK"
     assert lib.kvf_status_string(2) == b"KVF_ERR_UNSUPPORTED"
-    assert lib.kvf_abi_version() == 9
+    assert lib.kvf_abi_version() == 10
 
 
 def test_budget_matches_oracle(lib):
@@ -300,3 +300,68 @@ def test_noalloc_rejects_oversized_calls(lib):
     b2, keep2 = _batch([0, 5184], [5120])
     assert lib.kvf_score_workspace_size(1, ctypes.byref(Layer(4096, 32, 8, 128, 1)), ctypes.byref(b2),
                                         0) < 48 << 20
+
+
+class Q8(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("kc", "vc", "ks", "vs")] + [("rows", ctypes.c_int64)]
+
+
+def test_q8_validation(lib):
+    """The int8-resident calls check the cache descriptor, its row count
+    against the batch, the layer precision and the supported sources and
+    modes on the host."""
+    P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    lib.kvf_rerotate_q8.argtypes = [P, P, I32, I32, P, P, P, I64, P, P, I32, P, P]
+    lib.kvf_score_q8.argtypes = [I32, P, P, P, P, P, P, P]
+    lib.kvf_scatter_kv_q8.argtypes = [P, P, P, I64, P, P, I64, P, I32, P, P]
+    lib.kvf_sparse_q_attention_q8.argtypes = [P, P, P, P, P, P, ctypes.c_float, P, P, P,
+                                              ctypes.c_size_t, P]
+    bf = Layer(2048, 16, 2, 128, 1)
+    f32 = Layer(2048, 16, 2, 128, 0)
+    c = Q8(FAKE, FAKE, FAKE, FAKE, 100)
+    short = Q8(FAKE, FAKE, FAKE, FAKE, 99)
+    partial = Q8(FAKE, None, FAKE, FAKE, 100)
+
+    class Kivi(ctypes.Structure):
+        _fields_ = [(n, ctypes.c_void_p) for n in ("kc", "vc", "km", "ks", "vm", "vs")] + [
+            ("n", ctypes.c_int32), ("bits", ctypes.c_int32)]
+    k8 = Kivi(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8)
+    k4 = Kivi(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 4)
+    rr = lib.kvf_rerotate_q8
+    assert rr(ctypes.byref(f32), FAKE, 1, 4, None, None, ctypes.byref(k8), 4, FAKE, FAKE, 4,
+              ctypes.byref(c), None) == 2                      # bf16 layers only
+    assert rr(ctypes.byref(bf), FAKE, 1, 4, None, None, ctypes.byref(k4), 4, FAKE, FAKE, 4,
+              ctypes.byref(c), None) == 2                      # 4-bit sources unsupported
+    assert rr(ctypes.byref(bf), FAKE, 1, 4, FAKE, FAKE, ctypes.byref(k8), 4, FAKE, FAKE, 4,
+              ctypes.byref(c), None) == 1                      # dense and KIVI at once
+    assert rr(ctypes.byref(bf), FAKE, 1, 4, FAKE, None, None, 4, FAKE, FAKE, 4,
+              ctypes.byref(c), None) == 1                      # dense needs both tensors
+    assert rr(ctypes.byref(bf), FAKE, 1, 4, FAKE, FAKE, None, 4, FAKE, FAKE, 4,
+              None, None) == 1                                 # no cache
+    assert rr(ctypes.byref(bf), FAKE, 1, 4, FAKE, FAKE, None, 4, FAKE, FAKE, 4,
+              ctypes.byref(partial), None) == 1
+    assert rr(ctypes.byref(bf), FAKE, 0, 4, FAKE, FAKE, None, 4, FAKE, FAKE, 4,
+              ctypes.byref(c), None) == 0                      # no chunks: nothing to do
+    b, keep = _batch([0, 60, 100], [50, 30])
+    sq = lib.kvf_score_q8
+    assert sq(1, ctypes.byref(bf), ctypes.byref(b), ctypes.byref(c), FAKE, None, FAKE, None) == 2
+    assert sq(0, ctypes.byref(bf), ctypes.byref(b), ctypes.byref(c), None, None, FAKE, None) == 1
+    assert sq(0, ctypes.byref(bf), ctypes.byref(b), ctypes.byref(short), FAKE, None, FAKE, None) == 1
+    assert sq(3, ctypes.byref(bf), ctypes.byref(b), ctypes.byref(c), FAKE, None, FAKE, None) == 1
+    assert sq(0, ctypes.byref(f32), ctypes.byref(b), ctypes.byref(c), FAKE, None, FAKE, None) == 2
+    sc = lib.kvf_scatter_kv_q8
+    assert sc(ctypes.byref(bf), FAKE, None, 4, None, None, 0, FAKE, 5, ctypes.byref(c), None) == 1
+    assert sc(ctypes.byref(bf), FAKE, None, 4, None, None, 0, None, 4, ctypes.byref(c), None) == 1
+    assert sc(ctypes.byref(bf), None, None, 0, None, None, 0, None, 4, ctypes.byref(c), None) == 0
+    at = lib.kvf_sparse_q_attention_q8
+    cq = (ctypes.c_int32 * 3)(0, 20, 30)
+    assert at(ctypes.byref(bf), ctypes.byref(b), FAKE, FAKE, cq, ctypes.byref(short), 0.088, FAKE,
+              None, None, 0, None) == 1
+    assert at(ctypes.byref(f32), ctypes.byref(b), FAKE, FAKE, cq, ctypes.byref(c), 0.088, FAKE,
+              None, None, 0, None) == 2
+    lib.kvf_attention_workspace_size.restype = ctypes.c_size_t
+    need = lib.kvf_attention_workspace_size(ctypes.byref(bf), ctypes.byref(b), cq)
+    assert need > 0
+    assert at(ctypes.byref(bf), ctypes.byref(b), FAKE, FAKE, cq, ctypes.byref(c), 0.088, FAKE,
+              None, FAKE, need - 1, None) == 3
+
