@@ -27,7 +27,8 @@ The roofline object describes the call that takes longest; its `traffic` is
 the HBM bytes per launch from the committed counter summary of that kernel
 and workload under profiles/, or null when the kernel source has changed
 since the counters were taken.  The default run adds the 8-request pool
-workload at 30% and 15% as sub-objects.  The CPU baseline runs the float64
+workload at 30% and 15%, and the Qwen2.5-3B-shaped int8 KIVI layer with a
+bf16 and with an int8-resident fused cache, as sub-objects.  The CPU baseline runs the float64
 oracle on the same batch on the host cores.
 """
 from __future__ import annotations
@@ -65,8 +66,16 @@ CALL_KERNEL = {
     "select": ("topk_kernel", "kernels/topk.hip"),
     "recompute": ("gemm_qkv_bf16_kernel", "kernels/gemm_qkv.hip"),
     "scatter": ("scatter_kernel", "kernels/scatter_deviation.hip"),
-    "attention": ("attn_bf16_kernel", "kernels/attention.hip"),
+    "attention": ("attn_mfma_kernel", "kernels/attention.hip"),
 }
+# the int8-resident forms of the calls that touch the fused cache
+CALL_KERNEL_Q8 = {
+    "rerotate": ("rerotate_q8_kernel", "kernels/rope_rerotate.hip"),
+    "scatter": ("scatter_q8_kernel", "kernels/scatter_deviation.hip"),
+}
+# the int8 KIVI workload with a bf16 fused cache and with an int8-resident
+# one, measured in the default run as sub-objects
+Q8_WORKLOADS = ("qwen25_3b_kivi8", "qwen25_3b_kivi8_resident")
 
 
 def _parse():
@@ -99,10 +108,17 @@ def call_work(g):
     M = g.M
     pos = g.pos.cpu().numpy()[:M].astype("int64")
     work = {}
-    if wl.kivi_bits:
+    q8row = hkv * (d + 8)                          # int8-resident row: codes + (min, scale)
+    n_chunks = b.chunk_table.shape[0]
+    if g.q8:
+        # pool K codes (or bf16 K) and per-chunk K stats in; V codes and
+        # per-token stats copied (or bf16 V encoded); K and V codes + stats out
+        src = (2 * hkv * d + 8 * hkv) if wl.kivi_bits == 8 else 2 * krow
+        work["rerotate"] = ("hbm", n_ctx * (src + 2 * q8row)
+                            + (n_chunks * 8 * hkv * d if wl.kivi_bits else 0))
+    elif wl.kivi_bits:
         # read K/V codes (bits / 8 B each) + V per-token stats (min, scale) +
         # K per-channel stats once per chunk; write bf16 K and V
-        n_chunks = b.chunk_table.shape[0]
         work["rerotate"] = ("hbm", n_ctx * (2 * hkv * d * wl.kivi_bits // 8 + 8 * hkv + 2 * krow)
                             + n_chunks * 8 * hkv * d)
     elif g.k_only:
@@ -112,11 +128,11 @@ def call_work(g):
     if g.selector == "static":
         work["recompute"] = ("mfma", 2.0 * hid * d * (hq + 2 * hkv) * M)
     elif g.selector == "anchor":
-        work["score"] = ("hbm", n_ctx * (krow + 4))       # fused K -> one fp32 norm
+        work["score"] = ("hbm", n_ctx * ((q8row if g.q8 else krow) + 4))   # fused K -> one fp32 norm
         work["recompute"] = ("mfma", 2.0 * hid * d * (hq + 2 * hkv) * M)
     elif g.mode == "deviation":
         work["k_probe"] = ("mfma", 2.0 * hid * hkv * d * total)
-        work["score"] = ("hbm", n_ctx * (2 * krow + 4))   # fused K, probe K -> one fp32
+        work["score"] = ("hbm", n_ctx * ((q8row if g.q8 else krow) + krow + 4))   # fused K, probe K -> fp32
         work["recompute"] = ("mfma", 2.0 * hid * d * (hq + hkv) * M)
     else:
         work["u_probe"] = ("mfma", 2.0 * hid * d * (hq + 2 * hkv) * nU)
@@ -135,7 +151,9 @@ def call_work(g):
                       + (n_ctx if g.static_mask is not None else 0) + k_sum * 4 + M * 8)
     if g.static_mask is not None:
         work["static_mask"] = ("hbm", n_ctx + b.chunk_table.shape[0] * 32)   # mask out, table in
-    if g.probe:
+    if g.q8:
+        work["scatter"] = ("hbm", M * 2 * (krow + q8row))   # bf16 K, V rows in; codes + stats out
+    elif g.probe:
         work["scatter"] = ("hbm", M * 2 * krow)       # probe K in; fused K rows out
     work["attention"] = ("mfma", 4.0 * d * hq * float((pos + 1).sum()))   # QK^T + PV, causal
     return work
@@ -584,6 +602,14 @@ def main():
                                                 "roofline", "calls")}
             del gx
             torch.cuda.empty_cache()
+        # the int8 KIVI layer with a bf16 fused cache and with an int8-resident one
+        for name in Q8_WORKLOADS:
+            qwl = synth.get_workload(name)
+            sub, _, gx = measure(qwl, qwl.ratio_pct[-1], args.steps, args.warmup, flush)
+            out[name] = {k: sub[k] for k in ("value", "unit", "ms_per_step", "config", "timing",
+                                             "roofline", "calls")}
+            del gx
+            torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(batch, ratio)
     print(json.dumps(out), flush=True)
@@ -625,7 +651,7 @@ def measure(wl, ratio, steps, warmup, flush, graph=False):
                        "unit": unit, "frac": round(ach / peak, 4),
                        "algorithmic": float(amount), "ms_warm": round(per_call_warm[name], 5)}
     dom = max(per_call, key=per_call.get)
-    kname, ksrc = CALL_KERNEL[dom]
+    kname, ksrc = (CALL_KERNEL_Q8 if g.q8 and dom in CALL_KERNEL_Q8 else CALL_KERNEL)[dom]
     if dom == "score" and g.selector == "anchor":
         kname, ksrc = "key_norm_kernel", "kernels/scatter_deviation.hip"
     elif dom == "score" and g.mode == "deviation":
@@ -654,7 +680,9 @@ def measure(wl, ratio, steps, warmup, flush, graph=False):
               ("key_norm" if wl.selector == "anchor" else None),
               "recomputed_context_tokens": int(sum(g.k_per_req)),
               "rerotate": "keys only (values stitched by the loader)" if g.k_only else
-              ("KIVI decode" if wl.kivi_bits else "gather keys and values")}
+              ("KIVI decode" if wl.kivi_bits else "gather keys and values") +
+              (", int8-resident fused cache (8-bit codes + per-row min/scale)" if g.q8 else
+               ", bf16 fused cache")}
     res = {"value": round(n_ctx / (med * 1e-3), 1), "unit": UNIT, "ms_per_step": round(med, 5),
            "ms_median": round(med, 5), "config": config, "timing": timing, "roofline": roofline,
            "calls": calls}

@@ -389,18 +389,21 @@ attn_mfma_kernel(AttnArgs a) {
       slot[kAT + st_row] = fmaf(-1024.f, sc, mn) * a.scale_log2;
     }
   };
-  // values: min + code * scale as fp16 into the swizzled tile row
+  // values: min + code * scale as fp16 into the swizzled tile row, computed
+  // as (1024 + code) * scale + (min - 1024 scale) from the permuted fp16
+  // integer (one mixed-precision multiply-add, one rounding per value)
   auto stage_commit = [&](const u32x2_t (&c)[NPC], const u32x2_t& stv, bf16_t* dst)
       __attribute__((always_inline)) {
-    const float mn = __uint_as_float(stv[0]), sc = __uint_as_float(stv[1]);
+    const float sc = __uint_as_float(stv[1]);
+    const float m2 = fmaf(-1024.f, sc, __uint_as_float(stv[0]));
 #pragma unroll
     for (int i = 0; i < NPC; ++i) {
       u32x4_t w;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const uint32_t word = c[i][e >> 1] >> (16 * (e & 1));
-        w[e] = pack_f16x2(fmaf(static_cast<float>(word & 0xffu), sc, mn),
-                          fmaf(static_cast<float>((word >> 8) & 0xffu), sc, mn));
+        const f16x2_t x = __builtin_bit_cast(
+            f16x2_t, __builtin_amdgcn_perm(0x64646464u, c[i][e >> 1], (e & 1) ? 0x04030402u : 0x04010400u));
+        w[e] = pack_f16x2(fmaf(static_cast<float>(x[0]), sc, m2), fmaf(static_cast<float>(x[1]), sc, m2));
       }
       const int piece = (tid & 3) + 4 * i;
       *reinterpret_cast<u32x4_t*>(dst + st_row * D + ((piece ^ chunk_xor<D>(st_row)) << 3)) = w;

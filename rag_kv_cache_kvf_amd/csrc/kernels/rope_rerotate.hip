@@ -225,12 +225,12 @@ hipError_t launch_rerotate(const kvf_layer_desc& L, const kvf_chunk* chunks, int
 // ---------------------------------------------------------------------------
 // S1 into an int8-resident fused cache
 // ---------------------------------------------------------------------------
-// One wave per fused row of a chunk tile; a group of d/2 lanes takes one kv
-// head, lane j its rotation pair (j, j + d/2), so the row's 8-bit group is
-// encoded after one min/max reduction over the group and no value leaves
-// registers.  Code bytes j and j + d/2 of consecutive lanes are contiguous,
-// so every byte load and store of the wave covers whole 64- or 32-byte runs.
-constexpr int kQ8RotRows = 4;     // rows per workgroup (one per wave)
+// Work items are (row of a chunk, kv head), d/8 lanes each: lane j of an
+// item takes the four rotation pairs (4j + i, 4j + i + d/2), i < 4, so its
+// code bytes move as two 4-byte words, its statistics, cos and sin as float4
+// loads, and the item's 8-bit group is encoded after one min/max reduction
+// over its lanes.  A wave holds 8 (d = 128) or 16 (d = 64) items.
+constexpr int kQ8RotWaves = 4;
 
 struct RotQ8Args {
   const kvf_chunk* chunks;
@@ -252,83 +252,136 @@ struct RotQ8Args {
   int d;
 };
 
-// encode the pair (lo, hi) of every lane of a group of `half` lanes;
-// returns the codes, the group's (min, scale) in mn/sc
-__device__ __forceinline__ void encode_pair(float lo, float hi, int half, bool valid,
-                                            uint32_t& c_lo, uint32_t& c_hi, float& mn, float& sc) {
-  mn = valid ? fminf(lo, hi) : INFINITY;
-  float mx = valid ? fmaxf(lo, hi) : -INFINITY;
-  group_minmax(mn, mx, half);
+__device__ __forceinline__ void bytes4(uint32_t w, float (&x)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) x[i] = static_cast<float>((w >> (8 * i)) & 0xffu);
+}
+
+// the 8 values of one lane -> 8 codes (two words, channels 4j.. and
+// 4j + d/2..) and the item's (min, scale); `gl` lanes per item
+__device__ __forceinline__ void encode8(const float (&lo)[4], const float (&hi)[4], int gl, bool valid,
+                                        uint32_t& w_lo, uint32_t& w_hi, float& mn, float& sc) {
+  mn = INFINITY;
+  float mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    mn = fminf(mn, fminf(lo[i], hi[i]));
+    mx = fmaxf(mx, fmaxf(lo[i], hi[i]));
+  }
+  if (!valid) {
+    mn = INFINITY;
+    mx = -INFINITY;
+  }
+  group_minmax(mn, mx, gl);
   float inv;
   kivi_stats<8>(mn, mx, sc, inv);
-  c_lo = kivi_code<8>(lo, mn, inv);
-  c_hi = kivi_code<8>(hi, mn, inv);
+  w_lo = w_hi = 0u;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    w_lo |= kivi_code<8>(lo[i], mn, inv) << (8 * i);
+    w_hi |= kivi_code<8>(hi[i], mn, inv) << (8 * i);
+  }
 }
 
 // KB: 0 for a dense bf16 per-chunk cache, 8 for an 8-bit KIVI one
 template <int KB>
-__global__ void __launch_bounds__(256) rerotate_q8_kernel(RotQ8Args a) {
+__global__ void __launch_bounds__(64 * kQ8RotWaves) rerotate_q8_kernel(RotQ8Args a) {
   const kvf_chunk ch = a.chunks[blockIdx.x];
-  const int t = blockIdx.y * kQ8RotRows + static_cast<int>(threadIdx.x >> 6);
-  if (ch.len <= 0 || t >= ch.len) return;
+  if (ch.len <= 0) return;
   if (ch.src_row < 0 || static_cast<int64_t>(ch.src_row) + ch.len > a.pool_rows) return;
   if (ch.dst_row < 0 || static_cast<int64_t>(ch.dst_row) + ch.len > a.out.rows) return;
   if (ch.pos0 < 0 || ch.pos0 >= a.rope_n) return;
   if (KB && (ch.pool_chunk < 0 || ch.pool_chunk >= a.n_pool_chunks)) return;
 
   const int d = a.d, half = d >> 1, hkv = a.hkv;
-  const int lane = threadIdx.x & (kWave - 1);
-  const int j = lane & (half - 1);
-  const int hpp = kWave / half;                    // heads per pass
-  const int64_t srow = static_cast<int64_t>(ch.src_row) + t;
-  const int64_t drow = static_cast<int64_t>(ch.dst_row) + t;
-  const float c = a.rope_cos[static_cast<int64_t>(ch.pos0) * half + j];
-  const float sn = a.rope_sin[static_cast<int64_t>(ch.pos0) * half + j];
-  for (int h0 = 0; h0 < hkv; h0 += hpp) {
-    const int h = h0 + lane / half;
-    const bool valid = h < hkv;
-    const int64_t src = (srow * hkv + h) * d + j;  // element offsets of channel j
-    const int64_t dst = (drow * hkv + h) * d + j;
-    // keys: decode, rotate by R(pos0), encode
-    float lo = 0.f, hi = 0.f;
-    if (valid) {
-      if constexpr (KB == 8) {
-        const int64_t st = (static_cast<int64_t>(ch.pool_chunk) * hkv + h) * d + j;
-        lo = fmaf(static_cast<float>(a.k_codes[src]), a.k_scale[st], a.k_min[st]);
-        hi = fmaf(static_cast<float>(a.k_codes[src + half]), a.k_scale[st + half], a.k_min[st + half]);
-      } else {
-        lo = bf16_to_f32(a.pool_k[src]);
-        hi = bf16_to_f32(a.pool_k[src + half]);
-      }
-    }
-    const float rlo = lo * c - hi * sn;
-    const float rhi = hi * c + lo * sn;
-    uint32_t clo, chi;
-    float mn, sc;
-    encode_pair(rlo, rhi, half, valid, clo, chi, mn, sc);
-    if (valid) {
-      a.out.k_codes[dst] = static_cast<uint8_t>(clo);
-      a.out.k_codes[dst + half] = static_cast<uint8_t>(chi);
-      if (j == 0) *reinterpret_cast<float2*>(a.out.k_stats + (drow * hkv + h) * 2) = make_float2(mn, sc);
-    }
-    // values: 8-bit KIVI rows are copied, dense ones encoded
+  const int gl = d >> 3;                           // lanes per item
+  const int ipb = kQ8RotWaves * kWave / gl;        // items per workgroup
+  const int lane_in = threadIdx.x & (gl - 1);
+  const int item = blockIdx.y * ipb + static_cast<int>(threadIdx.x) / gl;
+  const int t = item / hkv, h = item - t * hkv;
+  // items past the chunk take part in the reductions of their wave only
+  const bool valid = t < ch.len;
+  const int j = 4 * lane_in;                       // first channel of the low quad
+  const int64_t srow = static_cast<int64_t>(ch.src_row) + (valid ? t : 0);
+  const int64_t drow = static_cast<int64_t>(ch.dst_row) + (valid ? t : 0);
+  const int64_t src = (srow * hkv + h) * d + j;    // element offset of channel j
+  const int64_t dst = (drow * hkv + h) * d + j;
+  // keys: decode, rotate by R(pos0), encode
+  float lo[4] = {0.f, 0.f, 0.f, 0.f}, hi[4] = {0.f, 0.f, 0.f, 0.f};
+  if (valid) {
     if constexpr (KB == 8) {
-      if (valid) {
-        a.out.v_codes[dst] = a.v_codes[src];
-        a.out.v_codes[dst + half] = a.v_codes[src + half];
-        if (j == 0)
-          *reinterpret_cast<float2*>(a.out.v_stats + (drow * hkv + h) * 2) =
-              make_float2(a.v_min[srow * hkv + h], a.v_scale[srow * hkv + h]);
+      const int64_t st = (static_cast<int64_t>(ch.pool_chunk) * hkv + h) * d + j;
+      float cl[4], chh[4];
+      bytes4(*reinterpret_cast<const uint32_t*>(a.k_codes + src), cl);
+      bytes4(*reinterpret_cast<const uint32_t*>(a.k_codes + src + half), chh);
+      const float4 ml = *reinterpret_cast<const float4*>(a.k_min + st);
+      const float4 sl = *reinterpret_cast<const float4*>(a.k_scale + st);
+      const float4 mh = *reinterpret_cast<const float4*>(a.k_min + st + half);
+      const float4 sh = *reinterpret_cast<const float4*>(a.k_scale + st + half);
+      const float mlv[4] = {ml.x, ml.y, ml.z, ml.w}, slv[4] = {sl.x, sl.y, sl.z, sl.w};
+      const float mhv[4] = {mh.x, mh.y, mh.z, mh.w}, shv[4] = {sh.x, sh.y, sh.z, sh.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        lo[i] = fmaf(cl[i], slv[i], mlv[i]);
+        hi[i] = fmaf(chh[i], shv[i], mhv[i]);
       }
     } else {
-      const float vlo = valid ? bf16_to_f32(a.pool_v[src]) : 0.f;
-      const float vhi = valid ? bf16_to_f32(a.pool_v[src + half]) : 0.f;
-      encode_pair(vlo, vhi, half, valid, clo, chi, mn, sc);
-      if (valid) {
-        a.out.v_codes[dst] = static_cast<uint8_t>(clo);
-        a.out.v_codes[dst + half] = static_cast<uint8_t>(chi);
-        if (j == 0) *reinterpret_cast<float2*>(a.out.v_stats + (drow * hkv + h) * 2) = make_float2(mn, sc);
+      const u32x2_t wl = *reinterpret_cast<const u32x2_t*>(a.pool_k + src);
+      const u32x2_t wh = *reinterpret_cast<const u32x2_t*>(a.pool_k + src + half);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        lo[2 * i] = __uint_as_float(wl[i] << 16);
+        lo[2 * i + 1] = __uint_as_float(wl[i] & 0xffff0000u);
+        hi[2 * i] = __uint_as_float(wh[i] << 16);
+        hi[2 * i + 1] = __uint_as_float(wh[i] & 0xffff0000u);
       }
+    }
+  }
+  const float4 c4 = *reinterpret_cast<const float4*>(a.rope_cos + static_cast<int64_t>(ch.pos0) * half + j);
+  const float4 s4 = *reinterpret_cast<const float4*>(a.rope_sin + static_cast<int64_t>(ch.pos0) * half + j);
+  const float cv[4] = {c4.x, c4.y, c4.z, c4.w}, sv[4] = {s4.x, s4.y, s4.z, s4.w};
+  float rlo[4], rhi[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    rlo[i] = lo[i] * cv[i] - hi[i] * sv[i];
+    rhi[i] = hi[i] * cv[i] + lo[i] * sv[i];
+  }
+  uint32_t w_lo, w_hi;
+  float mn, sc;
+  encode8(rlo, rhi, gl, valid, w_lo, w_hi, mn, sc);
+  if (valid) {
+    *reinterpret_cast<uint32_t*>(a.out.k_codes + dst) = w_lo;
+    *reinterpret_cast<uint32_t*>(a.out.k_codes + dst + half) = w_hi;
+    if (lane_in == 0) *reinterpret_cast<float2*>(a.out.k_stats + (drow * hkv + h) * 2) = make_float2(mn, sc);
+  }
+  // values: 8-bit KIVI rows are copied, dense ones encoded
+  if constexpr (KB == 8) {
+    if (valid) {
+      *reinterpret_cast<uint32_t*>(a.out.v_codes + dst) = *reinterpret_cast<const uint32_t*>(a.v_codes + src);
+      *reinterpret_cast<uint32_t*>(a.out.v_codes + dst + half) =
+          *reinterpret_cast<const uint32_t*>(a.v_codes + src + half);
+      if (lane_in == 0)
+        *reinterpret_cast<float2*>(a.out.v_stats + (drow * hkv + h) * 2) =
+            make_float2(a.v_min[srow * hkv + h], a.v_scale[srow * hkv + h]);
+    }
+  } else {
+    float vlo[4] = {0.f, 0.f, 0.f, 0.f}, vhi[4] = {0.f, 0.f, 0.f, 0.f};
+    if (valid) {
+      const u32x2_t wl = *reinterpret_cast<const u32x2_t*>(a.pool_v + src);
+      const u32x2_t wh = *reinterpret_cast<const u32x2_t*>(a.pool_v + src + half);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        vlo[2 * i] = __uint_as_float(wl[i] << 16);
+        vlo[2 * i + 1] = __uint_as_float(wl[i] & 0xffff0000u);
+        vhi[2 * i] = __uint_as_float(wh[i] << 16);
+        vhi[2 * i + 1] = __uint_as_float(wh[i] & 0xffff0000u);
+      }
+    }
+    encode8(vlo, vhi, gl, valid, w_lo, w_hi, mn, sc);
+    if (valid) {
+      *reinterpret_cast<uint32_t*>(a.out.v_codes + dst) = w_lo;
+      *reinterpret_cast<uint32_t*>(a.out.v_codes + dst + half) = w_hi;
+      if (lane_in == 0) *reinterpret_cast<float2*>(a.out.v_stats + (drow * hkv + h) * 2) = make_float2(mn, sc);
     }
   }
 }
@@ -357,12 +410,14 @@ hipError_t launch_rerotate_q8(const kvf_layer_desc& L, const kvf_chunk* chunks, 
   a.out = fused;
   a.hkv = L.n_kv_heads;
   a.d = L.head_dim;
-  const dim3 grid(n_chunks, ceil_div(max_len, kQ8RotRows));
-  if (grid.y > 65535) return hipErrorInvalidValue;
+  const int ipb = kQ8RotWaves * kWave / (L.head_dim / 8);    // items per workgroup
+  const int64_t gy = (static_cast<int64_t>(max_len) * L.n_kv_heads + ipb - 1) / ipb;
+  if (gy > 65535) return hipErrorInvalidValue;
+  const dim3 grid(n_chunks, static_cast<unsigned>(gy));
   if (q)
-    hipLaunchKernelGGL((rerotate_q8_kernel<8>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((rerotate_q8_kernel<8>), grid, dim3(64 * kQ8RotWaves), 0, st, a);
   else
-    hipLaunchKernelGGL((rerotate_q8_kernel<0>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((rerotate_q8_kernel<0>), grid, dim3(64 * kQ8RotWaves), 0, st, a);
   return hipGetLastError();
 }
 

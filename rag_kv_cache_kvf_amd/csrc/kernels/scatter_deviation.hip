@@ -87,9 +87,10 @@ hipError_t launch_scatter(const kvf_layer_desc& L, const void* ks, const int32_t
   return hipGetLastError();
 }
 
-// S5 into an int8-resident fused cache: one wave per recomputed row; a group
-// of d/2 lanes encodes one kv head's row from channels (j, j + d/2) of lane j
-// (the layout of the int8-resident re-positioning kernel).
+// S5 into an int8-resident fused cache: work items are (recomputed row, kv
+// head, tensor), d/8 lanes each; a lane loads 8 consecutive bf16 values (16
+// bytes), the item's min/max is reduced over its lanes, and the lane stores
+// its 8 codes as one 8-byte word.
 struct ScatterQ8Args {
   const bf16_t* k_src;
   const int32_t* k_src_row;
@@ -104,46 +105,47 @@ struct ScatterQ8Args {
   int d;
 };
 
-// one row of one tensor: src row s -> codes/stats at dst (lanes of invalid
-// heads take part in the reductions only)
-__device__ __forceinline__ void encode_row_q8(const bf16_t* src, int64_t s, int64_t dst, int hkv,
-                                              int d, uint8_t* codes, float* stats) {
-  const int half = d >> 1;
-  const int lane = threadIdx.x & (kWave - 1);
-  const int j = lane & (half - 1);
-  for (int h0 = 0; h0 < hkv; h0 += kWave / half) {
-    const int h = h0 + lane / half;
-    const bool valid = h < hkv;
-    const int64_t so = (s * hkv + h) * d + j;
-    const float lo = valid ? bf16_to_f32(src[so]) : 0.f;
-    const float hi = valid ? bf16_to_f32(src[so + half]) : 0.f;
-    float mn = valid ? fminf(lo, hi) : INFINITY;
-    float mx = valid ? fmaxf(lo, hi) : -INFINITY;
-    group_minmax(mn, mx, half);
-    float sc, inv;
-    kivi_stats<8>(mn, mx, sc, inv);
-    if (valid) {
-      const int64_t dof = (dst * hkv + h) * d + j;
-      codes[dof] = static_cast<uint8_t>(kivi_code<8>(lo, mn, inv));
-      codes[dof + half] = static_cast<uint8_t>(kivi_code<8>(hi, mn, inv));
-      if (j == 0) *reinterpret_cast<float2*>(stats + (dst * hkv + h) * 2) = make_float2(mn, sc);
+__global__ void __launch_bounds__(256) scatter_q8_kernel(ScatterQ8Args a) {
+  const int gl = a.d >> 3;                         // lanes per item
+  const int64_t item = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) / gl;
+  const int lane_in = threadIdx.x & (gl - 1);
+  // item = (m * hkv + h) * 2 + tensor (0: K, 1: V)
+  const int tensor = static_cast<int>(item & 1);
+  const int64_t mh = item >> 1;
+  const int64_t m = mh / a.hkv;
+  const int h = static_cast<int>(mh - m * a.hkv);
+  const bf16_t* src = tensor ? a.v_src : a.k_src;
+  const int32_t* srow_map = tensor ? a.v_src_row : a.k_src_row;
+  const int64_t src_rows = tensor ? a.v_src_rows : a.k_src_rows;
+  bool valid = m < a.M && src != nullptr;
+  int64_t dst = 0, s = 0;
+  if (valid) {
+    dst = a.dst_row[m];
+    s = srow_map ? srow_map[m] : m;
+    valid = dst >= 0 && dst < a.out.rows && s >= 0 && s < src_rows;
+  }
+  float x[8];
+  float mn = INFINITY, mx = -INFINITY;
+  if (valid) {
+    Elem<bf16_t>::load8(src + (s * a.hkv + h) * a.d + 8 * lane_in, x);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      mn = fminf(mn, x[i]);
+      mx = fmaxf(mx, x[i]);
     }
   }
-}
-
-__global__ void __launch_bounds__(256) scatter_q8_kernel(ScatterQ8Args a) {
-  const int m = static_cast<int>((static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) / kWave);
-  if (m >= a.M) return;
-  const int64_t dst = a.dst_row[m];
-  if (dst < 0 || dst >= a.out.rows) return;
-  if (a.k_src) {
-    const int64_t s = a.k_src_row ? a.k_src_row[m] : m;
-    if (s >= 0 && s < a.k_src_rows) encode_row_q8(a.k_src, s, dst, a.hkv, a.d, a.out.k_codes, a.out.k_stats);
-  }
-  if (a.v_src) {
-    const int64_t s = a.v_src_row ? a.v_src_row[m] : m;
-    if (s >= 0 && s < a.v_src_rows) encode_row_q8(a.v_src, s, dst, a.hkv, a.d, a.out.v_codes, a.out.v_stats);
-  }
+  // every lane of the wave takes part in the reduction
+  group_minmax(mn, mx, gl);
+  if (!valid) return;
+  float sc, inv;
+  kivi_stats<8>(mn, mx, sc, inv);
+  u32x2_t w = {0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) w[i >> 2] |= kivi_code<8>(x[i], mn, inv) << (8 * (i & 3));
+  uint8_t* codes = tensor ? a.out.v_codes : a.out.k_codes;
+  float* stats = tensor ? a.out.v_stats : a.out.k_stats;
+  *reinterpret_cast<u32x2_t*>(codes + (dst * a.hkv + h) * a.d + 8 * lane_in) = w;
+  if (lane_in == 0) *reinterpret_cast<float2*>(stats + (dst * a.hkv + h) * 2) = make_float2(mn, sc);
 }
 
 hipError_t launch_scatter_q8(const kvf_layer_desc& L, const void* ks, const int32_t* ksr,
@@ -161,7 +163,10 @@ hipError_t launch_scatter_q8(const kvf_layer_desc& L, const void* ks, const int3
   a.out = fused;
   a.hkv = L.n_kv_heads;
   a.d = L.head_dim;
-  hipLaunchKernelGGL(scatter_q8_kernel, dim3(ceil_div(M, 256 / kWave)), dim3(256), 0, st, a);
+  const int64_t threads = static_cast<int64_t>(M) * L.n_kv_heads * 2 * (L.head_dim / 8);
+  const int64_t blocks = (threads + 255) / 256;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(scatter_q8_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
