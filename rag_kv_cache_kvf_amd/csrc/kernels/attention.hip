@@ -205,6 +205,7 @@ attn_mfma_kernel(AttnArgs a) {
   bf16_t* const v0s = kvs + 2 * TILE;
   bf16_t* const v1s = kvs + 3 * TILE;
   __shared__ int s_pos[2];
+  __shared__ int s_wpos[2 * kAWaves];   // per wave: max and min valid position
   // Q8: per key of the last four K tiles, (scale, min - 1024 scale) times
   // the score scale; slot = tile & 3
   __shared__ __attribute__((aligned(16))) float kab[Q8 ? 4 * 2 * kAT : 4];
@@ -235,6 +236,8 @@ attn_mfma_kernel(AttnArgs a) {
   int pos[kQB], row_l[kQB], h[kQB];
   int64_t qrow[kQB];
   bool valid[kQB];
+  const bf16_t* Q = static_cast<const bf16_t*>(a.q);
+  bf16x8_t qraw[kQB][KS];
 #pragma unroll
   for (int qb = 0; qb < kQB; ++qb) {
     const int qv = 32 * (kQB * w + qb) + c;
@@ -247,24 +250,49 @@ attn_mfma_kernel(AttnArgs a) {
     if (valid[qb]) {
       int p = a.q_pos ? a.q_pos[qrow[qb]] : a.pos0[r] + lrow0 + row_l[qb];
       pos[qb] = (p < 0 || p >= T) ? -1 : p;
-    }
-  }
-  if (tid == 0) {
-    s_pos[0] = -1;                 // max position
-    s_pos[1] = 0x7fffffff;         // min position
-  }
-  __syncthreads();
+      // the query loads go out before the position scan, so that their
+      // latency overlaps it (rows skipped by position are zeroed after it)
 #pragma unroll
-  for (int qb = 0; qb < kQB; ++qb) {
-    if (pos[qb] >= 0) {
-      atomicMax(&s_pos[0], pos[qb]);
-      atomicMin(&s_pos[1], pos[qb]);
+      for (int ks = 0; ks < KS; ++ks)
+        qraw[qb][ks] = *reinterpret_cast<const bf16x8_t*>(Q + (qrow[qb] * a.hq + h[qb]) * D + ks * 16 + hf * 8);
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qraw[qb][ks][e] = static_cast<__bf16>(0.f);
+    }
+  }
+  // Largest and smallest valid position of the tile: reduced within each
+  // wave, one LDS slot per wave (atomics from every lane onto two words
+  // would serialise: 4-7 us per workgroup).
+  {
+    int pmx = -1, pmn = 0x7fffffff;
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb)
+      if (pos[qb] >= 0) {
+        pmx = max(pmx, pos[qb]);
+        pmn = min(pmn, pos[qb]);
+      }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      pmx = max(pmx, __shfl_xor(pmx, o, kWave));
+      pmn = min(pmn, __shfl_xor(pmn, o, kWave));
+    }
+    if (lane == 0) {
+      s_wpos[2 * w] = pmx;
+      s_wpos[2 * w + 1] = pmn;
     }
   }
   __syncthreads();
+  int pmx_all = -1, pmn_all = 0x7fffffff;
+#pragma unroll
+  for (int i = 0; i < kAWaves; ++i) {
+    pmx_all = max(pmx_all, s_wpos[2 * i]);
+    pmn_all = min(pmn_all, s_wpos[2 * i + 1]);
+  }
   // (uniform values: read once into scalar registers)
-  const int klim = __builtin_amdgcn_readfirstlane(s_pos[0] + 1);   // keys [0, klim) are visible to someone
-  const int pmin = __builtin_amdgcn_readfirstlane(s_pos[1]);       // keys <= pmin are visible to everyone
+  const int klim = __builtin_amdgcn_readfirstlane(pmx_all + 1);   // keys [0, klim) are visible to someone
+  const int pmin = __builtin_amdgcn_readfirstlane(pmn_all);       // keys <= pmin are visible to everyone
   const int n = klim > 0 ? ceil_div(klim, kAT) : 0;
   // leading tiles that every row sees completely need no mask
   const int n_plain = klim > 0 ? min(n, (pmin + 1) / kAT) : 0;
@@ -272,19 +300,21 @@ attn_mfma_kernel(AttnArgs a) {
   // (at most a.parts); part p takes key tiles [p n / np, (p + 1) n / np) and
   // whichever part finishes last merges every part's (m, l, O) and writes.
   const int np = a.parts > 1 ? max(1, min(a.parts, n / a.split_min)) : 1;
-  if (part >= np) return;                         // whole workgroup: s_pos is uniform
+  if (part >= np) {                               // whole workgroup: the scan is uniform
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the query loads land before the wave ends
+    return;
+  }
   const bool split = np > 1;
   const int t0 = part * n / np;
   const int t1 = (part + 1) * n / np;
 
-  const bf16_t* Q = static_cast<const bf16_t*>(a.q);
   OpT qf[kQB][KS];
 #pragma unroll
   for (int qb = 0; qb < kQB; ++qb)
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       if (pos[qb] >= 0) {
-        const bf16x8_t qv = *reinterpret_cast<const bf16x8_t*>(Q + (qrow[qb] * a.hq + h[qb]) * D + ks * 16 + hf * 8);
+        const bf16x8_t qv = qraw[qb][ks];
         if constexpr (Q8) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) qf[qb][ks][e] = static_cast<_Float16>(static_cast<float>(qv[e]));
@@ -606,22 +636,34 @@ attn_mfma_kernel(AttnArgs a) {
                        uint32_t (&pkc)[kQB][8]) __attribute__((always_inline)) {
     if constexpr (Q8) key_affine(sc, kb0);
     if (masked) apply_mask(sc, kb0);
-    scores(kt, kbs, sn);
     catch_up();
+    // From here one branch-free stretch: the score MFMAs of b+1 and the V
+    // MFMAs of b-1 beside the softmax of b, so the scheduler can interleave
+    // them (the raise of the running max is a select, not a branch).
+    scores(kt, kbs, sn);
     pv(vt, kbp, pkp);
     float bm[kQB], lb[kQB];
     block_max(sc, bm);
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb) {
-      if (bm[qb] > m_run[qb] + kRaise) {
-        alpha_pend[qb] = __builtin_amdgcn_exp2f(m_run[qb] - bm[qb]);   // m_run = -inf: 0 (O, l are 0)
-        l_lane[qb] *= alpha_pend[qb];
-        m_run[qb] = bm[qb];
-      }
+      const bool up = bm[qb] > m_run[qb] + kRaise;
+      const float al = __builtin_amdgcn_exp2f(m_run[qb] - bm[qb]);   // m_run = -inf: 0 (O, l are 0)
+      alpha_pend[qb] = up ? al : 1.f;
+      l_lane[qb] *= alpha_pend[qb];
+      m_run[qb] = up ? bm[qb] : m_run[qb];
     }
     probs(sc, pkc, lb);
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb) l_lane[qb] += lb[qb];
+    // Keep this block's softmax in this half step: without these uses the
+    // compiler sinks it past the barrier into the next half step, which then
+    // holds two blocks' softmax while this one holds only MFMAs.
+#pragma unroll
+    for (int qb = 0; qb < kQB; ++qb) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) asm volatile("" ::"v"(pkc[qb][i]));
+      asm volatile("" ::"v"(l_lane[qb]), "v"(m_run[qb]), "v"(alpha_pend[qb]));
+    }
   };
   // tile t: kc holds K_t, kn K_{t+1}; vc holds V_t, vp V_{t-1}
   auto tile_step = [&](int t, bf16_t* kc, const bf16_t* kn, const bf16_t* vc, bf16_t* vp)
