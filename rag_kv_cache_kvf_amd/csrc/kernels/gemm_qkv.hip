@@ -47,6 +47,7 @@ struct GemmArgs {
   // output (kv_rows rows; entries outside are skipped); nullptr: row m
   const int32_t* kv_row;
   int64_t kv_rows;
+  int group_rows;           // row tiles per group of the dispatch order (xcd_tile)
 };
 
 // Output row of row m in segment seg (0 Q, 1 K, 2 V), or -1 to skip it.
@@ -66,18 +67,26 @@ __device__ __forceinline__ bool row_ok(const GemmArgs& a, int m) {
 
 // Hardware hands workgroups to the 8 XCDs round-robin by linear id, and
 // each XCD has its own L2.  Renumber so that XCD x runs one contiguous range
-// of logical tiles: with the row tile varying fastest, the row tiles of a
-// column tile (which share its weight slab) then share one L2, and W is
-// fetched from HBM about once instead of once per XCD.
-__device__ __forceinline__ void xcd_tile(int& tx, int& ty, int& tz) {
+// of logical tiles, and order the logical tiles in groups of `gr` row tiles:
+// within a group the row tile varies fastest, then the column tile.  The
+// tiles an XCD holds at once then form a block of about gr rows by
+// (resident tiles / gr) columns, whose X row panels and W column slabs are
+// each fetched into that XCD's L2 once and shared by the block's tiles.
+// gr = all row tiles gives whole column slabs (one W slab, every X panel).
+__device__ __forceinline__ void xcd_tile(int gr, int& tx, int& ty, int& tz) {
   const int gx = gridDim.x, gy = gridDim.y;
   const int n = gx * gy * gridDim.z;
   const int b = blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z);
   const int q = n >> 3, r = n & 7, x = b & 7;
   const int l = x * q + min(x, r) + (b >> 3);
-  tx = l % gx;
-  ty = (l / gx) % gy;
-  tz = l / (gx * gy);
+  const int per_z = gx * gy;
+  tz = l / per_z;
+  const int lt = l - tz * per_z;
+  const int grp = lt / (gr * gy);
+  const int i = lt - grp * gr * gy;
+  const int rows = min(gr, gx - grp * gr);   // the last group may be shorter
+  ty = i / rows;
+  tx = grp * gr + (i - ty * rows);
 }
 
 __device__ __forceinline__ int segment_of(const int (&n_tiles)[3], int& t) {
@@ -202,7 +211,7 @@ gemm_qkv_bf16_kernel(GemmArgs a) {
   };
 
   int tx, t, kz;
-  xcd_tile(tx, t, kz);
+  xcd_tile(a.group_rows, tx, t, kz);
   const int tile_id = tx + static_cast<int>(gridDim.x) * t;   // output tile (row tile fastest)
   const int seg = segment_of(a.n_tiles, t);
   const int n0 = t * BN;                    // first column inside the segment
@@ -664,6 +673,37 @@ Bf16Plan plan_bf16(const kvf_layer_desc& L, int M, uint32_t mask) {
   return q;                                // smaller tiles, split or not: more workgroups than p
 }
 
+// Rows per group of the dispatch order (xcd_tile).  The tiles one XCD holds
+// at once (one workgroup per CU, at most its share of the grid: `resident`
+// consecutive logical tiles) span some row tiles and column tiles, whose
+// operands it fetches: bm rows of X per row tile and bn rows of W per column
+// tile, per k.  Pick the gr with the fewest, ties to the taller group.
+int group_rows(int nrow, int ncol, int bm, int bn) {
+  const int64_t tiles = static_cast<int64_t>(nrow) * ncol;
+  const int resident = static_cast<int>(std::min<int64_t>(kCUs / 8, (tiles + 7) / 8));
+  int best = nrow;
+  int64_t best_cost = INT64_MAX;
+  for (int gr = nrow; gr >= 1; --gr) {
+    int rows, cols;
+    if (resident <= gr) {                       // part of one column of a group
+      rows = resident;
+      cols = 1;
+    } else if (resident <= gr * ncol) {         // gr rows, a few columns
+      rows = gr;
+      cols = ceil_div(resident, gr);
+    } else {                                    // whole groups: every column
+      rows = ceil_div(resident, ncol);
+      cols = ncol;
+    }
+    const int64_t cost = static_cast<int64_t>(rows) * bm + static_cast<int64_t>(cols) * bn;
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = gr;
+    }
+  }
+  return best;
+}
+
 }  // namespace
 
 // Split-K workspace: kSplitCounterBytes of arrival counters (one int per
@@ -731,6 +771,7 @@ hipError_t launch_recompute(const kvf_layer_desc& L, const void* x, int64_t x_ro
       a.k_len = L.hidden / p.splits;
     }
     const dim3 grid(ceil_div(M, p.bm), total, p.splits);
+    a.group_rows = group_rows(static_cast<int>(grid.x), total, p.bm, p.bn);
     bool launched = false;
     const bool split = p.splits > 1;
 #define KVF_GEMM_CASE(BM_, BN_, WM_, SPLIT_)                                                  \
