@@ -15,10 +15,11 @@ re-positions the keys only).  The metric is fused context tokens per second
 per layer: (sum over requests of N) / step time.
 
 Timing, after W warm-up steps:
-  1. K steps, each after an untimed read-modify-write of a 1 GiB buffer
-     (which evicts the working set from the L2 caches and the Infinity
-     Cache), each timed by HIP events on the launch stream: `value` and
-     `ms_per_step` use the median, `timing` also gives p10 and p90;
+  1. K steps, each after an untimed read of a 1 GiB buffer (which evicts
+     the working set from the L2 caches and the Infinity Cache and leaves
+     clean lines), each timed by HIP events on the launch stream: `value`
+     and `ms_per_step` use the median, `timing` also gives p10 and p90, and
+     the median after a read-modify-write flush instead (dirty lines);
   2. K steps back to back (warm caches), for comparison;
   3. K flushed steps with every library call bracketed by HIP events: each
      call's average duration and its roofline fraction (algorithmic bytes or
@@ -162,14 +163,21 @@ def call_work(g):
 FLUSH_BYTES = 1 << 30
 
 
-def _flusher():
-    """A 1 GiB buffer whose read-modify-write before every timed step evicts
-    the step's working set from the L2 caches and the 256 MB Infinity Cache."""
+def _flusher(write=False):
+    """A 1 GiB buffer swept before every timed step, which evicts the step's
+    working set from the L2 caches and the 256 MB Infinity Cache.  The sweep
+    reads the buffer (a sum), so the lines it leaves behind are clean; with
+    write=True it is a read-modify-write instead, which leaves hundreds of MB
+    of dirty lines whose write-back then competes with the step's own reads
+    (a 50 MB weight read takes about twice as long after it)."""
     import torch
-    buf = torch.zeros(FLUSH_BYTES // 4, dtype=torch.int32, device="cuda")
+    buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.int32, device="cuda")
 
     def flush():
-        buf.add_(1)
+        if write:
+            buf.add_(1)
+        else:
+            buf.sum()
     return flush
 
 
@@ -632,6 +640,7 @@ def measure(wl, ratio, steps, warmup, flush, graph=False):
     torch.cuda.synchronize()
 
     times, wall = _timed_steps(step, steps, flush)
+    times_dirty, _ = _timed_steps(step, steps, _flusher(write=True))
     warm = _timed_back_to_back(step, steps)
     per_call = _timed_per_call(g, steps, flush)
     per_call_warm = _timed_per_call(g, steps, None)
@@ -665,10 +674,12 @@ def measure(wl, ratio, steps, warmup, flush, graph=False):
                 "frac": c["frac"], "avg_ms": c["ms"], "algorithmic_per_launch": float(amount),
                 "traffic": _traffic(kname, ksrc, wl.name)}
     timing = {"protocol": f"{steps} steps timed one by one with HIP events on the launch stream, "
-                          f"each after an untimed read-modify-write of {FLUSH_BYTES >> 30} GiB "
-                          "(evicts L2 and the Infinity Cache); value = context tokens / median",
+                          f"each after an untimed read of {FLUSH_BYTES >> 30} GiB "
+                          "(evicts L2 and the Infinity Cache, leaves clean lines); "
+                          "value = context tokens / median",
               "ms_median": round(med, 5), "ms_p10": round(_pct(times, 10), 5),
               "ms_p90": round(_pct(times, 90), 5), "flush_bytes": FLUSH_BYTES,
+              "ms_median_after_write_flush": round(_pct(times_dirty, 50), 5),
               "loop_wall_s": round(wall, 4),
               "ms_per_step_back_to_back": round(warm * 1e3, 5),
               "graph": bool(graph)}
