@@ -1190,6 +1190,9 @@ __global__ void __launch_bounds__(256) mass_stats_bf16_kernel(MassArgs a) {
     }
     return;
   }
+  // every key of the chunk is visible to every used query vector (their
+  // positions are pos0, pos0 + 1, ..): no mask
+  const bool full = key0 + kMK <= min(a.pos0[r] + 1, T);
   // this wave's 32 keys as the A operand: row = key, k = 8 hf + e
   const bf16_t* Kg = static_cast<const bf16_t*>(a.k);
   const int key_a = key0 + 32 * w + c;
@@ -1253,20 +1256,26 @@ __global__ void __launch_bounds__(256) mass_stats_bf16_kernel(MassArgs a) {
       for (int j = 0; j < 4; ++j) {
         // lane c: query vector qs + b0 + 32 j + c; keys key0 + 32 w + 8 (i/4) + 4 hf + (i%4)
         const int qv = qs + b0 + 32 * j + c;
-        const int pos = a.pos0[r] + qv / a.G;
-        const int lim = min(pos, T - 1) - (key0 + 32 * w + 4 * hf);
+        // raw scores: the max commutes with the positive scale, which goes
+        // into the exponent's multiply-add
         float sv[16];
-        float m = -INFINITY;
+        if (full) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          sv[i] = 8 * (i >> 2) + (i & 3) <= lim ? s[j][i] * cs : -INFINITY;
-          m = fmaxf(m, sv[i]);
+          for (int i = 0; i < 16; ++i) sv[i] = s[j][i];
+        } else {
+          const int pos = a.pos0[r] + qv / a.G;
+          const int lim = min(pos, T - 1) - (key0 + 32 * w + 4 * hf);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) sv[i] = 8 * (i >> 2) + (i & 3) <= lim ? s[j][i] : -INFINITY;
         }
-        m = fmaxf(m, __shfl_xor(m, 32, kWave));
+        float m = sv[0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) m = fmaxf(m, sv[i]);
+        m = fmaxf(m, __shfl_xor(m, 32, kWave)) * cs;
         float l = 0.f;
         if (m > -INFINITY) {
 #pragma unroll
-          for (int i = 0; i < 16; ++i) l += __builtin_amdgcn_exp2f(sv[i] - m);
+          for (int i = 0; i < 16; ++i) l += __builtin_amdgcn_exp2f(fmaf(sv[i], cs, -m));
         }
         l += __shfl_xor(l, 32, kWave);
         if (hf == 0) st[w][b0 + 32 * j + c] = make_float2(m, l);

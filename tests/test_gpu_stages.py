@@ -368,6 +368,7 @@ RECOMP_CASES = [
     ("bf16", 1024, 8, 2, 128, 100, 40, 7),      # K split in 4 slices, 64-row tile
     ("bf16", 2048, 8, 4, 64, 50, 1, 3),         # one row, K split
     ("bf16", 512, 16, 8, 128, 2100, 2050, 7),   # many rows, 256-wide column tile
+    ("bf16", 320, 32, 8, 128, 6000, 5641, 7),   # 36 x 24 tiles in groups of rows, ragged last row tile
     ("f32", 256, 4, 4, 64, 300, 108, 7),
     ("f32", 128, 4, 2, 64, 90, 45, 6),
 ]
