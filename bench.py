@@ -171,11 +171,13 @@ def _flusher(write=False):
     of dirty lines whose write-back then competes with the step's own reads
     (a 50 MB weight read takes about twice as long after it)."""
     import torch
-    buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.int32, device="cuda")
+    # float32: its sum is a single reduction over the buffer (an int32 sum
+    # would first widen the whole buffer to int64, writing 2 GiB)
+    buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
 
     def flush():
         if write:
-            buf.add_(1)
+            buf.add_(1.0)
         else:
             buf.sum()
     return flush
