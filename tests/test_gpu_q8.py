@@ -249,6 +249,59 @@ def test_attention_q8(kvf, case):
         assert_close(gl, np.concatenate(lses), "bf16", tag + " lse", tol=1e-3)
 
 
+def test_attention_q8_degenerate(kvf):
+    """Degenerate rows of an int8-resident cache: constant key and value rows
+    (scale 0: every code 0, the row is its minimum), all-zero rows (the
+    format of rows no chunk covers: statistics (0, 0)), a key row whose
+    affine map is 0 * q + min * sum(q), and queries at positions 0 and 1
+    (one or two visible keys).  The kernel's exact-key path must match the
+    oracle over the decoded cache; unsplit and split runs alike."""
+    import torch
+    hq, hkv, d = 8, 2, 128
+    Ts, Ms = [700, 64], [150, 64]
+    cu_T = np.concatenate([[0], np.cumsum(Ts)]).astype(int).tolist()
+    cu_q = np.concatenate([[0], np.cumsum(Ms)]).astype(int).tolist()
+    T = cu_T[-1]
+    K = synth.random_normal((T, hkv, d), 51, "q8d_k").astype(np.float64)
+    V = synth.random_normal((T, hkv, d), 51, "q8d_v").astype(np.float64)
+    K[0:100] = np.linspace(-2, 2, 100)[:, None, None]          # constant rows
+    V[50:150] = np.linspace(3, -1, 100)[:, None, None]
+    K[200:210] = 0.0
+    V[200:210] = 0.0
+    K[700:710] = 0.0                                             # start of request 1
+    cache = q8cache.Cache(*q8cache.encode(K), *q8cache.encode(V))
+    assert np.all(cache.k_stats[0:100, :, 1] == 0) and np.all(cache.k_codes[0:100] == 0)
+    cache.k_stats[200:210] = 0.0                                 # uncovered-row format
+    cache.v_stats[200:210] = 0.0
+    forced = [0, 1, 2, 99, 100, 205, 699]
+    rest = np.setdiff1d(synth.random_rows(700, 400, 52), forced)
+    pos0 = np.sort(np.concatenate([forced, rest[:Ms[0] - len(forced)]]))
+    assert len(pos0) == Ms[0] and len(np.unique(pos0)) == Ms[0]
+    pos = np.concatenate([pos0, np.arange(64)]).astype(np.int32)
+    q_s = encode(synth.random_normal((cu_q[-1], hq, d), 53, "q8d_q", 4.0), "bf16")
+    L = kvf.Layer(256, hq, hkv, d, "bf16")
+    kb = kvf.Batch(cu_T, list(Ts))
+    g = _upload(cache)
+    need = kvf.attention_workspace_size(L, kb, cu_q)
+    ws = torch.zeros(max(need, 1), dtype=torch.uint8, device="cuda") if need > 0 else None
+    lo = fusion.Layer(256, hq, hkv, d, 1e4)
+    dk, dv, dq = q8cache.decode_k(cache), q8cache.decode_v(cache), decode(q_s, "bf16")
+    refs, lses = [], []
+    for r in range(len(Ts)):
+        o, l = fusion.causal_attention(dq[cu_q[r]:cu_q[r + 1]], pos[cu_q[r]:cu_q[r + 1]],
+                                       dk[cu_T[r]:cu_T[r + 1]], dv[cu_T[r]:cu_T[r + 1]], lo)
+        refs.append(o)
+        lses.append(l)
+    for i, w in enumerate([None] + ([ws] if ws is not None else [])):
+        out = torch.zeros((cu_q[-1], hq, d), dtype=torch.bfloat16, device="cuda")
+        lse = torch.zeros((cu_q[-1], hq), dtype=torch.float32, device="cuda")
+        kvf.sparse_q_attention_q8(L, kb, to_gpu(q_s, "bf16"), to_gpu(pos), cu_q, g, 1 / math.sqrt(d),
+                                  out, lse, workspace=w)
+        tag = f"attention_q8 degenerate run {i}"
+        assert_close_vectors(from_gpu(out), np.concatenate(refs), "bf16", tag)
+        assert_close(from_gpu(lse), np.concatenate(lses), "bf16", tag + " lse", tol=1e-3)
+
+
 def test_attention_q8_full_size_sampled(kvf):
     """The Qwen2.5-3B-shaped workload (16 requests of 24 x 128 context + 64
     query tokens, 15% recomputed) with its workspace, sampled rows."""
