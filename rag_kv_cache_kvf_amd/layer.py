@@ -203,9 +203,15 @@ class FusedLayerGPU:
         self.out = torch.zeros((max(M, 1), hq, d), dtype=td, device=dev)
         self.lse = torch.zeros((max(M, 1), hq), dtype=torch.float32, device=dev)
         self.sm_scale = 1.0 / math.sqrt(d)
-        self.u_rows = _i32(batch.query_rows(), dev)
+        u_host = np.asarray(batch.query_rows(), dtype=np.int64)
+        self.u_rows = _i32(u_host, dev)
         self.u_pos = _i32(batch.query_pos(), dev)
         nU = int(self.u_rows.shape[0])
+        # one block of consecutive rows (a single request): the probe reads
+        # that slice of x directly, without a row map to gather through
+        self.u_span = None
+        if nU > 0 and np.all(np.diff(u_host) == 1):
+            self.u_span = (int(u_host[0]), int(u_host[0]) + nU)
         self.ws = None
         if self.probe:
             self.all_pos = _i32(batch.all_pos(), dev)
@@ -257,6 +263,12 @@ class FusedLayerGPU:
                                  self.rope_cos, self.rope_sin, k_out=self.k_probe, workspace=self.gemm_ws)
 
     def _u_probe(self):
+        if self.u_span is not None:
+            a, b = self.u_span
+            return kvf.recompute_qkv(self.layer, self.x[a:b], None, self.u_pos, self.w,
+                                     kvf.KVF_OUT_Q | kvf.KVF_OUT_K | kvf.KVF_OUT_V, self.rope_cos,
+                                     self.rope_sin, q_out=self.q_u, k_out=self.fused_k, v_out=self.fused_v,
+                                     kv_out_row=self.u_rows, workspace=self.gemm_ws)
         return kvf.recompute_qkv(self.layer, self.x, self.u_rows, self.u_pos, self.w,
                                  kvf.KVF_OUT_Q | kvf.KVF_OUT_K | kvf.KVF_OUT_V, self.rope_cos,
                                  self.rope_sin, q_out=self.q_u, k_out=self.fused_k, v_out=self.fused_v,
