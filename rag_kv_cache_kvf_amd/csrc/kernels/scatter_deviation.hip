@@ -237,28 +237,106 @@ __global__ void __launch_bounds__(256) deviation_kernel(BatchArgs B, KR fk,
   if (lane == 0) store_score(out, wave, 1.f - cos_acc / static_cast<float>(hkv));
 }
 
+// Narrow rows: a row of Hkv d <= 256 elements (8 per lane) fills
+// LPT = Hkv d / 8 lanes (a power of two), and 64 / LPT tokens share a wave
+// instead of leaving its other lanes idle (Hkv = 2, d = 128: two per wave).
+template <typename T, typename KR, int LPT>
+__global__ void __launch_bounds__(256) deviation_packed_kernel(BatchArgs B, KR fk,
+                                                        const T* __restrict__ kf, int hkv, int d,
+                                                        ScoreOut out) {
+  constexpr int TPW = kWave / LPT;              // tokens per wave
+  const int wave = (blockIdx.x * blockDim.x + threadIdx.x) / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int sub = lane & (LPT - 1);
+  const int total = B.cu_N[B.n_req];
+  if (static_cast<int64_t>(wave) * TPW >= total) return;     // the whole wave
+  const int tok = wave * TPW + lane / LPT;
+  // lanes of a token past the end or not eligible load nothing, but take
+  // part in the shuffles (with zeros) like every other lane of the wave
+  const bool live = tok < total && score_eligible(out, tok);
+  int64_t row = 0;
+  if (live) {
+    const int r = find_segment(B.cu_N, B.n_req, tok);
+    row = B.cu_T[r] + (tok - B.cu_N[r]);
+  }
+  const int row_elems = hkv * d;
+  const int lanes_per_head = d >> 3;           // 8 elements per lane
+  const T* b = kf + row * row_elems;
+  float cos_acc = 0.f;
+  for (int e0 = sub * 8; e0 < row_elems; e0 += LPT * 8) {
+    float x[8], y[8];
+    if (live) {
+      fk.load8(row, row_elems, e0, x);
+      Elem<T>::load8(b + e0, y);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] = y[i] = 0.f;
+    }
+    float dot = 0.f, nx = 0.f, ny = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      dot = fmaf(x[i], y[i], dot);
+      nx = fmaf(x[i], x[i], nx);
+      ny = fmaf(y[i], y[i], ny);
+    }
+    dot = group_sum(dot, lanes_per_head);
+    nx = group_sum(nx, lanes_per_head);
+    ny = group_sum(ny, lanes_per_head);
+    const float den = sqrtf(nx) * sqrtf(ny);
+    if ((sub & (lanes_per_head - 1)) == 0 && den > 0.f) cos_acc += dot / den;
+  }
+  // lanes past the row end still take part in the shuffles above with zeros
+  cos_acc = group_sum(cos_acc, LPT);
+  if (sub == 0 && tok < total) store_score(out, tok, live ? 1.f - cos_acc / static_cast<float>(hkv) : 0.f);
+}
+
+// Lanes per token for a row of `row_elems` elements (see deviation_packed_kernel).
+static int deviation_lanes(int row_elems) {
+  const int l = row_elems / 8;
+  return (row_elems % 8 == 0 && l <= 32 && (l & (l - 1)) == 0 && l >= 8) ? l : kWave;
+}
+
+template <typename T, typename KR>
+static void launch_deviation_lanes(const BatchArgs& B, KR fk, const T* kf, int hkv, int d,
+                                   const ScoreOut& out, hipStream_t st) {
+  const int total = B.cu_N[B.n_req];
+  const int lpt = deviation_lanes(hkv * d);
+  const int waves = ceil_div(total, kWave / lpt);
+  const int blocks = ceil_div(waves, 256 / kWave);
+  switch (lpt) {
+    case 8:
+      hipLaunchKernelGGL((deviation_packed_kernel<T, KR, 8>), dim3(blocks), dim3(256), 0, st, B, fk, kf, hkv, d, out);
+      break;
+    case 16:
+      hipLaunchKernelGGL((deviation_packed_kernel<T, KR, 16>), dim3(blocks), dim3(256), 0, st, B, fk, kf, hkv, d,
+                         out);
+      break;
+    case 32:
+      hipLaunchKernelGGL((deviation_packed_kernel<T, KR, 32>), dim3(blocks), dim3(256), 0, st, B, fk, kf, hkv, d,
+                         out);
+      break;
+    default:                                   // one wave per token
+      hipLaunchKernelGGL((deviation_kernel<T, KR>), dim3(blocks), dim3(256), 0, st, B, fk, kf, hkv, d, out);
+  }
+}
+
 hipError_t launch_deviation(const kvf_layer_desc& L, const BatchArgs& B, const void* fk,
                             const void* kf, const ScoreOut& out, hipStream_t st) {
-  const int total = B.cu_N[B.n_req];
-  const int blocks = ceil_div(total, 256 / kWave);
+  if (B.cu_N[B.n_req] == 0) return hipGetLastError();
   if (L.dtype == KVF_BF16)
-    hipLaunchKernelGGL((deviation_kernel<bf16_t, KeyRow<bf16_t>>), dim3(blocks), dim3(256), 0, st, B,
-                       KeyRow<bf16_t>{static_cast<const bf16_t*>(fk)}, static_cast<const bf16_t*>(kf),
-                       L.n_kv_heads, L.head_dim, out);
+    launch_deviation_lanes<bf16_t>(B, KeyRow<bf16_t>{static_cast<const bf16_t*>(fk)},
+                                   static_cast<const bf16_t*>(kf), L.n_kv_heads, L.head_dim, out, st);
   else
-    hipLaunchKernelGGL((deviation_kernel<float, KeyRow<float>>), dim3(blocks), dim3(256), 0, st, B,
-                       KeyRow<float>{static_cast<const float*>(fk)}, static_cast<const float*>(kf),
-                       L.n_kv_heads, L.head_dim, out);
+    launch_deviation_lanes<float>(B, KeyRow<float>{static_cast<const float*>(fk)},
+                                  static_cast<const float*>(kf), L.n_kv_heads, L.head_dim, out, st);
   return hipGetLastError();
 }
 
 hipError_t launch_deviation_q8(const kvf_layer_desc& L, const BatchArgs& B, const kvf_q8_cache& c,
                                const void* kf, const ScoreOut& out, hipStream_t st) {
-  const int total = B.cu_N[B.n_req];
-  const int blocks = ceil_div(total, 256 / kWave);
-  hipLaunchKernelGGL((deviation_kernel<bf16_t, KeyRow<uint8_t>>), dim3(blocks), dim3(256), 0, st, B,
-                     KeyRow<uint8_t>{c.k_codes, c.k_stats, L.head_dim}, static_cast<const bf16_t*>(kf),
-                     L.n_kv_heads, L.head_dim, out);
+  if (B.cu_N[B.n_req] == 0) return hipGetLastError();
+  launch_deviation_lanes<bf16_t>(B, KeyRow<uint8_t>{c.k_codes, c.k_stats, L.head_dim},
+                                 static_cast<const bf16_t*>(kf), L.n_kv_heads, L.head_dim, out, st);
   return hipGetLastError();
 }
 
