@@ -15,6 +15,8 @@
 // fetched once per tile.  In keys-only mode the values were stitched by the
 // loader and are not touched; the keys may be rotated in place (a thread
 // reads the 16 channels of a rotation pair set before it writes them).
+#include <algorithm>
+
 #include "../kvf_common.h"
 
 namespace kvf {
@@ -49,7 +51,7 @@ hipError_t launch_rope_table(double base, int d, int n_pos, float* c, float* s, 
 // ---------------------------------------------------------------------------
 // S1: re-position and stitch
 // ---------------------------------------------------------------------------
-constexpr int kRotRows = 8;       // tokens per workgroup tile
+constexpr int kRotRows = 8;       // tokens per workgroup tile (at least; see rot_rows)
 
 struct RotArgs {
   const kvf_chunk* chunks;
@@ -72,7 +74,16 @@ struct RotArgs {
   int hkv;
   int d;
   int k_only;                     // keys only: values are already in place
+  int rows;                       // tokens per workgroup tile
 };
+
+// Tokens per workgroup tile: kRotRows, or more when a token's key has too
+// few rotation units (Hkv d / 16) for the tile to give each of the 256
+// threads one (narrow rows: Hkv = 2, d = 128 takes 16 tokens).
+static int rot_rows(int hkv, int d) {
+  const int ku = std::max(1, hkv * d / 16);
+  return std::max(kRotRows, ceil_div(256, ku));
+}
 
 // the 8 codes of channels e..e+7 (e a multiple of 8), `codes` pointing at
 // their first byte: 8 bytes for b = 8, 4 bytes for b = 4 (channel i of the
@@ -110,7 +121,7 @@ template <typename T, int KB>
 __global__ void __launch_bounds__(256) rerotate_kernel(RotArgs a) {
   constexpr bool KIVI = KB != 0;
   const kvf_chunk ch = a.chunks[blockIdx.x];
-  const int t0 = blockIdx.y * kRotRows;
+  const int t0 = blockIdx.y * a.rows;
   if (ch.len <= 0 || t0 >= ch.len) return;
   // skip malformed descriptors instead of touching memory outside the buffers
   if (ch.src_row < 0 || static_cast<int64_t>(ch.src_row) + ch.len > a.pool_rows) return;
@@ -120,7 +131,7 @@ __global__ void __launch_bounds__(256) rerotate_kernel(RotArgs a) {
 
   const int d = a.d, half = d >> 1, hkv = a.hkv;
   const int row_elems = hkv * d;
-  const int nrows = min(kRotRows, ch.len - t0);
+  const int nrows = min(a.rows, ch.len - t0);
   const float* cosr = a.rope_cos + static_cast<int64_t>(ch.pos0) * half;
   const float* sinr = a.rope_sin + static_cast<int64_t>(ch.pos0) * half;
   T* fk = static_cast<T*>(a.fused_k);
@@ -209,7 +220,8 @@ hipError_t launch_rerotate(const kvf_layer_desc& L, const kvf_chunk* chunks, int
   a.hkv = L.n_kv_heads;
   a.d = L.head_dim;
   a.k_only = k_only;
-  const dim3 grid(n_chunks, ceil_div(max_len, kRotRows));
+  a.rows = rot_rows(a.hkv, a.d);
+  const dim3 grid(n_chunks, ceil_div(max_len, a.rows));
   if (grid.y > 65535) return hipErrorInvalidValue;
   if (q && q->bits == 4)
     hipLaunchKernelGGL((rerotate_kernel<bf16_t, 4>), grid, dim3(256), 0, st, a);
