@@ -80,9 +80,11 @@ struct RotArgs {
 // Tokens per workgroup tile: kRotRows, or more when a token's key has too
 // few rotation units (Hkv d / 16) for the tile to give each of the 256
 // threads one (narrow rows: Hkv = 2, d = 128 takes 16 tokens).
-static int rot_rows(int hkv, int d) {
+static int rot_rows(int hkv, int d, bool kivi) {
   const int ku = std::max(1, hkv * d / 16);
-  return std::max(kRotRows, ceil_div(256, ku));
+  const int rows = std::max(kRotRows, ceil_div(256, ku));
+  // KIVI: each thread reuses its unit's statistics over 4 rows
+  return kivi ? 4 * rows : rows;
 }
 
 // the 8 codes of channels e..e+7 (e a multiple of 8), `codes` pointing at
@@ -116,6 +118,14 @@ __device__ __forceinline__ void decode8(const uint8_t* codes, const float* mn, c
   for (int i = 0; i < 8; ++i) v[i] = fmaf(static_cast<float>(q[i]), s[i], m[i]);
 }
 
+// 8 consecutive floats (16-byte aligned)
+__device__ __forceinline__ void load8f(const float* p, float (&v)[8]) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  const float4 b = *reinterpret_cast<const float4*>(p + 4);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
 // KB: 0 for a dense cache in T, else the KIVI code width (8 or 4)
 template <typename T, int KB>
 __global__ void __launch_bounds__(256) rerotate_kernel(RotArgs a) {
@@ -140,6 +150,38 @@ __global__ void __launch_bounds__(256) rerotate_kernel(RotArgs a) {
   // keys: each unit rotates 8 low channels j0.. with their partners j0+half..
   const int kper = half >> 3;                 // units per head
   const int ku = hkv * kper;                  // units per token
+  if (KIVI && blockDim.x % ku == 0) {
+    // a thread keeps one unit (head, channels) over the tile's rows, so the
+    // chunk's per-channel key statistics and the rotation factors are read
+    // once per thread instead of once per row
+    const int w = threadIdx.x % ku;
+    const int h = w / kper, j0 = (w - h * kper) << 3;
+    const int64_t st = (static_cast<int64_t>(ch.pool_chunk) * hkv + h) * d;
+    float mlo[8], slo[8], mhi[8], shi[8], c[8], s[8];
+    load8f(a.k_min + st + j0, mlo);
+    load8f(a.k_scale + st + j0, slo);
+    load8f(a.k_min + st + half + j0, mhi);
+    load8f(a.k_scale + st + half + j0, shi);
+    load8f(cosr + j0, c);
+    load8f(sinr + j0, s);
+    for (int t = threadIdx.x / ku; t < nrows; t += blockDim.x / ku) {
+      const int64_t src = (static_cast<int64_t>(ch.src_row) + t0 + t) * row_elems + h * d;
+      const int64_t dst = (static_cast<int64_t>(ch.dst_row) + t0 + t) * row_elems + h * d;
+      uint32_t qlo[8], qhi[8];
+      codes8<KIVI ? KB : 8>(a.k_codes + (src + j0) * KB / 8, qlo);
+      codes8<KIVI ? KB : 8>(a.k_codes + (src + half + j0) * KB / 8, qhi);
+      float olo[8], ohi[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float lo = fmaf(static_cast<float>(qlo[i]), slo[i], mlo[i]);
+        const float hi = fmaf(static_cast<float>(qhi[i]), shi[i], mhi[i]);
+        olo[i] = lo * c[i] - hi * s[i];
+        ohi[i] = hi * c[i] + lo * s[i];
+      }
+      Elem<T>::store8(fk + dst + j0, olo);
+      Elem<T>::store8(fk + dst + half + j0, ohi);
+    }
+  } else
   for (int u = threadIdx.x; u < nrows * ku; u += blockDim.x) {
     const int t = u / ku, w = u - t * ku;
     const int h = w / kper, j0 = (w - h * kper) << 3;
@@ -220,7 +262,7 @@ hipError_t launch_rerotate(const kvf_layer_desc& L, const kvf_chunk* chunks, int
   a.hkv = L.n_kv_heads;
   a.d = L.head_dim;
   a.k_only = k_only;
-  a.rows = rot_rows(a.hkv, a.d);
+  a.rows = rot_rows(a.hkv, a.d, q != nullptr);
   const dim3 grid(n_chunks, ceil_div(max_len, a.rows));
   if (grid.y > 65535) return hipErrorInvalidValue;
   if (q && q->bits == 4)
