@@ -238,29 +238,23 @@ attn_mfma_kernel(AttnArgs a) {
   bool valid[kQB];
   const bf16_t* Q = static_cast<const bf16_t*>(a.q);
   bf16x8_t qraw[kQB][KS];
+  // Every lane loads a position and a query vector, lanes past the tile's
+  // rows or heads those of the tile's first row and head (their results are
+  // never written): with no branch around them the loads stay in flight
+  // through the position scan, which waits for the positions only.
 #pragma unroll
   for (int qb = 0; qb < kQB; ++qb) {
     const int qv = 32 * (kQB * w + qb) + c;
     row_l[qb] = qv % R;
     const int head_l = qv / R;
     valid[qb] = head_l < a.G && row_l[qb] < nrows;
-    qrow[qb] = static_cast<int64_t>(a.qrow0[r]) + lrow0 + row_l[qb];
-    h[qb] = g * a.G + head_l;
-    pos[qb] = -1;
-    if (valid[qb]) {
-      int p = a.q_pos ? a.q_pos[qrow[qb]] : a.pos0[r] + lrow0 + row_l[qb];
-      pos[qb] = (p < 0 || p >= T) ? -1 : p;
-      // the query loads go out before the position scan, so that their
-      // latency overlaps it (rows skipped by position are zeroed after it)
+    qrow[qb] = static_cast<int64_t>(a.qrow0[r]) + lrow0 + (valid[qb] ? row_l[qb] : 0);
+    h[qb] = g * a.G + (valid[qb] ? head_l : 0);
+    const int p = a.q_pos ? a.q_pos[qrow[qb]] : a.pos0[r] + lrow0 + row_l[qb];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        qraw[qb][ks] = *reinterpret_cast<const bf16x8_t*>(Q + (qrow[qb] * a.hq + h[qb]) * D + ks * 16 + hf * 8);
-    } else {
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qraw[qb][ks][e] = static_cast<__bf16>(0.f);
-    }
+    for (int ks = 0; ks < KS; ++ks)
+      qraw[qb][ks] = *reinterpret_cast<const bf16x8_t*>(Q + (qrow[qb] * a.hq + h[qb]) * D + ks * 16 + hf * 8);
+    pos[qb] = (!valid[qb] || p < 0 || p >= T) ? -1 : p;
   }
   // Largest and smallest valid position of the tile: reduced within each
   // wave, one LDS slot per wave (atomics from every lane onto two words
@@ -308,22 +302,24 @@ attn_mfma_kernel(AttnArgs a) {
   const int t0 = part * n / np;
   const int t1 = (part + 1) * n / np;
 
+  // MFMA operands of the queries.  bf16: the loaded vectors as they are, so
+  // that nothing reads them before the first product (their loads stay in
+  // flight beside the first tile copies); a lane without a valid row
+  // computes on the tile's first query, is masked at every key of a masked
+  // tile and is never written.  fp16 (int8-resident cache): converted, and
+  // zero for lanes without a valid row.
   OpT qf[kQB][KS];
 #pragma unroll
   for (int qb = 0; qb < kQB; ++qb)
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      if (pos[qb] >= 0) {
-        const bf16x8_t qv = qraw[qb][ks];
-        if constexpr (Q8) {
+      const bf16x8_t qv = qraw[qb][ks];
+      if constexpr (Q8) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) qf[qb][ks][e] = static_cast<_Float16>(static_cast<float>(qv[e]));
-        } else {
-          qf[qb][ks] = qv;
-        }
+        for (int e = 0; e < 8; ++e)
+          qf[qb][ks][e] = pos[qb] >= 0 ? static_cast<_Float16>(static_cast<float>(qv[e])) : static_cast<_Float16>(0.f);
       } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qf[qb][ks][e] = 0;
+        qf[qb][ks] = qv;
       }
     }
 

@@ -635,6 +635,48 @@ def test_attention(kvf, case):
                      tag + " lse", tol=1e-4 if dtype == "f32" else 1e-3)
 
 
+def test_attention_ignores_keys_past_last_position(kvf):
+    """Key rows past a request's last query position are never read into a
+    result: they hold NaN here, and the outputs must still match the oracle
+    (which reads rows j <= pos only).  Short requests put the whole key range
+    in the first two key tiles, where the first copies of a row tile go out
+    before its positions are known and the rows past the key limit are
+    cleared afterwards."""
+    import torch
+    dtype, hq, hkv, d = "bf16", 8, 2, 128
+    Ts, Ms = [300, 90, 700], [40, 30, 200]
+    lim = [100, 60, 650]                      # positions drawn below these
+    cu_T = np.concatenate([[0], np.cumsum(Ts)]).astype(int).tolist()
+    cu_q = np.concatenate([[0], np.cumsum(Ms)]).astype(int).tolist()
+    T = cu_T[-1]
+    K = _randn((T, hkv, d), 31, "att_nan_k")
+    V = _randn((T, hkv, d), 31, "att_nan_v")
+    Q = _randn((cu_q[-1], hq, d), 31, "att_nan_q", std=2.0)
+    pos = np.concatenate([synth.random_rows(lim[r], Ms[r], 33 + r) for r in range(len(Ts))])
+    k_s, v_s, q_s = encode(K, dtype), encode(V, dtype), encode(Q, dtype)
+    k_nan, v_nan = k_s.copy(), v_s.copy()
+    for r in range(len(Ts)):
+        last = int(pos[cu_q[r]:cu_q[r + 1]].max())
+        k_nan[cu_T[r] + last + 1:cu_T[r + 1]] = 0x7FC0    # bf16 quiet NaN
+        v_nan[cu_T[r] + last + 1:cu_T[r + 1]] = 0x7FC0
+    L = _layer(kvf, 256, hq, hkv, d, dtype)
+    kb = _kbatch(kvf, cu_T, Ts)
+    need = kvf.attention_workspace_size(L, kb, cu_q)
+    ws = torch.zeros(max(need, 1), dtype=torch.uint8, device="cuda") if need > 0 else None
+    lo = fusion.Layer(256, hq, hkv, d, 1e4)
+    dk, dv, dq = decode(k_s, dtype), decode(v_s, dtype), decode(q_s, dtype)
+    ref = np.concatenate([fusion.causal_attention(dq[cu_q[r]:cu_q[r + 1]], pos[cu_q[r]:cu_q[r + 1]],
+                                                  dk[cu_T[r]:cu_T[r + 1]], dv[cu_T[r]:cu_T[r + 1]], lo)[0]
+                          for r in range(len(Ts))])
+    for w in [None] + ([ws] if ws is not None else []):
+        out = torch.zeros((cu_q[-1], hq, d), dtype=L.torch_dtype, device="cuda")
+        kvf.sparse_q_attention(L, kb, to_gpu(q_s, dtype), to_gpu(pos), cu_q, to_gpu(k_nan, dtype),
+                               to_gpu(v_nan, dtype), 1 / math.sqrt(d), out, None, workspace=w)
+        go = from_gpu(out)
+        assert np.isfinite(go).all(), "a key row past the last position reached an output"
+        assert_close_vectors(go, ref, dtype, f"attention with NaN rows past the last position (ws={w is not None})")
+
+
 def test_attention_workspace_shared_across_shapes(kvf):
     """One zero-filled workspace serves calls of different shapes in turn:
     the arrival counters sit at a fixed offset and every call leaves them
