@@ -1156,9 +1156,15 @@ struct MassArgs {
 };
 
 constexpr int kMK = 128;         // keys per workgroup (4 waves x 32)
-constexpr int kMQS = 256;        // query vectors staged per round (LDS)
+// Query vectors staged per round (LDS), MQS: 256 when a request has at most
+// that many (one round), else 128, whose smaller LDS and register footprint
+// lets three workgroups share a CU instead of two, so one's products overlap
+// another's exponentials (measured 6% faster with 2048 vectors, 3% slower
+// with 256).
+constexpr int kMQSOne = 256;
+constexpr int kMQSMany = 128;
 
-template <int D>
+template <int D, int kMQS>
 __global__ void __launch_bounds__(256) mass_stats_bf16_kernel(MassArgs a) {
   constexpr int KS = D / 16;
   constexpr int LDQ = D + 8;     // padded rows: B-fragment reads hit distinct banks
@@ -1573,10 +1579,16 @@ hipError_t launch_attn_mass(const kvf_layer_desc& L, const BatchArgs& B, const v
   // pass 1: softmax statistics of the used query rows
   if (L.dtype == KVF_BF16) {
     const dim3 grid(lay.n_splits * m.hkv, B.n_req);
-    if (L.head_dim == 128)
-      hipLaunchKernelGGL(mass_stats_bf16_kernel<128>, grid, dim3(256), 0, st, m);
-    else
-      hipLaunchKernelGGL(mass_stats_bf16_kernel<64>, grid, dim3(256), 0, st, m);
+    int nqv_max = 0;
+    for (int r = 0; r < B.n_req; ++r) nqv_max = std::max(nqv_max, m.nq[r] * m.G);
+    const bool one = nqv_max <= kMQSOne;
+    if (L.head_dim == 128) {
+      if (one) hipLaunchKernelGGL((mass_stats_bf16_kernel<128, kMQSOne>), grid, dim3(256), 0, st, m);
+      else hipLaunchKernelGGL((mass_stats_bf16_kernel<128, kMQSMany>), grid, dim3(256), 0, st, m);
+    } else {
+      if (one) hipLaunchKernelGGL((mass_stats_bf16_kernel<64, kMQSOne>), grid, dim3(256), 0, st, m);
+      else hipLaunchKernelGGL((mass_stats_bf16_kernel<64, kMQSMany>), grid, dim3(256), 0, st, m);
+    }
   } else {
     AttnArgs a{};
     a.b = B;
