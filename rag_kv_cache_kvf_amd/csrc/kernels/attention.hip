@@ -1181,10 +1181,15 @@ __global__ void __launch_bounds__(256) mass_stats_bf16_kernel(MassArgs a) {
   const int T = a.b.cu_T[r + 1] - a.b.cu_T[r];
   const int64_t krow0 = a.b.cu_T[r];
   const int nqv = a.nq[r] * a.G;
+  // blockIdx.z splits the query vectors into gridDim.z parts (multiples of
+  // 32) so that small grids put more workgroups on the chip
+  const int per = ceil_div(ceil_div(nqv, static_cast<int>(gridDim.z)), 32) * 32;
+  const int q_lo = min(nqv, static_cast<int>(blockIdx.z) * per);
+  const int q_hi = min(nqv, q_lo + per);
   const int key0 = chunk * kMK;
   const int64_t out0 = static_cast<int64_t>(chunk) * a.plane;
   if (key0 >= T) {          // past this request's keys: an empty chunk
-    for (int qv = tid; qv < nqv; qv += 256) {
+    for (int qv = q_lo + tid; qv < q_hi; qv += 256) {
       const int row = qv / a.G, hl = qv - row * a.G;
       const int64_t idx = out0 + (static_cast<int64_t>(a.orow0[r]) + row) * a.hq + g * a.G + hl;
       a.part_m[idx] = -INFINITY;
@@ -1210,8 +1215,8 @@ __global__ void __launch_bounds__(256) mass_stats_bf16_kernel(MassArgs a) {
   }
   const bf16_t* Qg = static_cast<const bf16_t*>(a.q);
   const float cs = a.scale_log2;
-  for (int qs = 0; qs < nqv; qs += kMQS) {
-    const int qe = min(nqv, qs + kMQS);
+  for (int qs = q_lo; qs < q_hi; qs += kMQS) {
+    const int qe = min(q_hi, qs + kMQS);
     // stage this round's query vectors (zero rows past the end): all loads
     // in flight together, then the stores
     constexpr int NV = kMQS * VPR / 256;
@@ -1578,10 +1583,15 @@ hipError_t launch_attn_mass(const kvf_layer_desc& L, const BatchArgs& B, const v
 
   // pass 1: softmax statistics of the used query rows
   if (L.dtype == KVF_BF16) {
-    const dim3 grid(lay.n_splits * m.hkv, B.n_req);
     int nqv_max = 0;
     for (int r = 0; r < B.n_req; ++r) nqv_max = std::max(nqv_max, m.nq[r] * m.G);
-    const bool one = nqv_max <= kMQSOne;
+    // a grid under two workgroups per CU with at least 256 query vectors per
+    // request splits them in two (128-vector rounds, three workgroups per CU)
+    const int64_t wgs = static_cast<int64_t>(lay.n_splits) * m.hkv * B.n_req;
+    const int nqp = (wgs < 2 * kCUs && nqv_max >= 2 * kMQSMany) ? 2 : 1;
+    const dim3 grid(lay.n_splits * m.hkv, B.n_req, nqp);
+    const int per = ceil_div(ceil_div(nqv_max, nqp), 32) * 32;
+    const bool one = per > kMQSMany && per <= kMQSOne;
     if (L.head_dim == 128) {
       if (one) hipLaunchKernelGGL((mass_stats_bf16_kernel<128, kMQSOne>), grid, dim3(256), 0, st, m);
       else hipLaunchKernelGGL((mass_stats_bf16_kernel<128, kMQSMany>), grid, dim3(256), 0, st, m);
