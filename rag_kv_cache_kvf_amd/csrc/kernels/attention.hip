@@ -1344,9 +1344,15 @@ __global__ void __launch_bounds__(256) mass_colsum_bf16_kernel(MassArgs a) {
     }
   }
   const bf16_t* Qg = static_cast<const bf16_t*>(a.q);
-  const int nqv = a.nq[r] * a.G;
+  // blockIdx.y splits the query vectors into gridDim.y parts (multiples of
+  // 32), each summed by its own workgroup; the last arrival of a key tile
+  // adds every (part, kv head) sum
+  const int nqv_all = a.nq[r] * a.G;
+  const int per = ceil_div(ceil_div(nqv_all, static_cast<int>(gridDim.y)), 32) * 32;
+  const int q_lo = min(nqv_all, static_cast<int>(blockIdx.y) * per);
+  const int nqv = min(nqv_all, q_lo + per);
   float colsum = 0.f;
-  for (int q0 = 0; q0 < nqv; q0 += kMQB) {
+  for (int q0 = q_lo; q0 < nqv; q0 += kMQB) {
     // this round's query vectors and LSEs: all loads in flight together
     constexpr int NV = kMQB * VPR / 256;
     u32x4_t v4[NV];
@@ -1406,26 +1412,28 @@ __global__ void __launch_bounds__(256) mass_colsum_bf16_kernel(MassArgs a) {
   }
   colsum += __shfl_xor(colsum, 32, kWave);
   const int n_all = a.b.cu_N[a.b.n_req];
-  // per-head column sums [kv head][sum N], moved as plain buffer accesses
+  // column sums [query part][kv head][sum N], moved as plain buffer accesses
   // with the device-scope cache policy so a batch of them is in flight at
   // once (relaxed atomics would go one at a time)
-  const __amdgpu_buffer_rsrc_t pr = handoff_rsrc(a.part, static_cast<int64_t>(a.hkv) * n_all * 4);
+  const int n_sum = a.hkv * static_cast<int>(gridDim.y);    // partial sums per key
+  const __amdgpu_buffer_rsrc_t pr = handoff_rsrc(a.part, static_cast<int64_t>(n_sum) * n_all * 4);
   if (hf == 0 && kvalid)
-    put_dev1(pr, static_cast<uint32_t>(a.b.cu_N[r] + key) * 4, static_cast<uint32_t>(g) * n_all * 4, colsum);
-  // the last kv head of this key tile adds the heads in a fixed order
+    put_dev1(pr, static_cast<uint32_t>(a.b.cu_N[r] + key) * 4,
+             static_cast<uint32_t>(blockIdx.y * a.hkv + g) * n_all * 4, colsum);
+  // the last arrival of this key tile adds the partial sums in a fixed order
   __shared__ int s_flag;
-  if (!arrive_last(a.cnt_cols + kt, a.hkv, &s_flag)) return;
+  if (!arrive_last(a.cnt_cols + kt, n_sum, &s_flag)) return;
   if (tid < kMK && key0 + tid < N) {
     const uint32_t key_off = static_cast<uint32_t>(a.b.cu_N[r] + key0 + tid) * 4;
     float sum = 0.f;
-    for (int g0 = 0; g0 < a.hkv; g0 += 8) {
+    for (int g0 = 0; g0 < n_sum; g0 += 8) {
       float pv8[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u)
-        pv8[u] = get_dev1(pr, key_off, static_cast<uint32_t>(min(g0 + u, a.hkv - 1)) * n_all * 4);
+        pv8[u] = get_dev1(pr, key_off, static_cast<uint32_t>(min(g0 + u, n_sum - 1)) * n_all * 4);
 #pragma unroll
       for (int u = 0; u < 8; ++u)
-        if (g0 + u < a.hkv) sum += pv8[u];
+        if (g0 + u < n_sum) sum += pv8[u];
     }
     store_score(a.out, a.b.cu_N[r] + key0 + tid, sum);
   }
@@ -1476,6 +1484,9 @@ int64_t attn_mass_key_tiles(const BatchArgs& B) {
   return ktiles;
 }
 
+// Query-vector parts of a small grid's statistics and column-sum passes.
+constexpr int kMassQParts = 2;
+
 namespace {
 struct MassLayout {
   int64_t rows;          // query rows used (sum over requests)
@@ -1519,7 +1530,8 @@ MassLayout mass_layout(const kvf_layer_desc& L, const BatchArgs& B, int n_last_q
   m.off_pl = align(m.off_pm + sizeof(float) * plane * m.n_splits);
   m.off_lse = align(m.off_pl + sizeof(float) * plane * m.n_splits);
   m.off_part = align(m.off_lse + sizeof(float) * plane);
-  m.total = align(m.off_part + sizeof(float) * static_cast<size_t>(L.n_kv_heads) * B.cu_N[B.n_req]);
+  // column sums of up to kMassQParts query parts per kv head and key
+  m.total = align(m.off_part + sizeof(float) * kMassQParts * static_cast<size_t>(L.n_kv_heads) * B.cu_N[B.n_req]);
   return m;
 }
 }  // namespace
@@ -1588,7 +1600,7 @@ hipError_t launch_attn_mass(const kvf_layer_desc& L, const BatchArgs& B, const v
     // a grid under two workgroups per CU with at least 256 query vectors per
     // request splits them in two (128-vector rounds, three workgroups per CU)
     const int64_t wgs = static_cast<int64_t>(lay.n_splits) * m.hkv * B.n_req;
-    const int nqp = (wgs < 2 * kCUs && nqv_max >= 2 * kMQSMany) ? 2 : 1;
+    const int nqp = (wgs < 2 * kCUs && nqv_max >= kMassQParts * kMQSMany) ? kMassQParts : 1;
     const dim3 grid(lay.n_splits * m.hkv, B.n_req, nqp);
     const int per = ceil_div(ceil_div(nqv_max, nqp), 32) * 32;
     const bool one = per > kMQSMany && per <= kMQSOne;
@@ -1639,10 +1651,16 @@ hipError_t launch_attn_mass(const kvf_layer_desc& L, const BatchArgs& B, const v
   if (n == 0) return hipSuccess;
   if (L.dtype == KVF_BF16) {
     const int64_t blocks = static_cast<int64_t>(m.total_ktiles) * m.hkv;
+    // a grid under two workgroups per CU whose requests have more than one
+    // round of query vectors splits them over kMassQParts workgroups
+    int nqv_max = 0;
+    for (int r = 0; r < B.n_req; ++r) nqv_max = std::max(nqv_max, m.nq[r] * m.G);
+    const int nqp = (blocks < 2 * kCUs && nqv_max > kMQB) ? kMassQParts : 1;
+    const dim3 grid(static_cast<unsigned>(blocks), nqp);
     if (L.head_dim == 128)
-      hipLaunchKernelGGL(mass_colsum_bf16_kernel<128>, dim3(blocks), dim3(256), 0, st, m);
+      hipLaunchKernelGGL(mass_colsum_bf16_kernel<128>, grid, dim3(256), 0, st, m);
     else
-      hipLaunchKernelGGL(mass_colsum_bf16_kernel<64>, dim3(blocks), dim3(256), 0, st, m);
+      hipLaunchKernelGGL(mass_colsum_bf16_kernel<64>, grid, dim3(256), 0, st, m);
   } else {
     const int64_t waves = static_cast<int64_t>(n) * m.hkv;
     hipLaunchKernelGGL(mass_colsum_f32_kernel, dim3(ceil_div(static_cast<int>(waves), 4)),
