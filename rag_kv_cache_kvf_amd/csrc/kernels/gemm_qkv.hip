@@ -627,10 +627,16 @@ struct Bf16Plan {
 // is a multiple of it; row-tile height the candidate whose tiles fill 256 CUs
 // with the least per-CU work (rounds x tile area, ties to the larger tile).
 // A call with too few tiles for half the chip (few rows) takes 64 or
-// 128 x 128 tiles instead and may split K: 2^j slices of >= 256, the count that
-// brings the workgroups closest to one per CU (more slices shorten each
-// workgroup's K loop but add partial sums to store and read back), the
-// slices added by the last slice of each output tile to finish.
+// 128 x 128 tiles instead and may split K into 2^j slices of >= 256, added
+// by the last slice of each output tile to finish.  The slice count is the
+// one with the least estimated time: these tiles hold one workgroup per CU,
+// so the workgroups run in ceil(n / 256) rounds, each a K loop of hidden / sp
+// plus a fixed cost (prologue and epilogue, about kRoundFixedK k-columns of
+// loop), plus one hand-off when K is split.  (Counting only how close the
+// workgroups come to one per CU put the 70B-shaped 256-row probe at 320
+// workgroups, two rounds of half-length loops: 102 us.)
+constexpr int64_t kRoundFixedK = 1024;   // a round's fixed cost in k-columns of loop (about 5 us)
+constexpr int64_t kHandoffK = 1024;      // storing, counting and re-reading the slices
 Bf16Plan plan_bf16(const kvf_layer_desc& L, int M, uint32_t mask) {
   const int heads[3] = {L.n_q_heads, L.n_kv_heads, L.n_kv_heads};
   const uint32_t bits[3] = {KVF_OUT_Q, KVF_OUT_K, KVF_OUT_V};
@@ -661,12 +667,12 @@ Bf16Plan plan_bf16(const kvf_layer_desc& L, int M, uint32_t mask) {
   if (static_cast<int64_t>(ceil_div(M, p.bm)) * total >= 128) return p;
   Bf16Plan q{M <= 64 ? 64 : 128, 128, 1, 1, {0, 0, 0}};
   const int64_t base = static_cast<int64_t>(ceil_div(M, q.bm)) * tiles(128, q.n_tiles);
-  int64_t best_gap = base > kCUs ? base - kCUs : kCUs - base;
-  for (int sp = 2; L.hidden % (sp * kBK) == 0 && L.hidden / sp >= 256; sp *= 2) {
-    const int64_t n = base * sp;
-    const int64_t gap = n > kCUs ? n - kCUs : kCUs - n;
-    if (gap < best_gap) {
-      best_gap = gap;
+  int64_t best_time = INT64_MAX;
+  for (int sp = 1; sp == 1 || (L.hidden % (sp * kBK) == 0 && L.hidden / sp >= 256); sp *= 2) {
+    const int64_t rounds = (base * sp + kCUs - 1) / kCUs;
+    const int64_t cost = rounds * (L.hidden / sp + kRoundFixedK) + (sp > 1 ? kHandoffK : 0);
+    if (cost < best_time) {
+      best_time = cost;
       q.splits = sp;
     }
   }
