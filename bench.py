@@ -133,7 +133,12 @@ def call_work(g):
         work["recompute"] = ("mfma", 2.0 * hid * d * (hq + 2 * hkv) * M)
     elif g.mode == "deviation":
         work["k_probe"] = ("mfma", 2.0 * hid * hkv * d * total)
-        work["score"] = ("hbm", n_ctx * ((q8row if g.q8 else krow) + krow + 4))   # fused K, probe K -> fp32
+        if g.fuse_dev:
+            # the re-positioning pass also reads the probe K and writes the score
+            kind, nbytes = work["rerotate"]
+            work["rerotate"] = (kind, nbytes + n_ctx * (krow + 4))
+        else:
+            work["score"] = ("hbm", n_ctx * ((q8row if g.q8 else krow) + krow + 4))   # fused K, probe K -> fp32
         work["recompute"] = ("mfma", 2.0 * hid * d * (hq + hkv) * M)
     else:
         work["u_probe"] = ("mfma", 2.0 * hid * d * (hq + 2 * hkv) * nU)
@@ -695,7 +700,8 @@ def measure(wl, ratio, steps, warmup, flush, graph=False):
               "rerotate": "keys only (values stitched by the loader)" if g.k_only else
               ("KIVI decode" if wl.kivi_bits else "gather keys and values") +
               (", int8-resident fused cache (8-bit codes + per-row min/scale)" if g.q8 else
-               ", bf16 fused cache")}
+               ", bf16 fused cache") +
+              (", deviation score in the same pass" if g.fuse_dev else "")}
     res = {"value": round(n_ctx / (med * 1e-3), 1), "unit": UNIT, "ms_per_step": round(med, 5),
            "ms_median": round(med, 5), "config": config, "timing": timing, "roofline": roofline,
            "calls": calls}

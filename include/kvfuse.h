@@ -73,7 +73,7 @@
 extern "C" {
 #endif
 
-#define KVF_ABI_VERSION 10
+#define KVF_ABI_VERSION 11
 #define KVF_MAX_REQ 64      /* requests per call (batch metadata is passed by value) */
 
 typedef enum {
@@ -234,6 +234,36 @@ kvf_status kvf_rerotate(const kvf_layer_desc* layer, const kvf_chunk* chunks,
                         const float* rope_cos, const float* rope_sin,
                         int32_t rope_n_pos, void* fused_k, void* fused_v,
                         int64_t fused_rows, int32_t k_only, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * kvf_rerotate_deviation - S1 and the deviation score S2b in one pass
+ * ([KVB] 4.6.2 Algorithm 2 at one layer: the probe's fresh keys are compared
+ * with the re-positioned cached keys; [QCF] 2.1.2 Eq. 4 for the
+ * re-positioning).  Does exactly what kvf_rerotate does with the same
+ * arguments, and for every fused row a chunk writes that is a context row of
+ * `batch` (row cu_T[r] + i with i < n_ctx[r]) it also writes the
+ * KVF_SCORE_DEVIATION score of kvf_score to scores[cu_N[r] + i]
+ * (cu_N = prefix sums of n_ctx), computed from the key as fused_k stores it
+ * (bf16-rounded for bf16 layers), so that the score pass does not read the
+ * fused keys back.  eligible ([sum N] uint8 or NULL) and accumulate (0 or
+ * 1; 1 = scores[t] += this layer's score) behave as in kvf_score.
+ * k_fresh: [fused_rows, Hkv, d] in dtype, the probe's keys (kvf_recompute_qkv
+ *   with KVF_OUT_K over the rows), indexed like the fused cache; an
+ *   ineligible row's k_fresh is not read.
+ * Context rows that no chunk covers get no score (their entries are left
+ * as they were): the chunks should tile every request's context, as the
+ * loader's stitch does.
+ * Errors: those of kvf_rerotate; KVF_ERR_UNSUPPORTED unless Hkv * d / 16 is
+ * a power of two of at most 64 (a row's key is reduced within one wave).
+ */
+kvf_status kvf_rerotate_deviation(const kvf_layer_desc* layer, const kvf_batch* batch,
+                                  const kvf_chunk* chunks, int32_t n_chunks, int32_t max_chunk_len,
+                                  const void* pool_k, const void* pool_v, const kvf_kivi* kivi,
+                                  int64_t pool_rows, const float* rope_cos, const float* rope_sin,
+                                  int32_t rope_n_pos, void* fused_k, void* fused_v,
+                                  int64_t fused_rows, int32_t k_only, const void* k_fresh,
+                                  const uint8_t* eligible, int32_t accumulate, float* scores,
+                                  void* stream);
 
 /* ---------------------------------------------------------------------------
  * kvf_rerotate_q8 - S1 into an int8-resident fused cache (kvf_q8_cache):

@@ -16,6 +16,7 @@
 // loader and are not touched; the keys may be rotated in place (a thread
 // reads the 16 channels of a rotation pair set before it writes them).
 #include <algorithm>
+#include <type_traits>
 
 #include "../kvf_common.h"
 
@@ -75,6 +76,14 @@ struct RotArgs {
   int d;
   int k_only;                     // keys only: values are already in place
   int rows;                       // tokens per workgroup tile
+  // Deviation score of the re-positioned keys in the same pass (S2b fused
+  // into S1): k_fresh [fused rows, Hkv, d] in T, rows indexed like the fused
+  // cache; the score of a context row of request r goes to entry
+  // cu_N[r] + (row - cu_T[r]) of dev.scores.  Unused unless the kernel's
+  // DEV parameter is set.
+  const void* k_fresh;
+  ScoreOut dev;
+  BatchArgs B;
 };
 
 // Tokens per workgroup tile: kRotRows, or more when a token's key has too
@@ -126,8 +135,72 @@ __device__ __forceinline__ void load8f(const float* p, float (&v)[8]) {
   v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
 
-// KB: 0 for a dense cache in T, else the KIVI code width (8 or 4)
-template <typename T, int KB>
+// One RoPE pair (x, y) rotated by (c, s): (x c - y s, y c + x s), with the
+// multiply-adds spelled out so that every instantiation of a kernel rounds
+// the same way (left to the compiler, the contraction into fused
+// multiply-adds may differ between instantiations and change the last bit).
+__device__ __forceinline__ float rot_lo(float x, float y, float c, float s) {
+  return fmaf(x, c, -(y * s));
+}
+__device__ __forceinline__ float rot_hi(float x, float y, float c, float s) {
+  return fmaf(y, c, x * s);
+}
+
+// a value as the fused cache stores it (bf16: rounded to nearest even)
+template <typename T>
+__device__ __forceinline__ float stored(float x) {
+  if constexpr (std::is_same_v<T, float>) return x;
+  else return bf16_to_f32(f32_to_bf16(x));
+}
+
+// Deviation score of fused row `frow` (KVBoost page, section 4.6.2,
+// Algorithm 2 at one layer): 1 - (1/Hkv) sum_h cos(k_fused[h], k_fresh[h]),
+// a head's cosine 0 when either norm is 0, from the key as the fused cache
+// stores it.  The row's rotation units sit on ku consecutive lanes (ku a
+// power of two dividing 64), kper per head, and all of them call this
+// together; this lane holds channels j0.. and their partners half + j0.. of
+// head h.  Rows that are not context rows of the batch get no score.
+template <typename T>
+__device__ __forceinline__ void deviation_of_row(const RotArgs& a, int64_t frow, int h, int j0,
+                                                 const float (&lo)[8], const float (&hi)[8],
+                                                 int ku, int kper) {
+  const BatchArgs& B = a.B;
+  const int half = a.d >> 1;
+  bool ctx = frow < B.cu_T[B.n_req];
+  int64_t j = 0;
+  if (ctx) {
+    const int r = find_segment(B.cu_T, B.n_req, static_cast<int>(frow));
+    const int64_t i = frow - B.cu_T[r];
+    ctx = i < B.n_ctx[r];
+    j = B.cu_N[r] + i;
+  }
+  float dot = 0.f, nx = 0.f, ny = 0.f;
+  if (ctx && score_eligible(a.dev, j)) {       // ineligible rows' k_fresh is not read
+    const T* kf = static_cast<const T*>(a.k_fresh) + (frow * a.hkv + h) * a.d;
+    float ylo[8], yhi[8];
+    Elem<T>::load8(kf + j0, ylo);
+    Elem<T>::load8(kf + half + j0, yhi);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float xl = stored<T>(lo[i]), xh = stored<T>(hi[i]);
+      dot = fmaf(xl, ylo[i], fmaf(xh, yhi[i], dot));
+      nx = fmaf(xl, xl, fmaf(xh, xh, nx));
+      ny = fmaf(ylo[i], ylo[i], fmaf(yhi[i], yhi[i], ny));
+    }
+  }
+  dot = group_sum(dot, kper);
+  nx = group_sum(nx, kper);
+  ny = group_sum(ny, kper);
+  const int lane = threadIdx.x & (kWave - 1);
+  const float den = sqrtf(nx) * sqrtf(ny);
+  float c = ((lane & (kper - 1)) == 0 && den > 0.f) ? dot / den : 0.f;
+  c = group_sum(c, ku);
+  if ((lane & (ku - 1)) == 0 && ctx) store_score(a.dev, j, 1.f - c / static_cast<float>(a.hkv));
+}
+
+// KB: 0 for a dense cache in T, else the KIVI code width (8 or 4).
+// DEV: also the deviation score of every re-positioned context row.
+template <typename T, int KB, bool DEV>
 __global__ void __launch_bounds__(256) rerotate_kernel(RotArgs a) {
   constexpr bool KIVI = KB != 0;
   const kvf_chunk ch = a.chunks[blockIdx.x];
@@ -175,11 +248,13 @@ __global__ void __launch_bounds__(256) rerotate_kernel(RotArgs a) {
       for (int i = 0; i < 8; ++i) {
         const float lo = fmaf(static_cast<float>(qlo[i]), slo[i], mlo[i]);
         const float hi = fmaf(static_cast<float>(qhi[i]), shi[i], mhi[i]);
-        olo[i] = lo * c[i] - hi * s[i];
-        ohi[i] = hi * c[i] + lo * s[i];
+        olo[i] = rot_lo(lo, hi, c[i], s[i]);
+        ohi[i] = rot_hi(lo, hi, c[i], s[i]);
       }
       Elem<T>::store8(fk + dst + j0, olo);
       Elem<T>::store8(fk + dst + half + j0, ohi);
+      if constexpr (DEV)
+        deviation_of_row<T>(a, static_cast<int64_t>(ch.dst_row) + t0 + t, h, j0, olo, ohi, ku, kper);
     }
   } else
   for (int u = threadIdx.x; u < nrows * ku; u += blockDim.x) {
@@ -204,11 +279,13 @@ __global__ void __launch_bounds__(256) rerotate_kernel(RotArgs a) {
     float olo[8], ohi[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      olo[i] = lo[i] * c[i] - hi[i] * s[i];
-      ohi[i] = hi[i] * c[i] + lo[i] * s[i];
+      olo[i] = rot_lo(lo[i], hi[i], c[i], s[i]);
+      ohi[i] = rot_hi(lo[i], hi[i], c[i], s[i]);
     }
     Elem<T>::store8(fk + dst + j0, olo);
     Elem<T>::store8(fk + dst + half + j0, ohi);
+    if constexpr (DEV)
+      deviation_of_row<T>(a, static_cast<int64_t>(ch.dst_row) + t0 + t, h, j0, olo, ohi, ku, kper);
   }
 
   // values: stitched unchanged (decoded for int8 caches)
@@ -235,10 +312,19 @@ __global__ void __launch_bounds__(256) rerotate_kernel(RotArgs a) {
   }
 }
 
+// Rotation units of one fused row (8 channel pairs each) when the fused
+// deviation score can reduce a row within aligned lane groups: a power of
+// two dividing 64, else 0.
+int rerotate_deviation_lanes(int hkv, int d) {
+  const int ku = hkv * d / 16;
+  return (d % 16 == 0 && ku >= 1 && ku <= kWave && (ku & (ku - 1)) == 0) ? ku : 0;
+}
+
 hipError_t launch_rerotate(const kvf_layer_desc& L, const kvf_chunk* chunks, int n_chunks,
                            int max_len, const void* pk, const void* pv, const kvf_kivi* q,
                            int64_t pool_rows, const float* rc, const float* rs, int rope_n,
-                           void* fk, void* fv, int64_t fused_rows, int k_only, hipStream_t st) {
+                           void* fk, void* fv, int64_t fused_rows, int k_only, hipStream_t st,
+                           const RotDeviation* dev) {
   RotArgs a{};
   a.chunks = chunks;
   a.pool_k = pk;
@@ -265,14 +351,26 @@ hipError_t launch_rerotate(const kvf_layer_desc& L, const kvf_chunk* chunks, int
   a.rows = rot_rows(a.hkv, a.d, q != nullptr);
   const dim3 grid(n_chunks, ceil_div(max_len, a.rows));
   if (grid.y > 65535) return hipErrorInvalidValue;
+  if (dev) {
+    if (rerotate_deviation_lanes(a.hkv, a.d) == 0) return hipErrorInvalidValue;
+    a.k_fresh = dev->k_fresh;
+    a.dev = dev->out;
+    a.B = dev->B;
+  }
+#define KVF_ROT_LAUNCH(T_, KB_)                                                               \
+  do {                                                                                        \
+    if (dev) hipLaunchKernelGGL((rerotate_kernel<T_, KB_, true>), grid, dim3(256), 0, st, a); \
+    else hipLaunchKernelGGL((rerotate_kernel<T_, KB_, false>), grid, dim3(256), 0, st, a);    \
+  } while (0)
   if (q && q->bits == 4)
-    hipLaunchKernelGGL((rerotate_kernel<bf16_t, 4>), grid, dim3(256), 0, st, a);
+    KVF_ROT_LAUNCH(bf16_t, 4);
   else if (q)
-    hipLaunchKernelGGL((rerotate_kernel<bf16_t, 8>), grid, dim3(256), 0, st, a);
+    KVF_ROT_LAUNCH(bf16_t, 8);
   else if (L.dtype == KVF_BF16)
-    hipLaunchKernelGGL((rerotate_kernel<bf16_t, 0>), grid, dim3(256), 0, st, a);
+    KVF_ROT_LAUNCH(bf16_t, 0);
   else
-    hipLaunchKernelGGL((rerotate_kernel<float, 0>), grid, dim3(256), 0, st, a);
+    KVF_ROT_LAUNCH(float, 0);
+#undef KVF_ROT_LAUNCH
   return hipGetLastError();
 }
 

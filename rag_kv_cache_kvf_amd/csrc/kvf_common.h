@@ -259,10 +259,21 @@ __device__ __forceinline__ void store_score(const ScoreOut& o, int64_t j, float 
 // ---------------------------------------------------------------------------
 namespace kvf {
 hipError_t launch_rope_table(double base, int d, int n_pos, float* c, float* s, hipStream_t st);
+// The deviation score a re-positioning pass computes on the side
+// (kvf_rerotate_deviation): k_fresh rows indexed like the fused cache.
+struct RotDeviation {
+  const void* k_fresh;
+  ScoreOut out;
+  BatchArgs B;
+};
+// rotation units per fused row if the fused deviation score supports the
+// shape, else 0
+int rerotate_deviation_lanes(int hkv, int d);
 hipError_t launch_rerotate(const kvf_layer_desc& L, const kvf_chunk* chunks, int n_chunks,
                            int max_len, const void* pk, const void* pv, const kvf_kivi* q,
                            int64_t pool_rows, const float* rc, const float* rs, int rope_n,
-                           void* fk, void* fv, int64_t fused_rows, int k_only, hipStream_t st);
+                           void* fk, void* fv, int64_t fused_rows, int k_only, hipStream_t st,
+                           const RotDeviation* dev = nullptr);
 // int8-resident fused cache (kvf_q8_cache)
 hipError_t launch_rerotate_q8(const kvf_layer_desc& L, const kvf_chunk* chunks, int n_chunks,
                               int max_len, const void* pk, const void* pv, const kvf_kivi* q,

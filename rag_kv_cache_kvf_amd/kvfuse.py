@@ -87,6 +87,8 @@ _SIGS = {
     "kvf_rope_table": (_I32, [ctypes.c_double, _I32, _I32, _P, _P, _P]),
     "kvf_rerotate": (_I32, [_LP, _P, _I32, _I32, _P, _P, ctypes.POINTER(KiviDesc), _I64, _P, _P,
                             _I32, _P, _P, _I64, _I32, _P]),
+    "kvf_rerotate_deviation": (_I32, [_LP, _BP, _P, _I32, _I32, _P, _P, ctypes.POINTER(KiviDesc), _I64,
+                                      _P, _P, _I32, _P, _P, _I64, _I32, _P, _P, _I32, _P, _P]),
     "kvf_score": (_I32, [_I32, _LP, _BP, _P, _P, _P, _I32, _P, _P, _P, _SZ, _P]),
     "kvf_score_workspace_size": (_SZ, [_I32, _LP, _BP, _I32]),
     "kvf_score_attn_mass_noalloc": (_I32, [_LP, _BP, _P, _P, _I32, _P, _P, _I32, _P]),
@@ -278,6 +280,29 @@ def rerotate(layer: Layer, chunks: torch.Tensor, max_chunk_len: int,
                              _ptr(pool_k), _ptr(pool_v), kd, pool_rows, _ptr(rope_cos),
                              _ptr(rope_sin), int(rope_cos.shape[0]), _ptr(fused_k), _ptr(fused_v),
                              _rows(fused_k), 1 if k_only else 0), "kvf_rerotate", stream)
+
+
+def rerotate_deviation(layer: Layer, batch: Batch, chunks: torch.Tensor, max_chunk_len: int,
+                       pool_k: Optional[torch.Tensor], pool_v: Optional[torch.Tensor],
+                       rope_cos: torch.Tensor, rope_sin: torch.Tensor, fused_k: torch.Tensor,
+                       fused_v: Optional[torch.Tensor], k_fresh: torch.Tensor, scores: torch.Tensor,
+                       kivi: Optional[dict] = None, k_only: bool = False,
+                       eligible: Optional[torch.Tensor] = None, accumulate: bool = False,
+                       stream=None):
+    """kvf_rerotate_deviation: rerotate() plus the deviation score of every
+    re-positioned context row against k_fresh ([fused rows, Hkv, d])."""
+    kd = None
+    pool_rows = _rows(pool_k)
+    if kivi is not None:
+        kd = ctypes.byref(_kivi_desc(kivi))
+        pool_rows = int(kivi["k_codes"].shape[0])
+    d = layer.desc()
+    return _run(_lib.kvf_rerotate_deviation,
+                (ctypes.byref(d), ctypes.byref(batch.desc), _ptr(chunks), int(chunks.shape[0]),
+                 max_chunk_len, _ptr(pool_k), _ptr(pool_v), kd, pool_rows, _ptr(rope_cos),
+                 _ptr(rope_sin), int(rope_cos.shape[0]), _ptr(fused_k), _ptr(fused_v), _rows(fused_k),
+                 1 if k_only else 0, _ptr(k_fresh), _ptr(eligible), 1 if accumulate else 0,
+                 _ptr(scores)), "kvf_rerotate_deviation", stream, keep=(d, batch))
 
 
 def score_attn_mass_noalloc(layer: Layer, batch: Batch, fused_k: torch.Tensor, q_u: torch.Tensor,

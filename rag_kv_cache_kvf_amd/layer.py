@@ -5,8 +5,10 @@ requests and owns the device buffers between them; it computes nothing
 itself.  Order (all on one stream, no host synchronisation):
 
   deviation mode (KVBoost page, section 4.6.2, Algorithm 2 at one layer)
-    kvf_rerotate -> kvf_recompute_qkv(all rows, K: probe K~) ->
-    kvf_score(DEVIATION) -> kvf_select_topk ->
+    kvf_recompute_qkv(all rows, K: probe K~) ->
+    kvf_rerotate_deviation (re-positioning and the deviation score in one
+    pass; with fuse_deviation=False: kvf_rerotate, then kvf_score(DEVIATION)
+    after the probe) -> kvf_select_topk ->
     kvf_recompute_qkv(P+U, Q|V; V straight into the fused cache) ->
     kvf_scatter_kv(K of P+U from the probe) -> kvf_sparse_q_attention
   attention-mass mode (QCFuse page, section 3.2.1 at one layer)
@@ -66,11 +68,17 @@ class FusedLayerGPU:
     and the pass re-positions the keys only (QCFuse page, section 2.1.2: the
     values keep their token order; only the keys carry the rotation).  With
     k_only False, or for a shared chunk pool or KIVI codes, the pass gathers
-    keys and values from the per-chunk caches itself."""
+    keys and values from the per-chunk caches itself.
+
+    fuse_deviation (deviation mode, bf16 or fp32 fused cache): the key probe
+    runs first and the re-positioning pass scores every context row as it
+    writes its key (kvf_rerotate_deviation), so the score does not read the
+    fused keys back; False keeps kvf_rerotate and kvf_score apart."""
 
     def __init__(self, batch: SynthBatch, ratio_pct: int, device="cuda",
                  pic: Optional[dict] = None, n_last_q: int = 0, mode: Optional[str] = None,
-                 k_only: Optional[bool] = None, resident: Optional[str] = None):
+                 k_only: Optional[bool] = None, resident: Optional[str] = None,
+                 fuse_deviation: bool = True):
         wl = batch.wl
         self.q8 = (wl.resident if resident is None else resident) == "q8"
         self.wl = wl
@@ -83,6 +91,9 @@ class FusedLayerGPU:
         # the key probe of deviation scoring; other selectors project P+U only
         self.probe = self.selector == "score" and self.mode == "deviation"
         self.mass = self.selector == "score" and self.mode != "deviation"
+        ku = wl.n_kv_heads * wl.head_dim // 16     # rotation units of a row: one wave reduces them
+        self.fuse_dev = (fuse_deviation and self.probe and not self.q8 and wl.head_dim % 16 == 0
+                         and 1 <= ku <= 64 and ku & (ku - 1) == 0)
         self.n_last_q = n_last_q
         self.device = torch.device(device)
         dev = self.device
@@ -243,6 +254,12 @@ class FusedLayerGPU:
         if self.q8:
             return kvf.rerotate_q8(self.layer, self.chunks, self.max_chunk_len, self.pool_k, self.pool_v,
                                    self.rope_cos, self.rope_sin, self.fused, kivi=self.kivi)
+        if self.fuse_dev:
+            return kvf.rerotate_deviation(
+                self.layer, self.kb, self.chunks, self.max_chunk_len, self.pool_k,
+                None if self.k_only else self.pool_v, self.rope_cos, self.rope_sin, self.fused_k,
+                None if self.k_only else self.fused_v, self.k_probe, self.scores, kivi=self.kivi,
+                k_only=self.k_only)
         if self.k_only:
             return kvf.rerotate(self.layer, self.chunks, self.max_chunk_len, self.pool_k, None,
                                 self.rope_cos, self.rope_sin, self.fused_k, None, k_only=True)
@@ -374,7 +391,12 @@ class FusedLayerGPU:
         fuse = [("recompute", "recompute_fuse", f("recompute"))]
         if self.probe or self.q8:
             fuse.append(("scatter", "recompute_fuse", f("scatter")))
-        if self.probe:
+        first = [("rerotate", "rerotate", f("rerotate"))]
+        if self.fuse_dev:
+            # the probe first: the re-positioning pass scores against it
+            first.insert(0, ("k_probe", "rerotate", f("k_probe")))
+            score = []
+        elif self.probe:
             score = [("k_probe", "score", f("k_probe")), ("score", "score", f("score"))]
         elif self.mass:
             score = [("u_probe", "score", f("u_probe")), ("score", "score", f("score"))]
@@ -385,7 +407,7 @@ class FusedLayerGPU:
         select = [("select", "select", f("select"))]
         if self.static_mask is not None:
             select.insert(0, ("static_mask", "select", f("static_mask")))
-        return ([("rerotate", "rerotate", f("rerotate"))] + score + select + fuse +
+        return (first + score + select + fuse +
                 [("attention", "attention", f("attention"))])
 
     def _stage(self, stage):

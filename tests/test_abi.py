@@ -48,7 +48,7 @@ def test_status_strings_and_version(lib):
     lib.kvf_status_string.restype = ctypes.c_char_p
     assert lib.kvf_status_string(0) == b"KVF_OK"
     assert lib.kvf_status_string(2) == b"KVF_ERR_UNSUPPORTED"
-    assert lib.kvf_abi_version() == 10
+    assert lib.kvf_abi_version() == 11
 
 
 def test_budget_matches_oracle(lib):
@@ -109,8 +109,9 @@ def test_validation_errors(lib):
     # bf16 projection of few rows splits K and needs its workspace
     bf = Layer(4096, 32, 8, 128, 1)
     need = lib.kvf_recompute_workspace_size(ctypes.byref(bf), 64, 7)
-    # 48 column tiles of 128 x 4 slices = 192 workgroups, the closest to one per
-    # CU: 4096 bytes of arrival counters, then the slices' partial sums
+    # 48 column tiles of 128 x 4 slices = 192 workgroups in one round (8
+    # slices would take two): 4096 bytes of arrival counters, then the
+    # slices' partial sums
     assert need == 4096 + 4 * 64 * (32 + 16) * 128 * 4
     assert lib.kvf_recompute_qkv(ctypes.byref(bf), FAKE, 64, None, FAKE, 64, FAKE, 7, FAKE, FAKE, 4,
                                  FAKE, FAKE, FAKE, None, 0, None, 0, None) == 3
@@ -218,6 +219,30 @@ def test_validation_errors(lib):
     # gather mode needs fused_v
     assert lib.kvf_rerotate(ctypes.byref(bfl), FAKE, 1, 4, FAKE, FAKE, None, 4,
                             FAKE, FAKE, 4, FAKE, None, 4, 0, None) == 1
+    # re-positioning with the deviation score: a row's rotation units
+    # (Hkv d / 16) must be a power of two of at most 64, accumulate 0 or 1,
+    # k_fresh and scores given, plus kvf_rerotate's own checks
+    rd = lib.kvf_rerotate_deviation
+    rd.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int32] * 2 + [ctypes.c_void_p] * 3 + [
+        ctypes.c_int64] + [ctypes.c_void_p] * 2 + [ctypes.c_int32] + [ctypes.c_void_p] * 2 + [
+        ctypes.c_int64, ctypes.c_int32] + [ctypes.c_void_p] * 2 + [ctypes.c_int32] + [ctypes.c_void_p] * 2
+    b1, keep1 = _batch([0, 8], [6])
+
+    def dev_call(layer, k_fresh=FAKE, scores=FAKE, acc=0, kivi=None, pool=(FAKE, FAKE), fv=FAKE, k_only=0):
+        return rd(ctypes.byref(layer), ctypes.byref(b1), FAKE, 1, 4, pool[0], pool[1],
+                  kivi, 8, FAKE, FAKE, 8, FAKE, fv, 8, k_only, k_fresh, None, acc, scores, None)
+    assert dev_call(Layer(256, 4, 3, 64, 1)) == 2           # 12 units per row
+    assert dev_call(Layer(4096, 32, 16, 128, 1)) == 2       # 128 units per row
+    assert dev_call(Layer(256, 4, 4, 40, 1)) == 2           # head_dim 40
+    assert dev_call(bfl, acc=2) == 1
+    assert dev_call(bfl, k_fresh=None) == 1
+    assert dev_call(bfl, scores=None) == 1
+    assert dev_call(bfl, fv=None) == 1                      # gather mode needs fused_v
+    assert dev_call(ok, kivi=ctypes.byref(kv), pool=(None, None)) == 2   # KIVI decodes to bf16 only
+    assert dev_call(bfl, kivi=ctypes.byref(kv), pool=(None, None), fv=None, k_only=1) == 2
+    bad_batch, keep2 = _batch([0, 8, 4], [6, 2])            # cu_T decreasing
+    assert rd(ctypes.byref(bfl), ctypes.byref(bad_batch), FAKE, 1, 4, FAKE, FAKE, None, 8, FAKE, FAKE,
+              8, FAKE, FAKE, 8, 0, FAKE, None, 0, FAKE, None) == 1
 
 
 def test_empty_calls_are_noops(lib):
