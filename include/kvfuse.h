@@ -288,6 +288,27 @@ kvf_status kvf_rerotate_q8(const kvf_layer_desc* layer, const kvf_chunk* chunks,
                            void* stream);
 
 /* ---------------------------------------------------------------------------
+ * kvf_rerotate_q8_deviation - kvf_rerotate_q8 and the deviation score S2b in
+ * one pass ([KVB] 4.6.2 Algorithm 2 at one layer), as kvf_rerotate_deviation
+ * is for a bf16 cache: every context row a chunk writes also gets the
+ * KVF_SCORE_DEVIATION score of kvf_score_q8, from the key as the int8 cache
+ * now stores it (min + code * scale of its own codes and statistics), at
+ * scores[cu_N[r] + i].  k_fresh: bf16 [fused->rows, Hkv, d].  eligible and
+ * accumulate as in kvf_score.  Context rows no chunk covers get no score.
+ * Errors: those of kvf_rerotate_q8; KVF_ERR_UNSUPPORTED unless Hkv * d / 8
+ * is a power of two of at most 64 and divides 256 (a row's items stay
+ * within one wave and one workgroup).
+ */
+kvf_status kvf_rerotate_q8_deviation(const kvf_layer_desc* layer, const kvf_batch* batch,
+                                     const kvf_chunk* chunks, int32_t n_chunks,
+                                     int32_t max_chunk_len, const void* pool_k,
+                                     const void* pool_v, const kvf_kivi* kivi, int64_t pool_rows,
+                                     const float* rope_cos, const float* rope_sin,
+                                     int32_t rope_n_pos, const kvf_q8_cache* fused,
+                                     const void* k_fresh, const uint8_t* eligible,
+                                     int32_t accumulate, float* scores, void* stream);
+
+/* ---------------------------------------------------------------------------
  * kvf_score - S2: one fp32 score per context token; scores [sum_r n_ctx[r]]
  * request-major.  mode: one of the modes below, optionally OR KVF_SCORE_ACCUMULATE
  * (scores[t] += this layer's score; a NaN already there stays NaN).

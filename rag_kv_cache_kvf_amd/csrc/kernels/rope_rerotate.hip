@@ -402,6 +402,11 @@ struct RotQ8Args {
   kvf_q8_cache out;
   int hkv;
   int d;
+  // deviation score of the re-positioned keys as the cache stores them
+  // (kvf_rerotate_q8_deviation; unused unless the kernel's DEV is set)
+  const bf16_t* k_fresh;          // [out.rows, Hkv, d]
+  ScoreOut dev;
+  BatchArgs B;
 };
 
 __device__ __forceinline__ void bytes4(uint32_t w, float (&x)[4]) {
@@ -435,8 +440,11 @@ __device__ __forceinline__ void encode8(const float (&lo)[4], const float (&hi)[
   }
 }
 
-// KB: 0 for a dense bf16 per-chunk cache, 8 for an 8-bit KIVI one
-template <int KB>
+// KB: 0 for a dense bf16 per-chunk cache, 8 for an 8-bit KIVI one.
+// DEV: also the deviation score of every re-positioned context row; the
+// items of a row (its Hkv heads) then sit on Hkv * d / 8 consecutive lanes,
+// a power of two dividing 64, and no row straddles two workgroups.
+template <int KB, bool DEV>
 __global__ void __launch_bounds__(64 * kQ8RotWaves) rerotate_q8_kernel(RotQ8Args a) {
   const kvf_chunk ch = a.chunks[blockIdx.x];
   if (ch.len <= 0) return;
@@ -495,8 +503,8 @@ __global__ void __launch_bounds__(64 * kQ8RotWaves) rerotate_q8_kernel(RotQ8Args
   float rlo[4], rhi[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    rlo[i] = lo[i] * cv[i] - hi[i] * sv[i];
-    rhi[i] = hi[i] * cv[i] + lo[i] * sv[i];
+    rlo[i] = rot_lo(lo[i], hi[i], cv[i], sv[i]);
+    rhi[i] = rot_hi(lo[i], hi[i], cv[i], sv[i]);
   }
   uint32_t w_lo, w_hi;
   float mn, sc;
@@ -505,6 +513,44 @@ __global__ void __launch_bounds__(64 * kQ8RotWaves) rerotate_q8_kernel(RotQ8Args
     *reinterpret_cast<uint32_t*>(a.out.k_codes + dst) = w_lo;
     *reinterpret_cast<uint32_t*>(a.out.k_codes + dst + half) = w_hi;
     if (lane_in == 0) *reinterpret_cast<float2*>(a.out.k_stats + (drow * hkv + h) * 2) = make_float2(mn, sc);
+  }
+  if constexpr (DEV) {
+    // KVBoost page, section 4.6.2, Algorithm 2 at one layer: 1 - mean over
+    // heads of cos(stored key, probe key); the stored key decodes as
+    // min + code * scale, a head's cosine 0 when either norm is 0
+    const BatchArgs& B = a.B;
+    bool ctx = valid && drow < B.cu_T[B.n_req];
+    int64_t jdx = 0;
+    if (ctx) {
+      const int r = find_segment(B.cu_T, B.n_req, static_cast<int>(drow));
+      const int64_t i = drow - B.cu_T[r];
+      ctx = i < B.n_ctx[r];
+      jdx = B.cu_N[r] + i;
+    }
+    float dot = 0.f, nx = 0.f, ny = 0.f;
+    if (ctx && score_eligible(a.dev, jdx)) {
+      const u32x2_t fl = *reinterpret_cast<const u32x2_t*>(a.k_fresh + dst);
+      const u32x2_t fh = *reinterpret_cast<const u32x2_t*>(a.k_fresh + dst + half);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float yl = __uint_as_float((i & 1) ? (fl[i >> 1] & 0xffff0000u) : (fl[i >> 1] << 16));
+        const float yh = __uint_as_float((i & 1) ? (fh[i >> 1] & 0xffff0000u) : (fh[i >> 1] << 16));
+        const float xl = fmaf(static_cast<float>((w_lo >> (8 * i)) & 0xffu), sc, mn);
+        const float xh = fmaf(static_cast<float>((w_hi >> (8 * i)) & 0xffu), sc, mn);
+        dot = fmaf(xl, yl, fmaf(xh, yh, dot));
+        nx = fmaf(xl, xl, fmaf(xh, xh, nx));
+        ny = fmaf(yl, yl, fmaf(yh, yh, ny));
+      }
+    }
+    dot = group_sum(dot, gl);
+    nx = group_sum(nx, gl);
+    ny = group_sum(ny, gl);
+    const float den = sqrtf(nx) * sqrtf(ny);
+    float cs = (lane_in == 0 && den > 0.f) ? dot / den : 0.f;
+    const int rl = hkv * gl;                       // lanes of one row
+    cs = group_sum(cs, rl);
+    if ((static_cast<int>(threadIdx.x) & (rl - 1)) == 0 && ctx)
+      store_score(a.dev, jdx, 1.f - cs / static_cast<float>(hkv));
   }
   // values: 8-bit KIVI rows are copied, dense ones encoded
   if constexpr (KB == 8) {
@@ -538,10 +584,19 @@ __global__ void __launch_bounds__(64 * kQ8RotWaves) rerotate_q8_kernel(RotQ8Args
   }
 }
 
+// Lanes of one fused row in rerotate_q8_kernel when the fused deviation
+// score supports the shape (a power of two dividing 64, rows not straddling
+// workgroups), else 0.
+int rerotate_q8_deviation_lanes(int hkv, int d) {
+  if (d % 32 != 0 || d < 32) return 0;
+  const int gl = d / 8, rl = hkv * gl, ipb = kQ8RotWaves * kWave / gl;
+  return (rl <= kWave && (rl & (rl - 1)) == 0 && ipb % hkv == 0) ? rl : 0;
+}
+
 hipError_t launch_rerotate_q8(const kvf_layer_desc& L, const kvf_chunk* chunks, int n_chunks,
                               int max_len, const void* pk, const void* pv, const kvf_kivi* q,
                               int64_t pool_rows, const float* rc, const float* rs, int rope_n,
-                              const kvf_q8_cache& fused, hipStream_t st) {
+                              const kvf_q8_cache& fused, hipStream_t st, const RotDeviation* dev) {
   RotQ8Args a{};
   a.chunks = chunks;
   a.pool_k = static_cast<const bf16_t*>(pk);
@@ -566,10 +621,20 @@ hipError_t launch_rerotate_q8(const kvf_layer_desc& L, const kvf_chunk* chunks, 
   const int64_t gy = (static_cast<int64_t>(max_len) * L.n_kv_heads + ipb - 1) / ipb;
   if (gy > 65535) return hipErrorInvalidValue;
   const dim3 grid(n_chunks, static_cast<unsigned>(gy));
-  if (q)
-    hipLaunchKernelGGL((rerotate_q8_kernel<8>), grid, dim3(64 * kQ8RotWaves), 0, st, a);
-  else
-    hipLaunchKernelGGL((rerotate_q8_kernel<0>), grid, dim3(64 * kQ8RotWaves), 0, st, a);
+  if (dev) {
+    if (rerotate_q8_deviation_lanes(a.hkv, a.d) == 0) return hipErrorInvalidValue;
+    a.k_fresh = static_cast<const bf16_t*>(dev->k_fresh);
+    a.dev = dev->out;
+    a.B = dev->B;
+    if (q)
+      hipLaunchKernelGGL((rerotate_q8_kernel<8, true>), grid, dim3(64 * kQ8RotWaves), 0, st, a);
+    else
+      hipLaunchKernelGGL((rerotate_q8_kernel<0, true>), grid, dim3(64 * kQ8RotWaves), 0, st, a);
+  } else if (q) {
+    hipLaunchKernelGGL((rerotate_q8_kernel<8, false>), grid, dim3(64 * kQ8RotWaves), 0, st, a);
+  } else {
+    hipLaunchKernelGGL((rerotate_q8_kernel<0, false>), grid, dim3(64 * kQ8RotWaves), 0, st, a);
+  }
   return hipGetLastError();
 }
 

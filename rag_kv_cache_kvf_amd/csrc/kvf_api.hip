@@ -169,14 +169,16 @@ kvf_status kvf_rope_table(double base, int32_t head_dim, int32_t n_pos, float* c
   KVF_GUARD_END
 }
 
-kvf_status kvf_rerotate(const kvf_layer_desc* layer, const kvf_chunk* chunks, int32_t n_chunks,
-                        int32_t max_chunk_len, const void* pool_k, const void* pool_v,
-                        const kvf_kivi* kivi, int64_t pool_rows, const float* rope_cos,
-                        const float* rope_sin, int32_t rope_n_pos, void* fused_k, void* fused_v,
-                        int64_t fused_rows, int32_t k_only, void* stream) {
-  KVF_GUARD_BEGIN
-  kvf_status st = check_layer(layer);
-  if (st != KVF_OK) return st;
+namespace {
+
+// kvf_rerotate's checks and launch; dev (optional) adds the deviation score
+// of kvf_rerotate_deviation, whose own checks the caller has made.
+kvf_status rerotate_impl(const kvf_layer_desc* layer, const kvf_chunk* chunks, int32_t n_chunks,
+                         int32_t max_chunk_len, const void* pool_k, const void* pool_v,
+                         const kvf_kivi* kivi, int64_t pool_rows, const float* rope_cos,
+                         const float* rope_sin, int32_t rope_n_pos, void* fused_k, void* fused_v,
+                         int64_t fused_rows, int32_t k_only, const kvf::RotDeviation* dev,
+                         void* stream, const char* name) {
   KVF_CHECK(n_chunks >= 0 && max_chunk_len >= 0 && pool_rows >= 0 && fused_rows >= 0 &&
                 rope_n_pos >= 0, KVF_ERR_INVALID_ARG, "negative size");
   KVF_CHECK(k_only == 0 || k_only == 1, KVF_ERR_INVALID_ARG, "k_only must be 0 or 1");
@@ -202,79 +204,20 @@ kvf_status kvf_rerotate(const kvf_layer_desc* layer, const kvf_chunk* chunks, in
   KVF_CHECK(max_chunk_len <= (1 << 24), KVF_ERR_UNSUPPORTED, "max_chunk_len too large");
   return finish(kvf::launch_rerotate(*layer, chunks, n_chunks, max_chunk_len, pool_k, pool_v,
                                        kivi, pool_rows, rope_cos, rope_sin, rope_n_pos, fused_k,
-                                       fused_v, fused_rows, k_only, as_stream(stream)),
-                as_stream(stream), "kvf_rerotate");
-  KVF_GUARD_END
+                                       fused_v, fused_rows, k_only, as_stream(stream), dev),
+                as_stream(stream), name);
 }
 
-kvf_status kvf_rerotate_deviation(const kvf_layer_desc* layer, const kvf_batch* batch,
-                                  const kvf_chunk* chunks, int32_t n_chunks, int32_t max_chunk_len,
-                                  const void* pool_k, const void* pool_v, const kvf_kivi* kivi,
-                                  int64_t pool_rows, const float* rope_cos, const float* rope_sin,
-                                  int32_t rope_n_pos, void* fused_k, void* fused_v,
-                                  int64_t fused_rows, int32_t k_only, const void* k_fresh,
-                                  const uint8_t* eligible, int32_t accumulate, float* scores,
-                                  void* stream) {
-  KVF_GUARD_BEGIN
-  kvf_status st = check_layer(layer);
-  if (st != KVF_OK) return st;
-  kvf::BatchArgs B;
-  st = check_batch(batch, &B);
-  if (st != KVF_OK) return st;
-  KVF_CHECK(accumulate == 0 || accumulate == 1, KVF_ERR_INVALID_ARG, "accumulate must be 0 or 1");
-  KVF_CHECK(kvf::rerotate_deviation_lanes(layer->n_kv_heads, layer->head_dim) > 0,
-            KVF_ERR_UNSUPPORTED,
-            "the fused deviation score needs Hkv * d / 16 a power of two of at most 64 (Hkv %d, d %d)",
-            layer->n_kv_heads, layer->head_dim);
-  KVF_CHECK(n_chunks >= 0 && max_chunk_len >= 0 && pool_rows >= 0 && fused_rows >= 0 &&
-                rope_n_pos >= 0, KVF_ERR_INVALID_ARG, "negative size");
-  KVF_CHECK(k_only == 0 || k_only == 1, KVF_ERR_INVALID_ARG, "k_only must be 0 or 1");
-  if (n_chunks == 0 || max_chunk_len == 0 || B.cu_N[B.n_req] == 0) {
-    // no row is re-positioned or no context row is scored: the plain pass
-    return kvf_rerotate(layer, chunks, n_chunks, max_chunk_len, pool_k, pool_v, kivi, pool_rows,
-                        rope_cos, rope_sin, rope_n_pos, fused_k, fused_v, fused_rows, k_only,
-                        stream);
-  }
-  KVF_CHECK(k_fresh && scores, KVF_ERR_INVALID_ARG, "k_fresh or scores is NULL");
-  KVF_CHECK(chunks && rope_cos && rope_sin && fused_k && (k_only || fused_v), KVF_ERR_INVALID_ARG,
-            "required pointer is NULL");
-  if (k_only) {
-    KVF_CHECK(kivi == nullptr, KVF_ERR_UNSUPPORTED,
-              "keys-only re-positioning reads a dense cache (KIVI codes decode to new buffers)");
-    KVF_CHECK(pool_k != nullptr, KVF_ERR_INVALID_ARG, "pool_k is NULL");
-  } else if (kivi) {
-    KVF_CHECK(layer->dtype == KVF_BF16, KVF_ERR_UNSUPPORTED, "KIVI caches decode to bf16 only");
-    KVF_CHECK(kivi->bits == 8 || kivi->bits == 4, KVF_ERR_UNSUPPORTED,
-              "KIVI codes are 8 or 4 bits, not %d", kivi->bits);
-    KVF_CHECK(pool_k == nullptr && pool_v == nullptr, KVF_ERR_INVALID_ARG,
-              "pass either dense pool pointers or kivi, not both");
-    KVF_CHECK(kivi->k_codes && kivi->v_codes && kivi->k_min && kivi->k_scale && kivi->v_min &&
-                  kivi->v_scale && kivi->n_pool_chunks > 0, KVF_ERR_INVALID_ARG,
-              "incomplete kvf_kivi");
-  } else {
-    KVF_CHECK(pool_k && pool_v, KVF_ERR_INVALID_ARG, "pool pointers are NULL");
-  }
-  KVF_CHECK(max_chunk_len <= (1 << 24), KVF_ERR_UNSUPPORTED, "max_chunk_len too large");
-  const kvf::RotDeviation dev{k_fresh, kvf::ScoreOut{scores, eligible, accumulate}, B};
-  return finish(kvf::launch_rerotate(*layer, chunks, n_chunks, max_chunk_len, pool_k, pool_v,
-                                       kivi, pool_rows, rope_cos, rope_sin, rope_n_pos, fused_k,
-                                       fused_v, fused_rows, k_only, as_stream(stream), &dev),
-                as_stream(stream), "kvf_rerotate_deviation");
-  KVF_GUARD_END
-}
-
-kvf_status kvf_rerotate_q8(const kvf_layer_desc* layer, const kvf_chunk* chunks, int32_t n_chunks,
-                           int32_t max_chunk_len, const void* pool_k, const void* pool_v,
-                           const kvf_kivi* kivi, int64_t pool_rows, const float* rope_cos,
-                           const float* rope_sin, int32_t rope_n_pos, const kvf_q8_cache* fused,
-                           void* stream) {
-  KVF_GUARD_BEGIN
-  kvf_status st = check_layer(layer);
-  if (st != KVF_OK) return st;
+// kvf_rerotate_q8's checks and launch (dev as in rerotate_impl)
+kvf_status rerotate_q8_impl(const kvf_layer_desc* layer, const kvf_chunk* chunks, int32_t n_chunks,
+                            int32_t max_chunk_len, const void* pool_k, const void* pool_v,
+                            const kvf_kivi* kivi, int64_t pool_rows, const float* rope_cos,
+                            const float* rope_sin, int32_t rope_n_pos, const kvf_q8_cache* fused,
+                            const kvf::RotDeviation* dev, void* stream, const char* name) {
   KVF_CHECK(layer->dtype == KVF_BF16, KVF_ERR_UNSUPPORTED, "int8-resident caches need a bf16 layer");
   KVF_CHECK(n_chunks >= 0 && max_chunk_len >= 0 && pool_rows >= 0 && rope_n_pos >= 0,
             KVF_ERR_INVALID_ARG, "negative size");
-  st = check_q8(fused, 0);
+  kvf_status st = check_q8(fused, 0);
   if (st != KVF_OK) return st;
   if (n_chunks == 0 || max_chunk_len == 0) return KVF_OK;
   KVF_CHECK(chunks && rope_cos && rope_sin, KVF_ERR_INVALID_ARG, "required pointer is NULL");
@@ -292,8 +235,99 @@ kvf_status kvf_rerotate_q8(const kvf_layer_desc* layer, const kvf_chunk* chunks,
   KVF_CHECK(max_chunk_len <= (1 << 24), KVF_ERR_UNSUPPORTED, "max_chunk_len too large");
   return finish(kvf::launch_rerotate_q8(*layer, chunks, n_chunks, max_chunk_len, pool_k, pool_v,
                                           kivi, pool_rows, rope_cos, rope_sin, rope_n_pos, *fused,
-                                          as_stream(stream)),
-                as_stream(stream), "kvf_rerotate_q8");
+                                          as_stream(stream), dev),
+                as_stream(stream), name);
+}
+
+// The deviation-score half of kvf_rerotate_deviation / kvf_rerotate_q8_deviation:
+// checks its arguments and fills *dev; *skip when no context row is scored.
+kvf_status deviation_args(const kvf_layer_desc* layer, const kvf_batch* batch, int ok_lanes,
+                          const void* k_fresh, const uint8_t* eligible, int32_t accumulate,
+                          float* scores, kvf::RotDeviation* dev, bool* skip) {
+  kvf_status st = check_batch(batch, &dev->B);
+  if (st != KVF_OK) return st;
+  KVF_CHECK(accumulate == 0 || accumulate == 1, KVF_ERR_INVALID_ARG, "accumulate must be 0 or 1");
+  KVF_CHECK(ok_lanes > 0, KVF_ERR_UNSUPPORTED,
+            "the fused deviation score reduces a row within one wave: Hkv %d, d %d is not supported",
+            layer->n_kv_heads, layer->head_dim);
+  *skip = dev->B.cu_N[dev->B.n_req] == 0;
+  if (!*skip) KVF_CHECK(k_fresh && scores, KVF_ERR_INVALID_ARG, "k_fresh or scores is NULL");
+  dev->k_fresh = k_fresh;
+  dev->out = kvf::ScoreOut{scores, eligible, accumulate};
+  return KVF_OK;
+}
+
+}  // namespace
+
+kvf_status kvf_rerotate(const kvf_layer_desc* layer, const kvf_chunk* chunks, int32_t n_chunks,
+                        int32_t max_chunk_len, const void* pool_k, const void* pool_v,
+                        const kvf_kivi* kivi, int64_t pool_rows, const float* rope_cos,
+                        const float* rope_sin, int32_t rope_n_pos, void* fused_k, void* fused_v,
+                        int64_t fused_rows, int32_t k_only, void* stream) {
+  KVF_GUARD_BEGIN
+  kvf_status st = check_layer(layer);
+  if (st != KVF_OK) return st;
+  return rerotate_impl(layer, chunks, n_chunks, max_chunk_len, pool_k, pool_v, kivi, pool_rows,
+                       rope_cos, rope_sin, rope_n_pos, fused_k, fused_v, fused_rows, k_only,
+                       nullptr, stream, "kvf_rerotate");
+  KVF_GUARD_END
+}
+
+kvf_status kvf_rerotate_deviation(const kvf_layer_desc* layer, const kvf_batch* batch,
+                                  const kvf_chunk* chunks, int32_t n_chunks, int32_t max_chunk_len,
+                                  const void* pool_k, const void* pool_v, const kvf_kivi* kivi,
+                                  int64_t pool_rows, const float* rope_cos, const float* rope_sin,
+                                  int32_t rope_n_pos, void* fused_k, void* fused_v,
+                                  int64_t fused_rows, int32_t k_only, const void* k_fresh,
+                                  const uint8_t* eligible, int32_t accumulate, float* scores,
+                                  void* stream) {
+  KVF_GUARD_BEGIN
+  kvf_status st = check_layer(layer);
+  if (st != KVF_OK) return st;
+  kvf::RotDeviation dev;
+  bool skip = false;
+  st = deviation_args(layer, batch, kvf::rerotate_deviation_lanes(layer->n_kv_heads, layer->head_dim),
+                      k_fresh, eligible, accumulate, scores, &dev, &skip);
+  if (st != KVF_OK) return st;
+  return rerotate_impl(layer, chunks, n_chunks, max_chunk_len, pool_k, pool_v, kivi, pool_rows,
+                       rope_cos, rope_sin, rope_n_pos, fused_k, fused_v, fused_rows, k_only,
+                       skip ? nullptr : &dev, stream, "kvf_rerotate_deviation");
+  KVF_GUARD_END
+}
+
+kvf_status kvf_rerotate_q8(const kvf_layer_desc* layer, const kvf_chunk* chunks, int32_t n_chunks,
+                           int32_t max_chunk_len, const void* pool_k, const void* pool_v,
+                           const kvf_kivi* kivi, int64_t pool_rows, const float* rope_cos,
+                           const float* rope_sin, int32_t rope_n_pos, const kvf_q8_cache* fused,
+                           void* stream) {
+  KVF_GUARD_BEGIN
+  kvf_status st = check_layer(layer);
+  if (st != KVF_OK) return st;
+  return rerotate_q8_impl(layer, chunks, n_chunks, max_chunk_len, pool_k, pool_v, kivi, pool_rows,
+                          rope_cos, rope_sin, rope_n_pos, fused, nullptr, stream, "kvf_rerotate_q8");
+  KVF_GUARD_END
+}
+
+kvf_status kvf_rerotate_q8_deviation(const kvf_layer_desc* layer, const kvf_batch* batch,
+                                     const kvf_chunk* chunks, int32_t n_chunks,
+                                     int32_t max_chunk_len, const void* pool_k, const void* pool_v,
+                                     const kvf_kivi* kivi, int64_t pool_rows, const float* rope_cos,
+                                     const float* rope_sin, int32_t rope_n_pos,
+                                     const kvf_q8_cache* fused, const void* k_fresh,
+                                     const uint8_t* eligible, int32_t accumulate, float* scores,
+                                     void* stream) {
+  KVF_GUARD_BEGIN
+  kvf_status st = check_layer(layer);
+  if (st != KVF_OK) return st;
+  kvf::RotDeviation dev;
+  bool skip = false;
+  st = deviation_args(layer, batch,
+                      kvf::rerotate_q8_deviation_lanes(layer->n_kv_heads, layer->head_dim), k_fresh,
+                      eligible, accumulate, scores, &dev, &skip);
+  if (st != KVF_OK) return st;
+  return rerotate_q8_impl(layer, chunks, n_chunks, max_chunk_len, pool_k, pool_v, kivi, pool_rows,
+                          rope_cos, rope_sin, rope_n_pos, fused, skip ? nullptr : &dev, stream,
+                          "kvf_rerotate_q8_deviation");
   KVF_GUARD_END
 }
 

@@ -275,10 +275,14 @@ hipError_t launch_rerotate(const kvf_layer_desc& L, const kvf_chunk* chunks, int
                            void* fk, void* fv, int64_t fused_rows, int k_only, hipStream_t st,
                            const RotDeviation* dev = nullptr);
 // int8-resident fused cache (kvf_q8_cache)
+// rows' lanes in the int8-resident pass if its fused deviation score supports
+// the shape, else 0
+int rerotate_q8_deviation_lanes(int hkv, int d);
 hipError_t launch_rerotate_q8(const kvf_layer_desc& L, const kvf_chunk* chunks, int n_chunks,
                               int max_len, const void* pk, const void* pv, const kvf_kivi* q,
                               int64_t pool_rows, const float* rc, const float* rs, int rope_n,
-                              const kvf_q8_cache& fused, hipStream_t st);
+                              const kvf_q8_cache& fused, hipStream_t st,
+                              const RotDeviation* dev = nullptr);
 hipError_t launch_scatter_q8(const kvf_layer_desc& L, const void* ks, const int32_t* ksr,
                              int64_t ks_rows, const void* vs, const int32_t* vsr, int64_t vs_rows,
                              const int32_t* dst, int M, const kvf_q8_cache& fused, hipStream_t st);

@@ -106,6 +106,9 @@ _SIGS = {
     "kvf_attention_workspace_size": (_SZ, [_LP, _BP, _IP]),
     "kvf_rerotate_q8": (_I32, [_LP, _P, _I32, _I32, _P, _P, ctypes.POINTER(KiviDesc), _I64, _P, _P,
                                _I32, ctypes.POINTER(Q8CacheDesc), _P]),
+    "kvf_rerotate_q8_deviation": (_I32, [_LP, _BP, _P, _I32, _I32, _P, _P, ctypes.POINTER(KiviDesc),
+                                         _I64, _P, _P, _I32, ctypes.POINTER(Q8CacheDesc), _P, _P,
+                                         _I32, _P, _P]),
     "kvf_score_q8": (_I32, [_I32, _LP, _BP, ctypes.POINTER(Q8CacheDesc), _P, _P, _P, _P]),
     "kvf_scatter_kv_q8": (_I32, [_LP, _P, _P, _I64, _P, _P, _I64, _P, _I32,
                                  ctypes.POINTER(Q8CacheDesc), _P]),
@@ -481,6 +484,29 @@ def q8_cache(rows: int, n_kv_heads: int, head_dim: int, device="cuda") -> dict:
 def _q8_desc(c: dict) -> Q8CacheDesc:
     return Q8CacheDesc(_ptr(c["k_codes"]), _ptr(c["v_codes"]), _ptr(c["k_stats"]),
                        _ptr(c["v_stats"]), int(c["k_codes"].shape[0]))
+
+
+def rerotate_q8_deviation(layer: Layer, batch: Batch, chunks: torch.Tensor, max_chunk_len: int,
+                          pool_k: Optional[torch.Tensor], pool_v: Optional[torch.Tensor],
+                          rope_cos: torch.Tensor, rope_sin: torch.Tensor, fused: dict,
+                          k_fresh: torch.Tensor, scores: torch.Tensor, kivi: Optional[dict] = None,
+                          eligible: Optional[torch.Tensor] = None, accumulate: bool = False,
+                          stream=None):
+    """kvf_rerotate_q8_deviation: rerotate_q8() plus the deviation score of
+    every re-positioned context row against k_fresh (bf16 [rows, Hkv, d])."""
+    kd = None
+    pool_rows = _rows(pool_k)
+    if kivi is not None:
+        kd = ctypes.byref(_kivi_desc(kivi))
+        pool_rows = int(kivi["k_codes"].shape[0])
+    d = layer.desc()
+    fd = _q8_desc(fused)
+    return _run(_lib.kvf_rerotate_q8_deviation,
+                (ctypes.byref(d), ctypes.byref(batch.desc), _ptr(chunks), int(chunks.shape[0]),
+                 max_chunk_len, _ptr(pool_k), _ptr(pool_v), kd, pool_rows, _ptr(rope_cos),
+                 _ptr(rope_sin), int(rope_cos.shape[0]), ctypes.byref(fd), _ptr(k_fresh),
+                 _ptr(eligible), 1 if accumulate else 0, _ptr(scores)),
+                "kvf_rerotate_q8_deviation", stream, keep=(d, fd, batch))
 
 
 def rerotate_q8(layer: Layer, chunks: torch.Tensor, max_chunk_len: int,

@@ -27,8 +27,8 @@ itself.  Order (all on one stream, no host synchronisation):
   A score selector with static rules takes their positions as a forced set
   (kvf_select_static before kvf_select_topk).
   int8-resident fused cache (KVBoost page, section 4.5, Eq. 7 kept by the
-  fused cache; section 7.3): the same order with kvf_rerotate_q8,
-  kvf_score_q8 and kvf_sparse_q_attention_q8, and the recomputed K/V written
+  fused cache; section 7.3): the same order with kvf_rerotate_q8_deviation
+  (or kvf_rerotate_q8 and kvf_score_q8) and kvf_sparse_q_attention_q8, and the recomputed K/V written
   to compact bf16 rows that kvf_scatter_kv_q8 encodes into the cache.
 
 The per-chunk caches are built ahead of serving (QCFuse page, section 2.1.2,
@@ -70,10 +70,11 @@ class FusedLayerGPU:
     k_only False, or for a shared chunk pool or KIVI codes, the pass gathers
     keys and values from the per-chunk caches itself.
 
-    fuse_deviation (deviation mode, bf16 or fp32 fused cache): the key probe
-    runs first and the re-positioning pass scores every context row as it
-    writes its key (kvf_rerotate_deviation), so the score does not read the
-    fused keys back; False keeps kvf_rerotate and kvf_score apart."""
+    fuse_deviation (deviation mode): the key probe runs first and the
+    re-positioning pass scores every context row as it writes its key
+    (kvf_rerotate_deviation, or kvf_rerotate_q8_deviation for the
+    int8-resident cache), so the score does not read the fused keys back;
+    False keeps the re-positioning and the score apart."""
 
     def __init__(self, batch: SynthBatch, ratio_pct: int, device="cuda",
                  pic: Optional[dict] = None, n_last_q: int = 0, mode: Optional[str] = None,
@@ -91,9 +92,12 @@ class FusedLayerGPU:
         # the key probe of deviation scoring; other selectors project P+U only
         self.probe = self.selector == "score" and self.mode == "deviation"
         self.mass = self.selector == "score" and self.mode != "deviation"
-        ku = wl.n_kv_heads * wl.head_dim // 16     # rotation units of a row: one wave reduces them
-        self.fuse_dev = (fuse_deviation and self.probe and not self.q8 and wl.head_dim % 16 == 0
-                         and 1 <= ku <= 64 and ku & (ku - 1) == 0)
+        # the fused score reduces a row's key within one wave: its lanes (bf16
+        # or fp32 cache: Hkv d / 16 rotation units; int8-resident: Hkv d / 8
+        # lanes, a row within one 256-thread workgroup) a power of two <= 64
+        rl = wl.n_kv_heads * wl.head_dim // (8 if self.q8 else 16)
+        self.fuse_dev = (fuse_deviation and self.probe and wl.head_dim % (32 if self.q8 else 16) == 0
+                         and 1 <= rl <= 64 and rl & (rl - 1) == 0)
         self.n_last_q = n_last_q
         self.device = torch.device(device)
         dev = self.device
@@ -251,6 +255,10 @@ class FusedLayerGPU:
 
     # ------------------------------------------------------------------ calls
     def _rerotate(self):
+        if self.q8 and self.fuse_dev:
+            return kvf.rerotate_q8_deviation(self.layer, self.kb, self.chunks, self.max_chunk_len,
+                                             self.pool_k, self.pool_v, self.rope_cos, self.rope_sin,
+                                             self.fused, self.k_probe, self.scores, kivi=self.kivi)
         if self.q8:
             return kvf.rerotate_q8(self.layer, self.chunks, self.max_chunk_len, self.pool_k, self.pool_v,
                                    self.rope_cos, self.rope_sin, self.fused, kivi=self.kivi)

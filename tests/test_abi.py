@@ -367,6 +367,26 @@ def test_q8_validation(lib):
               ctypes.byref(partial), None) == 1
     assert rr(ctypes.byref(bf), FAKE, 0, 4, FAKE, FAKE, None, 4, FAKE, FAKE, 4,
               ctypes.byref(c), None) == 0                      # no chunks: nothing to do
+    # with the deviation score in the same pass: a row's lanes (Hkv d / 8)
+    # a power of two of at most 64, accumulate 0 or 1, k_fresh and scores,
+    # then kvf_rerotate_q8's own checks
+    rqd = lib.kvf_rerotate_q8_deviation
+    rqd.argtypes = [P, P, P, I32, I32, P, P, P, I64, P, P, I32, P, P, P, I32, P, P]
+    bq, keepq = _batch([0, 60, 100], [50, 30])
+
+    def q8dev(layer, kv=None, pool=(FAKE, FAKE), cache=c, k_fresh=FAKE, scores=FAKE, acc=0):
+        return rqd(ctypes.byref(layer), ctypes.byref(bq), FAKE, 1, 4, pool[0], pool[1], kv, 4, FAKE,
+                   FAKE, 4, None if cache is None else ctypes.byref(cache), k_fresh, None, acc, scores,
+                   None)
+    assert q8dev(Layer(4096, 32, 8, 128, 1)) == 2              # 128 lanes per row
+    assert q8dev(Layer(2048, 16, 2, 96, 1)) == 2               # head_dim 96
+    assert q8dev(bf, acc=3) == 1
+    assert q8dev(bf, k_fresh=None) == 1
+    assert q8dev(bf, scores=None) == 1
+    assert q8dev(f32) == 2                                     # bf16 layers only
+    assert q8dev(bf, kv=ctypes.byref(k4), pool=(None, None)) == 2
+    assert q8dev(bf, cache=None) == 1
+    assert q8dev(bf, cache=partial) == 1
     b, keep = _batch([0, 60, 100], [50, 30])
     sq = lib.kvf_score_q8
     assert sq(1, ctypes.byref(bf), ctypes.byref(b), ctypes.byref(c), FAKE, None, FAKE, None) == 2

@@ -120,6 +120,79 @@ def test_rerotate_q8(kvf, name):
     assert not got.k_codes[q].any() and not got.k_stats[q].any() and not got.v_stats[q].any()
 
 
+@pytest.mark.parametrize("name,variant", [("mini_bf16_kivi8", "plain"), ("mini_bf16_dev_pool", "eligible_acc"),
+                                          ("qwen25_3b_kivi8", "plain")])
+def test_rerotate_q8_deviation(kvf, name, variant):
+    """S1 into the int8-resident cache with the deviation score in the same
+    pass (kvf_rerotate_q8_deviation): the cache bit for bit as
+    kvf_rerotate_q8 writes it, the scores as kvf_score_q8 computes them from
+    that cache (to fp32 summation order; NaN where ineligible, added to the
+    previous scores when accumulating), and against the oracle: the
+    deviation of the oracle's int8-resident cache keys from the probe keys,
+    within the bf16 layer's tolerance."""
+    import torch
+    b = synth.make_batch(name)
+    wl = b.wl
+    hkv, d = wl.n_kv_heads, wl.head_dim
+    print(f"[case] rerotate_q8_deviation {name} {variant}", flush=True)
+    lo = fusion.Layer(wl.hidden, wl.n_q_heads, hkv, d, wl.rope_base)
+    pk = _bf(synth.random_normal((b.pool_rows, hkv, d), 15, "q8dev_k").astype(np.float64))
+    pv = _bf(synth.random_normal((b.pool_rows, hkv, d), 15, "q8dev_v").astype(np.float64))
+    L = kvf.Layer(wl.hidden, wl.n_q_heads, hkv, d, "bf16")
+    c, s = _rope(kvf, wl.rope_base, d, int(np.diff(b.cu_T).max()))
+    ch = to_gpu(b.chunk_table)
+    max_len = int(b.chunk_table[:, 3].max())
+    if wl.kivi_bits == 8:
+        kc, kmin, ksc = kivi.encode_keys(pk.astype(np.float32), b.pool_cu)
+        vc, vmin, vsc = kivi.encode_values(pv.astype(np.float32))
+        pq = {"k_codes": kc, "k_min": kmin, "k_scale": ksc, "v_codes": vc, "v_min": vmin, "v_scale": vsc}
+        kq = {k: to_gpu(v) for k, v in pq.items()}
+        pool = (None, None)
+        ref = q8cache.stitch(b.chunk_table, b.total_rows, lo, pool_q8=pq, pool_cu=b.pool_cu)
+        src_k = kivi.decode_keys(kc, kmin, ksc, b.pool_cu)
+    else:
+        kq = None
+        pool = (to_gpu(encode(pk, "bf16")), to_gpu(encode(pv, "bf16")))
+        ref = q8cache.stitch(b.chunk_table, b.total_rows, lo, pool_k=pk, pool_v=pv)
+        src_k = pk
+    exact_k, _ = fusion.rerotate_stitch(src_k, np.zeros_like(src_k), b.chunk_table, b.total_rows, lo)
+    kf = exact_k + 0.3 * synth.random_normal(exact_k.shape, 16, "q8dev_fresh").astype(np.float64)
+    ctx = b.context_rows()
+    kf[ctx[5], hkv - 1] = 0.0                     # a zero-norm head: cos := 0
+    kf_s = encode(kf, "bf16")
+    n_sum = int(np.sum(b.n_ctx))
+    elig, prefill = None, np.zeros(n_sum, dtype=np.float32)
+    if variant == "eligible_acc":
+        elig = (synth.random_rows(n_sum, n_sum, 17) % 5 != 0).astype(np.uint8)
+        prefill = (0.5 + 0.003 * np.arange(n_sum) % 1.0).astype(np.float32)
+    el_g = None if elig is None else to_gpu(elig)
+    acc = variant == "eligible_acc"
+    kb = kvf.Batch(b.cu_T, b.n_ctx)
+    kf_g = to_gpu(kf_s)
+    g1 = kvf.q8_cache(b.total_rows, hkv, d)
+    g2 = kvf.q8_cache(b.total_rows, hkv, d)
+    sc1, sc2 = to_gpu(prefill.copy()), to_gpu(prefill.copy())
+    kvf.rerotate_q8_deviation(L, kb, ch, max_len, pool[0], pool[1], c, s, g1, kf_g, sc1, kivi=kq,
+                              eligible=el_g, accumulate=acc)
+    kvf.rerotate_q8(L, ch, max_len, pool[0], pool[1], c, s, g2, kivi=kq)
+    kvf.score_q8(kvf.KVF_SCORE_DEVIATION, L, kb, g2, kf_g, sc2, eligible=el_g, accumulate=acc)
+    torch.cuda.synchronize()
+    got1, got2 = _download(g1), _download(g2)
+    for f in ("k_codes", "k_stats", "v_codes", "v_stats"):
+        assert np.array_equal(getattr(got1, f), getattr(got2, f)), f"{name}: {f} differ from kvf_rerotate_q8's"
+    s1, s2 = raw(sc1).astype(np.float64), raw(sc2).astype(np.float64)
+    nan1 = np.isnan(s1)
+    assert np.array_equal(nan1, np.isnan(s2))
+    assert np.array_equal(nan1, elig == 0) if elig is not None else not nan1.any()
+    keep = ~nan1
+    assert np.max(np.abs(s1[keep] - s2[keep])) < 2e-6, np.max(np.abs(s1[keep] - s2[keep]))
+    refk = q8cache.decode_k(ref)
+    want = np.concatenate([fusion.deviation(refk[b.cu_T[r]:b.cu_T[r] + b.n_ctx[r]],
+                                            decode(kf_s, "bf16")[b.cu_T[r]:b.cu_T[r] + b.n_ctx[r]])
+                           for r in range(b.n_req)]) + prefill.astype(np.float64)
+    assert_close(s1[keep], want[keep], "bf16", f"{name} {variant} int8-resident fused deviation score")
+
+
 @pytest.mark.parametrize("hkv,d,M", [(2, 128, 300), (8, 128, 77), (3, 64, 129), (1, 64, 40)])
 def test_scatter_q8_bit_exact(kvf, hkv, d, M):
     """S5 into the int8-resident cache: every destination row is the oracle's
