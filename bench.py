@@ -141,7 +141,7 @@ def call_work(g):
             work["score"] = ("hbm", n_ctx * ((q8row if g.q8 else krow) + krow + 4))   # fused K, probe K -> fp32
         work["recompute"] = ("mfma", 2.0 * hid * d * (hq + hkv) * M)
     else:
-        work["u_probe"] = ("mfma", 2.0 * hid * d * (hq + 2 * hkv) * nU)
+        work["u_probe"] = ("mfma", 2.0 * hid * d * (hq + hkv) * nU)    # Q and K of the query rows
         flops = 0.0
         for r in range(b.n_req):
             U = b.n_query(r)

@@ -12,7 +12,7 @@ itself.  Order (all on one stream, no host synchronisation):
     kvf_recompute_qkv(P+U, Q|V; V straight into the fused cache) ->
     kvf_scatter_kv(K of P+U from the probe) -> kvf_sparse_q_attention
   attention-mass mode (QCFuse page, section 3.2.1 at one layer)
-    kvf_rerotate -> kvf_recompute_qkv(U, Q|K|V; K/V into the fused cache) ->
+    kvf_rerotate -> kvf_recompute_qkv(U, Q|K; K into the fused cache) ->
     kvf_score(ATTN_MASS) -> kvf_select_topk ->
     kvf_recompute_qkv(P+U, Q|K|V; K/V into the fused cache) ->
     kvf_sparse_q_attention
@@ -242,7 +242,7 @@ class FusedLayerGPU:
         if self.probe:
             need.append(kvf.recompute_workspace_size(L, T_total, kvf.KVF_OUT_K))
         elif self.mass:
-            need.append(kvf.recompute_workspace_size(L, nU, QKV))
+            need.append(kvf.recompute_workspace_size(L, nU, kvf.KVF_OUT_Q | kvf.KVF_OUT_K))
         # zeroed: split projections keep arrival counters at its start
         self.gemm_ws = torch.zeros(max(max(need), 1), dtype=torch.uint8, device=dev)
         # key-split workspace of the attention call: zero-filled once, every
@@ -288,15 +288,17 @@ class FusedLayerGPU:
                                  self.rope_cos, self.rope_sin, k_out=self.k_probe, workspace=self.gemm_ws)
 
     def _u_probe(self):
+        # Q and K of the query rows only: the score reads the query keys (the
+        # causal part of each query row) but no values, and the recompute of
+        # P + U writes the query rows' K and V before attention reads them
+        mask = kvf.KVF_OUT_Q | kvf.KVF_OUT_K
         if self.u_span is not None:
             a, b = self.u_span
-            return kvf.recompute_qkv(self.layer, self.x[a:b], None, self.u_pos, self.w,
-                                     kvf.KVF_OUT_Q | kvf.KVF_OUT_K | kvf.KVF_OUT_V, self.rope_cos,
-                                     self.rope_sin, q_out=self.q_u, k_out=self.fused_k, v_out=self.fused_v,
+            return kvf.recompute_qkv(self.layer, self.x[a:b], None, self.u_pos, self.w, mask,
+                                     self.rope_cos, self.rope_sin, q_out=self.q_u, k_out=self.fused_k,
                                      kv_out_row=self.u_rows, workspace=self.gemm_ws)
-        return kvf.recompute_qkv(self.layer, self.x, self.u_rows, self.u_pos, self.w,
-                                 kvf.KVF_OUT_Q | kvf.KVF_OUT_K | kvf.KVF_OUT_V, self.rope_cos,
-                                 self.rope_sin, q_out=self.q_u, k_out=self.fused_k, v_out=self.fused_v,
+        return kvf.recompute_qkv(self.layer, self.x, self.u_rows, self.u_pos, self.w, mask,
+                                 self.rope_cos, self.rope_sin, q_out=self.q_u, k_out=self.fused_k,
                                  kv_out_row=self.u_rows, workspace=self.gemm_ws)
 
     def _static_mask(self):

@@ -503,7 +503,7 @@ def test_recompute_kv_destination_rows(kvf, dtype, hidden, M):
 
 
 @pytest.mark.parametrize("wl_name,kind", [("qwen3_8b_mass", "p_and_u"), ("qwen3_8b_mass", "u_probe"),
-                                          ("llama3_70b_mass", "p_and_u"),
+                                          ("llama3_70b_mass", "p_and_u"), ("llama3_70b_mass", "u_probe"),
                                           ("qwen25_3b_kivi8", "probe_all")])
 def test_recompute_full_size_sampled(kvf, wl_name, kind):
     import torch
@@ -521,8 +521,9 @@ def test_recompute_full_size_sampled(kvf, wl_name, kind):
         rows = np.concatenate([synth.random_rows(N, k, 12), np.arange(N, T, dtype=np.int32)])
         mask = 7
     elif kind == "u_probe":
+        # the query rows' Q and K (what the attention-mass score reads)
         rows = np.arange(N, T, dtype=np.int32)
-        mask = 7
+        mask = 3
     else:
         rows = np.arange(rows_total, dtype=np.int32)
         mask = 2
