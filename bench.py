@@ -90,6 +90,12 @@ def _parse():
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the pool workload's sub-objects in the default run")
     ap.add_argument("--graph", action="store_true", help="replay the step as one HIP graph")
+    ap.add_argument("--unfused", action="store_true",
+                    help="deviation workloads: re-positioning and score as separate calls "
+                         "(kvf_rerotate + kvf_score instead of kvf_rerotate_deviation)")
+    ap.add_argument("--fuse-mass", action="store_true",
+                    help="attention-mass workloads: re-position the keys inside the score's "
+                         "first pass (kvf_rerotate_score_attn_mass)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device-to-device copy of 1 GiB, 3 times")
     return ap.parse_args()
@@ -142,6 +148,8 @@ def call_work(g):
         work["recompute"] = ("mfma", 2.0 * hid * d * (hq + hkv) * M)
     else:
         work["u_probe"] = ("mfma", 2.0 * hid * d * (hq + hkv) * nU)    # Q and K of the query rows
+        # (with g.fuse_mass the score call also re-positions the keys: its
+        # bound stays the two MFMA passes)
         flops = 0.0
         for r in range(b.n_req):
             U = b.n_query(r)
@@ -585,7 +593,8 @@ def main():
         main_multilayer(args, wl, ratio)
         return
     flush = _flusher()
-    head, batch, g = measure(wl, ratio, args.steps, args.warmup, flush, graph=args.graph)
+    head, batch, g = measure(wl, ratio, args.steps, args.warmup, flush, graph=args.graph,
+                             fuse=not args.unfused, fuse_mass=args.fuse_mass)
     out = {
         "metric": METRIC,
         "value": head["value"],
@@ -611,7 +620,7 @@ def main():
         torch.cuda.empty_cache()
         extra = synth.get_workload(EXTRA_WORKLOAD)
         for pct in extra.ratio_pct[::-1]:
-            sub, _, gx = measure(extra, pct, args.steps, args.warmup, flush)
+            sub, _, gx = measure(extra, pct, args.steps, args.warmup, flush, fuse=not args.unfused)
             out[f"{EXTRA_WORKLOAD}@{pct}"] = {k: sub[k] for k in
                                                ("value", "unit", "ms_per_step", "config", "timing",
                                                 "roofline", "calls")}
@@ -620,7 +629,8 @@ def main():
         # the int8 KIVI layer with a bf16 fused cache and with an int8-resident one
         for name in Q8_WORKLOADS:
             qwl = synth.get_workload(name)
-            sub, _, gx = measure(qwl, qwl.ratio_pct[-1], args.steps, args.warmup, flush)
+            sub, _, gx = measure(qwl, qwl.ratio_pct[-1], args.steps, args.warmup, flush,
+                                 fuse=not args.unfused)
             out[name] = {k: sub[k] for k in ("value", "unit", "ms_per_step", "config", "timing",
                                              "roofline", "calls")}
             del gx
@@ -630,7 +640,7 @@ def main():
     print(json.dumps(out), flush=True)
 
 
-def measure(wl, ratio, steps, warmup, flush, graph=False):
+def measure(wl, ratio, steps, warmup, flush, graph=False, fuse=True, fuse_mass=False):
     """One single-layer workload: flushed per-step times, back-to-back time,
     per-call durations and the roofline of the longest call."""
     import numpy as np
@@ -639,7 +649,7 @@ def measure(wl, ratio, steps, warmup, flush, graph=False):
     from rag_kv_cache_kvf_amd.layer import FusedLayerGPU
 
     batch = synth.make_batch(wl)
-    g = FusedLayerGPU(batch, ratio)
+    g = FusedLayerGPU(batch, ratio, fuse_score=fuse, fuse_mass=fuse_mass)
     g.load()                              # the loader's stitch, ahead of the passes
     step = _graph_step(g) if graph else g.step
     for _ in range(max(warmup, 1)):
@@ -701,7 +711,8 @@ def measure(wl, ratio, steps, warmup, flush, graph=False):
               ("KIVI decode" if wl.kivi_bits else "gather keys and values") +
               (", int8-resident fused cache (8-bit codes + per-row min/scale)" if g.q8 else
                ", bf16 fused cache") +
-              (", deviation score in the same pass" if g.fuse_dev else "")}
+              (", deviation score in the same pass" if g.fuse_dev else "") +
+              (", keys re-positioned inside the attention-mass score's first pass" if g.fuse_mass else "")}
     res = {"value": round(n_ctx / (med * 1e-3), 1), "unit": UNIT, "ms_per_step": round(med, 5),
            "ms_median": round(med, 5), "config": config, "timing": timing, "roofline": roofline,
            "calls": calls}

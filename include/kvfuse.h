@@ -349,6 +349,35 @@ kvf_status kvf_score(kvf_score_mode mode, const kvf_layer_desc* layer,
 size_t kvf_score_workspace_size(kvf_score_mode mode, const kvf_layer_desc* layer,
                                 const kvf_batch* batch, int32_t n_last_q);
 
+/* ---------------------------------------------------------------------------
+ * kvf_rerotate_score_attn_mass - keys-only S1 and the attention-mass score
+ * S2c in one pass over the keys ([QCF] 2.1.2 Eq. 4 with [KVB] 3.2 Eq. 3 for
+ * the re-positioning; [QCF] 3.2.1 Eq. 9-10 for the score).  Equal to
+ * kvf_rerotate(k_only = 1) of `chunks` from pool_k into fused_k, followed by
+ * kvf_score(KVF_SCORE_ATTN_MASS [| ACCUMULATE when accumulate = 1]) over
+ * fused_k: the pass that first reads a tile of context keys reads them from
+ * pool_k, turns each by its chunk's R(pos0), scores them and writes them to
+ * fused_k, so the fused keys are not written and read back before the score.
+ *   chunks, pool_k [pool_rows, Hkv, d] (bf16 layers: bf16), rope tables,
+ *     max_chunk_len, fused_rows (>= the batch's rows): as in kvf_rerotate
+ *     with k_only = 1 (pool_k may be fused_k when every chunk has
+ *     src_row == dst_row); every chunk's fused rows must lie within the
+ *     batch's requests (rows outside them are not re-positioned).  Query
+ *     rows (N..T-1), which no chunk covers, must already hold the query
+ *     tokens' keys (kvf_recompute_qkv of the query rows).
+ *   q_u, n_last_q, eligible, scores, workspace (size from
+ *     kvf_score_workspace_size(KVF_SCORE_ATTN_MASS, ...)): as in kvf_score.
+ * Errors: those of kvf_rerotate and kvf_score.
+ */
+kvf_status kvf_rerotate_score_attn_mass(const kvf_layer_desc* layer, const kvf_batch* batch,
+                                        const kvf_chunk* chunks, int32_t n_chunks,
+                                        int32_t max_chunk_len, const void* pool_k, int64_t pool_rows,
+                                        const float* rope_cos, const float* rope_sin,
+                                        int32_t rope_n_pos, void* fused_k, int64_t fused_rows,
+                                        const void* q_u, int32_t n_last_q,
+                                        const uint8_t* eligible, int32_t accumulate, float* scores,
+                                        void* workspace, size_t ws_bytes, void* stream);
+
 /* kvf_score_q8 - kvf_score over an int8-resident fused cache: modes
  * KVF_SCORE_DEVIATION and KVF_SCORE_KEY_NORM (optionally OR
  * KVF_SCORE_ACCUMULATE), with the same definitions, batch, eligibility and

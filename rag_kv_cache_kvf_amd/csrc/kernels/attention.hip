@@ -1153,6 +1153,17 @@ struct MassArgs {
   // a key tile adds the kv heads.
   int* cnt_cols;                 // [total_ktiles]
   ScoreOut out;                  // scores [sum N]
+  // keys-only re-positioning fused into the statistics pass (ROT): the
+  // chunk table, per-chunk keys and rope tables of kvf_rerotate; k_rw is the
+  // fused K cache the pass writes the re-positioned keys to
+  const kvf_chunk* rot_chunks;
+  int rot_n;
+  const bf16_t* pool_k;
+  int64_t pool_rows;
+  const float* rope_cos;
+  const float* rope_sin;
+  int rope_n;
+  bf16_t* k_rw;
 };
 
 constexpr int kMK = 128;         // keys per workgroup (4 waves x 32)
@@ -1164,7 +1175,16 @@ constexpr int kMK = 128;         // keys per workgroup (4 waves x 32)
 constexpr int kMQSOne = 256;
 constexpr int kMQSMany = 128;
 
-template <int D, int kMQS>
+// ROT: the pass also re-positions the context keys (kvf_rerotate, keys
+// only): a key row that a chunk covers is read from the per-chunk cache
+// (pool row src_row + t), turned by R(pos0) of that chunk, scored, and
+// written to its fused row by the first query part (blockIdx.z == 0), so the
+// column-sum pass and everything after read the fused cache as kvf_rerotate
+// leaves it; rows no chunk covers (the query rows) are read from the fused
+// cache as they are.  With the per-chunk cache in the fused cache itself (in
+// place), the launch must not split the query vectors (gridDim.z == 1): a
+// second part could read a key the first has already turned.
+template <int D, int kMQS, bool ROT>
 __global__ void __launch_bounds__(256) mass_stats_bf16_kernel(MassArgs a) {
   constexpr int KS = D / 16;
   constexpr int LDQ = D + 8;     // padded rows: B-fragment reads hit distinct banks
@@ -1203,16 +1223,74 @@ __global__ void __launch_bounds__(256) mass_stats_bf16_kernel(MassArgs a) {
   // this wave's 32 keys as the A operand: row = key, k = 8 hf + e
   const bf16_t* Kg = static_cast<const bf16_t*>(a.k);
   const int key_a = key0 + 32 * w + c;
+  int kp = -1;                                    // ROT: the key's chunk start position
+  const bf16_t* krow = Kg + ((krow0 + key_a) * hkv + g) * D + hf * 8;
+  if constexpr (ROT) {
+    // the chunk covering this lane's key row: the wave's lanes test 64
+    // chunks at a time against the wave's 32 rows, and the few that
+    // intersect are broadcast to every lane
+    const int64_t row = krow0 + key_a;
+    const int64_t w_lo = krow0 + key0 + 32 * w;
+    const int64_t w_hi = min(w_lo + 32, krow0 + T);
+    int ksrc = 0;
+    for (int base = 0; base < a.rot_n; base += kWave) {
+      const int ci = base + lane;
+      kvf_chunk chn{};
+      bool hit = false;
+      if (ci < a.rot_n) {
+        chn = a.rot_chunks[ci];
+        hit = chn.len > 0 && chn.src_row >= 0 && static_cast<int64_t>(chn.src_row) + chn.len <= a.pool_rows &&
+              chn.pos0 >= 0 && chn.pos0 < a.rope_n && chn.dst_row < w_hi &&
+              static_cast<int64_t>(chn.dst_row) + chn.len > w_lo;
+      }
+      for (uint64_t hits = __ballot(hit); hits != 0; hits &= hits - 1) {
+        const int l = __builtin_ctzll(hits);
+        const int dst = __shfl(chn.dst_row, l, kWave), len = __shfl(chn.len, l, kWave);
+        const int p0 = __shfl(chn.pos0, l, kWave), src = __shfl(chn.src_row, l, kWave);
+        if (key_a < T && row >= dst && row < static_cast<int64_t>(dst) + len) {
+          kp = p0;
+          ksrc = src + static_cast<int>(row - dst);
+        }
+      }
+    }
+    if (kp >= 0) krow = a.pool_k + (static_cast<int64_t>(ksrc) * hkv + g) * D + hf * 8;
+  }
   bf16x8_t kf[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     if (key_a < T) {
-      kf[ks] = *reinterpret_cast<const bf16x8_t*>(Kg + ((krow0 + key_a) * hkv + g) * D + ks * 16 + hf * 8);
+      kf[ks] = *reinterpret_cast<const bf16x8_t*>(krow + ks * 16);
     } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e) kf[ks][e] = static_cast<__bf16>(0.f);
     }
   }
+  // ROT: re-position this lane's key (when a chunk covers it) and write it
+  // to the fused cache (first query part only); this lane holds channels
+  // 16 ks + 8 hf + e, and the partner of channel j < D/2 is j + D/2, in
+  // k-step ks + KS/2 of the same lane
+  auto rotate_keys = [&]() __attribute__((always_inline)) {
+    if (kp < 0) return;
+    const float* cr = a.rope_cos + static_cast<int64_t>(kp) * (D / 2) + hf * 8;
+    const float* sr = a.rope_sin + static_cast<int64_t>(kp) * (D / 2) + hf * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS / 2; ++ks) {
+      float cv[8], sv[8];
+      Elem<float>::load8(cr + ks * 16, cv);
+      Elem<float>::load8(sr + ks * 16, sv);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = static_cast<float>(kf[ks][e]), y = static_cast<float>(kf[ks + KS / 2][e]);
+        kf[ks][e] = static_cast<__bf16>(fmaf(x, cv[e], -(y * sv[e])));
+        kf[ks + KS / 2][e] = static_cast<__bf16>(fmaf(y, cv[e], x * sv[e]));
+      }
+    }
+    if (blockIdx.z == 0) {
+      bf16_t* Kw = a.k_rw + ((krow0 + key_a) * hkv + g) * D + hf * 8;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) *reinterpret_cast<bf16x8_t*>(Kw + ks * 16) = kf[ks];
+    }
+  };
   const bf16_t* Qg = static_cast<const bf16_t*>(a.q);
   const float cs = a.scale_log2;
   for (int qs = q_lo; qs < q_hi; qs += kMQS) {
@@ -1237,6 +1315,7 @@ __global__ void __launch_bounds__(256) mass_stats_bf16_kernel(MassArgs a) {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) asm volatile("" ::"v"(kf[ks]));
     }
+    if (ROT && qs == q_lo) rotate_keys();   // while this round's query loads are in flight
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
       const int idx = tid + 256 * j;
@@ -1308,6 +1387,7 @@ __global__ void __launch_bounds__(256) mass_stats_bf16_kernel(MassArgs a) {
     }
     __syncthreads();
   }
+  if (ROT && q_lo >= q_hi) rotate_keys();   // no query vectors here: the keys still move
 }
 
 constexpr int kMQB = 128;        // query vectors staged per column-sum round
@@ -1542,7 +1622,7 @@ size_t attn_mass_workspace(const kvf_layer_desc& L, const BatchArgs& B, int n_la
 
 hipError_t launch_attn_mass(const kvf_layer_desc& L, const BatchArgs& B, const void* fk,
                             const void* q_u, int n_last_q, const ScoreOut& out, void* ws,
-                            size_t ws_bytes, hipStream_t st) {
+                            size_t ws_bytes, hipStream_t st, const MassRotate* rot) {
   const MassLayout lay = mass_layout(L, B, n_last_q);
   if (ws_bytes < lay.total || lay.n_cnt > kMassMaxKeyTiles) return hipErrorInvalidValue;
   char* base = static_cast<char*>(ws);
@@ -1583,6 +1663,26 @@ hipError_t launch_attn_mass(const kvf_layer_desc& L, const BatchArgs& B, const v
   m.scale_log2 = scale_log2;
   m.cnt_cols = cnt;
   m.out = out;
+  // the re-positioning rides on the bf16 statistics pass; without one (no
+  // query rows, or fp32) it runs as its own keys-only kvf_rerotate launch
+  const bool fused_rot = rot != nullptr && L.dtype == KVF_BF16 && plane > 0;
+  if (rot != nullptr && !fused_rot) {
+    const hipError_t e = launch_rerotate(L, rot->chunks, rot->n_chunks, rot->max_len, rot->pool_k,
+                                         nullptr, nullptr, rot->pool_rows, rot->rope_cos,
+                                         rot->rope_sin, rot->rope_n, const_cast<void*>(fk), nullptr,
+                                         rot->fused_rows, 1, st);
+    if (e != hipSuccess) return e;
+  }
+  if (fused_rot) {
+    m.rot_chunks = rot->chunks;
+    m.rot_n = rot->n_chunks;
+    m.pool_k = static_cast<const bf16_t*>(rot->pool_k);
+    m.pool_rows = rot->pool_rows;
+    m.rope_cos = rot->rope_cos;
+    m.rope_sin = rot->rope_sin;
+    m.rope_n = rot->rope_n;
+    m.k_rw = static_cast<bf16_t*>(const_cast<void*>(fk));
+  }
   const int n = B.cu_N[B.n_req];
   if (plane == 0) {
     // no query rows: every key gets zero mass
@@ -1600,17 +1700,26 @@ hipError_t launch_attn_mass(const kvf_layer_desc& L, const BatchArgs& B, const v
     // a grid under two workgroups per CU with at least 256 query vectors per
     // request splits them in two (128-vector rounds, three workgroups per CU)
     const int64_t wgs = static_cast<int64_t>(lay.n_splits) * m.hkv * B.n_req;
-    const int nqp = (wgs < 2 * kCUs && nqv_max >= kMassQParts * kMQSMany) ? kMassQParts : 1;
+    // (not when re-positioning in place: a second part could read a key the
+    // first has already turned)
+    const bool in_place = fused_rot && rot->pool_k == fk;
+    const int nqp = (!in_place && wgs < 2 * kCUs && nqv_max >= kMassQParts * kMQSMany) ? kMassQParts : 1;
     const dim3 grid(lay.n_splits * m.hkv, B.n_req, nqp);
     const int per = ceil_div(ceil_div(nqv_max, nqp), 32) * 32;
     const bool one = per > kMQSMany && per <= kMQSOne;
+#define KVF_MASS_STATS(D_, Q_)                                                                   \
+  do {                                                                                           \
+    if (fused_rot) hipLaunchKernelGGL((mass_stats_bf16_kernel<D_, Q_, true>), grid, dim3(256), 0, st, m); \
+    else hipLaunchKernelGGL((mass_stats_bf16_kernel<D_, Q_, false>), grid, dim3(256), 0, st, m); \
+  } while (0)
     if (L.head_dim == 128) {
-      if (one) hipLaunchKernelGGL((mass_stats_bf16_kernel<128, kMQSOne>), grid, dim3(256), 0, st, m);
-      else hipLaunchKernelGGL((mass_stats_bf16_kernel<128, kMQSMany>), grid, dim3(256), 0, st, m);
+      if (one) KVF_MASS_STATS(128, kMQSOne);
+      else KVF_MASS_STATS(128, kMQSMany);
     } else {
-      if (one) hipLaunchKernelGGL((mass_stats_bf16_kernel<64, kMQSOne>), grid, dim3(256), 0, st, m);
-      else hipLaunchKernelGGL((mass_stats_bf16_kernel<64, kMQSMany>), grid, dim3(256), 0, st, m);
+      if (one) KVF_MASS_STATS(64, kMQSOne);
+      else KVF_MASS_STATS(64, kMQSMany);
     }
+#undef KVF_MASS_STATS
   } else {
     AttnArgs a{};
     a.b = B;

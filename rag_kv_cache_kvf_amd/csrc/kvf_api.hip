@@ -3,6 +3,7 @@
 // Every entry point validates on the host before anything is enqueued, maps
 // failures to kvf_status, records a thread-local message, and never lets a
 // C++ exception cross the interface.
+#include <climits>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -403,6 +404,55 @@ kvf_status kvf_score(kvf_score_mode mode_flags, const kvf_layer_desc* layer,
   return finish(kvf::launch_attn_mass(*layer, B, fused_k, q_u, n_last_q, out, workspace,
                                         ws_bytes, as_stream(stream)),
                 as_stream(stream), "kvf_score(attn_mass)");
+  KVF_GUARD_END
+}
+
+kvf_status kvf_rerotate_score_attn_mass(const kvf_layer_desc* layer, const kvf_batch* batch,
+                                        const kvf_chunk* chunks, int32_t n_chunks,
+                                        int32_t max_chunk_len, const void* pool_k, int64_t pool_rows,
+                                        const float* rope_cos, const float* rope_sin,
+                                        int32_t rope_n_pos, void* fused_k, int64_t fused_rows,
+                                        const void* q_u, int32_t n_last_q,
+                                        const uint8_t* eligible, int32_t accumulate, float* scores,
+                                        void* workspace, size_t ws_bytes, void* stream) {
+  KVF_GUARD_BEGIN
+  kvf_status st = check_layer(layer);
+  if (st != KVF_OK) return st;
+  kvf::BatchArgs B;
+  st = check_batch(batch, &B);
+  if (st != KVF_OK) return st;
+  KVF_CHECK(accumulate == 0 || accumulate == 1, KVF_ERR_INVALID_ARG, "accumulate must be 0 or 1");
+  KVF_CHECK(n_chunks >= 0 && max_chunk_len >= 0 && rope_n_pos >= 0 && fused_rows >= 0 &&
+                pool_rows >= 0, KVF_ERR_INVALID_ARG, "negative size");
+  KVF_CHECK(pool_rows <= INT32_MAX, KVF_ERR_UNSUPPORTED, "pool_rows too large");
+  KVF_CHECK(fused_rows >= B.cu_T[B.n_req], KVF_ERR_INVALID_ARG,
+            "the fused cache (%lld rows) must hold the batch (%d rows)",
+            static_cast<long long>(fused_rows), B.cu_T[B.n_req]);
+  KVF_CHECK(max_chunk_len <= (1 << 24), KVF_ERR_UNSUPPORTED, "max_chunk_len too large");
+  KVF_CHECK(fused_k != nullptr, KVF_ERR_INVALID_ARG, "fused_k is NULL");
+  const bool rotate = n_chunks > 0 && max_chunk_len > 0;
+  KVF_CHECK(!rotate || (chunks && pool_k && rope_cos && rope_sin), KVF_ERR_INVALID_ARG,
+            "required pointer is NULL");
+  const kvf::MassRotate rot{chunks, n_chunks, max_chunk_len, pool_k, pool_rows,
+                            rope_cos, rope_sin, rope_n_pos, fused_rows};
+  if (B.cu_N[B.n_req] == 0) {          // nothing to score: the re-positioning alone
+    if (!rotate) return KVF_OK;
+    return finish(kvf::launch_rerotate(*layer, chunks, n_chunks, max_chunk_len, pool_k, nullptr,
+                                         nullptr, pool_rows, rope_cos, rope_sin, rope_n_pos, fused_k,
+                                         nullptr, fused_rows, 1, as_stream(stream)),
+                  as_stream(stream), "kvf_rerotate_score_attn_mass");
+  }
+  KVF_CHECK(q_u && scores, KVF_ERR_INVALID_ARG, "q_u or scores is NULL");
+  KVF_CHECK(kvf::attn_mass_key_tiles(B) <= 16384, KVF_ERR_UNSUPPORTED,
+            "attention mass over %lld 128-key context tiles (at most 16384 per call)",
+            static_cast<long long>(kvf::attn_mass_key_tiles(B)));
+  const size_t need = kvf::attn_mass_workspace(*layer, B, n_last_q);
+  KVF_CHECK(ws_bytes >= need, KVF_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);
+  KVF_CHECK(need == 0 || workspace != nullptr, KVF_ERR_WORKSPACE, "workspace is NULL");
+  const kvf::ScoreOut out{scores, eligible, accumulate};
+  return finish(kvf::launch_attn_mass(*layer, B, fused_k, q_u, n_last_q, out, workspace, ws_bytes,
+                                        as_stream(stream), rotate ? &rot : nullptr),
+                as_stream(stream), "kvf_rerotate_score_attn_mass");
   KVF_GUARD_END
 }
 

@@ -299,9 +299,22 @@ hipError_t launch_kivi_encode(const kvf_layer_desc& L, const void* pk, const voi
                               int max_len, const kvf_kivi& out, hipStream_t st);
 hipError_t launch_deviation(const kvf_layer_desc& L, const BatchArgs& B, const void* fk,
                             const void* kf, const ScoreOut& out, hipStream_t st);
+// keys-only re-positioning fused into the attention-mass pass
+// (kvf_rerotate_score_attn_mass)
+struct MassRotate {
+  const kvf_chunk* chunks;
+  int n_chunks;
+  int max_len;
+  const void* pool_k;            // per-chunk keys (may be the fused cache: in place)
+  int64_t pool_rows;
+  const float* rope_cos;
+  const float* rope_sin;
+  int rope_n;
+  int64_t fused_rows;
+};
 hipError_t launch_attn_mass(const kvf_layer_desc& L, const BatchArgs& B, const void* fk,
                             const void* q_u, int n_last_q, const ScoreOut& out, void* ws,
-                            size_t ws_bytes, hipStream_t st);
+                            size_t ws_bytes, hipStream_t st, const MassRotate* rot = nullptr);
 size_t attn_mass_workspace(const kvf_layer_desc& L, const BatchArgs& B, int n_last_q);
 hipError_t launch_attn_mass_noalloc(const kvf_layer_desc& L, const BatchArgs& B, const void* fk,
                                     const void* q_u, int n_last_q, const ScoreOut& out,

@@ -90,6 +90,8 @@ _SIGS = {
     "kvf_rerotate_deviation": (_I32, [_LP, _BP, _P, _I32, _I32, _P, _P, ctypes.POINTER(KiviDesc), _I64,
                                       _P, _P, _I32, _P, _P, _I64, _I32, _P, _P, _I32, _P, _P]),
     "kvf_score": (_I32, [_I32, _LP, _BP, _P, _P, _P, _I32, _P, _P, _P, _SZ, _P]),
+    "kvf_rerotate_score_attn_mass": (_I32, [_LP, _BP, _P, _I32, _I32, _P, _I64, _P, _P, _I32, _P, _I64,
+                                            _P, _I32, _P, _I32, _P, _P, _SZ, _P]),
     "kvf_score_workspace_size": (_SZ, [_I32, _LP, _BP, _I32]),
     "kvf_score_attn_mass_noalloc": (_I32, [_LP, _BP, _P, _P, _I32, _P, _P, _I32, _P]),
     "kvf_select_topk": (_I32, [_P, _P, _BP, _IP, _P, _P, _P, _P, _P, _SZ, _P]),
@@ -306,6 +308,26 @@ def rerotate_deviation(layer: Layer, batch: Batch, chunks: torch.Tensor, max_chu
                  _ptr(rope_sin), int(rope_cos.shape[0]), _ptr(fused_k), _ptr(fused_v), _rows(fused_k),
                  1 if k_only else 0, _ptr(k_fresh), _ptr(eligible), 1 if accumulate else 0,
                  _ptr(scores)), "kvf_rerotate_deviation", stream, keep=(d, batch))
+
+
+def rerotate_score_attn_mass(layer: Layer, batch: Batch, chunks: torch.Tensor, max_chunk_len: int,
+                             pool_k: torch.Tensor, rope_cos: torch.Tensor, rope_sin: torch.Tensor,
+                             fused_k: torch.Tensor, q_u: torch.Tensor, scores: torch.Tensor,
+                             workspace: Optional[torch.Tensor], n_last_q: int = 0,
+                             eligible: Optional[torch.Tensor] = None, accumulate: bool = False,
+                             stream=None):
+    """kvf_rerotate_score_attn_mass: keys-only re-positioning of the chunks
+    (pool_k -> fused_k; pool_k may be fused_k) and the attention-mass score
+    in one pass."""
+    d = layer.desc()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return _run(_lib.kvf_rerotate_score_attn_mass,
+                (ctypes.byref(d), ctypes.byref(batch.desc), _ptr(chunks), int(chunks.shape[0]),
+                 max_chunk_len, _ptr(pool_k), _rows(pool_k), _ptr(rope_cos), _ptr(rope_sin),
+                 int(rope_cos.shape[0]), _ptr(fused_k), _rows(fused_k), _ptr(q_u), n_last_q,
+                 _ptr(eligible), 1 if accumulate else 0,
+                 _ptr(scores), _ptr(workspace), ws_bytes), "kvf_rerotate_score_attn_mass", stream,
+                keep=(d, batch))
 
 
 def score_attn_mass_noalloc(layer: Layer, batch: Batch, fused_k: torch.Tensor, q_u: torch.Tensor,

@@ -7,13 +7,15 @@ itself.  Order (all on one stream, no host synchronisation):
   deviation mode (KVBoost page, section 4.6.2, Algorithm 2 at one layer)
     kvf_recompute_qkv(all rows, K: probe K~) ->
     kvf_rerotate_deviation (re-positioning and the deviation score in one
-    pass; with fuse_deviation=False: kvf_rerotate, then kvf_score(DEVIATION)
+    pass; with fuse_score=False: kvf_rerotate, then kvf_score(DEVIATION)
     after the probe) -> kvf_select_topk ->
     kvf_recompute_qkv(P+U, Q|V; V straight into the fused cache) ->
     kvf_scatter_kv(K of P+U from the probe) -> kvf_sparse_q_attention
   attention-mass mode (QCFuse page, section 3.2.1 at one layer)
     kvf_rerotate -> kvf_recompute_qkv(U, Q|K; K into the fused cache) ->
-    kvf_score(ATTN_MASS) -> kvf_select_topk ->
+    kvf_score(ATTN_MASS) (with fuse_mass: the U-row probe, then
+    kvf_rerotate_score_attn_mass, which re-positions the keys inside the
+    score's first pass) -> kvf_select_topk ->
     kvf_recompute_qkv(P+U, Q|K|V; K/V into the fused cache) ->
     kvf_sparse_q_attention
   (the recompute call's destination-row output is the scatter of Eq. 7)
@@ -70,16 +72,20 @@ class FusedLayerGPU:
     k_only False, or for a shared chunk pool or KIVI codes, the pass gathers
     keys and values from the per-chunk caches itself.
 
-    fuse_deviation (deviation mode): the key probe runs first and the
+    fuse_score (deviation mode): the key probe runs first and the
     re-positioning pass scores every context row as it writes its key
     (kvf_rerotate_deviation, or kvf_rerotate_q8_deviation for the
-    int8-resident cache), so the score does not read the fused keys back;
-    False keeps the re-positioning and the score apart."""
+    int8-resident cache); False keeps the re-positioning and the score
+    apart.  fuse_mass (attention-mass mode with keys-only re-positioning,
+    off by default): the U-row probe runs first and the score's statistics
+    pass re-positions each tile of keys as it reads them
+    (kvf_rerotate_score_attn_mass); measured no faster than the two calls
+    at the Qwen3-8B and Llama-3-70B shapes."""
 
     def __init__(self, batch: SynthBatch, ratio_pct: int, device="cuda",
                  pic: Optional[dict] = None, n_last_q: int = 0, mode: Optional[str] = None,
                  k_only: Optional[bool] = None, resident: Optional[str] = None,
-                 fuse_deviation: bool = True):
+                 fuse_score: bool = True, fuse_mass: bool = False):
         wl = batch.wl
         self.q8 = (wl.resident if resident is None else resident) == "q8"
         self.wl = wl
@@ -96,7 +102,7 @@ class FusedLayerGPU:
         # or fp32 cache: Hkv d / 16 rotation units; int8-resident: Hkv d / 8
         # lanes, a row within one 256-thread workgroup) a power of two <= 64
         rl = wl.n_kv_heads * wl.head_dim // (8 if self.q8 else 16)
-        self.fuse_dev = (fuse_deviation and self.probe and wl.head_dim % (32 if self.q8 else 16) == 0
+        self.fuse_dev = (fuse_score and self.probe and wl.head_dim % (32 if self.q8 else 16) == 0
                          and 1 <= rl <= 64 and rl & (rl - 1) == 0)
         self.n_last_q = n_last_q
         self.device = torch.device(device)
@@ -162,6 +168,8 @@ class FusedLayerGPU:
                              "re-positioning and a score other than attention mass")
         if self.k_only and not dense:
             raise ValueError("keys-only re-positioning needs a dense per-chunk cache")
+        # attention mass: the keys-only re-positioning rides on the score's pass
+        self.fuse_mass = fuse_mass and self.mass and self.k_only and wl.dtype == "bf16"
         if self.k_only:
             src, dst = [], []
             for s0, d0, _, ln in batch.chunk_table[:, :4]:
@@ -317,6 +325,10 @@ class FusedLayerGPU:
         elif self.mode == "deviation":
             return kvf.score(kvf.KVF_SCORE_DEVIATION, self.layer, self.kb, self.fused_k, self.k_probe,
                              None, self.scores)
+        elif self.fuse_mass:
+            return kvf.rerotate_score_attn_mass(self.layer, self.kb, self.chunks, self.max_chunk_len,
+                                                self.pool_k, self.rope_cos, self.rope_sin, self.fused_k,
+                                                self.q_u, self.scores, self.ws, n_last_q=self.n_last_q)
         else:
             return kvf.score(kvf.KVF_SCORE_ATTN_MASS, self.layer, self.kb, self.fused_k, None, self.q_u,
                              self.scores, self.ws, n_last_q=self.n_last_q)
@@ -405,6 +417,10 @@ class FusedLayerGPU:
         if self.fuse_dev:
             # the probe first: the re-positioning pass scores against it
             first.insert(0, ("k_probe", "rerotate", f("k_probe")))
+            score = []
+        elif self.fuse_mass:
+            # the U-row probe first: the score's pass re-positions the keys
+            first = [("u_probe", "rerotate", f("u_probe")), ("score", "rerotate", f("score"))]
             score = []
         elif self.probe:
             score = [("k_probe", "score", f("k_probe")), ("score", "score", f("score"))]

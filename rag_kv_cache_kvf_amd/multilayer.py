@@ -57,10 +57,11 @@ class MultiLayerGPU:
         self.pcts = pcts
         self.device = torch.device(device)
         self.layers: List[FusedLayerGPU] = [
-            # (deviation layers keep the re-positioning and the score apart:
-            # progressive filtering probes and scores only the previous picks)
+            # (the layers keep the re-positioning and the score apart: the
+            # passes order them per layer, progressive filtering probes and
+            # scores only the previous picks)
             FusedLayerGPU(b, p, device=device, pic=None if pics is None else pics[l], k_only=False,
-                          fuse_deviation=False)
+                          fuse_score=False)
             for l, (b, p) in enumerate(zip(batches, pcts))]
         l0 = self.layers[0]
         self.kb = l0.kb

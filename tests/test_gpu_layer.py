@@ -180,6 +180,35 @@ def test_deterministic_and_graph_replay(layer_mod):
             assert np.array_equal(raw(getattr(g, k)), v), f"replay {rep}: {k} differs"
 
 
+@pytest.mark.parametrize("name", ["mini_bf16_mass", "mini_bf16_dev_pool", "mini_bf16_kivi8"])
+def test_fused_score_passes_match_separate_calls(layer_mod, name):
+    """The re-positioning pass that also scores (deviation: kvf_rerotate_
+    deviation; attention mass: kvf_rerotate_score_attn_mass) against the two
+    separate calls through the whole layer: attention mass bit for bit
+    everywhere (the same keys and arithmetic); deviation with the same
+    fused caches, scores within fp32 summation order, and everything after
+    the selection bit for bit when both take the same selection."""
+    import torch
+    b, wl, lo, x, w, pic, opk, opv, pct, ks = _oracle_inputs(name)
+    fields = ("scores", "sel", "fused_k", "fused_v", "out", "lse")
+    res = []
+    for fused in (True, False):
+        g = layer_mod.FusedLayerGPU(b, pct, pic=pic, fuse_score=fused, fuse_mass=fused)
+        assert (g.fuse_mass if g.mass else g.fuse_dev) == fused
+        g.run()
+        torch.cuda.synchronize()
+        res.append({k: raw(getattr(g, k)).copy() for k in fields})
+    a, c = res
+    if wl.score != "deviation":
+        for k in fields:
+            assert np.array_equal(a[k], c[k]), f"{k} differs"
+        return
+    assert np.max(np.abs(a["scores"].astype(np.float64) - c["scores"])) < 2e-6
+    if np.array_equal(a["sel"], c["sel"]):
+        for k in ("fused_k", "fused_v", "out", "lse"):
+            assert np.array_equal(a[k], c[k]), f"{k} differs"
+
+
 # ----------------------------------------------------------------------------
 # other selectors feeding the same path
 # ----------------------------------------------------------------------------

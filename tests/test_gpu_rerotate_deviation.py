@@ -153,3 +153,132 @@ def _rope(kvf, base, d, n):
     s = torch.empty_like(c)
     kvf.rope_table(base, d, n, c, s)
     return c, s
+
+
+MASS_CASES = [
+    # (workload, keys-only re-positioning form)
+    ("mini_bf16_mass", "landing"),        # two requests, ragged chunks
+    ("mini_bf16_mass", "in_place"),
+    ("mini_bf16_d64_mass", "landing"),    # head_dim 64
+    ("qwen3_8b_mass", "landing"),         # full size: 10 x 512 + 64
+    ("qwen3_8b_mass", "in_place"),
+    ("llama3_70b_mass", "landing"),       # full size: 32 x 1024 + 256 (128-vector rounds)
+]
+
+
+@pytest.mark.parametrize("case", MASS_CASES, ids=lambda c: "-".join(c))
+def test_rerotate_score_attn_mass(kvf, case):
+    """Keys-only re-positioning inside the attention-mass score's first pass
+    (kvf_rerotate_score_attn_mass): the fused keys bit for bit as
+    kvf_rerotate(k_only) writes them, the scores bit for bit as kvf_score
+    computes them after it (the same keys and the same arithmetic), and the
+    scores against the oracle's attention mass over the oracle's
+    re-positioned keys."""
+    import torch
+    name, form = case
+    b = synth.make_batch(name)
+    wl = b.wl
+    hq, hkv, d = wl.n_q_heads, wl.n_kv_heads, wl.head_dim
+    lo = _olayer(wl)
+    print(f"[case] rerotate_score_attn_mass {name} {form} rows={b.total_rows}", flush=True)
+    pk = _randn((b.pool_rows, hkv, d), 21, "rm_pool_k")
+    pk_s = encode(pk, "bf16")
+    nU = b.total_rows - int(np.sum(b.n_ctx))
+    qu = _randn((nU, hq, d), 22, "rm_q", std=1.5)
+    q_s = encode(qu, "bf16")
+    ku = encode(_randn((b.total_rows, hkv, d), 23, "rm_query_keys"), "bf16")   # query rows' keys
+    table = b.chunk_table.copy()
+    start = np.zeros_like(ku)
+    qrows = b.query_rows()
+    start[qrows] = ku[qrows]
+    if form == "in_place":
+        # the loader has landed every chunk's keys at its fused rows
+        for src, dst, _, ln in table[:, :4]:
+            start[dst:dst + ln] = pk_s[src:src + ln]
+        table[:, 0] = table[:, 1]
+    L = kvf.Layer(wl.hidden, hq, hkv, d, "bf16")
+    c, s = _rope(kvf, wl.rope_base, d, int(np.diff(b.cu_T).max()))
+    ch = to_gpu(table)
+    max_len = int(table[:, 3].max())
+    kb = kvf.Batch(b.cu_T, b.n_ctx)
+    n_sum = int(np.sum(b.n_ctx))
+    ws_n = kvf.score_workspace_size(kvf.KVF_SCORE_ATTN_MASS, L, kb, 0)
+    q_g = to_gpu(q_s, "bf16")
+    runs = []
+    for fused in (True, False):
+        fk = to_gpu(start, "bf16")
+        pool = fk if form == "in_place" else to_gpu(pk_s, "bf16")
+        ws = torch.zeros(max(ws_n, 1), dtype=torch.uint8, device="cuda")
+        sc = torch.zeros(n_sum, dtype=torch.float32, device="cuda")
+        if fused:
+            kvf.rerotate_score_attn_mass(L, kb, ch, max_len, pool, c, s, fk, q_g, sc, ws)
+        else:
+            kvf.rerotate(L, ch, max_len, pool, None, c, s, fk, None, k_only=True)
+            kvf.score(kvf.KVF_SCORE_ATTN_MASS, L, kb, fk, None, q_g, sc, ws)
+        torch.cuda.synchronize()
+        assert not bool(ws[:65536].any()), "arrival counters not reset"
+        runs.append((raw(fk).copy(), raw(sc).copy()))
+    assert np.array_equal(runs[0][0], runs[1][0]), "fused keys differ from kvf_rerotate's"
+    assert np.array_equal(runs[0][1], runs[1][1]), "scores differ from kvf_score's after kvf_rerotate"
+
+    # oracle: keys re-positioned in float64 from the stored per-chunk keys,
+    # stored as bf16 by the oracle's rounding; the query rows' keys as given
+    ok, _ = fusion.rerotate_stitch(decode(pk_s, "bf16"), np.zeros_like(pk), b.chunk_table, b.total_rows, lo)
+    keys = decode(encode(ok, "bf16"), "bf16")
+    keys[qrows] = decode(ku, "bf16")[qrows]
+    dq = decode(q_s, "bf16")
+    ref, uoff = [], 0
+    for r in range(b.n_req):
+        U = b.cu_T[r + 1] - b.cu_T[r] - b.n_ctx[r]
+        ref.append(fusion.attention_mass(dq[uoff:uoff + U], keys[b.cu_T[r]:b.cu_T[r + 1]], int(b.n_ctx[r]), lo))
+        uoff += U
+    ref = np.concatenate(ref)
+    assert_close(runs[0][1].astype(np.float64), ref, "bf16", f"{name} {form} fused attention mass")
+    ctx = b.context_rows()
+    rows = ctx[synth.random_rows(len(ctx), 4096, 24)] if len(ctx) > 4096 else ctx
+    assert_close(decode(runs[0][0], "bf16")[rows], ok[rows], "bf16", f"{name} {form} fused K")
+
+
+def test_rerotate_score_attn_mass_request_without_query(kvf):
+    """A request with no query rows scores nothing, yet its keys are still
+    re-positioned by the fused pass (its statistics workgroups have no
+    query vectors); the other request is scored as usual.  Bit for bit as
+    kvf_rerotate(k_only) then kvf_score, and against the oracle."""
+    import torch
+    hq, hkv, d, base = 8, 2, 128, 1e6
+    cu_T, n_ctx = [0, 300, 520], [300, 200]
+    # chunks: request 0 in two ragged chunks, request 1 in one
+    table = np.array([[0, 0, 0, 131, 0, 0, 0, 0], [131, 131, 131, 169, 1, 0, 0, 0],
+                      [300, 300, 0, 200, 2, 0, 0, 0]], dtype=np.int32)
+    pool_rows = 500
+    pk_s = encode(_randn((pool_rows, hkv, d), 31, "rq_pool"), "bf16")
+    q_s = encode(_randn((20, hq, d), 32, "rq_q", std=1.5), "bf16")
+    start = np.zeros((520, hkv, d), dtype=np.uint16)
+    start[500:520] = encode(_randn((20, hkv, d), 33, "rq_qk"), "bf16")
+    L = kvf.Layer(2048, hq, hkv, d, "bf16")
+    c, s = _rope(kvf, base, d, 600)
+    kb = kvf.Batch(cu_T, n_ctx)
+    ws_n = kvf.score_workspace_size(kvf.KVF_SCORE_ATTN_MASS, L, kb, 0)
+    runs = []
+    for fused in (True, False):
+        fk = to_gpu(start, "bf16")
+        ws = torch.zeros(max(ws_n, 1), dtype=torch.uint8, device="cuda")
+        sc = torch.zeros(500, dtype=torch.float32, device="cuda")
+        if fused:
+            kvf.rerotate_score_attn_mass(L, kb, to_gpu(table), 200, to_gpu(pk_s, "bf16"), c, s, fk,
+                                         to_gpu(q_s, "bf16"), sc, ws)
+        else:
+            kvf.rerotate(L, to_gpu(table), 200, to_gpu(pk_s, "bf16"), None, c, s, fk, None, k_only=True)
+            kvf.score(kvf.KVF_SCORE_ATTN_MASS, L, kb, fk, None, to_gpu(q_s, "bf16"), sc, ws)
+        torch.cuda.synchronize()
+        runs.append((raw(fk).copy(), raw(sc).copy()))
+    assert np.array_equal(runs[0][0], runs[1][0])
+    assert np.array_equal(runs[0][1], runs[1][1])
+    assert not runs[0][1][:300].any(), "a request without query rows gets zero mass"
+    lo = fusion.Layer(2048, hq, hkv, d, base)
+    ok, _ = fusion.rerotate_stitch(decode(pk_s, "bf16"), np.zeros((pool_rows, hkv, d)), table, 520, lo)
+    assert_close(decode(runs[0][0], "bf16")[:500], ok[:500], "bf16", "keys of both requests")
+    keys = decode(encode(ok, "bf16"), "bf16")
+    keys[500:] = decode(start[500:], "bf16")
+    ref = fusion.attention_mass(decode(q_s, "bf16"), keys[300:520], 200, lo)
+    assert_close(runs[0][1][300:].astype(np.float64), ref, "bf16", "attention mass of the second request")
