@@ -273,6 +273,43 @@ static void check_projection_and_attention(void) {
   CHECK(kvf_rope_table(1e4, 63, 4, FAKE, FAKE, NULL) == KVF_ERR_INVALID_ARG);
 }
 
+/* the re-positioning passes that also score: their batch checks read the
+ * host arrays (exact sizes here), then their own and kvf_rerotate's checks */
+static void check_fused_passes(void) {
+  const kvf_layer_desc bf = {2048, 16, 2, 128, KVF_BF16};
+  const kvf_layer_desc wide = {4096, 32, 16, 128, KVF_BF16};   /* 128 units per row */
+  batch_t b = make_batch(3, 100, 90);
+  kvf_chunk* ch = (kvf_chunk*)calloc(1, sizeof(kvf_chunk));
+  kvf_q8_cache q8 = {(uint8_t*)FAKE, (uint8_t*)FAKE, (float*)FAKE, (float*)FAKE, 300};
+  /* deviation, bf16 cache */
+  CHECK(kvf_rerotate_deviation(&bf, &b.b, ch, 1, 4, FAKE, FAKE, NULL, 4, FAKE, FAKE, 4, FAKE, FAKE,
+                               300, 0, FAKE, NULL, 2, FAKE, NULL) == KVF_ERR_INVALID_ARG);
+  CHECK(kvf_rerotate_deviation(&wide, &b.b, ch, 1, 4, FAKE, FAKE, NULL, 4, FAKE, FAKE, 4, FAKE, FAKE,
+                               300, 0, FAKE, NULL, 0, FAKE, NULL) == KVF_ERR_UNSUPPORTED);
+  CHECK(kvf_rerotate_deviation(&bf, &b.b, ch, 1, 4, FAKE, FAKE, NULL, 4, FAKE, FAKE, 4, FAKE, FAKE,
+                               300, 0, NULL, NULL, 0, FAKE, NULL) == KVF_ERR_INVALID_ARG);
+  CHECK(kvf_rerotate_deviation(&bf, &b.b, ch, 1, 4, FAKE, FAKE, NULL, 4, FAKE, FAKE, 4, FAKE, NULL,
+                               300, 0, FAKE, NULL, 0, FAKE, NULL) == KVF_ERR_INVALID_ARG);
+  /* deviation, int8-resident cache */
+  CHECK(kvf_rerotate_q8_deviation(&bf, &b.b, ch, 1, 4, FAKE, FAKE, NULL, 4, FAKE, FAKE, 4, &q8, FAKE,
+                                  NULL, 3, FAKE, NULL) == KVF_ERR_INVALID_ARG);
+  CHECK(kvf_rerotate_q8_deviation(&wide, &b.b, ch, 1, 4, FAKE, FAKE, NULL, 4, FAKE, FAKE, 4, &q8, FAKE,
+                                  NULL, 0, FAKE, NULL) == KVF_ERR_UNSUPPORTED);
+  CHECK(kvf_rerotate_q8_deviation(&bf, &b.b, ch, 1, 4, FAKE, FAKE, NULL, 4, FAKE, FAKE, 4, NULL, FAKE,
+                                  NULL, 0, FAKE, NULL) == KVF_ERR_INVALID_ARG);
+  /* attention mass with keys-only re-positioning */
+  CHECK(kvf_rerotate_score_attn_mass(&bf, &b.b, ch, 1, 4, FAKE, 100, FAKE, FAKE, 4, FAKE, 299, FAKE, 0,
+                                     NULL, 0, FAKE, FAKE, 1 << 30, NULL) == KVF_ERR_INVALID_ARG);
+  CHECK(kvf_rerotate_score_attn_mass(&bf, &b.b, ch, 1, 4, NULL, 100, FAKE, FAKE, 4, FAKE, 300, FAKE, 0,
+                                     NULL, 0, FAKE, FAKE, 1 << 30, NULL) == KVF_ERR_INVALID_ARG);
+  CHECK(kvf_rerotate_score_attn_mass(&bf, &b.b, ch, 1, 4, FAKE, 100, FAKE, FAKE, 4, FAKE, 300, FAKE, 0,
+                                     NULL, 5, FAKE, FAKE, 1 << 30, NULL) == KVF_ERR_INVALID_ARG);
+  CHECK(kvf_rerotate_score_attn_mass(&bf, &b.b, ch, 1, 4, FAKE, 100, FAKE, FAKE, 4, FAKE, 300, FAKE, 0,
+                                     NULL, 0, FAKE, FAKE, 0, NULL) == KVF_ERR_WORKSPACE);
+  free(ch);
+  free_batch(&b);
+}
+
 static void check_launch_failure(void) {
   /* a valid call on a machine without a GPU: the launch fails and the call
    * reports it as its own KVF_ERR_HIP */
@@ -290,6 +327,7 @@ int main(void) {
   check_select();
   check_static_counts();
   check_projection_and_attention();
+  check_fused_passes();
   const char* launch = getenv("KVF_ASAN_LAUNCH");
   if (launch && strcmp(launch, "1") == 0) check_launch_failure();
   if (failures) {

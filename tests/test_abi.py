@@ -245,6 +245,28 @@ def test_validation_errors(lib):
               8, FAKE, FAKE, 8, 0, FAKE, None, 0, FAKE, None) == 1
 
 
+def test_rerotate_score_attn_mass_validation(lib):
+    """Keys-only re-positioning inside the attention-mass pass: kvf_score's
+    and kvf_rerotate's checks on the host, plus the fused cache holding the
+    batch."""
+    P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    f = lib.kvf_rerotate_score_attn_mass
+    f.argtypes = [P, P, P, I32, I32, P, I64, P, P, I32, P, I64, P, I32, P, I32, P, P, ctypes.c_size_t, P]
+    bf = Layer(2048, 16, 2, 128, 1)
+    b, keep = _batch([0, 100, 200], [90, 90])
+
+    def call(layer=bf, pool=FAKE, fused_rows=200, acc=0, ws_bytes=1 << 30, q=FAKE, scores=FAKE, nch=1):
+        return f(ctypes.byref(layer), ctypes.byref(b), FAKE, nch, 8, pool, 100, FAKE, FAKE, 8, FAKE,
+                 fused_rows, q, 0, None, acc, scores, FAKE, ws_bytes, None)
+    assert call(fused_rows=199) == 1          # the fused cache must hold the batch
+    assert call(pool=None) == 1               # chunks need the per-chunk keys
+    assert call(acc=2) == 1
+    assert call(q=None) == 1
+    assert call(scores=None) == 1
+    assert call(ws_bytes=0) == 3
+    assert call(nch=-1) == 1
+
+
 def test_empty_calls_are_noops(lib):
     ok = Layer(256, 4, 4, 64, 0)
     assert lib.kvf_rope_table(ctypes.c_double(1e4), 64, 0, None, None, None) == 0
