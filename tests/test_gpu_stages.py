@@ -588,6 +588,10 @@ ATTN_CASES = [
     # a few long row tiles (a seam-window recompute set): up to 8 parts
     ("bf16", 32, 8, 128, [5184], [212]),
     ("bf16", 8, 2, 64, [6000, 300], [40, 3]),
+    # requests of equal shape: their row tiles are dispatched interleaved,
+    # longest first (with a workspace also split)
+    ("bf16", 16, 2, 128, [1100] * 6, [190] * 6),
+    ("bf16", 32, 8, 128, [2600] * 3, [330] * 3),
     ("f32", 4, 4, 64, [288], [108]),
     ("f32", 4, 2, 64, [150, 140], [70, 39]),
 ]
