@@ -30,6 +30,11 @@
  * fused cache (kvf_q8_cache) the calls that touch the cache have _q8 forms:
  *   kvf_rerotate_q8 -> kvf_score_q8 -> kvf_select_topk -> kvf_recompute_qkv
  *   -> kvf_scatter_kv_q8 -> kvf_sparse_q_attention_q8
+ * The re-positioning and a score can share one pass over the keys:
+ * kvf_rerotate_deviation / kvf_rerotate_q8_deviation (re-positioning plus
+ * the deviation score, with the probe keys computed first) and
+ * kvf_rerotate_score_attn_mass (keys-only re-positioning inside the
+ * attention-mass score's first pass).
  *
  * Conventions for every call:
  *  - Pointers are DEVICE pointers unless the comment says "host".
