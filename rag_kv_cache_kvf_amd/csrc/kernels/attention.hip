@@ -62,7 +62,7 @@ struct AttnArgs {
   int cu_tiles[KVF_MAX_REQ + 1]; // row-tile prefix
   int total_tiles;
   int fold_from;                 // dispatch slots at or past this run smallest-first
-  int interleave;                // requests of equal shape: the longest row tiles of every request first
+  int interleave;                // > 0: requests of equal shape, interleaved in groups of this many
   int parts;                     // > 1: long row tiles split their keys over up to this many workgroups
   int split_min;                 // key tiles from which a row tile is split
   float* ws_part;                // [tiles * Hkv, parts, 16-byte chunks, threads]
@@ -215,10 +215,10 @@ attn_mfma_kernel(AttnArgs a) {
   const int g = blockIdx.x % hkv;
   // Row tiles are numbered by position within each request, so a higher tile
   // of a request has more keys.  Dispatch runs largest-first: for requests
-  // of equal shape, the last row tile of every request, then the one
-  // before, and so on (the tile numbering alone would run one request's
-  // tiles down to its shortest before the next request's longest);
-  // otherwise by tile number.  When the whole grid is resident at once (two
+  // of equal shape, group by group from the last requests, the last row
+  // tile of every request of the group, then the one before, and so on
+  // (the tile numbering alone would run one request's tiles down to its
+  // shortest before the next request's longest); otherwise by tile number.  When the whole grid is resident at once (two
   // workgroups per CU), the second round of slots runs smallest-first so
   // each CU pairs a long tile with a short one.
   // With key splitting, the parts of a row tile are adjacent slots.
@@ -227,11 +227,14 @@ attn_mfma_kernel(AttnArgs a) {
   const int part = slot - rank0 * a.parts;
   const int rank = rank0 < a.fold_from ? rank0 : a.total_tiles - 1 - (rank0 - a.fold_from);
   int tile = a.total_tiles - 1 - rank;
-  if (a.interleave) {
-    const int nreq = a.b.n_req;
+  if (a.interleave > 0) {
+    const int gs = a.interleave;                 // requests per group
     const int per = a.cu_tiles[1];               // row tiles of every request
-    const int rr = rank % nreq;
-    tile = a.cu_tiles[rr] + per - 1 - rank / nreq;
+    const int j = rank / (gs * per);             // group, counted from the last requests
+    const int r_hi = a.b.n_req - j * gs;
+    const int r_lo = max(0, r_hi - gs);
+    const int lr = rank - j * gs * per;          // rank within the group
+    tile = a.cu_tiles[r_lo + lr % (r_hi - r_lo)] + per - 1 - lr / (r_hi - r_lo);
   }
   const int r = find_segment(a.cu_tiles, a.b.n_req, tile);
   const int tr = tile - a.cu_tiles[r];
@@ -1018,22 +1021,22 @@ static hipError_t attention_impl(const kvf_layer_desc& L, const BatchArgs& B, co
     // without splitting, a grid that one dispatch round holds runs its second
     // round smallest-first, pairing long and short tiles on a CU
     a.fold_from = a.parts == 1 && blocks <= 2 * kCUs ? std::max(1, kCUs / a.hkv) : a.total_tiles;
-    // Several requests with the same row tiles and length, in a grid of at
-    // most four dispatch rounds: interleave them longest-first, so the long
-    // row tiles of the last requests do not start late and end the kernel
-    // alone (Qwen2.5-3B-shaped batch, 16 requests x 33 row tiles x 2 kv
-    // heads: attention 181 -> 152 us).  Larger grids keep request order:
-    // their balance hardly depends on the order, and the workgroups in
-    // flight then share one request's keys and values in the caches
+    // Several requests with the same row tiles and length: interleave them
+    // longest-first, so the long row tiles of the last requests do not start
+    // late and end the kernel alone (Qwen2.5-3B-shaped batch, 16 requests x
+    // 33 row tiles x 2 kv heads: attention 181 -> 152 us).  A grid of at most
+    // four dispatch rounds interleaves the whole batch; larger grids
+    // interleave pairs of requests, so the workgroups in flight share the
+    // keys and values of two requests in the caches instead of all of them
     // (Qwen3-8B-shaped batch, 8 x 100 row tiles x 8 kv heads, 12.5 rounds:
-    // 3% slower interleaved).
+    // the whole batch interleaved was 3% slower than request order).
     a.interleave = 0;
-    if (B.n_req > 1 && blocks <= 4 * 2 * kCUs) {
+    if (B.n_req > 1) {
       bool same = true;
       const int per = a.cu_tiles[1], T0 = B.cu_T[1] - B.cu_T[0];
       for (int r = 1; r < B.n_req && same; ++r)
         same = a.cu_tiles[r + 1] - a.cu_tiles[r] == per && B.cu_T[r + 1] - B.cu_T[r] == T0;
-      a.interleave = same && per > 0 ? 1 : 0;
+      a.interleave = same && per > 0 ? (blocks <= 4 * 2 * kCUs ? B.n_req : 2) : 0;
     }
     hipError_t e;
     if (q8)
