@@ -790,3 +790,41 @@ def test_attention_full_size_sampled(kvf, wl_name):
         ref_l.append(l[0])
     assert_close_vectors(go[samp], np.array(ref_o), "bf16", f"{wl_name} attention (sampled rows)")
     assert_close(gl[samp], np.array(ref_l), "bf16", f"{wl_name} lse (sampled rows)", tol=1e-3)
+
+
+def test_attention_paired_dispatch_odd_request_count(kvf):
+    """Seven equal requests in a grid of more than four dispatch rounds: the
+    row tiles go out in pairs of requests, longest first, and the last group
+    holds a single request.  Every row is computed exactly once (each output
+    vector is written, sampled rows match the oracle)."""
+    import torch
+    n_req, hq, hkv, d, T, M = 7, 32, 8, 128, 1500, 1184      # 37 row tiles x 8 kv heads x 7 > 2048
+    cu_T = [r * T for r in range(n_req + 1)]
+    cu_q = [r * M for r in range(n_req + 1)]
+    pos = np.concatenate([np.sort(synth.random_rows(T, M, 40 + r)) for r in range(n_req)]).astype(np.int32)
+    k_s = encode(synth.random_normal((T * n_req, hkv, d), 41, "pd_k"), "bf16")
+    v_s = encode(synth.random_normal((T * n_req, hkv, d), 41, "pd_v"), "bf16")
+    q_s = encode(synth.random_normal((cu_q[-1], hq, d), 41, "pd_q", std=2.0), "bf16")
+    L = _layer(kvf, 4096, hq, hkv, d, "bf16")
+    kb = _kbatch(kvf, cu_T, [T] * n_req)
+    out = torch.full((cu_q[-1], hq, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((cu_q[-1], hq), float("nan"), dtype=torch.float32, device="cuda")
+    need = kvf.attention_workspace_size(L, kb, cu_q)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda") if need > 0 else None
+    kvf.sparse_q_attention(L, kb, to_gpu(q_s, "bf16"), to_gpu(pos), cu_q, to_gpu(k_s, "bf16"),
+                           to_gpu(v_s, "bf16"), 1 / math.sqrt(d), out, lse, workspace=ws)
+    go, gl = from_gpu(out), from_gpu(lse)
+    assert not np.isnan(go).any() and not np.isnan(gl).any(), "a row tile was not computed"
+    lo = fusion.Layer(4096, hq, hkv, d, 1e6)
+    # rows of every request, including the first request (the single-request group)
+    samp = np.unique(np.concatenate([synth.random_rows(cu_q[-1], 21, 42), [0, M - 1, cu_q[-1] - 1]]))
+    ref_o, ref_l = [], []
+    for m in samp:
+        r = int(m // M)
+        kr = decode(k_s[cu_T[r]:cu_T[r + 1]], "bf16")
+        vr = decode(v_s[cu_T[r]:cu_T[r + 1]], "bf16")
+        o, l = fusion.causal_attention(decode(q_s[m:m + 1], "bf16"), pos[m:m + 1], kr, vr, lo)
+        ref_o.append(o[0])
+        ref_l.append(l[0])
+    assert_close_vectors(go[samp], np.array(ref_o), "bf16", "paired dispatch attention (sampled rows)")
+    assert_close(gl[samp], np.array(ref_l), "bf16", "paired dispatch lse (sampled rows)", tol=1e-3)
